@@ -1,0 +1,374 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test ties one oracle step to a library routine, a closed form, brute
+force, an independent re-derivation (torch pooling / repeat ops that never use
+the oracle's index arithmetic), finite differences, or a number the pages
+print. A plausible mistake (wrong cube order, dropped 1/64, transposed
+operand, wrong sign in dS, missing coarse path in the gradient) fails at
+least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import workloads as WL
+from oracle import vsa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
+
+
+def _rand(shape, seed=0):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ---------------------------------------------------------------- step 0: tile
+@pytest.mark.parametrize("T,H,W", [(4, 4, 4), (8, 8, 8), (4, 8, 12), (12, 4, 8)])
+def test_tile_matches_reshape_transpose(T, H, W):
+    """Cube-major tiling equals the (T',4,H',4,W',4) reshape/transpose (an
+    independent construction: row-major cubes, row-major (t,y,x) in a cube)."""
+    d = 3
+    x = _rand((2, T, H, W, d))
+    ref = x.reshape(2, T // 4, 4, H // 4, 4, W // 4, 4, d).transpose(0, 1, 3, 5, 2, 4, 6, 7)
+    ref = ref.reshape(2, T * H * W // 64, 64, d)
+    np.testing.assert_array_equal(O.tile(x), ref)
+    np.testing.assert_array_equal(O.untile(O.tile(x), T, H, W), x)
+
+
+def test_tile_is_bijection():
+    perm = O.tiled_to_raster(8, 12, 16)
+    assert np.array_equal(np.sort(perm), np.arange(8 * 12 * 16))
+
+
+def test_tile_rejects_non_multiple_of_4():
+    with pytest.raises(ValueError):
+        O.tiled_to_raster(8, 6, 8)
+
+
+# ---------------------------------------------------------------- step 1: pool
+def test_pool_matches_avg_pool3d():
+    """Mean-pool equals torch avg_pool3d(kernel=stride=4) in row-major cube order."""
+    x = _rand((1, 2, 8, 12, 4, 5), 1)
+    xt = torch.from_numpy(x).permute(0, 1, 5, 2, 3, 4).reshape(2, 5, 8, 12, 4)
+    ref = F.avg_pool3d(xt, 4).reshape(2, 5, -1).transpose(1, 2).numpy()
+    np.testing.assert_allclose(O.pool(O.tile(x))[0], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_pool_brute_force_and_invariants():
+    T, H, W, d = 8, 4, 8, 2
+    x = _rand((T, H, W, d), 2)
+    got = O.pool(O.tile(x))
+    Hp, Wp = H // 4, W // 4
+    for tc in range(T // 4):
+        for yc in range(Hp):
+            for xc in range(Wp):
+                c = (tc * Hp + yc) * Wp + xc
+                acc = np.zeros(d)
+                for t in range(4):
+                    for y in range(4):
+                        for xx in range(4):
+                            acc += x[4 * tc + t, 4 * yc + y, 4 * xc + xx]
+                np.testing.assert_allclose(got[c], acc / 64, rtol=1e-14)
+    np.testing.assert_allclose(got.sum(0) * 64, x.reshape(-1, d).sum(0), rtol=1e-12)
+    np.testing.assert_array_equal(O.pool(O.tile(np.full((4, 4, 8, 3), 2.5))), np.full((2, 3), 2.5))
+
+
+# -------------------------------------------------------------- step 2: coarse
+def test_coarse_matches_sdpa():
+    qc, kc, vc = _rand((40, 16), 3), _rand((40, 16), 4), _rand((40, 16), 5)
+    s = 0.3
+    S, A, Oc, lse = O.coarse_attention(qc, kc, vc, s)
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(t)[None] for t in (qc, kc, vc)),
+                                         scale=s)[0].numpy()
+    np.testing.assert_allclose(Oc, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(A.sum(1), 1.0, rtol=1e-14)
+    ref_lse = torch.logsumexp(torch.from_numpy(S), dim=1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-14)
+    np.testing.assert_allclose(S, s * qc @ kc.T, rtol=1e-12, atol=1e-14)
+
+
+def test_coarse_uniform_closed_form():
+    """Equal keys give uniform weights: O_c is the mean of V_c in every row."""
+    qc = _rand((6, 4), 6)
+    kc = np.tile(_rand((1, 4), 7), (6, 1))
+    vc = _rand((6, 4), 8)
+    _, A, Oc, lse = O.coarse_attention(qc, kc, vc, 1.0)
+    np.testing.assert_allclose(A, 1 / 6, rtol=1e-14)
+    np.testing.assert_allclose(Oc, np.tile(vc.mean(0), (6, 1)), rtol=1e-13)
+    np.testing.assert_allclose(lse, qc @ kc[0] + math.log(6), rtol=1e-13)
+
+
+# --------------------------------------------------------------- step 3: top-K
+def _topk_brute(row, k):
+    """Sort (value desc, index asc) pairs by Python's sort and keep K."""
+    pairs = sorted(((-v, j) for j, v in enumerate(row)))
+    return sorted(j for _, j in pairs[:k])
+
+
+def test_topk_brute_force_with_ties():
+    rng = np.random.default_rng(9)
+    s = rng.integers(0, 4, size=(30, 12)).astype(float)   # many ties
+    for k in (1, 3, 7, 12):
+        idx, margin = O.topk_rows(s, k)
+        for i in range(s.shape[0]):
+            assert list(idx[i]) == _topk_brute(s[i], k)
+            sel = np.zeros(12, bool)
+            sel[idx[i]] = True
+            if k < 12:
+                assert s[i][sel].min() >= s[i][~sel].max()
+                srt = np.sort(s[i])[::-1]
+                assert margin[i] == srt[k - 1] - srt[k]
+            else:
+                assert sel.all() and margin[i] == np.inf
+
+
+def test_topk_rejects_bad_k():
+    with pytest.raises(ValueError):
+        O.topk_rows(np.zeros((2, 4)), 5)
+    with pytest.raises(ValueError):
+        O.topk_rows(np.zeros((2, 4)), 0)
+
+
+def test_mask_list_round_trip_and_transpose():
+    idx, lens = WL.random_lists(20, 20, 0, 9, seed=3)
+    m = O.lists_to_mask(idx, lens, 20)
+    assert np.array_equal(m.sum(1), lens)
+    idx2, lens2 = O.mask_to_lists(m, stride=idx.shape[1])
+    assert np.array_equal(lens2, lens)
+    for i in range(20):
+        assert np.array_equal(idx2[i, :lens[i]], idx[i, :lens[i]])
+    k2q, kl = O.transpose_lists(idx, lens, 20)
+    for j in range(20):
+        for i in range(20):
+            assert (i in k2q[j, :kl[j]]) == (j in idx[i, :lens[i]])
+        assert np.all(np.diff(k2q[j, :kl[j]]) > 0)
+
+
+def test_logit_error_bound_covers_fp32_pool_and_dot():
+    """An fp32 recomputation of the coarse logits stays inside the bound."""
+    w = WL.make_inputs("C2", heads=[0])
+    qt, kt = O.tile(w["q"][0, 0].astype(np.float64)), O.tile(w["k"][0, 0].astype(np.float64))
+    s = 1 / 8
+    tau = O.logit_error_bound(qt, kt, s)
+    qc32 = qt.astype(np.float32).sum(1, dtype=np.float32) / np.float32(64)
+    kc32 = kt.astype(np.float32).sum(1, dtype=np.float32) / np.float32(64)
+    s32 = (qc32 @ kc32.T).astype(np.float32) * np.float32(s)
+    exact = s * (O.pool(qt) @ O.pool(kt).T)
+    assert np.all(np.abs(s32 - exact).max(1) <= tau)
+    assert np.all(tau < 1e-3)
+
+
+# --------------------------------------------------------------- step 4: fine
+def test_fine_all_blocks_is_full_attention():
+    """With every cube listed the fine stage is textbook attention (SDPA, float64)."""
+    T, H, W, d = 8, 4, 8, 8
+    q, k, v = _rand((T, H, W, d), 10), _rand((T, H, W, d), 11), _rand((T, H, W, d), 12)
+    nc = T * H * W // 64
+    idx = np.tile(np.arange(nc), (nc, 1))
+    of, lse = O.fine_gathered(O.tile(q), O.tile(k), O.tile(v), idx, np.full(nc, nc), 0.4)
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(t.reshape(1, -1, d)) for t in (q, k, v)),
+                                         scale=0.4)[0].numpy()
+    np.testing.assert_allclose(O.untile(of, T, H, W).reshape(-1, d), ref, rtol=1e-11, atol=1e-13)
+    z = 0.4 * q.reshape(-1, d) @ k.reshape(-1, d).T
+    np.testing.assert_allclose(O.untile_rows(lse, T, H, W).reshape(-1),
+                               torch.logsumexp(torch.from_numpy(z), 1).numpy(), rtol=1e-13)
+
+
+def test_fine_literal_equals_gathered_and_order_invariance():
+    T, H, W, d = 8, 8, 4, 6
+    q, k, v = _rand((T, H, W, d), 13), _rand((T, H, W, d), 14), _rand((T, H, W, d), 15)
+    nc = T * H * W // 64
+    idx, lens = WL.random_lists(nc, nc, 0, nc, seed=5)
+    lens[0] = 0                                          # one empty list
+    m = O.lists_to_mask(idx, lens, nc)
+    of_l, lse_l = O.fine_literal(q, k, v, m, 0.5)
+    of_g, lse_g = O.fine_gathered(O.tile(q), O.tile(k), O.tile(v), idx, lens, 0.5)
+    np.testing.assert_allclose(O.untile(of_g, T, H, W), of_l, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(O.untile_rows(lse_g, T, H, W), lse_l, rtol=1e-13)
+    assert np.all(of_g[0] == 0) and np.all(np.isneginf(lse_g[0]))
+    # shuffled list order gives the same result
+    rng = np.random.default_rng(1)
+    idx_s = idx.copy()
+    for i in range(nc):
+        idx_s[i, :lens[i]] = rng.permutation(idx[i, :lens[i]])
+    of_s, _ = O.fine_gathered(O.tile(q), O.tile(k), O.tile(v), idx_s, lens, 0.5)
+    np.testing.assert_allclose(of_s, of_g, rtol=1e-12, atol=1e-14)
+
+
+def test_fine_rows_of_p_sum_to_one():
+    """V = constant c on every key gives O_f = c exactly where the row is live."""
+    T, H, W, d = 4, 8, 8, 4
+    q, k = _rand((T, H, W, d), 16), _rand((T, H, W, d), 17)
+    v = np.full((T, H, W, d), 1.75)
+    nc = 4
+    idx, lens = WL.random_lists(nc, nc, 1, 3, seed=2)
+    of, _ = O.fine_gathered(O.tile(q), O.tile(k), O.tile(v), idx, lens, 1.0)
+    np.testing.assert_allclose(of, 1.75, rtol=1e-14)
+
+
+# ------------------------------------------------------------ step 5: combine
+def test_combine_gate_special_cases():
+    oc, of = _rand((4, 4, 4, 3), 18), _rand((4, 4, 4, 3), 19)
+    g = np.abs(_rand((4, 4, 4, 3), 20))
+    np.testing.assert_array_equal(O.combine(oc, of, np.zeros_like(g), None), of)
+    np.testing.assert_array_equal(O.combine(oc, of, None, np.zeros_like(g)), oc)
+    np.testing.assert_allclose(O.combine(oc, of, 2 * g, g), 2 * oc * g + of * g, rtol=1e-15)
+
+
+def test_repeat_coarse_matches_repeat_interleave():
+    oc = _rand((1, 2, 8, 3), 21)          # 8 cubes of an 8x8x8 latent
+    got = O.repeat_coarse(oc, 8, 8, 8)
+    ref = torch.from_numpy(oc).reshape(1, 2, 2, 2, 2, 3)
+    for ax in (2, 3, 4):
+        ref = ref.repeat_interleave(4, dim=ax)
+    np.testing.assert_array_equal(got, ref.numpy())
+
+
+# ----------------------------------------------------------------- end to end
+def _torch_vsa(q, k, v, g_c, g_f, mask, scale):
+    """Independent torch expression of the forward with a fixed block mask:
+    avg_pool3d pooling, repeat_interleave broadcast, token-level masked softmax."""
+    B, h, T, H, W, d = q.shape
+    Tp, Hp, Wp = T // 4, H // 4, W // 4
+
+    def pool(x):
+        p = F.avg_pool3d(x.permute(0, 1, 5, 2, 3, 4).reshape(B * h, d, T, H, W), 4)
+        return p.reshape(B, h, d, -1).transpose(-1, -2)
+
+    qc, kc, vc = pool(q), pool(k), pool(v)
+    a = torch.softmax(scale * qc @ kc.transpose(-1, -2), dim=-1)
+    oc = (a @ vc).reshape(B, h, Tp, Hp, Wp, d)
+    for ax in (2, 3, 4):
+        oc = oc.repeat_interleave(4, dim=ax)
+    cid = torch.arange(Tp * Hp * Wp).reshape(Tp, Hp, Wp)
+    for ax in (0, 1, 2):
+        cid = cid.repeat_interleave(4, dim=ax)
+    cid = cid.reshape(-1)
+    tok_mask = mask[:, :, cid][:, :, :, cid]
+    qr, kr, vr = (x.reshape(B, h, -1, d) for x in (q, k, v))
+    z = (scale * qr @ kr.transpose(-1, -2)).masked_fill(~tok_mask, float("-inf"))
+    of = (torch.softmax(z, dim=-1) @ vr).reshape(B, h, T, H, W, d)
+    return oc * g_c + of * g_f
+
+
+def test_forward_equals_independent_torch_expression():
+    w = WL.make_inputs("C1")
+    fwd = O.forward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], topk=2, with_literal=True)
+    nc = 8
+    mask = np.stack([[O.lists_to_mask(fwd["idx"][b, h], fwd["len"][b, h], nc)
+                      for h in range(2)] for b in range(1)])
+    ref = _torch_vsa(*(torch.from_numpy(w[x].astype(np.float64)) for x in ("q", "k", "v", "g_c", "g_f")),
+                     torch.from_numpy(mask), 1 / 8)
+    np.testing.assert_allclose(fwd["o"], ref.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fwd["o_f"], fwd["o_f_literal"], rtol=1e-12, atol=1e-14)
+    assert np.all(np.diff(fwd["idx"], axis=-1) > 0)
+
+
+def test_adaptation_start_equals_full_attention():
+    """The pages: K = all cubes, G_c = 0 and G_f removed equals full attention
+    (VSA summary page, section 2 'Pretrained adaptation'; reading notes key design 5)."""
+    w = WL.make_inputs("C1")
+    nc = 8
+    fwd = O.forward(w["q"], w["k"], w["v"], np.zeros_like(w["g_c"]), None, topk=nc)
+    for h in range(2):
+        ref = F.scaled_dot_product_attention(
+            *(torch.from_numpy(w[x][0, h].astype(np.float64).reshape(1, -1, 64)) for x in ("q", "k", "v")))
+        np.testing.assert_allclose(fwd["o"][0, h].reshape(-1, 64), ref[0].numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_topk_margin_consistent_with_selection():
+    w = WL.make_inputs("C2", heads=[0])
+    qt, kt = O.tile(w["q"][0, 0].astype(np.float64)), O.tile(w["k"][0, 0].astype(np.float64))
+    S, _, _, _ = O.coarse_attention(O.pool(qt), O.pool(kt), O.pool(kt), 1 / 8)
+    idx, margin = O.topk_rows(S, 32)
+    assert np.all(margin >= 0)
+    for i in range(0, 256, 37):
+        sel = np.zeros(256, bool)
+        sel[idx[i]] = True
+        assert S[i][sel].min() - S[i][~sel].max() == pytest.approx(margin[i])
+
+
+# ------------------------------------------------------------------- backward
+def test_backward_matches_autograd_of_independent_expression():
+    w = WL.make_inputs_custom(1, 2, 4, 8, 8, 8, dtype="f32", seed=3, scale=0.5)
+    nc = 8
+    idx, lens = WL.random_lists(nc, 2 * nc, 1, 5, seed=4)
+    idx = idx.reshape(1, 2, nc, -1)
+    lens = lens.reshape(1, 2, nc)
+    fwd = O.forward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], topk=0, idx=idx, lens=lens)
+    bwd = O.backward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], w["d_o"], fwd)
+    mask = np.stack([[O.lists_to_mask(idx[0, h], lens[0, h], nc) for h in range(2)]])
+    ts = {x: torch.from_numpy(w[x].astype(np.float64)).requires_grad_(True)
+          for x in ("q", "k", "v", "g_c", "g_f")}
+    out = _torch_vsa(ts["q"], ts["k"], ts["v"], ts["g_c"], ts["g_f"], torch.from_numpy(mask),
+                     1 / math.sqrt(4))
+    np.testing.assert_allclose(fwd["o"], out.detach().numpy(), rtol=1e-12, atol=1e-14)
+    (out * torch.from_numpy(w["d_o"].astype(np.float64))).sum().backward()
+    for name, key in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg_c", "g_c"), ("dg_f", "g_f")):
+        np.testing.assert_allclose(bwd[name], ts[key].grad.numpy(), rtol=1e-10, atol=1e-12,
+                                   err_msg=name)
+
+
+def test_backward_finite_differences_topk_mode():
+    """Central differences along random directions, top-K mode, where every
+    row's selection margin is far above the perturbation (mask constant)."""
+    w = WL.make_inputs_custom(1, 1, 4, 8, 8, 8, dtype="f32", seed=11, scale=1.0)
+    args = {x: w[x].astype(np.float64) for x in ("q", "k", "v", "g_c", "g_f", "d_o")}
+    fwd = O.forward(args["q"], args["k"], args["v"], args["g_c"], args["g_f"], topk=3)
+    assert fwd["margin"].min() > 1e-4
+    bwd = O.backward(args["q"], args["k"], args["v"], args["g_c"], args["g_f"], args["d_o"], fwd)
+    rng = np.random.default_rng(0)
+    eps = 1e-6
+
+    def loss(a):
+        f = O.forward(a["q"], a["k"], a["v"], a["g_c"], a["g_f"], topk=3)
+        assert np.array_equal(f["idx"], fwd["idx"])
+        return float((f["o"] * args["d_o"]).sum())
+
+    for name, key in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg_c", "g_c"), ("dg_f", "g_f")):
+        dirn = rng.standard_normal(args[key].shape)
+        ap = dict(args); ap[key] = args[key] + eps * dirn
+        am = dict(args); am[key] = args[key] - eps * dirn
+        fd = (loss(ap) - loss(am)) / (2 * eps)
+        an = float((bwd[name] * dirn).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_backward_empty_lists_give_coarse_only_gradient():
+    """With every list empty the fine stage contributes nothing; dV then comes
+    from the coarse path alone and spreads evenly over each cube."""
+    w = WL.make_inputs_custom(1, 1, 4, 4, 4, 8, dtype="f32", seed=5)
+    idx = np.full((1, 1, 2, 1), -1)
+    lens = np.zeros((1, 1, 2), np.int64)
+    fwd = O.forward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], topk=0, idx=idx, lens=lens)
+    assert np.all(fwd["o_f"] == 0)
+    bwd = O.backward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], w["d_o"], fwd)
+    dvt = O.tile(bwd["dv"])[0, 0]
+    np.testing.assert_allclose(dvt, np.repeat(dvt[:, :1], 64, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(dvt[:, 0] * 64, bwd["dv_c"][0, 0], rtol=1e-13)
+
+
+# ----------------------------------------------------------- page-stated facts
+def test_page_facts_on_work_accounting():
+    facts = {f["id"]: f for f in json.load(open(GOLDEN))["facts"]}
+    cube = facts["cube_and_block"]["cube"]
+    assert int(np.prod(cube)) == facts["cube_and_block"]["block"] == O.TILE
+    T, H, W = facts["pseudocode_setting"]["video"]
+    k = facts["pseudocode_setting"]["topk"]
+    assert k == facts["default_topk"]["topk"]
+    n = T * H * W
+    nc = n // O.TILE
+    assert abs(n - facts["sequence_16k"]["tokens_approx"]) / n < 0.05
+    lens = np.full(nc, k)
+    assert 1 - lens.sum() / nc ** 2 == facts["sparsity_at_tile_64"]["sparsity"]
+    d = 64
+    fine = O.fine_flops_forward(lens, d)
+    dense = O.dense_flops(1, 1, n, d)
+    assert dense / fine == pytest.approx(facts["attention_flop_reduction"]["factor_approx"], rel=0.05)
+    coarse = O.coarse_flops(1, 1, nc, d)
+    assert coarse / dense < facts["coarse_share_of_attention"]["max_fraction"]
+    assert coarse / (coarse + fine) < facts["coarse_share_of_total"]["max_fraction"]
