@@ -1,0 +1,228 @@
+#!/usr/bin/env python
+"""Benchmark of the VSA forward on one MI355X: the 720p workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Workload (default): B=1, 40 heads, head_dim 128, a 24x44x80 latent (84480
+tokens, 1320 cubes of 4x4x4), top-32 cubes per query cube, bf16, rank-4
+shared component in Q/K/V, U(0,1) gates, seed 0. One step = one whole VSA
+forward (cube mean-pool, coarse attention + top-K + index lists, fine
+block-sparse attention with the gated combine), inputs resident in HBM.
+
+Prints one JSON line. `value` is attention TFLOP/s counting only computed
+64x64 blocks (4*64*64*d FLOP per selected (query cube, key cube) pair) over
+the whole forward's wall time. `roofline` covers the dominant kernel (the
+fused fine-attention + combine kernel), timed with HIP events on the stream
+it is launched on; `stages` gives every kernel of the step. `cpu_baseline`
+is the float64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_combine_720p_traffic.json")
+FINE_SRC = os.path.join(ROOT, "block_sparse_video_cube_amd", "csrc", "fine_fwd.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fine_source_hash() -> str:
+    with open(FINE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fine kernel from the committed counter
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != fine_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(workload: str, heads: list[int]) -> dict:
+    """The oracle, as it stands, on `heads` of the workload (full forward)."""
+    import numpy as np
+    import workloads as WL
+    from oracle import vsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl is optional
+        threads = 1
+    w = WL.get(workload)
+    x = WL.make_inputs(workload, heads=heads)
+    t0 = time.perf_counter()
+    f = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=w.topk)
+    dt = time.perf_counter() - t0
+    flops = O.fine_flops_forward(f["len"], w.head_dim)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"heads {heads} of {w.heads} (b=0) of the {workload} workload, full float64 forward "
+                      f"(pool, coarse, top-{w.topk}, fine, combine): {dt:.1f} s",
+            "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bf16_720p_24x44x80")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1, help="heads of the oracle sample")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the VSA operator is built and measured on a single MI355X "
+              "(heads are independent; the multi-GPU sharding is a design note, not run). Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import workloads as WL
+    import block_sparse_video_cube_amd as V
+
+    torch.cuda.set_device(0)
+    w = WL.get(args.workload)
+    log(f"generating {w.name} inputs")
+    t0 = time.perf_counter()
+    x = WL.make_inputs(w.name)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; copying to the GPU")
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(a, dtype):
+        return torch.from_numpy(a).to("cuda:0").to(dtype).contiguous()
+
+    q, k, v, gc, gf = (dev(x[n], td) for n in ("q", "k", "v", "g_c", "g_f"))
+    if w.topk == 0:
+        idx_in, len_in = dev(x["idx"], torch.int32), dev(x["len"], torch.int32)
+    del x
+    p = V.Problem(w.B, w.heads, w.T, w.H, w.W, w.head_dim, dtype=w.dtype, topk=w.topk,
+                  list_stride=w.list_stride)
+    ws = V.workspace(p, q)
+    o = torch.empty_like(q)
+    if w.topk > 0:
+        idx = torch.empty((w.B, w.heads, w.Nc, p.stride), dtype=torch.int32, device=q.device)
+        lens = torch.empty((w.B, w.heads, w.Nc), dtype=torch.int32, device=q.device)
+    else:
+        idx, lens = idx_in, len_in
+    pooled = [torch.empty((w.B, w.heads, w.Nc, w.head_dim), dtype=torch.float32, device=q.device)
+              for _ in range(4)]
+    lse_c = torch.empty((w.B, w.heads, w.Nc), dtype=torch.float32, device=q.device)
+
+    def step():
+        V.forward(p, q, k, v, gc, gf, idx=idx, lens=lens, ws=ws, out=o)
+
+    def staged(ev):
+        ev[0].record()
+        V.pool(p, q, k, v, ws=ws, out=pooled[:3])
+        ev[1].record()
+        V.coarse(p, *pooled[:3], out=(pooled[3], lse_c, idx if w.topk > 0 else None,
+                                      lens if w.topk > 0 else None))
+        ev[2].record()
+        V.fine_combine(p, q, k, v, idx, lens, pooled[3], gc, gf, ws=ws, out=o)
+        ev[3].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # Per-kernel breakdown: the same kernels through the stage entry points,
+    # events on the launch stream between them.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        staged(e)
+    torch.cuda.synchronize()
+    stage_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
+
+    n_pairs = int(lens.sum().item())
+    fine_flop = 4.0 * 64 * 64 * w.head_dim * n_pairs
+    coarse_flop = 4.0 * w.B * w.heads * w.Nc * w.Nc * w.head_dim
+    esz = 2 if w.dtype == "bf16" else 4
+    bh = w.B * w.heads
+    raster = bh * w.N * w.head_dim
+    pooled_b = bh * w.Nc * w.head_dim * 4
+    pool_bytes = 3 * raster * esz + 3 * pooled_b + (raster * 2 if w.dtype == "bf16" else 0)
+    fine_bytes = 6 * raster * esz + pooled_b + bh * w.Nc * p.stride * 4 * 2
+    value = fine_flop / (ms_step * 1e-3) / 1e12
+    achieved = fine_flop / (stage_ms[2] * 1e-3) / 1e12
+    traffic = measured_traffic()
+    line = {
+        "metric": "VSA attention TFLOP/s (computed blocks) + % bf16 MFMA peak, 720p fwd",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "heads": w.heads, "head_dim": w.head_dim,
+                   "latent": [w.T, w.H, w.W], "tokens": w.N, "cubes": w.Nc, "topk": w.topk,
+                   "computed_block_pairs": n_pairs, "fine_tflop": round(fine_flop / 1e12, 4),
+                   "sparsity": round(1 - n_pairs / (bh * w.Nc * w.Nc), 4)},
+        "pct_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(w.B * w.N / (ms_step * 1e-3), 1),
+        "roofline": {"kernel": "fine_fwd_bf16 (fine attention + gated combine)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_bytes": fine_bytes, "avg_launch_ms": round(stage_ms[2], 4)},
+        "stages": {
+            "pool": {"ms": round(stage_ms[0], 4), "bound": "hbm", "algorithmic_bytes": pool_bytes,
+                     "GB_per_s": round(pool_bytes / (stage_ms[0] * 1e-3) / 1e9, 1),
+                     "frac": round(pool_bytes / (stage_ms[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "coarse_topk": {"ms": round(stage_ms[1], 4), "bound": "mfma_fp32", "flop": coarse_flop,
+                            "TFLOP_per_s": round(coarse_flop / (stage_ms[1] * 1e-3) / 1e12, 2),
+                            "frac": round(coarse_flop / (stage_ms[1] * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)},
+            "fine_combine": {"ms": round(stage_ms[2], 4), "bound": "mfma", "flop": fine_flop,
+                             "TFLOP_per_s": round(achieved, 2), "frac": round(achieved / PEAK_BF16_TFLOPS, 4)},
+        },
+        "wall_s_timed": round(wall, 3),
+    }
+    log(f"forward {ms_step:.3f} ms/step = {value:.1f} TFLOP/s; pool {stage_ms[0]:.3f} ms, "
+        f"coarse {stage_ms[1]:.3f} ms, fine+combine {stage_ms[2]:.3f} ms ({achieved:.1f} TFLOP/s)")
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_heads} head(s)")
+        line["cpu_baseline"] = cpu_baseline(w.name, list(range(args.cpu_heads)))
+        log(f"cpu baseline {line['cpu_baseline']['value']:.4f} TFLOP/s")
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

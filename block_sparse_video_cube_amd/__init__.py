@@ -1,0 +1,237 @@
+"""VSA (Video Sparse Attention) coarse-fine attention on AMD MI355X (gfx950).
+
+Thin binding over the C ABI of libvsa.so (include/vsa.h): it allocates the
+output tensors with torch on the current device, passes raw pointers and the
+current HIP stream, and checks the returned status. Every step of the
+operator runs in the library's HIP kernels.
+
+Tensors: q, k, v, gates, outputs are [B, heads, T, H, W, head_dim]
+contiguous on the GPU, bf16 or fp32. Index lists are int32
+[B, heads, Nc, list_stride] with lengths int32 [B, heads, Nc].
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from ._native import VSA_BF16, VSA_F32, VsaError, VsaProblem, check, lib
+
+__all__ = ["Problem", "VsaError", "forward", "backward", "pool", "coarse", "fine_forward", "fine_combine", "combine",
+           "combine_backward", "index_transpose", "fine_backward", "coarse_backward",
+           "check_lists_host", "validate_lists", "workspace_bytes", "saved_bytes", "max_cubes"]
+
+
+@dataclass(frozen=True)
+class Problem:
+    B: int
+    heads: int
+    T: int
+    H: int
+    W: int
+    head_dim: int
+    dtype: str = "bf16"          # "bf16" or "f32"
+    topk: int = 32               # > 0: top-K mode; 0: explicit lists
+    list_stride: int = 0         # 0 => topk
+    scale: float = 0.0           # 0 => 1/sqrt(head_dim)
+
+    @property
+    def N(self) -> int:
+        return self.T * self.H * self.W
+
+    @property
+    def Nc(self) -> int:
+        return self.N // 64
+
+    @property
+    def stride(self) -> int:
+        return self.list_stride if self.list_stride else self.topk
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def c(self) -> VsaProblem:
+        code = {"bf16": VSA_BF16, "f32": VSA_F32}.get(self.dtype, 99)
+        return VsaProblem(self.B, self.heads, self.T, self.H, self.W, self.head_dim, code,
+                          float(self.scale), self.topk, self.list_stride)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the VSA library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _empty(shape, dtype, like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def workspace_bytes(p: Problem, training: bool = False) -> int:
+    return int(lib().vsa_workspace_bytes(ctypes.byref(p.c()), int(training)))
+
+
+def saved_bytes(p: Problem) -> int:
+    return int(lib().vsa_saved_bytes(ctypes.byref(p.c())))
+
+
+def max_cubes() -> int:
+    return int(lib().vsa_max_cubes())
+
+
+def workspace(p: Problem, like: torch.Tensor, training: bool = False) -> torch.Tensor:
+    n = workspace_bytes(p, training)
+    if n == 0:
+        raise VsaError(2, "workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=like.device)
+
+
+def _raster(p: Problem):
+    return (p.B, p.heads, p.T, p.H, p.W, p.head_dim)
+
+
+def _pooled(p: Problem):
+    return (p.B, p.heads, p.Nc, p.head_dim)
+
+
+def forward(p: Problem, q, k, v, g_c=None, g_f=None, idx=None, lens=None, training: bool = False,
+            ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Whole VSA forward. Returns (o, idx, lens, saved); saved is None unless training."""
+    if p.topk > 0:
+        idx = _empty((p.B, p.heads, p.Nc, p.stride), torch.int32, q) if idx is None else idx
+        lens = _empty((p.B, p.heads, p.Nc), torch.int32, q) if lens is None else lens
+    elif idx is None or lens is None:
+        raise ValueError("explicit-list mode (topk == 0) needs idx and lens")
+    o = _empty(_raster(p), p.torch_dtype, q) if out is None else out
+    saved = torch.empty(saved_bytes(p), dtype=torch.uint8, device=q.device) if training else None
+    ws = workspace(p, q) if ws is None else ws
+    check(lib().vsa_forward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(g_c), _ptr(g_f), _ptr(idx),
+                            _ptr(lens), _ptr(o), _ptr(saved), _ptr(ws), ws.numel(), _stream(q.device)),
+          "vsa_forward")
+    return o, idx, lens, saved
+
+
+def backward(p: Problem, q, k, v, g_c, g_f, idx, lens, saved, d_o, ws: Optional[torch.Tensor] = None):
+    """Whole VSA backward. Returns dict dq, dk, dv, dg_c, dg_f (gate grads None for NULL gates)."""
+    dq, dk, dv = (_empty(_raster(p), p.torch_dtype, q) for _ in range(3))
+    dgc = _empty(_raster(p), p.torch_dtype, q) if g_c is not None else None
+    dgf = _empty(_raster(p), p.torch_dtype, q) if g_f is not None else None
+    ws = workspace(p, q, training=True) if ws is None else ws
+    check(lib().vsa_backward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(g_c), _ptr(g_f), _ptr(idx),
+                             _ptr(lens), _ptr(saved), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgc),
+                             _ptr(dgf), _ptr(ws), ws.numel(), _stream(q.device)), "vsa_backward")
+    return dict(dq=dq, dk=dk, dv=dv, dg_c=dgc, dg_f=dgf)
+
+
+def pool(p: Problem, q, k, v, ws: Optional[torch.Tensor] = None, out=None):
+    qc, kc, vc = out if out is not None else (_empty(_pooled(p), torch.float32, q) for _ in range(3))
+    check(lib().vsa_pool(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(qc), _ptr(kc), _ptr(vc),
+                         _ptr(ws), 0 if ws is None else ws.numel(), _stream(q.device)), "vsa_pool")
+    return qc, kc, vc
+
+
+def coarse(p: Problem, q_c, k_c, v_c, out=None):
+    """Coarse stage; out = (o_c, lse_c, idx, lens) reuses caller buffers."""
+    if out is not None:
+        oc, lse, idx, lens = out
+    else:
+        oc = _empty(_pooled(p), torch.float32, q_c)
+        lse = _empty((p.B, p.heads, p.Nc), torch.float32, q_c)
+        idx = lens = None
+        if p.topk > 0:
+            idx = _empty((p.B, p.heads, p.Nc, p.stride), torch.int32, q_c)
+            lens = _empty((p.B, p.heads, p.Nc), torch.int32, q_c)
+    check(lib().vsa_coarse(ctypes.byref(p.c()), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(oc), _ptr(lse), _ptr(idx),
+                           _ptr(lens), _stream(q_c.device)), "vsa_coarse")
+    return oc, lse, idx, lens
+
+
+def fine_forward(p: Problem, q, k, v, idx, lens, ws: Optional[torch.Tensor] = None):
+    of = _empty(_raster(p), p.torch_dtype, q)
+    lse = _empty((p.B, p.heads, p.T, p.H, p.W), torch.float32, q)
+    check(lib().vsa_fine_forward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(lens), _ptr(of),
+                                 _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(q.device)),
+          "vsa_fine_forward")
+    return of, lse
+
+
+def fine_combine(p: Problem, q, k, v, idx, lens, o_c, g_c=None, g_f=None, ws: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, with_fine: bool = False):
+    """Fused fine stage + gated combine. Returns o, or (o, o_f, lse_f) with with_fine."""
+    o = _empty(_raster(p), p.torch_dtype, q) if out is None else out
+    of = _empty(_raster(p), p.torch_dtype, q) if with_fine else None
+    lse = _empty((p.B, p.heads, p.T, p.H, p.W), torch.float32, q) if with_fine else None
+    check(lib().vsa_fine_combine(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(lens), _ptr(o_c),
+                                 _ptr(g_c), _ptr(g_f), _ptr(o), _ptr(of), _ptr(lse), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(q.device)), "vsa_fine_combine")
+    return (o, of, lse) if with_fine else o
+
+
+def combine(p: Problem, o_c, o_f, g_c=None, g_f=None):
+    o = _empty(_raster(p), p.torch_dtype, o_f)
+    check(lib().vsa_combine(ctypes.byref(p.c()), _ptr(o_c), _ptr(o_f), _ptr(g_c), _ptr(g_f), _ptr(o),
+                            _stream(o_f.device)), "vsa_combine")
+    return o
+
+
+def combine_backward(p: Problem, d_o, o_c, o_f, g_c=None, g_f=None, ws: Optional[torch.Tensor] = None):
+    dgc = _empty(_raster(p), p.torch_dtype, d_o) if g_c is not None else None
+    dgf = _empty(_raster(p), p.torch_dtype, d_o) if g_f is not None else None
+    dof = _empty(_raster(p), p.torch_dtype, d_o)
+    delta = _empty((p.B, p.heads, p.T, p.H, p.W), torch.float32, d_o)
+    doc = _empty(_pooled(p), torch.float32, d_o)
+    check(lib().vsa_combine_backward(ctypes.byref(p.c()), _ptr(d_o), _ptr(o_c), _ptr(o_f), _ptr(g_c), _ptr(g_f),
+                                     _ptr(dgc), _ptr(dgf), _ptr(dof), _ptr(delta), _ptr(doc), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(d_o.device)),
+          "vsa_combine_backward")
+    return dict(dg_c=dgc, dg_f=dgf, d_o_f=dof, delta=delta, d_o_c=doc)
+
+
+def index_transpose(p: Problem, idx, lens):
+    off = _empty((p.B, p.heads, p.Nc + 1), torch.int32, idx)
+    k2q = _empty((p.B, p.heads, p.Nc * p.stride), torch.int32, idx)
+    check(lib().vsa_index_transpose(ctypes.byref(p.c()), _ptr(idx), _ptr(lens), _ptr(off), _ptr(k2q),
+                                    _stream(idx.device)), "vsa_index_transpose")
+    return off, k2q
+
+
+def fine_backward(p: Problem, q, k, v, idx, lens, k2q_off, k2q, lse_f, d_o_f, delta, dq_c, dk_c, dv_c,
+                  ws: torch.Tensor):
+    dq, dk, dv = (_empty(_raster(p), p.torch_dtype, q) for _ in range(3))
+    check(lib().vsa_fine_backward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(lens),
+                                  _ptr(k2q_off), _ptr(k2q), _ptr(lse_f), _ptr(d_o_f), _ptr(delta), _ptr(dq_c),
+                                  _ptr(dk_c), _ptr(dv_c), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                  _stream(q.device)), "vsa_fine_backward")
+    return dq, dk, dv
+
+
+def coarse_backward(p: Problem, q_c, k_c, v_c, o_c, lse_c, d_o_c, ws: torch.Tensor):
+    dqc, dkc, dvc = (_empty(_pooled(p), torch.float32, q_c) for _ in range(3))
+    check(lib().vsa_coarse_backward(ctypes.byref(p.c()), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(o_c),
+                                    _ptr(lse_c), _ptr(d_o_c), _ptr(dqc), _ptr(dkc), _ptr(dvc), _ptr(ws),
+                                    ws.numel(), _stream(q_c.device)), "vsa_coarse_backward")
+    return dqc, dkc, dvc
+
+
+def check_lists_host(p: Problem, idx, lens) -> None:
+    """CPU check of explicit lists given as numpy int32 arrays (raises VsaError)."""
+    import numpy as np
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    check(lib().vsa_check_lists_host(ctypes.byref(p.c()), idx.ctypes.data_as(ctypes.c_void_p),
+                                     lens.ctypes.data_as(ctypes.c_void_p)), "vsa_check_lists_host")
+
+
+def validate_lists(p: Problem, idx, lens) -> None:
+    """Device check of explicit lists (synchronises the current stream; raises VsaError)."""
+    flag = _empty((4,), torch.int32, idx)
+    check(lib().vsa_validate_lists(ctypes.byref(p.c()), _ptr(idx), _ptr(lens), _ptr(flag), _stream(idx.device)),
+          "vsa_validate_lists")

@@ -1,0 +1,444 @@
+// C ABI of the VSA operator: validation, buffer layouts, kernel sequencing.
+// Declarations and contracts: include/vsa.h.
+#include <cmath>
+#include <cstring>
+
+#include "../../include/vsa.h"
+#include "vsa_kernels.h"
+
+using namespace vsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Dims {
+  long BH, N, Nc, D, stride;
+  size_t elem;  // bytes per raster element
+};
+
+// Host-side validation of the problem; fills the launch context.
+vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
+  if (p == nullptr) return VSA_ERR_NULL;
+  if (p->B < 1 || p->heads < 1) return VSA_ERR_SHAPE;
+  if (p->T < 4 || p->H < 4 || p->W < 4 || (p->T & 3) || (p->H & 3) || (p->W & 3)) return VSA_ERR_SHAPE;
+  const long N = (long)p->T * p->H * p->W;
+  const long BH = (long)p->B * p->heads;
+  if (N > (1L << 30) || BH > (1L << 24)) return VSA_ERR_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return VSA_ERR_HEAD_DIM;
+  if (p->dtype != VSA_F32 && p->dtype != VSA_BF16) return VSA_ERR_DTYPE;
+  const long Nc = N / 64;
+  if (BH * Nc > 0x7fffffffL) return VSA_ERR_SHAPE;
+  if (BH * N * p->head_dim > (1L << 40)) return VSA_ERR_SHAPE;
+  if (!std::isfinite(p->scale) || p->scale < 0.f) return VSA_ERR_SCALE;
+  if (p->topk < 0 || p->topk > Nc) return VSA_ERR_TOPK;
+  const long stride = p->list_stride == 0 ? p->topk : p->list_stride;
+  if (p->topk > 0 && stride < p->topk) return VSA_ERR_TOPK;
+  if (stride < 1 || stride > Nc) return VSA_ERR_TOPK;
+  if (Nc > coarse_max_cubes()) return VSA_ERR_UNSUPPORTED;
+  if (L != nullptr) {
+    L->g = make_grid(p->T, p->H, p->W);
+    L->BH = (int)BH;
+    L->D = p->head_dim;
+    L->bf16 = p->dtype == VSA_BF16;
+    L->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
+    L->topk = p->topk;
+    L->stride = (int)stride;
+    L->stream = nullptr;
+  }
+  if (d != nullptr) {
+    d->BH = BH; d->N = N; d->Nc = Nc; d->D = p->head_dim; d->stride = stride;
+    d->elem = p->dtype == VSA_BF16 ? 2 : 4;
+  }
+  return VSA_OK;
+}
+
+inline bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+// Checks a list of (pointer, required) pairs: NULL and alignment.
+vsa_status check_ptrs(std::initializer_list<std::pair<const void*, bool>> ptrs) {
+  for (const auto& pr : ptrs) {
+    if (pr.first == nullptr) {
+      if (pr.second) return VSA_ERR_NULL;
+      continue;
+    }
+    if (misaligned(pr.first)) return VSA_ERR_ALIGN;
+  }
+  return VSA_OK;
+}
+
+// ---- buffer layouts (every region 256-byte aligned) -----------------------
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T> T* take(size_t count) {
+    T* r = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return r;
+  }
+};
+
+// Saved for backward: pooled means, O_c, LSE_c, LSE_f, O_f.
+struct Saved {
+  float *qc, *kc, *vc, *oc, *lse_c, *lse_f;
+  void* of;
+  size_t bytes;
+};
+Saved carve_saved(const Dims& d, void* base) {
+  Carver c(base);
+  Saved s;
+  const size_t pooled = d.BH * d.Nc * d.D;
+  s.qc = c.take<float>(pooled);
+  s.kc = c.take<float>(pooled);
+  s.vc = c.take<float>(pooled);
+  s.oc = c.take<float>(pooled);
+  s.lse_c = c.take<float>(d.BH * d.Nc);
+  s.lse_f = c.take<float>(d.BH * d.N);
+  s.of = c.take<char>(d.BH * d.N * d.D * d.elem);
+  s.bytes = c.off;
+  return s;
+}
+
+// Forward workspace: V T-tiles (bf16) and, for inference, the pooled tensors.
+struct FwdWs {
+  bf16* vt;
+  float *qc, *kc, *vc, *oc, *lse_c;
+  size_t bytes;
+};
+FwdWs carve_fwd_ws(const Dims& d, void* base) {
+  Carver c(base);
+  FwdWs w;
+  w.vt = d.elem == 2 ? c.take<bf16>(d.BH * d.N * d.D) : nullptr;
+  const size_t pooled = d.BH * d.Nc * d.D;
+  w.qc = c.take<float>(pooled);
+  w.kc = c.take<float>(pooled);
+  w.vc = c.take<float>(pooled);
+  w.oc = c.take<float>(pooled);
+  w.lse_c = c.take<float>(d.BH * d.Nc);
+  w.bytes = c.off;
+  return w;
+}
+
+// Backward workspace.
+struct BwdWs {
+  bf16 *dof, *doft, *qt, *kt;
+  float *delta, *doc, *dqc, *dkc, *dvc, *p_scr, *ds_scr;
+  int32_t *k2q_off, *k2q;
+  size_t bytes;
+};
+BwdWs carve_bwd_ws(const Dims& d, void* base) {
+  Carver c(base);
+  BwdWs w;
+  const size_t rast = d.BH * d.N * d.D;
+  w.dof = c.take<bf16>(rast);
+  w.doft = c.take<bf16>(rast);
+  w.qt = c.take<bf16>(rast);
+  w.kt = c.take<bf16>(rast);
+  w.delta = c.take<float>(d.BH * d.N);
+  const size_t pooled = d.BH * d.Nc * d.D;
+  w.doc = c.take<float>(pooled);
+  w.dqc = c.take<float>(pooled);
+  w.dkc = c.take<float>(pooled);
+  w.dvc = c.take<float>(pooled);
+  w.p_scr = c.take<float>(d.BH * d.Nc * d.Nc);
+  w.ds_scr = c.take<float>(d.BH * d.Nc * d.Nc);
+  w.k2q_off = c.take<int32_t>(d.BH * (d.Nc + 1));
+  w.k2q = c.take<int32_t>(d.BH * d.Nc * d.stride);
+  w.bytes = c.off;
+  return w;
+}
+
+inline vsa_status hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa_status_string(vsa_status s) {
+  switch (s) {
+    case VSA_OK: return "ok";
+    case VSA_ERR_NULL: return "a required pointer is NULL";
+    case VSA_ERR_SHAPE: return "invalid shape (B, heads >= 1; T, H, W positive multiples of 4; sizes in range)";
+    case VSA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case VSA_ERR_DTYPE: return "unknown dtype";
+    case VSA_ERR_TOPK: return "topk outside [0, Nc] or invalid list_stride";
+    case VSA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case VSA_ERR_WORKSPACE: return "workspace or saved buffer too small";
+    case VSA_ERR_INDEX: return "an index list is invalid";
+    case VSA_ERR_UNSUPPORTED: return "not supported by this build";
+    case VSA_ERR_HIP: return "a HIP call or kernel launch failed";
+    case VSA_ERR_SCALE: return "scale must be finite and >= 0";
+  }
+  return "unknown status";
+}
+
+int32_t vsa_version(void) { return 100; }
+
+int32_t vsa_max_cubes(void) { return coarse_max_cubes(); }
+
+size_t vsa_workspace_bytes(const vsa_problem* p, int32_t training) {
+  Dims d;
+  if (check_problem(p, nullptr, &d) != VSA_OK) return 0;
+  const size_t f = carve_fwd_ws(d, nullptr).bytes;
+  if (!training) return f;
+  const size_t b = carve_bwd_ws(d, nullptr).bytes;
+  return f > b ? f : b;
+}
+
+size_t vsa_saved_bytes(const vsa_problem* p) {
+  Dims d;
+  if (check_problem(p, nullptr, &d) != VSA_OK) return 0;
+  return carve_saved(d, nullptr).bytes;
+}
+
+vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const void* v, const void* g_c,
+                       const void* g_f, int32_t* idx, int32_t* len, void* o, void* saved, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{q, true}, {k, true}, {v, true}, {g_c, false}, {g_f, false}, {idx, true}, {len, true},
+                   {o, true}, {saved, false}, {workspace, true}});
+  if (st != VSA_OK) return st;
+  const FwdWs ws = carve_fwd_ws(d, workspace);
+  if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
+  L.stream = static_cast<hipStream_t>(stream);
+  float *qc = ws.qc, *kc = ws.kc, *vc = ws.vc, *oc = ws.oc, *lse_c = ws.lse_c, *lse_f = nullptr;
+  void* of = nullptr;
+  if (saved != nullptr) {
+    const Saved s = carve_saved(d, saved);
+    qc = s.qc; kc = s.kc; vc = s.vc; oc = s.oc; lse_c = s.lse_c; lse_f = s.lse_f; of = s.of;
+  }
+  hipError_t e = launch_pool(L, q, k, v, qc, kc, vc, ws.vt);
+  if (e == hipSuccess) e = launch_coarse(L, qc, kc, vc, oc, lse_c, L.topk > 0 ? idx : nullptr, L.topk > 0 ? len : nullptr);
+  if (e == hipSuccess) e = launch_fine_fwd(L, q, k, v, ws.vt, idx, len, of, lse_f, oc, g_c, g_f, o);
+  return hip_status(e);
+}
+
+vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v, const void* g_c,
+                        const void* g_f, const int32_t* idx, const int32_t* len, const void* saved,
+                        const void* d_o, void* dq, void* dk, void* dv, void* dg_c, void* dg_f, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  if (!L.bf16) return VSA_ERR_UNSUPPORTED;
+  st = check_ptrs({{q, true}, {k, true}, {v, true}, {g_c, false}, {g_f, false}, {idx, true}, {len, true},
+                   {saved, true}, {d_o, true}, {dq, true}, {dk, true}, {dv, true}, {dg_c, false},
+                   {dg_f, false}, {workspace, true}});
+  if (st != VSA_OK) return st;
+  const BwdWs ws = carve_bwd_ws(d, workspace);
+  if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
+  const Saved s = carve_saved(d, const_cast<void*>(saved));
+  L.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_combine_bwd(L, d_o, s.oc, s.of, g_c, g_f, g_c ? dg_c : nullptr, g_f ? dg_f : nullptr,
+                                    ws.dof, ws.delta, ws.doc, ws.doft);
+  if (e == hipSuccess) e = launch_index_transpose(L, idx, len, ws.k2q_off, ws.k2q);
+  if (e == hipSuccess)
+    e = launch_coarse_bwd(L, s.qc, s.kc, s.vc, s.oc, s.lse_c, ws.doc, ws.dqc, ws.dkc, ws.dvc, ws.ds_scr, ws.p_scr);
+  if (e == hipSuccess) e = launch_ttile(L, static_cast<const bf16*>(q), ws.qt);
+  if (e == hipSuccess) e = launch_ttile(L, static_cast<const bf16*>(k), ws.kt);
+  if (e == hipSuccess)
+    e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                        ws.qt, ws.kt, idx, len, ws.k2q_off, ws.k2q, s.lse_f, ws.dof, ws.doft, ws.delta, ws.dqc,
+                        ws.dkc, ws.dvc, static_cast<bf16*>(dq), static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+  return hip_status(e);
+}
+
+vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const void* v, float* q_c, float* k_c,
+                    float* v_c, void* workspace, size_t ws_bytes, void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{q, true}, {k, true}, {v, true}, {q_c, true}, {k_c, true}, {v_c, true}, {workspace, false}});
+  if (st != VSA_OK) return st;
+  bf16* vt = nullptr;
+  if (workspace != nullptr && L.bf16) {
+    const FwdWs ws = carve_fwd_ws(d, workspace);
+    if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
+    vt = ws.vt;
+  }
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_pool(L, q, k, v, q_c, k_c, v_c, vt));
+}
+
+vsa_status vsa_coarse(const vsa_problem* p, const float* q_c, const float* k_c, const float* v_c, float* o_c,
+                      float* lse_c, int32_t* idx, int32_t* len, void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  const bool sel = L.topk > 0;
+  st = check_ptrs({{q_c, true}, {k_c, true}, {v_c, true}, {o_c, true}, {lse_c, true}, {idx, sel}, {len, sel}});
+  if (st != VSA_OK) return st;
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_coarse(L, q_c, k_c, v_c, o_c, lse_c, sel ? idx : nullptr, sel ? len : nullptr));
+}
+
+vsa_status vsa_fine_forward(const vsa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
+                            const int32_t* len, void* o_f, float* lse_f, const void* workspace, size_t ws_bytes,
+                            void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{q, true}, {k, true}, {v, true}, {idx, true}, {len, true}, {o_f, true}, {lse_f, true},
+                   {workspace, L.bf16}});
+  if (st != VSA_OK) return st;
+  bf16* vt = nullptr;
+  if (L.bf16) {
+    const FwdWs ws = carve_fwd_ws(d, const_cast<void*>(workspace));
+    if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
+    vt = ws.vt;
+  }
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_fine_fwd(L, q, k, v, vt, idx, len, o_f, lse_f, nullptr, nullptr, nullptr, nullptr));
+}
+
+vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
+                            const int32_t* len, const float* o_c, const void* g_c, const void* g_f, void* o, void* o_f,
+                            float* lse_f, const void* workspace, size_t ws_bytes, void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{q, true}, {k, true}, {v, true}, {idx, true}, {len, true}, {o_c, true}, {g_c, false},
+                   {g_f, false}, {o, true}, {o_f, false}, {lse_f, false}, {workspace, L.bf16}});
+  if (st != VSA_OK) return st;
+  bf16* vt = nullptr;
+  if (L.bf16) {
+    const FwdWs ws = carve_fwd_ws(d, const_cast<void*>(workspace));
+    if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
+    vt = ws.vt;
+  }
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_fine_fwd(L, q, k, v, vt, idx, len, o_f, lse_f, o_c, g_c, g_f, o));
+}
+
+vsa_status vsa_combine(const vsa_problem* p, const float* o_c, const void* o_f, const void* g_c, const void* g_f,
+                       void* o, void* stream) {
+  Launch L;
+  vsa_status st = check_problem(p, &L, nullptr);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{o_c, true}, {o_f, true}, {g_c, false}, {g_f, false}, {o, true}});
+  if (st != VSA_OK) return st;
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_combine(L, o_c, o_f, g_c, g_f, o));
+}
+
+vsa_status vsa_combine_backward(const vsa_problem* p, const void* d_o, const float* o_c, const void* o_f,
+                                const void* g_c, const void* g_f, void* dg_c, void* dg_f, void* d_o_f, float* delta,
+                                float* d_o_c, void* workspace, size_t ws_bytes, void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{d_o, true}, {o_c, true}, {o_f, true}, {g_c, false}, {g_f, false}, {dg_c, false},
+                   {dg_f, false}, {d_o_f, true}, {delta, true}, {d_o_c, true}, {workspace, false}});
+  if (st != VSA_OK) return st;
+  bf16* doft = nullptr;
+  if (workspace != nullptr && L.bf16) {
+    const BwdWs ws = carve_bwd_ws(d, workspace);
+    if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
+    doft = ws.doft;
+  }
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_combine_bwd(L, d_o, o_c, o_f, g_c, g_f, dg_c, dg_f, d_o_f, delta, d_o_c, doft));
+}
+
+vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const int32_t* len, int32_t* k2q_off,
+                               int32_t* k2q, void* stream) {
+  Launch L;
+  vsa_status st = check_problem(p, &L, nullptr);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{idx, true}, {len, true}, {k2q_off, true}, {k2q, true}});
+  if (st != VSA_OK) return st;
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_index_transpose(L, idx, len, k2q_off, k2q));
+}
+
+vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
+                             const int32_t* len, const int32_t* k2q_off, const int32_t* k2q, const float* lse_f,
+                             const void* d_o_f, const float* delta, const float* dq_c, const float* dk_c,
+                             const float* dv_c, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  if (!L.bf16) return VSA_ERR_UNSUPPORTED;
+  st = check_ptrs({{q, true}, {k, true}, {v, true}, {idx, true}, {len, true}, {k2q_off, true}, {k2q, true},
+                   {lse_f, true}, {d_o_f, true}, {delta, true}, {dq_c, true}, {dk_c, true}, {dv_c, true},
+                   {dq, true}, {dk, true}, {dv, true}, {workspace, true}});
+  if (st != VSA_OK) return st;
+  const BwdWs ws = carve_bwd_ws(d, workspace);
+  if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
+  L.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_ttile(L, static_cast<const bf16*>(q), ws.qt);
+  if (e == hipSuccess) e = launch_ttile(L, static_cast<const bf16*>(k), ws.kt);
+  if (e == hipSuccess)
+    e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                        ws.qt, ws.kt, idx, len, k2q_off, k2q, lse_f, static_cast<const bf16*>(d_o_f), ws.doft,
+                        delta, dq_c, dk_c, dv_c, static_cast<bf16*>(dq), static_cast<bf16*>(dk),
+                        static_cast<bf16*>(dv));
+  return hip_status(e);
+}
+
+vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const float* k_c, const float* v_c,
+                               const float* o_c, const float* lse_c, const float* d_o_c, float* dq_c, float* dk_c,
+                               float* dv_c, void* workspace, size_t ws_bytes, void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{q_c, true}, {k_c, true}, {v_c, true}, {o_c, true}, {lse_c, true}, {d_o_c, true},
+                   {dq_c, true}, {dk_c, true}, {dv_c, true}, {workspace, true}});
+  if (st != VSA_OK) return st;
+  const BwdWs ws = carve_bwd_ws(d, workspace);
+  if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_coarse_bwd(L, q_c, k_c, v_c, o_c, lse_c, d_o_c, dq_c, dk_c, dv_c, ws.ds_scr, ws.p_scr));
+}
+
+vsa_status vsa_check_lists_host(const vsa_problem* p, const int32_t* idx, const int32_t* len) {
+  Dims d;
+  vsa_status st = check_problem(p, nullptr, &d);
+  if (st != VSA_OK) return st;
+  if (idx == nullptr || len == nullptr) return VSA_ERR_NULL;
+  const long rows = d.BH * d.Nc;
+  for (long r = 0; r < rows; ++r) {
+    const int n = len[r];
+    if (n < 0 || n > d.stride) return VSA_ERR_INDEX;
+    int prev = -1;
+    for (int t = 0; t < n; ++t) {
+      const int v = idx[r * d.stride + t];
+      if (v <= prev || v >= d.Nc) return VSA_ERR_INDEX;
+      prev = v;
+    }
+  }
+  return VSA_OK;
+}
+
+vsa_status vsa_validate_lists(const vsa_problem* p, const int32_t* idx, const int32_t* len, int32_t* flag,
+                              void* stream) {
+  Launch L;
+  vsa_status st = check_problem(p, &L, nullptr);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{idx, true}, {len, true}});
+  if (st != VSA_OK) return st;
+  if (flag == nullptr) return VSA_ERR_NULL;
+  L.stream = static_cast<hipStream_t>(stream);
+  if (hipMemsetAsync(flag, 0, sizeof(int32_t), L.stream) != hipSuccess) return VSA_ERR_HIP;
+  if (launch_validate_lists(L, idx, len, flag) != hipSuccess) return VSA_ERR_HIP;
+  int32_t h = 0;
+  if (hipMemcpyAsync(&h, flag, sizeof(int32_t), hipMemcpyDeviceToHost, L.stream) != hipSuccess) return VSA_ERR_HIP;
+  if (hipStreamSynchronize(L.stream) != hipSuccess) return VSA_ERR_HIP;
+  return h ? VSA_ERR_INDEX : VSA_OK;
+}
+
+}  // extern "C"

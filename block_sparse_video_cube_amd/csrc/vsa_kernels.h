@@ -1,0 +1,54 @@
+// Internal launchers of the VSA HIP kernels (not part of the C ABI).
+#pragma once
+
+#include "vsa_common.h"
+
+namespace vsa {
+
+// Launch context shared by the launchers: one problem, one stream.
+struct Launch {
+  Grid g;
+  int BH;          // B * heads
+  int D;           // head_dim (64 or 128)
+  bool bf16;       // dtype of raster tensors
+  float scale;     // softmax scale (resolved, > 0)
+  int topk;        // > 0: top-K mode
+  int stride;      // idx row stride
+  hipStream_t stream;
+};
+
+hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
+                       float* vc, bf16* vt);
+hipError_t launch_ttile(const Launch& L, const bf16* x, bf16* xt);
+
+int coarse_max_cubes();
+hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, const float* vc, float* oc,
+                         float* lse, int32_t* idx, int32_t* len);
+
+// Fine forward. For bf16, vt holds the V T-tiles. When oc is not null the
+// kernel also forms o = O_c * g_c + O_f * g_f (gates may be null = ones) and
+// writes it to `o`; o_f / lse_f may then be null (not written).
+hipError_t launch_fine_fwd(const Launch& L, const void* q, const void* k, const void* v, const bf16* vt,
+                           const int32_t* idx, const int32_t* len, void* o_f, float* lse_f, const float* oc,
+                           const void* g_c, const void* g_f, void* o);
+
+hipError_t launch_combine(const Launch& L, const float* oc, const void* of, const void* gc, const void* gf,
+                          void* o);
+hipError_t launch_combine_bwd(const Launch& L, const void* d_o, const float* oc, const void* of,
+                              const void* gc, const void* gf, void* dgc, void* dgf, void* dof,
+                              float* delta, float* doc, bf16* doft);
+
+hipError_t launch_index_transpose(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* k2q_off,
+                                  int32_t* k2q);
+hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, const float* vc,
+                             const float* oc, const float* lse, const float* doc, float* dqc, float* dkc,
+                             float* dvc, float* ds_scratch, float* p_scratch);
+hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const bf16* qt,
+                           const bf16* kt, const int32_t* idx, const int32_t* len, const int32_t* k2q_off,
+                           const int32_t* k2q, const float* lse_f, const bf16* dof, const bf16* doft,
+                           const float* delta, const float* dqc, const float* dkc, const float* dvc, bf16* dq,
+                           bf16* dk, bf16* dv);
+
+hipError_t launch_validate_lists(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* flag);
+
+}  // namespace vsa

@@ -1,0 +1,235 @@
+/*
+ * vsa.h - C ABI of the VSA (Video Sparse Attention) coarse-fine attention
+ * operator for one AMD Instinct MI355X (gfx950) GPU.
+ *
+ * The operator (VSA summary page, paperlayer.ai arXiv 2505.13389, section 2
+ * "Methods" and Appendix B "Pseudocode of VSA"; VSA reading notes, key
+ * designs 1-3):
+ *   1. partition the T x H x W latent into (4,4,4) cubes, one 64-token tile each;
+ *   2. mean-pool Q, K, V per cube and run dense attention over the cubes,
+ *      giving A_c and O_c;
+ *   3. keep the top-K key cubes of every row of A_c (or take caller-supplied
+ *      per-query-cube lists of variable length, the VSA2 "variable number of
+ *      key-value pairs per query", VSA2 abstract);
+ *   4. exact token attention of every query cube over the tokens of its kept
+ *      cubes only (O_f);
+ *   5. O = O_c (repeated to the cube's tokens) * G_c + O_f * G_f.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Float tensors are [B, heads, T, H, W, head_dim] contiguous (raster token
+ *   order, head_dim fastest) in the problem's dtype (fp32 or bf16), unless the
+ *   argument says otherwise. Pooled tensors ("_c") are fp32 [B, heads, Nc,
+ *   head_dim], cubes in row-major order over (T/4, H/4, W/4); Nc = T*H*W/64.
+ *   Per-token scalars (LSE_f, delta) are fp32 [B, heads, T, H, W].
+ * - Index lists: idx is int32 [B, heads, Nc, list_stride], len int32
+ *   [B, heads, Nc]. Row i holds len[i] strictly increasing key-cube ids in
+ *   [0, Nc); entries beyond len[i] are ignored.
+ * - Every pointer is a device pointer unless documented as host, and must be
+ *   16-byte aligned. The caller allocates and owns every buffer; the library
+ *   never allocates or frees device memory and keeps no per-call state.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   is asynchronous: nothing synchronises unless documented.
+ * - Outputs are fully overwritten, never accumulated.
+ * - Errors: host-checkable faults return an error before anything is
+ *   enqueued; a failed launch returns VSA_ERR_HIP. Nothing aborts or prints.
+ *   Invalid index lists (duplicates, out of range, unsorted) are undefined
+ *   behaviour unless checked first with vsa_check_lists_host or
+ *   vsa_validate_lists.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VSA_OK = 0,
+  VSA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  VSA_ERR_SHAPE = 2,       /* B/heads < 1, T/H/W not positive multiples of 4,
+                              or a size that overflows                        */
+  VSA_ERR_HEAD_DIM = 3,    /* head_dim not 64 or 128                         */
+  VSA_ERR_DTYPE = 4,       /* unknown dtype                                  */
+  VSA_ERR_TOPK = 5,        /* topk outside [0, Nc] or list_stride invalid    */
+  VSA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned               */
+  VSA_ERR_WORKSPACE = 7,   /* workspace / saved buffer smaller than required */
+  VSA_ERR_INDEX = 8,       /* an index list failed validation                */
+  VSA_ERR_UNSUPPORTED = 9, /* valid request this build does not implement    */
+  VSA_ERR_HIP = 10,        /* a HIP call or kernel launch failed             */
+  VSA_ERR_SCALE = 11       /* scale is negative, NaN or infinite             */
+} vsa_status;
+
+typedef enum { VSA_F32 = 0, VSA_BF16 = 1 } vsa_dtype;
+
+typedef struct {
+  int32_t B, heads;      /* batch and heads; every (b, h) is independent      */
+  int32_t T, H, W;       /* latent grid, each a positive multiple of 4         */
+  int32_t head_dim;      /* 64 or 128                                          */
+  int32_t dtype;         /* vsa_dtype of every float tensor except pooled ones */
+  float scale;           /* softmax scale of both stages; 0 => 1/sqrt(head_dim) */
+  int32_t topk;          /* > 0: keep the K best key cubes per query cube
+                            (1..Nc); 0: the caller supplies the lists          */
+  int32_t list_stride;   /* row stride of idx; 0 => topk. Top-K mode needs
+                            list_stride >= topk; list mode needs 1..Nc         */
+} vsa_problem;
+
+/* Short text for a status code (static storage, never NULL). */
+const char* vsa_status_string(vsa_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t vsa_version(void);
+
+/* Largest Nc (cubes per (b, h)) the coarse stage accepts in this build. */
+int32_t vsa_max_cubes(void);
+
+/* Bytes of device workspace vsa_forward (training = 0) or vsa_backward
+ * (training = 1) needs for problem p; 0 if p is invalid. The workspace holds
+ * transposed bf16 tiles and scratch; its contents are meaningless between
+ * calls. */
+size_t vsa_workspace_bytes(const vsa_problem* p, int32_t training);
+
+/* Bytes of the `saved` buffer a training forward fills and vsa_backward
+ * reads: pooled Q_c/K_c/V_c, O_c and LSE_c (fp32), O_f (dtype) and LSE_f
+ * (fp32). 0 if p is invalid. */
+size_t vsa_saved_bytes(const vsa_problem* p);
+
+/* Whole forward, steps 1-5 above.
+ *   q, k, v     : inputs (dtype, raster).
+ *   g_c, g_f    : gates, shaped like o (dtype). NULL means the gate is all
+ *                 ones (an ungated branch, as when the fine gate is removed at
+ *                 the start of sparse adaptation; reading notes key design 5).
+ *   idx, len    : topk > 0: outputs, the ascending top-K lists (len = K);
+ *                 topk == 0: inputs, the caller's lists.
+ *   o           : output (dtype, raster).
+ *   saved       : NULL for inference; otherwise vsa_saved_bytes(p) bytes that
+ *                 vsa_backward will read.
+ *   workspace   : ws_bytes >= vsa_workspace_bytes(p, 0) bytes. */
+vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const void* v,
+                       const void* g_c, const void* g_f, int32_t* idx, int32_t* len,
+                       void* o, void* saved, void* workspace, size_t ws_bytes, void* stream);
+
+/* Whole backward of sum(O * dO) with the selection held constant (the top-K
+ * mask is piecewise constant and carries no gradient). Inputs as for the
+ * forward that filled `saved` (same q, k, v, g_c, g_f, idx, len), d_o
+ * (dtype, raster). Outputs dq, dk, dv (dtype, raster) and dg_c, dg_f (dtype,
+ * raster; each may be NULL when its gate was NULL, then it is not written).
+ * workspace: ws_bytes >= vsa_workspace_bytes(p, 1). bf16 only in this build
+ * (fp32 returns VSA_ERR_UNSUPPORTED). */
+vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
+                        const void* g_c, const void* g_f, const int32_t* idx, const int32_t* len,
+                        const void* saved, const void* d_o, void* dq, void* dk, void* dv,
+                        void* dg_c, void* dg_f, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- stage-level entry points (same conventions; for per-stage parity and
+ * timing; vsa_forward / vsa_backward chain exactly these kernels) ---------- */
+
+/* Step 1, cube mean-pool: q_c/k_c/v_c (fp32 [B, heads, Nc, head_dim]) are
+ * the means of the 64 tokens of every cube (VSA summary page, Appendix B;
+ * reading notes key design 1). When dtype is bf16 and workspace is not NULL
+ * it also writes the transposed V tiles the fine forward reads
+ * (ws_bytes >= vsa_workspace_bytes(p, 0)). */
+vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const void* v,
+                    float* q_c, float* k_c, float* v_c, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/* Steps 2-3, coarse stage: S_c = scale * Q_c K_c^T, A_c = row softmax,
+ * o_c = A_c V_c (fp32 [B, heads, Nc, head_dim]) and lse_c = log-sum-exp of
+ * each row of S_c (fp32 [B, heads, Nc]). With topk > 0 it also writes idx /
+ * len: per row the K largest logits (ties to the smaller cube id) as an
+ * ascending list (VSA summary page, section 2 and Appendix B; reading notes
+ * key design 1, and the fused softmax + top-K + mask-to-index kernel of the
+ * notes' training section). With topk == 0 idx / len are not touched (may be
+ * NULL). S_c stays on chip. Requires Nc <= vsa_max_cubes(). */
+vsa_status vsa_coarse(const vsa_problem* p, const float* q_c, const float* k_c, const float* v_c,
+                      float* o_c, float* lse_c, int32_t* idx, int32_t* len, void* stream);
+
+/* Step 4, fine block-sparse attention: for every query token of cube i,
+ * softmax attention over the tokens of the cubes listed in row i only
+ * (VSA summary page, section 2 "Fine stage" and Appendix B; reading notes key
+ * design 2). o_f (dtype, raster) and lse_f (fp32 [B, heads, T, H, W]); an
+ * empty list gives o_f = 0 and lse_f = -inf. For bf16, workspace must hold
+ * the transposed V tiles written by vsa_pool (same problem, same v). */
+vsa_status vsa_fine_forward(const vsa_problem* p, const void* q, const void* k, const void* v,
+                            const int32_t* idx, const int32_t* len, void* o_f, float* lse_f,
+                            const void* workspace, size_t ws_bytes, void* stream);
+
+/* Steps 4 and 5 fused, the kernel vsa_forward runs: the fine stage with the
+ * gated combine in its epilogue, o = O_c[cube] * g_c + O_f * g_f (dtype,
+ * raster), so O_f never goes to memory unless o_f is given. o_f (dtype,
+ * raster) and lse_f (fp32) are optional outputs (NULL = not written); O_f is
+ * rounded to the dtype before the combine, so o equals vsa_combine of the
+ * returned o_f. Gates NULL => ones. Workspace as for vsa_fine_forward. */
+vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, const void* v,
+                            const int32_t* idx, const int32_t* len, const float* o_c,
+                            const void* g_c, const void* g_f, void* o, void* o_f, float* lse_f,
+                            const void* workspace, size_t ws_bytes, void* stream);
+
+/* Step 5, gated combine + untile: o = O_c[cube(token)] * g_c + o_f * g_f
+ * (reading notes key design 3; App. B repeat of the coarse output). Gates
+ * NULL => ones. */
+vsa_status vsa_combine(const vsa_problem* p, const float* o_c, const void* o_f,
+                       const void* g_c, const void* g_f, void* o, void* stream);
+
+/* Backward of step 5 (calculus of the combine): dg_c = dO * O_c[cube],
+ * dg_f = dO * O_f, d_o_f = dO * G_f (dtype, raster), delta = rowsum(d_o_f *
+ * o_f) (fp32 [B, heads, T, H, W]) and d_o_c[c] = sum over the 64 tokens of
+ * cube c of dO * G_c (fp32 [B, heads, Nc, head_dim]). dg_c / dg_f may be
+ * NULL (not written). When workspace is not NULL it also writes the
+ * transposed d_o_f tiles vsa_fine_backward reads. */
+vsa_status vsa_combine_backward(const vsa_problem* p, const void* d_o, const float* o_c,
+                                const void* o_f, const void* g_c, const void* g_f,
+                                void* dg_c, void* dg_f, void* d_o_f, float* delta, float* d_o_c,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+/* Index transpose for the backward: k2q_off int32 [B, heads, Nc + 1] and
+ * k2q int32 [B, heads, Nc * list_stride]: for key cube j the query cubes i
+ * whose list holds j, ascending, at k2q[(b,h) * Nc * list_stride +
+ * k2q_off[(b,h)][j] ... k2q_off[(b,h)][j+1]). */
+vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const int32_t* len,
+                               int32_t* k2q_off, int32_t* k2q, void* stream);
+
+/* Backward of step 4 and of the pooling: dq, dk, dv (dtype, raster) =
+ * fine-attention gradient + (dq_c, dk_c, dv_c)[cube] / 64, where the pooled
+ * gradients (fp32 [B, heads, Nc, head_dim]) come from vsa_coarse_backward.
+ * lse_f from the forward; d_o_f and delta from vsa_combine_backward, which
+ * must also have written the transposed d_o_f tiles into this same
+ * workspace (ws_bytes >= vsa_workspace_bytes(p, 1)); k2q_off / k2q from
+ * vsa_index_transpose. bf16 only. dQ walks each query cube's list, dK / dV
+ * walk the transposed lists, so no atomics are used and the result is
+ * deterministic. */
+vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
+                             const int32_t* idx, const int32_t* len, const int32_t* k2q_off,
+                             const int32_t* k2q, const float* lse_f, const void* d_o_f,
+                             const float* delta, const float* dq_c, const float* dk_c,
+                             const float* dv_c, void* dq, void* dk, void* dv, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/* Backward of steps 1-2 at cube level (dense attention backward in fp32):
+ * dq_c, dk_c, dv_c (fp32 [B, heads, Nc, head_dim]) from q_c, k_c, v_c, o_c,
+ * lse_c and d_o_c. workspace >= vsa_workspace_bytes(p, 1). */
+vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const float* k_c,
+                               const float* v_c, const float* o_c, const float* lse_c,
+                               const float* d_o_c, float* dq_c, float* dk_c, float* dv_c,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- list validation ----------------------------------------------------- */
+
+/* Host check of explicit lists (host pointers): every len in [0, list_stride],
+ * every listed id in [0, Nc), strictly increasing. Returns VSA_OK or
+ * VSA_ERR_INDEX. Runs on the CPU only. */
+vsa_status vsa_check_lists_host(const vsa_problem* p, const int32_t* idx, const int32_t* len);
+
+/* The same check on device lists; synchronises `stream` to read the verdict.
+ * `flag` is a caller-provided device int32 used as the result cell. */
+vsa_status vsa_validate_lists(const vsa_problem* p, const int32_t* idx, const int32_t* len,
+                              int32_t* flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H */

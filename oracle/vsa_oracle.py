@@ -158,24 +158,45 @@ def transpose_lists(idx: np.ndarray, lens: np.ndarray, nc: int):
     return mask_to_lists(lists_to_mask(idx, lens, nc).T.copy(), stride=idx.shape[0])
 
 
-def logit_error_bound(qt: np.ndarray, kt: np.ndarray, scale: float) -> np.ndarray:
+def _pool_error_bound(xt: np.ndarray, sig_bits: int) -> np.ndarray:
+    """Bound on |fp32 mean-pool - exact mean| per (cube, channel), any order.
+
+    The 64 inputs carry ``sig_bits`` significant bits (8 for bf16 values, 24
+    for fp32). If every input is a multiple of 2^q and the sum of their
+    magnitudes is below 2^(q+24), every partial sum is an fp32 number, so the
+    fp32 sum is exact whatever the order; otherwise the classic recursive-
+    summation bound gamma_63 * sum|x| applies. Dividing by 64 is exact.
+    """
+    u = 2.0 ** -24
+    mag = np.abs(xt)
+    _, e = np.frexp(mag)                      # |x| = m * 2^e, 0.5 <= m < 1
+    ulp_exp = np.where(mag > 0, e - sig_bits, np.iinfo(np.int32).max)
+    q = ulp_exp.min(axis=-2)
+    total = mag.sum(axis=-2)
+    exact = total < np.ldexp(1.0, np.minimum(q + 24, 1000))
+    gamma = (TILE - 1) * u / (1 - (TILE - 1) * u)
+    return np.where(exact, 0.0, gamma * total / TILE)
+
+
+def logit_error_bound(qt: np.ndarray, kt: np.ndarray, scale: float, sig_bits: int = 8) -> np.ndarray:
     """Per-row bound on |fp32 coarse logit - exact logit| for one (b, h).
 
-    Pooling 64 values and a d-term dot product in float32, in any summation
-    order, err by at most gamma_n = n*u/(1-n*u) (u = 2^-24) times the sum of
-    absolute terms (the standard forward error bound of recursive summation).
-    Returns tau[i] = max_j bound(i, j); two logits of a row compare correctly
-    whenever they differ by more than 2*tau[i].
+    The fp32 path pools 64 inputs (error bounded by ``_pool_error_bound``),
+    forms the d-term dot product of the pooled rows (error at most gamma_d
+    times the sum of absolute products, any order: the standard forward error
+    bound of recursive summation) and multiplies by the fp32 scale (a few
+    unit roundings of |S|). Returns tau[i] = max_j bound(i, j); two logits of
+    a row compare the same way in fp32 and exactly whenever they differ by
+    more than 2*tau[i].
     """
     u = 2.0 ** -24
     d = qt.shape[-1]
-    g = lambda n: n * u / (1 - n * u)
-    qc, kc = pool(qt), pool(kt)
-    qa, ka = np.abs(qt).mean(axis=-2), np.abs(kt).mean(axis=-2)
-    b = (g(d) * (np.abs(qc) @ np.abs(kc).T)
-         + g(TILE + 1) * (qa @ np.abs(kc).T + np.abs(qc) @ ka.T)
-         + g(TILE + 1) ** 2 * (qa @ ka.T))
-    b = scale * b * (1 + 4 * u) + 4 * u * np.abs(scale * (qc @ kc.T))
+    gd = d * u / (1 - d * u)
+    qc, kc = np.abs(pool(qt)), np.abs(pool(kt))
+    eq, ek = _pool_error_bound(qt, sig_bits), _pool_error_bound(kt, sig_bits)
+    pooled = eq @ kc.T + qc @ ek.T + eq @ ek.T
+    dot = gd * ((qc + eq) @ (kc + ek).T)
+    b = scale * (pooled + dot) + 4 * u * scale * (qc @ kc.T + pooled)
     return b.max(axis=1)
 
 
@@ -247,6 +268,12 @@ def combine(oc_rep, of, g_c=None, g_f=None):
 # --------------------------------------------------------------------------
 # Whole forward
 # --------------------------------------------------------------------------
+def _bf16_exact(x) -> bool:
+    """True when every value of x is a bf16 number (low 16 bits of fp32 zero)."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    return bool(np.all((a.view(np.uint32) & np.uint32(0xFFFF)) == 0))
+
+
 def _f64(x):
     return None if x is None else np.asarray(x, dtype=np.float64)
 
@@ -259,6 +286,7 @@ def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
     lists idx [B, h, Nc, L] / lens [B, h, Nc]. Returns a dict of float64
     results (raster layout unless the name says tiled / pooled).
     """
+    sig_bits = 24 if np.asarray(q).dtype == np.float32 and not _bf16_exact(q) else 8
     q, k, v, g_c, g_f = map(_f64, (q, k, v, g_c, g_f))
     B, nh, T, H, W, d = q.shape
     nc = T * H * W // TILE
@@ -285,7 +313,7 @@ def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
             s_c[b, h], _, oc[b, h], lse_c[b, h] = coarse_attention(qc[b, h], kc[b, h], vc[b, h], s)
             if topk > 0:
                 idx_o[b, h], margin[b, h] = topk_rows(s_c[b, h], topk)
-                tau[b, h] = logit_error_bound(qt[b, h], kt[b, h], s)
+                tau[b, h] = logit_error_bound(qt[b, h], kt[b, h], s, sig_bits)
             of_t[b, h], lse_t[b, h] = fine_gathered(qt[b, h], kt[b, h], vt[b, h],
                                                     idx_o[b, h], lens_o[b, h], s)
             if with_literal:

@@ -1,0 +1,160 @@
+"""C-ABI host tests (CPU only): the library loads, exports every symbol the
+header declares, and rejects every host-checkable fault before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_video_cube_amd as V
+from block_sparse_video_cube_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa.h")
+
+OK, NULL, SHAPE, HEAD_DIM, DTYPE, TOPK, ALIGN, WORKSPACE, INDEX, UNSUP, HIP, SCALE = range(12)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = N.lib()
+    names = header_functions()
+    assert len(names) >= 17
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in N.SIGNATURES, name
+    assert set(N.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version():
+    lib = N.lib()
+    for s in range(12):
+        assert lib.vsa_status_string(s)
+    assert lib.vsa_status_string(99) == b"unknown status"
+    assert lib.vsa_version() == 100
+    assert lib.vsa_max_cubes() >= 1320          # the 720p latent fits
+
+
+def _p(**kw):
+    base = dict(B=1, heads=2, T=8, H=8, W=8, head_dim=64, dtype="bf16", topk=2)
+    base.update(kw)
+    return V.Problem(**base)
+
+
+FAKE = ctypes.c_void_p(4096)          # aligned, never dereferenced (validation fails first)
+MIS = ctypes.c_void_p(4096 + 4)
+
+
+def _fwd(p, **ptrs):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g_c=None, g_f=None, idx=FAKE, len=FAKE, o=FAKE, saved=None,
+                ws=FAKE)
+    args.update(ptrs)
+    ws_bytes = ptrs.pop("ws_bytes", None)
+    if ws_bytes is None:
+        ws_bytes = V.workspace_bytes(p) if V.workspace_bytes(p) else 1 << 40
+    # Every call below must fail validation: a success would launch on fake pointers.
+    return N.lib().vsa_forward(ctypes.byref(p.c()), args["q"], args["k"], args["v"], args["g_c"], args["g_f"],
+                               args["idx"], args["len"], args["o"], args["saved"], args["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), SHAPE), (dict(heads=0), SHAPE), (dict(T=6), SHAPE), (dict(W=0), SHAPE), (dict(H=-4), SHAPE),
+    (dict(head_dim=96), HEAD_DIM), (dict(head_dim=32), HEAD_DIM), (dict(dtype="f16"), DTYPE),
+    (dict(topk=9), TOPK), (dict(topk=-1), TOPK), (dict(topk=0, list_stride=0), TOPK),
+    (dict(topk=0, list_stride=9), TOPK), (dict(topk=4, list_stride=3), TOPK),
+    (dict(scale=-1.0), SCALE), (dict(scale=float("nan")), SCALE), (dict(scale=float("inf")), SCALE),
+    (dict(T=4, H=4 * 64, W=4 * 33), UNSUP),       # Nc = 2112 > vsa_max_cubes()
+])
+def test_problem_validation(kw, code):
+    p = _p(**kw)
+    assert _fwd(p) == code
+    assert V.workspace_bytes(p) == 0 and V.saved_bytes(p) == 0
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "idx", "len", "o", "ws"])
+def test_null_pointers(name):
+    assert _fwd(_p(), **{name: None}) == NULL
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g_c", "g_f", "idx", "len", "o", "saved", "ws"])
+def test_misaligned_pointers(name):
+    assert _fwd(_p(), **{name: MIS}) == ALIGN
+
+
+def test_workspace_too_small():
+    p = _p()
+    assert _fwd(p, ws_bytes=V.workspace_bytes(p) - 1) == WORKSPACE
+
+
+def test_null_problem():
+    lib = N.lib()
+    assert lib.vsa_forward(None, *([FAKE] * 10), 0, None) == NULL
+    assert lib.vsa_workspace_bytes(None, 0) == 0
+
+
+def test_backward_fp32_unsupported_and_checks():
+    lib = N.lib()
+    p = _p(dtype="f32")
+    args = [FAKE] * 15 + [1 << 40, None]
+    assert lib.vsa_backward(ctypes.byref(p.c()), *args) == UNSUP
+    pb = _p()
+    args = [FAKE] * 7 + [None] + [FAKE] * 7 + [1 << 40, None]      # saved NULL
+    assert lib.vsa_backward(ctypes.byref(pb.c()), *args) == NULL
+    args = [FAKE] * 15 + [V.workspace_bytes(pb, True) - 1, None]
+    assert lib.vsa_backward(ctypes.byref(pb.c()), *args) == WORKSPACE
+
+
+def test_stage_entry_points_validate():
+    lib = N.lib()
+    p = _p()
+    c = ctypes.byref(p.c())
+    assert lib.vsa_pool(c, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == NULL
+    assert lib.vsa_pool(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
+    assert lib.vsa_coarse(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == NULL     # top-K needs idx
+    assert lib.vsa_fine_forward(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
+    assert lib.vsa_fine_forward(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == NULL
+    assert lib.vsa_combine(c, FAKE, MIS, None, None, FAKE, None) == ALIGN
+    assert lib.vsa_combine_backward(c, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, FAKE, 1,
+                                    None) == WORKSPACE
+    assert lib.vsa_index_transpose(c, FAKE, FAKE, None, FAKE, None) == NULL
+    assert lib.vsa_fine_backward(c, *([FAKE] * 17), 1, None) == WORKSPACE
+    assert lib.vsa_coarse_backward(c, *([FAKE] * 10), 1, None) == WORKSPACE
+    assert lib.vsa_validate_lists(c, FAKE, FAKE, None, None) == NULL
+    bad = ctypes.byref(_p(head_dim=80).c())
+    assert lib.vsa_pool(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == HEAD_DIM
+
+
+def test_workspace_and_saved_sizes_scale_with_problem():
+    small = _p()
+    big = _p(heads=4)
+    assert V.workspace_bytes(big) > V.workspace_bytes(small) > 0
+    assert V.saved_bytes(big) > V.saved_bytes(small) > 0
+    assert V.workspace_bytes(small, True) >= V.workspace_bytes(small)
+    p720 = V.Problem(1, 40, 24, 44, 80, 128, topk=32)
+    # V T-tiles (bf16 N*d per head) dominate the inference workspace
+    assert V.workspace_bytes(p720) >= 40 * 84480 * 128 * 2
+
+
+def test_check_lists_host():
+    p = V.Problem(1, 1, 8, 8, 8, 64, topk=0, list_stride=4)
+    idx = np.array([[0, 2, 5, -1]] * 8, np.int32).reshape(1, 1, 8, 4)
+    lens = np.full((1, 1, 8), 3, np.int32)
+    V.check_lists_host(p, idx, lens)
+    lens0 = lens.copy(); lens0[0, 0, 3] = 0
+    V.check_lists_host(p, idx, lens0)                     # empty row is valid
+    for mutate in ("dup", "unsorted", "range", "neg", "len"):
+        i2, l2 = idx.copy(), lens.copy()
+        if mutate == "dup": i2[0, 0, 1, 1] = 0
+        if mutate == "unsorted": i2[0, 0, 2, :3] = [5, 2, 0]
+        if mutate == "range": i2[0, 0, 7, 2] = 8
+        if mutate == "neg": i2[0, 0, 4, 0] = -1
+        if mutate == "len": l2[0, 0, 6] = 5
+        with pytest.raises(V.VsaError) as e:
+            V.check_lists_host(p, i2, l2)
+        assert e.value.status == INDEX

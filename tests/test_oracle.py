@@ -372,3 +372,27 @@ def test_page_facts_on_work_accounting():
     coarse = O.coarse_flops(1, 1, nc, d)
     assert coarse / dense < facts["coarse_share_of_attention"]["max_fraction"]
     assert coarse / (coarse + fine) < facts["coarse_share_of_total"]["max_fraction"]
+
+
+def test_pool_error_bound_exactness_claim():
+    """Where the bound claims an fp32 mean-pool is exact, fp32 sums in several
+    orders (forward, reverse, pairwise, shuffled) all equal the exact sum;
+    elsewhere the error stays inside the bound."""
+    w = WL.make_inputs("C3", heads=[2], gates=False)
+    xt = O.tile(w["q"][0, 0].astype(np.float64))[:40]
+    bound = O._pool_error_bound(xt, 8)
+    exact = xt.sum(axis=1) / 64
+    x32 = xt.astype(np.float32)
+    rng = np.random.default_rng(0)
+    orders = [np.arange(64), np.arange(64)[::-1], rng.permutation(64), rng.permutation(64)]
+    for order in orders:
+        acc = np.zeros(x32.shape[::2], np.float32)
+        for l in order:
+            acc = (acc + x32[:, l, :]).astype(np.float32)
+        got = acc.astype(np.float64) / 64
+        assert np.all(np.abs(got - exact) <= bound)
+    pair = x32.copy()
+    while pair.shape[1] > 1:
+        pair = (pair[:, 0::2, :] + pair[:, 1::2, :]).astype(np.float32)
+    assert np.all(np.abs(pair[:, 0, :].astype(np.float64) / 64 - exact) <= bound)
+    assert (bound == 0).mean() > 0.9

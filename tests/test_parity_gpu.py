@@ -1,0 +1,438 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Bars (from the operator's contract):
+  * index lists: bit-exact on every row whose top-K margin exceeds twice the
+    fp32 logit error bound; other (near-tie) rows must hold a valid top-K set;
+  * fp32 problems: max |gpu - oracle| <= 1e-4;
+  * bf16 problems: max |gpu - oracle| / max |oracle| <= 2e-2 per tensor;
+  * fp32 intermediates of bf16 problems (pooled means, coarse output): 1e-4
+    relative (the inputs are exact, only fp32 rounding differs).
+Outputs are compared with the oracle re-run on the GPU's own lists, so a
+legitimate near-tie choice cannot fail an output comparison.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_video_cube_amd as V
+import workloads as WL
+from oracle import vsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+BF16_REL = 2e-2
+F32_ABS = 1e-4
+# Sanity bound on the share of rows whose top-K margin is within the fp32
+# error bound (about 0.6% / 1.4% / 2.3% on the 16x32x32 / 480p / 720p inputs).
+NEAR_FRAC = 0.05
+
+
+def dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(dtype).contiguous()
+
+
+def host(t):
+    return t.detach().float().cpu().numpy() if t.dtype != torch.int32 else t.cpu().numpy()
+
+
+def rel_err(got, ref):
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def assert_close(got, ref, dtype, name, rel=BF16_REL, abs_=F32_ABS):
+    if dtype == "f32":
+        err = float(np.abs(got - ref).max())
+        assert err <= abs_, f"{name}: max abs err {err:.3e} > {abs_}"
+    else:
+        err = rel_err(got, ref)
+        assert err <= rel, f"{name}: rel err {err:.3e} > {rel}"
+
+
+def problem_of(w, **kw):
+    d = dict(B=w.B, heads=w.heads, T=w.T, H=w.H, W=w.W, head_dim=w.head_dim, dtype=w.dtype, topk=w.topk,
+             list_stride=w.list_stride)
+    d.update(kw)
+    return V.Problem(**d)
+
+
+def inputs_to_dev(x, dtype):
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = {k: dev(x[k], td) for k in ("q", "k", "v", "g_c", "g_f", "d_o") if k in x}
+    for k in ("idx", "len"):
+        if k in x:
+            out[k] = dev(x[k], torch.int32)
+    return out
+
+
+def check_topk(gpu_idx, ref, k):
+    """Index parity protocol. Returns the number of near-tie rows."""
+    s, tau, margin, ridx = ref["s_c"], ref["tau"], ref["margin"], ref["idx"]
+    strict = margin > 2 * tau
+    same = (gpu_idx == ridx).all(axis=-1)
+    bad = np.argwhere(strict & ~same)
+    assert bad.size == 0, f"{len(bad)} rows with a clear top-K margin differ, e.g. {bad[:3].tolist()}"
+    assert np.all(np.diff(gpu_idx, axis=-1) > 0)
+    near = np.argwhere(~strict)
+    for b, h, i in near:
+        row = s[b, h, i]
+        kth = np.sort(row)[::-1][k - 1]
+        assert np.all(row[gpu_idx[b, h, i]] >= kth - 2 * tau[b, h, i])
+    return len(near)
+
+
+# ------------------------------------------------------------------ stages
+@pytest.mark.parametrize("name", ["C1", "C2", "C3"])
+def test_pool_parity(name):
+    w = WL.get(name)
+    x = WL.make_inputs(name, heads=[0, w.heads - 1], gates=False)
+    p = problem_of(w, heads=2)
+    d = inputs_to_dev(x, w.dtype)
+    qc, kc, vc = V.pool(p, d["q"], d["k"], d["v"])
+    torch.cuda.synchronize()
+    for got, src in ((qc, "q"), (kc, "k"), (vc, "v")):
+        ref = O.pool(O.tile(x[src].astype(np.float64)))
+        err = rel_err(host(got), ref)
+        assert err <= 1e-5, (src, err)
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3"])
+def test_coarse_parity_and_topk_protocol(name):
+    w = WL.get(name)
+    heads = list(range(w.heads)) if w.heads <= 12 else [0, 5, 11]
+    heads = heads[:4]
+    x = WL.make_inputs(name, heads=heads, gates=False)
+    p = problem_of(w, heads=len(heads))
+    d = inputs_to_dev(x, w.dtype)
+    qc, kc, vc = V.pool(p, d["q"], d["k"], d["v"])
+    oc, lse, idx, lens = V.coarse(p, qc, kc, vc)
+    torch.cuda.synchronize()
+    ref = O.forward(x["q"], x["k"], x["v"], topk=w.topk)
+    near = check_topk(host(idx), ref, w.topk)
+    assert near <= NEAR_FRAC * idx.shape[0] * idx.shape[1] * idx.shape[2] + 2
+    assert np.all(host(lens) == w.topk)
+    assert rel_err(host(oc), ref["o_c"]) <= 1e-4
+    assert float(np.abs(host(lse) - ref["lse_c"]).max()) <= 1e-4 * max(1.0, np.abs(ref["lse_c"]).max())
+
+
+@pytest.mark.parametrize("name,heads", [("C1", 2), ("C2", 2), ("C3", 2)])
+def test_fine_forward_parity_ragged_lists(name, heads):
+    """Explicit ragged lists: lengths 0..Nc, including empty and full rows."""
+    w = WL.get(name)
+    x = WL.make_inputs(name, heads=list(range(heads)), gates=False)
+    nc = w.Nc
+    stride = nc
+    idx, lens = WL.random_lists(nc, heads * nc, 0, nc, seed=7, stride=stride)
+    lens[0], lens[1] = 0, nc
+    idx[1, :nc] = np.arange(nc)
+    idx = idx.reshape(1, heads, nc, stride)
+    lens = lens.reshape(1, heads, nc)
+    p = problem_of(w, heads=heads, topk=0, list_stride=stride)
+    d = inputs_to_dev(x, w.dtype)
+    ws = V.workspace(p, d["q"])
+    V.pool(p, d["q"], d["k"], d["v"], ws=ws)
+    of, lse = V.fine_forward(p, d["q"], d["k"], d["v"], dev(idx, torch.int32), dev(lens, torch.int32), ws=ws)
+    torch.cuda.synchronize()
+    ref = O.forward(x["q"], x["k"], x["v"], topk=0, idx=idx, lens=lens)
+    assert_close(host(of), ref["o_f"], w.dtype, "o_f")
+    got_lse = host(lse)
+    live = np.isfinite(ref["lse_f"])
+    assert np.array_equal(np.isfinite(got_lse), live)
+    assert float(np.abs(got_lse[live] - ref["lse_f"][live]).max()) <= 2e-3
+    assert np.all(host(of)[~live] == 0)
+
+
+@pytest.mark.parametrize("name", ["C1", "C2"])
+def test_combine_parity(name):
+    w = WL.get(name)
+    x = WL.make_inputs(name, heads=[0, 1])
+    p = problem_of(w, heads=2)
+    rng = np.random.default_rng(3)
+    oc = rng.standard_normal((1, 2, w.Nc, w.head_dim)).astype(np.float32)
+    of = x["v"]                                  # any dtype-exact tensor
+    d = inputs_to_dev(x, w.dtype)
+    td = p.torch_dtype
+    for gc, gf in ((d["g_c"], d["g_f"]), (None, d["g_f"]), (d["g_c"], None), (None, None)):
+        o = V.combine(p, dev(oc, torch.float32), dev(of, td), gc, gf)
+        torch.cuda.synchronize()
+        ref = O.combine(O.repeat_coarse(oc.astype(np.float64), w.T, w.H, w.W), of.astype(np.float64),
+                        None if gc is None else x["g_c"].astype(np.float64),
+                        None if gf is None else x["g_f"].astype(np.float64))
+        assert_close(host(o), ref, w.dtype, "o", rel=2 ** -7, abs_=1e-5)
+
+
+# ------------------------------------------------------------------ end to end
+def run_forward_and_compare(name, heads=None, training=False, gates=True):
+    w = WL.get(name)
+    hs = list(range(w.heads)) if heads is None else heads
+    x = WL.make_inputs(name, heads=hs)
+    p = problem_of(w, heads=len(hs))
+    d = inputs_to_dev(x, w.dtype)
+    gc, gf = (d["g_c"], d["g_f"]) if gates else (None, None)
+    if w.topk > 0:
+        o, idx, lens, saved = V.forward(p, d["q"], d["k"], d["v"], gc, gf, training=training)
+    else:
+        o, idx, lens, saved = V.forward(p, d["q"], d["k"], d["v"], gc, gf, idx=d["idx"], lens=d["len"],
+                                        training=training)
+    torch.cuda.synchronize()
+    gi, gl = host(idx), host(lens)
+    xg = (x["g_c"], x["g_f"]) if gates else (None, None)
+    if w.topk > 0:
+        ref_sel = O.forward(x["q"], x["k"], x["v"], topk=w.topk)
+        near = check_topk(gi, ref_sel, w.topk)
+    else:
+        near = 0
+    ref = O.forward(x["q"], x["k"], x["v"], *xg, topk=0, idx=gi, lens=gl)
+    assert_close(host(o), ref["o"], w.dtype, f"{name} o")
+    return near, (x, d, p, idx, lens, saved, ref)
+
+
+@pytest.mark.parametrize("name", ["C1", "C2"])
+@pytest.mark.parametrize("training", [False, True])
+def test_forward_end_to_end(name, training):
+    run_forward_and_compare(name, training=training)
+
+
+def test_forward_480p_heads_subset():
+    near, _ = run_forward_and_compare("C3", heads=[0, 6, 11])
+    assert near <= NEAR_FRAC * 3 * WL.get("C3").Nc + 2
+
+
+def test_forward_ungated():
+    run_forward_and_compare("C2", heads=[3], gates=False)
+
+
+def test_forward_saved_tensors():
+    _, (x, d, p, idx, lens, saved, ref) = run_forward_and_compare("C2", heads=[1, 2], training=True)
+    # the saved O_f / LSE_f equal the fine stage of the oracle on the same lists
+    w = WL.get("C2")
+    nbh, nc, D, N = 2, w.Nc, w.head_dim, w.N
+    raw = saved
+    off = 0
+
+    def take(n, dtype, esize):
+        nonlocal off
+        t = raw[off:off + n * esize].view(dtype)
+        off += (n * esize + 255) // 256 * 256
+        return t
+
+    for _ in range(4):
+        take(nbh * nc * D, torch.float32, 4)
+    take(nbh * nc, torch.float32, 4)
+    lse_f = take(nbh * N, torch.float32, 4).reshape(1, 2, w.T, w.H, w.W)
+    of = take(nbh * N * D, torch.bfloat16, 2).reshape(1, 2, w.T, w.H, w.W, D)
+    assert_close(host(of), ref["o_f"], "bf16", "saved o_f")
+    assert float(np.abs(host(lse_f) - ref["lse_f"]).max()) <= 2e-3
+
+
+@pytest.mark.timeout(900)
+def test_forward_720p_sampled():
+    """The benchmark configuration at full size (all 40 heads on the GPU, the
+    launch bench.py times); the oracle checks 3 heads: selection for every
+    query cube, outputs for 48 sampled query cubes per head."""
+    w = WL.get("C4")
+    print("[720p] generating inputs", flush=True)
+    x = WL.make_inputs("C4")
+    print("[720p] running the HIP forward", flush=True)
+    p = problem_of(w)
+    d = inputs_to_dev(x, w.dtype)
+    o, idx, lens, _ = V.forward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    heads = [0, 21, 39]
+    gi = host(idx)[:, heads]
+    sub = {k: x[k][:, heads] for k in ("q", "k", "v", "g_c", "g_f")}
+    qt, kt, vt = (O.tile(sub[k].astype(np.float64)) for k in ("q", "k", "v"))
+    rng = np.random.default_rng(0)
+    got_o = host(o[:, heads])
+    near = 0
+    for hi in range(len(heads)):
+        print(f"[720p] oracle head {heads[hi]}", flush=True)
+        qc, kc, vc = O.pool(qt[0, hi]), O.pool(kt[0, hi]), O.pool(vt[0, hi])
+        s = 1 / np.sqrt(w.head_dim)
+        S, _, oc, _ = O.coarse_attention(qc, kc, vc, s)
+        ridx, margin = O.topk_rows(S, w.topk)
+        tau = O.logit_error_bound(qt[0, hi], kt[0, hi], s, sig_bits=8)
+        ref = {"s_c": S[None, None], "tau": tau[None, None], "margin": margin[None, None], "idx": ridx[None, None]}
+        near += check_topk(gi[:, hi:hi + 1], ref, w.topk)
+        rows = np.sort(rng.choice(w.Nc, 48, replace=False))
+        of_rows, _ = O.fine_gathered(qt[0, hi][rows], kt[0, hi], vt[0, hi], gi[0, hi][rows],
+                                     np.full(48, w.topk), s)
+        gct = O.tile(sub["g_c"][0, hi].astype(np.float64))[rows]
+        gft = O.tile(sub["g_f"][0, hi].astype(np.float64))[rows]
+        ref_o = oc[rows][:, None, :] * gct + of_rows * gft
+        got = O.tile(got_o[0, hi])[rows]
+        err = rel_err(got, ref_o)
+        assert err <= BF16_REL, (heads[hi], err)
+    print(f"[720p] near-tie rows {near} of {3 * w.Nc}", flush=True)
+    assert near <= NEAR_FRAC * 3 * w.Nc + 2
+
+
+# ------------------------------------------------------------------ edge cases
+def test_all_cubes_selected_is_full_attention():
+    """K = Nc with G_c = 0 and no fine gate reproduces full attention."""
+    x = WL.make_inputs_custom(1, 2, 64, 8, 8, 16, dtype="bf16", seed=4)
+    p = V.Problem(1, 2, 8, 8, 16, 64, topk=16)
+    d = inputs_to_dev(x, "bf16")
+    zero = torch.zeros_like(d["q"])
+    o, idx, lens, _ = V.forward(p, d["q"], d["k"], d["v"], zero, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), np.tile(np.arange(16), (1, 2, 16, 1)))
+    for h in range(2):
+        qf, kf, vf = (torch.from_numpy(x[k][0, h].astype(np.float64)).reshape(1, -1, 64) for k in ("q", "k", "v"))
+        ref = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf)[0].numpy()
+        assert rel_err(host(o)[0, h].reshape(-1, 64), ref) <= BF16_REL
+
+
+@pytest.mark.parametrize("dtype,d,k,stride", [("bf16", 64, 1, 3), ("bf16", 128, 5, 5), ("f32", 128, 3, 4),
+                                              ("f32", 64, 8, 8)])
+def test_shapes_and_k_range(dtype, d, k, stride):
+    x = WL.make_inputs_custom(1, 3, d, 4, 8, 16, dtype=dtype, seed=9, scale=0.5)
+    p = V.Problem(1, 3, 4, 8, 16, d, dtype=dtype, topk=k, list_stride=stride)
+    dd = inputs_to_dev(x, dtype)
+    o, idx, lens, _ = V.forward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"])
+    torch.cuda.synchronize()
+    gi = host(idx)
+    if stride > k:
+        assert np.all(gi[..., k:] == -1)
+    gi = gi[..., :k]
+    ref_sel = O.forward(x["q"], x["k"], x["v"], topk=k)
+    check_topk(gi, ref_sel, k)
+    ref = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=host(lens))
+    assert_close(host(o), ref["o"], dtype, "o")
+
+
+def test_scale_override():
+    x = WL.make_inputs_custom(1, 1, 64, 8, 8, 8, dtype="bf16", seed=2)
+    p = V.Problem(1, 1, 8, 8, 8, 64, topk=3, scale=0.37)
+    d = inputs_to_dev(x, "bf16")
+    o, idx, lens, _ = V.forward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"])
+    torch.cuda.synchronize()
+    ref_sel = O.forward(x["q"], x["k"], x["v"], topk=3, scale=0.37)
+    check_topk(host(idx), ref_sel, 3)
+    ref = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=host(idx), lens=host(lens), scale=0.37)
+    assert_close(host(o), ref["o"], "bf16", "o")
+
+
+def test_repeat_calls_bitwise_identical():
+    x = WL.make_inputs("C2", heads=[0, 1])
+    p = problem_of(WL.get("C2"), heads=2)
+    d = inputs_to_dev(x, "bf16")
+    o1, i1, _, _ = V.forward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"])
+    o2, i2, _, _ = V.forward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(i1, i2)
+
+
+def test_validate_lists_device():
+    p = V.Problem(1, 1, 8, 8, 8, 64, topk=0, list_stride=4)
+    idx = np.array([[0, 2, 5, -1]] * 8, np.int32).reshape(1, 1, 8, 4)
+    lens = np.full((1, 1, 8), 3, np.int32)
+    V.validate_lists(p, dev(idx, torch.int32), dev(lens, torch.int32))
+    bad = idx.copy()
+    bad[0, 0, 5, 1] = 9
+    with pytest.raises(V.VsaError) as e:
+        V.validate_lists(p, dev(bad, torch.int32), dev(lens, torch.int32))
+    assert e.value.status == 8
+    badl = lens.copy()
+    badl[0, 0, 2] = 7
+    with pytest.raises(V.VsaError):
+        V.validate_lists(p, dev(idx, torch.int32), dev(badl, torch.int32))
+
+
+# ------------------------------------------------------------------ backward
+def backward_compare(x, p, dtype, rel=BF16_REL, gates=True):
+    d = inputs_to_dev(x, dtype)
+    gc, gf = (d["g_c"], d["g_f"]) if gates else (None, None)
+    o, idx, lens, saved = V.forward(p, d["q"], d["k"], d["v"], gc, gf, idx=d["idx"], lens=d["len"], training=True)
+    g = V.backward(p, d["q"], d["k"], d["v"], gc, gf, idx, lens, saved, d["d_o"])
+    torch.cuda.synchronize()
+    xg = (x["g_c"], x["g_f"]) if gates else (None, None)
+    fwd = O.forward(x["q"], x["k"], x["v"], *xg, topk=0, idx=x["idx"], lens=x["len"])
+    assert_close(host(o), fwd["o"], dtype, "o")
+    ref = O.backward(x["q"], x["k"], x["v"], *xg, x["d_o"], fwd)
+    names = ("dq", "dk", "dv", "dg_c", "dg_f") if gates else ("dq", "dk", "dv")
+    for nm in names:
+        assert_close(host(g[nm]), ref[nm], dtype, nm, rel=rel)
+    if not gates:
+        assert g["dg_c"] is None and g["dg_f"] is None
+
+
+def _small_train_inputs(d=64, seed=5, heads=2, T=8, H=16, W=16):
+    x = WL.make_inputs_custom(1, heads, d, T, H, W, dtype="bf16", seed=seed)
+    nc = T * H * W // 64
+    idx, lens = WL.random_lists(nc, heads * nc, 0, nc, seed=seed)
+    lens[0], lens[1] = 0, nc
+    idx[1, :nc] = np.arange(nc)
+    x["idx"] = idx.reshape(1, heads, nc, nc)
+    x["len"] = lens.reshape(1, heads, nc)
+    p = V.Problem(1, heads, T, H, W, d, topk=0, list_stride=nc)
+    return x, p
+
+
+def test_backward_small_ragged_full_compare():
+    x, p = _small_train_inputs()
+    backward_compare(x, p, "bf16")
+
+
+def test_backward_small_ungated():
+    x, p = _small_train_inputs(seed=6)
+    backward_compare(x, p, "bf16", gates=False)
+
+
+def test_backward_head_dim_128():
+    x, p = _small_train_inputs(d=128, seed=8, heads=1, T=8, H=8, W=16)
+    backward_compare(x, p, "bf16")
+
+
+def test_backward_training_config_sampled():
+    """The training workload at full size on the GPU (B=2, 12 heads, lists of
+    length U{8..64}); the oracle checks two (b, h) slices completely."""
+    w = WL.get("C5")
+    x = WL.make_inputs("C5")
+    p = problem_of(w)
+    d = inputs_to_dev(x, "bf16")
+    o, idx, lens, saved = V.forward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"], idx=d["idx"], lens=d["len"],
+                                    training=True)
+    g = V.backward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"], idx, lens, saved, d["d_o"])
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 7)):
+        sl = {k: x[k][b:b + 1, h:h + 1] for k in ("q", "k", "v", "g_c", "g_f", "d_o", "idx", "len")}
+        fwd = O.forward(sl["q"], sl["k"], sl["v"], sl["g_c"], sl["g_f"], topk=0, idx=sl["idx"], lens=sl["len"])
+        assert_close(host(o[b:b + 1, h:h + 1]), fwd["o"], "bf16", "o")
+        ref = O.backward(sl["q"], sl["k"], sl["v"], sl["g_c"], sl["g_f"], sl["d_o"], fwd)
+        for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
+            assert_close(host(g[nm][b:b + 1, h:h + 1]), ref[nm], "bf16", f"{nm}[{b},{h}]")
+
+
+def test_backward_stages():
+    x, p = _small_train_inputs(seed=12)
+    d = inputs_to_dev(x, "bf16")
+    fwd = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=x["idx"], lens=x["len"])
+    ref = O.backward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], x["d_o"], fwd)
+    # index transpose: bit-exact against the oracle's transposed lists
+    off, k2q = V.index_transpose(p, d["idx"], d["len"])
+    torch.cuda.synchronize()
+    off, k2q = host(off), host(k2q)
+    for h in range(2):
+        rk, rl = O.transpose_lists(x["idx"][0, h], x["len"][0, h], p.Nc)
+        assert np.array_equal(np.diff(off[0, h]), rl)
+        for j in range(p.Nc):
+            assert np.array_equal(k2q[0, h, off[0, h, j]:off[0, h, j + 1]], rk[j, :rl[j]])
+    # combine backward on the oracle's O_c / O_f (rounded to the GPU dtypes)
+    ws = V.workspace(p, d["q"], training=True)
+    oc32 = dev(fwd["o_c"].astype(np.float32), torch.float32)
+    of16 = dev(fwd["o_f"].astype(np.float32), torch.bfloat16)
+    cb = V.combine_backward(p, d["d_o"], oc32, of16, d["g_c"], d["g_f"], ws=ws)
+    torch.cuda.synchronize()
+    assert_close(host(cb["dg_c"]), ref["dg_c"], "bf16", "dg_c", rel=2 ** -7)
+    assert_close(host(cb["d_o_f"]), ref["d_o_f"], "bf16", "d_o_f", rel=2 ** -7)
+    assert rel_err(host(cb["d_o_c"]), ref["d_o_c"]) <= 1e-2
+    assert rel_err(host(cb["delta"]), ref["delta"]) <= 1e-2
+    # coarse backward on exact pooled inputs
+    f32 = lambda a: dev(a.astype(np.float32), torch.float32)
+    dqc, dkc, dvc = V.coarse_backward(p, f32(fwd["q_c"]), f32(fwd["k_c"]), f32(fwd["v_c"]), f32(fwd["o_c"]),
+                                      f32(fwd["lse_c"]), f32(ref["d_o_c"]), ws)
+    torch.cuda.synchronize()
+    for got, nm in ((dqc, "dq_c"), (dkc, "dk_c"), (dvc, "dv_c")):
+        assert rel_err(host(got), ref[nm]) <= 1e-4, nm
