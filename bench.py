@@ -87,7 +87,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bf16_720p_24x44x80")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1, help="heads of the oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the oracle sample")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -137,7 +137,7 @@ def main() -> int:
         V.pool(p, q, k, v, ws=ws, out=pooled[:3])
         ev[1].record()
         V.coarse(p, *pooled[:3], out=(pooled[3], lse_c, idx if w.topk > 0 else None,
-                                      lens if w.topk > 0 else None))
+                                      lens if w.topk > 0 else None), ws=ws)
         ev[2].record()
         V.fine_combine(p, q, k, v, idx, lens, pooled[3], gc, gf, ws=ws, out=o)
         ev[3].record()

@@ -138,8 +138,9 @@ def pool(p: Problem, q, k, v, ws: Optional[torch.Tensor] = None, out=None):
     return qc, kc, vc
 
 
-def coarse(p: Problem, q_c, k_c, v_c, out=None):
+def coarse(p: Problem, q_c, k_c, v_c, out=None, ws: Optional[torch.Tensor] = None):
     """Coarse stage; out = (o_c, lse_c, idx, lens) reuses caller buffers."""
+    ws = workspace(p, q_c) if ws is None else ws
     if out is not None:
         oc, lse, idx, lens = out
     else:
@@ -150,7 +151,7 @@ def coarse(p: Problem, q_c, k_c, v_c, out=None):
             idx = _empty((p.B, p.heads, p.Nc, p.stride), torch.int32, q_c)
             lens = _empty((p.B, p.heads, p.Nc), torch.int32, q_c)
     check(lib().vsa_coarse(ctypes.byref(p.c()), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(oc), _ptr(lse), _ptr(idx),
-                           _ptr(lens), _stream(q_c.device)), "vsa_coarse")
+                           _ptr(lens), _ptr(ws), ws.numel(), _stream(q_c.device)), "vsa_coarse")
     return oc, lse, idx, lens
 
 

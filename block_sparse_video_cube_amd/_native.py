@@ -41,7 +41,7 @@ SIGNATURES = {
     "vsa_forward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_backward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_pool": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
-    "vsa_coarse": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v]),
+    "vsa_coarse": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_fine_forward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_fine_combine": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_combine": (_i32, [_P, _v, _v, _v, _v, _v, _v]),

@@ -8,7 +8,8 @@
 // key designs 2-3. Variable-length lists per query cube: VSA2 abstract.
 //
 // bf16 kernel: one wave owns one query cube (64 query rows) and walks its
-// list of key cubes with an online softmax, all in registers:
+// list of key cubes (in 32-key halves) with an online softmax, all in
+// registers:
 //   S^T = K_j Q_i^T   16x16x32 bf16 MFMAs, A = K rows, B = Q rows (both read
 //                     straight from the raster tensors, 16-byte loads);
 //   the accumulator layout gives every lane one query column and 4+4+4+4 key
@@ -22,8 +23,11 @@
 
 namespace vsa {
 
+// Occupancy: D = 64 fits 2 waves per SIMD (<= 256 registers), D = 128 one.
+template <int D> struct FineOcc { static constexpr int kWaves = D == 64 ? 2 : 1; };
+
 template <int D, bool FUSED>
-__global__ __launch_bounds__(64) void fine_fwd_bf16_kernel(
+__global__ __launch_bounds__(64, FineOcc<D>::kWaves) void fine_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ vt,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, bf16* __restrict__ o_f,
     float* __restrict__ lse_f, const float* __restrict__ oc, const bf16* __restrict__ gc,
@@ -54,90 +58,144 @@ __global__ __launch_bounds__(64) void fine_fwd_bf16_kernel(
     for (int ks = 0; ks < KS; ++ks)
       qf[qb][ks] = *reinterpret_cast<const bf16x8*>(Q + (long)qrow[qb] * D + ks * 32 + grp * 8);
 
-  f32x4 acc[DB][4];
+  f32x4 acc[DB][4], lacc[4];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < 4; ++qb) {
+    lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4], l[4];
+    for (int db = 0; db < DB; ++db) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Reference max per query (log2 units), common to the 4 lanes of a query.
+  float m[4];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
+  for (int qb = 0; qb < 4; ++qb) m[qb] = -INFINITY;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
 
-  bf16x8 kf[4][KS];
-  auto load_k = [&](int j) {
+  // The list is walked in 32-key chunks, two per key cube: chunk h of cube j
+  // holds the key rows t' = 2h, 2h+1 (tokens 32h .. 32h+31), which is exactly
+  // k-step h of the cube's V T-tile. Online softmax over any chunking is the
+  // same softmax.
+  auto cube_at = [&](int t) { const int j = list[t]; return (j >= 0 && j < g.Nc) ? j : 0; };
+  bf16x8 kf[2][KS];
+  auto load_k = [&](int j, int h) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const long r = cube_row(g, j, kb, c16 >> 2) + (c16 & 3);
+    for (int kk = 0; kk < 2; ++kk) {
+      const long r = cube_row(g, j, 2 * h + kk, c16 >> 2) + (c16 & 3);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kf[kb][ks] = *reinterpret_cast<const bf16x8*>(K + r * D + ks * 32 + grp * 8);
+        kf[kk][ks] = *reinterpret_cast<const bf16x8*>(K + r * D + ks * 32 + grp * 8);
     }
   };
-  auto cube_at = [&](int t) { const int j = list[t]; return (j >= 0 && j < g.Nc) ? j : 0; };
-  if (L > 0) load_k(cube_at(0));
+  const int nchunks = 2 * L;
 
-  for (int t = 0; t < L; ++t) {
-    const int j = cube_at(t);
-    // S^T[kb][qb]: lane holds keys kb*16 + 4*grp + r (r = 0..3) of query qb*16 + c16.
-    f32x4 s[4][4];
+  auto scores = [&](f32x4 (&sx)[2][4]) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a = mfma16_bf16(kf[kb][ks], qf[qb][ks], a);
-        s[kb][qb] = a;
+        for (int ks = 0; ks < KS; ++ks) a = mfma16_bf16(kf[kk][ks], qf[qb][ks], a);
+        sx[kk][qb] = a;
       }
-    if (t + 1 < L) load_k(cube_at(t + 1));
-    bf16x8 vf[DB][2];
-    const bf16* vtile = vt + ((long)bh * g.Nc + j) * D * kTile;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int sx = 0; sx < 2; ++sx)
-        vf[db][sx] = *reinterpret_cast<const bf16x8*>(vtile + (db * 16 + c16) * kTile + sx * 32 + grp * 8);
+  };
 
-    bf16x8 pf[4][2];
+  // Online softmax against a lazily moved reference max m (log2 units): P =
+  // 2^(s*c - m) is formed as long as no exponent exceeds 16 (P < 2^16, so
+  // bf16 P and the fp32 sums keep their relative precision). A chunk that
+  // would exceed it leaves the hot loop; the reference then moves up to the
+  // chunk's row max, O and l are rescaled, and the chunk is redone. O and l
+  // always share m, so the result is exact whatever the schedule. The row
+  // sum l comes from an MFMA against a ones operand, so the hot loop touches
+  // the accumulators only through MFMAs. The first chunk's row max sets the
+  // initial reference.
+  constexpr float kHeadroom = 16.0f;
+  if (nchunks > 0) {
+    load_k(cube_at(0), 0);
+    f32x4 sx[2][4];
+    scores(sx);
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      float mx = s[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      float mx = fmaxf(fmaxf(fmaxf(sx[0][qb][0], sx[0][qb][1]), fmaxf(sx[0][qb][2], sx[0][qb][3])),
+                       fmaxf(fmaxf(sx[1][qb][0], sx[1][qb][1]), fmaxf(sx[1][qb][2], sx[1][qb][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m[qb], mx * scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
-      m[qb] = mnew;
-      float ls = 0.f;
+      m[qb] = mx * scale_log2;
+    }
+  }
+  int c = 0;
+  for (;;) {
+    bool retry = false;
+    float cmax[4];
+    if (c < nchunks) load_k(cube_at(c >> 1), c & 1);
+    for (; c < nchunks; ++c) {
+      const int h = c & 1;
+      const int j = cube_at(c >> 1);
+      bf16x8 vf[DB];
+      const bf16* vtile = vt + ((long)bh * g.Nc + j) * D * kTile;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int db = 0; db < DB; ++db)
+        vf[db] = *reinterpret_cast<const bf16x8*>(vtile + (db * 16 + c16) * kTile + h * 32 + grp * 8);
+      // S^T[kk][qb]: lane holds keys 32h + 16kk + 4*grp + r of query qb*16 + c16.
+      f32x4 sx[2][4];
+      scores(sx);
+      // exponent arguments x = s*c - m, and the largest of them per query
+      float xmax = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[kb][qb][r] * scale_log2 - mnew);
-          ls += p;
-          pf[qb][kb >> 1][(kb & 1) * 4 + r] = (bf16)p;
-        }
-      l[qb] = l[qb] * alpha + ls;
+      for (int qb = 0; qb < 4; ++qb) {
+        float mq = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sx[kk][qb][r] = sx[kk][qb][r] * scale_log2 - m[qb];
+            mq = fmaxf(mq, sx[kk][qb][r]);
+          }
+        cmax[qb] = mq;
+        xmax = fmaxf(xmax, mq);
+      }
+      if (__any(xmax > kHeadroom)) { retry = true; break; }
+      if (c + 1 < nchunks) load_k(cube_at((c + 1) >> 1), h ^ 1);
+      bf16x8 pf[4];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pf[qb][kk * 4 + r] = (bf16)__builtin_amdgcn_exp2f(sx[kk][qb][r]);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        lacc[qb] = mfma16_bf16(ones, pf[qb], lacc[qb]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db][qb] = mfma16_bf16(vf[db], pf[qb], acc[db][qb]);
+      }
+    }
+    if (!retry) break;
+    // Rare path: move each query's reference up to its row max over this
+    // chunk (the 4 lanes of a query agree through two exchanges); rescale.
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      float mx = cmax[qb];
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float shift = fmaxf(mx, 0.0f);
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      m[qb] += shift;
+      lacc[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int sx = 0; sx < 2; ++sx)
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) acc[db][qb] = mfma16_bf16(vf[db][sx], pf[qb][sx], acc[db][qb]);
   }
+  float l[4];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) l[qb] = lacc[qb][0];
 
   // Epilogue: lane holds O^T[channel db*16 + 4*grp + r][query qb*16 + c16].
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
-    float lt = l[qb];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = l[qb];
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const long n = tok0 + qrow[qb];
     if (lse_f != nullptr && grp == 0)

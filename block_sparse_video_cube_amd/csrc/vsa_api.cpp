@@ -101,16 +101,18 @@ Saved carve_saved(const Dims& d, void* base) {
   return s;
 }
 
-// Forward workspace: V T-tiles (bf16) and, for inference, the pooled tensors.
+// Forward workspace: V T-tiles (bf16), the coarse logits and, for
+// inference, the pooled tensors.
 struct FwdWs {
   bf16* vt;
-  float *qc, *kc, *vc, *oc, *lse_c;
+  float *s, *qc, *kc, *vc, *oc, *lse_c;
   size_t bytes;
 };
 FwdWs carve_fwd_ws(const Dims& d, void* base) {
   Carver c(base);
   FwdWs w;
   w.vt = d.elem == 2 ? c.take<bf16>(d.BH * d.N * d.D) : nullptr;
+  w.s = c.take<float>(d.BH * d.Nc * d.Nc);
   const size_t pooled = d.BH * d.Nc * d.D;
   w.qc = c.take<float>(pooled);
   w.kc = c.take<float>(pooled);
@@ -213,7 +215,8 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
     qc = s.qc; kc = s.kc; vc = s.vc; oc = s.oc; lse_c = s.lse_c; lse_f = s.lse_f; of = s.of;
   }
   hipError_t e = launch_pool(L, q, k, v, qc, kc, vc, ws.vt);
-  if (e == hipSuccess) e = launch_coarse(L, qc, kc, vc, oc, lse_c, L.topk > 0 ? idx : nullptr, L.topk > 0 ? len : nullptr);
+  if (e == hipSuccess)
+    e = launch_coarse(L, qc, kc, vc, oc, lse_c, L.topk > 0 ? idx : nullptr, L.topk > 0 ? len : nullptr, ws.s);
   if (e == hipSuccess) e = launch_fine_fwd(L, q, k, v, ws.vt, idx, len, of, lse_f, oc, g_c, g_f, o);
   return hip_status(e);
 }
@@ -268,16 +271,19 @@ vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const vo
 }
 
 vsa_status vsa_coarse(const vsa_problem* p, const float* q_c, const float* k_c, const float* v_c, float* o_c,
-                      float* lse_c, int32_t* idx, int32_t* len, void* stream) {
+                      float* lse_c, int32_t* idx, int32_t* len, void* workspace, size_t ws_bytes, void* stream) {
   Launch L;
   Dims d;
   vsa_status st = check_problem(p, &L, &d);
   if (st != VSA_OK) return st;
   const bool sel = L.topk > 0;
-  st = check_ptrs({{q_c, true}, {k_c, true}, {v_c, true}, {o_c, true}, {lse_c, true}, {idx, sel}, {len, sel}});
+  st = check_ptrs({{q_c, true}, {k_c, true}, {v_c, true}, {o_c, true}, {lse_c, true}, {idx, sel}, {len, sel},
+                   {workspace, true}});
   if (st != VSA_OK) return st;
+  const FwdWs ws = carve_fwd_ws(d, workspace);
+  if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
   L.stream = static_cast<hipStream_t>(stream);
-  return hip_status(launch_coarse(L, q_c, k_c, v_c, o_c, lse_c, sel ? idx : nullptr, sel ? len : nullptr));
+  return hip_status(launch_coarse(L, q_c, k_c, v_c, o_c, lse_c, sel ? idx : nullptr, sel ? len : nullptr, ws.s));
 }
 
 vsa_status vsa_fine_forward(const vsa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,

@@ -22,8 +22,9 @@ hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void
 hipError_t launch_ttile(const Launch& L, const bf16* x, bf16* xt);
 
 int coarse_max_cubes();
+// s_scratch: B*heads*Nc*Nc fp32 (the coarse logits).
 hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, const float* vc, float* oc,
-                         float* lse, int32_t* idx, int32_t* len);
+                         float* lse, int32_t* idx, int32_t* len, float* s_scratch);
 
 // Fine forward. For bf16, vt holds the V T-tiles. When oc is not null the
 // kernel also forms o = O_c * g_c + O_f * g_f (gates may be null = ones) and

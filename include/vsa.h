@@ -143,9 +143,11 @@ vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const vo
  * ascending list (VSA summary page, section 2 and Appendix B; reading notes
  * key design 1, and the fused softmax + top-K + mask-to-index kernel of the
  * notes' training section). With topk == 0 idx / len are not touched (may be
- * NULL). S_c stays on chip. Requires Nc <= vsa_max_cubes(). */
+ * NULL). S_c (fp32, Nc^2 per (b, h)) lives in the workspace
+ * (ws_bytes >= vsa_workspace_bytes(p, 0)). Requires Nc <= vsa_max_cubes(). */
 vsa_status vsa_coarse(const vsa_problem* p, const float* q_c, const float* k_c, const float* v_c,
-                      float* o_c, float* lse_c, int32_t* idx, int32_t* len, void* stream);
+                      float* o_c, float* lse_c, int32_t* idx, int32_t* len, void* workspace,
+                      size_t ws_bytes, void* stream);
 
 /* Step 4, fine block-sparse attention: for every query token of cube i,
  * softmax attention over the tokens of the cubes listed in row i only

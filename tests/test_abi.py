@@ -116,7 +116,8 @@ def test_stage_entry_points_validate():
     c = ctypes.byref(p.c())
     assert lib.vsa_pool(c, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == NULL
     assert lib.vsa_pool(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
-    assert lib.vsa_coarse(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == NULL     # top-K needs idx
+    assert lib.vsa_coarse(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == NULL  # top-K needs idx
+    assert lib.vsa_coarse(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
     assert lib.vsa_fine_forward(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
     assert lib.vsa_fine_forward(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == NULL
     assert lib.vsa_combine(c, FAKE, MIS, None, None, FAKE, None) == ALIGN

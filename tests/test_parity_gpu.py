@@ -26,6 +26,10 @@ F32_ABS = 1e-4
 # Sanity bound on the share of rows whose top-K margin is within the fp32
 # error bound (about 0.6% / 1.4% / 2.3% on the 16x32x32 / 480p / 720p inputs).
 NEAR_FRAC = 0.05
+# LSE_f bound: the fine kernel sums the bf16-rounded probabilities it also
+# multiplies V with, so l carries at most the bf16 half-ulp relative error
+# 2^-8, i.e. |ln l - ln l_exact| <= 2^-8; plus fp32 slack.
+LSE_ABS = 2.0 ** -8 + 1e-4
 
 
 def dev(x, dtype):
@@ -138,7 +142,7 @@ def test_fine_forward_parity_ragged_lists(name, heads):
     got_lse = host(lse)
     live = np.isfinite(ref["lse_f"])
     assert np.array_equal(np.isfinite(got_lse), live)
-    assert float(np.abs(got_lse[live] - ref["lse_f"][live]).max()) <= 2e-3
+    assert float(np.abs(got_lse[live] - ref["lse_f"][live]).max()) <= LSE_ABS
     assert np.all(host(of)[~live] == 0)
 
 
@@ -222,7 +226,7 @@ def test_forward_saved_tensors():
     lse_f = take(nbh * N, torch.float32, 4).reshape(1, 2, w.T, w.H, w.W)
     of = take(nbh * N * D, torch.bfloat16, 2).reshape(1, 2, w.T, w.H, w.W, D)
     assert_close(host(of), ref["o_f"], "bf16", "saved o_f")
-    assert float(np.abs(host(lse_f) - ref["lse_f"]).max()) <= 2e-3
+    assert float(np.abs(host(lse_f) - ref["lse_f"]).max()) <= LSE_ABS
 
 
 @pytest.mark.timeout(900)
