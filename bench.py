@@ -88,6 +88,11 @@ def main() -> int:
     ap.add_argument("--workload", default="bf16_720p_24x44x80")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the oracle sample")
+    ap.add_argument("--mode", choices=["forward", "fine", "copy"], default="forward",
+                    help="forward: the benchmark; fine: only the fused fine kernel, --steps launches "
+                         "(for counter collection); copy: a plain device copy of --copy-mib MiB, the "
+                         "calibration of the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--copy-mib", type=int, default=2048)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -102,6 +107,16 @@ def main() -> int:
     import block_sparse_video_cube_amd as V
 
     torch.cuda.set_device(0)
+    if args.mode == "copy":
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                          "copies": args.steps}), flush=True)
+        return 0
     w = WL.get(args.workload)
     log(f"generating {w.name} inputs")
     t0 = time.perf_counter()
@@ -141,6 +156,18 @@ def main() -> int:
         ev[2].record()
         V.fine_combine(p, q, k, v, idx, lens, pooled[3], gc, gf, ws=ws, out=o)
         ev[3].record()
+
+    if args.mode == "fine":
+        # inputs of the fine kernel, then only that kernel
+        V.pool(p, q, k, v, ws=ws, out=pooled[:3])
+        V.coarse(p, *pooled[:3], out=(pooled[3], lse_c, idx if w.topk > 0 else None,
+                                      lens if w.topk > 0 else None), ws=ws)
+        for _ in range(args.steps):
+            V.fine_combine(p, q, k, v, idx, lens, pooled[3], gc, gf, ws=ws, out=o)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "fine", "launches": args.steps, "workload": w.name,
+                          "block_pairs": int(lens.sum().item())}), flush=True)
+        return 0
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):

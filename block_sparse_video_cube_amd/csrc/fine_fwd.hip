@@ -23,20 +23,108 @@
 
 namespace vsa {
 
-// Occupancy: D = 64 fits 2 waves per SIMD (<= 256 registers), D = 128 one.
-template <int D> struct FineOcc { static constexpr int kWaves = D == 64 ? 2 : 1; };
+// bf16 kernel geometry. A workgroup of two waves owns one query cube; wave
+// w owns the 32 queries 32w .. 32w+31 (one MFMA column block). The cube's
+// list is walked in 32-key chunks (two per key cube); each chunk's K rows and
+// V tile go to LDS once (direct-to-LDS loads, half issued by each wave) and
+// both waves read them. MFMAs are 32x32x16.
+template <int D> struct FineCfg {
+  static constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
+  static constexpr int MB = D / 32;          // 32-channel blocks of O^T
+  static constexpr int U = D / 8;            // 16-byte units per key row
+  static constexpr int KUNITS = 32 * U;      // 16-byte units per K chunk
+  static constexpr int VUNITS = D * 4;       // 16-byte units per V chunk
+  static constexpr int KINS = KUNITS / 64;   // 1 KB direct-to-LDS loads per K chunk
+  static constexpr int VINS = VUNITS / 64;
+  static constexpr int NST = D == 64 ? 3 : 2;  // LDS stages (prefetch depth NST-1 chunks)
+};
+
+// K chunk in LDS: key row kappa (0..31) holds U 16-byte units; logical unit
+// u (channels 8u .. 8u+7) sits at unit u ^ kswz(kappa), so 16 consecutive
+// rows read at one logical unit hit 16 distinct bank groups.
+template <int U> __device__ __forceinline__ int kswz(int kappa) { return (kappa * U / 16) % U; }
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds + 16*l. Issued as inline assembly so that the compiler does not
+// treat later LDS reads of other stages as dependent on it; completion is
+// tracked by the vector-memory counter and waited for explicitly (wait_vmcnt).
+// The compiler never uses M0 in these kernels (checked on the generated code).
+// The address is a wave-uniform base (SGPRs) plus a per-lane 32-bit byte
+// offset, so issuing a load costs no vector instructions.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+// A pointer the compiler may keep in scalar registers (all lanes agree).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const unsigned long long b = (unsigned long long)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return (const void*)(((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Processing order of the query cubes of every (b, h): ascending by the first
+// two cubes of their lists (empty positions sort last), ties by cube id.
+// Query cubes with similar lists then run side by side on an XCD and share
+// the key / value blocks in its L2. One workgroup per (b, h): a bitonic sort
+// of (signature << 32 | cube) keys in LDS.
+__global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ len,
+                                                     int32_t* __restrict__ order, int Nc, int stride, int pow2) {
+  __shared__ unsigned long long key[2048];
+  const long bh = blockIdx.x;
+  for (int e = threadIdx.x; e < pow2; e += 1024) {
+    unsigned long long kv = ~0ull;
+    if (e < Nc) {
+      const long row = bh * Nc + e;
+      const int n = min(max(len[row], 0), stride);
+      const uint32_t a = n > 0 ? (uint32_t)idx[row * stride] : (uint32_t)Nc;
+      const uint32_t b = n > 1 ? (uint32_t)idx[row * stride + 1] : (uint32_t)Nc;
+      const uint32_t sig = min(a, (uint32_t)Nc) * (uint32_t)(Nc + 1) + min(b, (uint32_t)Nc);
+      kv = ((unsigned long long)sig << 32) | (uint32_t)e;
+    }
+    key[e] = kv;
+  }
+  __syncthreads();
+  for (int kk = 2; kk <= pow2; kk <<= 1)
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int e = threadIdx.x; e < pow2; e += 1024) {
+        const int p = e ^ jj;
+        if (p > e) {
+          const unsigned long long x = key[e], y = key[p];
+          const bool up = (e & kk) == 0;
+          if ((x > y) == up) { key[e] = y; key[p] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  for (int e = threadIdx.x; e < Nc; e += 1024) order[bh * Nc + e] = (int32_t)(key[e] & 0xffffffffu);
+}
 
 template <int D, bool FUSED>
-__global__ __launch_bounds__(64, FineOcc<D>::kWaves) void fine_fwd_bf16_kernel(
+__global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ vt,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ len, bf16* __restrict__ o_f,
-    float* __restrict__ lse_f, const float* __restrict__ oc, const bf16* __restrict__ gc,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
+    bf16* __restrict__ o_f, float* __restrict__ lse_f, const float* __restrict__ oc, const bf16* __restrict__ gc,
     const bf16* __restrict__ gf, bf16* __restrict__ o, Grid g, int stride, float scale_log2) {
-  constexpr int KS = D / 32;   // k-steps of the QK^T contraction
-  constexpr int DB = D / 16;   // 16-channel blocks of the output
-  const int lane = threadIdx.x, c16 = lane & 15, grp = lane >> 4;
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = item / g.Nc, i = item - bh * g.Nc;
+  using C = FineCfg<D>;
+  // NST stages of one K chunk and one V chunk each.
+  __shared__ __attribute__((aligned(16))) bf16 kbuf[C::NST * C::KUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 vbuf[C::NST * C::VUNITS * 8];
+
+  const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
+  const int slot = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = slot / g.Nc;
+  const int i = order != nullptr ? order[slot] : slot - bh * g.Nc;
+  const int item = bh * g.Nc + i;
   const long tok0 = (long)bh * g.N;
   const bf16* Q = q + tok0 * D;
   const bf16* K = k + tok0 * D;
@@ -44,168 +132,180 @@ __global__ __launch_bounds__(64, FineOcc<D>::kWaves) void fine_fwd_bf16_kernel(
   // from reading outside the tensors.
   const int L = min(max(len[item], 0), stride);
   const int32_t* list = idx + (long)item * stride;
+  auto cube_at = [&](int t) { const int j = list[t]; return (j >= 0 && j < g.Nc) ? j : 0; };
 
-  // Query rows of this lane: token qb*16 + c16 of cube i, qb = 0..3, i.e.
-  // (t' = qb, y' = c16 / 4, x' = c16 % 4).
-  int qrow[4];
+  // This lane's query: q = 32wv + n32, token (t' = 2wv + n32/16, y' = (n32/4)%4, x' = n32%4).
+  const int qrow = cube_row(g, i, 2 * wv + (n32 >> 4), (n32 >> 2) & 3) + (n32 & 3);
+  // B operand of S^T = K Q^T: lane holds Q[q][16ks + 8hf .. +8].
+  bf16x8 qf[C::KS];
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) qrow[qb] = cube_row(g, i, qb, c16 >> 2) + (c16 & 3);
+  for (int ks = 0; ks < C::KS; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(Q + (long)qrow * D + ks * 16 + hf * 8);
 
-  bf16x8 qf[4][KS];
+  f32x16 acc[C::MB], lacc;
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb)
+  for (int e = 0; e < 16; ++e) lacc[e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[qb][ks] = *reinterpret_cast<const bf16x8*>(Q + (long)qrow[qb] * D + ks * 32 + grp * 8);
-
-  f32x4 acc[DB][4], lacc[4];
+  for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // Reference max per query (log2 units), common to the 4 lanes of a query.
-  float m[4];
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb) m[qb] = -INFINITY;
+    for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
+  float m = -INFINITY;
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
 
-  // The list is walked in 32-key chunks, two per key cube: chunk h of cube j
-  // holds the key rows t' = 2h, 2h+1 (tokens 32h .. 32h+31), which is exactly
-  // k-step h of the cube's V T-tile. Online softmax over any chunking is the
-  // same softmax.
-  auto cube_at = [&](int t) { const int j = list[t]; return (j >= 0 && j < g.Nc) ? j : 0; };
-  bf16x8 kf[2][KS];
-  auto load_k = [&](int j, int h) {
+  // This wave's half of the loads of chunk c = key cube list[c/2], half c%2
+  // (tokens 32h .. 32h+31), into stage c % NST. Per-lane byte offsets are
+  // fixed for the whole list: K unit p = ins*64 + lane is key row kappa =
+  // p / U, logical unit (p % U) ^ kswz(kappa), i.e. token (t', y', x') =
+  // (2h + kappa/16, (kappa/4)%4, kappa%4) of the cube; V is a linear copy.
+  const uint32_t kbase = lds_addr(kbuf), vbase = lds_addr(vbuf);
+  uint32_t koff[C::KINS / 2], voff[C::VINS / 2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const long r = cube_row(g, j, 2 * h + kk, c16 >> 2) + (c16 & 3);
+  for (int t = 0; t < C::KINS / 2; ++t) {
+    const int ins = wv * (C::KINS / 2) + t;
+    const int p = ins * 64 + lane, kappa = p / C::U, u = (p % C::U) ^ kswz<C::U>(kappa);
+    const int tokoff = ((kappa >> 4) * g.H + ((kappa >> 2) & 3)) * g.W + (kappa & 3);
+    koff[t] = (uint32_t)(tokoff * D + u * 8) * 2u;
+  }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[kk][ks] = *reinterpret_cast<const bf16x8*>(K + r * D + ks * 32 + grp * 8);
-    }
+  for (int t = 0; t < C::VINS / 2; ++t) voff[t] = (uint32_t)((wv * (C::VINS / 2) + t) * 64 + lane) * 16u;
+  // Byte offsets of the list's cubes, 64 entries at a time, one per lane:
+  // kcube = first key row of the cube within this head's K, vcube = the
+  // cube's V chunk tiles. A chunk's issue reads them with readlane, so the
+  // per-chunk address work is scalar and division-free.
+  const uint32_t khalf = (uint32_t)(2 * g.H * g.W * D) * 2u;   // t' -> t' + 2
+  const char* vt_bh = reinterpret_cast<const char*>(vt + (long)bh * g.Nc * D * kTile);
+  uint32_t kcube = 0, vcube = 0;
+  auto load_cubes = [&](int t0) {
+    const int t = t0 + lane;
+    const int j = t < L ? cube_at(t) : 0;
+    kcube = (uint32_t)cube_row(g, j, 0, 0) * (uint32_t)(D * 2);
+    vcube = (uint32_t)j * (uint32_t)(D * kTile * 2);
   };
-  const int nchunks = 2 * L;
-
-  auto scores = [&](f32x4 (&sx)[2][4]) {
+  auto issue = [&](int c) {
+    const int e = c >> 1, h = c & 1, st = c % C::NST;
+    if ((e & 63) == 0 && h == 0) load_cubes(e);
+    const uint32_t kdst = kbase + st * (C::KUNITS * 16), vdst = vbase + st * (C::VUNITS * 16);
+    const uint32_t kc = __builtin_amdgcn_readlane(kcube, e & 63), vc = __builtin_amdgcn_readlane(vcube, e & 63);
+    const void* ksrc = uniform_ptr(reinterpret_cast<const char*>(K) + kc + (h ? khalf : 0u));
+    const void* vsrc = uniform_ptr(vt_bh + vc + (h ? (uint32_t)(D * 32 * 2) : 0u));
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int t = 0; t < C::KINS / 2; ++t) dma16(ksrc, koff[t], kdst + (wv * (C::KINS / 2) + t) * 1024);
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < C::VINS / 2; ++t) dma16(vsrc, voff[t], vdst + (wv * (C::VINS / 2) + t) * 1024);
+  };
+  // S^T (32 keys x 32 queries): lane holds, at accumulator index jj, key
+  // 8*(jj/4) + 4hf + jj%4 of the lane's query.
+  auto scores = [&](const bf16* kb, f32x16& sx) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a = mfma16_bf16(kf[kk][ks], qf[qb][ks], a);
-        sx[kk][qb] = a;
-      }
+    for (int e = 0; e < 16; ++e) sx[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (n32 * C::U + ((2 * ks + hf) ^ kswz<C::U>(n32))) * 8);
+      sx = mfma32_bf16(a, qf[ks], sx);
+    }
   };
 
   // Online softmax against a lazily moved reference max m (log2 units): P =
   // 2^(s*c - m) is formed as long as no exponent exceeds 16 (P < 2^16, so
   // bf16 P and the fp32 sums keep their relative precision). A chunk that
   // would exceed it leaves the hot loop; the reference then moves up to the
-  // chunk's row max, O and l are rescaled, and the chunk is redone. O and l
-  // always share m, so the result is exact whatever the schedule. The row
-  // sum l comes from an MFMA against a ones operand, so the hot loop touches
-  // the accumulators only through MFMAs. The first chunk's row max sets the
-  // initial reference.
+  // chunk's row max, O and l are rescaled, and the chunk is redone from the
+  // same LDS stage. O and l always share m, so the result is exact whatever
+  // the schedule; the hot loop touches the accumulators only through MFMAs.
   constexpr float kHeadroom = 16.0f;
-  if (nchunks > 0) {
-    load_k(cube_at(0), 0);
-    f32x4 sx[2][4];
-    scores(sx);
+  float cmax = 0.f;
+  auto compute = [&](const bf16* kb, const bf16* vb) -> bool {
+    f32x16 sx;
+    scores(kb, sx);
+    float mq = -INFINITY;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      float mx = fmaxf(fmaxf(fmaxf(sx[0][qb][0], sx[0][qb][1]), fmaxf(sx[0][qb][2], sx[0][qb][3])),
-                       fmaxf(fmaxf(sx[1][qb][0], sx[1][qb][1]), fmaxf(sx[1][qb][2], sx[1][qb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      m[qb] = mx * scale_log2;
+    for (int e = 0; e < 16; ++e) {
+      sx[e] = sx[e] * scale_log2 - m;
+      mq = fmaxf(mq, sx[e]);
     }
+    cmax = mq;
+    if (__any(mq > kHeadroom)) return true;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (bf16)__builtin_amdgcn_exp2f(sx[e]);
+    // Row sums of the rounded P (the weights O is formed with), by MFMA.
+    lacc = mfma32_bf16(ones, pf[0], lacc);
+    lacc = mfma32_bf16(ones, pf[1], lacc);
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const int dd = 32 * mb + n32;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + (dd * 4 + ((2 * s2 + hf) ^ vunit_swz(dd))) * 8);
+        acc[mb] = mfma32_bf16(a, pf[s2], acc[mb]);
+      }
+    }
+    return false;
+  };
+  const int nch = 2 * L;
+  constexpr int kPerWave = (C::KINS + C::VINS) / 2;   // this wave's loads per chunk
+  // Prologue: chunks 0 .. NST-2 in flight; the row max of chunk 0 sets the
+  // initial reference.
+#pragma unroll
+  for (int c0 = 0; c0 < C::NST - 1; ++c0)
+    if (c0 < nch) issue(c0);
+  if (nch > 0) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    f32x16 sx;
+    scores(kbuf, sx);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sx[e]);
+    m = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
   }
+  // Per chunk: wait for this wave's loads of chunk c (later chunks may stay in
+  // flight), barrier (both halves are then in LDS, and both waves are done
+  // with the stage about to be refilled), issue chunk c + NST - 1, compute
+  // chunk c. A redo after a rescale skips the wait / barrier / issue, so both
+  // waves still pass the same barriers. The barrier is a bare s_barrier: a
+  // fenced one would also wait for the prefetches in flight.
   int c = 0;
+  bool redo = false;
   for (;;) {
-    bool retry = false;
-    float cmax[4];
-    if (c < nchunks) load_k(cube_at(c >> 1), c & 1);
-    for (; c < nchunks; ++c) {
-      const int h = c & 1;
-      const int j = cube_at(c >> 1);
-      bf16x8 vf[DB];
-      const bf16* vtile = vt + ((long)bh * g.Nc + j) * D * kTile;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        vf[db] = *reinterpret_cast<const bf16x8*>(vtile + (db * 16 + c16) * kTile + h * 32 + grp * 8);
-      // S^T[kk][qb]: lane holds keys 32h + 16kk + 4*grp + r of query qb*16 + c16.
-      f32x4 sx[2][4];
-      scores(sx);
-      // exponent arguments x = s*c - m, and the largest of them per query
-      float xmax = -INFINITY;
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        float mq = -INFINITY;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sx[kk][qb][r] = sx[kk][qb][r] * scale_log2 - m[qb];
-            mq = fmaxf(mq, sx[kk][qb][r]);
-          }
-        cmax[qb] = mq;
-        xmax = fmaxf(xmax, mq);
+    for (; c < nch; ++c) {
+      if (!redo) {
+        if (C::NST == 3 && c + 1 < nch) wait_vmcnt<kPerWave>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (c + C::NST - 1 < nch) issue(c + C::NST - 1);
       }
-      if (__any(xmax > kHeadroom)) { retry = true; break; }
-      if (c + 1 < nchunks) load_k(cube_at((c + 1) >> 1), h ^ 1);
-      bf16x8 pf[4];
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pf[qb][kk * 4 + r] = (bf16)__builtin_amdgcn_exp2f(sx[kk][qb][r]);
-#pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        lacc[qb] = mfma16_bf16(ones, pf[qb], lacc[qb]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db][qb] = mfma16_bf16(vf[db], pf[qb], acc[db][qb]);
-      }
+      redo = false;
+      const int st = c % C::NST;
+      if (compute(kbuf + st * C::KUNITS * 8, vbuf + st * C::VUNITS * 8)) { redo = true; break; }
     }
-    if (!retry) break;
-    // Rare path: move each query's reference up to its row max over this
-    // chunk (the 4 lanes of a query agree through two exchanges); rescale.
+    if (!redo) break;
+    // Rare path: move the query's reference up to its row max over this
+    // chunk (the two lanes of a query agree through one exchange); rescale.
+    const float mx = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float shift = fmaxf(mx, 0.0f);
+    const float alpha = __builtin_amdgcn_exp2f(-shift);
+    m += shift;
+    lacc *= alpha;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      float mx = cmax[qb];
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float shift = fmaxf(mx, 0.0f);
-      const float alpha = __builtin_amdgcn_exp2f(-shift);
-      m[qb] += shift;
-      lacc[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db][qb] *= alpha;
-    }
+    for (int mb = 0; mb < C::MB; ++mb) acc[mb] *= alpha;
   }
-  float l[4];
-#pragma unroll
-  for (int qb = 0; qb < 4; ++qb) l[qb] = lacc[qb][0];
 
-  // Epilogue: lane holds O^T[channel db*16 + 4*grp + r][query qb*16 + c16].
+  // Epilogue: lane holds O^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query].
+  const float lt = lacc[0];   // every row of the ones-MFMA holds the full sum
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const long n = tok0 + qrow;
+  if (lse_f != nullptr && hf == 0) lse_f[n] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
 #pragma unroll
-  for (int qb = 0; qb < 4; ++qb) {
-    const float lt = l[qb];
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const long n = tok0 + qrow[qb];
-    if (lse_f != nullptr && grp == 0)
-      lse_f[n] = lt > 0.f ? (m[qb] + __log2f(lt)) * kLn2 : -INFINITY;
+  for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int ch = db * 16 + 4 * grp;
+    for (int jq = 0; jq < 4; ++jq) {
+      const int ch = 32 * mb + 8 * jq + 4 * hf;
       float of[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) of[r] = acc[db][qb][r] * inv;
+      for (int r = 0; r < 4; ++r) of[r] = acc[mb][4 * jq + r] * inv;
       if (o_f != nullptr) {
         bf16x4 w;
 #pragma unroll
@@ -230,7 +330,6 @@ __global__ __launch_bounds__(64, FineOcc<D>::kWaves) void fine_fwd_bf16_kernel(
         *reinterpret_cast<bf16x4*>(o + n * D + ch) = w;
       }
     }
-  }
 }
 
 // fp32 path: one thread per query token, K/V tiles staged in LDS. Used for
@@ -294,11 +393,11 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
 
 template <int D, bool FUSED>
 static void fine_launch_bf16(const Launch& L, const void* q, const void* k, const bf16* vt, const int32_t* idx,
-                             const int32_t* len, void* o_f, float* lse_f, const float* oc, const void* gc,
+                             const int32_t* len, const int32_t* order, void* o_f, float* lse_f, const float* oc, const void* gc,
                              const void* gf, void* o) {
   const int nitems = L.BH * L.g.Nc;
-  hipLaunchKernelGGL((fine_fwd_bf16_kernel<D, FUSED>), dim3(nitems), dim3(64), 0, L.stream, (const bf16*)q,
-                     (const bf16*)k, vt, idx, len, (bf16*)o_f, lse_f, oc, (const bf16*)gc, (const bf16*)gf,
+  hipLaunchKernelGGL((fine_fwd_bf16_kernel<D, FUSED>), dim3(nitems), dim3(128), 0, L.stream, (const bf16*)q,
+                     (const bf16*)k, vt, idx, len, order, (bf16*)o_f, lse_f, oc, (const bf16*)gc, (const bf16*)gf,
                      (bf16*)o, L.g, L.stride, L.scale * kLog2e);
 }
 
@@ -312,17 +411,25 @@ static void fine_launch_f32(const Launch& L, const void* q, const void* k, const
                      (const float*)gf, (float*)o, L.g, L.stride, L.scale);
 }
 
+hipError_t launch_order(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* order) {
+  int pow2 = 1;
+  while (pow2 < L.g.Nc) pow2 <<= 1;
+  if (pow2 > 2048) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(order_kernel, dim3(L.BH), dim3(1024), 0, L.stream, idx, len, order, L.g.Nc, L.stride, pow2);
+  return hipGetLastError();
+}
+
 hipError_t launch_fine_fwd(const Launch& L, const void* q, const void* k, const void* v, const bf16* vt,
-                           const int32_t* idx, const int32_t* len, void* o_f, float* lse_f, const float* oc,
-                           const void* g_c, const void* g_f, void* o) {
+                           const int32_t* idx, const int32_t* len, const int32_t* order, void* o_f, float* lse_f,
+                           const float* oc, const void* g_c, const void* g_f, void* o) {
   const bool fused = oc != nullptr;
   if (L.bf16) {
     if (L.D == 64) {
-      if (fused) fine_launch_bf16<64, true>(L, q, k, vt, idx, len, o_f, lse_f, oc, g_c, g_f, o);
-      else fine_launch_bf16<64, false>(L, q, k, vt, idx, len, o_f, lse_f, oc, g_c, g_f, o);
+      if (fused) fine_launch_bf16<64, true>(L, q, k, vt, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
+      else fine_launch_bf16<64, false>(L, q, k, vt, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
     } else {
-      if (fused) fine_launch_bf16<128, true>(L, q, k, vt, idx, len, o_f, lse_f, oc, g_c, g_f, o);
-      else fine_launch_bf16<128, false>(L, q, k, vt, idx, len, o_f, lse_f, oc, g_c, g_f, o);
+      if (fused) fine_launch_bf16<128, true>(L, q, k, vt, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
+      else fine_launch_bf16<128, false>(L, q, k, vt, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
     }
   } else {
     if (L.D == 64) {

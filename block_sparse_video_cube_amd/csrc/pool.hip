@@ -7,7 +7,8 @@
 // One workgroup per (b, h, cube). Each thread owns one 8-channel chunk of a
 // set of token rows, sums them in fp32, and the partial sums are reduced
 // through LDS. HBM-bound: every input element is read once; pooled means
-// (fp32) and optionally the bf16 T-tile of V are written once.
+// (fp32) and optionally the bf16 V chunk tiles of the fine forward kernel
+// (layout in vsa_common.h) are written once.
 #include "vsa_kernels.h"
 
 namespace vsa {
@@ -61,14 +62,16 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   }
 
   if (vt != nullptr) {
-    // T-tile [D][64]: 8 lanes write one 128-byte channel row.
+    // V chunk tiles: [2 halves][D channel rows][4 units of 8 slots]; one
+    // thread writes one 16-byte unit.
     bf16* dst = vt + (bh * g.Nc + c) * (long)D * kTile;
-    for (int w = tid; w < D * 8; w += 256) {
-      const int dd = w >> 3, j = w & 7;
+    for (int w = tid; w < 2 * D * 4; w += 256) {
+      const int h = w / (D * 4), rem = w - h * D * 4, dd = rem >> 2, up = rem & 3;
+      const int u = up ^ vunit_swz(dd);
       bf16x8 r;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = vtile[tslot(8 * j + e)][dd];
-      *reinterpret_cast<bf16x8*>(dst + dd * kTile + 8 * j) = r;
+      for (int e = 0; e < 8; ++e) r[e] = vtile[32 * h + vslot(8 * u + e)][dd];
+      *reinterpret_cast<bf16x8*>(dst + (long)w * 8) = r;
     }
   }
 }

@@ -105,6 +105,7 @@ Saved carve_saved(const Dims& d, void* base) {
 // inference, the pooled tensors.
 struct FwdWs {
   bf16* vt;
+  int32_t* order;
   float *s, *qc, *kc, *vc, *oc, *lse_c;
   size_t bytes;
 };
@@ -112,6 +113,7 @@ FwdWs carve_fwd_ws(const Dims& d, void* base) {
   Carver c(base);
   FwdWs w;
   w.vt = d.elem == 2 ? c.take<bf16>(d.BH * d.N * d.D) : nullptr;
+  w.order = c.take<int32_t>(d.BH * d.Nc);
   w.s = c.take<float>(d.BH * d.Nc * d.Nc);
   const size_t pooled = d.BH * d.Nc * d.D;
   w.qc = c.take<float>(pooled);
@@ -217,7 +219,9 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
   hipError_t e = launch_pool(L, q, k, v, qc, kc, vc, ws.vt);
   if (e == hipSuccess)
     e = launch_coarse(L, qc, kc, vc, oc, lse_c, L.topk > 0 ? idx : nullptr, L.topk > 0 ? len : nullptr, ws.s);
-  if (e == hipSuccess) e = launch_fine_fwd(L, q, k, v, ws.vt, idx, len, of, lse_f, oc, g_c, g_f, o);
+  if (e == hipSuccess && L.bf16) e = launch_order(L, idx, len, ws.order);
+  if (e == hipSuccess)
+    e = launch_fine_fwd(L, q, k, v, ws.vt, idx, len, L.bf16 ? ws.order : nullptr, of, lse_f, oc, g_c, g_f, o);
   return hip_status(e);
 }
 
@@ -297,13 +301,18 @@ vsa_status vsa_fine_forward(const vsa_problem* p, const void* q, const void* k, 
                    {workspace, L.bf16}});
   if (st != VSA_OK) return st;
   bf16* vt = nullptr;
+  int32_t* order = nullptr;
   if (L.bf16) {
     const FwdWs ws = carve_fwd_ws(d, const_cast<void*>(workspace));
     if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
     vt = ws.vt;
+    order = ws.order;
   }
   L.stream = static_cast<hipStream_t>(stream);
-  return hip_status(launch_fine_fwd(L, q, k, v, vt, idx, len, o_f, lse_f, nullptr, nullptr, nullptr, nullptr));
+  hipError_t e = order != nullptr ? launch_order(L, idx, len, order) : hipSuccess;
+  if (e == hipSuccess)
+    e = launch_fine_fwd(L, q, k, v, vt, idx, len, order, o_f, lse_f, nullptr, nullptr, nullptr, nullptr);
+  return hip_status(e);
 }
 
 vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
@@ -317,13 +326,17 @@ vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, 
                    {g_f, false}, {o, true}, {o_f, false}, {lse_f, false}, {workspace, L.bf16}});
   if (st != VSA_OK) return st;
   bf16* vt = nullptr;
+  int32_t* order = nullptr;
   if (L.bf16) {
     const FwdWs ws = carve_fwd_ws(d, const_cast<void*>(workspace));
     if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
     vt = ws.vt;
+    order = ws.order;
   }
   L.stream = static_cast<hipStream_t>(stream);
-  return hip_status(launch_fine_fwd(L, q, k, v, vt, idx, len, o_f, lse_f, o_c, g_c, g_f, o));
+  hipError_t e = order != nullptr ? launch_order(L, idx, len, order) : hipSuccess;
+  if (e == hipSuccess) e = launch_fine_fwd(L, q, k, v, vt, idx, len, order, o_f, lse_f, o_c, g_c, g_f, o);
+  return hip_status(e);
 }
 
 vsa_status vsa_combine(const vsa_problem* p, const float* o_c, const void* o_f, const void* g_c, const void* g_f,

@@ -78,6 +78,19 @@ __host__ __device__ __forceinline__ int tslot(int slot) {
   return 32 * (slot >> 5) + 16 * ((slot & 7) >> 2) + 4 * ((slot & 31) >> 3) + (slot & 3);
 }
 
+// V chunk tiles (read by the fine forward kernel, 32x32x16 MFMAs): for each
+// cube and each half h (tokens 32h .. 32h+31) a [D][32] bf16 block, channel
+// rows of 64 bytes = four 16-byte units. Slot t of a row holds token
+// 32h + vslot(t): the order in which a 32x32 MFMA accumulator hands its rows
+// to the k side of the next MFMA (lane half hf holds, for k-step s, rows
+// 16s + 4hf + {0..3} and 16s + 8 + 4hf + {0..3}). Unit u' of channel row dd
+// stores logical unit u' ^ ((dd >> 2) & 3), so 16 consecutive channel rows
+// read at the same logical unit hit 16 distinct LDS bank groups.
+__host__ __device__ __forceinline__ int vslot(int t) {
+  return 16 * (t >> 4) + 8 * ((t & 7) >> 2) + 4 * ((t & 15) >> 3) + (t & 3);
+}
+__host__ __device__ __forceinline__ int vunit_swz(int dd) { return (dd >> 2) & 3; }
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2). Map block b so that every XCD gets one contiguous range of work items:
 // neighbouring items (same head, neighbouring cubes) then share an L2.
@@ -141,6 +154,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ f32x4 mfma16_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma16_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

@@ -26,12 +26,16 @@ int coarse_max_cubes();
 hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, const float* vc, float* oc,
                          float* lse, int32_t* idx, int32_t* len, float* s_scratch);
 
-// Fine forward. For bf16, vt holds the V T-tiles. When oc is not null the
-// kernel also forms o = O_c * g_c + O_f * g_f (gates may be null = ones) and
-// writes it to `o`; o_f / lse_f may then be null (not written).
+// Processing order of query cubes (BH*Nc int32) from their lists.
+hipError_t launch_order(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* order);
+
+// Fine forward. For bf16, vt holds the V chunk tiles and `order` (may be
+// null = cube order) the processing order from launch_order. When oc is not
+// null the kernel also forms o = O_c * g_c + O_f * g_f (gates may be null =
+// ones) and writes it to `o`; o_f / lse_f may then be null (not written).
 hipError_t launch_fine_fwd(const Launch& L, const void* q, const void* k, const void* v, const bf16* vt,
-                           const int32_t* idx, const int32_t* len, void* o_f, float* lse_f, const float* oc,
-                           const void* g_c, const void* g_f, void* o);
+                           const int32_t* idx, const int32_t* len, const int32_t* order, void* o_f, float* lse_f,
+                           const float* oc, const void* g_c, const void* g_f, void* o);
 
 hipError_t launch_combine(const Launch& L, const float* oc, const void* of, const void* gc, const void* gf,
                           void* o);
