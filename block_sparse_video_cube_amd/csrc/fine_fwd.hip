@@ -36,7 +36,10 @@ template <int D> struct FineCfg {
   static constexpr int VUNITS = D * 4;       // 16-byte units per V chunk
   static constexpr int KINS = KUNITS / 64;   // 1 KB direct-to-LDS loads per K chunk
   static constexpr int VINS = VUNITS / 64;
-  static constexpr int NST = D == 64 ? 3 : 2;  // LDS stages (prefetch depth NST-1 chunks)
+  // LDS stages of K and V chunks. D = 128: (3 + 2) x 8 KB = 40 KB, so four
+  // workgroups (two waves per SIMD) fit in the 160 KB of LDS of a CU.
+  static constexpr int KST = 3;
+  static constexpr int VST = D == 64 ? 3 : 2;
 };
 
 // K chunk in LDS: key row kappa (0..31) holds U 16-byte units; logical unit
@@ -115,9 +118,8 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
     bf16* __restrict__ o_f, float* __restrict__ lse_f, const float* __restrict__ oc, const bf16* __restrict__ gc,
     const bf16* __restrict__ gf, bf16* __restrict__ o, Grid g, int stride, float scale_log2) {
   using C = FineCfg<D>;
-  // NST stages of one K chunk and one V chunk each.
-  __shared__ __attribute__((aligned(16))) bf16 kbuf[C::NST * C::KUNITS * 8];
-  __shared__ __attribute__((aligned(16))) bf16 vbuf[C::NST * C::VUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 kbuf[C::KST * C::KUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 vbuf[C::VST * C::VUNITS * 8];
 
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
@@ -142,23 +144,18 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   for (int ks = 0; ks < C::KS; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8*>(Q + (long)qrow * D + ks * 16 + hf * 8);
 
-  f32x16 acc[C::MB], lacc;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) lacc[e] = 0.f;
+  f32x16 acc[C::MB];
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
-  float m = -INFINITY;
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.0f;
+  float m = 0.f, lsum = 0.f;
 
-  // This wave's half of the loads of chunk c = key cube list[c/2], half c%2
-  // (tokens 32h .. 32h+31), into stage c % NST. Per-lane byte offsets are
-  // fixed for the whole list: K unit p = ins*64 + lane is key row kappa =
-  // p / U, logical unit (p % U) ^ kswz(kappa), i.e. token (t', y', x') =
-  // (2h + kappa/16, (kappa/4)%4, kappa%4) of the cube; V is a linear copy.
+  // Loads of chunk c = key cube list[c/2], half c%2 (tokens 32h .. 32h+31):
+  // this wave issues half of the K rows and half of the V tile. Per-lane byte
+  // offsets are fixed for the whole list: K unit p = ins*64 + lane is key row
+  // kappa = p / U, logical unit (p % U) ^ kswz(kappa), i.e. token (t', y', x')
+  // = (2h + kappa/16, (kappa/4)%4, kappa%4) of the cube; V is a linear copy.
   const uint32_t kbase = lds_addr(kbuf), vbase = lds_addr(vbuf);
   uint32_t koff[C::KINS / 2], voff[C::VINS / 2];
 #pragma unroll
@@ -172,129 +169,160 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   for (int t = 0; t < C::VINS / 2; ++t) voff[t] = (uint32_t)((wv * (C::VINS / 2) + t) * 64 + lane) * 16u;
   // Byte offsets of the list's cubes, 64 entries at a time, one per lane:
   // kcube = first key row of the cube within this head's K, vcube = the
-  // cube's V chunk tiles. A chunk's issue reads them with readlane, so the
-  // per-chunk address work is scalar and division-free.
+  // cube's V chunk tiles. A load reads them with readlane, so the per-chunk
+  // address work is scalar and division-free. The block of entries is
+  // refreshed when chunk c = 128 * n is loaded; K runs ahead of V, so V
+  // keeps its own copy.
   const uint32_t khalf = (uint32_t)(2 * g.H * g.W * D) * 2u;   // t' -> t' + 2
   const char* vt_bh = reinterpret_cast<const char*>(vt + (long)bh * g.Nc * D * kTile);
   uint32_t kcube = 0, vcube = 0;
-  auto load_cubes = [&](int t0) {
+  auto cubes_k = [&](int t0) {
     const int t = t0 + lane;
-    const int j = t < L ? cube_at(t) : 0;
-    kcube = (uint32_t)cube_row(g, j, 0, 0) * (uint32_t)(D * 2);
-    vcube = (uint32_t)j * (uint32_t)(D * kTile * 2);
+    kcube = (uint32_t)cube_row(g, t < L ? cube_at(t) : 0, 0, 0) * (uint32_t)(D * 2);
   };
-  auto issue = [&](int c) {
-    const int e = c >> 1, h = c & 1, st = c % C::NST;
-    if ((e & 63) == 0 && h == 0) load_cubes(e);
-    const uint32_t kdst = kbase + st * (C::KUNITS * 16), vdst = vbase + st * (C::VUNITS * 16);
-    const uint32_t kc = __builtin_amdgcn_readlane(kcube, e & 63), vc = __builtin_amdgcn_readlane(vcube, e & 63);
-    const void* ksrc = uniform_ptr(reinterpret_cast<const char*>(K) + kc + (h ? khalf : 0u));
-    const void* vsrc = uniform_ptr(vt_bh + vc + (h ? (uint32_t)(D * 32 * 2) : 0u));
-#pragma unroll
-    for (int t = 0; t < C::KINS / 2; ++t) dma16(ksrc, koff[t], kdst + (wv * (C::KINS / 2) + t) * 1024);
-#pragma unroll
-    for (int t = 0; t < C::VINS / 2; ++t) dma16(vsrc, voff[t], vdst + (wv * (C::VINS / 2) + t) * 1024);
+  auto cubes_v = [&](int t0) {
+    const int t = t0 + lane;
+    vcube = (uint32_t)(t < L ? cube_at(t) : 0) * (uint32_t)(D * kTile * 2);
   };
-  // S^T (32 keys x 32 queries): lane holds, at accumulator index jj, key
-  // 8*(jj/4) + 4hf + jj%4 of the lane's query.
-  auto scores = [&](const bf16* kb, f32x16& sx) {
+  auto issue_k = [&](int c) {
+    const int e = c >> 1, h = c & 1;
+    if ((e & 63) == 0 && h == 0) cubes_k(e);
+    const uint32_t dst = kbase + (c % C::KST) * (C::KUNITS * 16);
+    const uint32_t kc = __builtin_amdgcn_readlane(kcube, e & 63);
+    const void* src = uniform_ptr(reinterpret_cast<const char*>(K) + kc + (h ? khalf : 0u));
+#pragma unroll
+    for (int t = 0; t < C::KINS / 2; ++t) dma16(src, koff[t], dst + (wv * (C::KINS / 2) + t) * 1024);
+  };
+  auto issue_v = [&](int c) {
+    const int e = c >> 1, h = c & 1;
+    if ((e & 63) == 0 && h == 0) cubes_v(e);
+    const uint32_t dst = vbase + (c % C::VST) * (C::VUNITS * 16);
+    const uint32_t vc = __builtin_amdgcn_readlane(vcube, e & 63);
+    const void* src = uniform_ptr(vt_bh + vc + (h ? (uint32_t)(D * 32 * 2) : 0u));
+#pragma unroll
+    for (int t = 0; t < C::VINS / 2; ++t) dma16(src, voff[t], dst + (wv * (C::VINS / 2) + t) * 1024);
+  };
+  // S^T (32 keys x 32 queries) of the K chunk at kb: lane holds, at
+  // accumulator index jj, key 8*(jj/4) + 4hf + jj%4 of the lane's query.
+  // All fragments are read first so that LDS latency is paid once.
+  auto scores = [&](const bf16* kb) {
+    bf16x8 kf[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8*>(kb + (n32 * C::U + ((2 * ks + hf) ^ kswz<C::U>(n32))) * 8);
+    f32x16 sx;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sx[e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (n32 * C::U + ((2 * ks + hf) ^ kswz<C::U>(n32))) * 8);
-      sx = mfma32_bf16(a, qf[ks], sx);
-    }
+    for (int ks = 0; ks < C::KS; ++ks) sx = mfma32_bf16(kf[ks], qf[ks], sx);
+    return sx;
   };
-
+  // Software pipeline over chunks. Iteration c forms P from the scores of
+  // chunk c (computed in iteration c - 1) while the MFMAs of the scores of
+  // chunk c + 1 run, then adds V_c^T P^T into O^T. K chunks are loaded KST - 1
+  // iterations ahead of their scores, V chunks VST - 1 ahead of their use;
+  // iteration c issues V of chunk c + VST - 1 and then K of chunk c + KST.
+  // At its top it needs K of c + 1 and V of c; loads retire in order, so only
+  // the K loads issued in iteration c - 1 may stay in flight. Each wave waits
+  // for its own loads, then a barrier (a bare s_barrier: a fenced one would
+  // also wait for the loads in flight) makes both halves visible and frees
+  // the stages about to be refilled (K of c, V of c - 1, read in c - 1).
+  //
   // Online softmax against a lazily moved reference max m (log2 units): P =
   // 2^(s*c - m) is formed as long as no exponent exceeds 16 (P < 2^16, so
-  // bf16 P and the fp32 sums keep their relative precision). A chunk that
-  // would exceed it leaves the hot loop; the reference then moves up to the
-  // chunk's row max, O and l are rescaled, and the chunk is redone from the
-  // same LDS stage. O and l always share m, so the result is exact whatever
-  // the schedule; the hot loop touches the accumulators only through MFMAs.
+  // bf16 P and the fp32 sums keep their relative precision). Otherwise m
+  // moves up to the chunk's row max first and O and l are rescaled (rare:
+  // m starts at the row max of chunk 0). O and l always share m, so the
+  // result is exact whatever the schedule.
   constexpr float kHeadroom = 16.0f;
-  float cmax = 0.f;
-  auto compute = [&](const bf16* kb, const bf16* vb) -> bool {
-    f32x16 sx;
-    scores(kb, sx);
-    float mq = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sx[e] = sx[e] * scale_log2 - m;
-      mq = fmaxf(mq, sx[e]);
-    }
-    cmax = mq;
-    if (__any(mq > kHeadroom)) return true;
-    bf16x8 pf[2];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (bf16)__builtin_amdgcn_exp2f(sx[e]);
-    // Row sums of the rounded P (the weights O is formed with), by MFMA.
-    lacc = mfma32_bf16(ones, pf[0], lacc);
-    lacc = mfma32_bf16(ones, pf[1], lacc);
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
-      const int dd = 32 * mb + n32;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vb + (dd * 4 + ((2 * s2 + hf) ^ vunit_swz(dd))) * 8);
-        acc[mb] = mfma32_bf16(a, pf[s2], acc[mb]);
-      }
-    }
-    return false;
-  };
   const int nch = 2 * L;
-  constexpr int kPerWave = (C::KINS + C::VINS) / 2;   // this wave's loads per chunk
-  // Prologue: chunks 0 .. NST-2 in flight; the row max of chunk 0 sets the
-  // initial reference.
-#pragma unroll
-  for (int c0 = 0; c0 < C::NST - 1; ++c0)
-    if (c0 < nch) issue(c0);
+  f32x16 sx;
   if (nch > 0) {
+    issue_k(0);
+#pragma unroll
+    for (int c0 = 0; c0 < C::VST - 1; ++c0)
+      if (c0 < nch) issue_v(c0);
+#pragma unroll
+    for (int c0 = 1; c0 < C::KST; ++c0)
+      if (c0 < nch) issue_k(c0);
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    f32x16 sx;
-    scores(kbuf, sx);
+    sx = scores(kbuf);
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sx[e]);
     m = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
   }
-  // Per chunk: wait for this wave's loads of chunk c (later chunks may stay in
-  // flight), barrier (both halves are then in LDS, and both waves are done
-  // with the stage about to be refilled), issue chunk c + NST - 1, compute
-  // chunk c. A redo after a rescale skips the wait / barrier / issue, so both
-  // waves still pass the same barriers. The barrier is a bare s_barrier: a
-  // fenced one would also wait for the prefetches in flight.
-  int c = 0;
-  bool redo = false;
-  for (;;) {
-    for (; c < nch; ++c) {
-      if (!redo) {
-        if (C::NST == 3 && c + 1 < nch) wait_vmcnt<kPerWave>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (c + C::NST - 1 < nch) issue(c + C::NST - 1);
-      }
-      redo = false;
-      const int st = c % C::NST;
-      if (compute(kbuf + st * C::KUNITS * 8, vbuf + st * C::VUNITS * 8)) { redo = true; break; }
+  for (int c = 0; c < nch; ++c) {
+    if (c > 0) {
+      if (c - 1 + C::KST < nch) wait_vmcnt<C::KINS / 2>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
     }
-    if (!redo) break;
-    // Rare path: move the query's reference up to its row max over this
-    // chunk (the two lanes of a query agree through one exchange); rescale.
-    const float mx = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float shift = fmaxf(mx, 0.0f);
-    const float alpha = __builtin_amdgcn_exp2f(-shift);
-    m += shift;
-    lacc *= alpha;
+    if (c + C::VST - 1 < nch) issue_v(c + C::VST - 1);
+    if (c + C::KST < nch) issue_k(c + C::KST);
+
+    float mq = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) acc[mb] *= alpha;
+    for (int e = 0; e < 16; ++e) mq = fmaxf(mq, sx[e]);
+    mq = mq * scale_log2 - m;
+    if (__any(mq > kHeadroom)) {
+      const float shift = fmaxf(fmaxf(mq, __shfl_xor(mq, 32, 64)), 0.0f);
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      m += shift;
+      lsum *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) acc[mb] *= alpha;
+    }
+    // Scores of chunk c + 1 (when c + 1 == nch they read a stale stage and
+    // are discarded) interleaved with P of chunk c, then O^T += V_c^T P^T.
+    // Every LDS fragment is read first, so LDS latency is paid once; the
+    // scheduling fences keep each score MFMA next to an independent slice of
+    // the softmax, which runs while the MFMA does.
+    const bf16* kb = kbuf + ((c + 1) % C::KST) * C::KUNITS * 8;
+    const bf16* vb = vbuf + (c % C::VST) * C::VUNITS * 8;
+    bf16x8 kf[C::KS], vf[C::MB][2];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8*>(kb + (n32 * C::U + ((2 * ks + hf) ^ kswz<C::U>(n32))) * 8);
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb) {
+      const int dd = 32 * mb + n32;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        vf[mb][s2] = *reinterpret_cast<const bf16x8*>(vb + (dd * 4 + ((2 * s2 + hf) ^ vunit_swz(dd))) * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sn;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sn[e] = 0.f;
+    bf16x8 pf[2];
+    float lp[2] = {0.f, 0.f};
+    constexpr int PER = 16 / C::KS;   // softmax entries per score MFMA
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      sn = mfma32_bf16(kf[ks], qf[ks], sn);
+#pragma unroll
+      for (int t = 0; t < PER; ++t) {
+        const int e = ks * PER + t;
+        const float pv = __builtin_amdgcn_exp2f(sx[e] * scale_log2 - m);
+        lp[e & 1] += pv;
+        pf[e >> 3][e & 7] = (bf16)pv;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lsum += lp[0] + lp[1];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        acc[mb] = mfma32_bf16(vf[mb][s2], pf[s2], acc[mb]);
+      }
+    sx = sn;
   }
 
   // Epilogue: lane holds O^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query].
-  const float lt = lacc[0];   // every row of the ones-MFMA holds the full sum
+  const float lt = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const long n = tok0 + qrow;
   if (lse_f != nullptr && hf == 0) lse_f[n] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
