@@ -18,7 +18,8 @@
 //                     applied to the operand as it is loaded).
 // Selecting on the logits picks the same set as selecting on A_c: the
 // softmax is increasing within a row. S_c is Nc^2 fp32 per (b, h) of
-// workspace, written once and read twice (279 MB at the 720p latent).
+// workspace (rows padded to a multiple of 4 floats), written once and read
+// twice (279 MB at the 720p latent).
 #include "vsa_kernels.h"
 
 namespace vsa {
@@ -36,137 +37,192 @@ __device__ __forceinline__ uint32_t fkey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// ---------------------------------------------------------------------------
-// fp32 "NT" GEMM tile: C[m][n] = sum_k A[m][k] * B[n][k], A and B row-major
-// with k contiguous. One wave computes a 32x32 tile as 2x2 16x16x4 MFMA
-// blocks; lane (r = lane%16, g = lane/16) feeds, for every group of four
-// k-steps t, the float4 A[r][16t + 4g .. +3] (k-step 4t+e contracts k =
-// 16t + 4g + e), so loads are 16 bytes and four lanes cover 64 contiguous
-// bytes of a row. Rows/columns beyond the matrix read as zero.
-// ---------------------------------------------------------------------------
-struct OperandQK {   // scores: A = Q_c, B = K_c, k = channel
-  const float* p;
-  int rows, ld;
-  __device__ float4 ld4(int r, int k) const {
-    if (r >= rows) return make_float4(0.f, 0.f, 0.f, 0.f);
-    return *reinterpret_cast<const float4*>(p + (long)r * ld + k);
+// S[bh][i][j] = scale * Q_c[i] . K_c[j] (fp32 16x16x4 MFMAs). A workgroup
+// of 4 waves owns a 64x64 tile, each wave a 32x32 quarter as 2x2 MFMA
+// blocks. Lane (r = lane%16, g = lane/16) holds, for channel group t, the
+// float4 Q_c[row r][16t + 4g .. +3] (and likewise K_c), so four lanes cover 64
+// contiguous bytes of a row; k-step 4t+e contracts channel 16t + 4g + e. All
+// operands of the tile are loaded before the first MFMA.
+template <int D>
+__global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restrict__ qc,
+                                                            const float* __restrict__ kc, float* __restrict__ s,
+                                                            int Nc, int ld, float scale) {
+  constexpr int KT = D / 16;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const long bh = blockIdx.z;
+  const int m0 = blockIdx.y * 64 + (w >> 1) * 32, n0 = blockIdx.x * 64 + (w & 1) * 32;
+  const float* Q = qc + bh * (long)Nc * D;
+  const float* K = kc + bh * (long)Nc * D;
+  float4 av[2][KT], bv[2][KT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ra = m0 + 16 * i + r, rb = n0 + 16 * i + r;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      av[i][t] = ra < Nc ? *reinterpret_cast<const float4*>(Q + (long)ra * D + 16 * t + 4 * g)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      bv[i][t] = rb < Nc ? *reinterpret_cast<const float4*>(K + (long)rb * D + 16 * t + 4 * g)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
-};
-
-struct OperandP {    // P = exp(S - LSE) rows, k = key cube (masked beyond Nc)
-  const float* s;
-  const float* lse;
-  int rows, nk, ld;
-  __device__ float4 ld4(int r, int k) const {
-    if (r >= rows) return make_float4(0.f, 0.f, 0.f, 0.f);
-    const float* row = s + (long)r * ld + k;
-    const float l = lse[r];
-    float4 o;
-    o.x = k + 0 < nk ? __expf(row[0] - l) : 0.f;
-    o.y = k + 1 < nk ? __expf(row[1] - l) : 0.f;
-    o.z = k + 2 < nk ? __expf(row[2] - l) : 0.f;
-    o.w = k + 3 < nk ? __expf(row[3] - l) : 0.f;
-    return o;
-  }
-};
-
-struct OperandVt {   // V_c^T: element (n = channel, k = key) = V_c[k][n]
-  const float* v;
-  int d, nk;
-  __device__ float4 ld4(int n, int k) const {
-    float4 o;
-    o.x = k + 0 < nk ? v[(long)(k + 0) * d + n] : 0.f;
-    o.y = k + 1 < nk ? v[(long)(k + 1) * d + n] : 0.f;
-    o.z = k + 2 < nk ? v[(long)(k + 2) * d + n] : 0.f;
-    o.w = k + 3 < nk ? v[(long)(k + 3) * d + n] : 0.f;
-    return o;
-  }
-};
-
-template <typename OA, typename OB>
-__device__ __forceinline__ void gemm_nt_32x32(const OA& A, const OB& B, int m0, int n0, int K, f32x4 acc[2][2]) {
-  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const int k = k0 + 4 * g;
-    const float4 a0 = A.ld4(m0 + r, k), a1 = A.ld4(m0 + 16 + r, k);
-    const float4 b0 = B.ld4(n0 + r, k), b1 = B.ld4(n0 + 16 + r, k);
-    const float av[2][4] = {{a0.x, a0.y, a0.z, a0.w}, {a1.x, a1.y, a1.z, a1.w}};
-    const float bv[2][4] = {{b0.x, b0.y, b0.z, b0.w}, {b1.x, b1.y, b1.z, b1.w}};
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const float a4[2][4] = {{av[0][t].x, av[0][t].y, av[0][t].z, av[0][t].w},
+                            {av[1][t].x, av[1][t].y, av[1][t].z, av[1][t].w}};
+    const float b4[2][4] = {{bv[0][t].x, bv[0][t].y, bv[0][t].z, bv[0][t].w},
+                            {bv[1][t].x, bv[1][t].y, bv[1][t].z, bv[1][t].w}};
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16_f32(av[i][e], bv[j][e], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16_f32(a4[i][e], b4[j][e], acc[i][j]);
   }
-}
-
-// S[bh][i][j] = scale * Q_c[i] . K_c[j]; workgroup = 4 waves = 64x64 tile.
-template <int D>
-__global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restrict__ qc,
-                                                            const float* __restrict__ kc, float* __restrict__ s,
-                                                            int Nc, float scale) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
-  const long bh = blockIdx.z;
-  const int m0 = blockIdx.y * 64 + (w >> 1) * 32, n0 = blockIdx.x * 64 + (w & 1) * 32;
-  const OperandQK A{qc + bh * (long)Nc * D, Nc, D}, B{kc + bh * (long)Nc * D, Nc, D};
-  f32x4 acc[2][2];
-  gemm_nt_32x32(A, B, m0, n0, D, acc);
-  float* S = s + bh * (long)Nc * Nc;
+  float* S = s + bh * (long)Nc * ld;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = n0 + 16 * j + c16;
+      const int col = n0 + 16 * j + r;
       if (col >= Nc) continue;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = m0 + 16 * i + 4 * g + rr;
-        if (row < Nc) S[(long)row * Nc + col] = acc[i][j][rr] * scale;
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + 16 * i + 4 * g + e;
+        if (row < Nc) S[(long)row * ld + col] = acc[i][j][e] * scale;
       }
     }
 }
 
-// O_c[bh][i][dd] = sum_j exp(S[i][j] - LSE[i]) V_c[j][dd]; 64 rows x 64 channels per workgroup.
+// O_c[bh][i][:] = sum_j exp(S[i][j] - LSE[i]) V_c[j][:]. A workgroup owns 32
+// rows and every channel; keys go in chunks of 32 through LDS, double
+// buffered: P = exp(S - LSE) (the softmax applied as the tile is staged) and
+// V_c transposed (channel-major), so that for 16x16x4 MFMA k-step s a lane of
+// lane group g contracts key 8g + s and reads its eight A values (a P row)
+// and eight B values (a V_c column) as two 16-byte LDS reads each. Wave w
+// owns channels [16*CB*w, 16*CB*(w+1)) of both 16-row blocks.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_pv_kernel(const float* __restrict__ s, const float* __restrict__ lse,
-                                                        const float* __restrict__ vc, float* __restrict__ oc, int Nc) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
-  const long bh = blockIdx.z;
-  const int m0 = blockIdx.y * 64 + (w >> 1) * 32, n0 = blockIdx.x * 64 + (w & 1) * 32;
-  const OperandP A{s + bh * (long)Nc * Nc, lse + bh * Nc, Nc, Nc, Nc};
-  const OperandVt B{vc + bh * (long)Nc * D, D, Nc};
-  f32x4 acc[2][2];
-  gemm_nt_32x32(A, B, m0, n0, (Nc + 15) & ~15, acc);
+                                                        const float* __restrict__ vc, float* __restrict__ oc, int Nc,
+                                                        int ld) {
+  constexpr int KC = 32, RP = KC + 4;           // keys per chunk, LDS row pitch (floats)
+  constexpr int CB = D / 64;                     // 16-channel blocks per wave
+  constexpr int VF4 = KC * D / 4 / 256;          // V float4 loads per thread per chunk
+  __shared__ __attribute__((aligned(16))) float Pl[2][32][RP];
+  __shared__ __attribute__((aligned(16))) float Vl[2][D][RP];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const long bh = blockIdx.y;
+  const int r0 = blockIdx.x * 32;
+  const float* S = s + bh * (long)Nc * ld;
+  const float* Vc = vc + bh * (long)Nc * D;
+  // staging roles: P row pi, keys 4pq .. 4pq+3
+  const int pi = tid >> 3, pq = tid & 7;
+  const bool prow = r0 + pi < Nc;
+  const float plse = prow ? lse[bh * Nc + r0 + pi] : 0.f;
+  float4 pr, vr[VF4];
+  auto load = [&](int k0) {
+    const int kk = k0 + 4 * pq;
+    pr = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (prow && kk < Nc) {
+      pr = *reinterpret_cast<const float4*>(S + (long)(r0 + pi) * ld + kk);   // ld % 4 == 0
+      pr.x = __expf(pr.x - plse);
+      pr.y = kk + 1 < Nc ? __expf(pr.y - plse) : 0.f;
+      pr.z = kk + 2 < Nc ? __expf(pr.z - plse) : 0.f;
+      pr.w = kk + 3 < Nc ? __expf(pr.w - plse) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < VF4; ++j) {
+      const int f = tid + 256 * j, kap = f / (D / 4), c4 = f % (D / 4);
+      vr[j] = k0 + kap < Nc ? *reinterpret_cast<const float4*>(Vc + (long)(k0 + kap) * D + 4 * c4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store = [&](int b) {
+    *reinterpret_cast<float4*>(&Pl[b][pi][4 * pq]) = pr;
+#pragma unroll
+    for (int j = 0; j < VF4; ++j) {
+      const int f = tid + 256 * j, kap = f / (D / 4), c4 = f % (D / 4);
+      Vl[b][4 * c4 + 0][kap] = vr[j].x;
+      Vl[b][4 * c4 + 1][kap] = vr[j].y;
+      Vl[b][4 * c4 + 2][kap] = vr[j].z;
+      Vl[b][4 * c4 + 3][kap] = vr[j].w;
+    }
+  };
+  f32x4 acc[2][CB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nchunk = (Nc + KC - 1) / KC;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int b = c & 1;
+    if (c + 1 < nchunk) load((c + 1) * KC);
+    float av[2][8], bv[CB][8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float4 x0 = *reinterpret_cast<const float4*>(&Pl[b][16 * rb + r][8 * g]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&Pl[b][16 * rb + r][8 * g + 4]);
+      av[rb][0] = x0.x; av[rb][1] = x0.y; av[rb][2] = x0.z; av[rb][3] = x0.w;
+      av[rb][4] = x1.x; av[rb][5] = x1.y; av[rb][6] = x1.z; av[rb][7] = x1.w;
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = 16 * (CB * w + cb) + r;
+      const float4 x0 = *reinterpret_cast<const float4*>(&Vl[b][col][8 * g]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&Vl[b][col][8 * g + 4]);
+      bv[cb][0] = x0.x; bv[cb][1] = x0.y; bv[cb][2] = x0.z; bv[cb][3] = x0.w;
+      bv[cb][4] = x1.x; bv[cb][5] = x1.y; bv[cb][6] = x1.z; bv[cb][7] = x1.w;
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mfma16_f32(av[rb][st], bv[cb][st], acc[rb][cb]);
+    if (c + 1 < nchunk) {
+      store(b ^ 1);   // b ^ 1 was last read in chunk c - 1, which ended with a barrier
+      __syncthreads();
+    }
+  }
   float* O = oc + bh * (long)Nc * D;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + 16 * j + c16;
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = 16 * (CB * w + cb) + r;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = m0 + 16 * i + 4 * g + rr;
-        if (row < Nc) O[(long)row * D + col] = acc[i][j][rr];
+      for (int e = 0; e < 4; ++e) {
+        const int row = r0 + 16 * rb + 4 * g + e;
+        if (row < Nc) O[(long)row * D + col] = acc[rb][cb][e];
       }
     }
 }
 
 // One wave per row: LSE_c, and with topk > 0 the ascending top-K list.
+// Selection works on the order-preserving integer keys of the logits: a
+// radix select finds the key of the K-th largest logit, 8 bits per pass from
+// the most significant bit in which the row's keys differ (the bits above it
+// are shared by every key, and skipping them keeps the first histogram
+// spread over many buckets, so the LDS atomics rarely collide). Then every
+// key above it and the first (K - #above) keys equal to it, in ascending cube
+// order, are taken.
 template <int NCH>
 __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restrict__ s, float* __restrict__ lse,
                                                           int32_t* __restrict__ idx, int32_t* __restrict__ len,
-                                                          long rows, int Nc, int topk, int stride) {
+                                                          long rows, int Nc, int ld, int topk, int stride) {
   __shared__ int hist_all[4][256];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + w;
   if (row >= rows) return;   // wave-uniform; no block barrier below
-  const float* srow = s + row * Nc;
+  const float* srow = s + row * ld;
+  const int nused = (Nc + 63) >> 6;   // register slots holding any cube
   float v[NCH];
   float mx = -INFINITY;
 #pragma unroll
@@ -178,24 +234,43 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
   mx = wave_max(mx);
   float sm = 0.f;
 #pragma unroll
-  for (int t = 0; t < NCH; ++t) sm += __expf(v[t] - mx);   // exp(-inf) = 0 for padding
+  for (int t = 0; t < NCH; ++t) {
+    if (t >= nused) break;
+    sm += __expf(v[t] - mx);   // exp(-inf) = 0 for padding
+  }
   sm = wave_sum(sm);
   if (lane == 0) lse[row] = mx + __logf(sm);
   if (topk <= 0) return;
 
   int* h = hist_all[w];
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t key[NCH];
+  uint32_t kmin = 0xFFFFFFFFu;
 #pragma unroll
-  for (int t = 0; t < NCH; ++t) key[t] = (t * 64 + lane) < Nc ? fkey(v[t]) : 0u;
-  uint32_t prefix = 0u, pmask = 0u;
+  for (int t = 0; t < NCH; ++t) {
+    const bool valid = t * 64 + lane < Nc;
+    key[t] = valid ? fkey(v[t]) : 0u;
+    if (valid) kmin = min(kmin, key[t]);
+  }
+  kmin = wave_min_u32(kmin);
+  const uint32_t diff = kmin ^ fkey(mx);
+  // Keys matching `prefix` on the bits of `pmask` are the candidates.
+  uint32_t prefix = kmin, pmask = 0xFFFFFFFFu;
   int krem = topk;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  int hi = diff == 0u ? -1 : 31 - __clz(diff);   // highest free bit
+  if (hi >= 0) {
+    pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+    prefix = kmin & pmask;
+  }
+  while (hi >= 0) {
+    const int nb = min(8, hi + 1), shift = hi - nb + 1;
+    const uint32_t dmask = (1u << nb) - 1u;
     for (int b = lane; b < 256; b += 64) h[b] = 0;
     wave_sync();
 #pragma unroll
-    for (int t = 0; t < NCH; ++t)
-      if ((t * 64 + lane) < Nc && (key[t] & pmask) == prefix) atomicAdd(&h[(key[t] >> shift) & 255u], 1);
+    for (int t = 0; t < NCH; ++t) {
+      if (t >= nused) break;
+      if ((t * 64 + lane) < Nc && (key[t] & pmask) == prefix) atomicAdd(&h[(key[t] >> shift) & dmask], 1);
+    }
     wave_sync();
     const int b0 = h[4 * lane], b1 = h[4 * lane + 1], b2 = h[4 * lane + 2], b3 = h[4 * lane + 3];
     const int mine = b0 + b1 + b2 + b3;
@@ -218,16 +293,19 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
     const int fb = __shfl(found, src, 64);
     const int fbefore = __shfl(before, src, 64);
     prefix |= (uint32_t)fb << shift;
-    pmask |= 0xFFu << shift;
+    pmask |= dmask << shift;
     krem -= fbefore;
+    hi -= nb;
     wave_sync();
   }
   // prefix is the key of the K-th largest logit: take every larger one and
   // the first krem equal ones in ascending cube order.
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t* out = idx + row * (long)stride;
   int taken = 0, eq_seen = 0;
 #pragma unroll
   for (int t = 0; t < NCH; ++t) {
+    if (t >= nused) break;
     const int j = t * 64 + lane;
     const bool valid = j < Nc;
     const bool gt = valid && key[t] > prefix;
@@ -246,33 +324,35 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
 }
 
 int coarse_max_cubes() { return kCoarseMaxCubes; }
+int coarse_ld(int Nc) { return (Nc + 3) & ~3; }
 
 template <int NCH>
 static void launch_rows(const Launch& L, const float* s, float* lse, int32_t* idx, int32_t* len) {
   const long rows = (long)L.BH * L.g.Nc;
   hipLaunchKernelGGL((coarse_rows_kernel<NCH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream, s, lse,
-                     idx, len, rows, L.g.Nc, L.topk, L.stride);
+                     idx, len, rows, L.g.Nc, coarse_ld(L.g.Nc), L.topk, L.stride);
 }
 
 hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, const float* vc, float* oc,
                          float* lse, int32_t* idx, int32_t* len, float* s_scratch) {
-  const int Nc = L.g.Nc;
+  const int Nc = L.g.Nc, ld = coarse_ld(Nc);
   const int t64 = (Nc + 63) / 64;
   const dim3 block(256);
   if (L.D == 64)
     hipLaunchKernelGGL((coarse_scores_kernel<64>), dim3(t64, t64, L.BH), block, 0, L.stream, qc, kc, s_scratch, Nc,
-                       L.scale);
+                       ld, L.scale);
   else
     hipLaunchKernelGGL((coarse_scores_kernel<128>), dim3(t64, t64, L.BH), block, 0, L.stream, qc, kc, s_scratch, Nc,
-                       L.scale);
+                       ld, L.scale);
   if (Nc <= 256) launch_rows<4>(L, s_scratch, lse, idx, len);
   else if (Nc <= 512) launch_rows<8>(L, s_scratch, lse, idx, len);
   else if (Nc <= 1024) launch_rows<16>(L, s_scratch, lse, idx, len);
   else launch_rows<32>(L, s_scratch, lse, idx, len);
+  const dim3 pv_grid((Nc + 31) / 32, L.BH);
   if (L.D == 64)
-    hipLaunchKernelGGL((coarse_pv_kernel<64>), dim3(1, t64, L.BH), block, 0, L.stream, s_scratch, lse, vc, oc, Nc);
+    hipLaunchKernelGGL((coarse_pv_kernel<64>), pv_grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nc, ld);
   else
-    hipLaunchKernelGGL((coarse_pv_kernel<128>), dim3(2, t64, L.BH), block, 0, L.stream, s_scratch, lse, vc, oc, Nc);
+    hipLaunchKernelGGL((coarse_pv_kernel<128>), pv_grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nc, ld);
   return hipGetLastError();
 }
 

@@ -114,7 +114,7 @@ FwdWs carve_fwd_ws(const Dims& d, void* base) {
   FwdWs w;
   w.vt = d.elem == 2 ? c.take<bf16>(d.BH * d.N * d.D) : nullptr;
   w.order = c.take<int32_t>(d.BH * d.Nc);
-  w.s = c.take<float>(d.BH * d.Nc * d.Nc);
+  w.s = c.take<float>(d.BH * d.Nc * (size_t)coarse_ld((int)d.Nc));
   const size_t pooled = d.BH * d.Nc * d.D;
   w.qc = c.take<float>(pooled);
   w.kc = c.take<float>(pooled);

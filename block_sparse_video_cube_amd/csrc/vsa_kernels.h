@@ -22,7 +22,9 @@ hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void
 hipError_t launch_ttile(const Launch& L, const bf16* x, bf16* xt);
 
 int coarse_max_cubes();
-// s_scratch: B*heads*Nc*Nc fp32 (the coarse logits).
+// Row pitch (floats) of the coarse logits: Nc rounded up to a multiple of 4.
+int coarse_ld(int Nc);
+// s_scratch: B*heads*Nc*coarse_ld(Nc) fp32 (the coarse logits).
 hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, const float* vc, float* oc,
                          float* lse, int32_t* idx, int32_t* len, float* s_scratch);
 
