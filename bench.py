@@ -80,6 +80,88 @@ def cpu_baseline(workload: str, heads: list[int]) -> dict:
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
+def train_measure(name: str, steps: int, warmup: int) -> dict:
+    """Forward (saving for backward) + backward of one workload: whole-call
+    times with HIP events on the launch stream, and the backward's stages
+    through their entry points."""
+    import numpy as np
+    import torch
+    import workloads as WL
+    import block_sparse_video_cube_amd as V
+
+    w = WL.get(name)
+    x = WL.make_inputs(w.name)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(a, dtype):
+        return torch.from_numpy(a).to("cuda:0").to(dtype).contiguous()
+
+    q, k, v, gc, gf = (dev(x[n], td) for n in ("q", "k", "v", "g_c", "g_f"))
+    if "d_o" in x:
+        d_o = dev(x["d_o"], td)
+    else:   # timing only: a seeded device draw of the same shape
+        gen = torch.Generator(device="cuda:0").manual_seed(8)
+        d_o = torch.randn(q.shape, generator=gen, device="cuda:0", dtype=torch.float32).to(td)
+    p = V.Problem(w.B, w.heads, w.T, w.H, w.W, w.head_dim, dtype=w.dtype, topk=w.topk, list_stride=w.list_stride)
+    if w.topk == 0:
+        idx, lens = dev(x["idx"], torch.int32), dev(x["len"], torch.int32)
+    else:
+        idx = torch.empty((w.B, w.heads, w.Nc, p.stride), dtype=torch.int32, device=q.device)
+        lens = torch.empty((w.B, w.heads, w.Nc), dtype=torch.int32, device=q.device)
+    del x
+    ws_f = V.workspace(p, q)
+    ws_b = V.workspace(p, q, training=True)
+    o = torch.empty_like(q)
+    saved = torch.empty(V.saved_bytes(p), dtype=torch.uint8, device=q.device)
+
+    def fwd():
+        V.forward(p, q, k, v, gc, gf, idx=idx, lens=lens, ws=ws_f, out=o, saved=saved)
+
+    def bwd():
+        return V.backward(p, q, k, v, gc, gf, idx, lens, saved, d_o, ws=ws_b)
+
+    def timed(fn, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(n):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    fwd_ms = timed(fwd, steps)
+    bwd_ms = timed(bwd, steps)
+
+    # Backward stages through their entry points (same kernels as vsa_backward).
+    sv = V.saved_views(p, saved)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        cb = V.combine_backward(p, d_o, sv["o_c"], sv["o_f"], gc, gf, ws=ws_b)
+        e[1].record()
+        off, k2q = V.index_transpose(p, idx, lens)
+        e[2].record()
+        dqc, dkc, dvc = V.coarse_backward(p, sv["q_c"], sv["k_c"], sv["v_c"], sv["o_c"], sv["lse_c"], cb["d_o_c"], ws_b)
+        e[3].record()
+        V.fine_backward(p, q, k, v, idx, lens, off, k2q, sv["lse_f"], cb["d_o_f"], cb["delta"], dqc, dkc, dvc, ws_b)
+        e[4].record()
+    torch.cuda.synchronize()
+    st = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(4)]
+    pairs = int(lens.sum().item())
+    fl_f = 4.0 * 64 * 64 * w.head_dim * pairs
+    fl_b = 10.0 * 64 * 64 * w.head_dim * pairs
+    return {"workload": w.name, "steps": steps, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_tflops": round(fl_f / (fwd_ms * 1e-3) / 1e12, 2), "bwd_tflops": round(fl_b / (bwd_ms * 1e-3) / 1e12, 2),
+            "computed_block_pairs": pairs,
+            "bwd_stages_ms": {"combine_bwd": round(st[0], 4), "index_transpose": round(st[1], 4),
+                              "coarse_bwd": round(st[2], 4), "fine_bwd (T-tiles, dq, dk/dv, pool bwd)": round(st[3], 4)},
+            "fine_bwd_tflops": round(fl_b / (st[3] * 1e-3) / 1e12, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +175,8 @@ def main() -> int:
                          "(for counter collection); copy: a plain device copy of --copy-mib MiB, the "
                          "calibration of the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--copy-mib", type=int, default=2048)
+    ap.add_argument("--train", default="train_bf16_16x32x32_varlen,bf16_720p_24x44x80",
+                    help="comma-separated workloads whose forward + backward are timed ('' = none)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -241,6 +325,11 @@ def main() -> int:
     }
     log(f"forward {ms_step:.3f} ms/step = {value:.1f} TFLOP/s; pool {stage_ms[0]:.3f} ms, "
         f"coarse {stage_ms[1]:.3f} ms, fine+combine {stage_ms[2]:.3f} ms ({achieved:.1f} TFLOP/s)")
+    line["train"] = []
+    for name in [t for t in args.train.split(",") if t]:
+        log(f"timing forward + backward of {name}")
+        line["train"].append(train_measure(name, max(1, min(args.steps, 10)), 2))
+        log(f"  {line['train'][-1]}")
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_heads} head(s)")
         line["cpu_baseline"] = cpu_baseline(w.name, list(range(args.cpu_heads)))

@@ -103,20 +103,45 @@ def _pooled(p: Problem):
 
 
 def forward(p: Problem, q, k, v, g_c=None, g_f=None, idx=None, lens=None, training: bool = False,
-            ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
-    """Whole VSA forward. Returns (o, idx, lens, saved); saved is None unless training."""
+            ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            saved: Optional[torch.Tensor] = None):
+    """Whole VSA forward. Returns (o, idx, lens, saved); saved is None unless
+    training or a saved buffer (uint8, saved_bytes(p)) is passed in."""
     if p.topk > 0:
         idx = _empty((p.B, p.heads, p.Nc, p.stride), torch.int32, q) if idx is None else idx
         lens = _empty((p.B, p.heads, p.Nc), torch.int32, q) if lens is None else lens
     elif idx is None or lens is None:
         raise ValueError("explicit-list mode (topk == 0) needs idx and lens")
     o = _empty(_raster(p), p.torch_dtype, q) if out is None else out
-    saved = torch.empty(saved_bytes(p), dtype=torch.uint8, device=q.device) if training else None
+    if saved is None and training:
+        saved = torch.empty(saved_bytes(p), dtype=torch.uint8, device=q.device)
     ws = workspace(p, q) if ws is None else ws
     check(lib().vsa_forward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(g_c), _ptr(g_f), _ptr(idx),
                             _ptr(lens), _ptr(o), _ptr(saved), _ptr(ws), ws.numel(), _stream(q.device)),
           "vsa_forward")
     return o, idx, lens, saved
+
+
+def saved_views(p: Problem, saved: torch.Tensor) -> dict:
+    """Views of the tensors in a training forward's saved buffer, in the
+    order the header documents (each region starts on a 256-byte boundary)."""
+    off = 0
+
+    def take(shape, dtype):
+        nonlocal off
+        n = 1
+        for e in shape:
+            n *= e
+        esz = torch.empty((), dtype=dtype).element_size()
+        t = saved[off:off + n * esz].view(dtype).view(shape)
+        off += (n * esz + 255) // 256 * 256
+        return t
+
+    out = {name: take(_pooled(p), torch.float32) for name in ("q_c", "k_c", "v_c", "o_c")}
+    out["lse_c"] = take((p.B, p.heads, p.Nc), torch.float32)
+    out["lse_f"] = take((p.B, p.heads, p.T, p.H, p.W), torch.float32)
+    out["o_f"] = take(_raster(p), p.torch_dtype)
+    return out
 
 
 def backward(p: Problem, q, k, v, g_c, g_f, idx, lens, saved, d_o, ws: Optional[torch.Tensor] = None):

@@ -93,8 +93,10 @@ int32_t vsa_max_cubes(void);
 size_t vsa_workspace_bytes(const vsa_problem* p, int32_t training);
 
 /* Bytes of the `saved` buffer a training forward fills and vsa_backward
- * reads: pooled Q_c/K_c/V_c, O_c and LSE_c (fp32), O_f (dtype) and LSE_f
- * (fp32). 0 if p is invalid. */
+ * reads. 0 if p is invalid. Layout, each region starting on a 256-byte
+ * boundary of the buffer: Q_c, K_c, V_c, O_c (fp32 [B, heads, Nc,
+ * head_dim] each), LSE_c (fp32 [B, heads, Nc]), LSE_f (fp32 [B, heads, T, H,
+ * W]), O_f (dtype, raster). */
 size_t vsa_saved_bytes(const vsa_problem* p);
 
 /* Whole forward, steps 1-5 above.
