@@ -143,7 +143,7 @@ def train_measure(name: str, steps: int, warmup: int) -> dict:
         e[0].record()
         cb = V.combine_backward(p, d_o, sv["o_c"], sv["o_f"], gc, gf, ws=ws_b)
         e[1].record()
-        off, k2q = V.index_transpose(p, idx, lens)
+        off, k2q = V.index_transpose(p, idx, lens, ws=ws_b)
         e[2].record()
         dqc, dkc, dvc = V.coarse_backward(p, sv["q_c"], sv["k_c"], sv["v_c"], sv["o_c"], sv["lse_c"], cb["d_o_c"], ws_b)
         e[3].record()

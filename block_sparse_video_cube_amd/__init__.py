@@ -221,11 +221,12 @@ def combine_backward(p: Problem, d_o, o_c, o_f, g_c=None, g_f=None, ws: Optional
     return dict(dg_c=dgc, dg_f=dgf, d_o_f=dof, delta=delta, d_o_c=doc)
 
 
-def index_transpose(p: Problem, idx, lens):
+def index_transpose(p: Problem, idx, lens, ws: Optional[torch.Tensor] = None):
     off = _empty((p.B, p.heads, p.Nc + 1), torch.int32, idx)
     k2q = _empty((p.B, p.heads, p.Nc * p.stride), torch.int32, idx)
-    check(lib().vsa_index_transpose(ctypes.byref(p.c()), _ptr(idx), _ptr(lens), _ptr(off), _ptr(k2q),
-                                    _stream(idx.device)), "vsa_index_transpose")
+    ws = workspace(p, idx, training=True) if ws is None else ws
+    check(lib().vsa_index_transpose(ctypes.byref(p.c()), _ptr(idx), _ptr(lens), _ptr(off), _ptr(k2q), _ptr(ws),
+                                    ws.numel(), _stream(idx.device)), "vsa_index_transpose")
     return off, k2q
 
 

@@ -1,4 +1,5 @@
-// Backward of VSA (steps 1, 2 and 4) and the list utilities.
+// Backward of VSA (steps 1 and 4) and the list utilities; the coarse
+// attention's backward is with its forward GEMMs.
 //
 // The pages state that VSA trains end to end through one differentiable
 // kernel and that the coarse output takes part in the result, so the pooled
@@ -18,29 +19,37 @@
 namespace vsa {
 
 // ------------------------------------------------------------ list helpers
-// Is cube j in the ascending list `row` of length n? (binary search)
-__device__ __forceinline__ bool list_has(const int32_t* row, int n, int j) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const int v = row[mid];
-    if (v == j) return true;
-    if (v < j) lo = mid + 1; else hi = mid;
-  }
-  return false;
+// Index transpose through a key-major bitmask: bit i of row j of `bits`
+// (W = ceil(Nc / 32) words per row) is set when query cube i lists key cube
+// j. Counting a row's bits gives the length of j's list, and walking them
+// writes it in ascending order, so the result is deterministic.
+__global__ __launch_bounds__(256) void k2q_zero_kernel(uint32_t* __restrict__ bits, long n) {
+  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) bits[e] = 0u;
 }
 
-__global__ __launch_bounds__(256) void k2q_count_kernel(const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ len, int32_t* __restrict__ cnt,
-                                                        int Nc, int stride) {
+__global__ __launch_bounds__(256) void k2q_bits_kernel(const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ len, uint32_t* __restrict__ bits,
+                                                       int Nc, int stride, int W) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;   // entry of this head's lists
+  const long bh = blockIdx.y;
+  if (e >= (long)Nc * stride) return;
+  const int i = (int)(e / stride), t = (int)(e - (long)i * stride);
+  const long row = bh * Nc + i;
+  if (t >= min(max(len[row], 0), stride)) return;
+  const int j = idx[row * stride + t];
+  if (j < 0 || j >= Nc) return;
+  atomicOr(&bits[(bh * Nc + j) * W + (i >> 5)], 1u << (i & 31));
+}
+
+// cnt[bh][j + 1] = number of query cubes listing j (cnt[bh][0] is set by the scan).
+__global__ __launch_bounds__(256) void k2q_count_kernel(const uint32_t* __restrict__ bits, int32_t* __restrict__ cnt,
+                                                        int Nc, int W) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   const long bh = blockIdx.y;
   if (j >= Nc) return;
+  const uint32_t* r = bits + (bh * Nc + j) * W;
   int c = 0;
-  for (int i = 0; i < Nc; ++i) {
-    const long row = bh * Nc + i;
-    c += list_has(idx + row * stride, min(max(len[row], 0), stride), j) ? 1 : 0;
-  }
+  for (int w = 0; w < W; ++w) c += __popc(r[w]);
   cnt[bh * (Nc + 1) + j + 1] = c;
 }
 
@@ -66,29 +75,39 @@ __global__ __launch_bounds__(256) void k2q_scan_kernel(int32_t* __restrict__ off
   for (int j = b0; j < b1; ++j) { run += o[j + 1]; o[j + 1] = run; }
 }
 
-__global__ __launch_bounds__(256) void k2q_fill_kernel(const int32_t* __restrict__ idx,
-                                                       const int32_t* __restrict__ len,
+__global__ __launch_bounds__(256) void k2q_fill_kernel(const uint32_t* __restrict__ bits,
                                                        const int32_t* __restrict__ off, int32_t* __restrict__ k2q,
-                                                       int Nc, int stride) {
+                                                       int Nc, int stride, int W) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   const long bh = blockIdx.y;
   if (j >= Nc) return;
-  int pos = off[bh * (Nc + 1) + j];
-  const int end = off[bh * (Nc + 1) + j + 1];
+  const uint32_t* r = bits + (bh * Nc + j) * W;
   int32_t* out = k2q + bh * (long)Nc * stride;
-  for (int i = 0; i < Nc && pos < end; ++i) {
-    const long row = bh * Nc + i;
-    if (list_has(idx + row * stride, min(max(len[row], 0), stride), j)) out[pos++] = i;
+  int pos = off[bh * (Nc + 1) + j];
+  for (int w = 0; w < W; ++w) {
+    uint32_t word = r[w];
+    while (word != 0u) {
+      out[pos++] = 32 * w + __ffs(word) - 1;
+      word &= word - 1u;
+    }
   }
 }
 
+int k2q_bits_words(int Nc) { return (Nc + 31) / 32; }
+
 hipError_t launch_index_transpose(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* k2q_off,
-                                  int32_t* k2q) {
-  const int Nc = L.g.Nc;
+                                  int32_t* k2q, uint32_t* bits) {
+  const int Nc = L.g.Nc, W = k2q_bits_words(Nc);
+  const long nbits = (long)L.BH * Nc * W;
+  hipLaunchKernelGGL(k2q_zero_kernel, dim3((unsigned)min((nbits + 255) / 256, 65536L)), dim3(256), 0, L.stream,
+                     bits, nbits);
+  const long entries = (long)Nc * L.stride;
+  hipLaunchKernelGGL(k2q_bits_kernel, dim3((unsigned)((entries + 255) / 256), L.BH), dim3(256), 0, L.stream, idx,
+                     len, bits, Nc, L.stride, W);
   const dim3 grid((Nc + 255) / 256, L.BH);
-  hipLaunchKernelGGL(k2q_count_kernel, grid, dim3(256), 0, L.stream, idx, len, k2q_off, Nc, L.stride);
+  hipLaunchKernelGGL(k2q_count_kernel, grid, dim3(256), 0, L.stream, bits, k2q_off, Nc, W);
   hipLaunchKernelGGL(k2q_scan_kernel, dim3(L.BH), dim3(256), 0, L.stream, k2q_off, Nc);
-  hipLaunchKernelGGL(k2q_fill_kernel, grid, dim3(256), 0, L.stream, idx, len, k2q_off, k2q, Nc, L.stride);
+  hipLaunchKernelGGL(k2q_fill_kernel, grid, dim3(256), 0, L.stream, bits, k2q_off, k2q, Nc, L.stride, W);
   return hipGetLastError();
 }
 
@@ -115,108 +134,6 @@ hipError_t launch_validate_lists(const Launch& L, const int32_t* idx, const int3
   const long rows = (long)L.BH * L.g.Nc;
   hipLaunchKernelGGL(validate_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, L.stream, idx, len,
                      flag, rows, L.g.Nc, L.stride);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------ coarse backward
-// Row pass, one workgroup per (b, h, query cube i):
-//   P_ij = exp(S_ij - LSE_i), dA_ij = dO_c[i] . V_c[j], dS_ij = P_ij (dA_ij - D_i),
-//   D_i = dO_c[i] . O_c[i], dQ_c[i] = s * sum_j dS_ij K_c[j].
-// P and dS rows go to scratch for the column pass.
-template <int D>
-__global__ __launch_bounds__(256) void coarse_bwd_rows_kernel(const float* __restrict__ qc,
-                                                              const float* __restrict__ kc,
-                                                              const float* __restrict__ vc,
-                                                              const float* __restrict__ oc,
-                                                              const float* __restrict__ lse,
-                                                              const float* __restrict__ doc, float* __restrict__ dqc,
-                                                              float* __restrict__ pbuf, float* __restrict__ dsbuf,
-                                                              int Nc, float scale) {
-  extern __shared__ float sm[];
-  float* qrow = sm;            // [D]
-  float* drow = sm + D;        // [D]
-  float* dsrow = sm + 2 * D;   // [Nc]
-  __shared__ float red[4];
-  const int tid = threadIdx.x;
-  const int i = blockIdx.x;
-  const long bh = blockIdx.y;
-  const long base = bh * (long)Nc * D;
-  if (tid < D) {
-    qrow[tid] = qc[base + (long)i * D + tid];
-    drow[tid] = doc[base + (long)i * D + tid];
-  }
-  // D_i
-  float pd = 0.f;
-  if (tid < D) pd = doc[base + (long)i * D + tid] * oc[base + (long)i * D + tid];
-  pd = wave_sum(pd);
-  if ((tid & 63) == 0) red[tid >> 6] = pd;
-  __syncthreads();
-  const float Di = red[0] + red[1] + red[2] + red[3];
-  const float li = lse[bh * Nc + i];
-  for (int j = tid; j < Nc; j += 256) {
-    const float* kr = kc + base + (long)j * D;
-    const float* vr = vc + base + (long)j * D;
-    float s = 0.f, da = 0.f;
-#pragma unroll 8
-    for (int d = 0; d < D; d += 4) {
-      const float4 k4 = *reinterpret_cast<const float4*>(kr + d);
-      const float4 v4 = *reinterpret_cast<const float4*>(vr + d);
-      s += qrow[d] * k4.x + qrow[d + 1] * k4.y + qrow[d + 2] * k4.z + qrow[d + 3] * k4.w;
-      da += drow[d] * v4.x + drow[d + 1] * v4.y + drow[d + 2] * v4.z + drow[d + 3] * v4.w;
-    }
-    const float p = __expf(s * scale - li);
-    const float ds = p * (da - Di);
-    pbuf[(bh * Nc + i) * (long)Nc + j] = p;
-    dsbuf[(bh * Nc + i) * (long)Nc + j] = ds;
-    dsrow[j] = ds;
-  }
-  __syncthreads();
-  if (tid < D) {
-    float acc = 0.f;
-    for (int j = 0; j < Nc; ++j) acc += dsrow[j] * kc[base + (long)j * D + tid];
-    dqc[base + (long)i * D + tid] = scale * acc;
-  }
-}
-
-// Column pass, one workgroup per (b, h, key cube j):
-//   dK_c[j] = s * sum_i dS_ij Q_c[i], dV_c[j] = sum_i P_ij dO_c[i].
-template <int D>
-__global__ __launch_bounds__(D) void coarse_bwd_cols_kernel(const float* __restrict__ qc,
-                                                            const float* __restrict__ doc,
-                                                            const float* __restrict__ pbuf,
-                                                            const float* __restrict__ dsbuf, float* __restrict__ dkc,
-                                                            float* __restrict__ dvc, int Nc, float scale) {
-  const int tid = threadIdx.x;
-  const int j = blockIdx.x;
-  const long bh = blockIdx.y;
-  const long base = bh * (long)Nc * D;
-  float dk = 0.f, dv = 0.f;
-  for (int i = 0; i < Nc; ++i) {
-    const long e = (bh * Nc + i) * (long)Nc + j;
-    dk += dsbuf[e] * qc[base + (long)i * D + tid];
-    dv += pbuf[e] * doc[base + (long)i * D + tid];
-  }
-  dkc[base + (long)j * D + tid] = scale * dk;
-  dvc[base + (long)j * D + tid] = dv;
-}
-
-hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, const float* vc,
-                             const float* oc, const float* lse, const float* doc, float* dqc, float* dkc,
-                             float* dvc, float* ds_scratch, float* p_scratch) {
-  const int Nc = L.g.Nc;
-  const dim3 grid(Nc, L.BH);
-  const size_t smem = (size_t)(2 * L.D + Nc) * sizeof(float);
-  if (L.D == 64) {
-    hipLaunchKernelGGL((coarse_bwd_rows_kernel<64>), grid, dim3(256), smem, L.stream, qc, kc, vc, oc, lse, doc,
-                       dqc, p_scratch, ds_scratch, Nc, L.scale);
-    hipLaunchKernelGGL((coarse_bwd_cols_kernel<64>), grid, dim3(64), 0, L.stream, qc, doc, p_scratch, ds_scratch,
-                       dkc, dvc, Nc, L.scale);
-  } else {
-    hipLaunchKernelGGL((coarse_bwd_rows_kernel<128>), grid, dim3(256), smem, L.stream, qc, kc, vc, oc, lse, doc,
-                       dqc, p_scratch, ds_scratch, Nc, L.scale);
-    hipLaunchKernelGGL((coarse_bwd_cols_kernel<128>), grid, dim3(128), 0, L.stream, qc, doc, p_scratch,
-                       ds_scratch, dkc, dvc, Nc, L.scale);
-  }
   return hipGetLastError();
 }
 

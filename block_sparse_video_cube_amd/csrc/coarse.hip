@@ -7,15 +7,16 @@
 // reading notes, key design 1 (A_c, O_c, row Top-K into mask M) and the
 // training section (softmax, Top-K and mask-to-index fused in one kernel).
 //
-// Three kernels per call, all fp32:
+// Three kernels per forward call, all fp32:
 //   1. coarse_scores: S = scale * Q_c K_c^T (fp32 MFMA GEMM) into workspace;
 //   2. coarse_rows:   one wave per row: row max / sum -> LSE_c, then the exact
 //                     top-K by a 4-pass radix select on the order-preserving
 //                     integer image of the logits (ties: smaller cube id) and
 //                     one ordered pass that writes the ascending index list
 //                     (softmax, top-K and mask-to-index in one kernel);
-//   3. coarse_pv:     O_c = exp(S - LSE_c) V_c (the same GEMM, the softmax
-//                     applied to the operand as it is loaded).
+//   3. coarse_gemm:   O_c = exp(S - LSE_c) V_c (an LDS-tiled GEMM, the
+//                     softmax applied to the operand as it is staged).
+// The backward of the coarse attention is here too; it shares these GEMMs.
 // Selecting on the logits picks the same set as selecting on A_c: the
 // softmax is increasing within a row. S_c is Nc^2 fp32 per (b, h) of
 // workspace (rows padded to a multiple of 4 floats), written once and read
@@ -37,35 +38,30 @@ __device__ __forceinline__ uint32_t fkey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// S[bh][i][j] = scale * Q_c[i] . K_c[j] (fp32 16x16x4 MFMAs). A workgroup
-// of 4 waves owns a 64x64 tile, each wave a 32x32 quarter as 2x2 MFMA
-// blocks. Lane (r = lane%16, g = lane/16) holds, for channel group t, the
-// float4 Q_c[row r][16t + 4g .. +3] (and likewise K_c), so four lanes cover 64
-// contiguous bytes of a row; k-step 4t+e contracts channel 16t + 4g + e. All
-// operands of the tile are loaded before the first MFMA.
+// One wave's 32x32 quarter of a 64x64 tile of an "NT" product C = A B^T with
+// A, B row-major [Nc][D] (fp32 16x16x4 MFMAs, 2x2 blocks). Lane (r =
+// lane%16, g = lane/16) holds, for channel group t, the float4 A[row r][16t +
+// 4g .. +3] (and likewise B), so four lanes cover 64 contiguous bytes of a
+// row; k-step 4t+e contracts channel 16t + 4g + e. All operands are loaded
+// before the first MFMA. Rows beyond Nc read as zero. acc[i][j][e] is
+// C[m0 + 16i + 4g + e][n0 + 16j + r].
 template <int D>
-__global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restrict__ qc,
-                                                            const float* __restrict__ kc, float* __restrict__ s,
-                                                            int Nc, int ld, float scale) {
+__device__ __forceinline__ void nt_tile(const float* __restrict__ A, const float* __restrict__ B, int Nc, int m0,
+                                        int n0, f32x4 acc[2][2]) {
   constexpr int KT = D / 16;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const long bh = blockIdx.z;
-  const int m0 = blockIdx.y * 64 + (w >> 1) * 32, n0 = blockIdx.x * 64 + (w & 1) * 32;
-  const float* Q = qc + bh * (long)Nc * D;
-  const float* K = kc + bh * (long)Nc * D;
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   float4 av[2][KT], bv[2][KT];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int ra = m0 + 16 * i + r, rb = n0 + 16 * i + r;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      av[i][t] = ra < Nc ? *reinterpret_cast<const float4*>(Q + (long)ra * D + 16 * t + 4 * g)
+      av[i][t] = ra < Nc ? *reinterpret_cast<const float4*>(A + (long)ra * D + 16 * t + 4 * g)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
-      bv[i][t] = rb < Nc ? *reinterpret_cast<const float4*>(K + (long)rb * D + 16 * t + 4 * g)
+      bv[i][t] = rb < Nc ? *reinterpret_cast<const float4*>(B + (long)rb * D + 16 * t + 4 * g)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -83,6 +79,18 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma16_f32(a4[i][e], b4[j][e], acc[i][j]);
   }
+}
+
+// S[bh][i][j] = scale * Q_c[i] . K_c[j]; a workgroup of 4 waves owns a 64x64 tile.
+template <int D>
+__global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restrict__ qc,
+                                                            const float* __restrict__ kc, float* __restrict__ s,
+                                                            int Nc, int ld, float scale) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const long bh = blockIdx.z;
+  const int m0 = blockIdx.y * 64 + (w >> 1) * 32, n0 = blockIdx.x * 64 + (w & 1) * 32;
+  f32x4 acc[2][2];
+  nt_tile<D>(qc + bh * (long)Nc * D, kc + bh * (long)Nc * D, Nc, m0, n0, acc);
   float* S = s + bh * (long)Nc * ld;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -98,58 +106,86 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
     }
 }
 
-// O_c[bh][i][:] = sum_j exp(S[i][j] - LSE[i]) V_c[j][:]. A workgroup owns 32
-// rows and every channel; keys go in chunks of 32 through LDS, double
-// buffered: P = exp(S - LSE) (the softmax applied as the tile is staged) and
-// V_c transposed (channel-major), so that for 16x16x4 MFMA k-step s a lane of
-// lane group g contracts key 8g + s and reads its eight A values (a P row)
-// and eight B values (a V_c column) as two 16-byte LDS reads each. Wave w
-// owns channels [16*CB*w, 16*CB*(w+1)) of both 16-row blocks.
-template <int D>
-__global__ __launch_bounds__(256) void coarse_pv_kernel(const float* __restrict__ s, const float* __restrict__ lse,
-                                                        const float* __restrict__ vc, float* __restrict__ oc, int Nc,
-                                                        int ld) {
-  constexpr int KC = 32, RP = KC + 4;           // keys per chunk, LDS row pitch (floats)
+// C[bh][i][:] = scale * sum_j A[i][j] B[j][:] over an Nc x Nc fp32 matrix M
+// (row pitch ld) and B [Nc][D]: A = M, or A = M^T with TRANS_A, and with EXP
+// A[i][j] = exp(M[i][j] - lse[i]) (the coarse softmax applied as the tile is
+// staged). A workgroup owns 32 rows of C and every channel; k goes in chunks
+// of 32 through LDS, double buffered: the A tile row-major and the B tile
+// transposed (channel-major), so that for 16x16x4 MFMA k-step s a lane of
+// lane group g contracts k = 8g + s and reads its eight A values and eight B
+// values as two 16-byte LDS reads each. Wave w owns channels
+// [16*CB*w, 16*CB*(w+1)) of both 16-row blocks.
+template <int D, bool TRANS_A, bool EXP>
+__global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restrict__ m, const float* __restrict__ lse,
+                                                          const float* __restrict__ b, float* __restrict__ c, int Nc,
+                                                          int ld, float scale) {
+  constexpr int KC = 32, RP = KC + 4;           // k per chunk, LDS row pitch (floats)
   constexpr int CB = D / 64;                     // 16-channel blocks per wave
-  constexpr int VF4 = KC * D / 4 / 256;          // V float4 loads per thread per chunk
-  __shared__ __attribute__((aligned(16))) float Pl[2][32][RP];
-  __shared__ __attribute__((aligned(16))) float Vl[2][D][RP];
+  constexpr int BF4 = KC * D / 4 / 256;          // B float4 loads per thread per chunk
+  static_assert(!(TRANS_A && EXP), "the softmax is applied along rows of M only");
+  __shared__ __attribute__((aligned(16))) float Al[2][32][RP];
+  __shared__ __attribute__((aligned(16))) float Bl[2][D][RP];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const long bh = blockIdx.y;
   const int r0 = blockIdx.x * 32;
-  const float* S = s + bh * (long)Nc * ld;
-  const float* Vc = vc + bh * (long)Nc * D;
-  // staging roles: P row pi, keys 4pq .. 4pq+3
-  const int pi = tid >> 3, pq = tid & 7;
-  const bool prow = r0 + pi < Nc;
-  const float plse = prow ? lse[bh * Nc + r0 + pi] : 0.f;
-  float4 pr, vr[VF4];
+  const float* M = m + bh * (long)Nc * ld;
+  const float* Bm = b + bh * (long)Nc * D;
+  // A staging role: without TRANS_A, row ai of the tile, k = 4aq .. 4aq+3
+  // (M[r0 + ai][k0 + 4aq ..]); with TRANS_A, k = ai of the chunk and tile rows
+  // 4aq .. 4aq+3 (M[k0 + ai][r0 + 4aq ..]), written transposed.
+  const int ai = tid >> 3, aq = tid & 7;
+  const bool arow = r0 + ai < Nc;
+  const float alse = (EXP && arow) ? lse[bh * Nc + r0 + ai] : 0.f;
+  float4 ar, br[BF4];
   auto load = [&](int k0) {
-    const int kk = k0 + 4 * pq;
-    pr = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (prow && kk < Nc) {
-      pr = *reinterpret_cast<const float4*>(S + (long)(r0 + pi) * ld + kk);   // ld % 4 == 0
-      pr.x = __expf(pr.x - plse);
-      pr.y = kk + 1 < Nc ? __expf(pr.y - plse) : 0.f;
-      pr.z = kk + 2 < Nc ? __expf(pr.z - plse) : 0.f;
-      pr.w = kk + 3 < Nc ? __expf(pr.w - plse) : 0.f;
+    ar = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!TRANS_A) {
+      const int kk = k0 + 4 * aq;
+      if (arow && kk < Nc) {
+        ar = *reinterpret_cast<const float4*>(M + (long)(r0 + ai) * ld + kk);   // ld % 4 == 0
+        if (EXP) {
+          ar.x = __expf(ar.x - alse);
+          ar.y = kk + 1 < Nc ? __expf(ar.y - alse) : 0.f;
+          ar.z = kk + 2 < Nc ? __expf(ar.z - alse) : 0.f;
+          ar.w = kk + 3 < Nc ? __expf(ar.w - alse) : 0.f;
+        } else {
+          if (kk + 1 >= Nc) ar.y = 0.f;
+          if (kk + 2 >= Nc) ar.z = 0.f;
+          if (kk + 3 >= Nc) ar.w = 0.f;
+        }
+      }
+    } else {
+      const int kk = k0 + ai, cc = r0 + 4 * aq;
+      if (kk < Nc && cc < Nc) {
+        ar = *reinterpret_cast<const float4*>(M + (long)kk * ld + cc);
+        if (cc + 1 >= Nc) ar.y = 0.f;
+        if (cc + 2 >= Nc) ar.z = 0.f;
+        if (cc + 3 >= Nc) ar.w = 0.f;
+      }
     }
 #pragma unroll
-    for (int j = 0; j < VF4; ++j) {
+    for (int j = 0; j < BF4; ++j) {
       const int f = tid + 256 * j, kap = f / (D / 4), c4 = f % (D / 4);
-      vr[j] = k0 + kap < Nc ? *reinterpret_cast<const float4*>(Vc + (long)(k0 + kap) * D + 4 * c4)
+      br[j] = k0 + kap < Nc ? *reinterpret_cast<const float4*>(Bm + (long)(k0 + kap) * D + 4 * c4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  auto store = [&](int b) {
-    *reinterpret_cast<float4*>(&Pl[b][pi][4 * pq]) = pr;
+  auto store = [&](int bb) {
+    if (!TRANS_A) {
+      *reinterpret_cast<float4*>(&Al[bb][ai][4 * aq]) = ar;
+    } else {
+      Al[bb][4 * aq + 0][ai] = ar.x;
+      Al[bb][4 * aq + 1][ai] = ar.y;
+      Al[bb][4 * aq + 2][ai] = ar.z;
+      Al[bb][4 * aq + 3][ai] = ar.w;
+    }
 #pragma unroll
-    for (int j = 0; j < VF4; ++j) {
+    for (int j = 0; j < BF4; ++j) {
       const int f = tid + 256 * j, kap = f / (D / 4), c4 = f % (D / 4);
-      Vl[b][4 * c4 + 0][kap] = vr[j].x;
-      Vl[b][4 * c4 + 1][kap] = vr[j].y;
-      Vl[b][4 * c4 + 2][kap] = vr[j].z;
-      Vl[b][4 * c4 + 3][kap] = vr[j].w;
+      Bl[bb][4 * c4 + 0][kap] = br[j].x;
+      Bl[bb][4 * c4 + 1][kap] = br[j].y;
+      Bl[bb][4 * c4 + 2][kap] = br[j].z;
+      Bl[bb][4 * c4 + 3][kap] = br[j].w;
     }
   };
   f32x4 acc[2][CB];
@@ -161,22 +197,22 @@ __global__ __launch_bounds__(256) void coarse_pv_kernel(const float* __restrict_
   load(0);
   store(0);
   __syncthreads();
-  for (int c = 0; c < nchunk; ++c) {
-    const int b = c & 1;
-    if (c + 1 < nchunk) load((c + 1) * KC);
+  for (int ch = 0; ch < nchunk; ++ch) {
+    const int bb = ch & 1;
+    if (ch + 1 < nchunk) load((ch + 1) * KC);
     float av[2][8], bv[CB][8];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const float4 x0 = *reinterpret_cast<const float4*>(&Pl[b][16 * rb + r][8 * g]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&Pl[b][16 * rb + r][8 * g + 4]);
+      const float4 x0 = *reinterpret_cast<const float4*>(&Al[bb][16 * rb + r][8 * g]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&Al[bb][16 * rb + r][8 * g + 4]);
       av[rb][0] = x0.x; av[rb][1] = x0.y; av[rb][2] = x0.z; av[rb][3] = x0.w;
       av[rb][4] = x1.x; av[rb][5] = x1.y; av[rb][6] = x1.z; av[rb][7] = x1.w;
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int col = 16 * (CB * w + cb) + r;
-      const float4 x0 = *reinterpret_cast<const float4*>(&Vl[b][col][8 * g]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&Vl[b][col][8 * g + 4]);
+      const float4 x0 = *reinterpret_cast<const float4*>(&Bl[bb][col][8 * g]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&Bl[bb][col][8 * g + 4]);
       bv[cb][0] = x0.x; bv[cb][1] = x0.y; bv[cb][2] = x0.z; bv[cb][3] = x0.w;
       bv[cb][4] = x1.x; bv[cb][5] = x1.y; bv[cb][6] = x1.z; bv[cb][7] = x1.w;
     }
@@ -186,12 +222,12 @@ __global__ __launch_bounds__(256) void coarse_pv_kernel(const float* __restrict_
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = mfma16_f32(av[rb][st], bv[cb][st], acc[rb][cb]);
-    if (c + 1 < nchunk) {
-      store(b ^ 1);   // b ^ 1 was last read in chunk c - 1, which ended with a barrier
+    if (ch + 1 < nchunk) {
+      store(bb ^ 1);   // bb ^ 1 was last read in chunk ch - 1, which ended with a barrier
       __syncthreads();
     }
   }
-  float* O = oc + bh * (long)Nc * D;
+  float* C = c + bh * (long)Nc * D;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -200,7 +236,7 @@ __global__ __launch_bounds__(256) void coarse_pv_kernel(const float* __restrict_
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = r0 + 16 * rb + 4 * g + e;
-        if (row < Nc) O[(long)row * D + col] = acc[rb][cb][e];
+        if (row < Nc) C[(long)row * D + col] = scale * acc[rb][cb][e];
       }
     }
 }
@@ -324,6 +360,19 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
 }
 
 int coarse_max_cubes() { return kCoarseMaxCubes; }
+
+// C = scale * op(M) B, see coarse_gemm_kernel.
+template <bool TRANS_A, bool EXP>
+static void launch_gemm(const Launch& L, const float* m, const float* lse, const float* b, float* c, float scale) {
+  const int Nc = L.g.Nc, ld = coarse_ld(Nc);
+  const dim3 grid((Nc + 31) / 32, L.BH);
+  if (L.D == 64)
+    hipLaunchKernelGGL((coarse_gemm_kernel<64, TRANS_A, EXP>), grid, dim3(256), 0, L.stream, m, lse, b, c, Nc, ld,
+                       scale);
+  else
+    hipLaunchKernelGGL((coarse_gemm_kernel<128, TRANS_A, EXP>), grid, dim3(256), 0, L.stream, m, lse, b, c, Nc,
+                       ld, scale);
+}
 int coarse_ld(int Nc) { return (Nc + 3) & ~3; }
 
 template <int NCH>
@@ -348,11 +397,86 @@ hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, cons
   else if (Nc <= 512) launch_rows<8>(L, s_scratch, lse, idx, len);
   else if (Nc <= 1024) launch_rows<16>(L, s_scratch, lse, idx, len);
   else launch_rows<32>(L, s_scratch, lse, idx, len);
-  const dim3 pv_grid((Nc + 31) / 32, L.BH);
-  if (L.D == 64)
-    hipLaunchKernelGGL((coarse_pv_kernel<64>), pv_grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nc, ld);
-  else
-    hipLaunchKernelGGL((coarse_pv_kernel<128>), pv_grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nc, ld);
+  launch_gemm<false, true>(L, s_scratch, lse, vc, oc, 1.0f);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ backward
+// Calculus of the coarse softmax attention (the top-K selection carries no
+// gradient): with P = exp(s * Q_c K_c^T - LSE_c) recomputed,
+//   dP = dO_c V_c^T, D_i = dO_c[i] . O_c[i], dS = P * (dP - D),
+//   dQ_c = s dS K_c, dK_c = s dS^T Q_c, dV_c = P^T dO_c.
+
+// D_i = dO_c[i] . O_c[i]; one wave per row.
+template <int D>
+__global__ __launch_bounds__(256) void coarse_bwd_delta_kernel(const float* __restrict__ doc,
+                                                               const float* __restrict__ oc, float* __restrict__ dc,
+                                                               long rows) {
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float a = 0.f;
+#pragma unroll
+  for (int d = lane; d < D; d += 64) a += doc[row * D + d] * oc[row * D + d];
+  a = wave_sum(a);
+  if (lane == 0) dc[row] = a;
+}
+
+// P and dS tiles (64x64 per workgroup): the scores GEMM and dP = dO_c V_c^T on
+// the same tile, then the softmax and its derivative, elementwise.
+template <int D>
+__global__ __launch_bounds__(256) void coarse_bwd_pds_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
+                                                             const float* __restrict__ vc, const float* __restrict__ doc,
+                                                             const float* __restrict__ lse, const float* __restrict__ dc,
+                                                             float* __restrict__ pbuf, float* __restrict__ dsbuf,
+                                                             int Nc, int ld, float scale) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const long bh = blockIdx.z;
+  const int m0 = blockIdx.y * 64 + (w >> 1) * 32, n0 = blockIdx.x * 64 + (w & 1) * 32;
+  const long base = bh * (long)Nc * D;
+  f32x4 sacc[2][2], pacc[2][2];
+  nt_tile<D>(qc + base, kc + base, Nc, m0, n0, sacc);
+  nt_tile<D>(doc + base, vc + base, Nc, m0, n0, pacc);
+  float* P = pbuf + bh * (long)Nc * ld;
+  float* DS = dsbuf + bh * (long)Nc * ld;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = m0 + 16 * i + 4 * g + e;
+      if (row >= Nc) continue;
+      const float l = lse[bh * Nc + row], dd = dc[bh * Nc + row];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + 16 * j + r;
+        if (col >= Nc) continue;
+        const float pv = __expf(sacc[i][j][e] * scale - l);
+        P[(long)row * ld + col] = pv;
+        DS[(long)row * ld + col] = pv * (pacc[i][j][e] - dd);
+      }
+    }
+}
+
+hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, const float* vc,
+                             const float* oc, const float* lse, const float* doc, float* dqc, float* dkc,
+                             float* dvc, float* ds_scratch, float* p_scratch, float* dc_scratch) {
+  const int Nc = L.g.Nc, ld = coarse_ld(Nc);
+  const long rows = (long)L.BH * Nc;
+  const int t64 = (Nc + 63) / 64;
+  if (L.D == 64) {
+    hipLaunchKernelGGL((coarse_bwd_delta_kernel<64>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream, doc,
+                       oc, dc_scratch, rows);
+    hipLaunchKernelGGL((coarse_bwd_pds_kernel<64>), dim3(t64, t64, L.BH), dim3(256), 0, L.stream, qc, kc, vc, doc,
+                       lse, dc_scratch, p_scratch, ds_scratch, Nc, ld, L.scale);
+  } else {
+    hipLaunchKernelGGL((coarse_bwd_delta_kernel<128>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream,
+                       doc, oc, dc_scratch, rows);
+    hipLaunchKernelGGL((coarse_bwd_pds_kernel<128>), dim3(t64, t64, L.BH), dim3(256), 0, L.stream, qc, kc, vc, doc,
+                       lse, dc_scratch, p_scratch, ds_scratch, Nc, ld, L.scale);
+  }
+  launch_gemm<false, false>(L, ds_scratch, nullptr, kc, dqc, L.scale);
+  launch_gemm<true, false>(L, ds_scratch, nullptr, qc, dkc, L.scale);
+  launch_gemm<true, false>(L, p_scratch, nullptr, doc, dvc, 1.0f);
   return hipGetLastError();
 }
 

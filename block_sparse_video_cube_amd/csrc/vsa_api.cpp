@@ -128,8 +128,9 @@ FwdWs carve_fwd_ws(const Dims& d, void* base) {
 // Backward workspace.
 struct BwdWs {
   bf16 *dof, *doft, *qt, *kt;
-  float *delta, *doc, *dqc, *dkc, *dvc, *p_scr, *ds_scr;
+  float *delta, *doc, *dqc, *dkc, *dvc, *p_scr, *ds_scr, *dc_scr;
   int32_t *k2q_off, *k2q;
+  uint32_t* k2q_bits;
   size_t bytes;
 };
 BwdWs carve_bwd_ws(const Dims& d, void* base) {
@@ -146,10 +147,13 @@ BwdWs carve_bwd_ws(const Dims& d, void* base) {
   w.dqc = c.take<float>(pooled);
   w.dkc = c.take<float>(pooled);
   w.dvc = c.take<float>(pooled);
-  w.p_scr = c.take<float>(d.BH * d.Nc * d.Nc);
-  w.ds_scr = c.take<float>(d.BH * d.Nc * d.Nc);
+  const size_t ldc = (size_t)coarse_ld((int)d.Nc);
+  w.p_scr = c.take<float>(d.BH * d.Nc * ldc);
+  w.ds_scr = c.take<float>(d.BH * d.Nc * ldc);
+  w.dc_scr = c.take<float>(d.BH * d.Nc);
   w.k2q_off = c.take<int32_t>(d.BH * (d.Nc + 1));
   w.k2q = c.take<int32_t>(d.BH * d.Nc * d.stride);
+  w.k2q_bits = c.take<uint32_t>(d.BH * d.Nc * (size_t)k2q_bits_words((int)d.Nc));
   w.bytes = c.off;
   return w;
 }
@@ -244,9 +248,9 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   L.stream = static_cast<hipStream_t>(stream);
   hipError_t e = launch_combine_bwd(L, d_o, s.oc, s.of, g_c, g_f, g_c ? dg_c : nullptr, g_f ? dg_f : nullptr,
                                     ws.dof, ws.delta, ws.doc, ws.doft);
-  if (e == hipSuccess) e = launch_index_transpose(L, idx, len, ws.k2q_off, ws.k2q);
+  if (e == hipSuccess) e = launch_index_transpose(L, idx, len, ws.k2q_off, ws.k2q, ws.k2q_bits);
   if (e == hipSuccess)
-    e = launch_coarse_bwd(L, s.qc, s.kc, s.vc, s.oc, s.lse_c, ws.doc, ws.dqc, ws.dkc, ws.dvc, ws.ds_scr, ws.p_scr);
+    e = launch_coarse_bwd(L, s.qc, s.kc, s.vc, s.oc, s.lse_c, ws.doc, ws.dqc, ws.dkc, ws.dvc, ws.ds_scr, ws.p_scr, ws.dc_scr);
   if (e == hipSuccess) e = launch_ttile(L, static_cast<const bf16*>(q), ws.qt);
   if (e == hipSuccess) e = launch_ttile(L, static_cast<const bf16*>(k), ws.kt);
   if (e == hipSuccess)
@@ -371,14 +375,17 @@ vsa_status vsa_combine_backward(const vsa_problem* p, const void* d_o, const flo
 }
 
 vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const int32_t* len, int32_t* k2q_off,
-                               int32_t* k2q, void* stream) {
+                               int32_t* k2q, void* workspace, size_t ws_bytes, void* stream) {
   Launch L;
-  vsa_status st = check_problem(p, &L, nullptr);
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
   if (st != VSA_OK) return st;
-  st = check_ptrs({{idx, true}, {len, true}, {k2q_off, true}, {k2q, true}});
+  st = check_ptrs({{idx, true}, {len, true}, {k2q_off, true}, {k2q, true}, {workspace, true}});
   if (st != VSA_OK) return st;
+  const BwdWs ws = carve_bwd_ws(d, workspace);
+  if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
   L.stream = static_cast<hipStream_t>(stream);
-  return hip_status(launch_index_transpose(L, idx, len, k2q_off, k2q));
+  return hip_status(launch_index_transpose(L, idx, len, k2q_off, k2q, ws.k2q_bits));
 }
 
 vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
@@ -421,7 +428,7 @@ vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const flo
   const BwdWs ws = carve_bwd_ws(d, workspace);
   if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
   L.stream = static_cast<hipStream_t>(stream);
-  return hip_status(launch_coarse_bwd(L, q_c, k_c, v_c, o_c, lse_c, d_o_c, dq_c, dk_c, dv_c, ws.ds_scr, ws.p_scr));
+  return hip_status(launch_coarse_bwd(L, q_c, k_c, v_c, o_c, lse_c, d_o_c, dq_c, dk_c, dv_c, ws.ds_scr, ws.p_scr, ws.dc_scr));
 }
 
 vsa_status vsa_check_lists_host(const vsa_problem* p, const int32_t* idx, const int32_t* len) {

@@ -45,11 +45,14 @@ hipError_t launch_combine_bwd(const Launch& L, const void* d_o, const float* oc,
                               const void* gc, const void* gf, void* dgc, void* dgf, void* dof,
                               float* delta, float* doc, bf16* doft);
 
+// bits: B*heads*Nc*k2q_bits_words(Nc) uint32 of scratch.
+int k2q_bits_words(int Nc);
 hipError_t launch_index_transpose(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* k2q_off,
-                                  int32_t* k2q);
+                                  int32_t* k2q, uint32_t* bits);
+// Scratch: ds / p B*heads*Nc*coarse_ld(Nc) fp32, dc B*heads*Nc fp32.
 hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, const float* vc,
                              const float* oc, const float* lse, const float* doc, float* dqc, float* dkc,
-                             float* dvc, float* ds_scratch, float* p_scratch);
+                             float* dvc, float* ds_scratch, float* p_scratch, float* dc_scratch);
 hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const bf16* qt,
                            const bf16* kt, const int32_t* idx, const int32_t* len, const int32_t* k2q_off,
                            const int32_t* k2q, const float* lse_f, const bf16* dof, const bf16* doft,

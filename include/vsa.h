@@ -192,9 +192,11 @@ vsa_status vsa_combine_backward(const vsa_problem* p, const void* d_o, const flo
 /* Index transpose for the backward: k2q_off int32 [B, heads, Nc + 1] and
  * k2q int32 [B, heads, Nc * list_stride]: for key cube j the query cubes i
  * whose list holds j, ascending, at k2q[(b,h) * Nc * list_stride +
- * k2q_off[(b,h)][j] ... k2q_off[(b,h)][j+1]). */
+ * k2q_off[(b,h)][j] ... k2q_off[(b,h)][j+1]). Uses a bitmask in the
+ * workspace (ws_bytes >= vsa_workspace_bytes(p, 1)). */
 vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const int32_t* len,
-                               int32_t* k2q_off, int32_t* k2q, void* stream);
+                               int32_t* k2q_off, int32_t* k2q, void* workspace, size_t ws_bytes,
+                               void* stream);
 
 /* Backward of step 4 and of the pooling: dq, dk, dv (dtype, raster) =
  * fine-attention gradient + (dq_c, dk_c, dv_c)[cube] / 64, where the pooled
