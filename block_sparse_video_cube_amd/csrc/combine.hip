@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // Backward of the combine, one workgroup per (b, h, cube):
 //   dg_c = dO * O_c[c], dg_f = dO * O_f, d_o_f = dO * G_f (rounded to T),
 //   delta[token] = sum_ch d_o_f * O_f, d_o_c[c] = sum over the cube of dO * G_c,
-//   and (bf16, optional) the T-tile of d_o_f.
+//   and (bf16, optional) the chunk tiles of d_o_f.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ d_o, const float* __restrict__ oc, const T* __restrict__ of, const T* __restrict__ gc,
@@ -96,16 +96,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     for (int r = 0; r < RPP; ++r) s += part[r][tid];
     doc[(bh * g.Nc + c) * D + tid] = s;
   }
-  if (doft != nullptr) {
-    bf16* dst = doft + (bh * g.Nc + c) * (long)D * kTile;
-    for (int w = tid; w < D * 8; w += 256) {
-      const int dd = w >> 3, j = w & 7;
-      bf16x8 r;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = tile[tslot(8 * j + e)][dd];
-      *reinterpret_cast<bf16x8*>(dst + dd * kTile + 8 * j) = r;
-    }
-  }
+  if (doft != nullptr) store_chunk_tiles<D, VPITCH>(tile, doft + (bh * g.Nc + c) * (long)D * kTile, tid, 256);
 }
 
 hipError_t launch_combine(const Launch& L, const float* oc, const void* of, const void* gc, const void* gf,

@@ -1,0 +1,358 @@
+// Backward of step 4 (fine block-sparse attention) and of the pooling.
+//
+// The pages state that VSA trains end to end through one differentiable
+// kernel (VSA summary page, paperlayer.ai arXiv 2505.13389, abstract and
+// section 2); the top-K mask is piecewise constant and held fixed. The
+// formulas are the calculus of softmax attention: with P = exp(s*q.k - LSE),
+//   dV = P^T dO, dP = dO V^T, dS = P * (dP - delta), delta = rowsum(dO * O),
+//   dQ = s * dS K, dK = s * dS^T Q,
+// and the mean-pool spreads dX_c[c] / 64 over the cube's tokens, added here.
+//
+// Two kernels, both deterministic (no atomics), in the style of the forward:
+// a workgroup of two waves owns one cube, wave w its tokens 32w .. 32w+31,
+// one per lane (column) of 32x32x16 bf16 MFMAs, and walks a list of partner
+// cubes in 32-token chunks staged in LDS by direct-to-LDS loads (each wave
+// issues half; the next chunk loads while this one is computed).
+//  * dQ, per query cube i over its list of key cubes (the forward's list):
+//      S^T = K_c Q^T, dP^T = V_c dO^T        A = K / V row tiles, B = the
+//                                            lane's Q / dO row (registers)
+//      dS^T = P^T * (dP^T - delta)            LSE and delta are lane scalars
+//      dQ^T += K_c^T dS^T                     A = K chunk tile, B = dS^T
+//  * dK and dV, per key cube j over the query cubes whose lists hold j (the
+//    transposed lists), longest list first:
+//      S = Q_c K^T, dP = dO_c V^T            A = Q / dO row tiles, B = the
+//                                            lane's K / V row (registers)
+//      dS = P * (dP - delta)                 LSE and delta per row (query)
+//      dV^T += dO_c^T P, dK^T += Q_c^T dS     A = dO / Q chunk tiles
+#include "fine_common.h"
+#include "vsa_kernels.h"
+
+namespace vsa {
+
+// Processing order of the key cubes of every (b, h) for the dK / dV kernel:
+// descending length of their transposed lists, ties by cube id, so the
+// longest walks start first. One workgroup per (b, h): a bitonic sort of
+// ((Nc - count) << 32 | cube) keys in LDS.
+__global__ __launch_bounds__(1024) void order_by_count_kernel(const int32_t* __restrict__ k2q_off,
+                                                              int32_t* __restrict__ order, int Nc, int pow2) {
+  __shared__ unsigned long long key[2048];
+  const long bh = blockIdx.x;
+  const int32_t* off = k2q_off + bh * (Nc + 1);
+  for (int e = threadIdx.x; e < pow2; e += 1024) {
+    unsigned long long kv = ~0ull;
+    if (e < Nc) {
+      const int cnt = max(off[e + 1] - off[e], 0);
+      kv = ((unsigned long long)(uint32_t)max(Nc - cnt, 0) << 32) | (uint32_t)e;
+    }
+    key[e] = kv;
+  }
+  __syncthreads();
+  for (int kk = 2; kk <= pow2; kk <<= 1)
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int e = threadIdx.x; e < pow2; e += 1024) {
+        const int p = e ^ jj;
+        if (p > e) {
+          const unsigned long long x = key[e], y = key[p];
+          const bool up = (e & kk) == 0;
+          if ((x > y) == up) { key[e] = y; key[p] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  for (int e = threadIdx.x; e < Nc; e += 1024) order[bh * Nc + e] = (int32_t)(key[e] & 0xffffffffu);
+}
+
+template <int D>
+__global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ kct,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
+    const float* __restrict__ lse_f, const bf16* __restrict__ dof, const float* __restrict__ delta,
+    const float* __restrict__ dqc, bf16* __restrict__ dq, Grid g, int stride, float scale) {
+  using G = ChunkGeom<D>;
+  __shared__ __attribute__((aligned(16))) bf16 rk[2][G::RUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 rv[2][G::RUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 tk[2][G::TUNITS * 8];
+
+  const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = slot / g.Nc;
+  const int i = order != nullptr ? order[slot] : slot - bh * g.Nc;
+  const int item = bh * g.Nc + i;
+  const long tok0 = (long)bh * g.N;
+  // Lists are validated by contract; the clamps only keep a malformed list
+  // from reading outside the tensors.
+  const int L = min(max(len[item], 0), stride);
+  const int32_t* list = idx + (long)item * stride;
+
+  // This lane's query: token (2wv + n32/16, (n32/4)%4, n32%4) of cube i.
+  const long n = tok0 + cube_row(g, i, 2 * wv + (n32 >> 4), (n32 >> 2) & 3) + (n32 & 3);
+  bf16x8 qf[G::KS], df[G::KS];
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) {
+    qf[ks] = *reinterpret_cast<const bf16x8*>(q + n * D + ks * 16 + hf * 8);
+    df[ks] = *reinterpret_cast<const bf16x8*>(dof + n * D + ks * 16 + hf * 8);
+  }
+  const float sl2 = scale * kLog2e;
+  const float lse2 = lse_f[n] * kLog2e, dl = delta[n];
+  f32x16 acc[G::MB];
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
+
+  uint32_t roff[G::RINS / 2], toff[G::TINS / 2];
+  row_tile_offsets<D>(g, wv, lane, roff);
+  chunk_tile_offsets<D>(wv, lane, toff);
+  const uint32_t rhalf = (uint32_t)(2 * g.H * g.W * D) * 2u, thalf = (uint32_t)(D * 32) * 2u;
+  const char* Kb = reinterpret_cast<const char*>(k + tok0 * D);
+  const char* Vb = reinterpret_cast<const char*>(v + tok0 * D);
+  const char* Tb = reinterpret_cast<const char*>(kct + (long)bh * g.Nc * D * kTile);
+  // Byte offsets of the list's cubes, 64 entries at a time, one per lane.
+  uint32_t rcube = 0, tcube = 0;
+  auto cubes = [&](int t0) {
+    const int t = t0 + lane;
+    int j = t < L ? list[t] : 0;
+    j = (j >= 0 && j < g.Nc) ? j : 0;
+    rcube = (uint32_t)cube_row(g, j, 0, 0) * (uint32_t)(D * 2);
+    tcube = (uint32_t)j * (uint32_t)(D * kTile * 2);
+  };
+  const uint32_t rkb = lds_addr(rk), rvb = lds_addr(rv), tkb = lds_addr(tk);
+  auto issue = [&](int c) {
+    const int e = c >> 1, h = c & 1, st = c & 1;
+    if ((e & 63) == 0 && h == 0) cubes(e);
+    const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + (h ? rhalf : 0u);
+    const uint32_t tc = __builtin_amdgcn_readlane(tcube, e & 63) + (h ? thalf : 0u);
+    issue_row_tile<D>(uniform_ptr(Kb + rc), roff, rkb + st * (G::RUNITS * 16), wv);
+    issue_row_tile<D>(uniform_ptr(Vb + rc), roff, rvb + st * (G::RUNITS * 16), wv);
+    issue_chunk_tile<D>(uniform_ptr(Tb + tc), toff, tkb + st * (G::TUNITS * 16), wv);
+  };
+
+  // Per chunk: wait for this wave's loads, barrier (both halves are in LDS
+  // and both waves are done with the other stage), issue the next chunk,
+  // compute this one.
+  const int nch = 2 * L;
+  if (nch > 0) issue(0);
+  for (int c = 0; c < nch; ++c) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (c + 1 < nch) issue(c + 1);
+    const int st = c & 1;
+    bf16x8 kf[G::KS], vf[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+      kf[ks] = row_frag<D>(rk[st], n32, hf, ks);
+      vf[ks] = row_frag<D>(rv[st], n32, hf, ks);
+    }
+    f32x16 sx, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { sx[e] = 0.f; dp[e] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+      sx = mfma32_bf16(kf[ks], qf[ks], sx);
+      dp = mfma32_bf16(vf[ks], df[ks], dp);
+    }
+    bf16x8 sf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2);
+      sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl));
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb) acc[mb] = mfma32_bf16(chunk_frag(tk[st], 32 * mb + n32, hf, s2), sf[s2], acc[mb]);
+  }
+
+  // lane holds dQ^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query]
+  const float* dqc_i = dqc + ((long)bh * g.Nc + i) * D;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const int ch = 32 * mb + 8 * jq + 4 * hf;
+      const float4 c4 = *reinterpret_cast<const float4*>(dqc_i + ch);
+      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+      bf16x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = (bf16)(scale * acc[mb][4 * jq + r] + cv[r] * (1.0f / kTile));
+      *reinterpret_cast<bf16x4*>(dq + n * D + ch) = w;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ qct, const bf16* __restrict__ doct, const int32_t* __restrict__ k2q_off,
+    const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
+    const bf16* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dkc,
+    const float* __restrict__ dvc, bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, int stride, float scale) {
+  using G = ChunkGeom<D>;
+  __shared__ __attribute__((aligned(16))) bf16 rq[2][G::RUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 rd[2][G::RUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 tq[2][G::TUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 td[2][G::TUNITS * 8];
+
+  const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slot = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = slot / g.Nc;
+  const int j = order != nullptr ? order[slot] : slot - bh * g.Nc;
+  const long tok0 = (long)bh * g.N;
+  const int32_t* offs = k2q_off + (long)bh * (g.Nc + 1);
+  const int t0 = min(max(offs[j], 0), g.Nc * stride), t1 = min(max(offs[j + 1], t0), g.Nc * stride);
+  const int32_t* list = k2q + (long)bh * g.Nc * stride + t0;
+  const int L = t1 - t0;
+
+  // This lane's key: token (2wv + n32/16, (n32/4)%4, n32%4) of cube j.
+  const long n = tok0 + cube_row(g, j, 2 * wv + (n32 >> 4), (n32 >> 2) & 3) + (n32 & 3);
+  bf16x8 kf[G::KS], vf[G::KS];
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) {
+    kf[ks] = *reinterpret_cast<const bf16x8*>(k + n * D + ks * 16 + hf * 8);
+    vf[ks] = *reinterpret_cast<const bf16x8*>(v + n * D + ks * 16 + hf * 8);
+  }
+  const float sl2 = scale * kLog2e;
+  f32x16 adk[G::MB], adv[G::MB];
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { adk[mb][e] = 0.f; adv[mb][e] = 0.f; }
+
+  uint32_t roff[G::RINS / 2], toff[G::TINS / 2];
+  row_tile_offsets<D>(g, wv, lane, roff);
+  chunk_tile_offsets<D>(wv, lane, toff);
+  const uint32_t rhalf = (uint32_t)(2 * g.H * g.W * D) * 2u, thalf = (uint32_t)(D * 32) * 2u;
+  const char* Qb = reinterpret_cast<const char*>(q + tok0 * D);
+  const char* Db = reinterpret_cast<const char*>(dof + tok0 * D);
+  const char* TQb = reinterpret_cast<const char*>(qct + (long)bh * g.Nc * D * kTile);
+  const char* TDb = reinterpret_cast<const char*>(doct + (long)bh * g.Nc * D * kTile);
+  // Per lane, for 64 list entries at a time: the partner cube, its first
+  // row's byte offset and its chunk tiles' byte offset.
+  int icube = 0;
+  uint32_t rcube = 0, tcube = 0;
+  auto cubes = [&](int e0) {
+    const int t = e0 + lane;
+    int ii = t < L ? list[t] : 0;
+    ii = (ii >= 0 && ii < g.Nc) ? ii : 0;
+    icube = ii;
+    rcube = (uint32_t)cube_row(g, ii, 0, 0) * (uint32_t)(D * 2);
+    tcube = (uint32_t)ii * (uint32_t)(D * kTile * 2);
+  };
+  const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd), tqb = lds_addr(tq), tdb = lds_addr(td);
+  // LSE and delta of the chunk's query rows this lane's accumulator holds:
+  // rows 8m + 4hf + r (m, r = 0..3) = token (2h + m/2, (2m + hf)%4, r).
+  float4 lsn[4], dln[4];
+  auto issue = [&](int c) {
+    const int e = c >> 1, h = c & 1, st = c & 1;
+    if ((e & 63) == 0 && h == 0) cubes(e);
+    const int ii = __builtin_amdgcn_readlane(icube, e & 63);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const long r = tok0 + cube_row(g, ii, 2 * h + (m >> 1), (2 * m + hf) & 3);
+      lsn[m] = *reinterpret_cast<const float4*>(lse_f + r);
+      dln[m] = *reinterpret_cast<const float4*>(delta + r);
+    }
+    const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + (h ? rhalf : 0u);
+    const uint32_t tc = __builtin_amdgcn_readlane(tcube, e & 63) + (h ? thalf : 0u);
+    issue_row_tile<D>(uniform_ptr(Qb + rc), roff, rqb + st * (G::RUNITS * 16), wv);
+    issue_row_tile<D>(uniform_ptr(Db + rc), roff, rdb + st * (G::RUNITS * 16), wv);
+    issue_chunk_tile<D>(uniform_ptr(TQb + tc), toff, tqb + st * (G::TUNITS * 16), wv);
+    issue_chunk_tile<D>(uniform_ptr(TDb + tc), toff, tdb + st * (G::TUNITS * 16), wv);
+  };
+
+  const int nch = 2 * L;
+  if (nch > 0) issue(0);
+  for (int c = 0; c < nch; ++c) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    float lse2[16], dl[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      lse2[4 * m + 0] = lsn[m].x * kLog2e; lse2[4 * m + 1] = lsn[m].y * kLog2e;
+      lse2[4 * m + 2] = lsn[m].z * kLog2e; lse2[4 * m + 3] = lsn[m].w * kLog2e;
+      dl[4 * m + 0] = dln[m].x; dl[4 * m + 1] = dln[m].y; dl[4 * m + 2] = dln[m].z; dl[4 * m + 3] = dln[m].w;
+    }
+    if (c + 1 < nch) issue(c + 1);
+    const int st = c & 1;
+    bf16x8 qa[G::KS], da[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+      qa[ks] = row_frag<D>(rq[st], n32, hf, ks);
+      da[ks] = row_frag<D>(rd[st], n32, hf, ks);
+    }
+    f32x16 sx, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { sx[e] = 0.f; dp[e] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+      sx = mfma32_bf16(qa[ks], kf[ks], sx);
+      dp = mfma32_bf16(da[ks], vf[ks], dp);
+    }
+    bf16x8 pf[2], sf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);
+      pf[e >> 3][e & 7] = (bf16)p;
+      sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl[e]));
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int mb = 0; mb < G::MB; ++mb) {
+        adv[mb] = mfma32_bf16(chunk_frag(td[st], 32 * mb + n32, hf, s2), pf[s2], adv[mb]);
+        adk[mb] = mfma32_bf16(chunk_frag(tq[st], 32 * mb + n32, hf, s2), sf[s2], adk[mb]);
+      }
+  }
+
+  // lane holds d{K,V}^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its key]
+  const float* dkc_j = dkc + ((long)bh * g.Nc + j) * D;
+  const float* dvc_j = dvc + ((long)bh * g.Nc + j) * D;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const int ch = 32 * mb + 8 * jq + 4 * hf;
+      const float4 k4 = *reinterpret_cast<const float4*>(dkc_j + ch);
+      const float4 v4 = *reinterpret_cast<const float4*>(dvc_j + ch);
+      const float kcv[4] = {k4.x, k4.y, k4.z, k4.w}, vcv[4] = {v4.x, v4.y, v4.z, v4.w};
+      bf16x4 wk, wvv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        wk[r] = (bf16)(scale * adk[mb][4 * jq + r] + kcv[r] * (1.0f / kTile));
+        wvv[r] = (bf16)(adv[mb][4 * jq + r] + vcv[r] * (1.0f / kTile));
+      }
+      *reinterpret_cast<bf16x4*>(dk + n * D + ch) = wk;
+      *reinterpret_cast<bf16x4*>(dv + n * D + ch) = wvv;
+    }
+}
+
+hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_t* order) {
+  int pow2 = 1;
+  while (pow2 < L.g.Nc) pow2 <<= 1;
+  if (pow2 > 2048) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(order_by_count_kernel, dim3(L.BH), dim3(1024), 0, L.stream, k2q_off, order, L.g.Nc, pow2);
+  return hipGetLastError();
+}
+
+hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const bf16* qct,
+                           const bf16* kct, const int32_t* idx, const int32_t* len, const int32_t* qorder,
+                           const int32_t* k2q_off, const int32_t* k2q, const int32_t* korder, const float* lse_f,
+                           const bf16* dof, const bf16* doct, const float* delta, const float* dqc,
+                           const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv) {
+  const int nitems = L.BH * L.g.Nc;
+  if (L.D == 64) {
+    hipLaunchKernelGGL((fine_bwd_dq_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, kct, idx, len,
+                       qorder, lse_f, dof, delta, dqc, dq, L.g, L.stride, L.scale);
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, qct, doct,
+                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, dk, dv, L.g, L.stride, L.scale);
+  } else {
+    hipLaunchKernelGGL((fine_bwd_dq_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, kct, idx, len,
+                       qorder, lse_f, dof, delta, dqc, dq, L.g, L.stride, L.scale);
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, qct, doct,
+                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, dk, dv, L.g, L.stride, L.scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vsa

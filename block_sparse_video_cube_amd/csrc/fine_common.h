@@ -1,0 +1,102 @@
+// Device helpers shared by the fine-stage kernels (forward and backward):
+// direct-to-LDS loads of 32-token chunks, and the LDS layouts they fill.
+//
+// A chunk is half h of a cube (tokens 32h .. 32h+31 in cube order). Two LDS
+// layouts hold a chunk of one tensor (D channels):
+//  * row tile: 32 token rows of U = D/8 16-byte units; row kappa is token
+//    (t', y', x') = (2h + kappa/16, (kappa/4)%4, kappa%4), and its logical
+//    unit u (channels 8u .. 8u+7) sits at unit u ^ kswz(kappa), so 16
+//    consecutive rows read at one logical unit hit 16 distinct bank groups.
+//    Read as the A operand of a 32x32x16 MFMA (rows = tokens, k = channels).
+//    Loaded from the raster tensor.
+//  * chunk tile: D channel rows of 32 slots in the layout of the chunk-tile
+//    tensors (vsa_common.h); read as the A operand with k = tokens, whose
+//    B operand is a 32x32 accumulator. Loaded as a linear copy.
+#pragma once
+
+#include "vsa_common.h"
+
+namespace vsa {
+
+template <int D> struct ChunkGeom {
+  static constexpr int KS = D / 16;          // k-steps over channels
+  static constexpr int MB = D / 32;          // 32-channel blocks
+  static constexpr int U = D / 8;            // 16-byte units per token row
+  static constexpr int RUNITS = 32 * U;      // 16-byte units per row tile
+  static constexpr int TUNITS = D * 4;       // 16-byte units per chunk tile
+  static constexpr int RINS = RUNITS / 64;   // 1 KB loads per row tile
+  static constexpr int TINS = TUNITS / 64;   // 1 KB loads per chunk tile
+};
+
+template <int U> __device__ __forceinline__ int kswz(int kappa) { return (kappa * U / 16) % U; }
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds + 16*l. Issued as inline assembly so that the compiler does not
+// treat later LDS reads of other stages as dependent on it; completion is
+// tracked by the vector-memory counter and waited for explicitly (wait_vmcnt).
+// The compiler never uses M0 in these kernels (checked on the generated code).
+// The address is a wave-uniform base (SGPRs) plus a per-lane 32-bit byte
+// offset, so issuing a load costs no vector instructions.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+// A pointer the compiler may keep in scalar registers (all lanes agree).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const unsigned long long b = (unsigned long long)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return (const void*)(((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Per-lane byte offsets (within a chunk) of wave wv's half of a row tile's
+// loads: load t of the wave is unit p = (wv*RINS/2 + t)*64 + lane.
+template <int D> __device__ __forceinline__ void row_tile_offsets(const Grid& g, int wv, int lane,
+                                                                   uint32_t* off) {
+  using G = ChunkGeom<D>;
+#pragma unroll
+  for (int t = 0; t < G::RINS / 2; ++t) {
+    const int p = (wv * (G::RINS / 2) + t) * 64 + lane, kappa = p / G::U;
+    const int u = (p % G::U) ^ kswz<G::U>(kappa);
+    const int tokoff = ((kappa >> 4) * g.H + ((kappa >> 2) & 3)) * g.W + (kappa & 3);
+    off[t] = (uint32_t)(tokoff * D + u * 8) * 2u;
+  }
+}
+template <int D> __device__ __forceinline__ void chunk_tile_offsets(int wv, int lane, uint32_t* off) {
+  using G = ChunkGeom<D>;
+#pragma unroll
+  for (int t = 0; t < G::TINS / 2; ++t) off[t] = (uint32_t)((wv * (G::TINS / 2) + t) * 64 + lane) * 16u;
+}
+// Issue wave wv's half of a row tile: src = first row of the chunk (token
+// (2h, 0, 0) of the cube), dst = LDS byte address of the tile.
+template <int D> __device__ __forceinline__ void issue_row_tile(const void* src, const uint32_t* off, uint32_t dst,
+                                                                int wv) {
+  using G = ChunkGeom<D>;
+#pragma unroll
+  for (int t = 0; t < G::RINS / 2; ++t) dma16(src, off[t], dst + (wv * (G::RINS / 2) + t) * 1024);
+}
+template <int D> __device__ __forceinline__ void issue_chunk_tile(const void* src, const uint32_t* off,
+                                                                  uint32_t dst, int wv) {
+  using G = ChunkGeom<D>;
+#pragma unroll
+  for (int t = 0; t < G::TINS / 2; ++t) dma16(src, off[t], dst + (wv * (G::TINS / 2) + t) * 1024);
+}
+// A operand fragments: row tile (rows = tokens, k-step ks over channels) and
+// chunk tile (rows = channels 32mb + n32, k-step s2 over the chunk's slots).
+template <int D> __device__ __forceinline__ bf16x8 row_frag(const bf16* tile, int n32, int hf, int ks) {
+  using G = ChunkGeom<D>;
+  return *reinterpret_cast<const bf16x8*>(tile + (n32 * G::U + ((2 * ks + hf) ^ kswz<G::U>(n32))) * 8);
+}
+__device__ __forceinline__ bf16x8 chunk_frag(const bf16* tile, int dd, int hf, int s2) {
+  return *reinterpret_cast<const bf16x8*>(tile + (dd * 4 + ((2 * s2 + hf) ^ vunit_swz(dd))) * 8);
+}
+
+}  // namespace vsa

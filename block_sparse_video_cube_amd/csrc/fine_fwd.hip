@@ -7,18 +7,20 @@
 // mask unselected, softmax, times V; combine, untile); VSA reading notes,
 // key designs 2-3. Variable-length lists per query cube: VSA2 abstract.
 //
-// bf16 kernel: one wave owns one query cube (64 query rows) and walks its
-// list of key cubes (in 32-key halves) with an online softmax, all in
-// registers:
-//   S^T = K_j Q_i^T   16x16x32 bf16 MFMAs, A = K rows, B = Q rows (both read
-//                     straight from the raster tensors, 16-byte loads);
-//   the accumulator layout gives every lane one query column and 4+4+4+4 key
-//   rows, so row max / sum are lane-local plus one exchange over the 4 lane
-//   groups, and P^T is already the B operand of
-//   O^T += V_j^T P^T  with A = the V T-tile of cube j (channel rows, keys
-//                     contiguous in the accumulator's slot order).
-// Every lane ends with O^T for its query column, so the 1/l normalisation,
-// LSE and the fused gate epilogue need no data exchange.
+// bf16 kernel: a workgroup of two waves owns one query cube; wave w owns the
+// queries 32w .. 32w+31 and walks the cube's list of key cubes in 32-key
+// chunks with an online softmax (32x32x16 bf16 MFMAs):
+//   S^T = K_chunk Q^T    A = the chunk's K row tile (LDS), B = the lane's Q
+//                        row (registers, loaded once);
+//   the accumulator gives every lane one query column and 16 of the 32 keys,
+//   so the row max and sum are lane-local plus one exchange between the two
+//   lane halves, and P^T is already the B operand of
+//   O^T += V_chunk^T P^T  A = the chunk's V chunk tile (LDS; slots in the
+//                        accumulator's row order).
+// Chunks go to LDS with direct-to-LDS loads, each wave issuing half, several
+// chunks ahead. Every lane ends with O^T for its query column, so the 1/l
+// normalisation, LSE and the fused gate epilogue need no data exchange.
+#include "fine_common.h"
 #include "vsa_kernels.h"
 
 namespace vsa {
@@ -41,38 +43,6 @@ template <int D> struct FineCfg {
   static constexpr int KST = 3;
   static constexpr int VST = D == 64 ? 3 : 2;
 };
-
-// K chunk in LDS: key row kappa (0..31) holds U 16-byte units; logical unit
-// u (channels 8u .. 8u+7) sits at unit u ^ kswz(kappa), so 16 consecutive
-// rows read at one logical unit hit 16 distinct bank groups.
-template <int U> __device__ __forceinline__ int kswz(int kappa) { return (kappa * U / 16) % U; }
-
-// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
-// address lds + 16*l. Issued as inline assembly so that the compiler does not
-// treat later LDS reads of other stages as dependent on it; completion is
-// tracked by the vector-memory counter and waited for explicitly (wait_vmcnt).
-// The compiler never uses M0 in these kernels (checked on the generated code).
-// The address is a wave-uniform base (SGPRs) plus a per-lane 32-bit byte
-// offset, so issuing a load costs no vector instructions.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
-}
-// A pointer the compiler may keep in scalar registers (all lanes agree).
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const unsigned long long b = (unsigned long long)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  return (const void*)(((unsigned long long)hi << 32) | lo);
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-// Wait until at most N of this wave's vector-memory loads are outstanding.
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // Processing order of the query cubes of every (b, h): ascending by the first
 // two cubes of their lists (empty positions sort last), ties by cube id.

@@ -61,25 +61,12 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
     __syncthreads();
   }
 
-  if (vt != nullptr) {
-    // V chunk tiles: [2 halves][D channel rows][4 units of 8 slots]; one
-    // thread writes one 16-byte unit.
-    bf16* dst = vt + (bh * g.Nc + c) * (long)D * kTile;
-    for (int w = tid; w < 2 * D * 4; w += 256) {
-      const int h = w / (D * 4), rem = w - h * D * 4, dd = rem >> 2, up = rem & 3;
-      const int u = up ^ vunit_swz(dd);
-      bf16x8 r;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = vtile[32 * h + vslot(8 * u + e)][dd];
-      *reinterpret_cast<bf16x8*>(dst + (long)w * 8) = r;
-    }
-  }
+  if (vt != nullptr) store_chunk_tiles<D, VPITCH>(vtile, vt + (bh * g.Nc + c) * (long)D * kTile, tid, 256);
 }
 
-// T-tiles of a raster tensor (used by the backward for Q, K and dO_f).
+// Chunk tiles of a raster bf16 tensor (the backward's Q and K).
 template <int D>
-__global__ __launch_bounds__(256) void ttile_kernel(const bf16* __restrict__ x, bf16* __restrict__ xt,
-                                                    Grid g) {
+__global__ __launch_bounds__(256) void ctile_kernel(const bf16* __restrict__ x, bf16* __restrict__ xt, Grid g) {
   constexpr int CH = D / 8, RPP = 256 / CH, PASSES = kTile / RPP, VPITCH = D + 8;
   __shared__ bf16 tile[kTile][VPITCH];
   const int tid = threadIdx.x;
@@ -94,14 +81,7 @@ __global__ __launch_bounds__(256) void ttile_kernel(const bf16* __restrict__ x, 
         *reinterpret_cast<const bf16x8*>(src + (long)cube_token(g, c, l) * D + ch * 8);
   }
   __syncthreads();
-  bf16* dst = xt + (bh * g.Nc + c) * (long)D * kTile;
-  for (int w = tid; w < D * 8; w += 256) {
-    const int dd = w >> 3, j = w & 7;
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = tile[tslot(8 * j + e)][dd];
-    *reinterpret_cast<bf16x8*>(dst + dd * kTile + 8 * j) = r;
-  }
+  store_chunk_tiles<D, VPITCH>(tile, xt + (bh * g.Nc + c) * (long)D * kTile, tid, 256);
 }
 
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
@@ -125,12 +105,12 @@ hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void
   return hipGetLastError();
 }
 
-hipError_t launch_ttile(const Launch& L, const bf16* x, bf16* xt) {
+hipError_t launch_ctile(const Launch& L, const bf16* x, bf16* xt) {
   const dim3 grid(L.g.Nc, L.BH), block(256);
   if (L.D == 64)
-    hipLaunchKernelGGL((ttile_kernel<64>), grid, block, 0, L.stream, x, xt, L.g);
+    hipLaunchKernelGGL((ctile_kernel<64>), grid, block, 0, L.stream, x, xt, L.g);
   else
-    hipLaunchKernelGGL((ttile_kernel<128>), grid, block, 0, L.stream, x, xt, L.g);
+    hipLaunchKernelGGL((ctile_kernel<128>), grid, block, 0, L.stream, x, xt, L.g);
   return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ Saved carve_saved(const Dims& d, void* base) {
   return s;
 }
 
-// Forward workspace: V T-tiles (bf16), the coarse logits and, for
+// Forward workspace: V chunk tiles (bf16), the coarse logits and, for
 // inference, the pooled tensors.
 struct FwdWs {
   bf16* vt;
@@ -127,9 +127,9 @@ FwdWs carve_fwd_ws(const Dims& d, void* base) {
 
 // Backward workspace.
 struct BwdWs {
-  bf16 *dof, *doft, *qt, *kt;
+  bf16 *dof, *doft, *qt, *kt;   // d_o_f (raster) and chunk tiles of d_o_f, q, k
   float *delta, *doc, *dqc, *dkc, *dvc, *p_scr, *ds_scr, *dc_scr;
-  int32_t *k2q_off, *k2q;
+  int32_t *k2q_off, *k2q, *qorder, *korder;
   uint32_t* k2q_bits;
   size_t bytes;
 };
@@ -154,6 +154,8 @@ BwdWs carve_bwd_ws(const Dims& d, void* base) {
   w.k2q_off = c.take<int32_t>(d.BH * (d.Nc + 1));
   w.k2q = c.take<int32_t>(d.BH * d.Nc * d.stride);
   w.k2q_bits = c.take<uint32_t>(d.BH * d.Nc * (size_t)k2q_bits_words((int)d.Nc));
+  w.qorder = c.take<int32_t>(d.BH * d.Nc);
+  w.korder = c.take<int32_t>(d.BH * d.Nc);
   w.bytes = c.off;
   return w;
 }
@@ -251,12 +253,15 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   if (e == hipSuccess) e = launch_index_transpose(L, idx, len, ws.k2q_off, ws.k2q, ws.k2q_bits);
   if (e == hipSuccess)
     e = launch_coarse_bwd(L, s.qc, s.kc, s.vc, s.oc, s.lse_c, ws.doc, ws.dqc, ws.dkc, ws.dvc, ws.ds_scr, ws.p_scr, ws.dc_scr);
-  if (e == hipSuccess) e = launch_ttile(L, static_cast<const bf16*>(q), ws.qt);
-  if (e == hipSuccess) e = launch_ttile(L, static_cast<const bf16*>(k), ws.kt);
+  if (e == hipSuccess) e = launch_ctile(L, static_cast<const bf16*>(q), ws.qt);
+  if (e == hipSuccess) e = launch_ctile(L, static_cast<const bf16*>(k), ws.kt);
+  if (e == hipSuccess) e = launch_order(L, idx, len, ws.qorder);
+  if (e == hipSuccess) e = launch_order_by_count(L, ws.k2q_off, ws.korder);
   if (e == hipSuccess)
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                        ws.qt, ws.kt, idx, len, ws.k2q_off, ws.k2q, s.lse_f, ws.dof, ws.doft, ws.delta, ws.dqc,
-                        ws.dkc, ws.dvc, static_cast<bf16*>(dq), static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+                        ws.qt, ws.kt, idx, len, ws.qorder, ws.k2q_off, ws.k2q, ws.korder, s.lse_f, ws.dof, ws.doft,
+                        ws.delta, ws.dqc, ws.dkc, ws.dvc, static_cast<bf16*>(dq), static_cast<bf16*>(dk),
+                        static_cast<bf16*>(dv));
   return hip_status(e);
 }
 
@@ -405,13 +410,15 @@ vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k,
   const BwdWs ws = carve_bwd_ws(d, workspace);
   if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
   L.stream = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_ttile(L, static_cast<const bf16*>(q), ws.qt);
-  if (e == hipSuccess) e = launch_ttile(L, static_cast<const bf16*>(k), ws.kt);
+  hipError_t e = launch_ctile(L, static_cast<const bf16*>(q), ws.qt);
+  if (e == hipSuccess) e = launch_ctile(L, static_cast<const bf16*>(k), ws.kt);
+  if (e == hipSuccess) e = launch_order(L, idx, len, ws.qorder);
+  if (e == hipSuccess) e = launch_order_by_count(L, k2q_off, ws.korder);
   if (e == hipSuccess)
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                        ws.qt, ws.kt, idx, len, k2q_off, k2q, lse_f, static_cast<const bf16*>(d_o_f), ws.doft,
-                        delta, dq_c, dk_c, dv_c, static_cast<bf16*>(dq), static_cast<bf16*>(dk),
-                        static_cast<bf16*>(dv));
+                        ws.qt, ws.kt, idx, len, ws.qorder, k2q_off, k2q, ws.korder, lse_f,
+                        static_cast<const bf16*>(d_o_f), ws.doft, delta, dq_c, dk_c, dv_c, static_cast<bf16*>(dq),
+                        static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   return hip_status(e);
 }
 

@@ -6,14 +6,8 @@
 //    c = (tc * H4 + yc) * W4 + xc (row-major cube order); token l of a cube
 //    (0..63) is (t', y', x') = (l / 16, (l / 4) % 4, l % 4). Within a cube the
 //    four tokens x' = 0..3 are contiguous in raster memory (4*D elements).
-//  * Transposed bf16 tiles ("T-tiles") hold one cube of one tensor as
-//    [D][64]: row dd holds the cube's 64 values of channel dd, in slot order
-//    slot -> token tslot(slot). The slot order matches the register layout of
-//    a 16x16 MFMA accumulator: lanes 16*g .. 16*g+15 hold rows 4g..4g+3 of a
-//    16-row block, so the 8 bf16 a lane feeds to the k = 32 side of the next
-//    16x16x32 MFMA are rows {4g..4g+3} of two consecutive 16-row blocks.
-//    A T-tile row therefore stores, for k-step s and lane group g, the 8
-//    tokens {32s + 4g + e, 32s + 16 + 4g + e : e = 0..3} contiguously.
+//  * Chunk tiles hold one cube of one tensor transposed, channel-major, in
+//    the slot order of a 32x32 MFMA accumulator (see vslot below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,12 +67,7 @@ __device__ __forceinline__ int token_cube(const Grid& g, int n) {
   return ((t >> 2) * g.H4 + (y >> 2)) * g.W4 + (x >> 2);
 }
 
-// Token (0..63) stored at slot `slot` of a T-tile row.
-__host__ __device__ __forceinline__ int tslot(int slot) {
-  return 32 * (slot >> 5) + 16 * ((slot & 7) >> 2) + 4 * ((slot & 31) >> 3) + (slot & 3);
-}
-
-// V chunk tiles (read by the fine forward kernel, 32x32x16 MFMAs): for each
+// Chunk tiles (read by the fine kernels, 32x32x16 MFMAs): for each
 // cube and each half h (tokens 32h .. 32h+31) a [D][32] bf16 block, channel
 // rows of 64 bytes = four 16-byte units. Slot t of a row holds token
 // 32h + vslot(t): the order in which a 32x32 MFMA accumulator hands its rows
@@ -90,6 +79,21 @@ __host__ __device__ __forceinline__ int vslot(int t) {
   return 16 * (t >> 4) + 8 * ((t & 7) >> 2) + 4 * ((t & 15) >> 3) + (t & 3);
 }
 __host__ __device__ __forceinline__ int vunit_swz(int dd) { return (dd >> 2) & 3; }
+
+// Writes the chunk tiles of one cube (D * 64 bf16 at dst) from an LDS copy
+// tile[l][channel] of its 64 tokens (cube order); `nthreads` threads
+// cooperate, one 16-byte unit each per step.
+template <int D, int PITCH>
+__device__ __forceinline__ void store_chunk_tiles(const bf16 (*tile)[PITCH], bf16* dst, int tid, int nthreads) {
+  for (int w = tid; w < 2 * D * 4; w += nthreads) {
+    const int h = w / (D * 4), rem = w - h * D * 4, dd = rem >> 2, up = rem & 3;
+    const int u = up ^ vunit_swz(dd);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = tile[32 * h + vslot(8 * u + e)][dd];
+    *reinterpret_cast<bf16x8*>(dst + (long)w * 8) = r;
+  }
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2). Map block b so that every XCD gets one contiguous range of work items:

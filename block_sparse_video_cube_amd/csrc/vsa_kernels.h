@@ -19,7 +19,8 @@ struct Launch {
 
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
                        float* vc, bf16* vt);
-hipError_t launch_ttile(const Launch& L, const bf16* x, bf16* xt);
+// Chunk tiles (layout in vsa_common.h) of a raster bf16 tensor.
+hipError_t launch_ctile(const Launch& L, const bf16* x, bf16* xt);
 
 int coarse_max_cubes();
 // Row pitch (floats) of the coarse logits: Nc rounded up to a multiple of 4.
@@ -53,11 +54,17 @@ hipError_t launch_index_transpose(const Launch& L, const int32_t* idx, const int
 hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, const float* vc,
                              const float* oc, const float* lse, const float* doc, float* dqc, float* dkc,
                              float* dvc, float* ds_scratch, float* p_scratch, float* dc_scratch);
-hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const bf16* qt,
-                           const bf16* kt, const int32_t* idx, const int32_t* len, const int32_t* k2q_off,
-                           const int32_t* k2q, const float* lse_f, const bf16* dof, const bf16* doft,
-                           const float* delta, const float* dqc, const float* dkc, const float* dvc, bf16* dq,
-                           bf16* dk, bf16* dv);
+// Key cubes of every (b, h) ordered by descending transposed-list length.
+hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_t* order);
+// Fine backward (bf16): dq over the forward lists (qorder from launch_order,
+// may be null), dk / dv over the transposed lists (korder from
+// launch_order_by_count, may be null). qct / kct / doct: chunk tiles of q, k
+// and d_o_f. The pooled gradients dqc / dkc / dvc are spread over their cubes.
+hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const bf16* qct,
+                           const bf16* kct, const int32_t* idx, const int32_t* len, const int32_t* qorder,
+                           const int32_t* k2q_off, const int32_t* k2q, const int32_t* korder, const float* lse_f,
+                           const bf16* dof, const bf16* doct, const float* delta, const float* dqc,
+                           const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv);
 
 hipError_t launch_validate_lists(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* flag);
 
