@@ -26,9 +26,10 @@ F32_ABS = 1e-4
 # Sanity bound on the share of rows whose top-K margin is within the fp32
 # error bound (about 0.6% / 1.4% / 2.3% on the 16x32x32 / 480p / 720p inputs).
 NEAR_FRAC = 0.05
-# LSE_f bound: the fine kernel sums the bf16-rounded probabilities it also
-# multiplies V with, so l carries at most the bf16 half-ulp relative error
-# 2^-8, i.e. |ln l - ln l_exact| <= 2^-8; plus fp32 slack.
+# LSE_f bound: l is the fp32 sum of the probabilities whose bf16-rounded
+# values multiply V, so however l is summed it is within the bf16 half-ulp
+# relative error 2^-8 of the exact sum, i.e. |ln l - ln l_exact| <= 2^-8;
+# plus fp32 slack.
 LSE_ABS = 2.0 ** -8 + 1e-4
 
 
