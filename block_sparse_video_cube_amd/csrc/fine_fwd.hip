@@ -20,6 +20,8 @@
 // Chunks go to LDS with direct-to-LDS loads, each wave issuing half, several
 // chunks ahead. Every lane ends with O^T for its query column, so the 1/l
 // normalisation, LSE and the fused gate epilogue need no data exchange.
+#include <type_traits>
+
 #include "fine_common.h"
 #include "vsa_kernels.h"
 
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   // result is exact whatever the schedule.
   constexpr float kHeadroom = 16.0f;
   const int nch = 2 * L;
-  f32x16 sx;
+  f32x16 sxa, sxb;
   if (nch > 0) {
     issue_k(0);
 #pragma unroll
@@ -217,13 +219,30 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
       if (c0 < nch) issue_k(c0);
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    sx = scores(kbuf);
+    sxa = scores(kbuf);
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sx[e]);
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sxa[e]);
     m = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
   }
-  for (int c = 0; c < nch; ++c) {
+  // Bytes of this lane's LDS fragments within a stage: K row fragment ks and
+  // V fragment (mb, s2) (the 32-channel block mb adds 2048 bytes).
+  uint32_t koffs[C::KS], voffs[2];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koffs[ks] = (n32 * C::U + ((2 * ks + hf) ^ kswz<C::U>(n32))) * 16;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) voffs[s2] = (n32 * 4 + ((2 * s2 + hf) ^ vunit_swz(n32))) * 16;
+  const char* kbytes = reinterpret_cast<const char*>(kbuf);
+  const char* vbytes = reinterpret_cast<const char*>(vbuf);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
+
+  // One chunk; P is the chunk's position in the 6-chunk unrolled block
+  // (6 is a multiple of both stage counts, so both stages are constants and
+  // every LDS address is a per-lane register plus an immediate). sx holds
+  // the scores of chunk c, sn receives those of chunk c + 1.
+  auto step = [&](auto P, f32x16& sx, f32x16& sn, int c) {
+    constexpr int p = decltype(P)::value;
     if (c > 0) {
       if (c - 1 + C::KST < nch) wait_vmcnt<C::KINS / 2>();
       else wait_vmcnt<0>();
@@ -249,25 +268,19 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
     // Every LDS fragment is read first, so LDS latency is paid once; the
     // scheduling fences keep each score MFMA next to an independent slice of
     // the softmax, which runs while the MFMA does.
-    const bf16* kb = kbuf + ((c + 1) % C::KST) * C::KUNITS * 8;
-    const bf16* vb = vbuf + (c % C::VST) * C::VUNITS * 8;
+    constexpr uint32_t kst = ((p + 1) % C::KST) * C::KUNITS * 16, vst = (p % C::VST) * C::VUNITS * 16;
     bf16x8 kf[C::KS], vf[C::MB][2];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      kf[ks] = *reinterpret_cast<const bf16x8*>(kb + (n32 * C::U + ((2 * ks + hf) ^ kswz<C::U>(n32))) * 8);
+    for (int ks = 0; ks < C::KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kbytes + kst + koffs[ks]);
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
-      const int dd = 32 * mb + n32;
+    for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        vf[mb][s2] = *reinterpret_cast<const bf16x8*>(vb + (dd * 4 + ((2 * s2 + hf) ^ vunit_swz(dd))) * 8);
-    }
+        vf[mb][s2] = *reinterpret_cast<const bf16x8*>(vbytes + vst + mb * 2048 + voffs[s2]);
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 sn;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sn[e] = 0.f;
     bf16x8 pf[2];
-    float lp[2] = {0.f, 0.f};
     constexpr int PER = 16 / C::KS;   // softmax entries per score MFMA
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -275,20 +288,43 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
 #pragma unroll
       for (int t = 0; t < PER; ++t) {
         const int e = ks * PER + t;
-        const float pv = __builtin_amdgcn_exp2f(sx[e] * scale_log2 - m);
-        lp[e & 1] += pv;
-        pf[e >> 3][e & 7] = (bf16)pv;
+        pf[e >> 3][e & 7] = (bf16)__builtin_amdgcn_exp2f(sx[e] * scale_log2 - m);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    lsum += lp[0] + lp[1];
+    // Row sums of the rounded P (the weights O is formed with), two at a time.
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 a0 = {pf[0][e], pf[0][e + 1]}, a1 = {pf[1][e], pf[1][e + 1]};
+      l0 = __builtin_amdgcn_fdot2_f32_bf16(a0, ones2, l0, false);
+      l1 = __builtin_amdgcn_fdot2_f32_bf16(a1, ones2, l1, false);
+    }
+    lsum += l0 + l1;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        acc[mb] = mfma32_bf16(vf[mb][s2], pf[s2], acc[mb]);
-      }
-    sx = sn;
+      for (int mb = 0; mb < C::MB; ++mb) acc[mb] = mfma32_bf16(vf[mb][s2], pf[s2], acc[mb]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  static_assert(6 % C::KST == 0 && 6 % C::VST == 0, "stages must divide the unroll");
+  for (int c0 = 0; c0 < nch; c0 += 6) {
+    step(I0(), sxa, sxb, c0);
+    if (c0 + 1 >= nch) break;
+    step(I1(), sxb, sxa, c0 + 1);
+    if (c0 + 2 >= nch) break;
+    step(I2(), sxa, sxb, c0 + 2);
+    if (c0 + 3 >= nch) break;
+    step(I3(), sxb, sxa, c0 + 3);
+    if (c0 + 4 >= nch) break;
+    step(I4(), sxa, sxb, c0 + 4);
+    if (c0 + 5 >= nch) break;
+    step(I5(), sxb, sxa, c0 + 5);
   }
 
   // Epilogue: lane holds O^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query].
