@@ -154,12 +154,44 @@ def train_measure(name: str, steps: int, warmup: int) -> dict:
     pairs = int(lens.sum().item())
     fl_f = 4.0 * 64 * 64 * w.head_dim * pairs
     fl_b = 10.0 * 64 * 64 * w.head_dim * pairs
+    esz = 2 if w.dtype == "bf16" else 4
+    raster = w.B * w.heads * w.N * w.head_dim
+    # combine backward: read dO, O_f, G_c, G_f; write dG_c, dG_f, dO_f, its chunk tiles; + delta
+    cb_bytes = 8 * raster * esz + w.B * w.heads * w.N * 4
     return {"workload": w.name, "steps": steps, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_tflops": round(fl_f / (fwd_ms * 1e-3) / 1e12, 2), "bwd_tflops": round(fl_b / (bwd_ms * 1e-3) / 1e12, 2),
             "computed_block_pairs": pairs,
             "bwd_stages_ms": {"combine_bwd": round(st[0], 4), "index_transpose": round(st[1], 4),
                               "coarse_bwd": round(st[2], 4), "fine_bwd (T-tiles, dq, dk/dv, pool bwd)": round(st[3], 4)},
-            "fine_bwd_tflops": round(fl_b / (st[3] * 1e-3) / 1e12, 2)}
+            "fine_bwd_tflops": round(fl_b / (st[3] * 1e-3) / 1e12, 2),
+            "fine_bwd_frac_bf16_peak": round(fl_b / (st[3] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "combine_bwd_GB_per_s": round(cb_bytes / (st[0] * 1e-3) / 1e9, 1),
+            "combine_bwd_frac_hbm_peak": round(cb_bytes / (st[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
+def dense_flash_context(heads: int, n: int, d: int, reps: int = 3):
+    """Dense attention through PyTorch's flash SDPA backend (no other backend
+    allowed) on one head-count / length / head_dim: the vendor kernel's
+    TFLOP/s on this GPU, as context for the fine kernel's TFLOP/s."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    try:
+        q = torch.randn(1, heads, n, d, device="cuda:0", dtype=torch.bfloat16)
+        k, v = torch.randn_like(q), torch.randn_like(q)
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            torch.nn.functional.scaled_dot_product_attention(q, k, v)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                torch.nn.functional.scaled_dot_product_attention(q, k, v)
+            b.record()
+            torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        return {"kernel": "torch SDPA, flash backend, dense", "shape": [1, heads, n, d], "ms": round(ms, 3),
+                "tflops": round(4.0 * heads * n * n * d / (ms * 1e-3) / 1e12, 1)}
+    except Exception as e:  # noqa: BLE001 - context only
+        return {"error": repr(e)[:200]}
 
 
 def main() -> int:
@@ -325,6 +357,11 @@ def main() -> int:
     }
     log(f"forward {ms_step:.3f} ms/step = {value:.1f} TFLOP/s; pool {stage_ms[0]:.3f} ms, "
         f"coarse {stage_ms[1]:.3f} ms, fine+combine {stage_ms[2]:.3f} ms ({achieved:.1f} TFLOP/s)")
+    ctx = dense_flash_context(w.heads, 16384, w.head_dim)
+    if "tflops" in ctx:
+        ctx["fine_kernel_vs_dense"] = round(achieved / ctx["tflops"], 3)
+    line["dense_attention_context"] = ctx
+    log(f"dense flash SDPA context: {ctx}")
     line["train"] = []
     for name in [t for t in args.train.split(",") if t]:
         log(f"timing forward + backward of {name}")
