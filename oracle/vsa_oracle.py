@@ -29,7 +29,9 @@ the design notes of the repository):
   within a row), ties going to the smaller cube index, no forced diagonal;
 * masked logits are exactly -inf; an empty list gives O_f = 0, LSE_f = -inf;
 * gates are elementwise, shaped like the output; a missing gate means 1;
-* the top-K mask carries no gradient (it is piecewise constant).
+* the top-K mask carries no gradient (it is piecewise constant);
+* the max-pool variant (ablation of the coarse pooling) takes the per-channel
+  maximum over a cube; its gradient goes to the first maximum in cube order.
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle.py`` (library routines, closed forms, brute force,
@@ -93,8 +95,19 @@ def untile_rows(rt: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Step 1: cube mean-pool (section 2 "Methods"; App. B; notes key design 1)
 # --------------------------------------------------------------------------
-def pool(xt: np.ndarray) -> np.ndarray:
-    """X_c[c] = (1/64) * sum over the 64 tokens of cube c.  [..., Nc, 64, d] -> [..., Nc, d]."""
+POOL_MODES = ("mean", "max")
+
+
+def pool(xt: np.ndarray, mode: str = "mean") -> np.ndarray:
+    """X_c[c] = (1/64) * sum over the 64 tokens of cube c.  [..., Nc, 64, d] -> [..., Nc, d].
+
+    mode "max": the per-channel maximum over the cube's tokens instead, the
+    pooling variant the VSA summary page's ablation study compares with
+    average pooling (section 3 "Experiments", ablation studies)."""
+    if mode == "max":
+        return xt.max(axis=-2)
+    if mode != "mean":
+        raise ValueError(f"pool mode {mode!r}")
     return xt.sum(axis=-2) / TILE
 
 
@@ -178,7 +191,8 @@ def _pool_error_bound(xt: np.ndarray, sig_bits: int) -> np.ndarray:
     return np.where(exact, 0.0, gamma * total / TILE)
 
 
-def logit_error_bound(qt: np.ndarray, kt: np.ndarray, scale: float, sig_bits: int = 8) -> np.ndarray:
+def logit_error_bound(qt: np.ndarray, kt: np.ndarray, scale: float, sig_bits: int = 8,
+                      pool_mode: str = "mean") -> np.ndarray:
     """Per-row bound on |fp32 coarse logit - exact logit| for one (b, h).
 
     The fp32 path pools 64 inputs (error bounded by ``_pool_error_bound``),
@@ -192,8 +206,11 @@ def logit_error_bound(qt: np.ndarray, kt: np.ndarray, scale: float, sig_bits: in
     u = 2.0 ** -24
     d = qt.shape[-1]
     gd = d * u / (1 - d * u)
-    qc, kc = np.abs(pool(qt)), np.abs(pool(kt))
-    eq, ek = _pool_error_bound(qt, sig_bits), _pool_error_bound(kt, sig_bits)
+    qc, kc = np.abs(pool(qt, pool_mode)), np.abs(pool(kt, pool_mode))
+    if pool_mode == "max":   # a maximum of exact values is exact
+        eq, ek = np.zeros_like(qc), np.zeros_like(kc)
+    else:
+        eq, ek = _pool_error_bound(qt, sig_bits), _pool_error_bound(kt, sig_bits)
     pooled = eq @ kc.T + qc @ ek.T + eq @ ek.T
     dot = gd * ((qc + eq) @ (kc + ek).T)
     b = scale * (pooled + dot) + 4 * u * scale * (qc @ kc.T + pooled)
@@ -279,7 +296,7 @@ def _f64(x):
 
 
 def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
-            scale: Optional[float] = None, with_literal: bool = False):
+            scale: Optional[float] = None, with_literal: bool = False, pool_mode: str = "mean"):
     """VSA forward for [B, h, T, H, W, d] inputs.
 
     topk > 0 selects the K best cubes per row; topk == 0 uses the caller's
@@ -292,7 +309,7 @@ def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
     nc = T * H * W // TILE
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     qt, kt, vt = tile(q), tile(k), tile(v)
-    qc, kc, vc = pool(qt), pool(kt), pool(vt)
+    qc, kc, vc = pool(qt, pool_mode), pool(kt, pool_mode), pool(vt, pool_mode)
     oc = np.empty_like(qc)
     lse_c = np.empty(qc.shape[:-1])
     s_c = np.empty((B, nh, nc, nc))
@@ -313,7 +330,7 @@ def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
             s_c[b, h], _, oc[b, h], lse_c[b, h] = coarse_attention(qc[b, h], kc[b, h], vc[b, h], s)
             if topk > 0:
                 idx_o[b, h], margin[b, h] = topk_rows(s_c[b, h], topk)
-                tau[b, h] = logit_error_bound(qt[b, h], kt[b, h], s, sig_bits)
+                tau[b, h] = logit_error_bound(qt[b, h], kt[b, h], s, sig_bits, pool_mode)
             of_t[b, h], lse_t[b, h] = fine_gathered(qt[b, h], kt[b, h], vt[b, h],
                                                     idx_o[b, h], lens_o[b, h], s)
             if with_literal:
@@ -321,7 +338,7 @@ def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
                 of_lit[b, h], _ = fine_literal(q[b, h], k[b, h], v[b, h], m, s)
     of = untile(of_t, T, H, W)
     oc_rep = repeat_coarse(oc, T, H, W)
-    out = dict(scale=s, q_c=qc, k_c=kc, v_c=vc, s_c=s_c, o_c=oc, lse_c=lse_c,
+    out = dict(scale=s, pool_mode=pool_mode, q_c=qc, k_c=kc, v_c=vc, s_c=s_c, o_c=oc, lse_c=lse_c,
                idx=idx_o, len=lens_o, margin=margin, tau=tau,
                o_f=of, lse_f=untile_rows(lse_t, T, H, W), o_c_rep=oc_rep,
                o=combine(oc_rep, of, g_c, g_f))
@@ -379,8 +396,17 @@ def coarse_backward(qc, kc, vc, doc, scale):
     return scale * (ds @ kc), scale * (ds.T @ qc), dv
 
 
-def pool_backward(dxc: np.ndarray) -> np.ndarray:
-    """Gradient of the mean-pool: each of the 64 tokens of cube c gets dX_c[c]/64."""
+def pool_backward(dxc: np.ndarray, xt: Optional[np.ndarray] = None, mode: str = "mean") -> np.ndarray:
+    """Gradient of the mean-pool: each of the 64 tokens of cube c gets dX_c[c]/64.
+
+    mode "max" (xt = the pooled input, tiled): per channel, the whole dX_c[c]
+    goes to the token holding the maximum; among equal maxima, the first in
+    cube order (reading: the subgradient a sequential scan picks)."""
+    if mode == "max":
+        arg = np.argmax(xt, axis=-2)                      # first maximum
+        out = np.zeros(xt.shape, dtype=np.result_type(dxc, np.float64))
+        np.put_along_axis(out, arg[..., None, :], dxc[..., None, :], axis=-2)
+        return out
     return np.repeat(dxc[..., :, None, :], TILE, axis=-2) / TILE
 
 
@@ -405,9 +431,10 @@ def backward(q, k, v, g_c, g_f, d_o, fwd: dict):
                 fwd["idx"][b, h], fwd["len"][b, h], s)
             dqc[b, h], dkc[b, h], dvc[b, h] = coarse_backward(
                 fwd["q_c"][b, h], fwd["k_c"][b, h], fwd["v_c"][b, h], doc[b, h], s)
-    dq = untile(dqt + pool_backward(dqc), T, H, W)
-    dk = untile(dkt + pool_backward(dkc), T, H, W)
-    dv = untile(dvt + pool_backward(dvc), T, H, W)
+    pm = fwd.get("pool_mode", "mean")
+    dq = untile(dqt + pool_backward(dqc, qt, pm), T, H, W)
+    dk = untile(dkt + pool_backward(dkc, kt, pm), T, H, W)
+    dv = untile(dvt + pool_backward(dvc, vt, pm), T, H, W)
     return dict(dq=dq, dk=dk, dv=dv, dg_c=dgc, dg_f=dgf, d_o_f=dof, d_o_c=doc,
                 delta=untile_rows(dd_t, T, H, W), dq_c=dqc, dk_c=dkc, dv_c=dvc)
 

@@ -229,14 +229,16 @@ def test_repeat_coarse_matches_repeat_interleave():
 
 
 # ----------------------------------------------------------------- end to end
-def _torch_vsa(q, k, v, g_c, g_f, mask, scale):
+def _torch_vsa(q, k, v, g_c, g_f, mask, scale, pool_mode="mean"):
     """Independent torch expression of the forward with a fixed block mask:
-    avg_pool3d pooling, repeat_interleave broadcast, token-level masked softmax."""
+    avg_pool3d (or max_pool3d) pooling, repeat_interleave broadcast,
+    token-level masked softmax."""
     B, h, T, H, W, d = q.shape
     Tp, Hp, Wp = T // 4, H // 4, W // 4
+    pool3d = F.max_pool3d if pool_mode == "max" else F.avg_pool3d
 
     def pool(x):
-        p = F.avg_pool3d(x.permute(0, 1, 5, 2, 3, 4).reshape(B * h, d, T, H, W), 4)
+        p = pool3d(x.permute(0, 1, 5, 2, 3, 4).reshape(B * h, d, T, H, W), 4)
         return p.reshape(B, h, d, -1).transpose(-1, -2)
 
     qc, kc, vc = pool(q), pool(k), pool(v)
@@ -311,6 +313,46 @@ def test_backward_matches_autograd_of_independent_expression():
     for name, key in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg_c", "g_c"), ("dg_f", "g_f")):
         np.testing.assert_allclose(bwd[name], ts[key].grad.numpy(), rtol=1e-10, atol=1e-12,
                                    err_msg=name)
+
+
+def test_max_pool_matches_max_pool3d_and_first_argmax():
+    x = _rand((8, 8, 12, 5), 31)                       # T, H, W, d
+    xt = O.tile(x[None, None])[0, 0]
+    ref = F.max_pool3d(torch.from_numpy(x).permute(3, 0, 1, 2)[None], 4)[0]
+    np.testing.assert_array_equal(O.pool(xt, "max"), ref.reshape(5, -1).T.numpy())
+    # ties: the gradient of every (cube, channel) goes to its first maximum
+    xt2 = np.round(xt * 2) / 2                         # many equal values
+    g = _rand(O.pool(xt2, "max").shape, 32)
+    got = O.pool_backward(g, xt2, "max")
+    for c in range(xt2.shape[0]):
+        for ch in range(5):
+            col = xt2[c, :, ch]
+            first = int(np.flatnonzero(col == col.max())[0])
+            want = np.zeros(64)
+            want[first] = g[c, ch]
+            np.testing.assert_array_equal(got[c, :, ch], want)
+
+
+def test_max_pool_forward_backward_match_autograd():
+    """Max-pool variant end to end against the independent expression with
+    max_pool3d (continuous inputs: no ties, so the subgradient is unique)."""
+    w = WL.make_inputs_custom(1, 2, 4, 8, 8, 8, dtype="f32", seed=5, scale=0.5)
+    nc = 8
+    idx, lens = WL.random_lists(nc, 2 * nc, 1, 5, seed=6)
+    idx, lens = idx.reshape(1, 2, nc, -1), lens.reshape(1, 2, nc)
+    fwd = O.forward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], topk=0, idx=idx, lens=lens, pool_mode="max")
+    bwd = O.backward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], w["d_o"], fwd)
+    mask = np.stack([[O.lists_to_mask(idx[0, h], lens[0, h], nc) for h in range(2)]])
+    ts = {x: torch.from_numpy(w[x].astype(np.float64)).requires_grad_(True)
+          for x in ("q", "k", "v", "g_c", "g_f")}
+    out = _torch_vsa(ts["q"], ts["k"], ts["v"], ts["g_c"], ts["g_f"], torch.from_numpy(mask), 0.5, "max")
+    np.testing.assert_allclose(fwd["o"], out.detach().numpy(), rtol=1e-12, atol=1e-14)
+    (out * torch.from_numpy(w["d_o"].astype(np.float64))).sum().backward()
+    for name, key in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg_c", "g_c"), ("dg_f", "g_f")):
+        np.testing.assert_allclose(bwd[name], ts[key].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+    # the variant differs from the mean-pool operator
+    mean = O.forward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], topk=0, idx=idx, lens=lens)
+    assert np.abs(mean["o"] - fwd["o"]).max() > 1e-3
 
 
 def test_backward_finite_differences_topk_mode():
