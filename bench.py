@@ -357,6 +357,21 @@ def main() -> int:
     }
     log(f"forward {ms_step:.3f} ms/step = {value:.1f} TFLOP/s; pool {stage_ms[0]:.3f} ms, "
         f"coarse {stage_ms[1]:.3f} ms, fine+combine {stage_ms[2]:.3f} ms ({achieved:.1f} TFLOP/s)")
+    # The max-pool variant of the coarse pooling on the same workload (forward).
+    import dataclasses
+    pm = dataclasses.replace(p, pool="max")
+    for _ in range(2):
+        V.forward(pm, q, k, v, gc, gf, idx=idx, lens=lens, ws=ws, out=o)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        V.forward(pm, q, k, v, gc, gf, idx=idx, lens=lens, ws=ws, out=o)
+    ev1.record()
+    torch.cuda.synchronize()
+    mp_ms = ev0.elapsed_time(ev1) / 5
+    line["variants"] = {"max_pool_forward": {"ms_per_step": round(mp_ms, 4),
+                                             "TFLOP_per_s": round(4.0 * 64 * 64 * w.head_dim * int(lens.sum().item())
+                                                                  / (mp_ms * 1e-3) / 1e12, 2)}}
     ctx = dense_flash_context(w.heads, 16384, w.head_dim)
     if "tflops" in ctx:
         ctx["fine_kernel_vs_dense"] = round(achieved / ctx["tflops"], 3)

@@ -36,6 +36,7 @@ class Problem:
     topk: int = 32               # > 0: top-K mode; 0: explicit lists
     list_stride: int = 0         # 0 => topk
     scale: float = 0.0           # 0 => 1/sqrt(head_dim)
+    pool: str = "mean"           # cube pooling of the coarse stage: "mean" or "max"
 
     @property
     def N(self) -> int:
@@ -55,8 +56,9 @@ class Problem:
 
     def c(self) -> VsaProblem:
         code = {"bf16": VSA_BF16, "f32": VSA_F32}.get(self.dtype, 99)
+        pool = {"mean": 0, "max": 1}.get(self.pool, 99)
         return VsaProblem(self.B, self.heads, self.T, self.H, self.W, self.head_dim, code,
-                          float(self.scale), self.topk, self.list_stride)
+                          float(self.scale), self.topk, self.list_stride, pool)
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -23,7 +23,7 @@ class VsaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("topk", ctypes.c_int32),
-                ("list_stride", ctypes.c_int32)]
+                ("list_stride", ctypes.c_int32), ("pool_mode", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER(VsaProblem)

@@ -6,7 +6,8 @@
 // formulas are the calculus of softmax attention: with P = exp(s*q.k - LSE),
 //   dV = P^T dO, dP = dO V^T, dS = P * (dP - delta), delta = rowsum(dO * O),
 //   dQ = s * dS K, dK = s * dS^T Q,
-// and the mean-pool spreads dX_c[c] / 64 over the cube's tokens, added here.
+// and the mean-pool spreads dX_c[c] / 64 over the cube's tokens (the
+// max-pool variant sends it to the cube's maximum), added here.
 //
 // Two kernels, both deterministic (no atomics), in the style of the forward:
 // a workgroup of two waves owns one cube, wave w its tokens 32w .. 32w+31,
@@ -28,6 +29,23 @@
 #include "vsa_kernels.h"
 
 namespace vsa {
+
+// Pool backward for one token and channels ch .. ch+3 of its cube: the pooled
+// gradient / 64 (mean pooling), or the whole pooled gradient where the token
+// holds the cube's maximum (arg = the cube's argmax positions, max pooling).
+__device__ __forceinline__ void pooled_grad(const float* dxc, const uint8_t* arg, int ch, int l, float out[4]) {
+  const float4 c4 = *reinterpret_cast<const float4*>(dxc + ch);
+  const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+  if (arg == nullptr) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[r] = cv[r] * (1.0f / kTile);
+  } else {
+    const uchar4 a4 = *reinterpret_cast<const uchar4*>(arg + ch);
+    const int av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[r] = av[r] == l ? cv[r] : 0.f;
+  }
+}
 
 // Processing order of the key cubes of every (b, h) for the dK / dV kernel:
 // descending length of their transposed lists, ties by cube id, so the
@@ -67,7 +85,8 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ kct,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
     const float* __restrict__ lse_f, const bf16* __restrict__ dof, const float* __restrict__ delta,
-    const float* __restrict__ dqc, bf16* __restrict__ dq, Grid g, int stride, float scale) {
+    const float* __restrict__ dqc, const uint8_t* __restrict__ qarg, bf16* __restrict__ dq, Grid g, int stride,
+    float scale) {
   using G = ChunkGeom<D>;
   __shared__ __attribute__((aligned(16))) bf16 rk[2][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rv[2][G::RUNITS * 8];
@@ -164,18 +183,21 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
       for (int mb = 0; mb < G::MB; ++mb) acc[mb] = mfma32_bf16(chunk_frag(tk[st], 32 * mb + n32, hf, s2), sf[s2], acc[mb]);
   }
 
-  // lane holds dQ^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query]
+  // lane holds dQ^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query]; the
+  // pooled gradient goes to every token (mean) or to the cube's maximum.
   const float* dqc_i = dqc + ((long)bh * g.Nc + i) * D;
+  const uint8_t* qarg_i = qarg != nullptr ? qarg + ((long)bh * g.Nc + i) * D : nullptr;
+  const int lq = 32 * wv + n32;   // the query's position in its cube
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
       const int ch = 32 * mb + 8 * jq + 4 * hf;
-      const float4 c4 = *reinterpret_cast<const float4*>(dqc_i + ch);
-      const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+      float cv[4];
+      pooled_grad(dqc_i, qarg_i, ch, lq, cv);
       bf16x4 w;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = (bf16)(scale * acc[mb][4 * jq + r] + cv[r] * (1.0f / kTile));
+      for (int r = 0; r < 4; ++r) w[r] = (bf16)(scale * acc[mb][4 * jq + r] + cv[r]);
       *reinterpret_cast<bf16x4*>(dq + n * D + ch) = w;
     }
 }
@@ -186,7 +208,8 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ qct, const bf16* __restrict__ doct, const int32_t* __restrict__ k2q_off,
     const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
     const bf16* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dkc,
-    const float* __restrict__ dvc, bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, int stride, float scale) {
+    const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, int stride, float scale) {
   using G = ChunkGeom<D>;
   __shared__ __attribute__((aligned(16))) bf16 rq[2][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rd[2][G::RUNITS * 8];
@@ -306,21 +329,23 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
   }
 
   // lane holds d{K,V}^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its key]
-  const float* dkc_j = dkc + ((long)bh * g.Nc + j) * D;
-  const float* dvc_j = dvc + ((long)bh * g.Nc + j) * D;
+  const long cj = ((long)bh * g.Nc + j) * D;
+  const uint8_t* karg_j = karg != nullptr ? karg + cj : nullptr;
+  const uint8_t* varg_j = varg != nullptr ? varg + cj : nullptr;
+  const int lk = 32 * wv + n32;   // the key's position in its cube
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
       const int ch = 32 * mb + 8 * jq + 4 * hf;
-      const float4 k4 = *reinterpret_cast<const float4*>(dkc_j + ch);
-      const float4 v4 = *reinterpret_cast<const float4*>(dvc_j + ch);
-      const float kcv[4] = {k4.x, k4.y, k4.z, k4.w}, vcv[4] = {v4.x, v4.y, v4.z, v4.w};
+      float kcv[4], vcv[4];
+      pooled_grad(dkc + cj, karg_j, ch, lk, kcv);
+      pooled_grad(dvc + cj, varg_j, ch, lk, vcv);
       bf16x4 wk, wvv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        wk[r] = (bf16)(scale * adk[mb][4 * jq + r] + kcv[r] * (1.0f / kTile));
-        wvv[r] = (bf16)(adv[mb][4 * jq + r] + vcv[r] * (1.0f / kTile));
+        wk[r] = (bf16)(scale * adk[mb][4 * jq + r] + kcv[r]);
+        wvv[r] = (bf16)(adv[mb][4 * jq + r] + vcv[r]);
       }
       *reinterpret_cast<bf16x4*>(dk + n * D + ch) = wk;
       *reinterpret_cast<bf16x4*>(dv + n * D + ch) = wvv;
@@ -339,18 +364,23 @@ hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const 
                            const bf16* kct, const int32_t* idx, const int32_t* len, const int32_t* qorder,
                            const int32_t* k2q_off, const int32_t* k2q, const int32_t* korder, const float* lse_f,
                            const bf16* dof, const bf16* doct, const float* delta, const float* dqc,
-                           const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv) {
+                           const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
+                           const uint8_t* args) {
   const int nitems = L.BH * L.g.Nc;
+  const long plane = (long)nitems * L.D;
+  const uint8_t* qarg = args;
+  const uint8_t* karg = args != nullptr ? args + plane : nullptr;
+  const uint8_t* varg = args != nullptr ? args + 2 * plane : nullptr;
   if (L.D == 64) {
     hipLaunchKernelGGL((fine_bwd_dq_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, kct, idx, len,
-                       qorder, lse_f, dof, delta, dqc, dq, L.g, L.stride, L.scale);
+                       qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
     hipLaunchKernelGGL((fine_bwd_dkdv_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, qct, doct,
-                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, dk, dv, L.g, L.stride, L.scale);
+                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
   } else {
     hipLaunchKernelGGL((fine_bwd_dq_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, kct, idx, len,
-                       qorder, lse_f, dof, delta, dqc, dq, L.g, L.stride, L.scale);
+                       qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
     hipLaunchKernelGGL((fine_bwd_dkdv_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, qct, doct,
-                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, dk, dv, L.g, L.stride, L.scale);
+                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
   }
   return hipGetLastError();
 }

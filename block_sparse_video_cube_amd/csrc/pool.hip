@@ -1,28 +1,32 @@
-// Step 1 of VSA: cube mean-pool, and the transposed V tiles of the fine stage.
+// Step 1 of VSA: cube mean-pool (or the max-pool variant), and the chunk
+// tiles of the fine stage.
 //
 // VSA summary page (paperlayer.ai, arXiv 2505.13389), section 2 "Methods"
 // (coarse stage mean-pools each cube) and Appendix B (block-mean of q, k, v);
 // VSA reading notes, key design 1 (Q_c, K_c, V_c: 64x shorter sequence).
 //
 // One workgroup per (b, h, cube). Each thread owns one 8-channel chunk of a
-// set of token rows, sums them in fp32, and the partial sums are reduced
-// through LDS. HBM-bound: every input element is read once; pooled means
+// set of token rows, sums them in fp32 (or keeps their maximum and its first
+// position), and the partial results are reduced through LDS. The max-pool
+// variant is the pooling the VSA summary page's ablation study compares
+// (section 3, Experiments). HBM-bound: every input element is read once; pooled means
 // (fp32) and optionally the bf16 V chunk tiles of the fine forward kernel
 // (layout in vsa_common.h) are written once.
 #include "vsa_kernels.h"
 
 namespace vsa {
 
-template <typename T, int D>
+template <typename T, int D, bool MAX>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, float* __restrict__ qc,
                                                    float* __restrict__ kc, float* __restrict__ vc,
-                                                   bf16* __restrict__ vt, Grid g) {
+                                                   bf16* __restrict__ vt, uint8_t* __restrict__ args, Grid g) {
   constexpr int CH = D / 8;            // 8-channel chunks per token row
   constexpr int RPP = 256 / CH;        // token rows per pass
   constexpr int PASSES = kTile / RPP;
   constexpr int VPITCH = D + 8;        // LDS row pitch of the staged V tile (bf16)
   __shared__ float part[RPP][D + 4];
+  __shared__ uint8_t parg[MAX ? RPP : 1][D + 4];
   __shared__ bf16 vtile[kTile][VPITCH];
 
   const int tid = threadIdx.x;
@@ -30,33 +34,59 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   const int c = blockIdx.x;
   const int ch = tid % CH, rsub = tid / CH;
   const long base = bh * (long)g.N * D;
+  const long plane = (long)gridDim.y * g.Nc * D;   // one tensor's args
 
   const T* srcs[3] = {q, k, v};
   float* dsts[3] = {qc, kc, vc};
 #pragma unroll
   for (int which = 0; which < 3; ++which) {
     const T* src = srcs[which] + base;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float acc[8];
+    int am[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { acc[e] = MAX ? -INFINITY : 0.f; am[e] = 0; }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      const int l = p * RPP + rsub;
+      const int l = p * RPP + rsub;   // increasing: a strict compare keeps the first maximum
       float x[8];
       load8(src + (long)cube_token(g, c, l) * D + ch * 8, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+      for (int e = 0; e < 8; ++e) {
+        if (MAX) {
+          if (x[e] > acc[e]) { acc[e] = x[e]; am[e] = l; }
+        } else {
+          acc[e] += x[e];
+        }
+      }
       if (which == 2 && vt != nullptr) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vtile[l][ch * 8 + e] = (bf16)x[e];
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) part[rsub][ch * 8 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) {
+      part[rsub][ch * 8 + e] = acc[e];
+      if (MAX) parg[rsub][ch * 8 + e] = (uint8_t)am[e];
+    }
     __syncthreads();
     if (tid < D) {
-      float s = 0.f;
+      if (MAX) {
+        float best = part[0][tid];
+        int ba = parg[0][tid];
 #pragma unroll
-      for (int r = 0; r < RPP; ++r) s += part[r][tid];
-      dsts[which][(bh * g.Nc + c) * D + tid] = s * (1.0f / kTile);
+        for (int r = 1; r < RPP; ++r) {
+          const float y = part[r][tid];
+          const int a = parg[r][tid];
+          if (y > best || (y == best && a < ba)) { best = y; ba = a; }   // ties: first in cube order
+        }
+        if (dsts[which] != nullptr) dsts[which][(bh * g.Nc + c) * D + tid] = best;
+        if (args != nullptr) args[which * plane + (bh * g.Nc + c) * D + tid] = (uint8_t)ba;
+      } else {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPP; ++r) s += part[r][tid];
+        if (dsts[which] != nullptr) dsts[which][(bh * g.Nc + c) * D + tid] = s * (1.0f / kTile);
+      }
     }
     __syncthreads();
   }
@@ -84,23 +114,26 @@ __global__ __launch_bounds__(256) void ctile_kernel(const bf16* __restrict__ x, 
   store_chunk_tiles<D, VPITCH>(tile, xt + (bh * g.Nc + c) * (long)D * kTile, tid, 256);
 }
 
-hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
-                       float* vc, bf16* vt) {
+template <typename T, bool MAX>
+static void pool_launch(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
+                        float* vc, bf16* vt, uint8_t* args) {
   const dim3 grid(L.g.Nc, L.BH), block(256);
+  if (L.D == 64)
+    hipLaunchKernelGGL((pool_kernel<T, 64, MAX>), grid, block, 0, L.stream, (const T*)q, (const T*)k, (const T*)v,
+                       qc, kc, vc, vt, args, L.g);
+  else
+    hipLaunchKernelGGL((pool_kernel<T, 128, MAX>), grid, block, 0, L.stream, (const T*)q, (const T*)k,
+                       (const T*)v, qc, kc, vc, vt, args, L.g);
+}
+
+hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
+                       float* vc, bf16* vt, uint8_t* args) {
   if (L.bf16) {
-    if (L.D == 64)
-      hipLaunchKernelGGL((pool_kernel<bf16, 64>), grid, block, 0, L.stream, (const bf16*)q, (const bf16*)k,
-                         (const bf16*)v, qc, kc, vc, vt, L.g);
-    else
-      hipLaunchKernelGGL((pool_kernel<bf16, 128>), grid, block, 0, L.stream, (const bf16*)q, (const bf16*)k,
-                         (const bf16*)v, qc, kc, vc, vt, L.g);
+    if (L.pool_max) pool_launch<bf16, true>(L, q, k, v, qc, kc, vc, vt, args);
+    else pool_launch<bf16, false>(L, q, k, v, qc, kc, vc, vt, nullptr);
   } else {
-    if (L.D == 64)
-      hipLaunchKernelGGL((pool_kernel<float, 64>), grid, block, 0, L.stream, (const float*)q, (const float*)k,
-                         (const float*)v, qc, kc, vc, (bf16*)nullptr, L.g);
-    else
-      hipLaunchKernelGGL((pool_kernel<float, 128>), grid, block, 0, L.stream, (const float*)q,
-                         (const float*)k, (const float*)v, qc, kc, vc, (bf16*)nullptr, L.g);
+    if (L.pool_max) pool_launch<float, true>(L, q, k, v, qc, kc, vc, nullptr, args);
+    else pool_launch<float, false>(L, q, k, v, qc, kc, vc, nullptr, nullptr);
   }
   return hipGetLastError();
 }

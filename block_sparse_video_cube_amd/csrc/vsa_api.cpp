@@ -37,6 +37,7 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
   if (p->topk > 0 && stride < p->topk) return VSA_ERR_TOPK;
   if (stride < 1 || stride > Nc) return VSA_ERR_TOPK;
   if (Nc > coarse_max_cubes()) return VSA_ERR_UNSUPPORTED;
+  if (p->pool_mode != VSA_POOL_MEAN && p->pool_mode != VSA_POOL_MAX) return VSA_ERR_UNSUPPORTED;
   if (L != nullptr) {
     L->g = make_grid(p->T, p->H, p->W);
     L->BH = (int)BH;
@@ -45,6 +46,7 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
     L->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
     L->topk = p->topk;
     L->stride = (int)stride;
+    L->pool_max = p->pool_mode == VSA_POOL_MAX;
     L->stream = nullptr;
   }
   if (d != nullptr) {
@@ -131,6 +133,7 @@ struct BwdWs {
   float *delta, *doc, *dqc, *dkc, *dvc, *p_scr, *ds_scr, *dc_scr;
   int32_t *k2q_off, *k2q, *qorder, *korder;
   uint32_t* k2q_bits;
+  uint8_t* args;   // max pooling: argmax positions of q, k, v
   size_t bytes;
 };
 BwdWs carve_bwd_ws(const Dims& d, void* base) {
@@ -156,6 +159,7 @@ BwdWs carve_bwd_ws(const Dims& d, void* base) {
   w.k2q_bits = c.take<uint32_t>(d.BH * d.Nc * (size_t)k2q_bits_words((int)d.Nc));
   w.qorder = c.take<int32_t>(d.BH * d.Nc);
   w.korder = c.take<int32_t>(d.BH * d.Nc);
+  w.args = c.take<uint8_t>(3 * d.BH * d.Nc * d.D);
   w.bytes = c.off;
   return w;
 }
@@ -257,11 +261,12 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   if (e == hipSuccess) e = launch_ctile(L, static_cast<const bf16*>(k), ws.kt);
   if (e == hipSuccess) e = launch_order(L, idx, len, ws.qorder);
   if (e == hipSuccess) e = launch_order_by_count(L, ws.k2q_off, ws.korder);
+  if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, nullptr, ws.args);
   if (e == hipSuccess)
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                         ws.qt, ws.kt, idx, len, ws.qorder, ws.k2q_off, ws.k2q, ws.korder, s.lse_f, ws.dof, ws.doft,
                         ws.delta, ws.dqc, ws.dkc, ws.dvc, static_cast<bf16*>(dq), static_cast<bf16*>(dk),
-                        static_cast<bf16*>(dv));
+                        static_cast<bf16*>(dv), L.pool_max ? ws.args : nullptr);
   return hip_status(e);
 }
 
@@ -414,11 +419,12 @@ vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k,
   if (e == hipSuccess) e = launch_ctile(L, static_cast<const bf16*>(k), ws.kt);
   if (e == hipSuccess) e = launch_order(L, idx, len, ws.qorder);
   if (e == hipSuccess) e = launch_order_by_count(L, k2q_off, ws.korder);
+  if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, nullptr, ws.args);
   if (e == hipSuccess)
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                         ws.qt, ws.kt, idx, len, ws.qorder, k2q_off, k2q, ws.korder, lse_f,
                         static_cast<const bf16*>(d_o_f), ws.doft, delta, dq_c, dk_c, dv_c, static_cast<bf16*>(dq),
-                        static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+                        static_cast<bf16*>(dk), static_cast<bf16*>(dv), L.pool_max ? ws.args : nullptr);
   return hip_status(e);
 }
 

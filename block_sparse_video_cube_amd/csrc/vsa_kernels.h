@@ -14,11 +14,16 @@ struct Launch {
   float scale;     // softmax scale (resolved, > 0)
   int topk;        // > 0: top-K mode
   int stride;      // idx row stride
+  bool pool_max;   // max pooling instead of mean (the ablation variant)
   hipStream_t stream;
 };
 
+// Pooled q / k / v (fp32; each may be null = not written), the V chunk tiles
+// (bf16 problems; may be null) and, with max pooling, the in-cube index of
+// each (cube, channel) maximum (args: 3 x B*heads*Nc*D bytes for q, k, v;
+// may be null).
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
-                       float* vc, bf16* vt);
+                       float* vc, bf16* vt, uint8_t* args = nullptr);
 // Chunk tiles (layout in vsa_common.h) of a raster bf16 tensor.
 hipError_t launch_ctile(const Launch& L, const bf16* x, bf16* xt);
 
@@ -59,12 +64,15 @@ hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_
 // Fine backward (bf16): dq over the forward lists (qorder from launch_order,
 // may be null), dk / dv over the transposed lists (korder from
 // launch_order_by_count, may be null). qct / kct / doct: chunk tiles of q, k
-// and d_o_f. The pooled gradients dqc / dkc / dvc are spread over their cubes.
+// and d_o_f. The pooled gradients dqc / dkc / dvc are spread over their cubes
+// (mean pooling), or go to the maxima given by args (max pooling; layout of
+// launch_pool's args).
 hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const bf16* qct,
                            const bf16* kct, const int32_t* idx, const int32_t* len, const int32_t* qorder,
                            const int32_t* k2q_off, const int32_t* k2q, const int32_t* korder, const float* lse_f,
                            const bf16* dof, const bf16* doct, const float* delta, const float* dqc,
-                           const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv);
+                           const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
+                           const uint8_t* args);
 
 hipError_t launch_validate_lists(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* flag);
 

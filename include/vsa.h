@@ -58,12 +58,19 @@ typedef enum {
   VSA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned               */
   VSA_ERR_WORKSPACE = 7,   /* workspace / saved buffer smaller than required */
   VSA_ERR_INDEX = 8,       /* an index list failed validation                */
-  VSA_ERR_UNSUPPORTED = 9, /* valid request this build does not implement    */
+  VSA_ERR_UNSUPPORTED = 9, /* valid request this build does not implement,
+                              or an unknown pool_mode                         */
   VSA_ERR_HIP = 10,        /* a HIP call or kernel launch failed             */
   VSA_ERR_SCALE = 11       /* scale is negative, NaN or infinite             */
 } vsa_status;
 
 typedef enum { VSA_F32 = 0, VSA_BF16 = 1 } vsa_dtype;
+
+/* Cube pooling of the coarse stage. MEAN is the method (VSA summary page,
+ * section 2 and Appendix B); MAX is the variant its ablation study compares
+ * (section 3, Experiments): the per-channel maximum over a cube, whose
+ * gradient goes to the first maximum in cube order. */
+typedef enum { VSA_POOL_MEAN = 0, VSA_POOL_MAX = 1 } vsa_pool_mode;
 
 typedef struct {
   int32_t B, heads;      /* batch and heads; every (b, h) is independent      */
@@ -75,6 +82,7 @@ typedef struct {
                             (1..Nc); 0: the caller supplies the lists          */
   int32_t list_stride;   /* row stride of idx; 0 => topk. Top-K mode needs
                             list_stride >= topk; list mode needs 1..Nc         */
+  int32_t pool_mode;     /* vsa_pool_mode; 0 = mean                            */
 } vsa_problem;
 
 /* Short text for a status code (static storage, never NULL). */

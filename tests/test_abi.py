@@ -70,11 +70,18 @@ def _fwd(p, **ptrs):
     (dict(topk=0, list_stride=9), TOPK), (dict(topk=4, list_stride=3), TOPK),
     (dict(scale=-1.0), SCALE), (dict(scale=float("nan")), SCALE), (dict(scale=float("inf")), SCALE),
     (dict(T=4, H=4 * 64, W=4 * 33), UNSUP),       # Nc = 2112 > vsa_max_cubes()
+    (dict(pool="median"), UNSUP),                 # unknown pool_mode
 ])
 def test_problem_validation(kw, code):
     p = _p(**kw)
     assert _fwd(p) == code
     assert V.workspace_bytes(p) == 0 and V.saved_bytes(p) == 0
+
+
+def test_max_pool_problem_is_valid():
+    p = _p(pool="max")
+    assert V.workspace_bytes(p) > 0 and V.saved_bytes(p) > 0
+    assert V.workspace_bytes(p, training=True) >= V.workspace_bytes(_p(), training=True)
 
 
 @pytest.mark.parametrize("name", ["q", "k", "v", "idx", "len", "o", "ws"])

@@ -10,6 +10,8 @@ Bars (from the operator's contract):
 Outputs are compared with the oracle re-run on the GPU's own lists, so a
 legitimate near-tie choice cannot fail an output comparison.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -353,7 +355,7 @@ def backward_compare(x, p, dtype, rel=BF16_REL, gates=True):
     g = V.backward(p, d["q"], d["k"], d["v"], gc, gf, idx, lens, saved, d["d_o"])
     torch.cuda.synchronize()
     xg = (x["g_c"], x["g_f"]) if gates else (None, None)
-    fwd = O.forward(x["q"], x["k"], x["v"], *xg, topk=0, idx=x["idx"], lens=x["len"])
+    fwd = O.forward(x["q"], x["k"], x["v"], *xg, topk=0, idx=x["idx"], lens=x["len"], pool_mode=p.pool)
     assert_close(host(o), fwd["o"], dtype, "o")
     ref = O.backward(x["q"], x["k"], x["v"], *xg, x["d_o"], fwd)
     names = ("dq", "dk", "dv", "dg_c", "dg_f") if gates else ("dq", "dk", "dv")
@@ -441,3 +443,35 @@ def test_backward_stages():
     torch.cuda.synchronize()
     for got, nm in ((dqc, "dq_c"), (dkc, "dk_c"), (dvc, "dv_c")):
         assert rel_err(host(got), ref[nm]) <= 1e-4, nm
+
+
+# ------------------------------------------------------- max-pool variant
+@pytest.mark.parametrize("name", ["C1", "C2"])
+def test_max_pool_forward_topk(name):
+    """The max-pool variant: pooled maxima bit-exact (a maximum of exact
+    inputs is exact in fp32), top-K protocol with the variant's error bound,
+    end-to-end output on the GPU's lists."""
+    w = WL.get(name)
+    hs = [0, 1]
+    x = WL.make_inputs(name, heads=hs)
+    p = problem_of(w, heads=2, pool="max")
+    d = inputs_to_dev(x, w.dtype)
+    qc, kc, vc = V.pool(p, d["q"], d["k"], d["v"])
+    o, idx, lens, _ = V.forward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"])
+    torch.cuda.synchronize()
+    for got, src in ((qc, "q"), (kc, "k"), (vc, "v")):
+        assert np.array_equal(host(got), O.pool(O.tile(x[src].astype(np.float64)), "max")), src
+    ref_sel = O.forward(x["q"], x["k"], x["v"], topk=w.topk, pool_mode="max")
+    gi = host(idx)
+    near = check_topk(gi, ref_sel, w.topk)
+    assert near <= NEAR_FRAC * gi.shape[0] * gi.shape[1] * gi.shape[2] + 2
+    ref = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=host(lens), pool_mode="max")
+    assert_close(host(o), ref["o"], w.dtype, "o")
+    mean = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=host(lens))
+    assert rel_err(mean["o"], ref["o"]) > 1e-2   # the variant is a different operator
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_max_pool_backward(d):
+    x, p = _small_train_inputs(d=d, seed=9, heads=2 if d == 64 else 1, T=8, H=8 if d == 128 else 16, W=16)
+    backward_compare(x, dataclasses.replace(p, pool="max"), "bf16")
