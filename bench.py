@@ -141,7 +141,7 @@ def train_measure(name: str, steps: int, warmup: int) -> dict:
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for e in ev:
         e[0].record()
-        cb = V.combine_backward(p, d_o, sv["o_c"], sv["o_f"], gc, gf, ws=ws_b)
+        cb = V.combine_backward(p, d_o, sv["o_c"], sv["o_f"], gc, gf)
         e[1].record()
         off, k2q = V.index_transpose(p, idx, lens, ws=ws_b)
         e[2].record()

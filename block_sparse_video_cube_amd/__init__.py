@@ -210,15 +210,14 @@ def combine(p: Problem, o_c, o_f, g_c=None, g_f=None):
     return o
 
 
-def combine_backward(p: Problem, d_o, o_c, o_f, g_c=None, g_f=None, ws: Optional[torch.Tensor] = None):
+def combine_backward(p: Problem, d_o, o_c, o_f, g_c=None, g_f=None):
     dgc = _empty(_raster(p), p.torch_dtype, d_o) if g_c is not None else None
     dgf = _empty(_raster(p), p.torch_dtype, d_o) if g_f is not None else None
     dof = _empty(_raster(p), p.torch_dtype, d_o)
     delta = _empty((p.B, p.heads, p.T, p.H, p.W), torch.float32, d_o)
     doc = _empty(_pooled(p), torch.float32, d_o)
     check(lib().vsa_combine_backward(ctypes.byref(p.c()), _ptr(d_o), _ptr(o_c), _ptr(o_f), _ptr(g_c), _ptr(g_f),
-                                     _ptr(dgc), _ptr(dgf), _ptr(dof), _ptr(delta), _ptr(doc), _ptr(ws),
-                                     0 if ws is None else ws.numel(), _stream(d_o.device)),
+                                     _ptr(dgc), _ptr(dgf), _ptr(dof), _ptr(delta), _ptr(doc), _stream(d_o.device)),
           "vsa_combine_backward")
     return dict(dg_c=dgc, dg_f=dgf, d_o_f=dof, delta=delta, d_o_c=doc)
 

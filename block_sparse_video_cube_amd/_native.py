@@ -45,7 +45,7 @@ SIGNATURES = {
     "vsa_fine_forward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_fine_combine": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_combine": (_i32, [_P, _v, _v, _v, _v, _v, _v]),
-    "vsa_combine_backward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
+    "vsa_combine_backward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v]),
     "vsa_index_transpose": (_i32, [_P, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_fine_backward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v,
                                  _v, _sz, _v]),

@@ -37,15 +37,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // Backward of the combine, one workgroup per (b, h, cube):
 //   dg_c = dO * O_c[c], dg_f = dO * O_f, d_o_f = dO * G_f (rounded to T),
 //   delta[token] = sum_ch d_o_f * O_f, d_o_c[c] = sum over the cube of dO * G_c,
-//   and (bf16, optional) the chunk tiles of d_o_f.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ d_o, const float* __restrict__ oc, const T* __restrict__ of, const T* __restrict__ gc,
     const T* __restrict__ gf, T* __restrict__ dgc, T* __restrict__ dgf, T* __restrict__ dof,
-    float* __restrict__ delta, float* __restrict__ doc, bf16* __restrict__ doft, Grid g) {
-  constexpr int CH = D / 8, RPP = 256 / CH, PASSES = kTile / RPP, VPITCH = D + 8;
+    float* __restrict__ delta, float* __restrict__ doc, Grid g) {
+  constexpr int CH = D / 8, RPP = 256 / CH, PASSES = kTile / RPP;
   __shared__ float part[RPP][D + 4];
-  __shared__ bf16 tile[kTile][VPITCH];
   const int tid = threadIdx.x;
   const long bh = blockIdx.y;
   const int c = blockIdx.x;
@@ -79,10 +77,6 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     if (dgc != nullptr) store8(dgc + off, r1);
     if (dgf != nullptr) store8(dgf + off, r2);
     store8(dof + off, r3);
-    if (doft != nullptr) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) tile[l][ch * 8 + i] = (bf16)r3[i];
-    }
 #pragma unroll
     for (int o = CH / 2; o >= 1; o >>= 1) dsum += __shfl_xor(dsum, o, 64);
     if (ch == 0) delta[tok] = dsum;
@@ -96,7 +90,6 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     for (int r = 0; r < RPP; ++r) s += part[r][tid];
     doc[(bh * g.Nc + c) * D + tid] = s;
   }
-  if (doft != nullptr) store_chunk_tiles<D, VPITCH>(tile, doft + (bh * g.Nc + c) * (long)D * kTile, tid, 256);
 }
 
 hipError_t launch_combine(const Launch& L, const float* oc, const void* of, const void* gc, const void* gf,
@@ -123,26 +116,26 @@ hipError_t launch_combine(const Launch& L, const float* oc, const void* of, cons
 
 hipError_t launch_combine_bwd(const Launch& L, const void* d_o, const float* oc, const void* of,
                               const void* gc, const void* gf, void* dgc, void* dgf, void* dof,
-                              float* delta, float* doc, bf16* doft) {
+                              float* delta, float* doc) {
   const dim3 grid(L.g.Nc, L.BH), block(256);
   if (L.bf16) {
     if (L.D == 64)
       hipLaunchKernelGGL((combine_bwd_kernel<bf16, 64>), grid, block, 0, L.stream, (const bf16*)d_o, oc,
                          (const bf16*)of, (const bf16*)gc, (const bf16*)gf, (bf16*)dgc, (bf16*)dgf, (bf16*)dof,
-                         delta, doc, doft, L.g);
+                         delta, doc, L.g);
     else
       hipLaunchKernelGGL((combine_bwd_kernel<bf16, 128>), grid, block, 0, L.stream, (const bf16*)d_o, oc,
                          (const bf16*)of, (const bf16*)gc, (const bf16*)gf, (bf16*)dgc, (bf16*)dgf, (bf16*)dof,
-                         delta, doc, doft, L.g);
+                         delta, doc, L.g);
   } else {
     if (L.D == 64)
       hipLaunchKernelGGL((combine_bwd_kernel<float, 64>), grid, block, 0, L.stream, (const float*)d_o, oc,
                          (const float*)of, (const float*)gc, (const float*)gf, (float*)dgc, (float*)dgf,
-                         (float*)dof, delta, doc, (bf16*)nullptr, L.g);
+                         (float*)dof, delta, doc, L.g);
     else
       hipLaunchKernelGGL((combine_bwd_kernel<float, 128>), grid, block, 0, L.stream, (const float*)d_o, oc,
                          (const float*)of, (const float*)gc, (const float*)gf, (float*)dgc, (float*)dgf,
-                         (float*)dof, delta, doc, (bf16*)nullptr, L.g);
+                         (float*)dof, delta, doc, L.g);
   }
   return hipGetLastError();
 }

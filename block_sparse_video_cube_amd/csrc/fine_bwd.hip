@@ -12,19 +12,21 @@
 // Two kernels, both deterministic (no atomics), in the style of the forward:
 // a workgroup of two waves owns one cube, wave w its tokens 32w .. 32w+31,
 // one per lane (column) of 32x32x16 bf16 MFMAs, and walks a list of partner
-// cubes in 32-token chunks staged in LDS by direct-to-LDS loads (each wave
-// issues half; the next chunk loads while this one is computed).
+// cubes in 32-token chunks: row tiles of the partner's tensors staged in LDS
+// by direct-to-LDS loads (each wave issues half; the next chunk loads while
+// this one is computed). The transposed operands come from the same row
+// tiles through LDS transpose reads.
 //  * dQ, per query cube i over its list of key cubes (the forward's list):
 //      S^T = K_c Q^T, dP^T = V_c dO^T        A = K / V row tiles, B = the
 //                                            lane's Q / dO row (registers)
 //      dS^T = P^T * (dP^T - delta)            LSE and delta are lane scalars
-//      dQ^T += K_c^T dS^T                     A = K chunk tile, B = dS^T
+//      dQ^T += K_c^T dS^T                     A = K row tile read transposed, B = dS^T
 //  * dK and dV, per key cube j over the query cubes whose lists hold j (the
 //    transposed lists), longest list first:
 //      S = Q_c K^T, dP = dO_c V^T            A = Q / dO row tiles, B = the
 //                                            lane's K / V row (registers)
 //      dS = P * (dP - delta)                 LSE and delta per row (query)
-//      dV^T += dO_c^T P, dK^T += Q_c^T dS     A = dO / Q chunk tiles
+//      dV^T += dO_c^T P, dK^T += Q_c^T dS     A = dO / Q row tiles read transposed
 #include "fine_common.h"
 #include "vsa_kernels.h"
 
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(1024) void order_by_count_kernel(const int32_t* __r
 
 template <int D>
 __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v, const bf16* __restrict__ kct,
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
     const float* __restrict__ lse_f, const bf16* __restrict__ dof, const float* __restrict__ delta,
     const float* __restrict__ dqc, const uint8_t* __restrict__ qarg, bf16* __restrict__ dq, Grid g, int stride,
@@ -90,7 +92,6 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
   using G = ChunkGeom<D>;
   __shared__ __attribute__((aligned(16))) bf16 rk[2][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rv[2][G::RUNITS * 8];
-  __shared__ __attribute__((aligned(16))) bf16 tk[2][G::TUNITS * 8];
 
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -120,31 +121,31 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
 
-  uint32_t roff[G::RINS / 2], toff[G::TINS / 2];
+  uint32_t roff[G::RINS / 2];
   row_tile_offsets<D>(g, wv, lane, roff);
-  chunk_tile_offsets<D>(wv, lane, toff);
-  const uint32_t rhalf = (uint32_t)(2 * g.H * g.W * D) * 2u, thalf = (uint32_t)(D * 32) * 2u;
+  uint32_t toffs[G::MB][2][2];   // transposed reads of the K row tile (dQ^T += K^T dS^T)
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, toffs[mb][s2]);
+  const uint32_t rhalf = (uint32_t)(2 * g.H * g.W * D) * 2u;
   const char* Kb = reinterpret_cast<const char*>(k + tok0 * D);
   const char* Vb = reinterpret_cast<const char*>(v + tok0 * D);
-  const char* Tb = reinterpret_cast<const char*>(kct + (long)bh * g.Nc * D * kTile);
   // Byte offsets of the list's cubes, 64 entries at a time, one per lane.
-  uint32_t rcube = 0, tcube = 0;
+  uint32_t rcube = 0;
   auto cubes = [&](int t0) {
     const int t = t0 + lane;
     int j = t < L ? list[t] : 0;
     j = (j >= 0 && j < g.Nc) ? j : 0;
     rcube = (uint32_t)cube_row(g, j, 0, 0) * (uint32_t)(D * 2);
-    tcube = (uint32_t)j * (uint32_t)(D * kTile * 2);
   };
-  const uint32_t rkb = lds_addr(rk), rvb = lds_addr(rv), tkb = lds_addr(tk);
+  const uint32_t rkb = lds_addr(rk), rvb = lds_addr(rv);
   auto issue = [&](int c) {
     const int e = c >> 1, h = c & 1, st = c & 1;
     if ((e & 63) == 0 && h == 0) cubes(e);
     const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + (h ? rhalf : 0u);
-    const uint32_t tc = __builtin_amdgcn_readlane(tcube, e & 63) + (h ? thalf : 0u);
     issue_row_tile<D>(uniform_ptr(Kb + rc), roff, rkb + st * (G::RUNITS * 16), wv);
     issue_row_tile<D>(uniform_ptr(Vb + rc), roff, rvb + st * (G::RUNITS * 16), wv);
-    issue_chunk_tile<D>(uniform_ptr(Tb + tc), toff, tkb + st * (G::TUNITS * 16), wv);
   };
 
   // Per chunk: wait for this wave's loads, barrier (both halves are in LDS
@@ -177,10 +178,12 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
       const float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2);
       sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl));
     }
+    const char* kt = reinterpret_cast<const char*>(rk[st]);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int mb = 0; mb < G::MB; ++mb) acc[mb] = mfma32_bf16(chunk_frag(tk[st], 32 * mb + n32, hf, s2), sf[s2], acc[mb]);
+      for (int mb = 0; mb < G::MB; ++mb)
+        acc[mb] = mfma32_bf16(rowt_frag(kt, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], acc[mb]);
   }
 
   // lane holds dQ^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query]; the
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
 template <int D>
 __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const bf16* __restrict__ qct, const bf16* __restrict__ doct, const int32_t* __restrict__ k2q_off,
+    const int32_t* __restrict__ k2q_off,
     const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
     const bf16* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dkc,
     const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
@@ -213,8 +216,6 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
   using G = ChunkGeom<D>;
   __shared__ __attribute__((aligned(16))) bf16 rq[2][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rd[2][G::RUNITS * 8];
-  __shared__ __attribute__((aligned(16))) bf16 tq[2][G::TUNITS * 8];
-  __shared__ __attribute__((aligned(16))) bf16 td[2][G::TUNITS * 8];
 
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -242,27 +243,28 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) { adk[mb][e] = 0.f; adv[mb][e] = 0.f; }
 
-  uint32_t roff[G::RINS / 2], toff[G::TINS / 2];
+  uint32_t roff[G::RINS / 2];
   row_tile_offsets<D>(g, wv, lane, roff);
-  chunk_tile_offsets<D>(wv, lane, toff);
-  const uint32_t rhalf = (uint32_t)(2 * g.H * g.W * D) * 2u, thalf = (uint32_t)(D * 32) * 2u;
+  uint32_t toffs[G::MB][2][2];   // transposed reads of the Q / dO row tiles
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, toffs[mb][s2]);
+  const uint32_t rhalf = (uint32_t)(2 * g.H * g.W * D) * 2u;
   const char* Qb = reinterpret_cast<const char*>(q + tok0 * D);
   const char* Db = reinterpret_cast<const char*>(dof + tok0 * D);
-  const char* TQb = reinterpret_cast<const char*>(qct + (long)bh * g.Nc * D * kTile);
-  const char* TDb = reinterpret_cast<const char*>(doct + (long)bh * g.Nc * D * kTile);
-  // Per lane, for 64 list entries at a time: the partner cube, its first
-  // row's byte offset and its chunk tiles' byte offset.
+  // Per lane, for 64 list entries at a time: the partner cube and its first
+  // row's byte offset.
   int icube = 0;
-  uint32_t rcube = 0, tcube = 0;
+  uint32_t rcube = 0;
   auto cubes = [&](int e0) {
     const int t = e0 + lane;
     int ii = t < L ? list[t] : 0;
     ii = (ii >= 0 && ii < g.Nc) ? ii : 0;
     icube = ii;
     rcube = (uint32_t)cube_row(g, ii, 0, 0) * (uint32_t)(D * 2);
-    tcube = (uint32_t)ii * (uint32_t)(D * kTile * 2);
   };
-  const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd), tqb = lds_addr(tq), tdb = lds_addr(td);
+  const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd);
   // LSE and delta of the chunk's query rows this lane's accumulator holds:
   // rows 8m + 4hf + r (m, r = 0..3) = token (2h + m/2, (2m + hf)%4, r).
   float4 lsn[4], dln[4];
@@ -277,11 +279,8 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
       dln[m] = *reinterpret_cast<const float4*>(delta + r);
     }
     const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + (h ? rhalf : 0u);
-    const uint32_t tc = __builtin_amdgcn_readlane(tcube, e & 63) + (h ? thalf : 0u);
     issue_row_tile<D>(uniform_ptr(Qb + rc), roff, rqb + st * (G::RUNITS * 16), wv);
     issue_row_tile<D>(uniform_ptr(Db + rc), roff, rdb + st * (G::RUNITS * 16), wv);
-    issue_chunk_tile<D>(uniform_ptr(TQb + tc), toff, tqb + st * (G::TUNITS * 16), wv);
-    issue_chunk_tile<D>(uniform_ptr(TDb + tc), toff, tdb + st * (G::TUNITS * 16), wv);
   };
 
   const int nch = 2 * L;
@@ -319,12 +318,14 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
       pf[e >> 3][e & 7] = (bf16)p;
       sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl[e]));
     }
+    const char* qtile = reinterpret_cast<const char*>(rq[st]);
+    const char* dtile = reinterpret_cast<const char*>(rd[st]);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb) {
-        adv[mb] = mfma32_bf16(chunk_frag(td[st], 32 * mb + n32, hf, s2), pf[s2], adv[mb]);
-        adk[mb] = mfma32_bf16(chunk_frag(tq[st], 32 * mb + n32, hf, s2), sf[s2], adk[mb]);
+        adv[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], adv[mb]);
+        adk[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], adk[mb]);
       }
   }
 
@@ -360,11 +361,10 @@ hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_
   return hipGetLastError();
 }
 
-hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const bf16* qct,
-                           const bf16* kct, const int32_t* idx, const int32_t* len, const int32_t* qorder,
-                           const int32_t* k2q_off, const int32_t* k2q, const int32_t* korder, const float* lse_f,
-                           const bf16* dof, const bf16* doct, const float* delta, const float* dqc,
-                           const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
+hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
+                           const int32_t* len, const int32_t* qorder, const int32_t* k2q_off, const int32_t* k2q,
+                           const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
+                           const float* dqc, const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
                            const uint8_t* args) {
   const int nitems = L.BH * L.g.Nc;
   const long plane = (long)nitems * L.D;
@@ -372,15 +372,15 @@ hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const 
   const uint8_t* karg = args != nullptr ? args + plane : nullptr;
   const uint8_t* varg = args != nullptr ? args + 2 * plane : nullptr;
   if (L.D == 64) {
-    hipLaunchKernelGGL((fine_bwd_dq_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, kct, idx, len,
-                       qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
-    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, qct, doct,
-                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
+    hipLaunchKernelGGL((fine_bwd_dq_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, idx, len, qorder,
+                       lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, k2q_off, k2q,
+                       korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
   } else {
-    hipLaunchKernelGGL((fine_bwd_dq_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, kct, idx, len,
-                       qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
-    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, qct, doct,
-                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
+    hipLaunchKernelGGL((fine_bwd_dq_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, idx, len, qorder,
+                       lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, k2q_off, k2q,
+                       korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
   }
   return hipGetLastError();
 }

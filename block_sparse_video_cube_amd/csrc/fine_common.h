@@ -99,4 +99,37 @@ __device__ __forceinline__ bf16x8 chunk_frag(const bf16* tile, int dd, int hf, i
   return *reinterpret_cast<const bf16x8*>(tile + (dd * 4 + ((2 * s2 + hf) ^ vunit_swz(dd))) * 8);
 }
 
+// Transposed A fragments straight from a row tile, by the LDS transpose read
+// ds_read_b64_tr_b16. Within each group of 16 lanes, that read hands output
+// lane t the element t % 4 of the 8 bytes source lane 4e + t / 4 addressed,
+// as its element e. So if source lane 4e + j reads row r0 + e at channels
+// c0 + 4j .. +3, output lane t receives channel c0 + t of rows r0 .. r0 + 3.
+// For the A operand of O^T-style products (A[m = channel 32mb + lane%32][k =
+// slot 16s2 + 8hf + e], whose B operand is a 32x32 accumulator), slot e of
+// lane half hf must hold row 16s2 + 8(e/4) + 4hf + e%4 (the accumulator's row
+// order, as in the chunk tiles): two reads, rows 16s2 + 4hf + 0..3 and
+// 16s2 + 8 + 4hf + 0..3. rowt_offsets gives each lane's two byte offsets
+// (within a tile) for fragment (mb, s2); rowt_frag performs the reads.
+typedef short tr16x4 __attribute__((ext_vector_type(4)));
+template <int D> __device__ __forceinline__ void rowt_offsets(int lane, int mb, int s2, uint32_t off[2]) {
+  using G = ChunkGeom<D>;
+  const int g16 = lane >> 4, s = lane & 15, e = s >> 2, j = s & 3;
+  const int hf = g16 >> 1, ch = 32 * mb + 16 * (g16 & 1) + 4 * j;
+  const int u = ch >> 3, within = (ch & 7) * 2;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int r = 16 * s2 + 8 * half + 4 * hf + e;
+    off[half] = (uint32_t)((r * G::U + (u ^ kswz<G::U>(r))) * 16 + within);
+  }
+}
+__device__ __forceinline__ bf16x8 rowt_frag(const char* tile, uint32_t off0, uint32_t off1) {
+  typedef __attribute__((address_space(3))) tr16x4 lds_tr;
+  const tr16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr*)(tile + off0));
+  const tr16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_tr*)(tile + off1));
+  const tr16x4 v[2] = {a, b};
+  bf16x8 r;
+  __builtin_memcpy(&r, v, sizeof(r));
+  return r;
+}
+
 }  // namespace vsa

@@ -94,26 +94,6 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   if (vt != nullptr) store_chunk_tiles<D, VPITCH>(vtile, vt + (bh * g.Nc + c) * (long)D * kTile, tid, 256);
 }
 
-// Chunk tiles of a raster bf16 tensor (the backward's Q and K).
-template <int D>
-__global__ __launch_bounds__(256) void ctile_kernel(const bf16* __restrict__ x, bf16* __restrict__ xt, Grid g) {
-  constexpr int CH = D / 8, RPP = 256 / CH, PASSES = kTile / RPP, VPITCH = D + 8;
-  __shared__ bf16 tile[kTile][VPITCH];
-  const int tid = threadIdx.x;
-  const long bh = blockIdx.y;
-  const int c = blockIdx.x;
-  const int ch = tid % CH, rsub = tid / CH;
-  const bf16* src = x + bh * (long)g.N * D;
-#pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int l = p * RPP + rsub;
-    *reinterpret_cast<bf16x8*>(&tile[l][ch * 8]) =
-        *reinterpret_cast<const bf16x8*>(src + (long)cube_token(g, c, l) * D + ch * 8);
-  }
-  __syncthreads();
-  store_chunk_tiles<D, VPITCH>(tile, xt + (bh * g.Nc + c) * (long)D * kTile, tid, 256);
-}
-
 template <typename T, bool MAX>
 static void pool_launch(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
                         float* vc, bf16* vt, uint8_t* args) {
@@ -135,15 +115,6 @@ hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void
     if (L.pool_max) pool_launch<float, true>(L, q, k, v, qc, kc, vc, nullptr, args);
     else pool_launch<float, false>(L, q, k, v, qc, kc, vc, nullptr, nullptr);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_ctile(const Launch& L, const bf16* x, bf16* xt) {
-  const dim3 grid(L.g.Nc, L.BH), block(256);
-  if (L.D == 64)
-    hipLaunchKernelGGL((ctile_kernel<64>), grid, block, 0, L.stream, x, xt, L.g);
-  else
-    hipLaunchKernelGGL((ctile_kernel<128>), grid, block, 0, L.stream, x, xt, L.g);
   return hipGetLastError();
 }
 

@@ -129,7 +129,7 @@ FwdWs carve_fwd_ws(const Dims& d, void* base) {
 
 // Backward workspace.
 struct BwdWs {
-  bf16 *dof, *doft, *qt, *kt;   // d_o_f (raster) and chunk tiles of d_o_f, q, k
+  bf16* dof;   // d_o_f
   float *delta, *doc, *dqc, *dkc, *dvc, *p_scr, *ds_scr, *dc_scr;
   int32_t *k2q_off, *k2q, *qorder, *korder;
   uint32_t* k2q_bits;
@@ -141,9 +141,6 @@ BwdWs carve_bwd_ws(const Dims& d, void* base) {
   BwdWs w;
   const size_t rast = d.BH * d.N * d.D;
   w.dof = c.take<bf16>(rast);
-  w.doft = c.take<bf16>(rast);
-  w.qt = c.take<bf16>(rast);
-  w.kt = c.take<bf16>(rast);
   w.delta = c.take<float>(d.BH * d.N);
   const size_t pooled = d.BH * d.Nc * d.D;
   w.doc = c.take<float>(pooled);
@@ -253,20 +250,18 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   const Saved s = carve_saved(d, const_cast<void*>(saved));
   L.stream = static_cast<hipStream_t>(stream);
   hipError_t e = launch_combine_bwd(L, d_o, s.oc, s.of, g_c, g_f, g_c ? dg_c : nullptr, g_f ? dg_f : nullptr,
-                                    ws.dof, ws.delta, ws.doc, ws.doft);
+                                    ws.dof, ws.delta, ws.doc);
   if (e == hipSuccess) e = launch_index_transpose(L, idx, len, ws.k2q_off, ws.k2q, ws.k2q_bits);
   if (e == hipSuccess)
     e = launch_coarse_bwd(L, s.qc, s.kc, s.vc, s.oc, s.lse_c, ws.doc, ws.dqc, ws.dkc, ws.dvc, ws.ds_scr, ws.p_scr, ws.dc_scr);
-  if (e == hipSuccess) e = launch_ctile(L, static_cast<const bf16*>(q), ws.qt);
-  if (e == hipSuccess) e = launch_ctile(L, static_cast<const bf16*>(k), ws.kt);
   if (e == hipSuccess) e = launch_order(L, idx, len, ws.qorder);
   if (e == hipSuccess) e = launch_order_by_count(L, ws.k2q_off, ws.korder);
   if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, nullptr, ws.args);
   if (e == hipSuccess)
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                        ws.qt, ws.kt, idx, len, ws.qorder, ws.k2q_off, ws.k2q, ws.korder, s.lse_f, ws.dof, ws.doft,
-                        ws.delta, ws.dqc, ws.dkc, ws.dvc, static_cast<bf16*>(dq), static_cast<bf16*>(dk),
-                        static_cast<bf16*>(dv), L.pool_max ? ws.args : nullptr);
+                        idx, len, ws.qorder, ws.k2q_off, ws.k2q, ws.korder, s.lse_f, ws.dof, ws.delta, ws.dqc,
+                        ws.dkc, ws.dvc, static_cast<bf16*>(dq), static_cast<bf16*>(dk), static_cast<bf16*>(dv),
+                        L.pool_max ? ws.args : nullptr);
   return hip_status(e);
 }
 
@@ -366,22 +361,15 @@ vsa_status vsa_combine(const vsa_problem* p, const float* o_c, const void* o_f, 
 
 vsa_status vsa_combine_backward(const vsa_problem* p, const void* d_o, const float* o_c, const void* o_f,
                                 const void* g_c, const void* g_f, void* dg_c, void* dg_f, void* d_o_f, float* delta,
-                                float* d_o_c, void* workspace, size_t ws_bytes, void* stream) {
+                                float* d_o_c, void* stream) {
   Launch L;
-  Dims d;
-  vsa_status st = check_problem(p, &L, &d);
+  vsa_status st = check_problem(p, &L, nullptr);
   if (st != VSA_OK) return st;
   st = check_ptrs({{d_o, true}, {o_c, true}, {o_f, true}, {g_c, false}, {g_f, false}, {dg_c, false},
-                   {dg_f, false}, {d_o_f, true}, {delta, true}, {d_o_c, true}, {workspace, false}});
+                   {dg_f, false}, {d_o_f, true}, {delta, true}, {d_o_c, true}});
   if (st != VSA_OK) return st;
-  bf16* doft = nullptr;
-  if (workspace != nullptr && L.bf16) {
-    const BwdWs ws = carve_bwd_ws(d, workspace);
-    if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
-    doft = ws.doft;
-  }
   L.stream = static_cast<hipStream_t>(stream);
-  return hip_status(launch_combine_bwd(L, d_o, o_c, o_f, g_c, g_f, dg_c, dg_f, d_o_f, delta, d_o_c, doft));
+  return hip_status(launch_combine_bwd(L, d_o, o_c, o_f, g_c, g_f, dg_c, dg_f, d_o_f, delta, d_o_c));
 }
 
 vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const int32_t* len, int32_t* k2q_off,
@@ -415,16 +403,14 @@ vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k,
   const BwdWs ws = carve_bwd_ws(d, workspace);
   if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
   L.stream = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_ctile(L, static_cast<const bf16*>(q), ws.qt);
-  if (e == hipSuccess) e = launch_ctile(L, static_cast<const bf16*>(k), ws.kt);
-  if (e == hipSuccess) e = launch_order(L, idx, len, ws.qorder);
+  hipError_t e = launch_order(L, idx, len, ws.qorder);
   if (e == hipSuccess) e = launch_order_by_count(L, k2q_off, ws.korder);
   if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, nullptr, ws.args);
   if (e == hipSuccess)
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                        ws.qt, ws.kt, idx, len, ws.qorder, k2q_off, k2q, ws.korder, lse_f,
-                        static_cast<const bf16*>(d_o_f), ws.doft, delta, dq_c, dk_c, dv_c, static_cast<bf16*>(dq),
-                        static_cast<bf16*>(dk), static_cast<bf16*>(dv), L.pool_max ? ws.args : nullptr);
+                        idx, len, ws.qorder, k2q_off, k2q, ws.korder, lse_f, static_cast<const bf16*>(d_o_f), delta,
+                        dq_c, dk_c, dv_c, static_cast<bf16*>(dq), static_cast<bf16*>(dk), static_cast<bf16*>(dv),
+                        L.pool_max ? ws.args : nullptr);
   return hip_status(e);
 }
 

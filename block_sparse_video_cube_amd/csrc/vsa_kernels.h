@@ -24,8 +24,6 @@ struct Launch {
 // may be null).
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
                        float* vc, bf16* vt, uint8_t* args = nullptr);
-// Chunk tiles (layout in vsa_common.h) of a raster bf16 tensor.
-hipError_t launch_ctile(const Launch& L, const bf16* x, bf16* xt);
 
 int coarse_max_cubes();
 // Row pitch (floats) of the coarse logits: Nc rounded up to a multiple of 4.
@@ -49,7 +47,7 @@ hipError_t launch_combine(const Launch& L, const float* oc, const void* of, cons
                           void* o);
 hipError_t launch_combine_bwd(const Launch& L, const void* d_o, const float* oc, const void* of,
                               const void* gc, const void* gf, void* dgc, void* dgf, void* dof,
-                              float* delta, float* doc, bf16* doft);
+                              float* delta, float* doc);
 
 // bits: B*heads*Nc*k2q_bits_words(Nc) uint32 of scratch.
 int k2q_bits_words(int Nc);
@@ -63,15 +61,13 @@ hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, 
 hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_t* order);
 // Fine backward (bf16): dq over the forward lists (qorder from launch_order,
 // may be null), dk / dv over the transposed lists (korder from
-// launch_order_by_count, may be null). qct / kct / doct: chunk tiles of q, k
-// and d_o_f. The pooled gradients dqc / dkc / dvc are spread over their cubes
-// (mean pooling), or go to the maxima given by args (max pooling; layout of
-// launch_pool's args).
-hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const bf16* qct,
-                           const bf16* kct, const int32_t* idx, const int32_t* len, const int32_t* qorder,
-                           const int32_t* k2q_off, const int32_t* k2q, const int32_t* korder, const float* lse_f,
-                           const bf16* dof, const bf16* doct, const float* delta, const float* dqc,
-                           const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
+// launch_order_by_count, may be null). The pooled gradients dqc / dkc / dvc
+// are spread over their cubes (mean pooling), or go to the maxima given by
+// args (max pooling; layout of launch_pool's args).
+hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
+                           const int32_t* len, const int32_t* qorder, const int32_t* k2q_off, const int32_t* k2q,
+                           const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
+                           const float* dqc, const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
                            const uint8_t* args);
 
 hipError_t launch_validate_lists(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* flag);

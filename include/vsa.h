@@ -190,12 +190,11 @@ vsa_status vsa_combine(const vsa_problem* p, const float* o_c, const void* o_f,
  * dg_f = dO * O_f, d_o_f = dO * G_f (dtype, raster), delta = rowsum(d_o_f *
  * o_f) (fp32 [B, heads, T, H, W]) and d_o_c[c] = sum over the 64 tokens of
  * cube c of dO * G_c (fp32 [B, heads, Nc, head_dim]). dg_c / dg_f may be
- * NULL (not written). When workspace is not NULL it also writes the
- * transposed d_o_f tiles vsa_fine_backward reads. */
+ * NULL (not written). */
 vsa_status vsa_combine_backward(const vsa_problem* p, const void* d_o, const float* o_c,
                                 const void* o_f, const void* g_c, const void* g_f,
                                 void* dg_c, void* dg_f, void* d_o_f, float* delta, float* d_o_c,
-                                void* workspace, size_t ws_bytes, void* stream);
+                                void* stream);
 
 /* Index transpose for the backward: k2q_off int32 [B, heads, Nc + 1] and
  * k2q int32 [B, heads, Nc * list_stride]: for key cube j the query cubes i
@@ -209,9 +208,8 @@ vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const i
 /* Backward of step 4 and of the pooling: dq, dk, dv (dtype, raster) =
  * fine-attention gradient + (dq_c, dk_c, dv_c)[cube] / 64, where the pooled
  * gradients (fp32 [B, heads, Nc, head_dim]) come from vsa_coarse_backward.
- * lse_f from the forward; d_o_f and delta from vsa_combine_backward, which
- * must also have written the transposed d_o_f tiles into this same
- * workspace (ws_bytes >= vsa_workspace_bytes(p, 1)); k2q_off / k2q from
+ * lse_f from the forward; d_o_f and delta from vsa_combine_backward
+ * (workspace: ws_bytes >= vsa_workspace_bytes(p, 1)); k2q_off / k2q from
  * vsa_index_transpose. bf16 only. dQ walks each query cube's list, dK / dV
  * walk the transposed lists, so no atomics are used and the result is
  * deterministic. */

@@ -128,8 +128,8 @@ def test_stage_entry_points_validate():
     assert lib.vsa_fine_forward(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
     assert lib.vsa_fine_forward(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == NULL
     assert lib.vsa_combine(c, FAKE, MIS, None, None, FAKE, None) == ALIGN
-    assert lib.vsa_combine_backward(c, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, FAKE, FAKE, 1,
-                                    None) == WORKSPACE
+    assert lib.vsa_combine_backward(c, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, None, None) == NULL
+    assert lib.vsa_combine_backward(c, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, MIS, None) == ALIGN
     assert lib.vsa_index_transpose(c, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == NULL
     assert lib.vsa_index_transpose(c, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
     assert lib.vsa_fine_backward(c, *([FAKE] * 17), 1, None) == WORKSPACE

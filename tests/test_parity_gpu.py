@@ -430,7 +430,7 @@ def test_backward_stages():
     ws = V.workspace(p, d["q"], training=True)
     oc32 = dev(fwd["o_c"].astype(np.float32), torch.float32)
     of16 = dev(fwd["o_f"].astype(np.float32), torch.bfloat16)
-    cb = V.combine_backward(p, d["d_o"], oc32, of16, d["g_c"], d["g_f"], ws=ws)
+    cb = V.combine_backward(p, d["d_o"], oc32, of16, d["g_c"], d["g_f"])
     torch.cuda.synchronize()
     assert_close(host(cb["dg_c"]), ref["dg_c"], "bf16", "dg_c", rel=2 ** -7)
     assert_close(host(cb["d_o_f"]), ref["d_o_f"], "bf16", "d_o_f", rel=2 ** -7)
