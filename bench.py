@@ -265,7 +265,7 @@ def main() -> int:
 
     def staged(ev):
         ev[0].record()
-        V.pool(p, q, k, v, ws=ws, out=pooled[:3])
+        V.pool(p, q, k, v, out=pooled[:3])
         ev[1].record()
         V.coarse(p, *pooled[:3], out=(pooled[3], lse_c, idx if w.topk > 0 else None,
                                       lens if w.topk > 0 else None), ws=ws)
@@ -275,7 +275,7 @@ def main() -> int:
 
     if args.mode == "fine":
         # inputs of the fine kernel, then only that kernel
-        V.pool(p, q, k, v, ws=ws, out=pooled[:3])
+        V.pool(p, q, k, v, out=pooled[:3])
         V.coarse(p, *pooled[:3], out=(pooled[3], lse_c, idx if w.topk > 0 else None,
                                       lens if w.topk > 0 else None), ws=ws)
         for _ in range(args.steps):

@@ -158,10 +158,10 @@ def backward(p: Problem, q, k, v, g_c, g_f, idx, lens, saved, d_o, ws: Optional[
     return dict(dq=dq, dk=dk, dv=dv, dg_c=dgc, dg_f=dgf)
 
 
-def pool(p: Problem, q, k, v, ws: Optional[torch.Tensor] = None, out=None):
+def pool(p: Problem, q, k, v, out=None):
     qc, kc, vc = out if out is not None else (_empty(_pooled(p), torch.float32, q) for _ in range(3))
     check(lib().vsa_pool(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(qc), _ptr(kc), _ptr(vc),
-                         _ptr(ws), 0 if ws is None else ws.numel(), _stream(q.device)), "vsa_pool")
+                         _stream(q.device)), "vsa_pool")
     return qc, kc, vc
 
 

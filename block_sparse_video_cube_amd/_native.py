@@ -40,7 +40,7 @@ SIGNATURES = {
     "vsa_saved_bytes": (_sz, [_P]),
     "vsa_forward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_backward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
-    "vsa_pool": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
+    "vsa_pool": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v]),
     "vsa_coarse": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_fine_forward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_fine_combine": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),

@@ -1,17 +1,14 @@
 // Device helpers shared by the fine-stage kernels (forward and backward):
 // direct-to-LDS loads of 32-token chunks, and the LDS layouts they fill.
 //
-// A chunk is half h of a cube (tokens 32h .. 32h+31 in cube order). Two LDS
-// layouts hold a chunk of one tensor (D channels):
-//  * row tile: 32 token rows of U = D/8 16-byte units; row kappa is token
-//    (t', y', x') = (2h + kappa/16, (kappa/4)%4, kappa%4), and its logical
-//    unit u (channels 8u .. 8u+7) sits at unit u ^ kswz(kappa), so 16
-//    consecutive rows read at one logical unit hit 16 distinct bank groups.
-//    Read as the A operand of a 32x32x16 MFMA (rows = tokens, k = channels).
-//    Loaded from the raster tensor.
-//  * chunk tile: D channel rows of 32 slots in the layout of the chunk-tile
-//    tensors (vsa_common.h); read as the A operand with k = tokens, whose
-//    B operand is a 32x32 accumulator. Loaded as a linear copy.
+// A chunk is half h of a cube (tokens 32h .. 32h+31 in cube order). In LDS a
+// chunk of one tensor (D channels) is a row tile: 32 token rows of U = D/8
+// 16-byte units; row kappa is token (t', y', x') = (2h + kappa/16,
+// (kappa/4)%4, kappa%4), and its logical unit u (channels 8u .. 8u+7) sits at
+// unit u ^ kswz(kappa), so 16 consecutive rows read at one logical unit hit 16
+// distinct bank groups. It is loaded from the raster tensor, read directly as
+// the A operand of a 32x32x16 MFMA (rows = tokens, k = channels) and, by LDS
+// transpose reads, as the A operand with k = tokens (rows = channels).
 #pragma once
 
 #include "vsa_common.h"
@@ -23,9 +20,7 @@ template <int D> struct ChunkGeom {
   static constexpr int MB = D / 32;          // 32-channel blocks
   static constexpr int U = D / 8;            // 16-byte units per token row
   static constexpr int RUNITS = 32 * U;      // 16-byte units per row tile
-  static constexpr int TUNITS = D * 4;       // 16-byte units per chunk tile
   static constexpr int RINS = RUNITS / 64;   // 1 KB loads per row tile
-  static constexpr int TINS = TUNITS / 64;   // 1 KB loads per chunk tile
 };
 
 template <int U> __device__ __forceinline__ int kswz(int kappa) { return (kappa * U / 16) % U; }
@@ -70,11 +65,6 @@ template <int D> __device__ __forceinline__ void row_tile_offsets(const Grid& g,
     off[t] = (uint32_t)(tokoff * D + u * 8) * 2u;
   }
 }
-template <int D> __device__ __forceinline__ void chunk_tile_offsets(int wv, int lane, uint32_t* off) {
-  using G = ChunkGeom<D>;
-#pragma unroll
-  for (int t = 0; t < G::TINS / 2; ++t) off[t] = (uint32_t)((wv * (G::TINS / 2) + t) * 64 + lane) * 16u;
-}
 // Issue wave wv's half of a row tile: src = first row of the chunk (token
 // (2h, 0, 0) of the cube), dst = LDS byte address of the tile.
 template <int D> __device__ __forceinline__ void issue_row_tile(const void* src, const uint32_t* off, uint32_t dst,
@@ -83,22 +73,11 @@ template <int D> __device__ __forceinline__ void issue_row_tile(const void* src,
 #pragma unroll
   for (int t = 0; t < G::RINS / 2; ++t) dma16(src, off[t], dst + (wv * (G::RINS / 2) + t) * 1024);
 }
-template <int D> __device__ __forceinline__ void issue_chunk_tile(const void* src, const uint32_t* off,
-                                                                  uint32_t dst, int wv) {
-  using G = ChunkGeom<D>;
-#pragma unroll
-  for (int t = 0; t < G::TINS / 2; ++t) dma16(src, off[t], dst + (wv * (G::TINS / 2) + t) * 1024);
-}
-// A operand fragments: row tile (rows = tokens, k-step ks over channels) and
-// chunk tile (rows = channels 32mb + n32, k-step s2 over the chunk's slots).
+// A operand fragment of a row tile (rows = tokens, k-step ks over channels).
 template <int D> __device__ __forceinline__ bf16x8 row_frag(const bf16* tile, int n32, int hf, int ks) {
   using G = ChunkGeom<D>;
   return *reinterpret_cast<const bf16x8*>(tile + (n32 * G::U + ((2 * ks + hf) ^ kswz<G::U>(n32))) * 8);
 }
-__device__ __forceinline__ bf16x8 chunk_frag(const bf16* tile, int dd, int hf, int s2) {
-  return *reinterpret_cast<const bf16x8*>(tile + (dd * 4 + ((2 * s2 + hf) ^ vunit_swz(dd))) * 8);
-}
-
 // Transposed A fragments straight from a row tile, by the LDS transpose read
 // ds_read_b64_tr_b16. Within each group of 16 lanes, that read hands output
 // lane t the element t % 4 of the 8 bytes source lane 4e + t / 4 addressed,
@@ -106,8 +85,8 @@ __device__ __forceinline__ bf16x8 chunk_frag(const bf16* tile, int dd, int hf, i
 // c0 + 4j .. +3, output lane t receives channel c0 + t of rows r0 .. r0 + 3.
 // For the A operand of O^T-style products (A[m = channel 32mb + lane%32][k =
 // slot 16s2 + 8hf + e], whose B operand is a 32x32 accumulator), slot e of
-// lane half hf must hold row 16s2 + 8(e/4) + 4hf + e%4 (the accumulator's row
-// order, as in the chunk tiles): two reads, rows 16s2 + 4hf + 0..3 and
+// lane half hf must hold row 16s2 + 8(e/4) + 4hf + e%4 (the order in which a
+// 32x32 accumulator holds its rows): two reads, rows 16s2 + 4hf + 0..3 and
 // 16s2 + 8 + 4hf + 0..3. rowt_offsets gives each lane's two byte offsets
 // (within a tile) for fragment (mb, s2); rowt_frag performs the reads.
 typedef short tr16x4 __attribute__((ext_vector_type(4)));

@@ -15,8 +15,8 @@
 //   the accumulator gives every lane one query column and 16 of the 32 keys,
 //   so the row max and sum are lane-local plus one exchange between the two
 //   lane halves, and P^T is already the B operand of
-//   O^T += V_chunk^T P^T  A = the chunk's V chunk tile (LDS; slots in the
-//                        accumulator's row order).
+//   O^T += V_chunk^T P^T  A = the chunk's V row tile read transposed (LDS
+//                        transpose reads, in the accumulator's row order).
 // Chunks go to LDS with direct-to-LDS loads, each wave issuing half, several
 // chunks ahead. Every lane ends with O^T for its query column, so the 1/l
 // normalisation, LSE and the fused gate epilogue need no data exchange.
@@ -37,7 +37,7 @@ template <int D> struct FineCfg {
   static constexpr int MB = D / 32;          // 32-channel blocks of O^T
   static constexpr int U = D / 8;            // 16-byte units per key row
   static constexpr int KUNITS = 32 * U;      // 16-byte units per K chunk
-  static constexpr int VUNITS = D * 4;       // 16-byte units per V chunk
+  static constexpr int VUNITS = 32 * U;      // 16-byte units per V chunk
   static constexpr int KINS = KUNITS / 64;   // 1 KB direct-to-LDS loads per K chunk
   static constexpr int VINS = VUNITS / 64;
   // LDS stages of K and V chunks. D = 128: (3 + 2) x 8 KB = 40 KB, so four
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__
 
 template <int D, bool FUSED>
 __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ vt,
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
     bf16* __restrict__ o_f, float* __restrict__ lse_f, const float* __restrict__ oc, const bf16* __restrict__ gc,
     const bf16* __restrict__ gf, bf16* __restrict__ o, Grid g, int stride, float scale_log2) {
@@ -124,21 +124,14 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   float m = 0.f, lsum = 0.f;
 
   // Loads of chunk c = key cube list[c/2], half c%2 (tokens 32h .. 32h+31):
-  // this wave issues half of the K rows and half of the V tile. Per-lane byte
-  // offsets are fixed for the whole list: K unit p = ins*64 + lane is key row
-  // kappa = p / U, logical unit (p % U) ^ kswz(kappa), i.e. token (t', y', x')
-  // = (2h + kappa/16, (kappa/4)%4, kappa%4) of the cube; V is a linear copy.
+  // this wave issues half of the K rows and half of the V rows, both into
+  // row tiles. Per-lane byte offsets are fixed for the whole list: unit p =
+  // ins*64 + lane is key row kappa = p / U, logical unit (p % U) ^
+  // kswz(kappa), i.e. token (t', y', x') = (2h + kappa/16, (kappa/4)%4,
+  // kappa%4) of the cube.
   const uint32_t kbase = lds_addr(kbuf), vbase = lds_addr(vbuf);
-  uint32_t koff[C::KINS / 2], voff[C::VINS / 2];
-#pragma unroll
-  for (int t = 0; t < C::KINS / 2; ++t) {
-    const int ins = wv * (C::KINS / 2) + t;
-    const int p = ins * 64 + lane, kappa = p / C::U, u = (p % C::U) ^ kswz<C::U>(kappa);
-    const int tokoff = ((kappa >> 4) * g.H + ((kappa >> 2) & 3)) * g.W + (kappa & 3);
-    koff[t] = (uint32_t)(tokoff * D + u * 8) * 2u;
-  }
-#pragma unroll
-  for (int t = 0; t < C::VINS / 2; ++t) voff[t] = (uint32_t)((wv * (C::VINS / 2) + t) * 64 + lane) * 16u;
+  uint32_t koff[C::KINS / 2];
+  row_tile_offsets<D>(g, wv, lane, koff);
   // Byte offsets of the list's cubes, 64 entries at a time, one per lane:
   // kcube = first key row of the cube within this head's K, vcube = the
   // cube's V chunk tiles. A load reads them with readlane, so the per-chunk
@@ -146,7 +139,7 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   // refreshed when chunk c = 128 * n is loaded; K runs ahead of V, so V
   // keeps its own copy.
   const uint32_t khalf = (uint32_t)(2 * g.H * g.W * D) * 2u;   // t' -> t' + 2
-  const char* vt_bh = reinterpret_cast<const char*>(vt + (long)bh * g.Nc * D * kTile);
+  const bf16* V = v + tok0 * D;
   uint32_t kcube = 0, vcube = 0;
   auto cubes_k = [&](int t0) {
     const int t = t0 + lane;
@@ -154,7 +147,7 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   };
   auto cubes_v = [&](int t0) {
     const int t = t0 + lane;
-    vcube = (uint32_t)(t < L ? cube_at(t) : 0) * (uint32_t)(D * kTile * 2);
+    vcube = (uint32_t)cube_row(g, t < L ? cube_at(t) : 0, 0, 0) * (uint32_t)(D * 2);
   };
   auto issue_k = [&](int c) {
     const int e = c >> 1, h = c & 1;
@@ -170,9 +163,9 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
     if ((e & 63) == 0 && h == 0) cubes_v(e);
     const uint32_t dst = vbase + (c % C::VST) * (C::VUNITS * 16);
     const uint32_t vc = __builtin_amdgcn_readlane(vcube, e & 63);
-    const void* src = uniform_ptr(vt_bh + vc + (h ? (uint32_t)(D * 32 * 2) : 0u));
+    const void* src = uniform_ptr(reinterpret_cast<const char*>(V) + vc + (h ? khalf : 0u));
 #pragma unroll
-    for (int t = 0; t < C::VINS / 2; ++t) dma16(src, voff[t], dst + (wv * (C::VINS / 2) + t) * 1024);
+    for (int t = 0; t < C::KINS / 2; ++t) dma16(src, koff[t], dst + (wv * (C::KINS / 2) + t) * 1024);
   };
   // S^T (32 keys x 32 queries) of the K chunk at kb: lane holds, at
   // accumulator index jj, key 8*(jj/4) + 4hf + jj%4 of the lane's query.
@@ -225,13 +218,15 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sxa[e]);
     m = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
   }
-  // Bytes of this lane's LDS fragments within a stage: K row fragment ks and
-  // V fragment (mb, s2) (the 32-channel block mb adds 2048 bytes).
-  uint32_t koffs[C::KS], voffs[2];
+  // Bytes of this lane's LDS fragments within a stage: K row fragment ks,
+  // and the two transposed reads of V fragment (mb, s2).
+  uint32_t koffs[C::KS], voffs[C::MB][2][2];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) koffs[ks] = (n32 * C::U + ((2 * ks + hf) ^ kswz<C::U>(n32))) * 16;
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) voffs[s2] = (n32 * 4 + ((2 * s2 + hf) ^ vunit_swz(n32))) * 16;
+  for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, voffs[mb][s2]);
   const char* kbytes = reinterpret_cast<const char*>(kbuf);
   const char* vbytes = reinterpret_cast<const char*>(vbuf);
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -275,8 +270,7 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
 #pragma unroll
     for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        vf[mb][s2] = *reinterpret_cast<const bf16x8*>(vbytes + vst + mb * 2048 + voffs[s2]);
+      for (int s2 = 0; s2 < 2; ++s2) vf[mb][s2] = rowt_frag(vbytes + vst, voffs[mb][s2][0], voffs[mb][s2][1]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < 16; ++e) sn[e] = 0.f;
@@ -426,12 +420,12 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
 }
 
 template <int D, bool FUSED>
-static void fine_launch_bf16(const Launch& L, const void* q, const void* k, const bf16* vt, const int32_t* idx,
+static void fine_launch_bf16(const Launch& L, const void* q, const void* k, const void* v, const int32_t* idx,
                              const int32_t* len, const int32_t* order, void* o_f, float* lse_f, const float* oc, const void* gc,
                              const void* gf, void* o) {
   const int nitems = L.BH * L.g.Nc;
   hipLaunchKernelGGL((fine_fwd_bf16_kernel<D, FUSED>), dim3(nitems), dim3(128), 0, L.stream, (const bf16*)q,
-                     (const bf16*)k, vt, idx, len, order, (bf16*)o_f, lse_f, oc, (const bf16*)gc, (const bf16*)gf,
+                     (const bf16*)k, (const bf16*)v, idx, len, order, (bf16*)o_f, lse_f, oc, (const bf16*)gc, (const bf16*)gf,
                      (bf16*)o, L.g, L.stride, L.scale * kLog2e);
 }
 
@@ -453,17 +447,16 @@ hipError_t launch_order(const Launch& L, const int32_t* idx, const int32_t* len,
   return hipGetLastError();
 }
 
-hipError_t launch_fine_fwd(const Launch& L, const void* q, const void* k, const void* v, const bf16* vt,
-                           const int32_t* idx, const int32_t* len, const int32_t* order, void* o_f, float* lse_f,
+hipError_t launch_fine_fwd(const Launch& L, const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* len, const int32_t* order, void* o_f, float* lse_f,
                            const float* oc, const void* g_c, const void* g_f, void* o) {
   const bool fused = oc != nullptr;
   if (L.bf16) {
     if (L.D == 64) {
-      if (fused) fine_launch_bf16<64, true>(L, q, k, vt, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
-      else fine_launch_bf16<64, false>(L, q, k, vt, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
+      if (fused) fine_launch_bf16<64, true>(L, q, k, v, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
+      else fine_launch_bf16<64, false>(L, q, k, v, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
     } else {
-      if (fused) fine_launch_bf16<128, true>(L, q, k, vt, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
-      else fine_launch_bf16<128, false>(L, q, k, vt, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
+      if (fused) fine_launch_bf16<128, true>(L, q, k, v, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
+      else fine_launch_bf16<128, false>(L, q, k, v, idx, len, order, o_f, lse_f, oc, g_c, g_f, o);
     }
   } else {
     if (L.D == 64) {

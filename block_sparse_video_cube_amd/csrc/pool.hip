@@ -1,5 +1,4 @@
-// Step 1 of VSA: cube mean-pool (or the max-pool variant), and the chunk
-// tiles of the fine stage.
+// Step 1 of VSA: cube mean-pool (or the max-pool variant).
 //
 // VSA summary page (paperlayer.ai, arXiv 2505.13389), section 2 "Methods"
 // (coarse stage mean-pools each cube) and Appendix B (block-mean of q, k, v);
@@ -9,9 +8,8 @@
 // set of token rows, sums them in fp32 (or keeps their maximum and its first
 // position), and the partial results are reduced through LDS. The max-pool
 // variant is the pooling the VSA summary page's ablation study compares
-// (section 3, Experiments). HBM-bound: every input element is read once; pooled means
-// (fp32) and optionally the bf16 V chunk tiles of the fine forward kernel
-// (layout in vsa_common.h) are written once.
+// (section 3, Experiments). HBM-bound: every input element is read once and
+// the pooled values (fp32) are written once.
 #include "vsa_kernels.h"
 
 namespace vsa {
@@ -20,14 +18,12 @@ template <typename T, int D, bool MAX>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, float* __restrict__ qc,
                                                    float* __restrict__ kc, float* __restrict__ vc,
-                                                   bf16* __restrict__ vt, uint8_t* __restrict__ args, Grid g) {
+                                                   uint8_t* __restrict__ args, Grid g) {
   constexpr int CH = D / 8;            // 8-channel chunks per token row
   constexpr int RPP = 256 / CH;        // token rows per pass
   constexpr int PASSES = kTile / RPP;
-  constexpr int VPITCH = D + 8;        // LDS row pitch of the staged V tile (bf16)
   __shared__ float part[RPP][D + 4];
   __shared__ uint8_t parg[MAX ? RPP : 1][D + 4];
-  __shared__ bf16 vtile[kTile][VPITCH];
 
   const int tid = threadIdx.x;
   const long bh = blockIdx.y;
@@ -58,10 +54,6 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
           acc[e] += x[e];
         }
       }
-      if (which == 2 && vt != nullptr) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vtile[l][ch * 8 + e] = (bf16)x[e];
-      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -90,30 +82,28 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
     }
     __syncthreads();
   }
-
-  if (vt != nullptr) store_chunk_tiles<D, VPITCH>(vtile, vt + (bh * g.Nc + c) * (long)D * kTile, tid, 256);
 }
 
 template <typename T, bool MAX>
 static void pool_launch(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
-                        float* vc, bf16* vt, uint8_t* args) {
+                        float* vc, uint8_t* args) {
   const dim3 grid(L.g.Nc, L.BH), block(256);
   if (L.D == 64)
     hipLaunchKernelGGL((pool_kernel<T, 64, MAX>), grid, block, 0, L.stream, (const T*)q, (const T*)k, (const T*)v,
-                       qc, kc, vc, vt, args, L.g);
+                       qc, kc, vc, args, L.g);
   else
     hipLaunchKernelGGL((pool_kernel<T, 128, MAX>), grid, block, 0, L.stream, (const T*)q, (const T*)k,
-                       (const T*)v, qc, kc, vc, vt, args, L.g);
+                       (const T*)v, qc, kc, vc, args, L.g);
 }
 
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
-                       float* vc, bf16* vt, uint8_t* args) {
+                       float* vc, uint8_t* args) {
   if (L.bf16) {
-    if (L.pool_max) pool_launch<bf16, true>(L, q, k, v, qc, kc, vc, vt, args);
-    else pool_launch<bf16, false>(L, q, k, v, qc, kc, vc, vt, nullptr);
+    if (L.pool_max) pool_launch<bf16, true>(L, q, k, v, qc, kc, vc, args);
+    else pool_launch<bf16, false>(L, q, k, v, qc, kc, vc, nullptr);
   } else {
-    if (L.pool_max) pool_launch<float, true>(L, q, k, v, qc, kc, vc, nullptr, args);
-    else pool_launch<float, false>(L, q, k, v, qc, kc, vc, nullptr, nullptr);
+    if (L.pool_max) pool_launch<float, true>(L, q, k, v, qc, kc, vc, args);
+    else pool_launch<float, false>(L, q, k, v, qc, kc, vc, nullptr);
   }
   return hipGetLastError();
 }

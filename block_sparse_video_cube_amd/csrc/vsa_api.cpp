@@ -103,10 +103,9 @@ Saved carve_saved(const Dims& d, void* base) {
   return s;
 }
 
-// Forward workspace: V chunk tiles (bf16), the coarse logits and, for
+// Forward workspace: the query-cube order, the coarse logits and, for
 // inference, the pooled tensors.
 struct FwdWs {
-  bf16* vt;
   int32_t* order;
   float *s, *qc, *kc, *vc, *oc, *lse_c;
   size_t bytes;
@@ -114,7 +113,6 @@ struct FwdWs {
 FwdWs carve_fwd_ws(const Dims& d, void* base) {
   Carver c(base);
   FwdWs w;
-  w.vt = d.elem == 2 ? c.take<bf16>(d.BH * d.N * d.D) : nullptr;
   w.order = c.take<int32_t>(d.BH * d.Nc);
   w.s = c.take<float>(d.BH * d.Nc * (size_t)coarse_ld((int)d.Nc));
   const size_t pooled = d.BH * d.Nc * d.D;
@@ -223,12 +221,12 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
     const Saved s = carve_saved(d, saved);
     qc = s.qc; kc = s.kc; vc = s.vc; oc = s.oc; lse_c = s.lse_c; lse_f = s.lse_f; of = s.of;
   }
-  hipError_t e = launch_pool(L, q, k, v, qc, kc, vc, ws.vt);
+  hipError_t e = launch_pool(L, q, k, v, qc, kc, vc);
   if (e == hipSuccess)
     e = launch_coarse(L, qc, kc, vc, oc, lse_c, L.topk > 0 ? idx : nullptr, L.topk > 0 ? len : nullptr, ws.s);
   if (e == hipSuccess && L.bf16) e = launch_order(L, idx, len, ws.order);
   if (e == hipSuccess)
-    e = launch_fine_fwd(L, q, k, v, ws.vt, idx, len, L.bf16 ? ws.order : nullptr, of, lse_f, oc, g_c, g_f, o);
+    e = launch_fine_fwd(L, q, k, v, idx, len, L.bf16 ? ws.order : nullptr, of, lse_f, oc, g_c, g_f, o);
   return hip_status(e);
 }
 
@@ -256,7 +254,7 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
     e = launch_coarse_bwd(L, s.qc, s.kc, s.vc, s.oc, s.lse_c, ws.doc, ws.dqc, ws.dkc, ws.dvc, ws.ds_scr, ws.p_scr, ws.dc_scr);
   if (e == hipSuccess) e = launch_order(L, idx, len, ws.qorder);
   if (e == hipSuccess) e = launch_order_by_count(L, ws.k2q_off, ws.korder);
-  if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, nullptr, ws.args);
+  if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, ws.args);
   if (e == hipSuccess)
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                         idx, len, ws.qorder, ws.k2q_off, ws.k2q, ws.korder, s.lse_f, ws.dof, ws.delta, ws.dqc,
@@ -266,21 +264,14 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
 }
 
 vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const void* v, float* q_c, float* k_c,
-                    float* v_c, void* workspace, size_t ws_bytes, void* stream) {
+                    float* v_c, void* stream) {
   Launch L;
-  Dims d;
-  vsa_status st = check_problem(p, &L, &d);
+  vsa_status st = check_problem(p, &L, nullptr);
   if (st != VSA_OK) return st;
-  st = check_ptrs({{q, true}, {k, true}, {v, true}, {q_c, true}, {k_c, true}, {v_c, true}, {workspace, false}});
+  st = check_ptrs({{q, true}, {k, true}, {v, true}, {q_c, true}, {k_c, true}, {v_c, true}});
   if (st != VSA_OK) return st;
-  bf16* vt = nullptr;
-  if (workspace != nullptr && L.bf16) {
-    const FwdWs ws = carve_fwd_ws(d, workspace);
-    if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
-    vt = ws.vt;
-  }
   L.stream = static_cast<hipStream_t>(stream);
-  return hip_status(launch_pool(L, q, k, v, q_c, k_c, v_c, vt));
+  return hip_status(launch_pool(L, q, k, v, q_c, k_c, v_c));
 }
 
 vsa_status vsa_coarse(const vsa_problem* p, const float* q_c, const float* k_c, const float* v_c, float* o_c,
@@ -309,18 +300,16 @@ vsa_status vsa_fine_forward(const vsa_problem* p, const void* q, const void* k, 
   st = check_ptrs({{q, true}, {k, true}, {v, true}, {idx, true}, {len, true}, {o_f, true}, {lse_f, true},
                    {workspace, L.bf16}});
   if (st != VSA_OK) return st;
-  bf16* vt = nullptr;
   int32_t* order = nullptr;
   if (L.bf16) {
     const FwdWs ws = carve_fwd_ws(d, const_cast<void*>(workspace));
     if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
-    vt = ws.vt;
     order = ws.order;
   }
   L.stream = static_cast<hipStream_t>(stream);
   hipError_t e = order != nullptr ? launch_order(L, idx, len, order) : hipSuccess;
   if (e == hipSuccess)
-    e = launch_fine_fwd(L, q, k, v, vt, idx, len, order, o_f, lse_f, nullptr, nullptr, nullptr, nullptr);
+    e = launch_fine_fwd(L, q, k, v, idx, len, order, o_f, lse_f, nullptr, nullptr, nullptr, nullptr);
   return hip_status(e);
 }
 
@@ -334,17 +323,15 @@ vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, 
   st = check_ptrs({{q, true}, {k, true}, {v, true}, {idx, true}, {len, true}, {o_c, true}, {g_c, false},
                    {g_f, false}, {o, true}, {o_f, false}, {lse_f, false}, {workspace, L.bf16}});
   if (st != VSA_OK) return st;
-  bf16* vt = nullptr;
   int32_t* order = nullptr;
   if (L.bf16) {
     const FwdWs ws = carve_fwd_ws(d, const_cast<void*>(workspace));
     if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
-    vt = ws.vt;
     order = ws.order;
   }
   L.stream = static_cast<hipStream_t>(stream);
   hipError_t e = order != nullptr ? launch_order(L, idx, len, order) : hipSuccess;
-  if (e == hipSuccess) e = launch_fine_fwd(L, q, k, v, vt, idx, len, order, o_f, lse_f, o_c, g_c, g_f, o);
+  if (e == hipSuccess) e = launch_fine_fwd(L, q, k, v, idx, len, order, o_f, lse_f, o_c, g_c, g_f, o);
   return hip_status(e);
 }
 
@@ -405,7 +392,7 @@ vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k,
   L.stream = static_cast<hipStream_t>(stream);
   hipError_t e = launch_order(L, idx, len, ws.qorder);
   if (e == hipSuccess) e = launch_order_by_count(L, k2q_off, ws.korder);
-  if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, nullptr, ws.args);
+  if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, ws.args);
   if (e == hipSuccess)
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                         idx, len, ws.qorder, k2q_off, k2q, ws.korder, lse_f, static_cast<const bf16*>(d_o_f), delta,

@@ -6,8 +6,6 @@
 //    c = (tc * H4 + yc) * W4 + xc (row-major cube order); token l of a cube
 //    (0..63) is (t', y', x') = (l / 16, (l / 4) % 4, l % 4). Within a cube the
 //    four tokens x' = 0..3 are contiguous in raster memory (4*D elements).
-//  * Chunk tiles hold one cube of one tensor transposed, channel-major, in
-//    the slot order of a 32x32 MFMA accumulator (see vslot below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -65,34 +63,6 @@ __device__ __forceinline__ int token_cube(const Grid& g, int n) {
   const int y = r % g.H;
   const int t = r / g.H;
   return ((t >> 2) * g.H4 + (y >> 2)) * g.W4 + (x >> 2);
-}
-
-// Chunk tiles (read by the fine kernels, 32x32x16 MFMAs): for each
-// cube and each half h (tokens 32h .. 32h+31) a [D][32] bf16 block, channel
-// rows of 64 bytes = four 16-byte units. Slot t of a row holds token
-// 32h + vslot(t): the order in which a 32x32 MFMA accumulator hands its rows
-// to the k side of the next MFMA (lane half hf holds, for k-step s, rows
-// 16s + 4hf + {0..3} and 16s + 8 + 4hf + {0..3}). Unit u' of channel row dd
-// stores logical unit u' ^ ((dd >> 2) & 3), so 16 consecutive channel rows
-// read at the same logical unit hit 16 distinct LDS bank groups.
-__host__ __device__ __forceinline__ int vslot(int t) {
-  return 16 * (t >> 4) + 8 * ((t & 7) >> 2) + 4 * ((t & 15) >> 3) + (t & 3);
-}
-__host__ __device__ __forceinline__ int vunit_swz(int dd) { return (dd >> 2) & 3; }
-
-// Writes the chunk tiles of one cube (D * 64 bf16 at dst) from an LDS copy
-// tile[l][channel] of its 64 tokens (cube order); `nthreads` threads
-// cooperate, one 16-byte unit each per step.
-template <int D, int PITCH>
-__device__ __forceinline__ void store_chunk_tiles(const bf16 (*tile)[PITCH], bf16* dst, int tid, int nthreads) {
-  for (int w = tid; w < 2 * D * 4; w += nthreads) {
-    const int h = w / (D * 4), rem = w - h * D * 4, dd = rem >> 2, up = rem & 3;
-    const int u = up ^ vunit_swz(dd);
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = tile[32 * h + vslot(8 * u + e)][dd];
-    *reinterpret_cast<bf16x8*>(dst + (long)w * 8) = r;
-  }
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own

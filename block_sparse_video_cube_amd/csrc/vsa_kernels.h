@@ -18,12 +18,11 @@ struct Launch {
   hipStream_t stream;
 };
 
-// Pooled q / k / v (fp32; each may be null = not written), the V chunk tiles
-// (bf16 problems; may be null) and, with max pooling, the in-cube index of
-// each (cube, channel) maximum (args: 3 x B*heads*Nc*D bytes for q, k, v;
-// may be null).
+// Pooled q / k / v (fp32; each may be null = not written) and, with max
+// pooling, the in-cube index of each (cube, channel) maximum (args: 3 x
+// B*heads*Nc*D bytes for q, k, v; may be null).
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
-                       float* vc, bf16* vt, uint8_t* args = nullptr);
+                       float* vc, uint8_t* args = nullptr);
 
 int coarse_max_cubes();
 // Row pitch (floats) of the coarse logits: Nc rounded up to a multiple of 4.
@@ -35,12 +34,12 @@ hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, cons
 // Processing order of query cubes (BH*Nc int32) from their lists.
 hipError_t launch_order(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* order);
 
-// Fine forward. For bf16, vt holds the V chunk tiles and `order` (may be
-// null = cube order) the processing order from launch_order. When oc is not
-// null the kernel also forms o = O_c * g_c + O_f * g_f (gates may be null =
-// ones) and writes it to `o`; o_f / lse_f may then be null (not written).
-hipError_t launch_fine_fwd(const Launch& L, const void* q, const void* k, const void* v, const bf16* vt,
-                           const int32_t* idx, const int32_t* len, const int32_t* order, void* o_f, float* lse_f,
+// Fine forward. For bf16, `order` (may be null = cube order) is the
+// processing order from launch_order. When oc is not null the kernel also
+// forms o = O_c * g_c + O_f * g_f (gates may be null = ones) and writes it to
+// `o`; o_f / lse_f may then be null (not written).
+hipError_t launch_fine_fwd(const Launch& L, const void* q, const void* k, const void* v, const int32_t* idx,
+                           const int32_t* len, const int32_t* order, void* o_f, float* lse_f,
                            const float* oc, const void* g_c, const void* g_f, void* o);
 
 hipError_t launch_combine(const Launch& L, const float* oc, const void* of, const void* gc, const void* gf,

@@ -139,12 +139,10 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
 
 /* Step 1, cube mean-pool: q_c/k_c/v_c (fp32 [B, heads, Nc, head_dim]) are
  * the means of the 64 tokens of every cube (VSA summary page, Appendix B;
- * reading notes key design 1). When dtype is bf16 and workspace is not NULL
- * it also writes the transposed V tiles the fine forward reads
- * (ws_bytes >= vsa_workspace_bytes(p, 0)). */
+ * reading notes key design 1), or their per-channel maxima when pool_mode
+ * is VSA_POOL_MAX. */
 vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const void* v,
-                    float* q_c, float* k_c, float* v_c, void* workspace, size_t ws_bytes,
-                    void* stream);
+                    float* q_c, float* k_c, float* v_c, void* stream);
 
 /* Steps 2-3, coarse stage: S_c = scale * Q_c K_c^T, A_c = row softmax,
  * o_c = A_c V_c (fp32 [B, heads, Nc, head_dim]) and lse_c = log-sum-exp of
@@ -163,8 +161,9 @@ vsa_status vsa_coarse(const vsa_problem* p, const float* q_c, const float* k_c, 
  * softmax attention over the tokens of the cubes listed in row i only
  * (VSA summary page, section 2 "Fine stage" and Appendix B; reading notes key
  * design 2). o_f (dtype, raster) and lse_f (fp32 [B, heads, T, H, W]); an
- * empty list gives o_f = 0 and lse_f = -inf. For bf16, workspace must hold
- * the transposed V tiles written by vsa_pool (same problem, same v). */
+ * empty list gives o_f = 0 and lse_f = -inf. For bf16, the workspace
+ * (ws_bytes >= vsa_workspace_bytes(p, 0)) holds the query-cube processing
+ * order; fp32 problems need none (may be NULL). */
 vsa_status vsa_fine_forward(const vsa_problem* p, const void* q, const void* k, const void* v,
                             const int32_t* idx, const int32_t* len, void* o_f, float* lse_f,
                             const void* workspace, size_t ws_bytes, void* stream);

@@ -121,8 +121,8 @@ def test_stage_entry_points_validate():
     lib = N.lib()
     p = _p()
     c = ctypes.byref(p.c())
-    assert lib.vsa_pool(c, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == NULL
-    assert lib.vsa_pool(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
+    assert lib.vsa_pool(c, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == NULL
+    assert lib.vsa_pool(c, FAKE, FAKE, FAKE, FAKE, MIS, FAKE, None) == ALIGN
     assert lib.vsa_coarse(c, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == NULL  # top-K needs idx
     assert lib.vsa_coarse(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
     assert lib.vsa_fine_forward(c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == WORKSPACE
@@ -136,7 +136,7 @@ def test_stage_entry_points_validate():
     assert lib.vsa_coarse_backward(c, *([FAKE] * 10), 1, None) == WORKSPACE
     assert lib.vsa_validate_lists(c, FAKE, FAKE, None, None) == NULL
     bad = ctypes.byref(_p(head_dim=80).c())
-    assert lib.vsa_pool(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == HEAD_DIM
+    assert lib.vsa_pool(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == HEAD_DIM
 
 
 def test_workspace_and_saved_sizes_scale_with_problem():
@@ -147,7 +147,7 @@ def test_workspace_and_saved_sizes_scale_with_problem():
     assert V.workspace_bytes(small, True) >= V.workspace_bytes(small)
     p720 = V.Problem(1, 40, 24, 44, 80, 128, topk=32)
     # V T-tiles (bf16 N*d per head) dominate the inference workspace
-    assert V.workspace_bytes(p720) >= 40 * 84480 * 128 * 2
+    assert V.workspace_bytes(p720) >= 40 * 1320 * 1320 * 4   # the coarse logits
 
 
 def test_check_lists_host():

@@ -137,7 +137,7 @@ def test_fine_forward_parity_ragged_lists(name, heads):
     p = problem_of(w, heads=heads, topk=0, list_stride=stride)
     d = inputs_to_dev(x, w.dtype)
     ws = V.workspace(p, d["q"])
-    V.pool(p, d["q"], d["k"], d["v"], ws=ws)
+    V.pool(p, d["q"], d["k"], d["v"])
     of, lse = V.fine_forward(p, d["q"], d["k"], d["v"], dev(idx, torch.int32), dev(lens, torch.int32), ws=ws)
     torch.cuda.synchronize()
     ref = O.forward(x["q"], x["k"], x["v"], topk=0, idx=idx, lens=lens)
