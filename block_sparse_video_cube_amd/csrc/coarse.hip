@@ -38,64 +38,69 @@ __device__ __forceinline__ uint32_t fkey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One wave's 32x32 quarter of a 64x64 tile of an "NT" product C = A B^T with
-// A, B row-major [Nc][D] (fp32 16x16x4 MFMAs, 2x2 blocks). Lane (r =
-// lane%16, g = lane/16) holds, for channel group t, the float4 A[row r][16t +
-// 4g .. +3] (and likewise B), so four lanes cover 64 contiguous bytes of a
-// row; k-step 4t+e contracts channel 16t + 4g + e. All operands are loaded
-// before the first MFMA. Rows beyond Nc read as zero. acc[i][j][e] is
-// C[m0 + 16i + 4g + e][n0 + 16j + r].
+// One wave's 64x64 block of an "NT" product C = A B^T with A, B row-major
+// [Nc][D] (fp32 16x16x4 MFMAs, 4x4 blocks). Lane (r = lane%16, g = lane/16)
+// holds, for channel group t, the float4 A[row r][16t + 4g .. +3] (and
+// likewise B), so four lanes cover 64 contiguous bytes of a row; k-step 4t+e
+// contracts channel 16t + 4g + e. Channel groups are double-buffered in
+// registers: the next group loads while this one's 64 MFMAs run. Rows beyond
+// Nc read as zero. acc[i][j][e] is C[m0 + 16i + 4g + e][n0 + 16j + r].
 template <int D>
-__device__ __forceinline__ void nt_tile(const float* __restrict__ A, const float* __restrict__ B, int Nc, int m0,
-                                        int n0, f32x4 acc[2][2]) {
+__device__ __forceinline__ void nt_block64(const float* __restrict__ A, const float* __restrict__ B, int Nc,
+                                           int m0, int n0, f32x4 acc[4][4]) {
   constexpr int KT = D / 16;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  float4 av[2][KT], bv[2][KT];
+  float4 av[2][4], bv[2][4];
+  auto load = [&](int t, int buf) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ra = m0 + 16 * i + r, rb = n0 + 16 * i + r;
-#pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      av[i][t] = ra < Nc ? *reinterpret_cast<const float4*>(A + (long)ra * D + 16 * t + 4 * g)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-      bv[i][t] = rb < Nc ? *reinterpret_cast<const float4*>(B + (long)rb * D + 16 * t + 4 * g)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < 4; ++i) {
+      const int ra = m0 + 16 * i + r, rb = n0 + 16 * i + r;
+      av[buf][i] = ra < Nc ? *reinterpret_cast<const float4*>(A + (long)ra * D + 16 * t + 4 * g)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      bv[buf][i] = rb < Nc ? *reinterpret_cast<const float4*>(B + (long)rb * D + 16 * t + 4 * g)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-  }
+  };
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(0, 0);
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
-    const float a4[2][4] = {{av[0][t].x, av[0][t].y, av[0][t].z, av[0][t].w},
-                            {av[1][t].x, av[1][t].y, av[1][t].z, av[1][t].w}};
-    const float b4[2][4] = {{bv[0][t].x, bv[0][t].y, bv[0][t].z, bv[0][t].w},
-                            {bv[1][t].x, bv[1][t].y, bv[1][t].z, bv[1][t].w}};
+    if (t + 1 < KT) load(t + 1, (t + 1) & 1);
+    const int bf = t & 1;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const float a = e == 0 ? av[bf][i].x : e == 1 ? av[bf][i].y : e == 2 ? av[bf][i].z : av[bf][i].w;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16_f32(a4[i][e], b4[j][e], acc[i][j]);
+        for (int j = 0; j < 4; ++j) {
+          const float b = e == 0 ? bv[bf][j].x : e == 1 ? bv[bf][j].y : e == 2 ? bv[bf][j].z : bv[bf][j].w;
+          acc[i][j] = mfma16_f32(a, b, acc[i][j]);
+        }
+      }
   }
 }
 
-// S[bh][i][j] = scale * Q_c[i] . K_c[j]; a workgroup of 4 waves owns a 64x64 tile.
+// S[bh][i][j] = scale * Q_c[i] . K_c[j]; a workgroup of 4 waves owns a
+// 128x128 tile, each wave a 64x64 quarter.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restrict__ qc,
                                                             const float* __restrict__ kc, float* __restrict__ s,
                                                             int Nc, int ld, float scale) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const long bh = blockIdx.z;
-  const int m0 = blockIdx.y * 64 + (w >> 1) * 32, n0 = blockIdx.x * 64 + (w & 1) * 32;
-  f32x4 acc[2][2];
-  nt_tile<D>(qc + bh * (long)Nc * D, kc + bh * (long)Nc * D, Nc, m0, n0, acc);
+  const int m0 = blockIdx.y * 128 + (w >> 1) * 64, n0 = blockIdx.x * 128 + (w & 1) * 64;
+  if (m0 >= Nc || n0 >= Nc) return;   // wave-uniform; no barrier in this kernel
+  f32x4 acc[4][4];
+  nt_block64<D>(qc + bh * (long)Nc * D, kc + bh * (long)Nc * D, Nc, m0, n0, acc);
   float* S = s + bh * (long)Nc * ld;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int col = n0 + 16 * j + r;
       if (col >= Nc) continue;
 #pragma unroll
@@ -385,14 +390,14 @@ static void launch_rows(const Launch& L, const float* s, float* lse, int32_t* id
 hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, const float* vc, float* oc,
                          float* lse, int32_t* idx, int32_t* len, float* s_scratch) {
   const int Nc = L.g.Nc, ld = coarse_ld(Nc);
-  const int t64 = (Nc + 63) / 64;
+  const int t128 = (Nc + 127) / 128;
   const dim3 block(256);
   if (L.D == 64)
-    hipLaunchKernelGGL((coarse_scores_kernel<64>), dim3(t64, t64, L.BH), block, 0, L.stream, qc, kc, s_scratch, Nc,
-                       ld, L.scale);
+    hipLaunchKernelGGL((coarse_scores_kernel<64>), dim3(t128, t128, L.BH), block, 0, L.stream, qc, kc, s_scratch,
+                       Nc, ld, L.scale);
   else
-    hipLaunchKernelGGL((coarse_scores_kernel<128>), dim3(t64, t64, L.BH), block, 0, L.stream, qc, kc, s_scratch, Nc,
-                       ld, L.scale);
+    hipLaunchKernelGGL((coarse_scores_kernel<128>), dim3(t128, t128, L.BH), block, 0, L.stream, qc, kc, s_scratch,
+                       Nc, ld, L.scale);
   if (Nc <= 256) launch_rows<4>(L, s_scratch, lse, idx, len);
   else if (Nc <= 512) launch_rows<8>(L, s_scratch, lse, idx, len);
   else if (Nc <= 1024) launch_rows<16>(L, s_scratch, lse, idx, len);
@@ -422,8 +427,9 @@ __global__ __launch_bounds__(256) void coarse_bwd_delta_kernel(const float* __re
   if (lane == 0) dc[row] = a;
 }
 
-// P and dS tiles (64x64 per workgroup): the scores GEMM and dP = dO_c V_c^T on
-// the same tile, then the softmax and its derivative, elementwise.
+// P and dS tiles (128x128 per workgroup, 64x64 per wave): the scores GEMM and
+// dP = dO_c V_c^T on the same block, then the softmax and its derivative,
+// elementwise.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_bwd_pds_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
                                                              const float* __restrict__ vc, const float* __restrict__ doc,
@@ -432,22 +438,23 @@ __global__ __launch_bounds__(256) void coarse_bwd_pds_kernel(const float* __rest
                                                              int Nc, int ld, float scale) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const long bh = blockIdx.z;
-  const int m0 = blockIdx.y * 64 + (w >> 1) * 32, n0 = blockIdx.x * 64 + (w & 1) * 32;
+  const int m0 = blockIdx.y * 128 + (w >> 1) * 64, n0 = blockIdx.x * 128 + (w & 1) * 64;
+  if (m0 >= Nc || n0 >= Nc) return;   // wave-uniform; no barrier in this kernel
   const long base = bh * (long)Nc * D;
-  f32x4 sacc[2][2], pacc[2][2];
-  nt_tile<D>(qc + base, kc + base, Nc, m0, n0, sacc);
-  nt_tile<D>(doc + base, vc + base, Nc, m0, n0, pacc);
+  f32x4 sacc[4][4], pacc[4][4];
+  nt_block64<D>(qc + base, kc + base, Nc, m0, n0, sacc);
+  nt_block64<D>(doc + base, vc + base, Nc, m0, n0, pacc);
   float* P = pbuf + bh * (long)Nc * ld;
   float* DS = dsbuf + bh * (long)Nc * ld;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = m0 + 16 * i + 4 * g + e;
       if (row >= Nc) continue;
       const float l = lse[bh * Nc + row], dd = dc[bh * Nc + row];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 4; ++j) {
         const int col = n0 + 16 * j + r;
         if (col >= Nc) continue;
         const float pv = __expf(sacc[i][j][e] * scale - l);
@@ -462,16 +469,16 @@ hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, 
                              float* dvc, float* ds_scratch, float* p_scratch, float* dc_scratch) {
   const int Nc = L.g.Nc, ld = coarse_ld(Nc);
   const long rows = (long)L.BH * Nc;
-  const int t64 = (Nc + 63) / 64;
+  const int t128 = (Nc + 127) / 128;
   if (L.D == 64) {
     hipLaunchKernelGGL((coarse_bwd_delta_kernel<64>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream, doc,
                        oc, dc_scratch, rows);
-    hipLaunchKernelGGL((coarse_bwd_pds_kernel<64>), dim3(t64, t64, L.BH), dim3(256), 0, L.stream, qc, kc, vc, doc,
+    hipLaunchKernelGGL((coarse_bwd_pds_kernel<64>), dim3(t128, t128, L.BH), dim3(256), 0, L.stream, qc, kc, vc, doc,
                        lse, dc_scratch, p_scratch, ds_scratch, Nc, ld, L.scale);
   } else {
     hipLaunchKernelGGL((coarse_bwd_delta_kernel<128>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream,
                        doc, oc, dc_scratch, rows);
-    hipLaunchKernelGGL((coarse_bwd_pds_kernel<128>), dim3(t64, t64, L.BH), dim3(256), 0, L.stream, qc, kc, vc, doc,
+    hipLaunchKernelGGL((coarse_bwd_pds_kernel<128>), dim3(t128, t128, L.BH), dim3(256), 0, L.stream, qc, kc, vc, doc,
                        lse, dc_scratch, p_scratch, ds_scratch, Nc, ld, L.scale);
   }
   launch_gemm<false, false>(L, ds_scratch, nullptr, kc, dqc, L.scale);
