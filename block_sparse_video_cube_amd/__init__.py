@@ -37,6 +37,7 @@ class Problem:
     list_stride: int = 0         # 0 => topk
     scale: float = 0.0           # 0 => 1/sqrt(head_dim)
     pool: str = "mean"           # cube pooling of the coarse stage: "mean" or "max"
+    layout: str = "raster"       # token order: "raster" [B,h,T,H,W,d] or "tiled" [B,h,Nc,64,d]
 
     @property
     def N(self) -> int:
@@ -57,8 +58,9 @@ class Problem:
     def c(self) -> VsaProblem:
         code = {"bf16": VSA_BF16, "f32": VSA_F32}.get(self.dtype, 99)
         pool = {"mean": 0, "max": 1}.get(self.pool, 99)
+        layout = {"raster": 0, "tiled": 1}.get(self.layout, 99)
         return VsaProblem(self.B, self.heads, self.T, self.H, self.W, self.head_dim, code,
-                          float(self.scale), self.topk, self.list_stride, pool)
+                          float(self.scale), self.topk, self.list_stride, pool, layout)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -97,7 +99,29 @@ def workspace(p: Problem, like: torch.Tensor, training: bool = False) -> torch.T
 
 
 def _raster(p: Problem):
+    """Shape of a token tensor in the problem's layout."""
+    if p.layout == "tiled":
+        return (p.B, p.heads, p.Nc, 64, p.head_dim)
     return (p.B, p.heads, p.T, p.H, p.W, p.head_dim)
+
+
+def _tokens(p: Problem):
+    """Shape of a per-token fp32 array (LSE_f, delta) in the problem's layout."""
+    return _raster(p)[:-1]
+
+
+def tile(p: Problem, x):
+    """Cube-major copy [B, h, Nc, 64, d] of a raster token tensor."""
+    xt = _empty((p.B, p.heads, p.Nc, 64, p.head_dim), x.dtype, x)
+    check(lib().vsa_tile(ctypes.byref(p.c()), _ptr(x), _ptr(xt), _stream(x.device)), "vsa_tile")
+    return xt
+
+
+def untile(p: Problem, xt):
+    """Raster copy [B, h, T, H, W, d] of a cube-major token tensor."""
+    x = _empty((p.B, p.heads, p.T, p.H, p.W, p.head_dim), xt.dtype, xt)
+    check(lib().vsa_untile(ctypes.byref(p.c()), _ptr(xt), _ptr(x), _stream(xt.device)), "vsa_untile")
+    return x
 
 
 def _pooled(p: Problem):
@@ -141,7 +165,7 @@ def saved_views(p: Problem, saved: torch.Tensor) -> dict:
 
     out = {name: take(_pooled(p), torch.float32) for name in ("q_c", "k_c", "v_c", "o_c")}
     out["lse_c"] = take((p.B, p.heads, p.Nc), torch.float32)
-    out["lse_f"] = take((p.B, p.heads, p.T, p.H, p.W), torch.float32)
+    out["lse_f"] = take(_tokens(p), torch.float32)
     out["o_f"] = take(_raster(p), p.torch_dtype)
     return out
 
@@ -184,7 +208,7 @@ def coarse(p: Problem, q_c, k_c, v_c, out=None, ws: Optional[torch.Tensor] = Non
 
 def fine_forward(p: Problem, q, k, v, idx, lens, ws: Optional[torch.Tensor] = None):
     of = _empty(_raster(p), p.torch_dtype, q)
-    lse = _empty((p.B, p.heads, p.T, p.H, p.W), torch.float32, q)
+    lse = _empty(_tokens(p), torch.float32, q)
     check(lib().vsa_fine_forward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(lens), _ptr(of),
                                  _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(q.device)),
           "vsa_fine_forward")
@@ -196,7 +220,7 @@ def fine_combine(p: Problem, q, k, v, idx, lens, o_c, g_c=None, g_f=None, ws: Op
     """Fused fine stage + gated combine. Returns o, or (o, o_f, lse_f) with with_fine."""
     o = _empty(_raster(p), p.torch_dtype, q) if out is None else out
     of = _empty(_raster(p), p.torch_dtype, q) if with_fine else None
-    lse = _empty((p.B, p.heads, p.T, p.H, p.W), torch.float32, q) if with_fine else None
+    lse = _empty(_tokens(p), torch.float32, q) if with_fine else None
     check(lib().vsa_fine_combine(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(lens), _ptr(o_c),
                                  _ptr(g_c), _ptr(g_f), _ptr(o), _ptr(of), _ptr(lse), _ptr(ws),
                                  0 if ws is None else ws.numel(), _stream(q.device)), "vsa_fine_combine")
@@ -214,7 +238,7 @@ def combine_backward(p: Problem, d_o, o_c, o_f, g_c=None, g_f=None):
     dgc = _empty(_raster(p), p.torch_dtype, d_o) if g_c is not None else None
     dgf = _empty(_raster(p), p.torch_dtype, d_o) if g_f is not None else None
     dof = _empty(_raster(p), p.torch_dtype, d_o)
-    delta = _empty((p.B, p.heads, p.T, p.H, p.W), torch.float32, d_o)
+    delta = _empty(_tokens(p), torch.float32, d_o)
     doc = _empty(_pooled(p), torch.float32, d_o)
     check(lib().vsa_combine_backward(ctypes.byref(p.c()), _ptr(d_o), _ptr(o_c), _ptr(o_f), _ptr(g_c), _ptr(g_f),
                                      _ptr(dgc), _ptr(dgf), _ptr(dof), _ptr(delta), _ptr(doc), _stream(d_o.device)),

@@ -23,7 +23,7 @@ class VsaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("topk", ctypes.c_int32),
-                ("list_stride", ctypes.c_int32), ("pool_mode", ctypes.c_int32)]
+                ("list_stride", ctypes.c_int32), ("pool_mode", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER(VsaProblem)
@@ -33,6 +33,8 @@ _i32 = ctypes.c_int32
 
 # name -> (restype, argtypes); every symbol include/vsa.h declares.
 SIGNATURES = {
+    "vsa_tile": (_i32, [_P, _v, _v, _v]),
+    "vsa_untile": (_i32, [_P, _v, _v, _v]),
     "vsa_status_string": (ctypes.c_char_p, [_i32]),
     "vsa_version": (_i32, []),
     "vsa_max_cubes": (_i32, []),

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, toffs[mb][s2]);
-  const uint32_t rhalf = (uint32_t)(2 * g.H * g.W * D) * 2u;
+  const uint32_t rhalf = (uint32_t)(half_rows(g) * D) * 2u;
   const char* Kb = reinterpret_cast<const char*>(k + tok0 * D);
   const char* Vb = reinterpret_cast<const char*>(v + tok0 * D);
   // Byte offsets of the list's cubes, 64 entries at a time, one per lane.
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, toffs[mb][s2]);
-  const uint32_t rhalf = (uint32_t)(2 * g.H * g.W * D) * 2u;
+  const uint32_t rhalf = (uint32_t)(half_rows(g) * D) * 2u;
   const char* Qb = reinterpret_cast<const char*>(q + tok0 * D);
   const char* Db = reinterpret_cast<const char*>(dof + tok0 * D);
   // Per lane, for 64 list entries at a time: the partner cube and its first

@@ -61,8 +61,7 @@ template <int D> __device__ __forceinline__ void row_tile_offsets(const Grid& g,
   for (int t = 0; t < G::RINS / 2; ++t) {
     const int p = (wv * (G::RINS / 2) + t) * 64 + lane, kappa = p / G::U;
     const int u = (p % G::U) ^ kswz<G::U>(kappa);
-    const int tokoff = ((kappa >> 4) * g.H + ((kappa >> 2) & 3)) * g.W + (kappa & 3);
-    off[t] = (uint32_t)(tokoff * D + u * 8) * 2u;
+    off[t] = (uint32_t)(chunk_row(g, kappa) * D + u * 8) * 2u;
   }
 }
 // Issue wave wv's half of a row tile: src = first row of the chunk (token

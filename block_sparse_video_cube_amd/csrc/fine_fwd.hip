@@ -138,7 +138,7 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   // address work is scalar and division-free. The block of entries is
   // refreshed when chunk c = 128 * n is loaded; K runs ahead of V, so V
   // keeps its own copy.
-  const uint32_t khalf = (uint32_t)(2 * g.H * g.W * D) * 2u;   // t' -> t' + 2
+  const uint32_t khalf = (uint32_t)(half_rows(g) * D) * 2u;   // t' -> t' + 2
   const bf16* V = v + tok0 * D;
   uint32_t kcube = 0, vcube = 0;
   auto cubes_k = [&](int t0) {

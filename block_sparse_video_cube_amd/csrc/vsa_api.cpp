@@ -38,8 +38,9 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
   if (stride < 1 || stride > Nc) return VSA_ERR_TOPK;
   if (Nc > coarse_max_cubes()) return VSA_ERR_UNSUPPORTED;
   if (p->pool_mode != VSA_POOL_MEAN && p->pool_mode != VSA_POOL_MAX) return VSA_ERR_UNSUPPORTED;
+  if (p->layout != VSA_LAYOUT_RASTER && p->layout != VSA_LAYOUT_TILED) return VSA_ERR_UNSUPPORTED;
   if (L != nullptr) {
-    L->g = make_grid(p->T, p->H, p->W);
+    L->g = make_grid(p->T, p->H, p->W, p->layout == VSA_LAYOUT_TILED ? 1 : 0);
     L->BH = (int)BH;
     L->D = p->head_dim;
     L->bf16 = p->dtype == VSA_BF16;
@@ -415,6 +416,25 @@ vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const flo
   if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
   L.stream = static_cast<hipStream_t>(stream);
   return hip_status(launch_coarse_bwd(L, q_c, k_c, v_c, o_c, lse_c, d_o_c, dq_c, dk_c, dv_c, ws.ds_scr, ws.p_scr, ws.dc_scr));
+}
+
+static vsa_status relayout(const vsa_problem* p, const void* src, void* dst, bool to_tiled, void* stream) {
+  Launch L;
+  vsa_status st = check_problem(p, &L, nullptr);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{src, true}, {dst, true}});
+  if (st != VSA_OK) return st;
+  if (src == dst) return VSA_ERR_UNSUPPORTED;
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_relayout(L, src, dst, to_tiled));
+}
+
+vsa_status vsa_tile(const vsa_problem* p, const void* x, void* xt, void* stream) {
+  return relayout(p, x, xt, true, stream);
+}
+
+vsa_status vsa_untile(const vsa_problem* p, const void* xt, void* x, void* stream) {
+  return relayout(p, xt, x, false, stream);
 }
 
 vsa_status vsa_check_lists_host(const vsa_problem* p, const int32_t* idx, const int32_t* len) {

@@ -1,7 +1,10 @@
 // Shared device-side definitions of the VSA HIP kernels (gfx950 / CDNA4).
 //
 // Layout facts used by every kernel:
-//  * Raster tensors are [B, heads, T, H, W, D], D fastest.
+//  * Token tensors are [B, heads, T, H, W, D] (raster order) or, with the
+//    tiled layout, [B, heads, Nc, 64, D] (cube-major); D fastest. Kernels
+//    address tokens only through cube_token / cube_row / token_cube /
+//    chunk_row, which know the order.
 //  * Cube c of a (T, H, W) latent has origin (4*tc, 4*yc, 4*xc) with
 //    c = (tc * H4 + yc) * W4 + xc (row-major cube order); token l of a cube
 //    (0..63) is (t', y', x') = (l / 16, (l / 4) % 4, l % 4). Within a cube the
@@ -26,18 +29,21 @@ struct Grid {
   int T, H, W;       // latent
   int H4, W4;        // cube grid (T4 implied)
   int N, Nc;         // tokens, cubes
+  int tiled;         // token order: 0 = raster (t, y, x); 1 = cube-major (token l of cube c at 64c + l)
 };
 
-__host__ __device__ inline Grid make_grid(int T, int H, int W) {
+__host__ __device__ inline Grid make_grid(int T, int H, int W, int tiled = 0) {
   Grid g;
   g.T = T; g.H = H; g.W = W;
   g.H4 = H / 4; g.W4 = W / 4;
   g.N = T * H * W; g.Nc = g.N / kTile;
+  g.tiled = tiled;
   return g;
 }
 
-// Raster index of token l (0..63) of cube c.
+// Index (row) of token l (0..63) of cube c in the problem's token order.
 __device__ __forceinline__ int cube_token(const Grid& g, int c, int l) {
+  if (g.tiled) return c * kTile + l;
   const int xc = c % g.W4;
   const int r = c / g.W4;
   const int yc = r % g.H4;
@@ -46,9 +52,10 @@ __device__ __forceinline__ int cube_token(const Grid& g, int c, int l) {
   return (t * g.H + y) * g.W + x;
 }
 
-// Raster index of the first token of row (t', y') of cube c; the row's four
-// tokens x' = 0..3 follow contiguously.
+// Index of the first token of row (t', y') of cube c; the row's four tokens
+// x' = 0..3 follow contiguously in either token order.
 __device__ __forceinline__ int cube_row(const Grid& g, int c, int tl, int yl) {
+  if (g.tiled) return c * kTile + 16 * tl + 4 * yl;
   const int xc = c % g.W4;
   const int r = c / g.W4;
   const int yc = r % g.H4;
@@ -56,14 +63,24 @@ __device__ __forceinline__ int cube_row(const Grid& g, int c, int tl, int yl) {
   return ((4 * tc + tl) * g.H + 4 * yc + yl) * g.W + 4 * xc;
 }
 
-// Cube id of raster token n.
+// Cube of the token at index n.
 __device__ __forceinline__ int token_cube(const Grid& g, int n) {
+  if (g.tiled) return n / kTile;
   const int x = n % g.W;
   const int r = n / g.W;
   const int y = r % g.H;
   const int t = r / g.H;
   return ((t >> 2) * g.H4 + (y >> 2)) * g.W4 + (x >> 2);
 }
+
+// Rows between token (t', y', x') of a chunk (half h: t' = 2h, 2h + 1) and
+// its first token (2h, 0, 0): kappa = 16(t' - 2h) + 4y' + x' is the token's
+// position in the chunk. And rows between the first tokens of the two halves.
+__host__ __device__ __forceinline__ int chunk_row(const Grid& g, int kappa) {
+  if (g.tiled) return kappa;
+  return ((kappa >> 4) * g.H + ((kappa >> 2) & 3)) * g.W + (kappa & 3);
+}
+__host__ __device__ __forceinline__ int half_rows(const Grid& g) { return g.tiled ? 32 : 2 * g.H * g.W; }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2). Map block b so that every XCD gets one contiguous range of work items:

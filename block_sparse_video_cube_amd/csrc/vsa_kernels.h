@@ -24,6 +24,9 @@ struct Launch {
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
                        float* vc, uint8_t* args = nullptr);
 
+// Raster <-> cube-major copy of one token tensor (D channels, problem dtype).
+hipError_t launch_relayout(const Launch& L, const void* src, void* dst, bool to_tiled);
+
 int coarse_max_cubes();
 // Row pitch (floats) of the coarse logits: Nc rounded up to a multiple of 4.
 int coarse_ld(int Nc);

@@ -58,8 +58,8 @@ typedef enum {
   VSA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned               */
   VSA_ERR_WORKSPACE = 7,   /* workspace / saved buffer smaller than required */
   VSA_ERR_INDEX = 8,       /* an index list failed validation                */
-  VSA_ERR_UNSUPPORTED = 9, /* valid request this build does not implement,
-                              or an unknown pool_mode                         */
+  VSA_ERR_UNSUPPORTED = 9, /* valid request this build does not implement, an
+                              unknown pool_mode or layout, or in-place tiling */
   VSA_ERR_HIP = 10,        /* a HIP call or kernel launch failed             */
   VSA_ERR_SCALE = 11       /* scale is negative, NaN or infinite             */
 } vsa_status;
@@ -72,6 +72,16 @@ typedef enum { VSA_F32 = 0, VSA_BF16 = 1 } vsa_dtype;
  * gradient goes to the first maximum in cube order. */
 typedef enum { VSA_POOL_MEAN = 0, VSA_POOL_MAX = 1 } vsa_pool_mode;
 
+/* Token order of every token tensor of a problem (q, k, v, gates, o, d_o,
+ * gradients, O_f, and the per-token fp32 arrays LSE_f / delta). RASTER is
+ * [B, heads, T, H, W, ...]; TILED is cube-major [B, heads, Nc, 64, ...] with
+ * token l of cube c at position 64c + l, the tiled sequence of the VSA
+ * summary page's pseudocode (Appendix B), which tiles before the attention
+ * layer and untiles after it, so a model can keep activations tiled across
+ * layers (vsa_tile / vsa_untile convert). Index lists and pooled tensors do
+ * not depend on it. */
+typedef enum { VSA_LAYOUT_RASTER = 0, VSA_LAYOUT_TILED = 1 } vsa_layout;
+
 typedef struct {
   int32_t B, heads;      /* batch and heads; every (b, h) is independent      */
   int32_t T, H, W;       /* latent grid, each a positive multiple of 4         */
@@ -83,6 +93,7 @@ typedef struct {
   int32_t list_stride;   /* row stride of idx; 0 => topk. Top-K mode needs
                             list_stride >= topk; list mode needs 1..Nc         */
   int32_t pool_mode;     /* vsa_pool_mode; 0 = mean                            */
+  int32_t layout;        /* vsa_layout; 0 = raster                             */
 } vsa_problem;
 
 /* Short text for a status code (static storage, never NULL). */
@@ -228,6 +239,12 @@ vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const flo
                                void* workspace, size_t ws_bytes, void* stream);
 
 /* ---- list validation ----------------------------------------------------- */
+
+/* Token-order conversion: xt (cube-major [B, heads, Nc, 64, head_dim]) from
+ * x (raster [B, heads, T, H, W, head_dim]) and back, both in the problem's
+ * dtype; the problem's layout field is ignored. Not in place (x != xt). */
+vsa_status vsa_tile(const vsa_problem* p, const void* x, void* xt, void* stream);
+vsa_status vsa_untile(const vsa_problem* p, const void* xt, void* x, void* stream);
 
 /* Host check of explicit lists (host pointers): every len in [0, list_stride],
  * every listed id in [0, Nc), strictly increasing. Returns VSA_OK or

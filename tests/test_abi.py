@@ -71,11 +71,20 @@ def _fwd(p, **ptrs):
     (dict(scale=-1.0), SCALE), (dict(scale=float("nan")), SCALE), (dict(scale=float("inf")), SCALE),
     (dict(T=4, H=4 * 64, W=4 * 33), UNSUP),       # Nc = 2112 > vsa_max_cubes()
     (dict(pool="median"), UNSUP),                 # unknown pool_mode
+    (dict(layout="zorder"), UNSUP),               # unknown layout
 ])
 def test_problem_validation(kw, code):
     p = _p(**kw)
     assert _fwd(p) == code
     assert V.workspace_bytes(p) == 0 and V.saved_bytes(p) == 0
+
+
+def test_tile_validation():
+    lib = N.lib()
+    c = ctypes.byref(_p().c())
+    assert lib.vsa_tile(c, FAKE, None, None) == NULL
+    assert lib.vsa_untile(c, MIS, FAKE, None) == ALIGN
+    assert lib.vsa_tile(c, FAKE, FAKE, None) == UNSUP   # in place
 
 
 def test_max_pool_problem_is_valid():

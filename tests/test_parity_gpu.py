@@ -475,3 +475,61 @@ def test_max_pool_forward_topk(name):
 def test_max_pool_backward(d):
     x, p = _small_train_inputs(d=d, seed=9, heads=2 if d == 64 else 1, T=8, H=8 if d == 128 else 16, W=16)
     backward_compare(x, dataclasses.replace(p, pool="max"), "bf16")
+
+
+# ------------------------------------------------------------ tiled layout
+def test_tile_untile_match_oracle():
+    w = WL.get("C2")
+    x = WL.make_inputs("C2", heads=[0, 1], gates=False)
+    p = problem_of(w, heads=2)
+    q = dev(x["q"], torch.bfloat16)
+    qt = V.tile(p, q)
+    back = V.untile(p, qt)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qt), O.tile(host(q)))
+    assert torch.equal(back, q)
+
+
+def _tiled(p, d, keys):
+    return {k: (V.tile(p, d[k]) if d.get(k) is not None else None) for k in keys}
+
+
+@pytest.mark.parametrize("name", ["C1", "C2"])
+def test_tiled_layout_forward_equals_raster(name):
+    """The cube-major layout runs the same arithmetic in the same order, so
+    its outputs equal the raster run's bit for bit once untiled."""
+    w = WL.get(name)
+    x = WL.make_inputs(name, heads=[0, 1])
+    p = problem_of(w, heads=2)
+    pt = dataclasses.replace(p, layout="tiled")
+    d = inputs_to_dev(x, w.dtype)
+    o, idx, lens, saved = V.forward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"], training=True)
+    t = _tiled(p, d, ("q", "k", "v", "g_c", "g_f"))
+    ot, idxt, lenst, savedt = V.forward(pt, t["q"], t["k"], t["v"], t["g_c"], t["g_f"], training=True)
+    torch.cuda.synchronize()
+    assert tuple(ot.shape) == (1, 2, w.Nc, 64, w.head_dim)
+    assert torch.equal(idx, idxt) and torch.equal(lens, lenst)
+    assert torch.equal(V.untile(p, ot), o)
+    sv, svt = V.saved_views(p, saved), V.saved_views(pt, savedt)
+    assert torch.equal(V.untile(p, svt["o_f"]), sv["o_f"])
+    # per-token arrays follow the token order too
+    lse_r = sv["lse_f"].reshape(1, 2, w.T // 4, 4, w.H // 4, 4, w.W // 4, 4)
+    lse_t = lse_r.permute(0, 1, 2, 4, 6, 3, 5, 7).reshape(1, 2, w.Nc, 64)
+    assert torch.equal(svt["lse_f"], lse_t)
+
+
+def test_tiled_layout_backward_equals_raster():
+    x, p = _small_train_inputs(seed=13)
+    pt = dataclasses.replace(p, layout="tiled")
+    d = inputs_to_dev(x, "bf16")
+    o, idx, lens, saved = V.forward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"], idx=d["idx"], lens=d["len"],
+                                    training=True)
+    g = V.backward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"], idx, lens, saved, d["d_o"])
+    t = _tiled(p, d, ("q", "k", "v", "g_c", "g_f", "d_o"))
+    ot, _, _, savedt = V.forward(pt, t["q"], t["k"], t["v"], t["g_c"], t["g_f"], idx=d["idx"], lens=d["len"],
+                                 training=True)
+    gt = V.backward(pt, t["q"], t["k"], t["v"], t["g_c"], t["g_f"], idx, lens, savedt, t["d_o"])
+    torch.cuda.synchronize()
+    assert torch.equal(V.untile(p, ot), o)
+    for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
+        assert torch.equal(V.untile(p, gt[nm]), g[nm]), nm
