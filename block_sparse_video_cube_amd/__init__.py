@@ -21,7 +21,8 @@ from ._native import VSA_BF16, VSA_F32, VsaError, VsaProblem, check, lib
 
 __all__ = ["Problem", "VsaError", "forward", "backward", "pool", "coarse", "fine_forward", "fine_combine", "combine",
            "combine_backward", "index_transpose", "fine_backward", "coarse_backward",
-           "check_lists_host", "validate_lists", "workspace_bytes", "saved_bytes", "max_cubes"]
+           "check_lists_host", "validate_lists", "workspace_bytes", "saved_bytes", "max_cubes", "tile", "untile",
+           "compatible_latent", "crop", "pad", "saved_views"]
 
 
 @dataclass(frozen=True)
@@ -122,6 +123,28 @@ def untile(p: Problem, xt):
     x = _empty((p.B, p.heads, p.T, p.H, p.W, p.head_dim), xt.dtype, xt)
     check(lib().vsa_untile(ctypes.byref(p.c()), _ptr(xt), _ptr(x), _stream(xt.device)), "vsa_untile")
     return x
+
+
+def compatible_latent(T: int, H: int, W: int) -> tuple:
+    """Smallest latent with sides that are multiples of 4 containing T x H x W."""
+    o = [ctypes.c_int32() for _ in range(3)]
+    check(lib().vsa_compatible_latent(T, H, W, *(ctypes.byref(v) for v in o)), "vsa_compatible_latent")
+    return tuple(v.value for v in o)
+
+
+def crop(p: Problem, x, T: int, H: int, W: int):
+    """Raster [B, h, T, H, W, d] copy of the leading region of a token tensor of p (p's layout)."""
+    out = _empty((p.B, p.heads, T, H, W, p.head_dim), x.dtype, x)
+    check(lib().vsa_crop(ctypes.byref(p.c()), _ptr(x), T, H, W, _ptr(out), _stream(x.device)), "vsa_crop")
+    return out
+
+
+def pad(p: Problem, x):
+    """Token tensor of p (p's layout) holding raster x [B, h, T, H, W, d] at the origin, zeros elsewhere."""
+    T, H, W = x.shape[2:5]
+    out = _empty(_raster(p), x.dtype, x)
+    check(lib().vsa_pad(ctypes.byref(p.c()), _ptr(x), T, H, W, _ptr(out), _stream(x.device)), "vsa_pad")
+    return out
 
 
 def _pooled(p: Problem):

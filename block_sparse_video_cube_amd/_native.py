@@ -35,6 +35,9 @@ _i32 = ctypes.c_int32
 SIGNATURES = {
     "vsa_tile": (_i32, [_P, _v, _v, _v]),
     "vsa_untile": (_i32, [_P, _v, _v, _v]),
+    "vsa_compatible_latent": (_i32, [_i32, _i32, _i32, _v, _v, _v]),
+    "vsa_crop": (_i32, [_P, _v, _i32, _i32, _i32, _v, _v]),
+    "vsa_pad": (_i32, [_P, _v, _i32, _i32, _i32, _v, _v]),
     "vsa_status_string": (ctypes.c_char_p, [_i32]),
     "vsa_version": (_i32, []),
     "vsa_max_cubes": (_i32, []),

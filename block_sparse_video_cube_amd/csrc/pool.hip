@@ -108,35 +108,4 @@ hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void
   return hipGetLastError();
 }
 
-// Token-order conversion, one workgroup per (b, h, cube): the cube's 64
-// token rows move between raster and cube-major order, 16 bytes per thread
-// and step.
-template <typename T>
-__global__ __launch_bounds__(256) void relayout_kernel(const T* __restrict__ src, T* __restrict__ dst, Grid g,
-                                                       int D, int to_tiled) {
-  const long bh = blockIdx.y;
-  const int c = blockIdx.x;
-  Grid r = g;
-  r.tiled = 0;
-  const int units = D * (int)sizeof(T) / 16;   // 16-byte units per token row
-  for (int w = threadIdx.x; w < kTile * units; w += 256) {
-    const int l = w / units, u = w - l * units;
-    const long ras = bh * g.N + cube_token(r, c, l);
-    const long til = bh * g.N + (long)c * kTile + l;
-    const long from = to_tiled ? ras : til, to = to_tiled ? til : ras;
-    reinterpret_cast<uint4*>(dst + to * D)[u] = reinterpret_cast<const uint4*>(src + from * D)[u];
-  }
-}
-
-hipError_t launch_relayout(const Launch& L, const void* src, void* dst, bool to_tiled) {
-  const dim3 grid(L.g.Nc, L.BH), block(256);
-  if (L.bf16)
-    hipLaunchKernelGGL((relayout_kernel<bf16>), grid, block, 0, L.stream, (const bf16*)src, (bf16*)dst, L.g, L.D,
-                       (int)to_tiled);
-  else
-    hipLaunchKernelGGL((relayout_kernel<float>), grid, block, 0, L.stream, (const float*)src, (float*)dst, L.g,
-                       L.D, (int)to_tiled);
-  return hipGetLastError();
-}
-
 }  // namespace vsa

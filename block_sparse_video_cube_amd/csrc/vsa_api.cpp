@@ -437,6 +437,37 @@ vsa_status vsa_untile(const vsa_problem* p, const void* xt, void* x, void* strea
   return relayout(p, xt, x, false, stream);
 }
 
+vsa_status vsa_compatible_latent(int32_t T, int32_t H, int32_t W, int32_t* Tc, int32_t* Hc, int32_t* Wc) {
+  if (Tc == nullptr || Hc == nullptr || Wc == nullptr) return VSA_ERR_NULL;
+  const int32_t lim = 0x7fffffff - 3;
+  if (T <= 0 || H <= 0 || W <= 0 || T > lim || H > lim || W > lim) return VSA_ERR_SHAPE;
+  *Tc = (T + 3) / 4 * 4;
+  *Hc = (H + 3) / 4 * 4;
+  *Wc = (W + 3) / 4 * 4;
+  return VSA_OK;
+}
+
+static vsa_status crop_pad(const vsa_problem* p, const void* src, int32_t T, int32_t H, int32_t W, void* dst,
+                           bool to_small, void* stream) {
+  Launch L;
+  vsa_status st = check_problem(p, &L, nullptr);
+  if (st != VSA_OK) return st;
+  if (T <= 0 || H <= 0 || W <= 0 || T > p->T || H > p->H || W > p->W) return VSA_ERR_SHAPE;
+  st = check_ptrs({{src, true}, {dst, true}});
+  if (st != VSA_OK) return st;
+  if (src == dst) return VSA_ERR_UNSUPPORTED;
+  L.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_crop_pad(L, src, dst, T, H, W, to_small));
+}
+
+vsa_status vsa_crop(const vsa_problem* p, const void* x, int32_t T, int32_t H, int32_t W, void* out, void* stream) {
+  return crop_pad(p, x, T, H, W, out, true, stream);
+}
+
+vsa_status vsa_pad(const vsa_problem* p, const void* x, int32_t T, int32_t H, int32_t W, void* out, void* stream) {
+  return crop_pad(p, x, T, H, W, out, false, stream);
+}
+
 vsa_status vsa_check_lists_host(const vsa_problem* p, const int32_t* idx, const int32_t* len) {
   Dims d;
   vsa_status st = check_problem(p, nullptr, &d);

@@ -26,6 +26,7 @@ hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void
 
 // Raster <-> cube-major copy of one token tensor (D channels, problem dtype).
 hipError_t launch_relayout(const Launch& L, const void* src, void* dst, bool to_tiled);
+hipError_t launch_crop_pad(const Launch& L, const void* src, void* dst, int ts, int hs, int ws, bool to_small);
 
 int coarse_max_cubes();
 // Row pitch (floats) of the coarse logits: Nc rounded up to a multiple of 4.

@@ -246,6 +246,30 @@ vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const flo
 vsa_status vsa_tile(const vsa_problem* p, const void* x, void* xt, void* stream);
 vsa_status vsa_untile(const vsa_problem* p, const void* xt, void* x, void* stream);
 
+/* Latents whose sides are not multiples of 4. The VSA summary page
+ * (paperlayer.ai, arXiv 2505.13389), section 5 "Limitation and Conclusion",
+ * notes that (4, 4, 4) cubes need sides divisible by 4 and names the remedy:
+ * generate a slightly larger latent and crop the result.
+ *
+ * vsa_compatible_latent: the smallest grid Tc x Hc x Wc with every side a
+ * multiple of 4 that contains T x H x W (each side rounded up). Host only;
+ * VSA_ERR_NULL for a NULL output pointer, VSA_ERR_SHAPE for a side <= 0 or
+ * one that would overflow int32 when rounded. */
+vsa_status vsa_compatible_latent(int32_t T, int32_t H, int32_t W, int32_t* Tc, int32_t* Hc, int32_t* Wc);
+
+/* vsa_crop: out = the leading T x H x W region of x, a token tensor of the
+ * (compatible) problem p in p's layout, written in raster order
+ * [B, heads, T, H, W, head_dim], p's dtype. From the tiled layout this is the
+ * untile and the crop in one pass.
+ * vsa_pad: the reverse embedding. out, a token tensor of p in p's layout,
+ * takes x (raster [B, heads, T, H, W, head_dim]) at the origin and zeros at
+ * every token outside it.
+ * Both need 1 <= T <= p->T, 1 <= H <= p->H, 1 <= W <= p->W (else
+ * VSA_ERR_SHAPE), 16-byte aligned non-NULL pointers and x != out
+ * (VSA_ERR_UNSUPPORTED); asynchronous on `stream`. */
+vsa_status vsa_crop(const vsa_problem* p, const void* x, int32_t T, int32_t H, int32_t W, void* out, void* stream);
+vsa_status vsa_pad(const vsa_problem* p, const void* x, int32_t T, int32_t H, int32_t W, void* out, void* stream);
+
 /* Host check of explicit lists (host pointers): every len in [0, list_stride],
  * every listed id in [0, Nc), strictly increasing. Returns VSA_OK or
  * VSA_ERR_INDEX. Runs on the CPU only. */

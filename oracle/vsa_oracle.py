@@ -87,6 +87,30 @@ def untile(xt: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
     return out.reshape(xt.shape[:-3] + (T, H, W, d))
 
 
+def compatible_latent(T: int, H: int, W: int) -> tuple:
+    """Smallest latent whose sides are multiples of the cube edge and which
+    contains T x H x W. Section 5 "Limitation and Conclusion" of the summary
+    page: (4, 4, 4) cubes need sides divisible by 4; a slightly larger latent
+    is generated and the result cropped."""
+    if min(T, H, W) <= 0:
+        raise ValueError("latent sides must be positive")
+    return tuple(-(-n // CUBE) * CUBE for n in (T, H, W))
+
+
+def crop(x: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
+    """Leading T x H x W region of a raster tensor [..., Tc, Hc, Wc, d]."""
+    return x[..., :T, :H, :W, :].copy()
+
+
+def pad(x: np.ndarray, Tc: int, Hc: int, Wc: int) -> np.ndarray:
+    """Raster [..., Tc, Hc, Wc, d] holding x [..., T, H, W, d] at the origin
+    and zeros at every other token."""
+    T, H, W, d = x.shape[-4:]
+    out = np.zeros(x.shape[:-4] + (Tc, Hc, Wc, d), dtype=x.dtype)
+    out[..., :T, :H, :W, :] = x
+    return out
+
+
 def untile_rows(rt: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
     """Inverse of tiling for per-token scalars: [..., Nc, 64] -> [..., T, H, W]."""
     return untile(rt[..., None], T, H, W)[..., 0]

@@ -87,6 +87,31 @@ def test_tile_validation():
     assert lib.vsa_tile(c, FAKE, FAKE, None) == UNSUP   # in place
 
 
+def test_compatible_latent_host():
+    lib = N.lib()
+    o = [ctypes.c_int32() for _ in range(3)]
+    refs = [ctypes.byref(v) for v in o]
+    assert lib.vsa_compatible_latent(9, 13, 30, *refs) == OK
+    assert [v.value for v in o] == [12, 16, 32]
+    assert lib.vsa_compatible_latent(24, 44, 80, *refs) == OK
+    assert [v.value for v in o] == [24, 44, 80]
+    assert lib.vsa_compatible_latent(0, 4, 4, *refs) == SHAPE
+    assert lib.vsa_compatible_latent(2**31 - 1, 4, 4, *refs) == SHAPE
+    assert lib.vsa_compatible_latent(4, 4, 4, None, refs[1], refs[2]) == NULL
+
+
+def test_crop_pad_validation():
+    lib = N.lib()
+    c = ctypes.byref(_p().c())                      # compatible grid 8 x 8 x 8
+    other = ctypes.c_void_p(8192)
+    assert lib.vsa_crop(c, FAKE, 9, 8, 8, other, None) == SHAPE
+    assert lib.vsa_crop(c, FAKE, 5, 0, 8, other, None) == SHAPE
+    assert lib.vsa_pad(c, None, 5, 5, 5, other, None) == NULL
+    assert lib.vsa_pad(c, FAKE, 5, 5, 5, MIS, None) == ALIGN
+    assert lib.vsa_crop(c, FAKE, 5, 5, 5, FAKE, None) == UNSUP   # in place
+    assert lib.vsa_crop(ctypes.byref(_p(T=7).c()), FAKE, 5, 5, 5, other, None) == SHAPE
+
+
 def test_max_pool_problem_is_valid():
     p = _p(pool="max")
     assert V.workspace_bytes(p) > 0 and V.saved_bytes(p) > 0

@@ -49,6 +49,36 @@ def test_tile_rejects_non_multiple_of_4():
         O.tiled_to_raster(8, 6, 8)
 
 
+def test_compatible_latent_brute_force():
+    """Smallest multiple of 4 not below each side, found by counting up."""
+    for n in range(1, 41):
+        m = n
+        while m % 4:
+            m += 1
+        assert O.compatible_latent(n, 4, 4)[0] == m
+        assert O.compatible_latent(4, n, 4)[1] == m
+        assert O.compatible_latent(4, 4, n)[2] == m
+    with pytest.raises(ValueError):
+        O.compatible_latent(0, 4, 4)
+
+
+def test_crop_pad_round_trip_and_zero_fill():
+    x = _rand((2, 3, 5, 6, 7, 3), 2)
+    Tc, Hc, Wc = O.compatible_latent(5, 6, 7)
+    xp = O.pad(x, Tc, Hc, Wc)
+    assert xp.shape == (2, 3, 8, 8, 8, 3)
+    np.testing.assert_array_equal(O.crop(xp, 5, 6, 7), x)
+    for t in range(Tc):
+        for y in range(Hc):
+            for w in range(Wc):
+                inside = t < 5 and y < 6 and w < 7
+                cell = xp[:, :, t, y, w, :]
+                if inside:
+                    np.testing.assert_array_equal(cell, x[:, :, t, y, w, :])
+                else:
+                    assert not cell.any()
+
+
 # ---------------------------------------------------------------- step 1: pool
 def test_pool_matches_avg_pool3d():
     """Mean-pool equals torch avg_pool3d(kernel=stride=4) in row-major cube order."""

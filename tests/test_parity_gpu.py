@@ -533,3 +533,51 @@ def test_tiled_layout_backward_equals_raster():
     assert torch.equal(V.untile(p, ot), o)
     for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
         assert torch.equal(V.untile(p, gt[nm]), g[nm]), nm
+
+
+# ------------------------------------------- latents not divisible by the cube
+@pytest.mark.parametrize("layout", ["raster", "tiled"])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 128)])
+def test_crop_pad_match_oracle(layout, dtype, d):
+    T, H, W = 9, 13, 30
+    Tc, Hc, Wc = V.compatible_latent(T, H, W)
+    assert (Tc, Hc, Wc) == O.compatible_latent(T, H, W) == (12, 16, 32)
+    p = V.Problem(1, 2, Tc, Hc, Wc, d, dtype=dtype, topk=2, layout=layout)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rng = np.random.default_rng(3)
+    xs = dev(rng.standard_normal((1, 2, T, H, W, d)).astype(np.float32), td)
+    ref = O.pad(host(xs), Tc, Hc, Wc)
+    got = V.pad(p, xs)
+    big = rng.standard_normal((1, 2, Tc, Hc, Wc, d)).astype(np.float32)
+    bigd = dev(O.tile(big) if layout == "tiled" else big, td)
+    cropped = V.crop(p, bigd, T, H, W)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got), O.tile(ref) if layout == "tiled" else ref)
+    assert np.array_equal(host(cropped), O.crop(host(bigd) if layout == "raster" else
+                                                O.untile(host(bigd), Tc, Hc, Wc), T, H, W))
+
+
+def test_forward_on_compatible_latent_then_crop():
+    """The remedy for latents whose sides are not multiples of 4: run the
+    operator on the compatible (larger) latent and crop. In either token
+    order the cropped output matches the oracle's pad -> forward -> crop."""
+    T, H, W, heads, d = 7, 10, 13, 2, 64
+    Tc, Hc, Wc = V.compatible_latent(T, H, W)
+    x = WL.make_inputs_custom(1, heads, d, T, H, W, dtype="bf16", seed=21)
+    nc = Tc * Hc * Wc // 64
+    idx, lens = WL.random_lists(nc, heads * nc, 1, nc, seed=21, stride=nc)
+    idx, lens = idx.reshape(1, heads, nc, nc), lens.reshape(1, heads, nc)
+    ref = O.forward(*(O.pad(x[k], Tc, Hc, Wc) for k in ("q", "k", "v", "g_c", "g_f")), topk=0, idx=idx, lens=lens)
+    ref_o = O.crop(ref["o"], T, H, W)
+    d_in = inputs_to_dev(x, "bf16")
+    idx_d, lens_d = dev(idx, torch.int32), dev(lens, torch.int32)
+    outs = []
+    for layout in ("raster", "tiled"):
+        p = V.Problem(1, heads, Tc, Hc, Wc, d, topk=0, list_stride=nc, layout=layout)
+        padded = [V.pad(p, d_in[k]) for k in ("q", "k", "v", "g_c", "g_f")]
+        o, _, _, _ = V.forward(p, *padded, idx=idx_d, lens=lens_d)
+        outs.append(V.crop(p, o, T, H, W))
+    torch.cuda.synchronize()
+    assert tuple(outs[0].shape) == (1, heads, T, H, W, d)
+    assert torch.equal(outs[0], outs[1])
+    assert_close(host(outs[0]), ref_o, "bf16", "o (cropped)")
