@@ -156,13 +156,14 @@ def train_measure(name: str, steps: int, warmup: int) -> dict:
     fl_b = 10.0 * 64 * 64 * w.head_dim * pairs
     esz = 2 if w.dtype == "bf16" else 4
     raster = w.B * w.heads * w.N * w.head_dim
-    # combine backward: read dO, O_f, G_c, G_f; write dG_c, dG_f, dO_f, its chunk tiles; + delta
-    cb_bytes = 8 * raster * esz + w.B * w.heads * w.N * 4
+    # combine backward: read dO, O_f, G_c, G_f and O_c; write dG_c, dG_f, dO_f, delta and dO_c
+    pooled_b = w.B * w.heads * w.Nc * w.head_dim * 4
+    cb_bytes = 7 * raster * esz + w.B * w.heads * w.N * 4 + 2 * pooled_b
     return {"workload": w.name, "steps": steps, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_tflops": round(fl_f / (fwd_ms * 1e-3) / 1e12, 2), "bwd_tflops": round(fl_b / (bwd_ms * 1e-3) / 1e12, 2),
             "computed_block_pairs": pairs,
             "bwd_stages_ms": {"combine_bwd": round(st[0], 4), "index_transpose": round(st[1], 4),
-                              "coarse_bwd": round(st[2], 4), "fine_bwd (T-tiles, dq, dk/dv, pool bwd)": round(st[3], 4)},
+                              "coarse_bwd": round(st[2], 4), "fine_bwd (dq, dk/dv, pool bwd)": round(st[3], 4)},
             "fine_bwd_tflops": round(fl_b / (st[3] * 1e-3) / 1e12, 2),
             "fine_bwd_frac_bf16_peak": round(fl_b / (st[3] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "combine_bwd_GB_per_s": round(cb_bytes / (st[0] * 1e-3) / 1e9, 1),
@@ -315,7 +316,7 @@ def main() -> int:
     bh = w.B * w.heads
     raster = bh * w.N * w.head_dim
     pooled_b = bh * w.Nc * w.head_dim * 4
-    pool_bytes = 3 * raster * esz + 3 * pooled_b + (raster * 2 if w.dtype == "bf16" else 0)
+    pool_bytes = 3 * raster * esz + 3 * pooled_b
     fine_bytes = 6 * raster * esz + pooled_b + bh * w.Nc * p.stride * 4 * 2
     value = fine_flop / (ms_step * 1e-3) / 1e12
     achieved = fine_flop / (stage_ms[2] * 1e-3) / 1e12
