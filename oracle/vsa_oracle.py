@@ -30,6 +30,9 @@ the design notes of the repository):
 * masked logits are exactly -inf; an empty list gives O_f = 0, LSE_f = -inf;
 * gates are elementwise, shaped like the output; a missing gate means 1;
 * the top-K mask carries no gradient (it is piecewise constant);
+* cube shapes other than (4, 4, 4) (the summary page's tile-size exploration,
+  section 2 "Methods"): the same definitions with B = Ct*Ch*Cw tokens per cube,
+  cubes row-major over the grid and tokens row-major inside a cube;
 * the max-pool variant (ablation of the coarse pooling) takes the per-channel
   maximum over a cube; its gradient goes to the first maximum in cube order.
 
@@ -47,54 +50,68 @@ import numpy as np
 
 CUBE = 4                      # cube edge (4, 4, 4): section 2 "Methods", App. B
 TILE = CUBE * CUBE * CUBE     # 64 tokens per cube = one tile (block = 64)
+DEFAULT_CUBE = (CUBE, CUBE, CUBE)
+# Section 2 "Methods" of the summary page names the cube (Ct, Ch, Cw) with tile
+# size B = Ct*Ch*Cw and its design exploration compares tile sizes; every
+# function below takes the cube shape, (4, 4, 4) unless stated.
+
+
+def _cube(cube) -> tuple:
+    ct, ch, cw = (int(e) for e in cube)
+    if min(ct, ch, cw) <= 0:
+        raise ValueError("cube sides must be positive")
+    return ct, ch, cw
 
 
 # --------------------------------------------------------------------------
 # Step 0: cube partition, tile and untile (section 2 "Methods"; App. B)
 # --------------------------------------------------------------------------
-def tiled_to_raster(T: int, H: int, W: int) -> np.ndarray:
-    """perm[p] = raster token index of tiled position p = 64*c + l.
+def tiled_to_raster(T: int, H: int, W: int, cube=DEFAULT_CUBE) -> np.ndarray:
+    """perm[p] = raster token index of tiled position p = B*c + l (B = Ct*Ch*Cw).
 
-    Token (t, y, x) lies in cube c = ((t//4)*(H/4) + y//4)*(W/4) + x//4 at
-    local index l = ((t%4)*4 + y%4)*4 + x%4.
+    Token (t, y, x) lies in cube c = ((t//Ct)*(H/Ch) + y//Ch)*(W/Cw) + x//Cw
+    (row-major cube order) at local index l = ((t%Ct)*Ch + y%Ch)*Cw + x%Cw
+    (row-major inside the cube).
     """
-    if T % CUBE or H % CUBE or W % CUBE:
-        raise ValueError("latent dims must be multiples of 4")
-    Hp, Wp = H // CUBE, W // CUBE
+    ct, ch, cw = _cube(cube)
+    if T % ct or H % ch or W % cw:
+        raise ValueError(f"latent dims must be multiples of the cube {cube}")
+    Hp, Wp = H // ch, W // cw
     t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
-    c = ((t // CUBE) * Hp + y // CUBE) * Wp + x // CUBE
-    l = ((t % CUBE) * CUBE + y % CUBE) * CUBE + x % CUBE
+    c = ((t // ct) * Hp + y // ch) * Wp + x // cw
+    l = ((t % ct) * ch + y % ch) * cw + x % cw
     raster = (t * H + y) * W + x
     perm = np.empty(T * H * W, dtype=np.int64)
-    perm[(c * TILE + l).reshape(-1)] = raster.reshape(-1)
+    perm[(c * (ct * ch * cw) + l).reshape(-1)] = raster.reshape(-1)
     return perm
 
 
-def tile(x: np.ndarray) -> np.ndarray:
-    """[..., T, H, W, d] (raster) -> [..., Nc, 64, d] (cube-major)."""
+def tile(x: np.ndarray, cube=DEFAULT_CUBE) -> np.ndarray:
+    """[..., T, H, W, d] (raster) -> [..., Nc, B, d] (cube-major)."""
     T, H, W, d = x.shape[-4:]
+    b = int(np.prod(_cube(cube)))
     flat = x.reshape(x.shape[:-4] + (T * H * W, d))
-    return flat[..., tiled_to_raster(T, H, W), :].reshape(
-        x.shape[:-4] + (T * H * W // TILE, TILE, d))
+    return flat[..., tiled_to_raster(T, H, W, cube), :].reshape(
+        x.shape[:-4] + (T * H * W // b, b, d))
 
 
-def untile(xt: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
-    """Inverse of ``tile``: [..., Nc, 64, d] -> [..., T, H, W, d]."""
+def untile(xt: np.ndarray, T: int, H: int, W: int, cube=DEFAULT_CUBE) -> np.ndarray:
+    """Inverse of ``tile``: [..., Nc, B, d] -> [..., T, H, W, d]."""
     d = xt.shape[-1]
     N = T * H * W
     out = np.empty(xt.shape[:-3] + (N, d), dtype=xt.dtype)
-    out[..., tiled_to_raster(T, H, W), :] = xt.reshape(xt.shape[:-3] + (N, d))
+    out[..., tiled_to_raster(T, H, W, cube), :] = xt.reshape(xt.shape[:-3] + (N, d))
     return out.reshape(xt.shape[:-3] + (T, H, W, d))
 
 
-def compatible_latent(T: int, H: int, W: int) -> tuple:
-    """Smallest latent whose sides are multiples of the cube edge and which
+def compatible_latent(T: int, H: int, W: int, cube=DEFAULT_CUBE) -> tuple:
+    """Smallest latent whose sides are multiples of the cube's sides and which
     contains T x H x W. Section 5 "Limitation and Conclusion" of the summary
     page: (4, 4, 4) cubes need sides divisible by 4; a slightly larger latent
     is generated and the result cropped."""
     if min(T, H, W) <= 0:
         raise ValueError("latent sides must be positive")
-    return tuple(-(-n // CUBE) * CUBE for n in (T, H, W))
+    return tuple(-(-n // e) * e for n, e in zip((T, H, W), _cube(cube)))
 
 
 def crop(x: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
@@ -111,9 +128,9 @@ def pad(x: np.ndarray, Tc: int, Hc: int, Wc: int) -> np.ndarray:
     return out
 
 
-def untile_rows(rt: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
-    """Inverse of tiling for per-token scalars: [..., Nc, 64] -> [..., T, H, W]."""
-    return untile(rt[..., None], T, H, W)[..., 0]
+def untile_rows(rt: np.ndarray, T: int, H: int, W: int, cube=DEFAULT_CUBE) -> np.ndarray:
+    """Inverse of tiling for per-token scalars: [..., Nc, B] -> [..., T, H, W]."""
+    return untile(rt[..., None], T, H, W, cube)[..., 0]
 
 
 # --------------------------------------------------------------------------
@@ -123,7 +140,7 @@ POOL_MODES = ("mean", "max")
 
 
 def pool(xt: np.ndarray, mode: str = "mean") -> np.ndarray:
-    """X_c[c] = (1/64) * sum over the 64 tokens of cube c.  [..., Nc, 64, d] -> [..., Nc, d].
+    """X_c[c] = (1/B) * sum over the B tokens of cube c.  [..., Nc, B, d] -> [..., Nc, d].
 
     mode "max": the per-channel maximum over the cube's tokens instead, the
     pooling variant the VSA summary page's ablation study compares with
@@ -132,7 +149,7 @@ def pool(xt: np.ndarray, mode: str = "mean") -> np.ndarray:
         return xt.max(axis=-2)
     if mode != "mean":
         raise ValueError(f"pool mode {mode!r}")
-    return xt.sum(axis=-2) / TILE
+    return xt.sum(axis=-2) / xt.shape[-2]
 
 
 # --------------------------------------------------------------------------
@@ -198,11 +215,12 @@ def transpose_lists(idx: np.ndarray, lens: np.ndarray, nc: int):
 def _pool_error_bound(xt: np.ndarray, sig_bits: int) -> np.ndarray:
     """Bound on |fp32 mean-pool - exact mean| per (cube, channel), any order.
 
-    The 64 inputs carry ``sig_bits`` significant bits (8 for bf16 values, 24
-    for fp32). If every input is a multiple of 2^q and the sum of their
-    magnitudes is below 2^(q+24), every partial sum is an fp32 number, so the
-    fp32 sum is exact whatever the order; otherwise the classic recursive-
-    summation bound gamma_63 * sum|x| applies. Dividing by 64 is exact.
+    The B inputs of a cube carry ``sig_bits`` significant bits (8 for bf16
+    values, 24 for fp32). If every input is a multiple of 2^q and the sum of
+    their magnitudes is below 2^(q+24), every partial sum is an fp32 number, so
+    the fp32 sum is exact whatever the order; otherwise the classic recursive-
+    summation bound gamma_(B-1) * sum|x| applies. Dividing by B (a power of
+    two) is exact.
     """
     u = 2.0 ** -24
     mag = np.abs(xt)
@@ -211,15 +229,16 @@ def _pool_error_bound(xt: np.ndarray, sig_bits: int) -> np.ndarray:
     q = ulp_exp.min(axis=-2)
     total = mag.sum(axis=-2)
     exact = total < np.ldexp(1.0, np.minimum(q + 24, 1000))
-    gamma = (TILE - 1) * u / (1 - (TILE - 1) * u)
-    return np.where(exact, 0.0, gamma * total / TILE)
+    b = xt.shape[-2]
+    gamma = (b - 1) * u / (1 - (b - 1) * u)
+    return np.where(exact, 0.0, gamma * total / b)
 
 
 def logit_error_bound(qt: np.ndarray, kt: np.ndarray, scale: float, sig_bits: int = 8,
                       pool_mode: str = "mean") -> np.ndarray:
     """Per-row bound on |fp32 coarse logit - exact logit| for one (b, h).
 
-    The fp32 path pools 64 inputs (error bounded by ``_pool_error_bound``),
+    The fp32 path pools B inputs (error bounded by ``_pool_error_bound``),
     forms the d-term dot product of the pooled rows (error at most gamma_d
     times the sum of absolute products, any order: the standard forward error
     bound of recursive summation) and multiplies by the fp32 scale (a few
@@ -247,13 +266,13 @@ def logit_error_bound(qt: np.ndarray, kt: np.ndarray, scale: float, sig_bits: in
 def fine_gathered(qt, kt, vt, idx, lens, scale):
     """Token attention of each query cube over the tokens of its listed cubes.
 
-    For one (b, h): qt, kt, vt [Nc, 64, d]; idx [Nc, L] and lens [Nc].
-    Returns O_f [Nc, 64, d] and LSE_f [Nc, 64]. An empty list gives O_f = 0
+    For one (b, h): qt, kt, vt [Nc, B, d]; idx [Nc, L] and lens [Nc].
+    Returns O_f [Nc, B, d] and LSE_f [Nc, B]. An empty list gives O_f = 0
     and LSE_f = -inf.
     """
-    nc, _, d = qt.shape
+    nc, b, d = qt.shape
     of = np.zeros_like(qt)
-    lse = np.full((nc, TILE), -np.inf)
+    lse = np.full((nc, b), -np.inf)
     for i in range(nc):
         sel = idx[i, :lens[i]]
         if sel.size == 0:
@@ -269,7 +288,7 @@ def fine_gathered(qt, kt, vt, idx, lens, scale):
     return of, lse
 
 
-def fine_literal(q, k, v, mask, scale):
+def fine_literal(q, k, v, mask, scale, cube=DEFAULT_CUBE):
     """The App. B form: full token-level scores, unselected blocks set to -inf,
     row softmax, times V. For one (b, h) in raster layout, q/k/v [T, H, W, d],
     mask [Nc, Nc]. Quadratic in N: small shapes only. Returns (O_f, LSE_f) raster."""
@@ -277,7 +296,7 @@ def fine_literal(q, k, v, mask, scale):
     n = T * H * W
     qr, kr, vr = q.reshape(n, d), k.reshape(n, d), v.reshape(n, d)
     cube_of = np.empty(n, dtype=np.int64)
-    cube_of[tiled_to_raster(T, H, W)] = np.arange(n) // TILE
+    cube_of[tiled_to_raster(T, H, W, cube)] = np.arange(n) // int(np.prod(_cube(cube)))
     allowed = mask[cube_of[:, None], cube_of[None, :]]
     z = np.where(allowed, scale * (qr @ kr.T), -np.inf)
     o = np.zeros((n, d))
@@ -294,9 +313,10 @@ def fine_literal(q, k, v, mask, scale):
 # --------------------------------------------------------------------------
 # Step 5: gated combination and untile (section 2; App. B; key design 3)
 # --------------------------------------------------------------------------
-def repeat_coarse(oc: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
-    """O_c of each cube repeated to its 64 tokens, raster layout [..., T, H, W, d]."""
-    return untile(np.repeat(oc[..., :, None, :], TILE, axis=-2), T, H, W)
+def repeat_coarse(oc: np.ndarray, T: int, H: int, W: int, cube=DEFAULT_CUBE) -> np.ndarray:
+    """O_c of each cube repeated to its B tokens, raster layout [..., T, H, W, d]."""
+    b = int(np.prod(_cube(cube)))
+    return untile(np.repeat(oc[..., :, None, :], b, axis=-2), T, H, W, cube)
 
 
 def combine(oc_rep, of, g_c=None, g_f=None):
@@ -320,8 +340,9 @@ def _f64(x):
 
 
 def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
-            scale: Optional[float] = None, with_literal: bool = False, pool_mode: str = "mean"):
-    """VSA forward for [B, h, T, H, W, d] inputs.
+            scale: Optional[float] = None, with_literal: bool = False, pool_mode: str = "mean",
+            cube=DEFAULT_CUBE):
+    """VSA forward for [B, h, T, H, W, d] inputs with cubes of shape ``cube``.
 
     topk > 0 selects the K best cubes per row; topk == 0 uses the caller's
     lists idx [B, h, Nc, L] / lens [B, h, Nc]. Returns a dict of float64
@@ -330,9 +351,10 @@ def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
     sig_bits = 24 if np.asarray(q).dtype == np.float32 and not _bf16_exact(q) else 8
     q, k, v, g_c, g_f = map(_f64, (q, k, v, g_c, g_f))
     B, nh, T, H, W, d = q.shape
-    nc = T * H * W // TILE
+    cube = _cube(cube)
+    nc = T * H * W // int(np.prod(cube))
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    qt, kt, vt = tile(q), tile(k), tile(v)
+    qt, kt, vt = tile(q, cube), tile(k, cube), tile(v, cube)
     qc, kc, vc = pool(qt, pool_mode), pool(kt, pool_mode), pool(vt, pool_mode)
     oc = np.empty_like(qc)
     lse_c = np.empty(qc.shape[:-1])
@@ -359,12 +381,12 @@ def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
                                                     idx_o[b, h], lens_o[b, h], s)
             if with_literal:
                 m = lists_to_mask(idx_o[b, h], lens_o[b, h], nc)
-                of_lit[b, h], _ = fine_literal(q[b, h], k[b, h], v[b, h], m, s)
-    of = untile(of_t, T, H, W)
-    oc_rep = repeat_coarse(oc, T, H, W)
-    out = dict(scale=s, pool_mode=pool_mode, q_c=qc, k_c=kc, v_c=vc, s_c=s_c, o_c=oc, lse_c=lse_c,
+                of_lit[b, h], _ = fine_literal(q[b, h], k[b, h], v[b, h], m, s, cube)
+    of = untile(of_t, T, H, W, cube)
+    oc_rep = repeat_coarse(oc, T, H, W, cube)
+    out = dict(scale=s, pool_mode=pool_mode, cube=cube, q_c=qc, k_c=kc, v_c=vc, s_c=s_c, o_c=oc, lse_c=lse_c,
                idx=idx_o, len=lens_o, margin=margin, tau=tau,
-               o_f=of, lse_f=untile_rows(lse_t, T, H, W), o_c_rep=oc_rep,
+               o_f=of, lse_f=untile_rows(lse_t, T, H, W, cube), o_c_rep=oc_rep,
                o=combine(oc_rep, of, g_c, g_f))
     if with_literal:
         out["o_f_literal"] = of_lit
@@ -387,9 +409,9 @@ def fine_backward(qt, kt, vt, dof_t, of_t, lse_t, idx, lens, scale):
 
     With P = exp(s*q.k - LSE_f) on the listed blocks: dV = P^T dO_f,
     dP = dO_f V^T, D = rowsum(dO_f * O_f), dS = P * (dP - D),
-    dQ = s*dS K, dK = s*dS^T Q. Returns dQ, dK, dV [Nc, 64, d] and D [Nc, 64].
+    dQ = s*dS K, dK = s*dS^T Q. Returns dQ, dK, dV [Nc, B, d] and D [Nc, B].
     """
-    nc, _, d = qt.shape
+    nc, b, d = qt.shape
     dq = np.zeros_like(qt)
     dk = np.zeros_like(kt)
     dv = np.zeros_like(vt)
@@ -404,8 +426,8 @@ def fine_backward(qt, kt, vt, dof_t, of_t, lse_t, idx, lens, scale):
         dp = dof_t[i] @ vs.T
         ds = p * (dp - dd[i][:, None])
         dq[i] = scale * (ds @ ks)
-        dk_sel = (scale * (ds.T @ qt[i])).reshape(-1, TILE, d)
-        dv_sel = (p.T @ dof_t[i]).reshape(-1, TILE, d)
+        dk_sel = (scale * (ds.T @ qt[i])).reshape(-1, b, d)
+        dv_sel = (p.T @ dof_t[i]).reshape(-1, b, d)
         np.add.at(dk, sel, dk_sel)
         np.add.at(dv, sel, dv_sel)
     return dq, dk, dv, dd
@@ -420,8 +442,10 @@ def coarse_backward(qc, kc, vc, doc, scale):
     return scale * (ds @ kc), scale * (ds.T @ qc), dv
 
 
-def pool_backward(dxc: np.ndarray, xt: Optional[np.ndarray] = None, mode: str = "mean") -> np.ndarray:
-    """Gradient of the mean-pool: each of the 64 tokens of cube c gets dX_c[c]/64.
+def pool_backward(dxc: np.ndarray, xt: Optional[np.ndarray] = None, mode: str = "mean",
+                  tile_size: int = TILE) -> np.ndarray:
+    """Gradient of the mean-pool: each of the B tokens of cube c gets dX_c[c]/B
+    (B = xt.shape[-2] when xt is given, else tile_size).
 
     mode "max" (xt = the pooled input, tiled): per channel, the whole dX_c[c]
     goes to the token holding the maximum; among equal maxima, the first in
@@ -431,7 +455,8 @@ def pool_backward(dxc: np.ndarray, xt: Optional[np.ndarray] = None, mode: str = 
         out = np.zeros(xt.shape, dtype=np.result_type(dxc, np.float64))
         np.put_along_axis(out, arg[..., None, :], dxc[..., None, :], axis=-2)
         return out
-    return np.repeat(dxc[..., :, None, :], TILE, axis=-2) / TILE
+    b = xt.shape[-2] if xt is not None else tile_size
+    return np.repeat(dxc[..., :, None, :], b, axis=-2) / b
 
 
 def backward(q, k, v, g_c, g_f, d_o, fwd: dict):
@@ -440,11 +465,12 @@ def backward(q, k, v, g_c, g_f, d_o, fwd: dict):
     q, k, v, g_c, g_f, d_o = map(_f64, (q, k, v, g_c, g_f, d_o))
     B, nh, T, H, W, d = q.shape
     s = fwd["scale"]
+    cube = fwd.get("cube", DEFAULT_CUBE)
     dgc, dgf, dof, docr = combine_backward(d_o, fwd["o_c_rep"], fwd["o_f"], g_c, g_f)
-    doc = tile(docr).sum(axis=-2)   # the repeat's gradient sums over the cube
-    qt, kt, vt = tile(q), tile(k), tile(v)
-    dof_t, of_t = tile(dof), tile(fwd["o_f"])
-    lse_t = tile(fwd["lse_f"][..., None])[..., 0]
+    doc = tile(docr, cube).sum(axis=-2)   # the repeat's gradient sums over the cube
+    qt, kt, vt = tile(q, cube), tile(k, cube), tile(v, cube)
+    dof_t, of_t = tile(dof, cube), tile(fwd["o_f"], cube)
+    lse_t = tile(fwd["lse_f"][..., None], cube)[..., 0]
     dqt, dkt, dvt = np.empty_like(qt), np.empty_like(kt), np.empty_like(vt)
     dd_t = np.empty(qt.shape[:-1])
     dqc, dkc, dvc = (np.empty_like(fwd["q_c"]) for _ in range(3))
@@ -456,24 +482,24 @@ def backward(q, k, v, g_c, g_f, d_o, fwd: dict):
             dqc[b, h], dkc[b, h], dvc[b, h] = coarse_backward(
                 fwd["q_c"][b, h], fwd["k_c"][b, h], fwd["v_c"][b, h], doc[b, h], s)
     pm = fwd.get("pool_mode", "mean")
-    dq = untile(dqt + pool_backward(dqc, qt, pm), T, H, W)
-    dk = untile(dkt + pool_backward(dkc, kt, pm), T, H, W)
-    dv = untile(dvt + pool_backward(dvc, vt, pm), T, H, W)
+    dq = untile(dqt + pool_backward(dqc, qt, pm), T, H, W, cube)
+    dk = untile(dkt + pool_backward(dkc, kt, pm), T, H, W, cube)
+    dv = untile(dvt + pool_backward(dvc, vt, pm), T, H, W, cube)
     return dict(dq=dq, dk=dk, dv=dv, dg_c=dgc, dg_f=dgf, d_o_f=dof, d_o_c=doc,
-                delta=untile_rows(dd_t, T, H, W), dq_c=dqc, dk_c=dkc, dv_c=dvc)
+                delta=untile_rows(dd_t, T, H, W, cube), dq_c=dqc, dk_c=dkc, dv_c=dvc)
 
 
 # --------------------------------------------------------------------------
 # Work accounting (computed blocks only)
 # --------------------------------------------------------------------------
-def fine_flops_forward(lens: np.ndarray, d: int) -> float:
-    """4*64*64*d FLOPs per computed (query cube, key cube) block pair."""
-    return 4.0 * TILE * TILE * d * float(np.sum(lens))
+def fine_flops_forward(lens: np.ndarray, d: int, tile_size: int = TILE) -> float:
+    """4*B*B*d FLOPs per computed (query cube, key cube) block pair."""
+    return 4.0 * tile_size * tile_size * d * float(np.sum(lens))
 
 
-def fine_flops_backward(lens: np.ndarray, d: int) -> float:
-    """10*64*64*d FLOPs per block pair (2.5x the forward, the usual convention)."""
-    return 10.0 * TILE * TILE * d * float(np.sum(lens))
+def fine_flops_backward(lens: np.ndarray, d: int, tile_size: int = TILE) -> float:
+    """10*B*B*d FLOPs per block pair (2.5x the forward, the usual convention)."""
+    return 10.0 * tile_size * tile_size * d * float(np.sum(lens))
 
 
 def coarse_flops(B: int, nh: int, nc: int, d: int) -> float:

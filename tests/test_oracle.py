@@ -39,6 +39,25 @@ def test_tile_matches_reshape_transpose(T, H, W):
     np.testing.assert_array_equal(O.untile(O.tile(x), T, H, W), x)
 
 
+@pytest.mark.parametrize("cube", [(2, 4, 4), (4, 4, 8), (1, 8, 8), (4, 2, 8), (2, 2, 8)])
+def test_tile_general_cube_matches_reshape_transpose(cube):
+    """Other cube shapes (Ct, Ch, Cw): the same row-major construction."""
+    ct, ch, cw = cube
+    T, H, W, d = 2 * ct, 3 * ch, 2 * cw, 3
+    x = _rand((2, T, H, W, d), 7)
+    ref = x.reshape(2, T // ct, ct, H // ch, ch, W // cw, cw, d).transpose(0, 1, 3, 5, 2, 4, 6, 7)
+    ref = ref.reshape(2, T * H * W // (ct * ch * cw), ct * ch * cw, d)
+    np.testing.assert_array_equal(O.tile(x, cube), ref)
+    np.testing.assert_array_equal(O.untile(O.tile(x, cube), T, H, W, cube), x)
+    want = []
+    for n, e in zip((T - 1, H, W + 1), cube):
+        m = n
+        while m % e:
+            m += 1
+        want.append(m)
+    assert O.compatible_latent(T - 1, H, W + 1, cube) == tuple(want)
+
+
 def test_tile_is_bijection():
     perm = O.tiled_to_raster(8, 12, 16)
     assert np.array_equal(np.sort(perm), np.arange(8 * 12 * 16))
@@ -259,26 +278,26 @@ def test_repeat_coarse_matches_repeat_interleave():
 
 
 # ----------------------------------------------------------------- end to end
-def _torch_vsa(q, k, v, g_c, g_f, mask, scale, pool_mode="mean"):
+def _torch_vsa(q, k, v, g_c, g_f, mask, scale, pool_mode="mean", cube=(4, 4, 4)):
     """Independent torch expression of the forward with a fixed block mask:
-    avg_pool3d (or max_pool3d) pooling, repeat_interleave broadcast,
-    token-level masked softmax."""
+    avg_pool3d (or max_pool3d) pooling with the cube as kernel,
+    repeat_interleave broadcast, token-level masked softmax."""
     B, h, T, H, W, d = q.shape
-    Tp, Hp, Wp = T // 4, H // 4, W // 4
+    Tp, Hp, Wp = T // cube[0], H // cube[1], W // cube[2]
     pool3d = F.max_pool3d if pool_mode == "max" else F.avg_pool3d
 
     def pool(x):
-        p = pool3d(x.permute(0, 1, 5, 2, 3, 4).reshape(B * h, d, T, H, W), 4)
+        p = pool3d(x.permute(0, 1, 5, 2, 3, 4).reshape(B * h, d, T, H, W), tuple(cube))
         return p.reshape(B, h, d, -1).transpose(-1, -2)
 
     qc, kc, vc = pool(q), pool(k), pool(v)
     a = torch.softmax(scale * qc @ kc.transpose(-1, -2), dim=-1)
     oc = (a @ vc).reshape(B, h, Tp, Hp, Wp, d)
     for ax in (2, 3, 4):
-        oc = oc.repeat_interleave(4, dim=ax)
+        oc = oc.repeat_interleave(cube[ax - 2], dim=ax)
     cid = torch.arange(Tp * Hp * Wp).reshape(Tp, Hp, Wp)
     for ax in (0, 1, 2):
-        cid = cid.repeat_interleave(4, dim=ax)
+        cid = cid.repeat_interleave(cube[ax], dim=ax)
     cid = cid.reshape(-1)
     tok_mask = mask[:, :, cid][:, :, :, cid]
     qr, kr, vr = (x.reshape(B, h, -1, d) for x in (q, k, v))
@@ -343,6 +362,37 @@ def test_backward_matches_autograd_of_independent_expression():
     for name, key in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg_c", "g_c"), ("dg_f", "g_f")):
         np.testing.assert_allclose(bwd[name], ts[key].grad.numpy(), rtol=1e-10, atol=1e-12,
                                    err_msg=name)
+
+
+@pytest.mark.parametrize("cube", [(2, 4, 4), (4, 4, 8), (1, 8, 8)])
+def test_general_cube_forward_backward_match_autograd(cube):
+    """Other cube shapes (tile size B = 32, 128, 64): forward and backward of
+    the oracle against the independent expression pooled with avg_pool3d over
+    the cube, and the literal masked-dense form against the gathered one."""
+    ct, ch, cw = cube
+    T, H, W = 2 * ct, 2 * ch, 2 * cw
+    w = WL.make_inputs_custom(1, 2, 4, T, H, W, dtype="f32", seed=8, scale=0.5)
+    nc = 8
+    idx, lens = WL.random_lists(nc, 2 * nc, 1, 5, seed=9)
+    idx, lens = idx.reshape(1, 2, nc, -1), lens.reshape(1, 2, nc)
+    fwd = O.forward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], topk=0, idx=idx, lens=lens,
+                    with_literal=True, cube=cube)
+    bwd = O.backward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], w["d_o"], fwd)
+    mask = np.stack([[O.lists_to_mask(idx[0, h], lens[0, h], nc) for h in range(2)]])
+    ts = {x: torch.from_numpy(w[x].astype(np.float64)).requires_grad_(True)
+          for x in ("q", "k", "v", "g_c", "g_f")}
+    out = _torch_vsa(ts["q"], ts["k"], ts["v"], ts["g_c"], ts["g_f"], torch.from_numpy(mask), 0.5, cube=cube)
+    np.testing.assert_allclose(fwd["o"], out.detach().numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fwd["o_f"], fwd["o_f_literal"], rtol=1e-12, atol=1e-14)
+    (out * torch.from_numpy(w["d_o"].astype(np.float64))).sum().backward()
+    for name, key in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg_c", "g_c"), ("dg_f", "g_f")):
+        np.testing.assert_allclose(bwd[name], ts[key].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+    # adaptation start (K = all cubes, G_c = 0, G_f removed) is full attention for any cube
+    full = O.forward(w["q"], w["k"], w["v"], np.zeros_like(w["g_c"]), None, topk=nc, cube=cube)
+    for h in range(2):
+        ref = F.scaled_dot_product_attention(
+            *(torch.from_numpy(w[x][0, h].astype(np.float64).reshape(1, -1, 4)) for x in ("q", "k", "v")))
+        np.testing.assert_allclose(full["o"][0, h].reshape(-1, 4), ref[0].numpy(), rtol=1e-11, atol=1e-13)
 
 
 def test_max_pool_matches_max_pool3d_and_first_argmax():
