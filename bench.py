@@ -170,6 +170,66 @@ def train_measure(name: str, steps: int, warmup: int) -> dict:
             "combine_bwd_frac_hbm_peak": round(cb_bytes / (st[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
+def tile_case(V, torch, name, q, k, v, gc, gf, cube, steps=5):
+    """Forward of one workload's inputs with cubes of shape `cube` at the same
+    token-level sparsity as K = 32 with 64-token tiles (K * Bt = 2048)."""
+    B, heads, T, H, W, d = q.shape
+    bt = cube[0] * cube[1] * cube[2]
+    p = V.Problem(B, heads, T, H, W, d, topk=max(1, 32 * 64 // bt), cube=cube)
+    ws = V.workspace(p, q)
+    o = torch.empty_like(q)
+    idx = torch.empty((B, heads, p.Nc, p.stride), dtype=torch.int32, device=q.device)
+    lens = torch.empty((B, heads, p.Nc), dtype=torch.int32, device=q.device)
+    pooled = [torch.empty((B, heads, p.Nc, d), dtype=torch.float32, device=q.device) for _ in range(4)]
+    lse_c = torch.empty((B, heads, p.Nc), dtype=torch.float32, device=q.device)
+    for _ in range(2):
+        V.forward(p, q, k, v, gc, gf, idx=idx, lens=lens, ws=ws, out=o)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for _ in range(steps):
+        V.forward(p, q, k, v, gc, gf, idx=idx, lens=lens, ws=ws, out=o)
+    ev[1].record()
+    V.pool(p, q, k, v, out=pooled[:3])
+    V.coarse(p, *pooled[:3], out=(pooled[3], lse_c, idx, lens), ws=ws)
+    ev[2].record()
+    for _ in range(steps):
+        V.fine_combine(p, q, k, v, idx, lens, pooled[3], gc, gf, ws=ws, out=o)
+    ev[3].record()
+    torch.cuda.synchronize()
+    fwd_ms = ev[0].elapsed_time(ev[1]) / steps
+    fine_ms = ev[2].elapsed_time(ev[3]) / steps
+    flop = 4.0 * bt * bt * d * int(lens.sum().item())
+    return {"workload": name, "cube": list(cube), "tile_tokens": bt, "topk": p.topk,
+            "forward_ms": round(fwd_ms, 4), "fine_combine_ms": round(fine_ms, 4),
+            "fine_TFLOP_per_s": round(flop / (fine_ms * 1e-3) / 1e12, 2),
+            "forward_TFLOP_per_s": round(flop / (fwd_ms * 1e-3) / 1e12, 2),
+            "tokens_per_s": round(B * T * H * W / (fwd_ms * 1e-3), 1)}
+
+
+def tile_tradeoff(V, WL, torch, main_name, main_inputs):
+    """The tile-size trade-off: the same inputs with 32-, 64- and 128-token
+    tiles where the latent allows them (a cube side must divide the latent's,
+    and Nc must stay within the coarse stage's limit)."""
+    out = []
+    for cube in ((4, 4, 4), (4, 4, 8), (2, 4, 4)):
+        T, H, W = main_inputs[0].shape[2:5]
+        bt = cube[0] * cube[1] * cube[2]
+        if T % cube[0] or H % cube[1] or W % cube[2] or T * H * W // bt > V.max_cubes():
+            continue
+        out.append(tile_case(V, torch, main_name, *main_inputs, cube))
+        log(f"  tiles {cube}: {out[-1]}")
+    for name, cubes in (("bf16_480p_20x28x52", ((4, 4, 4), (2, 4, 4))),
+                        ("bf16_16x32x32_spikes", ((4, 4, 4), (2, 4, 4), (4, 4, 8)))):
+        x = WL.make_inputs(name)
+        t = [torch.from_numpy(x[n]).to("cuda:0").to(torch.bfloat16).contiguous() for n in ("q", "k", "v", "g_c", "g_f")]
+        del x
+        for cube in cubes:
+            out.append(tile_case(V, torch, name, *t, cube))
+            log(f"  tiles {cube}: {out[-1]}")
+        del t
+    return out
+
+
 def dense_flash_context(heads: int, n: int, d: int, reps: int = 3):
     """Dense attention through PyTorch's flash SDPA backend (no other backend
     allowed) on one head-count / length / head_dim: the vendor kernel's
@@ -373,6 +433,9 @@ def main() -> int:
     line["variants"] = {"max_pool_forward": {"ms_per_step": round(mp_ms, 4),
                                              "TFLOP_per_s": round(4.0 * 64 * 64 * w.head_dim * int(lens.sum().item())
                                                                   / (mp_ms * 1e-3) / 1e12, 2)}}
+    if w.dtype == "bf16":
+        log("timing the tile-size trade-off")
+        line["variants"]["tile_tradeoff"] = tile_tradeoff(V, WL, torch, w.name, (q, k, v, gc, gf))
     ctx = dense_flash_context(w.heads, 16384, w.head_dim)
     if "tflops" in ctx:
         ctx["fine_kernel_vs_dense"] = round(achieved / ctx["tflops"], 3)

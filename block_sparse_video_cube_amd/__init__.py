@@ -38,15 +38,20 @@ class Problem:
     list_stride: int = 0         # 0 => topk
     scale: float = 0.0           # 0 => 1/sqrt(head_dim)
     pool: str = "mean"           # cube pooling of the coarse stage: "mean" or "max"
-    layout: str = "raster"       # token order: "raster" [B,h,T,H,W,d] or "tiled" [B,h,Nc,64,d]
+    layout: str = "raster"       # token order: "raster" [B,h,T,H,W,d] or "tiled" [B,h,Nc,Bt,d]
+    cube: tuple = (4, 4, 4)      # cube sides (Ct, Ch, Cw); Bt = Ct*Ch*Cw tokens per tile
 
     @property
     def N(self) -> int:
         return self.T * self.H * self.W
 
     @property
+    def Bt(self) -> int:
+        return self.cube[0] * self.cube[1] * self.cube[2]
+
+    @property
     def Nc(self) -> int:
-        return self.N // 64
+        return self.N // self.Bt
 
     @property
     def stride(self) -> int:
@@ -61,7 +66,7 @@ class Problem:
         pool = {"mean": 0, "max": 1}.get(self.pool, 99)
         layout = {"raster": 0, "tiled": 1}.get(self.layout, 99)
         return VsaProblem(self.B, self.heads, self.T, self.H, self.W, self.head_dim, code,
-                          float(self.scale), self.topk, self.list_stride, pool, layout)
+                          float(self.scale), self.topk, self.list_stride, pool, layout, *self.cube)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -102,7 +107,7 @@ def workspace(p: Problem, like: torch.Tensor, training: bool = False) -> torch.T
 def _raster(p: Problem):
     """Shape of a token tensor in the problem's layout."""
     if p.layout == "tiled":
-        return (p.B, p.heads, p.Nc, 64, p.head_dim)
+        return (p.B, p.heads, p.Nc, p.Bt, p.head_dim)
     return (p.B, p.heads, p.T, p.H, p.W, p.head_dim)
 
 
@@ -112,8 +117,8 @@ def _tokens(p: Problem):
 
 
 def tile(p: Problem, x):
-    """Cube-major copy [B, h, Nc, 64, d] of a raster token tensor."""
-    xt = _empty((p.B, p.heads, p.Nc, 64, p.head_dim), x.dtype, x)
+    """Cube-major copy [B, h, Nc, Bt, d] of a raster token tensor."""
+    xt = _empty((p.B, p.heads, p.Nc, p.Bt, p.head_dim), x.dtype, x)
     check(lib().vsa_tile(ctypes.byref(p.c()), _ptr(x), _ptr(xt), _stream(x.device)), "vsa_tile")
     return xt
 
@@ -125,10 +130,10 @@ def untile(p: Problem, xt):
     return x
 
 
-def compatible_latent(T: int, H: int, W: int) -> tuple:
-    """Smallest latent with sides that are multiples of 4 containing T x H x W."""
+def compatible_latent(T: int, H: int, W: int, cube: tuple = (4, 4, 4)) -> tuple:
+    """Smallest latent with sides that are multiples of the cube's containing T x H x W."""
     o = [ctypes.c_int32() for _ in range(3)]
-    check(lib().vsa_compatible_latent(T, H, W, *(ctypes.byref(v) for v in o)), "vsa_compatible_latent")
+    check(lib().vsa_compatible_latent(T, H, W, *cube, *(ctypes.byref(v) for v in o)), "vsa_compatible_latent")
     return tuple(v.value for v in o)
 
 

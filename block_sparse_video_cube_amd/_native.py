@@ -23,7 +23,8 @@ class VsaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("heads", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("topk", ctypes.c_int32),
-                ("list_stride", ctypes.c_int32), ("pool_mode", ctypes.c_int32), ("layout", ctypes.c_int32)]
+                ("list_stride", ctypes.c_int32), ("pool_mode", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("cube_t", ctypes.c_int32), ("cube_h", ctypes.c_int32), ("cube_w", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER(VsaProblem)
@@ -35,7 +36,7 @@ _i32 = ctypes.c_int32
 SIGNATURES = {
     "vsa_tile": (_i32, [_P, _v, _v, _v]),
     "vsa_untile": (_i32, [_P, _v, _v, _v]),
-    "vsa_compatible_latent": (_i32, [_i32, _i32, _i32, _v, _v, _v]),
+    "vsa_compatible_latent": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _v, _v, _v]),
     "vsa_crop": (_i32, [_P, _v, _i32, _i32, _i32, _v, _v]),
     "vsa_pad": (_i32, [_P, _v, _i32, _i32, _i32, _v, _v]),
     "vsa_status_string": (ctypes.c_char_p, [_i32]),

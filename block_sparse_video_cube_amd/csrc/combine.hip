@@ -4,7 +4,7 @@
 // the hidden states); VSA summary page (paperlayer.ai, arXiv 2505.13389),
 // Appendix B (coarse output repeated over each block, combination, untile).
 // The backward is the calculus of that elementwise sum; the repeat's gradient
-// sums over the cube's 64 tokens.
+// sums over the cube's tokens.
 #include "vsa_kernels.h"
 
 namespace vsa {
@@ -37,12 +37,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // Backward of the combine, one workgroup per (b, h, cube):
 //   dg_c = dO * O_c[c], dg_f = dO * O_f, d_o_f = dO * G_f (rounded to T),
 //   delta[token] = sum_ch d_o_f * O_f, d_o_c[c] = sum over the cube of dO * G_c,
-template <typename T, int D>
+template <typename T, int D, int BT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ d_o, const float* __restrict__ oc, const T* __restrict__ of, const T* __restrict__ gc,
     const T* __restrict__ gf, T* __restrict__ dgc, T* __restrict__ dgf, T* __restrict__ dof,
     float* __restrict__ delta, float* __restrict__ doc, Grid g) {
-  constexpr int CH = D / 8, RPP = 256 / CH, PASSES = kTile / RPP;
+  constexpr int CH = D / 8, RPP = 256 / CH, PASSES = BT / RPP;   // BT = tokens per cube
   __shared__ float part[RPP][D + 4];
   const int tid = threadIdx.x;
   const long bh = blockIdx.y;
@@ -114,28 +114,28 @@ hipError_t launch_combine(const Launch& L, const float* oc, const void* of, cons
   return hipGetLastError();
 }
 
+template <typename T, int D>
+static void combine_bwd_launch(const Launch& L, const void* d_o, const float* oc, const void* of, const void* gc,
+                               const void* gf, void* dgc, void* dgf, void* dof, float* delta, float* doc) {
+  const dim3 grid(L.g.Nc, L.BH), block(256);
+#define VSA_COMBINE_BWD(BT)                                                                                   \
+  hipLaunchKernelGGL((combine_bwd_kernel<T, D, BT>), grid, block, 0, L.stream, (const T*)d_o, oc, (const T*)of, \
+                     (const T*)gc, (const T*)gf, (T*)dgc, (T*)dgf, (T*)dof, delta, doc, L.g)
+  if (L.g.B == 32) VSA_COMBINE_BWD(32);
+  else if (L.g.B == 128) VSA_COMBINE_BWD(128);
+  else VSA_COMBINE_BWD(64);
+#undef VSA_COMBINE_BWD
+}
+
 hipError_t launch_combine_bwd(const Launch& L, const void* d_o, const float* oc, const void* of,
                               const void* gc, const void* gf, void* dgc, void* dgf, void* dof,
                               float* delta, float* doc) {
-  const dim3 grid(L.g.Nc, L.BH), block(256);
   if (L.bf16) {
-    if (L.D == 64)
-      hipLaunchKernelGGL((combine_bwd_kernel<bf16, 64>), grid, block, 0, L.stream, (const bf16*)d_o, oc,
-                         (const bf16*)of, (const bf16*)gc, (const bf16*)gf, (bf16*)dgc, (bf16*)dgf, (bf16*)dof,
-                         delta, doc, L.g);
-    else
-      hipLaunchKernelGGL((combine_bwd_kernel<bf16, 128>), grid, block, 0, L.stream, (const bf16*)d_o, oc,
-                         (const bf16*)of, (const bf16*)gc, (const bf16*)gf, (bf16*)dgc, (bf16*)dgf, (bf16*)dof,
-                         delta, doc, L.g);
+    if (L.D == 64) combine_bwd_launch<bf16, 64>(L, d_o, oc, of, gc, gf, dgc, dgf, dof, delta, doc);
+    else combine_bwd_launch<bf16, 128>(L, d_o, oc, of, gc, gf, dgc, dgf, dof, delta, doc);
   } else {
-    if (L.D == 64)
-      hipLaunchKernelGGL((combine_bwd_kernel<float, 64>), grid, block, 0, L.stream, (const float*)d_o, oc,
-                         (const float*)of, (const float*)gc, (const float*)gf, (float*)dgc, (float*)dgf,
-                         (float*)dof, delta, doc, L.g);
-    else
-      hipLaunchKernelGGL((combine_bwd_kernel<float, 128>), grid, block, 0, L.stream, (const float*)d_o, oc,
-                         (const float*)of, (const float*)gc, (const float*)gf, (float*)dgc, (float*)dgf,
-                         (float*)dof, delta, doc, L.g);
+    if (L.D == 64) combine_bwd_launch<float, 64>(L, d_o, oc, of, gc, gf, dgc, dgf, dof, delta, doc);
+    else combine_bwd_launch<float, 128>(L, d_o, oc, of, gc, gf, dgc, dgf, dof, delta, doc);
   }
   return hipGetLastError();
 }

@@ -6,15 +6,15 @@
 // formulas are the calculus of softmax attention: with P = exp(s*q.k - LSE),
 //   dV = P^T dO, dP = dO V^T, dS = P * (dP - delta), delta = rowsum(dO * O),
 //   dQ = s * dS K, dK = s * dS^T Q,
-// and the mean-pool spreads dX_c[c] / 64 over the cube's tokens (the
+// and the mean-pool spreads dX_c[c] / Bt over the cube's Bt tokens (the
 // max-pool variant sends it to the cube's maximum), added here.
 //
 // Two kernels, both deterministic (no atomics), in the style of the forward:
-// a workgroup of two waves owns one cube, wave w its tokens 32w .. 32w+31,
-// one per lane (column) of 32x32x16 bf16 MFMAs, and walks a list of partner
-// cubes in 32-token chunks: row tiles of the partner's tensors staged in LDS
-// by direct-to-LDS loads (each wave issues half; the next chunk loads while
-// this one is computed). The transposed operands come from the same row
+// a workgroup of NW = Bt/32 waves owns one cube, wave w its tokens
+// 32w .. 32w+31, one per lane (column) of 32x32x16 bf16 MFMAs, and walks a
+// list of partner cubes in 32-token chunks: row tiles of the partner's
+// tensors staged in LDS by direct-to-LDS loads (each wave issues 1/NW; the
+// next chunk loads while this one is computed). The transposed operands come from the same row
 // tiles through LDS transpose reads.
 //  * dQ, per query cube i over its list of key cubes (the forward's list):
 //      S^T = K_c Q^T, dP^T = V_c dO^T        A = K / V row tiles, B = the
@@ -33,14 +33,16 @@
 namespace vsa {
 
 // Pool backward for one token and channels ch .. ch+3 of its cube: the pooled
-// gradient / 64 (mean pooling), or the whole pooled gradient where the token
-// holds the cube's maximum (arg = the cube's argmax positions, max pooling).
-__device__ __forceinline__ void pooled_grad(const float* dxc, const uint8_t* arg, int ch, int l, float out[4]) {
+// gradient / Bt (mean pooling; inv_b = 1/Bt, exact), or the whole pooled
+// gradient where the token holds the cube's maximum (arg = the cube's argmax
+// positions, max pooling).
+__device__ __forceinline__ void pooled_grad(const float* dxc, const uint8_t* arg, int ch, int l, float inv_b,
+                                            float out[4]) {
   const float4 c4 = *reinterpret_cast<const float4*>(dxc + ch);
   const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
   if (arg == nullptr) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) out[r] = cv[r] * (1.0f / kTile);
+    for (int r = 0; r < 4; ++r) out[r] = cv[r] * inv_b;
   } else {
     const uchar4 a4 = *reinterpret_cast<const uchar4*>(arg + ch);
     const int av[4] = {a4.x, a4.y, a4.z, a4.w};
@@ -82,8 +84,8 @@ __global__ __launch_bounds__(1024) void order_by_count_kernel(const int32_t* __r
   for (int e = threadIdx.x; e < Nc; e += 1024) order[bh * Nc + e] = (int32_t)(key[e] & 0xffffffffu);
 }
 
-template <int D>
-__global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void fine_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
     const float* __restrict__ lse_f, const bf16* __restrict__ dof, const float* __restrict__ delta,
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
   const int L = min(max(len[item], 0), stride);
   const int32_t* list = idx + (long)item * stride;
 
-  // This lane's query: token (2wv + n32/16, (n32/4)%4, n32%4) of cube i.
-  const long n = tok0 + cube_row(g, i, 2 * wv + (n32 >> 4), (n32 >> 2) & 3) + (n32 & 3);
+  // This lane's query: in-cube token 32wv + n32 of cube i.
+  const long n = tok0 + cube_token(g, i, 32 * wv + n32);
   bf16x8 qf[G::KS], df[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
@@ -121,14 +123,15 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
 
-  uint32_t roff[G::RINS / 2];
-  row_tile_offsets<D>(g, wv, lane, roff);
+  uint32_t roff[G::RINS / NW];
+  row_tile_offsets<D, NW>(g, wv, lane, roff);
   uint32_t toffs[G::MB][2][2];   // transposed reads of the K row tile (dQ^T += K^T dS^T)
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, toffs[mb][s2]);
-  const uint32_t rhalf = (uint32_t)(half_rows(g) * D) * 2u;
+  // Bytes from a cube's first row to the first row of its chunk h.
+  auto chunk_bytes = [&](int h) { return NW == 1 ? 0u : (uint32_t)(chunk_first(g, h) * D) * 2u; };
   const char* Kb = reinterpret_cast<const char*>(k + tok0 * D);
   const char* Vb = reinterpret_cast<const char*>(v + tok0 * D);
   // Byte offsets of the list's cubes, 64 entries at a time, one per lane.
@@ -137,21 +140,21 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
     const int t = t0 + lane;
     int j = t < L ? list[t] : 0;
     j = (j >= 0 && j < g.Nc) ? j : 0;
-    rcube = (uint32_t)cube_row(g, j, 0, 0) * (uint32_t)(D * 2);
+    rcube = (uint32_t)cube_first(g, j) * (uint32_t)(D * 2);
   };
   const uint32_t rkb = lds_addr(rk), rvb = lds_addr(rv);
   auto issue = [&](int c) {
-    const int e = c >> 1, h = c & 1, st = c & 1;
+    const int e = c / NW, h = c % NW, st = c & 1;
     if ((e & 63) == 0 && h == 0) cubes(e);
-    const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + (h ? rhalf : 0u);
-    issue_row_tile<D>(uniform_ptr(Kb + rc), roff, rkb + st * (G::RUNITS * 16), wv);
-    issue_row_tile<D>(uniform_ptr(Vb + rc), roff, rvb + st * (G::RUNITS * 16), wv);
+    const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + chunk_bytes(h);
+    issue_row_tile<D, NW>(uniform_ptr(Kb + rc), roff, rkb + st * (G::RUNITS * 16), wv);
+    issue_row_tile<D, NW>(uniform_ptr(Vb + rc), roff, rvb + st * (G::RUNITS * 16), wv);
   };
 
-  // Per chunk: wait for this wave's loads, barrier (both halves are in LDS
-  // and both waves are done with the other stage), issue the next chunk,
+  // Per chunk: wait for this wave's loads, barrier (every wave's share is in
+  // LDS and every wave is done with the other stage), issue the next chunk,
   // compute this one.
-  const int nch = 2 * L;
+  const int nch = NW * L;
   if (nch > 0) issue(0);
   for (int c = 0; c < nch; ++c) {
     wait_vmcnt<0>();
@@ -191,13 +194,14 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
   const float* dqc_i = dqc + ((long)bh * g.Nc + i) * D;
   const uint8_t* qarg_i = qarg != nullptr ? qarg + ((long)bh * g.Nc + i) * D : nullptr;
   const int lq = 32 * wv + n32;   // the query's position in its cube
+  const float inv_b = 1.0f / (float)g.B;
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
       const int ch = 32 * mb + 8 * jq + 4 * hf;
       float cv[4];
-      pooled_grad(dqc_i, qarg_i, ch, lq, cv);
+      pooled_grad(dqc_i, qarg_i, ch, lq, inv_b, cv);
       bf16x4 w;
 #pragma unroll
       for (int r = 0; r < 4; ++r) w[r] = (bf16)(scale * acc[mb][4 * jq + r] + cv[r]);
@@ -205,8 +209,8 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dq_kernel(
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ k2q_off,
     const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
@@ -228,8 +232,8 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
   const int32_t* list = k2q + (long)bh * g.Nc * stride + t0;
   const int L = t1 - t0;
 
-  // This lane's key: token (2wv + n32/16, (n32/4)%4, n32%4) of cube j.
-  const long n = tok0 + cube_row(g, j, 2 * wv + (n32 >> 4), (n32 >> 2) & 3) + (n32 & 3);
+  // This lane's key: in-cube token 32wv + n32 of cube j.
+  const long n = tok0 + cube_token(g, j, 32 * wv + n32);
   bf16x8 kf[G::KS], vf[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
@@ -243,14 +247,15 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) { adk[mb][e] = 0.f; adv[mb][e] = 0.f; }
 
-  uint32_t roff[G::RINS / 2];
-  row_tile_offsets<D>(g, wv, lane, roff);
+  uint32_t roff[G::RINS / NW];
+  row_tile_offsets<D, NW>(g, wv, lane, roff);
   uint32_t toffs[G::MB][2][2];   // transposed reads of the Q / dO row tiles
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, toffs[mb][s2]);
-  const uint32_t rhalf = (uint32_t)(half_rows(g) * D) * 2u;
+  // Bytes from a cube's first row to the first row of its chunk h.
+  auto chunk_bytes = [&](int h) { return NW == 1 ? 0u : (uint32_t)(chunk_first(g, h) * D) * 2u; };
   const char* Qb = reinterpret_cast<const char*>(q + tok0 * D);
   const char* Db = reinterpret_cast<const char*>(dof + tok0 * D);
   // Per lane, for 64 list entries at a time: the partner cube and its first
@@ -262,28 +267,29 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
     int ii = t < L ? list[t] : 0;
     ii = (ii >= 0 && ii < g.Nc) ? ii : 0;
     icube = ii;
-    rcube = (uint32_t)cube_row(g, ii, 0, 0) * (uint32_t)(D * 2);
+    rcube = (uint32_t)cube_first(g, ii) * (uint32_t)(D * 2);
   };
   const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd);
   // LSE and delta of the chunk's query rows this lane's accumulator holds:
-  // rows 8m + 4hf + r (m, r = 0..3) = token (2h + m/2, (2m + hf)%4, r).
+  // rows kappa = 8m + 4hf + r (m, r = 0..3) = in-cube tokens 32h + kappa; the
+  // four tokens r = 0..3 are consecutive in memory (Cw >= 4).
   float4 lsn[4], dln[4];
   auto issue = [&](int c) {
-    const int e = c >> 1, h = c & 1, st = c & 1;
+    const int e = c / NW, h = c % NW, st = c & 1;
     if ((e & 63) == 0 && h == 0) cubes(e);
     const int ii = __builtin_amdgcn_readlane(icube, e & 63);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const long r = tok0 + cube_row(g, ii, 2 * h + (m >> 1), (2 * m + hf) & 3);
+      const long r = tok0 + cube_token(g, ii, 32 * h + 8 * m + 4 * hf);
       lsn[m] = *reinterpret_cast<const float4*>(lse_f + r);
       dln[m] = *reinterpret_cast<const float4*>(delta + r);
     }
-    const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + (h ? rhalf : 0u);
-    issue_row_tile<D>(uniform_ptr(Qb + rc), roff, rqb + st * (G::RUNITS * 16), wv);
-    issue_row_tile<D>(uniform_ptr(Db + rc), roff, rdb + st * (G::RUNITS * 16), wv);
+    const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + chunk_bytes(h);
+    issue_row_tile<D, NW>(uniform_ptr(Qb + rc), roff, rqb + st * (G::RUNITS * 16), wv);
+    issue_row_tile<D, NW>(uniform_ptr(Db + rc), roff, rdb + st * (G::RUNITS * 16), wv);
   };
 
-  const int nch = 2 * L;
+  const int nch = NW * L;
   if (nch > 0) issue(0);
   for (int c = 0; c < nch; ++c) {
     wait_vmcnt<0>();
@@ -334,14 +340,15 @@ __global__ __launch_bounds__(128, 1) void fine_bwd_dkdv_kernel(
   const uint8_t* karg_j = karg != nullptr ? karg + cj : nullptr;
   const uint8_t* varg_j = varg != nullptr ? varg + cj : nullptr;
   const int lk = 32 * wv + n32;   // the key's position in its cube
+  const float inv_b = 1.0f / (float)g.B;
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
       const int ch = 32 * mb + 8 * jq + 4 * hf;
       float kcv[4], vcv[4];
-      pooled_grad(dkc + cj, karg_j, ch, lk, kcv);
-      pooled_grad(dvc + cj, varg_j, ch, lk, vcv);
+      pooled_grad(dkc + cj, karg_j, ch, lk, inv_b, kcv);
+      pooled_grad(dvc + cj, varg_j, ch, lk, inv_b, vcv);
       bf16x4 wk, wvv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -361,6 +368,19 @@ hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_
   return hipGetLastError();
 }
 
+template <int D, int NW>
+static void fine_bwd_launch(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
+                            const int32_t* len, const int32_t* qorder, const int32_t* k2q_off, const int32_t* k2q,
+                            const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
+                            const float* dqc, const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
+                            const uint8_t* qarg, const uint8_t* karg, const uint8_t* varg) {
+  const int nitems = L.BH * L.g.Nc;
+  hipLaunchKernelGGL((fine_bwd_dq_kernel<D, NW>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v, idx, len,
+                     qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
+  hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v, k2q_off,
+                     k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
+}
+
 hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
                            const int32_t* len, const int32_t* qorder, const int32_t* k2q_off, const int32_t* k2q,
                            const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
@@ -372,15 +392,13 @@ hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const 
   const uint8_t* karg = args != nullptr ? args + plane : nullptr;
   const uint8_t* varg = args != nullptr ? args + 2 * plane : nullptr;
   if (L.D == 64) {
-    hipLaunchKernelGGL((fine_bwd_dq_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, idx, len, qorder,
-                       lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
-    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<64>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, k2q_off, k2q,
-                       korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
+    if (L.g.B == 32) fine_bwd_launch<64, 1>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
+    else if (L.g.B == 128) fine_bwd_launch<64, 4>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
+    else fine_bwd_launch<64, 2>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
   } else {
-    hipLaunchKernelGGL((fine_bwd_dq_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, idx, len, qorder,
-                       lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
-    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<128>), dim3(nitems), dim3(128), 0, L.stream, q, k, v, k2q_off, k2q,
-                       korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
+    if (L.g.B == 32) fine_bwd_launch<128, 1>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
+    else if (L.g.B == 128) fine_bwd_launch<128, 4>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
+    else fine_bwd_launch<128, 2>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
   }
   return hipGetLastError();
 }

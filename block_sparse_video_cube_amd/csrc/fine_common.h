@@ -1,11 +1,11 @@
 // Device helpers shared by the fine-stage kernels (forward and backward):
 // direct-to-LDS loads of 32-token chunks, and the LDS layouts they fill.
 //
-// A chunk is half h of a cube (tokens 32h .. 32h+31 in cube order). In LDS a
-// chunk of one tensor (D channels) is a row tile: 32 token rows of U = D/8
-// 16-byte units; row kappa is token (t', y', x') = (2h + kappa/16,
-// (kappa/4)%4, kappa%4), and its logical unit u (channels 8u .. 8u+7) sits at
-// unit u ^ kswz(kappa), so 16 consecutive rows read at one logical unit hit 16
+// A chunk is tokens 32h .. 32h+31 of a cube in cube order (a cube of Bt
+// tokens has Bt/32 chunks). In LDS a chunk of one tensor (D channels) is a
+// row tile: 32 token rows of U = D/8 16-byte units; row kappa is in-cube token
+// 32h + kappa, and its logical unit u (channels 8u .. 8u+7) sits at unit
+// u ^ kswz(kappa), so 16 consecutive rows read at one logical unit hit 16
 // distinct bank groups. It is loaded from the raster tensor, read directly as
 // the A operand of a 32x32x16 MFMA (rows = tokens, k = channels) and, by LDS
 // transpose reads, as the A operand with k = tokens (rows = channels).
@@ -52,25 +52,27 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Per-lane byte offsets (within a chunk) of wave wv's half of a row tile's
-// loads: load t of the wave is unit p = (wv*RINS/2 + t)*64 + lane.
-template <int D> __device__ __forceinline__ void row_tile_offsets(const Grid& g, int wv, int lane,
-                                                                   uint32_t* off) {
+// Per-lane byte offsets (within a chunk) of wave wv's share of a row tile's
+// loads when NW waves share them: load t of the wave is unit
+// p = (wv*RINS/NW + t)*64 + lane.
+template <int D, int NW> __device__ __forceinline__ void row_tile_offsets(const Grid& g, int wv, int lane,
+                                                                          uint32_t* off) {
   using G = ChunkGeom<D>;
+  static_assert(G::RINS % NW == 0, "every wave issues whole 1 KB loads");
 #pragma unroll
-  for (int t = 0; t < G::RINS / 2; ++t) {
-    const int p = (wv * (G::RINS / 2) + t) * 64 + lane, kappa = p / G::U;
+  for (int t = 0; t < G::RINS / NW; ++t) {
+    const int p = (wv * (G::RINS / NW) + t) * 64 + lane, kappa = p / G::U;
     const int u = (p % G::U) ^ kswz<G::U>(kappa);
     off[t] = (uint32_t)(chunk_row(g, kappa) * D + u * 8) * 2u;
   }
 }
-// Issue wave wv's half of a row tile: src = first row of the chunk (token
-// (2h, 0, 0) of the cube), dst = LDS byte address of the tile.
-template <int D> __device__ __forceinline__ void issue_row_tile(const void* src, const uint32_t* off, uint32_t dst,
-                                                                int wv) {
+// Issue wave wv's share of a row tile: src = first row of the chunk, dst =
+// LDS byte address of the tile.
+template <int D, int NW> __device__ __forceinline__ void issue_row_tile(const void* src, const uint32_t* off,
+                                                                       uint32_t dst, int wv) {
   using G = ChunkGeom<D>;
 #pragma unroll
-  for (int t = 0; t < G::RINS / 2; ++t) dma16(src, off[t], dst + (wv * (G::RINS / 2) + t) * 1024);
+  for (int t = 0; t < G::RINS / NW; ++t) dma16(src, off[t], dst + (wv * (G::RINS / NW) + t) * 1024);
 }
 // A operand fragment of a row tile (rows = tokens, k-step ks over channels).
 template <int D> __device__ __forceinline__ bf16x8 row_frag(const bf16* tile, int n32, int hf, int ks) {

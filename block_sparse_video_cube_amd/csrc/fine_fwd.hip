@@ -7,9 +7,10 @@
 // mask unselected, softmax, times V; combine, untile); VSA reading notes,
 // key designs 2-3. Variable-length lists per query cube: VSA2 abstract.
 //
-// bf16 kernel: a workgroup of two waves owns one query cube; wave w owns the
-// queries 32w .. 32w+31 and walks the cube's list of key cubes in 32-key
-// chunks with an online softmax (32x32x16 bf16 MFMAs):
+// bf16 kernel: a workgroup of NW = Bt/32 waves owns one query cube of Bt
+// tokens (two waves for the default 64-token cube); wave w owns the queries
+// 32w .. 32w+31 and walks the cube's list of key cubes in 32-key chunks with
+// an online softmax (32x32x16 bf16 MFMAs):
 //   S^T = K_chunk Q^T    A = the chunk's K row tile (LDS), B = the lane's Q
 //                        row (registers, loaded once);
 //   the accumulator gives every lane one query column and 16 of the 32 keys,
@@ -17,8 +18,8 @@
 //   lane halves, and P^T is already the B operand of
 //   O^T += V_chunk^T P^T  A = the chunk's V row tile read transposed (LDS
 //                        transpose reads, in the accumulator's row order).
-// Chunks go to LDS with direct-to-LDS loads, each wave issuing half, several
-// chunks ahead. Every lane ends with O^T for its query column, so the 1/l
+// Chunks go to LDS with direct-to-LDS loads, each wave issuing 1/NW of them,
+// several chunks ahead, and all NW waves read them. Every lane ends with O^T for its query column, so the 1/l
 // normalisation, LSE and the fused gate epilogue need no data exchange.
 #include <type_traits>
 
@@ -27,11 +28,11 @@
 
 namespace vsa {
 
-// bf16 kernel geometry. A workgroup of two waves owns one query cube; wave
+// bf16 kernel geometry. A workgroup of NW waves owns one query cube; wave
 // w owns the 32 queries 32w .. 32w+31 (one MFMA column block). The cube's
-// list is walked in 32-key chunks (two per key cube); each chunk's K rows and
-// V tile go to LDS once (direct-to-LDS loads, half issued by each wave) and
-// both waves read them. MFMAs are 32x32x16.
+// list is walked in 32-key chunks (NW per key cube); each chunk's K and V
+// rows go to LDS once (direct-to-LDS loads, 1/NW issued by each wave) and
+// all waves read them. MFMAs are 32x32x16.
 template <int D> struct FineCfg {
   static constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
   static constexpr int MB = D / 32;          // 32-channel blocks of O^T
@@ -83,8 +84,8 @@ __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__
   for (int e = threadIdx.x; e < Nc; e += 1024) order[bh * Nc + e] = (int32_t)(key[e] & 0xffffffffu);
 }
 
-template <int D, bool FUSED>
-__global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
+template <int D, int NW, bool FUSED>
+__global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
     bf16* __restrict__ o_f, float* __restrict__ lse_f, const float* __restrict__ oc, const bf16* __restrict__ gc,
@@ -108,8 +109,8 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   const int32_t* list = idx + (long)item * stride;
   auto cube_at = [&](int t) { const int j = list[t]; return (j >= 0 && j < g.Nc) ? j : 0; };
 
-  // This lane's query: q = 32wv + n32, token (t' = 2wv + n32/16, y' = (n32/4)%4, x' = n32%4).
-  const int qrow = cube_row(g, i, 2 * wv + (n32 >> 4), (n32 >> 2) & 3) + (n32 & 3);
+  // This lane's query: in-cube token 32wv + n32.
+  const int qrow = cube_token(g, i, 32 * wv + n32);
   // B operand of S^T = K Q^T: lane holds Q[q][16ks + 8hf .. +8].
   bf16x8 qf[C::KS];
 #pragma unroll
@@ -123,49 +124,49 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
   float m = 0.f, lsum = 0.f;
 
-  // Loads of chunk c = key cube list[c/2], half c%2 (tokens 32h .. 32h+31):
-  // this wave issues half of the K rows and half of the V rows, both into
-  // row tiles. Per-lane byte offsets are fixed for the whole list: unit p =
-  // ins*64 + lane is key row kappa = p / U, logical unit (p % U) ^
-  // kswz(kappa), i.e. token (t', y', x') = (2h + kappa/16, (kappa/4)%4,
-  // kappa%4) of the cube.
+  // Loads of chunk c = key cube list[c/NW], chunk h = c%NW of it (tokens
+  // 32h .. 32h+31): this wave issues 1/NW of the K rows and of the V rows,
+  // both into row tiles. Per-lane byte offsets are fixed for the whole list:
+  // unit p = ins*64 + lane is key row kappa = p / U, logical unit (p % U) ^
+  // kswz(kappa), i.e. in-cube token 32h + kappa.
+  constexpr int KPW = C::KINS / NW;   // loads per wave per K (or V) chunk
   const uint32_t kbase = lds_addr(kbuf), vbase = lds_addr(vbuf);
-  uint32_t koff[C::KINS / 2];
-  row_tile_offsets<D>(g, wv, lane, koff);
+  uint32_t koff[KPW];
+  row_tile_offsets<D, NW>(g, wv, lane, koff);
   // Byte offsets of the list's cubes, 64 entries at a time, one per lane:
-  // kcube = first key row of the cube within this head's K, vcube = the
-  // cube's V chunk tiles. A load reads them with readlane, so the per-chunk
-  // address work is scalar and division-free. The block of entries is
-  // refreshed when chunk c = 128 * n is loaded; K runs ahead of V, so V
-  // keeps its own copy.
-  const uint32_t khalf = (uint32_t)(half_rows(g) * D) * 2u;   // t' -> t' + 2
+  // kcube = first key row of the cube within this head's K (and V). A load
+  // reads it with readlane, so the per-chunk address work is scalar and
+  // division-free. The block of entries is refreshed when the first chunk of
+  // entry 64 * n is loaded; K runs ahead of V, so V keeps its own copy.
   const bf16* V = v + tok0 * D;
   uint32_t kcube = 0, vcube = 0;
   auto cubes_k = [&](int t0) {
     const int t = t0 + lane;
-    kcube = (uint32_t)cube_row(g, t < L ? cube_at(t) : 0, 0, 0) * (uint32_t)(D * 2);
+    kcube = (uint32_t)cube_first(g, t < L ? cube_at(t) : 0) * (uint32_t)(D * 2);
   };
   auto cubes_v = [&](int t0) {
     const int t = t0 + lane;
-    vcube = (uint32_t)cube_row(g, t < L ? cube_at(t) : 0, 0, 0) * (uint32_t)(D * 2);
+    vcube = (uint32_t)cube_first(g, t < L ? cube_at(t) : 0) * (uint32_t)(D * 2);
   };
+  // Bytes from a cube's first row to the first row of its chunk h.
+  auto chunk_bytes = [&](int h) { return NW == 1 ? 0u : (uint32_t)(chunk_first(g, h) * D) * 2u; };
   auto issue_k = [&](int c) {
-    const int e = c >> 1, h = c & 1;
+    const int e = c / NW, h = c % NW;
     if ((e & 63) == 0 && h == 0) cubes_k(e);
     const uint32_t dst = kbase + (c % C::KST) * (C::KUNITS * 16);
     const uint32_t kc = __builtin_amdgcn_readlane(kcube, e & 63);
-    const void* src = uniform_ptr(reinterpret_cast<const char*>(K) + kc + (h ? khalf : 0u));
+    const void* src = uniform_ptr(reinterpret_cast<const char*>(K) + kc + chunk_bytes(h));
 #pragma unroll
-    for (int t = 0; t < C::KINS / 2; ++t) dma16(src, koff[t], dst + (wv * (C::KINS / 2) + t) * 1024);
+    for (int t = 0; t < KPW; ++t) dma16(src, koff[t], dst + (wv * KPW + t) * 1024);
   };
   auto issue_v = [&](int c) {
-    const int e = c >> 1, h = c & 1;
+    const int e = c / NW, h = c % NW;
     if ((e & 63) == 0 && h == 0) cubes_v(e);
     const uint32_t dst = vbase + (c % C::VST) * (C::VUNITS * 16);
     const uint32_t vc = __builtin_amdgcn_readlane(vcube, e & 63);
-    const void* src = uniform_ptr(reinterpret_cast<const char*>(V) + vc + (h ? khalf : 0u));
+    const void* src = uniform_ptr(reinterpret_cast<const char*>(V) + vc + chunk_bytes(h));
 #pragma unroll
-    for (int t = 0; t < C::KINS / 2; ++t) dma16(src, koff[t], dst + (wv * (C::KINS / 2) + t) * 1024);
+    for (int t = 0; t < KPW; ++t) dma16(src, koff[t], dst + (wv * KPW + t) * 1024);
   };
   // S^T (32 keys x 32 queries) of the K chunk at kb: lane holds, at
   // accumulator index jj, key 8*(jj/4) + 4hf + jj%4 of the lane's query.
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   // At its top it needs K of c + 1 and V of c; loads retire in order, so only
   // the K loads issued in iteration c - 1 may stay in flight. Each wave waits
   // for its own loads, then a barrier (a bare s_barrier: a fenced one would
-  // also wait for the loads in flight) makes both halves visible and frees
+  // also wait for the loads in flight) makes every wave's share visible and frees
   // the stages about to be refilled (K of c, V of c - 1, read in c - 1).
   //
   // Online softmax against a lazily moved reference max m (log2 units): P =
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   // m starts at the row max of chunk 0). O and l always share m, so the
   // result is exact whatever the schedule.
   constexpr float kHeadroom = 16.0f;
-  const int nch = 2 * L;
+  const int nch = NW * L;
   f32x16 sxa, sxb;
   if (nch > 0) {
     issue_k(0);
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
   auto step = [&](auto P, f32x16& sx, f32x16& sn, int c) {
     constexpr int p = decltype(P)::value;
     if (c > 0) {
-      if (c - 1 + C::KST < nch) wait_vmcnt<C::KINS / 2>();
+      if (c - 1 + C::KST < nch) wait_vmcnt<KPW>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
     }
@@ -360,17 +361,19 @@ __global__ __launch_bounds__(128, 2) void fine_fwd_bf16_kernel(
     }
 }
 
-// fp32 path: one thread per query token, K/V tiles staged in LDS. Used for
-// fp32 problems (small, correctness-first shapes).
+// fp32 path: one thread per query token (a workgroup of Bt threads per query
+// cube), K/V rows staged in LDS 32 at a time. Used for fp32 problems (small,
+// correctness-first shapes).
 template <int D, bool FUSED>
-__global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
+__global__ __launch_bounds__(128) void fine_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, float* __restrict__ o_f,
     float* __restrict__ lse_f, const float* __restrict__ oc, const float* __restrict__ gc,
     const float* __restrict__ gf, float* __restrict__ o, Grid g, int stride, float scale) {
-  __shared__ float ks[kTile][D];
-  __shared__ float vs[kTile][D];
-  const int tid = threadIdx.x;
+  constexpr int R = 32;   // key rows per LDS stage
+  __shared__ float ks[R][D];
+  __shared__ float vs[R][D];
+  const int tid = threadIdx.x, nt = blockDim.x;
   const int item = blockIdx.x;
   const int bh = item / g.Nc, i = item - bh * g.Nc;
   const long tok0 = (long)bh * g.N;
@@ -381,18 +384,18 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
   float m = -INFINITY, l = 0.f;
   const int L = min(max(len[item], 0), stride);
   const int32_t* list = idx + (long)item * stride;
-  for (int t = 0; t < L; ++t) {
-    const int j = list[t];
+  for (int t = 0; t < L * (g.B / R); ++t) {
+    const int j = list[t / (g.B / R)], r0 = (t % (g.B / R)) * R;
     if (j < 0 || j >= g.Nc) continue;
     __syncthreads();
-    for (int e = tid; e < kTile * D; e += 64) {
+    for (int e = tid; e < R * D; e += nt) {
       const int r = e / D, d = e - r * D;
-      const long src = (tok0 + cube_token(g, j, r)) * D + d;
+      const long src = (tok0 + cube_token(g, j, r0 + r)) * D + d;
       ks[r][d] = k[src];
       vs[r][d] = v[src];
     }
     __syncthreads();
-    for (int r = 0; r < kTile; ++r) {
+    for (int r = 0; r < R; ++r) {
       float z = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) z = fmaf(qv[d], ks[r][d], z);
@@ -419,14 +422,24 @@ __global__ __launch_bounds__(64) void fine_fwd_f32_kernel(
   }
 }
 
+template <int D, int NW, bool FUSED>
+static void fine_launch_bf16_nw(const Launch& L, const void* q, const void* k, const void* v, const int32_t* idx,
+                                const int32_t* len, const int32_t* order, void* o_f, float* lse_f, const float* oc,
+                                const void* gc, const void* gf, void* o) {
+  const int nitems = L.BH * L.g.Nc;
+  hipLaunchKernelGGL((fine_fwd_bf16_kernel<D, NW, FUSED>), dim3(nitems), dim3(64 * NW), 0, L.stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, idx, len, order, (bf16*)o_f, lse_f, oc,
+                     (const bf16*)gc, (const bf16*)gf, (bf16*)o, L.g, L.stride, L.scale * kLog2e);
+}
+
+// Waves per workgroup = cube tokens / 32 (32, 64 or 128 tokens).
 template <int D, bool FUSED>
 static void fine_launch_bf16(const Launch& L, const void* q, const void* k, const void* v, const int32_t* idx,
                              const int32_t* len, const int32_t* order, void* o_f, float* lse_f, const float* oc, const void* gc,
                              const void* gf, void* o) {
-  const int nitems = L.BH * L.g.Nc;
-  hipLaunchKernelGGL((fine_fwd_bf16_kernel<D, FUSED>), dim3(nitems), dim3(128), 0, L.stream, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, idx, len, order, (bf16*)o_f, lse_f, oc, (const bf16*)gc, (const bf16*)gf,
-                     (bf16*)o, L.g, L.stride, L.scale * kLog2e);
+  if (L.g.B == 32) fine_launch_bf16_nw<D, 1, FUSED>(L, q, k, v, idx, len, order, o_f, lse_f, oc, gc, gf, o);
+  else if (L.g.B == 128) fine_launch_bf16_nw<D, 4, FUSED>(L, q, k, v, idx, len, order, o_f, lse_f, oc, gc, gf, o);
+  else fine_launch_bf16_nw<D, 2, FUSED>(L, q, k, v, idx, len, order, o_f, lse_f, oc, gc, gf, o);
 }
 
 template <int D, bool FUSED>
@@ -434,7 +447,7 @@ static void fine_launch_f32(const Launch& L, const void* q, const void* k, const
                             const int32_t* len, void* o_f, float* lse_f, const float* oc, const void* gc,
                             const void* gf, void* o) {
   const int nitems = L.BH * L.g.Nc;
-  hipLaunchKernelGGL((fine_fwd_f32_kernel<D, FUSED>), dim3(nitems), dim3(64), 0, L.stream, (const float*)q,
+  hipLaunchKernelGGL((fine_fwd_f32_kernel<D, FUSED>), dim3(nitems), dim3(L.g.B), 0, L.stream, (const float*)q,
                      (const float*)k, (const float*)v, idx, len, (float*)o_f, lse_f, oc, (const float*)gc,
                      (const float*)gf, (float*)o, L.g, L.stride, L.scale);
 }

@@ -17,7 +17,7 @@
 
 namespace vsa {
 
-// One workgroup per (b, h, cube): the cube's 64 token rows move between
+// One workgroup per (b, h, cube): the cube's Bt token rows move between
 // raster and cube-major order.
 template <typename T>
 __global__ __launch_bounds__(256) void relayout_kernel(const T* __restrict__ src, T* __restrict__ dst, Grid g,
@@ -27,10 +27,10 @@ __global__ __launch_bounds__(256) void relayout_kernel(const T* __restrict__ src
   Grid r = g;
   r.tiled = 0;
   const int units = D * (int)sizeof(T) / 16;   // 16-byte units per token row
-  for (int w = threadIdx.x; w < kTile * units; w += 256) {
+  for (int w = threadIdx.x; w < g.B * units; w += 256) {
     const int l = w / units, u = w - l * units;
     const long ras = bh * g.N + cube_token(r, c, l);
-    const long til = bh * g.N + (long)c * kTile + l;
+    const long til = bh * g.N + (long)c * g.B + l;
     const long from = to_tiled ? ras : til, to = to_tiled ? til : ras;
     reinterpret_cast<uint4*>(dst + to * D)[u] = reinterpret_cast<const uint4*>(src + from * D)[u];
   }
@@ -50,8 +50,9 @@ hipError_t launch_relayout(const Launch& L, const void* src, void* dst, bool to_
 // Index, in the problem's token order, of raster token (t, y, x).
 __device__ __forceinline__ long token_index(const Grid& g, int t, int y, int x) {
   if (!g.tiled) return ((long)t * g.H + y) * g.W + x;
-  const int c = ((t >> 2) * g.H4 + (y >> 2)) * g.W4 + (x >> 2);
-  return (long)c * kTile + 16 * (t & 3) + 4 * (y & 3) + (x & 3);
+  const int c = ((t >> g.lct) * g.Hn + (y >> g.lch)) * g.Wn + (x >> g.lcw);
+  const int ct = t & ((1 << g.lct) - 1), cy = y & ((1 << g.lch) - 1), cx = x & ((1 << g.lcw) - 1);
+  return (long)c * g.B + (((ct << g.lch) | cy) << g.lcw | cx);
 }
 
 // Crop (to_small = 1): small[b, h, t, y, x] = big[b, h, token (t, y, x)] for
@@ -77,10 +78,10 @@ __global__ __launch_bounds__(256) void crop_pad_kernel(const uint4* __restrict__
       const int n = (int)(row - bh * g.N);
       int t, y, x;
       if (g.tiled) {
-        const int c = n / kTile, l = n % kTile;
-        x = 4 * (c % g.W4) + (l & 3);
-        y = 4 * ((c / g.W4) % g.H4) + ((l >> 2) & 3);
-        t = 4 * (c / (g.W4 * g.H4)) + (l >> 4);
+        const int c = n / g.B, l = n % g.B;
+        x = ((c % g.Wn) << g.lcw) + (l & ((1 << g.lcw) - 1));
+        y = (((c / g.Wn) % g.Hn) << g.lch) + ((l >> g.lcw) & ((1 << g.lch) - 1));
+        t = ((c / (g.Wn * g.Hn)) << g.lct) + (l >> (g.lch + g.lcw));
       } else {
         x = n % g.W;
         y = (n / g.W) % g.H;

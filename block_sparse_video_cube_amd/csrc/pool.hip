@@ -14,14 +14,14 @@
 
 namespace vsa {
 
-template <typename T, int D, bool MAX>
+template <typename T, int D, bool MAX, int BT>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, float* __restrict__ qc,
                                                    float* __restrict__ kc, float* __restrict__ vc,
                                                    uint8_t* __restrict__ args, Grid g) {
   constexpr int CH = D / 8;            // 8-channel chunks per token row
   constexpr int RPP = 256 / CH;        // token rows per pass
-  constexpr int PASSES = kTile / RPP;
+  constexpr int PASSES = BT / RPP;     // BT = tokens per cube
   __shared__ float part[RPP][D + 4];
   __shared__ uint8_t parg[MAX ? RPP : 1][D + 4];
 
@@ -77,23 +77,31 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
         float s = 0.f;
 #pragma unroll
         for (int r = 0; r < RPP; ++r) s += part[r][tid];
-        if (dsts[which] != nullptr) dsts[which][(bh * g.Nc + c) * D + tid] = s * (1.0f / kTile);
+        if (dsts[which] != nullptr) dsts[which][(bh * g.Nc + c) * D + tid] = s * (1.0f / BT);
       }
     }
     __syncthreads();
   }
 }
 
+template <typename T, bool MAX, int BT>
+static void pool_launch_bt(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
+                           float* vc, uint8_t* args) {
+  const dim3 grid(L.g.Nc, L.BH), block(256);
+  if (L.D == 64)
+    hipLaunchKernelGGL((pool_kernel<T, 64, MAX, BT>), grid, block, 0, L.stream, (const T*)q, (const T*)k,
+                       (const T*)v, qc, kc, vc, args, L.g);
+  else
+    hipLaunchKernelGGL((pool_kernel<T, 128, MAX, BT>), grid, block, 0, L.stream, (const T*)q, (const T*)k,
+                       (const T*)v, qc, kc, vc, args, L.g);
+}
+
 template <typename T, bool MAX>
 static void pool_launch(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
                         float* vc, uint8_t* args) {
-  const dim3 grid(L.g.Nc, L.BH), block(256);
-  if (L.D == 64)
-    hipLaunchKernelGGL((pool_kernel<T, 64, MAX>), grid, block, 0, L.stream, (const T*)q, (const T*)k, (const T*)v,
-                       qc, kc, vc, args, L.g);
-  else
-    hipLaunchKernelGGL((pool_kernel<T, 128, MAX>), grid, block, 0, L.stream, (const T*)q, (const T*)k,
-                       (const T*)v, qc, kc, vc, args, L.g);
+  if (L.g.B == 32) pool_launch_bt<T, MAX, 32>(L, q, k, v, qc, kc, vc, args);
+  else if (L.g.B == 128) pool_launch_bt<T, MAX, 128>(L, q, k, v, qc, kc, vc, args);
+  else pool_launch_bt<T, MAX, 64>(L, q, k, v, qc, kc, vc, args);
 }
 
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,

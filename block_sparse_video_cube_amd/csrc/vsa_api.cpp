@@ -18,17 +18,24 @@ struct Dims {
   size_t elem;  // bytes per raster element
 };
 
+// A cube side: a power of two in [1, 128].
+inline bool pow2_side(int v) { return v > 0 && v <= 128 && (v & (v - 1)) == 0; }
+
 // Host-side validation of the problem; fills the launch context.
 vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
   if (p == nullptr) return VSA_ERR_NULL;
   if (p->B < 1 || p->heads < 1) return VSA_ERR_SHAPE;
-  if (p->T < 4 || p->H < 4 || p->W < 4 || (p->T & 3) || (p->H & 3) || (p->W & 3)) return VSA_ERR_SHAPE;
+  const int ct = p->cube_t ? p->cube_t : 4, ch = p->cube_h ? p->cube_h : 4, cw = p->cube_w ? p->cube_w : 4;
+  if (!pow2_side(ct) || !pow2_side(ch) || !pow2_side(cw) || cw < 4) return VSA_ERR_SHAPE;
+  if (p->T < ct || p->H < ch || p->W < cw || p->T % ct || p->H % ch || p->W % cw) return VSA_ERR_SHAPE;
+  const long Bt = (long)ct * ch * cw;
+  if (Bt != 32 && Bt != 64 && Bt != 128) return VSA_ERR_UNSUPPORTED;
   const long N = (long)p->T * p->H * p->W;
   const long BH = (long)p->B * p->heads;
   if (N > (1L << 30) || BH > (1L << 24)) return VSA_ERR_SHAPE;
   if (p->head_dim != 64 && p->head_dim != 128) return VSA_ERR_HEAD_DIM;
   if (p->dtype != VSA_F32 && p->dtype != VSA_BF16) return VSA_ERR_DTYPE;
-  const long Nc = N / 64;
+  const long Nc = N / Bt;
   if (BH * Nc > 0x7fffffffL) return VSA_ERR_SHAPE;
   if (BH * N * p->head_dim > (1L << 40)) return VSA_ERR_SHAPE;
   if (!std::isfinite(p->scale) || p->scale < 0.f) return VSA_ERR_SCALE;
@@ -40,7 +47,7 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
   if (p->pool_mode != VSA_POOL_MEAN && p->pool_mode != VSA_POOL_MAX) return VSA_ERR_UNSUPPORTED;
   if (p->layout != VSA_LAYOUT_RASTER && p->layout != VSA_LAYOUT_TILED) return VSA_ERR_UNSUPPORTED;
   if (L != nullptr) {
-    L->g = make_grid(p->T, p->H, p->W, p->layout == VSA_LAYOUT_TILED ? 1 : 0);
+    L->g = make_grid(p->T, p->H, p->W, p->layout == VSA_LAYOUT_TILED ? 1 : 0, ct, ch, cw);
     L->BH = (int)BH;
     L->D = p->head_dim;
     L->bf16 = p->dtype == VSA_BF16;
@@ -437,13 +444,20 @@ vsa_status vsa_untile(const vsa_problem* p, const void* xt, void* x, void* strea
   return relayout(p, xt, x, false, stream);
 }
 
-vsa_status vsa_compatible_latent(int32_t T, int32_t H, int32_t W, int32_t* Tc, int32_t* Hc, int32_t* Wc) {
+vsa_status vsa_compatible_latent(int32_t T, int32_t H, int32_t W, int32_t ct, int32_t ch, int32_t cw, int32_t* Tc,
+                                 int32_t* Hc, int32_t* Wc) {
   if (Tc == nullptr || Hc == nullptr || Wc == nullptr) return VSA_ERR_NULL;
-  const int32_t lim = 0x7fffffff - 3;
-  if (T <= 0 || H <= 0 || W <= 0 || T > lim || H > lim || W > lim) return VSA_ERR_SHAPE;
-  *Tc = (T + 3) / 4 * 4;
-  *Hc = (H + 3) / 4 * 4;
-  *Wc = (W + 3) / 4 * 4;
+  const int32_t side[3] = {ct ? ct : 4, ch ? ch : 4, cw ? cw : 4}, n[3] = {T, H, W};
+  int32_t out[3];
+  for (int a = 0; a < 3; ++a) {
+    if (!pow2_side(side[a]) || n[a] <= 0) return VSA_ERR_SHAPE;
+    const long r = ((long)n[a] + side[a] - 1) / side[a] * side[a];
+    if (r > 0x7fffffffL) return VSA_ERR_SHAPE;
+    out[a] = (int32_t)r;
+  }
+  *Tc = out[0];
+  *Hc = out[1];
+  *Wc = out[2];
   return VSA_OK;
 }
 

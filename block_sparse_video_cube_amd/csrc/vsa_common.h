@@ -2,13 +2,19 @@
 //
 // Layout facts used by every kernel:
 //  * Token tensors are [B, heads, T, H, W, D] (raster order) or, with the
-//    tiled layout, [B, heads, Nc, 64, D] (cube-major); D fastest. Kernels
-//    address tokens only through cube_token / cube_row / token_cube /
-//    chunk_row, which know the order.
-//  * Cube c of a (T, H, W) latent has origin (4*tc, 4*yc, 4*xc) with
-//    c = (tc * H4 + yc) * W4 + xc (row-major cube order); token l of a cube
-//    (0..63) is (t', y', x') = (l / 16, (l / 4) % 4, l % 4). Within a cube the
-//    four tokens x' = 0..3 are contiguous in raster memory (4*D elements).
+//    tiled layout, [B, heads, Nc, Bt, D] (cube-major, Bt tokens per cube);
+//    D fastest. Kernels address tokens only through cube_first / cube_rel /
+//    cube_token / token_cube / chunk_row, which know the order.
+//  * Cubes are (Ct, Ch, Cw) blocks of Bt = Ct*Ch*Cw tokens (every side a
+//    power of two; (4, 4, 4) and 64 tokens by default). Cube c of a (T, H, W)
+//    latent has origin (Ct*tc, Ch*yc, Cw*xc) with c = (tc * Hn + yc) * Wn + xc
+//    (row-major cube order); token l of a cube is (t', y', x') =
+//    (l / (Ch*Cw), (l / Cw) % Ch, l % Cw). Within a cube the Cw tokens of a
+//    row are contiguous in raster memory.
+//  * A chunk is 32 consecutive tokens of a cube (l = 32h .. 32h + 31); the
+//    offset of its token kappa from its first token does not depend on h or
+//    on the cube, because 32 and Ch*Cw are powers of two (one divides the
+//    other) and Cw divides 32 or 32 divides Cw.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,66 +27,72 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 64;   // tokens per (4,4,4) cube
+constexpr int kTile = 64;   // tokens per default (4,4,4) cube
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct Grid {
   int T, H, W;       // latent
-  int H4, W4;        // cube grid (T4 implied)
+  int lct, lch, lcw; // log2 of the cube sides (Ct, Ch, Cw)
+  int B;             // tokens per cube, Ct * Ch * Cw
+  int Hn, Wn;        // cubes along H and along W (T / Ct along T)
   int N, Nc;         // tokens, cubes
-  int tiled;         // token order: 0 = raster (t, y, x); 1 = cube-major (token l of cube c at 64c + l)
+  int tiled;         // token order: 0 = raster (t, y, x); 1 = cube-major (token l of cube c at B*c + l)
 };
 
-__host__ __device__ inline Grid make_grid(int T, int H, int W, int tiled = 0) {
+__host__ __device__ inline int ilog2(int v) {
+  int r = 0;
+  while ((1 << (r + 1)) <= v) ++r;
+  return r;
+}
+
+// Cube sides must be powers of two dividing T, H, W (checked on the host).
+__host__ __device__ inline Grid make_grid(int T, int H, int W, int tiled = 0, int ct = 4, int ch = 4, int cw = 4) {
   Grid g;
   g.T = T; g.H = H; g.W = W;
-  g.H4 = H / 4; g.W4 = W / 4;
-  g.N = T * H * W; g.Nc = g.N / kTile;
+  g.lct = ilog2(ct); g.lch = ilog2(ch); g.lcw = ilog2(cw);
+  g.B = ct * ch * cw;
+  g.Hn = H / ch; g.Wn = W / cw;
+  g.N = T * H * W; g.Nc = g.N / g.B;
   g.tiled = tiled;
   return g;
 }
 
-// Index (row) of token l (0..63) of cube c in the problem's token order.
-__device__ __forceinline__ int cube_token(const Grid& g, int c, int l) {
-  if (g.tiled) return c * kTile + l;
-  const int xc = c % g.W4;
-  const int r = c / g.W4;
-  const int yc = r % g.H4;
-  const int tc = r / g.H4;
-  const int t = 4 * tc + (l >> 4), y = 4 * yc + ((l >> 2) & 3), x = 4 * xc + (l & 3);
+// Index (row) of token 0 of cube c in the problem's token order.
+__host__ __device__ __forceinline__ int cube_first(const Grid& g, int c) {
+  if (g.tiled) return c * g.B;
+  const int xc = c % g.Wn;
+  const int r = c / g.Wn;
+  const int yc = r % g.Hn;
+  const int tc = r / g.Hn;
+  return ((tc << g.lct) * g.H + (yc << g.lch)) * g.W + (xc << g.lcw);
+}
+
+// Rows between in-cube token l and token 0 of the same cube (any cube).
+__host__ __device__ __forceinline__ int cube_rel(const Grid& g, int l) {
+  if (g.tiled) return l;
+  const int t = l >> (g.lch + g.lcw), y = (l >> g.lcw) & ((1 << g.lch) - 1), x = l & ((1 << g.lcw) - 1);
   return (t * g.H + y) * g.W + x;
 }
 
-// Index of the first token of row (t', y') of cube c; the row's four tokens
-// x' = 0..3 follow contiguously in either token order.
-__device__ __forceinline__ int cube_row(const Grid& g, int c, int tl, int yl) {
-  if (g.tiled) return c * kTile + 16 * tl + 4 * yl;
-  const int xc = c % g.W4;
-  const int r = c / g.W4;
-  const int yc = r % g.H4;
-  const int tc = r / g.H4;
-  return ((4 * tc + tl) * g.H + 4 * yc + yl) * g.W + 4 * xc;
-}
+// Index of token l of cube c in the problem's token order.
+__host__ __device__ __forceinline__ int cube_token(const Grid& g, int c, int l) { return cube_first(g, c) + cube_rel(g, l); }
 
 // Cube of the token at index n.
 __device__ __forceinline__ int token_cube(const Grid& g, int n) {
-  if (g.tiled) return n / kTile;
+  if (g.tiled) return n / g.B;
   const int x = n % g.W;
   const int r = n / g.W;
   const int y = r % g.H;
   const int t = r / g.H;
-  return ((t >> 2) * g.H4 + (y >> 2)) * g.W4 + (x >> 2);
+  return ((t >> g.lct) * g.Hn + (y >> g.lch)) * g.Wn + (x >> g.lcw);
 }
 
-// Rows between token (t', y', x') of a chunk (half h: t' = 2h, 2h + 1) and
-// its first token (2h, 0, 0): kappa = 16(t' - 2h) + 4y' + x' is the token's
-// position in the chunk. And rows between the first tokens of the two halves.
-__host__ __device__ __forceinline__ int chunk_row(const Grid& g, int kappa) {
-  if (g.tiled) return kappa;
-  return ((kappa >> 4) * g.H + ((kappa >> 2) & 3)) * g.W + (kappa & 3);
-}
-__host__ __device__ __forceinline__ int half_rows(const Grid& g) { return g.tiled ? 32 : 2 * g.H * g.W; }
+// Rows between token kappa (0..31) of a chunk and the chunk's first token:
+// the same for every chunk of every cube (see the layout facts above).
+__host__ __device__ __forceinline__ int chunk_row(const Grid& g, int kappa) { return cube_rel(g, kappa); }
+// Rows between the first token of chunk h of a cube and the cube's first token.
+__host__ __device__ __forceinline__ int chunk_first(const Grid& g, int h) { return cube_rel(g, 32 * h); }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2). Map block b so that every XCD gets one contiguous range of work items:

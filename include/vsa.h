@@ -5,7 +5,8 @@
  * The operator (VSA summary page, paperlayer.ai arXiv 2505.13389, section 2
  * "Methods" and Appendix B "Pseudocode of VSA"; VSA reading notes, key
  * designs 1-3):
- *   1. partition the T x H x W latent into (4,4,4) cubes, one 64-token tile each;
+ *   1. partition the T x H x W latent into (Ct, Ch, Cw) cubes ((4, 4, 4) by
+ *      default), one tile of Bt = Ct*Ch*Cw tokens each (64 by default);
  *   2. mean-pool Q, K, V per cube and run dense attention over the cubes,
  *      giving A_c and O_c;
  *   3. keep the top-K key cubes of every row of A_c (or take caller-supplied
@@ -20,7 +21,7 @@
  * - Float tensors are [B, heads, T, H, W, head_dim] contiguous (raster token
  *   order, head_dim fastest) in the problem's dtype (fp32 or bf16), unless the
  *   argument says otherwise. Pooled tensors ("_c") are fp32 [B, heads, Nc,
- *   head_dim], cubes in row-major order over (T/4, H/4, W/4); Nc = T*H*W/64.
+ *   head_dim], cubes in row-major order over (T/Ct, H/Ch, W/Cw); Nc = T*H*W/Bt.
  *   Per-token scalars (LSE_f, delta) are fp32 [B, heads, T, H, W].
  * - Index lists: idx is int32 [B, heads, Nc, list_stride], len int32
  *   [B, heads, Nc]. Row i holds len[i] strictly increasing key-cube ids in
@@ -50,16 +51,19 @@ extern "C" {
 typedef enum {
   VSA_OK = 0,
   VSA_ERR_NULL = 1,        /* a required pointer is NULL                      */
-  VSA_ERR_SHAPE = 2,       /* B/heads < 1, T/H/W not positive multiples of 4,
-                              or a size that overflows                        */
+  VSA_ERR_SHAPE = 2,       /* B/heads < 1, T/H/W not positive multiples of the
+                              cube sides, an invalid cube side, or a size that
+                              overflows                                       */
   VSA_ERR_HEAD_DIM = 3,    /* head_dim not 64 or 128                         */
   VSA_ERR_DTYPE = 4,       /* unknown dtype                                  */
   VSA_ERR_TOPK = 5,        /* topk outside [0, Nc] or list_stride invalid    */
   VSA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned               */
   VSA_ERR_WORKSPACE = 7,   /* workspace / saved buffer smaller than required */
   VSA_ERR_INDEX = 8,       /* an index list failed validation                */
-  VSA_ERR_UNSUPPORTED = 9, /* valid request this build does not implement, an
-                              unknown pool_mode or layout, or in-place tiling */
+  VSA_ERR_UNSUPPORTED = 9, /* valid request this build does not implement (a
+                              cube of other than 32, 64 or 128 tokens, too
+                              many cubes), an unknown pool_mode or layout, or
+                              in-place tiling                                 */
   VSA_ERR_HIP = 10,        /* a HIP call or kernel launch failed             */
   VSA_ERR_SCALE = 11       /* scale is negative, NaN or infinite             */
 } vsa_status;
@@ -74,8 +78,8 @@ typedef enum { VSA_POOL_MEAN = 0, VSA_POOL_MAX = 1 } vsa_pool_mode;
 
 /* Token order of every token tensor of a problem (q, k, v, gates, o, d_o,
  * gradients, O_f, and the per-token fp32 arrays LSE_f / delta). RASTER is
- * [B, heads, T, H, W, ...]; TILED is cube-major [B, heads, Nc, 64, ...] with
- * token l of cube c at position 64c + l, the tiled sequence of the VSA
+ * [B, heads, T, H, W, ...]; TILED is cube-major [B, heads, Nc, Bt, ...] with
+ * token l of cube c at position Bt*c + l, the tiled sequence of the VSA
  * summary page's pseudocode (Appendix B), which tiles before the attention
  * layer and untiles after it, so a model can keep activations tiled across
  * layers (vsa_tile / vsa_untile convert). Index lists and pooled tensors do
@@ -84,7 +88,7 @@ typedef enum { VSA_LAYOUT_RASTER = 0, VSA_LAYOUT_TILED = 1 } vsa_layout;
 
 typedef struct {
   int32_t B, heads;      /* batch and heads; every (b, h) is independent      */
-  int32_t T, H, W;       /* latent grid, each a positive multiple of 4         */
+  int32_t T, H, W;       /* latent grid, multiples of the cube sides           */
   int32_t head_dim;      /* 64 or 128                                          */
   int32_t dtype;         /* vsa_dtype of every float tensor except pooled ones */
   float scale;           /* softmax scale of both stages; 0 => 1/sqrt(head_dim) */
@@ -94,6 +98,15 @@ typedef struct {
                             list_stride >= topk; list mode needs 1..Nc         */
   int32_t pool_mode;     /* vsa_pool_mode; 0 = mean                            */
   int32_t layout;        /* vsa_layout; 0 = raster                             */
+  int32_t cube_t, cube_h, cube_w;
+                         /* cube sides (Ct, Ch, Cw); 0 => 4. The VSA summary
+                            page (section 2 "Methods") names the cube
+                            (Ct, Ch, Cw) with tile size Bt = Ct*Ch*Cw and
+                            weighs tile sizes in its design exploration.
+                            Each side a power of two, Cw >= 4, Bt in
+                            {32, 64, 128}; query and key tiles are both Bt
+                            tokens (Bt x Bt blocks). In-cube token order is
+                            row-major (t', y', x').                           */
 } vsa_problem;
 
 /* Short text for a status code (static storage, never NULL). */
@@ -246,16 +259,18 @@ vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const flo
 vsa_status vsa_tile(const vsa_problem* p, const void* x, void* xt, void* stream);
 vsa_status vsa_untile(const vsa_problem* p, const void* xt, void* x, void* stream);
 
-/* Latents whose sides are not multiples of 4. The VSA summary page
+/* Latents whose sides are not multiples of the cube's. The VSA summary page
  * (paperlayer.ai, arXiv 2505.13389), section 5 "Limitation and Conclusion",
  * notes that (4, 4, 4) cubes need sides divisible by 4 and names the remedy:
  * generate a slightly larger latent and crop the result.
  *
  * vsa_compatible_latent: the smallest grid Tc x Hc x Wc with every side a
- * multiple of 4 that contains T x H x W (each side rounded up). Host only;
- * VSA_ERR_NULL for a NULL output pointer, VSA_ERR_SHAPE for a side <= 0 or
- * one that would overflow int32 when rounded. */
-vsa_status vsa_compatible_latent(int32_t T, int32_t H, int32_t W, int32_t* Tc, int32_t* Hc, int32_t* Wc);
+ * multiple of the matching cube side (ct, ch, cw; 0 => 4) that contains
+ * T x H x W (each side rounded up). Host only; VSA_ERR_NULL for a NULL output
+ * pointer, VSA_ERR_SHAPE for a side <= 0, a cube side that is not a power of
+ * two, or a result that would overflow int32. */
+vsa_status vsa_compatible_latent(int32_t T, int32_t H, int32_t W, int32_t ct, int32_t ch, int32_t cw, int32_t* Tc,
+                                 int32_t* Hc, int32_t* Wc);
 
 /* vsa_crop: out = the leading T x H x W region of x, a token tensor of the
  * (compatible) problem p in p's layout, written in raster order

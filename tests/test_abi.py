@@ -91,13 +91,16 @@ def test_compatible_latent_host():
     lib = N.lib()
     o = [ctypes.c_int32() for _ in range(3)]
     refs = [ctypes.byref(v) for v in o]
-    assert lib.vsa_compatible_latent(9, 13, 30, *refs) == OK
+    assert lib.vsa_compatible_latent(9, 13, 30, 0, 0, 0, *refs) == OK
     assert [v.value for v in o] == [12, 16, 32]
-    assert lib.vsa_compatible_latent(24, 44, 80, *refs) == OK
+    assert lib.vsa_compatible_latent(24, 44, 80, 4, 4, 4, *refs) == OK
     assert [v.value for v in o] == [24, 44, 80]
-    assert lib.vsa_compatible_latent(0, 4, 4, *refs) == SHAPE
-    assert lib.vsa_compatible_latent(2**31 - 1, 4, 4, *refs) == SHAPE
-    assert lib.vsa_compatible_latent(4, 4, 4, None, refs[1], refs[2]) == NULL
+    assert lib.vsa_compatible_latent(9, 13, 30, 2, 8, 8, *refs) == OK
+    assert [v.value for v in o] == [10, 16, 32]
+    assert lib.vsa_compatible_latent(0, 4, 4, 0, 0, 0, *refs) == SHAPE
+    assert lib.vsa_compatible_latent(4, 4, 4, 3, 4, 4, *refs) == SHAPE      # not a power of two
+    assert lib.vsa_compatible_latent(2**31 - 1, 4, 4, 0, 0, 0, *refs) == SHAPE
+    assert lib.vsa_compatible_latent(4, 4, 4, 0, 0, 0, None, refs[1], refs[2]) == NULL
 
 
 def test_crop_pad_validation():
@@ -110,6 +113,29 @@ def test_crop_pad_validation():
     assert lib.vsa_pad(c, FAKE, 5, 5, 5, MIS, None) == ALIGN
     assert lib.vsa_crop(c, FAKE, 5, 5, 5, FAKE, None) == UNSUP   # in place
     assert lib.vsa_crop(ctypes.byref(_p(T=7).c()), FAKE, 5, 5, 5, other, None) == SHAPE
+
+
+@pytest.mark.parametrize("cube,ok", [((4, 4, 4), True), ((2, 4, 4), True), ((4, 4, 8), True), ((1, 8, 8), True),
+                                     ((8, 4, 4), True), ((2, 2, 8), True), ((4, 8, 2), False), ((3, 4, 4), False),
+                                     ((2, 2, 4), False), ((4, 8, 8), False)])
+def test_cube_shapes(cube, ok):
+    """Cube sides: powers of two with Cw >= 4 and 32, 64 or 128 tokens."""
+    p = _p(T=8, H=16, W=16, cube=cube, topk=1)
+    bt = cube[0] * cube[1] * cube[2]
+    got = N.lib().vsa_workspace_bytes(ctypes.byref(p.c()), 0)
+    assert (got > 0) == ok
+    if ok:
+        assert p.Nc == 8 * 16 * 16 // bt
+    else:
+        st = N.lib().vsa_forward(ctypes.byref(p.c()), *([FAKE] * 8), None, FAKE, 1 << 30, None)
+        assert st in (SHAPE, UNSUP)
+
+
+def test_cube_must_divide_latent():
+    p = _p(T=6, H=8, W=8, cube=(4, 4, 4))
+    assert N.lib().vsa_workspace_bytes(ctypes.byref(p.c()), 0) == 0
+    p = _p(T=6, H=8, W=8, cube=(2, 4, 8), topk=1)
+    assert N.lib().vsa_workspace_bytes(ctypes.byref(p.c()), 0) > 0
 
 
 def test_max_pool_problem_is_valid():

@@ -355,7 +355,8 @@ def backward_compare(x, p, dtype, rel=BF16_REL, gates=True):
     g = V.backward(p, d["q"], d["k"], d["v"], gc, gf, idx, lens, saved, d["d_o"])
     torch.cuda.synchronize()
     xg = (x["g_c"], x["g_f"]) if gates else (None, None)
-    fwd = O.forward(x["q"], x["k"], x["v"], *xg, topk=0, idx=x["idx"], lens=x["len"], pool_mode=p.pool)
+    fwd = O.forward(x["q"], x["k"], x["v"], *xg, topk=0, idx=x["idx"], lens=x["len"], pool_mode=p.pool,
+                    cube=p.cube)
     assert_close(host(o), fwd["o"], dtype, "o")
     ref = O.backward(x["q"], x["k"], x["v"], *xg, x["d_o"], fwd)
     names = ("dq", "dk", "dv", "dg_c", "dg_f") if gates else ("dq", "dk", "dv")
@@ -365,15 +366,15 @@ def backward_compare(x, p, dtype, rel=BF16_REL, gates=True):
         assert g["dg_c"] is None and g["dg_f"] is None
 
 
-def _small_train_inputs(d=64, seed=5, heads=2, T=8, H=16, W=16):
+def _small_train_inputs(d=64, seed=5, heads=2, T=8, H=16, W=16, cube=(4, 4, 4)):
     x = WL.make_inputs_custom(1, heads, d, T, H, W, dtype="bf16", seed=seed)
-    nc = T * H * W // 64
+    nc = T * H * W // (cube[0] * cube[1] * cube[2])
     idx, lens = WL.random_lists(nc, heads * nc, 0, nc, seed=seed)
     lens[0], lens[1] = 0, nc
     idx[1, :nc] = np.arange(nc)
     x["idx"] = idx.reshape(1, heads, nc, nc)
     x["len"] = lens.reshape(1, heads, nc)
-    p = V.Problem(1, heads, T, H, W, d, topk=0, list_stride=nc)
+    p = V.Problem(1, heads, T, H, W, d, topk=0, list_stride=nc, cube=cube)
     return x, p
 
 
@@ -581,3 +582,74 @@ def test_forward_on_compatible_latent_then_crop():
     assert tuple(outs[0].shape) == (1, heads, T, H, W, d)
     assert torch.equal(outs[0], outs[1])
     assert_close(host(outs[0]), ref_o, "bf16", "o (cropped)")
+
+
+# ------------------------------------------- other cube shapes (tile sizes)
+CUBES = [(2, 4, 4), (4, 4, 8), (1, 8, 8)]   # 32, 128 and another 64-token tile
+
+
+@pytest.mark.parametrize("cube", CUBES)
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_general_cube_forward_topk(cube, dtype, d):
+    """Top-K selection bit-exact (near-tie protocol) and the output against the
+    oracle on the GPU's lists, for tiles of 32, 64 and 128 tokens."""
+    T, H, W, heads = 8, 16, 32, 2
+    bt = cube[0] * cube[1] * cube[2]
+    nc = T * H * W // bt
+    k = max(nc // 8, 1)
+    x = WL.make_inputs_custom(1, heads, d, T, H, W, dtype=dtype, seed=17, scale=1.0 if dtype == "bf16" else 0.125)
+    p = V.Problem(1, heads, T, H, W, d, dtype=dtype, topk=k, cube=cube)
+    dd = inputs_to_dev(x, dtype)
+    o, idx, lens, saved = V.forward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"], training=True)
+    torch.cuda.synchronize()
+    gi, gl = host(idx), host(lens)
+    assert (gl == k).all()
+    sel = O.forward(x["q"], x["k"], x["v"], topk=k, cube=cube)
+    near = check_topk(gi, sel, k)
+    assert near <= NEAR_FRAC * heads * nc
+    ref = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=gl, cube=cube)
+    assert_close(host(o), ref["o"], dtype, f"{cube} o")
+    sv = V.saved_views(p, saved)
+    assert_close(host(sv["o_f"]), ref["o_f"], dtype, f"{cube} o_f")
+    lse = host(sv["lse_f"])
+    assert np.abs(lse - ref["lse_f"]).max() <= (LSE_ABS if dtype == "bf16" else 1e-4)
+    np.testing.assert_allclose(host(sv["q_c"]), ref["q_c"], rtol=1e-4, atol=1e-5)
+
+
+@pytest.mark.parametrize("cube", CUBES)
+@pytest.mark.parametrize("d", [64, 128])
+def test_general_cube_backward(cube, d):
+    x, p = _small_train_inputs(d=d, seed=19, T=8, H=16, W=16, cube=cube)
+    backward_compare(x, p, "bf16")
+
+
+@pytest.mark.parametrize("cube", [(4, 4, 8), (2, 4, 4)])
+def test_general_cube_tiled_equals_raster_and_max_pool(cube):
+    x, p = _small_train_inputs(d=64, seed=23, T=8, H=16, W=16, cube=cube)
+    pm = dataclasses.replace(p, pool="max")
+    backward_compare(x, pm, "bf16")
+    pt = dataclasses.replace(p, layout="tiled")
+    d = inputs_to_dev(x, "bf16")
+    o, idx, lens, saved = V.forward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"], idx=d["idx"], lens=d["len"],
+                                    training=True)
+    g = V.backward(p, d["q"], d["k"], d["v"], d["g_c"], d["g_f"], idx, lens, saved, d["d_o"])
+    t = _tiled(p, d, ("q", "k", "v", "g_c", "g_f", "d_o"))
+    assert tuple(t["q"].shape) == (1, 2, p.Nc, p.Bt, 64)
+    assert np.array_equal(host(t["q"]), O.tile(host(d["q"]), cube))
+    ot, _, _, savedt = V.forward(pt, t["q"], t["k"], t["v"], t["g_c"], t["g_f"], idx=d["idx"], lens=d["len"],
+                                 training=True)
+    gt = V.backward(pt, t["q"], t["k"], t["v"], t["g_c"], t["g_f"], idx, lens, savedt, t["d_o"])
+    torch.cuda.synchronize()
+    assert torch.equal(V.untile(p, ot), o)
+    for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
+        assert torch.equal(V.untile(p, gt[nm]), g[nm]), nm
+    # crop / pad with this cube, from the tiled layout
+    Tc, Hc, Wc = V.compatible_latent(7, 13, 9, cube)
+    assert (Tc, Hc, Wc) == O.compatible_latent(7, 13, 9, cube)
+    pc = V.Problem(1, 2, Tc, Hc, Wc, 64, topk=1, cube=cube, layout="tiled")
+    xs = d["q"][:, :, :7, :13, :9].contiguous()
+    xp = V.pad(pc, xs)
+    back = V.crop(pc, xp, 7, 13, 9)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(xp), O.tile(O.pad(host(xs), Tc, Hc, Wc), cube))
+    assert torch.equal(back, xs)
