@@ -119,17 +119,21 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
 // transposed (channel-major), so that for 16x16x4 MFMA k-step s a lane of
 // lane group g contracts k = 8g + s and reads its eight A values and eight B
 // values as two 16-byte LDS reads each. Wave w owns channels
-// [16*CB*w, 16*CB*(w+1)) of both 16-row blocks.
+// [16*CB*w, 16*CB*(w+1)) of both 16-row blocks. The B tile is staged with k
+// varying fastest across lanes, so the transposing LDS stores of a wave fall
+// on consecutive banks (its two channel rows are BRP floats apart, which
+// keeps their 32-bank windows disjoint).
 template <int D, bool TRANS_A, bool EXP>
 __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restrict__ m, const float* __restrict__ lse,
                                                           const float* __restrict__ b, float* __restrict__ c, int Nc,
                                                           int ld, float scale) {
-  constexpr int KC = 32, RP = KC + 4;           // k per chunk, LDS row pitch (floats)
+  constexpr int KC = 32, RP = KC + 4;           // k per chunk, LDS row pitch of A (floats)
+  constexpr int BRP = KC + 8;                    // LDS row pitch of the transposed B tile
   constexpr int CB = D / 64;                     // 16-channel blocks per wave
   constexpr int BF4 = KC * D / 4 / 256;          // B float4 loads per thread per chunk
   static_assert(!(TRANS_A && EXP), "the softmax is applied along rows of M only");
   __shared__ __attribute__((aligned(16))) float Al[2][32][RP];
-  __shared__ __attribute__((aligned(16))) float Bl[2][D][RP];
+  __shared__ __attribute__((aligned(16))) float Bl[2][D][BRP];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const long bh = blockIdx.y;
   const int r0 = blockIdx.x * 32;
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
     }
 #pragma unroll
     for (int j = 0; j < BF4; ++j) {
-      const int f = tid + 256 * j, kap = f / (D / 4), c4 = f % (D / 4);
+      const int f = tid + 256 * j, kap = f % KC, c4 = f / KC;
       br[j] = k0 + kap < Nc ? *reinterpret_cast<const float4*>(Bm + (long)(k0 + kap) * D + 4 * c4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
     }
 #pragma unroll
     for (int j = 0; j < BF4; ++j) {
-      const int f = tid + 256 * j, kap = f / (D / 4), c4 = f % (D / 4);
+      const int f = tid + 256 * j, kap = f % KC, c4 = f / KC;
       Bl[bb][4 * c4 + 0][kap] = br[j].x;
       Bl[bb][4 * c4 + 1][kap] = br[j].y;
       Bl[bb][4 * c4 + 2][kap] = br[j].z;
