@@ -5,10 +5,10 @@
 // tokens has Bt/32 chunks). In LDS a chunk of one tensor (D channels) is a
 // row tile: 32 token rows of U = D/8 16-byte units; row kappa is in-cube token
 // 32h + kappa, and its logical unit u (channels 8u .. 8u+7) sits at unit
-// u ^ kswz(kappa), so 16 consecutive rows read at one logical unit hit 16
-// distinct bank groups. It is loaded from the raster tensor, read directly as
-// the A operand of a 32x32x16 MFMA (rows = tokens, k = channels) and, by LDS
-// transpose reads, as the A operand with k = tokens (rows = channels).
+// u ^ kswz(kappa), which spreads the tile's readers over the LDS banks. It
+// is loaded from the token tensor, read directly as the A operand of a
+// 32x32x16 MFMA (rows = tokens, k = channels) and, by LDS transpose reads,
+// as the A operand with k = tokens (rows = channels).
 #pragma once
 
 #include "vsa_common.h"
@@ -23,7 +23,17 @@ template <int D> struct ChunkGeom {
   static constexpr int RINS = RUNITS / 64;   // 1 KB loads per row tile
 };
 
-template <int U> __device__ __forceinline__ int kswz(int kappa) { return (kappa * U / 16) % U; }
+// The unit swizzle of row kappa: an XOR mask linear in kappa's low four bits,
+// chosen (by an exhaustive search over such masks against a model of the LDS
+// banks) so that both readers of a row tile are free of bank conflicts: the
+// 16-byte row reads (16 consecutive rows at one logical unit) and the
+// transpose reads (8 rows x 4 consecutive units per instruction).
+template <int U> __device__ __forceinline__ int kswz(int kappa) {
+  static_assert(U == 8 || U == 16, "row tiles of 64 or 128 channels");
+  const int b0 = kappa & 1, b1 = (kappa >> 1) & 1, b2 = (kappa >> 2) & 1, b3 = (kappa >> 3) & 1;
+  if (U == 16) return (b0 * 4) ^ (b1 * 10) ^ b2 ^ (b3 * 2);
+  return (b0 * 2) ^ (b1 * 4) ^ b2 ^ (b3 * 2);
+}
 
 // Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS byte
 // address lds + 16*l. Issued as inline assembly so that the compiler does not
