@@ -189,10 +189,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   // iterations ahead of their scores, V chunks VST - 1 ahead of their use;
   // iteration c issues V of chunk c + VST - 1 and then K of chunk c + KST.
   // At its top it needs K of c + 1 and V of c; loads retire in order, so only
-  // the K loads issued in iteration c - 1 may stay in flight. Each wave waits
-  // for its own loads, then a barrier (a bare s_barrier: a fenced one would
-  // also wait for the loads in flight) makes every wave's share visible and frees
-  // the stages about to be refilled (K of c, V of c - 1, read in c - 1).
+  // the loads issued in iteration c - 1 for later chunks (K of c + KST - 1 and,
+  // with three V stages, V of c + 1) may stay in flight. Each wave waits for
+  // its own loads, then a barrier (a bare s_barrier: a fenced one would also
+  // wait for the loads in flight) makes every wave's share visible and frees
+  // the stages about to be refilled (K of c, V of c + 1 - VST, read before).
   //
   // Online softmax against a lazily moved reference max m (log2 units): P =
   // 2^(s*c - m) is formed as long as no exponent exceeds 16 (P < 2^16, so
@@ -240,7 +241,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   auto step = [&](auto P, f32x16& sx, f32x16& sn, int c) {
     constexpr int p = decltype(P)::value;
     if (c > 0) {
-      if (c - 1 + C::KST < nch) wait_vmcnt<KPW>();
+      // Loads issued in iteration c - 1 that iteration c does not need yet:
+      // K of c - 1 + KST and, with three V stages, V of c + 1.
+      const bool kin = c - 1 + C::KST < nch;
+      const bool vin = C::VST >= 3 && c + C::VST - 2 < nch;
+      if (kin && vin) wait_vmcnt<2 * KPW>();
+      else if (kin || vin) wait_vmcnt<KPW>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
     }
