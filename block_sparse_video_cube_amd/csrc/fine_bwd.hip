@@ -84,8 +84,10 @@ __global__ __launch_bounds__(1024) void order_by_count_kernel(const int32_t* __r
   for (int e = threadIdx.x; e < Nc; e += 1024) order[bh * Nc + e] = (int32_t)(key[e] & 0xffffffffu);
 }
 
+// Two waves per SIMD (the register budget of 256 per lane holds the whole
+// working set without spills at either head dim).
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void fine_bwd_dq_kernel(
+__global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
     const float* __restrict__ lse_f, const bf16* __restrict__ dof, const float* __restrict__ delta,
@@ -209,8 +211,12 @@ __global__ __launch_bounds__(64 * NW, 1) void fine_bwd_dq_kernel(
     }
 }
 
+// Two waves per SIMD at 64 channels; at 128 channels the two accumulators
+// (dK^T and dV^T, 128 registers) and the lane's K and V rows do not fit in
+// 256 registers without spills, which cost far more than the second wave
+// gains, so it runs one wave per SIMD.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void fine_bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ k2q_off,
     const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
