@@ -211,12 +211,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
     }
 }
 
-// Two waves per SIMD at 64 channels; at 128 channels the two accumulators
-// (dK^T and dV^T, 128 registers) and the lane's K and V rows do not fit in
-// 256 registers without spills, which cost far more than the second wave
-// gains, so it runs one wave per SIMD.
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void fine_bwd_dkdv_kernel(
+// What a dK / dV pass computes: both gradients in one walk, or one of them
+// (two walks over the same lists, so that each pass's working set fits the
+// register budget of two waves per SIMD).
+enum DkdvMode { kDkDv = 0, kDvOnly = 1, kDkOnly = 2 };
+
+// Two waves per SIMD: at 64 channels both gradients fit in one pass; at 128
+// channels the two accumulators (dK^T and dV^T, 128 registers) and the lane's
+// K and V rows do not fit in 256 registers without spills, so the work is
+// split into a dV pass (S, P, dV) and a dK pass (S, dP, dS, dK).
+template <int D, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ k2q_off,
     const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
@@ -224,8 +229,12 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void fine_bwd_dkdv_kernel
     const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
     bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, int stride, float scale) {
   using G = ChunkGeom<D>;
+  constexpr bool DO_DV = MODE != kDkOnly, DO_DK = MODE != kDvOnly;
   __shared__ __attribute__((aligned(16))) bf16 rq[2][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rd[2][G::RUNITS * 8];
+  // LSE (log2 units after the load) and delta of the chunk's 32 query rows.
+  __shared__ __attribute__((aligned(16))) float rls[2][32];
+  __shared__ __attribute__((aligned(16))) float rdl[2][32];
 
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -240,18 +249,21 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void fine_bwd_dkdv_kernel
 
   // This lane's key: in-cube token 32wv + n32 of cube j.
   const long n = tok0 + cube_token(g, j, 32 * wv + n32);
-  bf16x8 kf[G::KS], vf[G::KS];
+  bf16x8 kf[G::KS], vf[DO_DK ? G::KS : 1];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
     kf[ks] = *reinterpret_cast<const bf16x8*>(k + n * D + ks * 16 + hf * 8);
-    vf[ks] = *reinterpret_cast<const bf16x8*>(v + n * D + ks * 16 + hf * 8);
+    if (DO_DK) vf[ks] = *reinterpret_cast<const bf16x8*>(v + n * D + ks * 16 + hf * 8);
   }
   const float sl2 = scale * kLog2e;
-  f32x16 adk[G::MB], adv[G::MB];
+  f32x16 adk[DO_DK ? G::MB : 1], adv[DO_DV ? G::MB : 1];
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) { adk[mb][e] = 0.f; adv[mb][e] = 0.f; }
+    for (int e = 0; e < 16; ++e) {
+      if (DO_DK) adk[mb][e] = 0.f;
+      if (DO_DV) adv[mb][e] = 0.f;
+    }
 
   uint32_t roff[G::RINS / NW];
   row_tile_offsets<D, NW>(g, wv, lane, roff);
@@ -264,35 +276,31 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void fine_bwd_dkdv_kernel
   auto chunk_bytes = [&](int h) { return NW == 1 ? 0u : (uint32_t)(chunk_first(g, h) * D) * 2u; };
   const char* Qb = reinterpret_cast<const char*>(q + tok0 * D);
   const char* Db = reinterpret_cast<const char*>(dof + tok0 * D);
-  // Per lane, for 64 list entries at a time: the partner cube and its first
-  // row's byte offset.
-  int icube = 0;
-  uint32_t rcube = 0;
+  const char* Lb = reinterpret_cast<const char*>(lse_f + tok0);
+  const char* Eb = reinterpret_cast<const char*>(delta + tok0);
+  // Per lane, for 64 list entries at a time: the partner cube's first row.
+  int rcube = 0;
   auto cubes = [&](int e0) {
     const int t = e0 + lane;
     int ii = t < L ? list[t] : 0;
     ii = (ii >= 0 && ii < g.Nc) ? ii : 0;
-    icube = ii;
-    rcube = (uint32_t)cube_first(g, ii) * (uint32_t)(D * 2);
+    rcube = cube_first(g, ii);
   };
-  const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd);
-  // LSE and delta of the chunk's query rows this lane's accumulator holds:
-  // rows kappa = 8m + 4hf + r (m, r = 0..3) = in-cube tokens 32h + kappa; the
-  // four tokens r = 0..3 are consecutive in memory (Cw >= 4).
-  float4 lsn[4], dln[4];
+  const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd), rlb = lds_addr(rls), reb = lds_addr(rdl);
+  // Rows 4t .. 4t+3 of a chunk are consecutive in memory (Cw >= 4): lane t
+  // < 8 of wave 0 moves them for LSE (and delta) with one 16-byte load.
+  const uint32_t soff = (uint32_t)chunk_row(g, 4 * (lane & 7)) * 4u;
   auto issue = [&](int c) {
     const int e = c / NW, h = c % NW, st = c & 1;
     if ((e & 63) == 0 && h == 0) cubes(e);
-    const int ii = __builtin_amdgcn_readlane(icube, e & 63);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const long r = tok0 + cube_token(g, ii, 32 * h + 8 * m + 4 * hf);
-      lsn[m] = *reinterpret_cast<const float4*>(lse_f + r);
-      dln[m] = *reinterpret_cast<const float4*>(delta + r);
-    }
-    const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + chunk_bytes(h);
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(rcube, e & 63) + (uint32_t)chunk_first(g, h);
+    const uint32_t rc = r0 * (uint32_t)(D * 2);
     issue_row_tile<D, NW>(uniform_ptr(Qb + rc), roff, rqb + st * (G::RUNITS * 16), wv);
     issue_row_tile<D, NW>(uniform_ptr(Db + rc), roff, rdb + st * (G::RUNITS * 16), wv);
+    if (wv == 0 && lane < 8) {
+      dma16(uniform_ptr(Lb + r0 * 4u), soff, rlb + st * 128);
+      if (DO_DK) dma16(uniform_ptr(Eb + r0 * 4u), soff, reb + st * 128);
+    }
   };
 
   const int nch = NW * L;
@@ -300,35 +308,34 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void fine_bwd_dkdv_kernel
   for (int c = 0; c < nch; ++c) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
+    if (c + 1 < nch) issue(c + 1);
+    const int st = c & 1;
+    // LSE and delta of the accumulator rows this lane holds: rows 8m + 4hf + r.
     float lse2[16], dl[16];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      lse2[4 * m + 0] = lsn[m].x * kLog2e; lse2[4 * m + 1] = lsn[m].y * kLog2e;
-      lse2[4 * m + 2] = lsn[m].z * kLog2e; lse2[4 * m + 3] = lsn[m].w * kLog2e;
-      dl[4 * m + 0] = dln[m].x; dl[4 * m + 1] = dln[m].y; dl[4 * m + 2] = dln[m].z; dl[4 * m + 3] = dln[m].w;
-    }
-    if (c + 1 < nch) issue(c + 1);
-    const int st = c & 1;
-    bf16x8 qa[G::KS], da[G::KS];
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      qa[ks] = row_frag<D>(rq[st], n32, hf, ks);
-      da[ks] = row_frag<D>(rd[st], n32, hf, ks);
+      const float4 a = *reinterpret_cast<const float4*>(&rls[st][8 * m + 4 * hf]);
+      lse2[4 * m + 0] = a.x * kLog2e; lse2[4 * m + 1] = a.y * kLog2e;
+      lse2[4 * m + 2] = a.z * kLog2e; lse2[4 * m + 3] = a.w * kLog2e;
+      if (DO_DK) {
+        const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * m + 4 * hf]);
+        dl[4 * m + 0] = b.x; dl[4 * m + 1] = b.y; dl[4 * m + 2] = b.z; dl[4 * m + 3] = b.w;
+      }
     }
     f32x16 sx, dp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { sx[e] = 0.f; dp[e] = 0.f; }
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
-      sx = mfma32_bf16(qa[ks], kf[ks], sx);
-      dp = mfma32_bf16(da[ks], vf[ks], dp);
+      sx = mfma32_bf16(row_frag<D>(rq[st], n32, hf, ks), kf[ks], sx);
+      if (DO_DK) dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), vf[ks], dp);
     }
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);
-      pf[e >> 3][e & 7] = (bf16)p;
-      sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl[e]));
+      if (DO_DV) pf[e >> 3][e & 7] = (bf16)p;
+      if (DO_DK) sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl[e]));
     }
     const char* qtile = reinterpret_cast<const char*>(rq[st]);
     const char* dtile = reinterpret_cast<const char*>(rd[st]);
@@ -336,8 +343,8 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void fine_bwd_dkdv_kernel
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb) {
-        adv[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], adv[mb]);
-        adk[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], adk[mb]);
+        if (DO_DV) adv[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], adv[mb]);
+        if (DO_DK) adk[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], adk[mb]);
       }
   }
 
@@ -352,17 +359,22 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 2 : 1) void fine_bwd_dkdv_kernel
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
       const int ch = 32 * mb + 8 * jq + 4 * hf;
-      float kcv[4], vcv[4];
-      pooled_grad(dkc + cj, karg_j, ch, lk, inv_b, kcv);
-      pooled_grad(dvc + cj, varg_j, ch, lk, inv_b, vcv);
-      bf16x4 wk, wvv;
+      if (DO_DK) {
+        float kcv[4];
+        pooled_grad(dkc + cj, karg_j, ch, lk, inv_b, kcv);
+        bf16x4 wk;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        wk[r] = (bf16)(scale * adk[mb][4 * jq + r] + kcv[r]);
-        wvv[r] = (bf16)(adv[mb][4 * jq + r] + vcv[r]);
+        for (int r = 0; r < 4; ++r) wk[r] = (bf16)(scale * adk[mb][4 * jq + r] + kcv[r]);
+        *reinterpret_cast<bf16x4*>(dk + n * D + ch) = wk;
       }
-      *reinterpret_cast<bf16x4*>(dk + n * D + ch) = wk;
-      *reinterpret_cast<bf16x4*>(dv + n * D + ch) = wvv;
+      if (DO_DV) {
+        float vcv[4];
+        pooled_grad(dvc + cj, varg_j, ch, lk, inv_b, vcv);
+        bf16x4 wvv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wvv[r] = (bf16)(adv[mb][4 * jq + r] + vcv[r]);
+        *reinterpret_cast<bf16x4*>(dv + n * D + ch) = wvv;
+      }
     }
 }
 
@@ -383,8 +395,15 @@ static void fine_bwd_launch(const Launch& L, const bf16* q, const bf16* k, const
   const int nitems = L.BH * L.g.Nc;
   hipLaunchKernelGGL((fine_bwd_dq_kernel<D, NW>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v, idx, len,
                      qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
-  hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v, k2q_off,
-                     k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
+  if constexpr (D == 64) {
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW, kDkDv>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v,
+                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
+  } else {
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW, kDvOnly>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v,
+                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW, kDkOnly>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v,
+                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
+  }
 }
 
 hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
