@@ -22,8 +22,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   constexpr int CH = D / 8;            // 8-channel chunks per token row
   constexpr int RPP = 256 / CH;        // token rows per pass
   constexpr int PASSES = BT / RPP;     // BT = tokens per cube
-  __shared__ float part[RPP][D + 4];
-  __shared__ uint8_t parg[MAX ? RPP : 1][D + 4];
+  __shared__ float part[3][RPP][D + 4];
+  __shared__ uint8_t parg[MAX ? 3 : 1][MAX ? RPP : 1][D + 4];
 
   const int tid = threadIdx.x;
   const long bh = blockIdx.y;
@@ -32,55 +32,61 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   const long base = bh * (long)g.N * D;
   const long plane = (long)gridDim.y * g.Nc * D;   // one tensor's args
 
-  const T* srcs[3] = {q, k, v};
+  const T* srcs[3] = {q + base, k + base, v + base};
   float* dsts[3] = {qc, kc, vc};
+  // Every load of the three tensors is issued before any reduction, so a
+  // thread keeps 3 * PASSES independent 16-byte loads in flight.
+  float acc[3][8];
+  int am[3][8];
 #pragma unroll
-  for (int which = 0; which < 3; ++which) {
-    const T* src = srcs[which] + base;
-    float acc[8];
-    int am[8];
+  for (int w = 0; w < 3; ++w)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { acc[e] = MAX ? -INFINITY : 0.f; am[e] = 0; }
+    for (int e = 0; e < 8; ++e) { acc[w][e] = MAX ? -INFINITY : 0.f; am[w][e] = 0; }
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int l = p * RPP + rsub;   // increasing: a strict compare keeps the first maximum
+  for (int p = 0; p < PASSES; ++p) {
+    const int l = p * RPP + rsub;   // increasing: a strict compare keeps the first maximum
+    const long off = (long)cube_token(g, c, l) * D + ch * 8;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
       float x[8];
-      load8(src + (long)cube_token(g, c, l) * D + ch * 8, x);
+      load8(srcs[w] + off, x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (MAX) {
-          if (x[e] > acc[e]) { acc[e] = x[e]; am[e] = l; }
+          if (x[e] > acc[w][e]) { acc[w][e] = x[e]; am[w][e] = l; }
         } else {
-          acc[e] += x[e];
+          acc[w][e] += x[e];
         }
       }
     }
+  }
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      part[rsub][ch * 8 + e] = acc[e];
-      if (MAX) parg[rsub][ch * 8 + e] = (uint8_t)am[e];
+      part[w][rsub][ch * 8 + e] = acc[w][e];
+      if (MAX) parg[w][rsub][ch * 8 + e] = (uint8_t)am[w][e];
     }
-    __syncthreads();
-    if (tid < D) {
-      if (MAX) {
-        float best = part[0][tid];
-        int ba = parg[0][tid];
+  __syncthreads();
+  for (int t = tid; t < 3 * D; t += 256) {
+    const int w = t / D, col = t - w * D;
+    if (MAX) {
+      float best = part[w][0][col];
+      int ba = parg[w][0][col];
 #pragma unroll
-        for (int r = 1; r < RPP; ++r) {
-          const float y = part[r][tid];
-          const int a = parg[r][tid];
-          if (y > best || (y == best && a < ba)) { best = y; ba = a; }   // ties: first in cube order
-        }
-        if (dsts[which] != nullptr) dsts[which][(bh * g.Nc + c) * D + tid] = best;
-        if (args != nullptr) args[which * plane + (bh * g.Nc + c) * D + tid] = (uint8_t)ba;
-      } else {
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < RPP; ++r) s += part[r][tid];
-        if (dsts[which] != nullptr) dsts[which][(bh * g.Nc + c) * D + tid] = s * (1.0f / BT);
+      for (int r = 1; r < RPP; ++r) {
+        const float y = part[w][r][col];
+        const int a = parg[w][r][col];
+        if (y > best || (y == best && a < ba)) { best = y; ba = a; }   // ties: first in cube order
       }
+      if (dsts[w] != nullptr) dsts[w][(bh * g.Nc + c) * D + col] = best;
+      if (args != nullptr) args[w * plane + (bh * g.Nc + c) * D + col] = (uint8_t)ba;
+    } else {
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < RPP; ++r) s += part[w][r][col];
+      if (dsts[w] != nullptr) dsts[w][(bh * g.Nc + c) * D + col] = s * (1.0f / BT);
     }
-    __syncthreads();
   }
 }
 
