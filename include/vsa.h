@@ -22,7 +22,10 @@
  *   order, head_dim fastest) in the problem's dtype (fp32 or bf16), unless the
  *   argument says otherwise. Pooled tensors ("_c") are fp32 [B, heads, Nc,
  *   head_dim], cubes in row-major order over (T/Ct, H/Ch, W/Cw); Nc = T*H*W/Bt.
- *   Per-token scalars (LSE_f, delta) are fp32 [B, heads, T, H, W].
+ *   Per-token scalars (LSE_f, delta) are fp32 [B, heads, T, H, W]. With the
+ *   TILED layout (vsa_layout below) every token tensor and per-token array of
+ *   the problem is cube-major instead ([B, heads, Nc, Bt, ...]): wherever an
+ *   argument below says "raster", read "in the problem's token order".
  * - Index lists: idx is int32 [B, heads, Nc, list_stride], len int32
  *   [B, heads, Nc]. Row i holds len[i] strictly increasing key-cube ids in
  *   [0, Nc); entries beyond len[i] are ignored.
@@ -120,8 +123,10 @@ int32_t vsa_max_cubes(void);
 
 /* Bytes of device workspace vsa_forward (training = 0) or vsa_backward
  * (training = 1) needs for problem p; 0 if p is invalid. The workspace holds
- * transposed bf16 tiles and scratch; its contents are meaningless between
- * calls. */
+ * scratch only (the coarse logits, fp32 Nc x Nc per (b, h), the processing
+ * orders, and for the backward the coarse softmax and its gradient, d_o_f,
+ * delta, the transposed lists and their bitmask); its contents are
+ * meaningless between calls. */
 size_t vsa_workspace_bytes(const vsa_problem* p, int32_t training);
 
 /* Bytes of the `saved` buffer a training forward fills and vsa_backward
@@ -162,7 +167,7 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
  * timing; vsa_forward / vsa_backward chain exactly these kernels) ---------- */
 
 /* Step 1, cube mean-pool: q_c/k_c/v_c (fp32 [B, heads, Nc, head_dim]) are
- * the means of the 64 tokens of every cube (VSA summary page, Appendix B;
+ * the means of the Bt tokens of every cube (VSA summary page, Appendix B;
  * reading notes key design 1), or their per-channel maxima when pool_mode
  * is VSA_POOL_MAX. */
 vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const void* v,
@@ -211,7 +216,7 @@ vsa_status vsa_combine(const vsa_problem* p, const float* o_c, const void* o_f,
 
 /* Backward of step 5 (calculus of the combine): dg_c = dO * O_c[cube],
  * dg_f = dO * O_f, d_o_f = dO * G_f (dtype, raster), delta = rowsum(d_o_f *
- * o_f) (fp32 [B, heads, T, H, W]) and d_o_c[c] = sum over the 64 tokens of
+ * o_f) (fp32 [B, heads, T, H, W]) and d_o_c[c] = sum over the Bt tokens of
  * cube c of dO * G_c (fp32 [B, heads, Nc, head_dim]). dg_c / dg_f may be
  * NULL (not written). */
 vsa_status vsa_combine_backward(const vsa_problem* p, const void* d_o, const float* o_c,
@@ -229,7 +234,8 @@ vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const i
                                void* stream);
 
 /* Backward of step 4 and of the pooling: dq, dk, dv (dtype, raster) =
- * fine-attention gradient + (dq_c, dk_c, dv_c)[cube] / 64, where the pooled
+ * fine-attention gradient + (dq_c, dk_c, dv_c)[cube] / Bt (with max pooling
+ * the pooled gradient goes to the cube's argmax token instead), where the pooled
  * gradients (fp32 [B, heads, Nc, head_dim]) come from vsa_coarse_backward.
  * lse_f from the forward; d_o_f and delta from vsa_combine_backward
  * (workspace: ws_bytes >= vsa_workspace_bytes(p, 1)); k2q_off / k2q from
