@@ -360,6 +360,17 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
+    # Per-step latency spread (separate from the timed loop): events around
+    # each step of a second pass.
+    per = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        per.append((a, b))
+    torch.cuda.synchronize()
+    lat = np.array([a.elapsed_time(b) for a, b in per])
 
     # Per-kernel breakdown: the same kernels through the stage entry points,
     # events on the launch stream between them.
@@ -389,6 +400,9 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms_percentiles": {"p10": round(float(np.percentile(lat, 10)), 4),
+                                "p50": round(float(np.percentile(lat, 50)), 4),
+                                "p90": round(float(np.percentile(lat, 90)), 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
