@@ -42,15 +42,17 @@ __device__ __forceinline__ uint32_t fkey(float f) {
 // [Nc][D] (fp32 16x16x4 MFMAs, 4x4 blocks). Lane (r = lane%16, g = lane/16)
 // holds, for channel group t, the float4 A[row r][16t + 4g .. +3] (and
 // likewise B), so four lanes cover 64 contiguous bytes of a row; k-step 4t+e
-// contracts channel 16t + 4g + e. Channel groups are double-buffered in
-// registers: the next group loads while this one's 64 MFMAs run. Rows beyond
-// Nc read as zero. acc[i][j][e] is C[m0 + 16i + 4g + e][n0 + 16j + r].
-template <int D>
+// contracts channel 16t + 4g + e. With NBUF = 2 channel groups are
+// double-buffered in registers (the next group loads while this one's 64
+// MFMAs run); NBUF = 1 loads each group just before its MFMAs, 32 registers
+// fewer. Rows beyond Nc read as zero. acc[i][j][e] is
+// C[m0 + 16i + 4g + e][n0 + 16j + r].
+template <int D, int NBUF = 2>
 __device__ __forceinline__ void nt_block64(const float* __restrict__ A, const float* __restrict__ B, int Nc,
                                            int m0, int n0, f32x4 acc[4][4]) {
   constexpr int KT = D / 16;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  float4 av[2][4], bv[2][4];
+  float4 av[NBUF][4], bv[NBUF][4];
   auto load = [&](int t, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -65,11 +67,12 @@ __device__ __forceinline__ void nt_block64(const float* __restrict__ A, const fl
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  load(0, 0);
+  if (NBUF == 2) load(0, 0);
 #pragma unroll
   for (int t = 0; t < KT; ++t) {
-    if (t + 1 < KT) load(t + 1, (t + 1) & 1);
-    const int bf = t & 1;
+    if (NBUF == 1) load(t, 0);
+    else if (t + 1 < KT) load(t + 1, (t + 1) % NBUF);
+    const int bf = t % NBUF;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -435,7 +438,7 @@ __global__ __launch_bounds__(256) void coarse_bwd_delta_kernel(const float* __re
 // dP = dO_c V_c^T on the same block, then the softmax and its derivative,
 // elementwise.
 template <int D>
-__global__ __launch_bounds__(256) void coarse_bwd_pds_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
+__global__ __launch_bounds__(256, 2) void coarse_bwd_pds_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
                                                              const float* __restrict__ vc, const float* __restrict__ doc,
                                                              const float* __restrict__ lse, const float* __restrict__ dc,
                                                              float* __restrict__ pbuf, float* __restrict__ dsbuf,
@@ -447,7 +450,10 @@ __global__ __launch_bounds__(256) void coarse_bwd_pds_kernel(const float* __rest
   const long base = bh * (long)Nc * D;
   f32x4 sacc[4][4], pacc[4][4];
   nt_block64<D>(qc + base, kc + base, Nc, m0, n0, sacc);
-  nt_block64<D>(doc + base, vc + base, Nc, m0, n0, pacc);
+  // The second product's loads start after the first product's MFMAs, so
+  // only one set of operand buffers is live (two waves per SIMD).
+  __builtin_amdgcn_sched_barrier(0);
+  nt_block64<D, 1>(doc + base, vc + base, Nc, m0, n0, pacc);
   float* P = pbuf + bh * (long)Nc * ld;
   float* DS = dsbuf + bh * (long)Nc * ld;
 #pragma unroll
