@@ -211,16 +211,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
     }
 }
 
-// What a dK / dV pass computes: both gradients in one walk, or one of them
-// (two walks over the same lists, so that each pass's working set fits the
-// register budget of two waves per SIMD).
-enum DkdvMode { kDkDv = 0, kDvOnly = 1, kDkOnly = 2 };
-
-// Two waves per SIMD: at 64 channels both gradients fit in one pass; at 128
-// channels the two accumulators (dK^T and dV^T, 128 registers) and the lane's
-// K and V rows do not fit in 256 registers without spills, so the work is
-// split into a dV pass (S, P, dV) and a dK pass (S, dP, dS, dK).
-template <int D, int NW, int MODE>
+// dK and dV at 64 channels: every wave computes both for its 32 keys, two
+// waves per SIMD. (At 128 channels the two accumulators, 128 registers, and
+// the lane's K and V rows do not fit 256 registers without spills; the
+// warp-specialized kernel below splits the roles over the waves instead.)
+template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ k2q_off,
@@ -229,7 +224,6 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
     bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, int stride, float scale) {
   using G = ChunkGeom<D>;
-  constexpr bool DO_DV = MODE != kDkOnly, DO_DK = MODE != kDvOnly;
   __shared__ __attribute__((aligned(16))) bf16 rq[2][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rd[2][G::RUNITS * 8];
   // LSE (log2 units after the load) and delta of the chunk's 32 query rows.
@@ -249,21 +243,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
 
   // This lane's key: in-cube token 32wv + n32 of cube j.
   const long n = tok0 + cube_token(g, j, 32 * wv + n32);
-  bf16x8 kf[G::KS], vf[DO_DK ? G::KS : 1];
+  bf16x8 kf[G::KS], vf[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
     kf[ks] = *reinterpret_cast<const bf16x8*>(k + n * D + ks * 16 + hf * 8);
-    if (DO_DK) vf[ks] = *reinterpret_cast<const bf16x8*>(v + n * D + ks * 16 + hf * 8);
+    vf[ks] = *reinterpret_cast<const bf16x8*>(v + n * D + ks * 16 + hf * 8);
   }
   const float sl2 = scale * kLog2e;
-  f32x16 adk[DO_DK ? G::MB : 1], adv[DO_DV ? G::MB : 1];
+  f32x16 adk[G::MB], adv[G::MB];
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (DO_DK) adk[mb][e] = 0.f;
-      if (DO_DV) adv[mb][e] = 0.f;
-    }
+    for (int e = 0; e < 16; ++e) { adk[mb][e] = 0.f; adv[mb][e] = 0.f; }
 
   uint32_t roff[G::RINS / NW];
   row_tile_offsets<D, NW>(g, wv, lane, roff);
@@ -299,7 +290,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     issue_row_tile<D, NW>(uniform_ptr(Db + rc), roff, rdb + st * (G::RUNITS * 16), wv);
     if (wv == 0 && lane < 8) {
       dma16(uniform_ptr(Lb + r0 * 4u), soff, rlb + st * 128);
-      if (DO_DK) dma16(uniform_ptr(Eb + r0 * 4u), soff, reb + st * 128);
+      dma16(uniform_ptr(Eb + r0 * 4u), soff, reb + st * 128);
     }
   };
 
@@ -317,10 +308,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
       const float4 a = *reinterpret_cast<const float4*>(&rls[st][8 * m + 4 * hf]);
       lse2[4 * m + 0] = a.x * kLog2e; lse2[4 * m + 1] = a.y * kLog2e;
       lse2[4 * m + 2] = a.z * kLog2e; lse2[4 * m + 3] = a.w * kLog2e;
-      if (DO_DK) {
-        const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * m + 4 * hf]);
-        dl[4 * m + 0] = b.x; dl[4 * m + 1] = b.y; dl[4 * m + 2] = b.z; dl[4 * m + 3] = b.w;
-      }
+      const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * m + 4 * hf]);
+      dl[4 * m + 0] = b.x; dl[4 * m + 1] = b.y; dl[4 * m + 2] = b.z; dl[4 * m + 3] = b.w;
     }
     f32x16 sx, dp;
 #pragma unroll
@@ -328,14 +317,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
       sx = mfma32_bf16(row_frag<D>(rq[st], n32, hf, ks), kf[ks], sx);
-      if (DO_DK) dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), vf[ks], dp);
+      dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), vf[ks], dp);
     }
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);
-      if (DO_DV) pf[e >> 3][e & 7] = (bf16)p;
-      if (DO_DK) sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl[e]));
+      pf[e >> 3][e & 7] = (bf16)p;
+      sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl[e]));
     }
     const char* qtile = reinterpret_cast<const char*>(rq[st]);
     const char* dtile = reinterpret_cast<const char*>(rd[st]);
@@ -343,8 +332,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb) {
-        if (DO_DV) adv[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], adv[mb]);
-        if (DO_DK) adk[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], adk[mb]);
+        adv[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], adv[mb]);
+        adk[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], adk[mb]);
       }
   }
 
@@ -359,22 +348,180 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
       const int ch = 32 * mb + 8 * jq + 4 * hf;
-      if (DO_DK) {
-        float kcv[4];
-        pooled_grad(dkc + cj, karg_j, ch, lk, inv_b, kcv);
-        bf16x4 wk;
+      float kcv[4], vcv[4];
+      pooled_grad(dkc + cj, karg_j, ch, lk, inv_b, kcv);
+      pooled_grad(dvc + cj, varg_j, ch, lk, inv_b, vcv);
+      bf16x4 wk, wvv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wk[r] = (bf16)(scale * adk[mb][4 * jq + r] + kcv[r]);
-        *reinterpret_cast<bf16x4*>(dk + n * D + ch) = wk;
+      for (int r = 0; r < 4; ++r) {
+        wk[r] = (bf16)(scale * adk[mb][4 * jq + r] + kcv[r]);
+        wvv[r] = (bf16)(adv[mb][4 * jq + r] + vcv[r]);
       }
-      if (DO_DV) {
-        float vcv[4];
-        pooled_grad(dvc + cj, varg_j, ch, lk, inv_b, vcv);
-        bf16x4 wvv;
+      *reinterpret_cast<bf16x4*>(dk + n * D + ch) = wk;
+      *reinterpret_cast<bf16x4*>(dv + n * D + ch) = wvv;
+    }
+}
+
+// dK and dV at 128 channels, warp-specialized: a workgroup of 2 NW waves owns
+// a key cube; NW waves compute dV (S, P, dV^T += dO^T P) and NW waves dK (S,
+// dP, dS, dK^T += Q^T dS) for the same keys, from one copy of every Q / dO
+// chunk in LDS (each of the 2 NW waves issues its share of the loads). The
+// roles swap with the workgroup's parity, so that the two workgroups sharing
+// a CU tend to put a wave of each role on every SIMD. One accumulator array
+// holds dV^T or dK^T, so a wave's working set is the dK pass's.
+template <int D, int NW>
+__global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const int32_t* __restrict__ k2q_off,
+    const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
+    const bf16* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dkc,
+    const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, int stride, float scale) {
+  using G = ChunkGeom<D>;
+  constexpr int NWT = 2 * NW;   // waves in the workgroup
+  static_assert(G::RINS % NWT == 0, "every wave issues whole 1 KB loads");
+  __shared__ __attribute__((aligned(16))) bf16 rq[2][G::RUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 rd[2][G::RUNITS * 8];
+  __shared__ __attribute__((aligned(16))) float rls[2][32];
+  __shared__ __attribute__((aligned(16))) float rdl[2][32];
+
+  const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kw = wv % NW;                                     // keys 32kw .. 32kw + 31
+  const bool isk = ((wv / NW) ^ (int)(blockIdx.x & 1)) != 0;  // this wave computes dK (else dV)
+  const int slot = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = slot / g.Nc;
+  const int j = order != nullptr ? order[slot] : slot - bh * g.Nc;
+  const long tok0 = (long)bh * g.N;
+  const int32_t* offs = k2q_off + (long)bh * (g.Nc + 1);
+  const int t0 = min(max(offs[j], 0), g.Nc * stride), t1 = min(max(offs[j + 1], t0), g.Nc * stride);
+  const int32_t* list = k2q + (long)bh * g.Nc * stride + t0;
+  const int L = t1 - t0;
+
+  // This lane's key: in-cube token 32kw + n32 of cube j.
+  const long n = tok0 + cube_token(g, j, 32 * kw + n32);
+  bf16x8 kf[G::KS], vf[G::KS];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wvv[r] = (bf16)(adv[mb][4 * jq + r] + vcv[r]);
-        *reinterpret_cast<bf16x4*>(dv + n * D + ch) = wvv;
+  for (int ks = 0; ks < G::KS; ++ks) {
+    kf[ks] = *reinterpret_cast<const bf16x8*>(k + n * D + ks * 16 + hf * 8);
+    if (isk) vf[ks] = *reinterpret_cast<const bf16x8*>(v + n * D + ks * 16 + hf * 8);
+  }
+  const float sl2 = scale * kLog2e;
+  f32x16 acc[G::MB];
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
+
+  uint32_t roff[G::RINS / NWT];
+  row_tile_offsets<D, NWT>(g, wv, lane, roff);
+  uint32_t toffs[G::MB][2][2];   // transposed reads of the Q / dO row tiles
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, toffs[mb][s2]);
+  const char* Qb = reinterpret_cast<const char*>(q + tok0 * D);
+  const char* Db = reinterpret_cast<const char*>(dof + tok0 * D);
+  const char* Lb = reinterpret_cast<const char*>(lse_f + tok0);
+  const char* Eb = reinterpret_cast<const char*>(delta + tok0);
+  int rcube = 0;
+  auto cubes = [&](int e0) {
+    const int t = e0 + lane;
+    int ii = t < L ? list[t] : 0;
+    ii = (ii >= 0 && ii < g.Nc) ? ii : 0;
+    rcube = cube_first(g, ii);
+  };
+  const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd), rlb = lds_addr(rls), reb = lds_addr(rdl);
+  const uint32_t soff = (uint32_t)chunk_row(g, 4 * (lane & 7)) * 4u;
+  // Query chunks: query cube list[e], its chunk h (NW chunks per cube).
+  auto issue = [&](int c) {
+    const int e = c / NW, h = c % NW, st = c & 1;
+    if ((e & 63) == 0 && h == 0) cubes(e);
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(rcube, e & 63) + (uint32_t)chunk_first(g, h);
+    const uint32_t rc = r0 * (uint32_t)(D * 2);
+    issue_row_tile<D, NWT>(uniform_ptr(Qb + rc), roff, rqb + st * (G::RUNITS * 16), wv);
+    issue_row_tile<D, NWT>(uniform_ptr(Db + rc), roff, rdb + st * (G::RUNITS * 16), wv);
+    if (wv == 0 && lane < 8) {
+      dma16(uniform_ptr(Lb + r0 * 4u), soff, rlb + st * 128);
+      dma16(uniform_ptr(Eb + r0 * 4u), soff, reb + st * 128);
+    }
+  };
+
+  const int nch = NW * L;
+  if (nch > 0) issue(0);
+  for (int c = 0; c < nch; ++c) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (c + 1 < nch) issue(c + 1);
+    const int st = c & 1;
+    float lse2[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float4 a = *reinterpret_cast<const float4*>(&rls[st][8 * m + 4 * hf]);
+      lse2[4 * m + 0] = a.x * kLog2e; lse2[4 * m + 1] = a.y * kLog2e;
+      lse2[4 * m + 2] = a.z * kLog2e; lse2[4 * m + 3] = a.w * kLog2e;
+    }
+    f32x16 sx;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sx[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) sx = mfma32_bf16(row_frag<D>(rq[st], n32, hf, ks), kf[ks], sx);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sx[e] = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);   // P
+    const char* qtile = reinterpret_cast<const char*>(rq[st]);
+    const char* dtile = reinterpret_cast<const char*>(rd[st]);
+    if (isk) {
+      float dl[16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * m + 4 * hf]);
+        dl[4 * m + 0] = b.x; dl[4 * m + 1] = b.y; dl[4 * m + 2] = b.z; dl[4 * m + 3] = b.w;
       }
+      f32x16 dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dp[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), vf[ks], dp);
+      bf16x8 sf[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sf[e >> 3][e & 7] = (bf16)(sx[e] * (dp[e] - dl[e]));
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int mb = 0; mb < G::MB; ++mb)
+          acc[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], acc[mb]);
+    } else {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (bf16)sx[e];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int mb = 0; mb < G::MB; ++mb)
+          acc[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], acc[mb]);
+    }
+  }
+
+  // lane holds d{K,V}^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its key]
+  const long cj = ((long)bh * g.Nc + j) * D;
+  const uint8_t* arg_j = isk ? (karg != nullptr ? karg + cj : nullptr) : (varg != nullptr ? varg + cj : nullptr);
+  const float* xc = (isk ? dkc : dvc) + cj;
+  bf16* out = isk ? dk : dv;
+  const float sc = isk ? scale : 1.0f;
+  const int lk = 32 * kw + n32;   // the key's position in its cube
+  const float inv_b = 1.0f / (float)g.B;
+#pragma unroll
+  for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const int ch = 32 * mb + 8 * jq + 4 * hf;
+      float cv[4];
+      pooled_grad(xc, arg_j, ch, lk, inv_b, cv);
+      bf16x4 w4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w4[r] = (bf16)(sc * acc[mb][4 * jq + r] + cv[r]);
+      *reinterpret_cast<bf16x4*>(out + n * D + ch) = w4;
     }
 }
 
@@ -396,12 +543,10 @@ static void fine_bwd_launch(const Launch& L, const bf16* q, const bf16* k, const
   hipLaunchKernelGGL((fine_bwd_dq_kernel<D, NW>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v, idx, len,
                      qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
   if constexpr (D == 64) {
-    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW, kDkDv>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v,
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v,
                        k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
   } else {
-    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW, kDvOnly>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v,
-                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
-    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW, kDkOnly>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v,
+    hipLaunchKernelGGL((fine_bwd_dkdv_ws_kernel<D, NW>), dim3(nitems), dim3(128 * NW), 0, L.stream, q, k, v,
                        k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
   }
 }
