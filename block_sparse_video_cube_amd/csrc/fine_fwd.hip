@@ -40,7 +40,6 @@ template <int D> struct FineCfg {
   static constexpr int KUNITS = 32 * U;      // 16-byte units per K chunk
   static constexpr int VUNITS = 32 * U;      // 16-byte units per V chunk
   static constexpr int KINS = KUNITS / 64;   // 1 KB direct-to-LDS loads per K chunk
-  static constexpr int VINS = VUNITS / 64;
   // LDS stages of K and V chunks. D = 128: (3 + 2) x 8 KB = 40 KB, so four
   // workgroups (two waves per SIMD) fit in the 160 KB of LDS of a CU.
   static constexpr int KST = 3;

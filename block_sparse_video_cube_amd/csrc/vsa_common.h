@@ -102,8 +102,6 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   return x * q + (x < rem ? x : rem) + k;
 }
 
-__device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
-__device__ __forceinline__ bf16 f2bf(float v) { return (bf16)v; }  // round to nearest even
 
 template <typename T> struct Io;
 template <> struct Io<float> {
