@@ -32,7 +32,10 @@ the design notes of the repository):
 * the top-K mask carries no gradient (it is piecewise constant);
 * cube shapes other than (4, 4, 4) (the summary page's tile-size exploration,
   section 2 "Methods"): the same definitions with B = Ct*Ch*Cw tokens per cube,
-  cubes row-major over the grid and tokens row-major inside a cube;
+  cubes row-major over the grid and tokens row-major inside a cube; with key
+  blocks of their own shape (Bq x Bk tiles, as the page's 64 x 16 example),
+  queries are pooled and attend per query cube, keys and values are pooled
+  and selected per key block;
 * the max-pool variant (ablation of the coarse pooling) takes the per-channel
   maximum over a cube; its gradient goes to the first maximum in cube order.
 
@@ -288,16 +291,20 @@ def fine_gathered(qt, kt, vt, idx, lens, scale):
     return of, lse
 
 
-def fine_literal(q, k, v, mask, scale, cube=DEFAULT_CUBE):
+def fine_literal(q, k, v, mask, scale, cube=DEFAULT_CUBE, kcube=None):
     """The App. B form: full token-level scores, unselected blocks set to -inf,
     row softmax, times V. For one (b, h) in raster layout, q/k/v [T, H, W, d],
-    mask [Nc, Nc]. Quadratic in N: small shapes only. Returns (O_f, LSE_f) raster."""
+    mask [Nq, Nk] (query cubes x key cubes; kcube = cube unless given).
+    Quadratic in N: small shapes only. Returns (O_f, LSE_f) raster."""
     T, H, W, d = q.shape
+    kcube = cube if kcube is None else kcube
     n = T * H * W
     qr, kr, vr = q.reshape(n, d), k.reshape(n, d), v.reshape(n, d)
-    cube_of = np.empty(n, dtype=np.int64)
-    cube_of[tiled_to_raster(T, H, W, cube)] = np.arange(n) // int(np.prod(_cube(cube)))
-    allowed = mask[cube_of[:, None], cube_of[None, :]]
+    qcube_of = np.empty(n, dtype=np.int64)
+    qcube_of[tiled_to_raster(T, H, W, cube)] = np.arange(n) // int(np.prod(_cube(cube)))
+    kcube_of = np.empty(n, dtype=np.int64)
+    kcube_of[tiled_to_raster(T, H, W, kcube)] = np.arange(n) // int(np.prod(_cube(kcube)))
+    allowed = mask[qcube_of[:, None], kcube_of[None, :]]
     z = np.where(allowed, scale * (qr @ kr.T), -np.inf)
     o = np.zeros((n, d))
     lse = np.full(n, -np.inf)
@@ -341,29 +348,33 @@ def _f64(x):
 
 def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
             scale: Optional[float] = None, with_literal: bool = False, pool_mode: str = "mean",
-            cube=DEFAULT_CUBE):
-    """VSA forward for [B, h, T, H, W, d] inputs with cubes of shape ``cube``.
+            cube=DEFAULT_CUBE, kcube=None):
+    """VSA forward for [B, h, T, H, W, d] inputs with query cubes of shape
+    ``cube`` and key blocks of shape ``kcube`` (the same unless given: the
+    Bq x Bk tiles of the summary page's tile-size exploration).
 
-    topk > 0 selects the K best cubes per row; topk == 0 uses the caller's
-    lists idx [B, h, Nc, L] / lens [B, h, Nc]. Returns a dict of float64
-    results (raster layout unless the name says tiled / pooled).
+    topk > 0 selects the K best key blocks per query cube; topk == 0 uses the
+    caller's lists idx [B, h, Nq, L] / lens [B, h, Nq]. Returns a dict of
+    float64 results (raster layout unless the name says tiled / pooled).
     """
     sig_bits = 24 if np.asarray(q).dtype == np.float32 and not _bf16_exact(q) else 8
     q, k, v, g_c, g_f = map(_f64, (q, k, v, g_c, g_f))
     B, nh, T, H, W, d = q.shape
     cube = _cube(cube)
-    nc = T * H * W // int(np.prod(cube))
+    kcube = cube if kcube is None else _cube(kcube)
+    nq = T * H * W // int(np.prod(cube))
+    nc = T * H * W // int(np.prod(kcube))     # key blocks: the coarse columns
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    qt, kt, vt = tile(q, cube), tile(k, cube), tile(v, cube)
+    qt, kt, vt = tile(q, cube), tile(k, kcube), tile(v, kcube)
     qc, kc, vc = pool(qt, pool_mode), pool(kt, pool_mode), pool(vt, pool_mode)
     oc = np.empty_like(qc)
     lse_c = np.empty(qc.shape[:-1])
-    s_c = np.empty((B, nh, nc, nc))
+    s_c = np.empty((B, nh, nq, nc))
     if topk > 0:
-        idx_o = np.empty((B, nh, nc, topk), dtype=np.int64)
-        lens_o = np.full((B, nh, nc), topk, dtype=np.int64)
-        margin = np.empty((B, nh, nc))
-        tau = np.empty((B, nh, nc))
+        idx_o = np.empty((B, nh, nq, topk), dtype=np.int64)
+        lens_o = np.full((B, nh, nq), topk, dtype=np.int64)
+        margin = np.empty((B, nh, nq))
+        tau = np.empty((B, nh, nq))
     else:
         idx_o = np.asarray(idx, dtype=np.int64)
         lens_o = np.asarray(lens, dtype=np.int64)
@@ -381,10 +392,10 @@ def forward(q, k, v, g_c=None, g_f=None, topk: int = 0, idx=None, lens=None,
                                                     idx_o[b, h], lens_o[b, h], s)
             if with_literal:
                 m = lists_to_mask(idx_o[b, h], lens_o[b, h], nc)
-                of_lit[b, h], _ = fine_literal(q[b, h], k[b, h], v[b, h], m, s, cube)
+                of_lit[b, h], _ = fine_literal(q[b, h], k[b, h], v[b, h], m, s, cube, kcube)
     of = untile(of_t, T, H, W, cube)
     oc_rep = repeat_coarse(oc, T, H, W, cube)
-    out = dict(scale=s, pool_mode=pool_mode, cube=cube, q_c=qc, k_c=kc, v_c=vc, s_c=s_c, o_c=oc, lse_c=lse_c,
+    out = dict(scale=s, pool_mode=pool_mode, cube=cube, kcube=kcube, q_c=qc, k_c=kc, v_c=vc, s_c=s_c, o_c=oc, lse_c=lse_c,
                idx=idx_o, len=lens_o, margin=margin, tau=tau,
                o_f=of, lse_f=untile_rows(lse_t, T, H, W, cube), o_c_rep=oc_rep,
                o=combine(oc_rep, of, g_c, g_f))
@@ -409,9 +420,11 @@ def fine_backward(qt, kt, vt, dof_t, of_t, lse_t, idx, lens, scale):
 
     With P = exp(s*q.k - LSE_f) on the listed blocks: dV = P^T dO_f,
     dP = dO_f V^T, D = rowsum(dO_f * O_f), dS = P * (dP - D),
-    dQ = s*dS K, dK = s*dS^T Q. Returns dQ, dK, dV [Nc, B, d] and D [Nc, B].
+    dQ = s*dS K, dK = s*dS^T Q. Returns dQ [Nq, Bq, d], dK, dV [Nk, Bk, d] and
+    D [Nq, Bq].
     """
     nc, b, d = qt.shape
+    bk = kt.shape[1]
     dq = np.zeros_like(qt)
     dk = np.zeros_like(kt)
     dv = np.zeros_like(vt)
@@ -426,8 +439,8 @@ def fine_backward(qt, kt, vt, dof_t, of_t, lse_t, idx, lens, scale):
         dp = dof_t[i] @ vs.T
         ds = p * (dp - dd[i][:, None])
         dq[i] = scale * (ds @ ks)
-        dk_sel = (scale * (ds.T @ qt[i])).reshape(-1, b, d)
-        dv_sel = (p.T @ dof_t[i]).reshape(-1, b, d)
+        dk_sel = (scale * (ds.T @ qt[i])).reshape(-1, bk, d)
+        dv_sel = (p.T @ dof_t[i]).reshape(-1, bk, d)
         np.add.at(dk, sel, dk_sel)
         np.add.at(dv, sel, dv_sel)
     return dq, dk, dv, dd
@@ -466,14 +479,15 @@ def backward(q, k, v, g_c, g_f, d_o, fwd: dict):
     B, nh, T, H, W, d = q.shape
     s = fwd["scale"]
     cube = fwd.get("cube", DEFAULT_CUBE)
+    kcube = fwd.get("kcube") or cube
     dgc, dgf, dof, docr = combine_backward(d_o, fwd["o_c_rep"], fwd["o_f"], g_c, g_f)
     doc = tile(docr, cube).sum(axis=-2)   # the repeat's gradient sums over the cube
-    qt, kt, vt = tile(q, cube), tile(k, cube), tile(v, cube)
+    qt, kt, vt = tile(q, cube), tile(k, kcube), tile(v, kcube)
     dof_t, of_t = tile(dof, cube), tile(fwd["o_f"], cube)
     lse_t = tile(fwd["lse_f"][..., None], cube)[..., 0]
     dqt, dkt, dvt = np.empty_like(qt), np.empty_like(kt), np.empty_like(vt)
     dd_t = np.empty(qt.shape[:-1])
-    dqc, dkc, dvc = (np.empty_like(fwd["q_c"]) for _ in range(3))
+    dqc, dkc, dvc = np.empty_like(fwd["q_c"]), np.empty_like(fwd["k_c"]), np.empty_like(fwd["v_c"])
     for b in range(B):
         for h in range(nh):
             dqt[b, h], dkt[b, h], dvt[b, h], dd_t[b, h] = fine_backward(
@@ -483,8 +497,8 @@ def backward(q, k, v, g_c, g_f, d_o, fwd: dict):
                 fwd["q_c"][b, h], fwd["k_c"][b, h], fwd["v_c"][b, h], doc[b, h], s)
     pm = fwd.get("pool_mode", "mean")
     dq = untile(dqt + pool_backward(dqc, qt, pm), T, H, W, cube)
-    dk = untile(dkt + pool_backward(dkc, kt, pm), T, H, W, cube)
-    dv = untile(dvt + pool_backward(dvc, vt, pm), T, H, W, cube)
+    dk = untile(dkt + pool_backward(dkc, kt, pm), T, H, W, kcube)
+    dv = untile(dvt + pool_backward(dvc, vt, pm), T, H, W, kcube)
     return dict(dq=dq, dk=dk, dv=dv, dg_c=dgc, dg_f=dgf, d_o_f=dof, d_o_c=doc,
                 delta=untile_rows(dd_t, T, H, W, cube), dq_c=dqc, dk_c=dkc, dv_c=dvc)
 

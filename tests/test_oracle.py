@@ -278,28 +278,32 @@ def test_repeat_coarse_matches_repeat_interleave():
 
 
 # ----------------------------------------------------------------- end to end
-def _torch_vsa(q, k, v, g_c, g_f, mask, scale, pool_mode="mean", cube=(4, 4, 4)):
+def _torch_vsa(q, k, v, g_c, g_f, mask, scale, pool_mode="mean", cube=(4, 4, 4), kcube=None):
     """Independent torch expression of the forward with a fixed block mask:
-    avg_pool3d (or max_pool3d) pooling with the cube as kernel,
-    repeat_interleave broadcast, token-level masked softmax."""
+    avg_pool3d (or max_pool3d) pooling with the query cube (queries) or the
+    key block (keys, values) as kernel, repeat_interleave broadcast,
+    token-level masked softmax."""
     B, h, T, H, W, d = q.shape
+    kcube = cube if kcube is None else kcube
     Tp, Hp, Wp = T // cube[0], H // cube[1], W // cube[2]
     pool3d = F.max_pool3d if pool_mode == "max" else F.avg_pool3d
 
-    def pool(x):
-        p = pool3d(x.permute(0, 1, 5, 2, 3, 4).reshape(B * h, d, T, H, W), tuple(cube))
+    def pool(x, c):
+        p = pool3d(x.permute(0, 1, 5, 2, 3, 4).reshape(B * h, d, T, H, W), tuple(c))
         return p.reshape(B, h, d, -1).transpose(-1, -2)
 
-    qc, kc, vc = pool(q), pool(k), pool(v)
+    qc, kc, vc = pool(q, cube), pool(k, kcube), pool(v, kcube)
     a = torch.softmax(scale * qc @ kc.transpose(-1, -2), dim=-1)
     oc = (a @ vc).reshape(B, h, Tp, Hp, Wp, d)
     for ax in (2, 3, 4):
         oc = oc.repeat_interleave(cube[ax - 2], dim=ax)
-    cid = torch.arange(Tp * Hp * Wp).reshape(Tp, Hp, Wp)
-    for ax in (0, 1, 2):
-        cid = cid.repeat_interleave(cube[ax], dim=ax)
-    cid = cid.reshape(-1)
-    tok_mask = mask[:, :, cid][:, :, :, cid]
+    def ids(c):
+        cid = torch.arange((T // c[0]) * (H // c[1]) * (W // c[2])).reshape(T // c[0], H // c[1], W // c[2])
+        for ax in (0, 1, 2):
+            cid = cid.repeat_interleave(c[ax], dim=ax)
+        return cid.reshape(-1)
+
+    tok_mask = mask[:, :, ids(cube)][:, :, :, ids(kcube)]
     qr, kr, vr = (x.reshape(B, h, -1, d) for x in (q, k, v))
     z = (scale * qr @ kr.transpose(-1, -2)).masked_fill(~tok_mask, float("-inf"))
     of = (torch.softmax(z, dim=-1) @ vr).reshape(B, h, T, H, W, d)
@@ -389,6 +393,39 @@ def test_general_cube_forward_backward_match_autograd(cube):
         np.testing.assert_allclose(bwd[name], ts[key].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
     # adaptation start (K = all cubes, G_c = 0, G_f removed) is full attention for any cube
     full = O.forward(w["q"], w["k"], w["v"], np.zeros_like(w["g_c"]), None, topk=nc, cube=cube)
+    for h in range(2):
+        ref = F.scaled_dot_product_attention(
+            *(torch.from_numpy(w[x][0, h].astype(np.float64).reshape(1, -1, 4)) for x in ("q", "k", "v")))
+        np.testing.assert_allclose(full["o"][0, h].reshape(-1, 4), ref[0].numpy(), rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("cube,kcube", [((4, 4, 4), (2, 4, 4)), ((4, 4, 4), (4, 4, 8)), ((2, 4, 4), (4, 4, 4))])
+def test_asymmetric_tiles_forward_backward_match_autograd(cube, kcube):
+    """Query tiles and key blocks of different shapes (Bq x Bk tiles, the
+    summary page's 64 x 16 example generalised): forward and backward against
+    the independent expression, literal = gathered, and all key blocks kept
+    with G_c = 0 and G_f removed equals full attention."""
+    T, H, W = 8, 8, 16
+    w = WL.make_inputs_custom(1, 2, 4, T, H, W, dtype="f32", seed=12, scale=0.5)
+    nq = T * H * W // (cube[0] * cube[1] * cube[2])
+    nk = T * H * W // (kcube[0] * kcube[1] * kcube[2])
+    idx, lens = WL.random_lists(nk, 2 * nq, 1, min(nk, 5), seed=13)
+    idx, lens = idx.reshape(1, 2, nq, -1), lens.reshape(1, 2, nq)
+    fwd = O.forward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], topk=0, idx=idx, lens=lens,
+                    with_literal=True, cube=cube, kcube=kcube)
+    assert fwd["q_c"].shape[-2] == nq and fwd["k_c"].shape[-2] == nk and fwd["s_c"].shape[-2:] == (nq, nk)
+    bwd = O.backward(w["q"], w["k"], w["v"], w["g_c"], w["g_f"], w["d_o"], fwd)
+    mask = np.stack([[O.lists_to_mask(idx[0, h], lens[0, h], nk) for h in range(2)]])
+    ts = {x: torch.from_numpy(w[x].astype(np.float64)).requires_grad_(True)
+          for x in ("q", "k", "v", "g_c", "g_f")}
+    out = _torch_vsa(ts["q"], ts["k"], ts["v"], ts["g_c"], ts["g_f"], torch.from_numpy(mask), 0.5,
+                     cube=cube, kcube=kcube)
+    np.testing.assert_allclose(fwd["o"], out.detach().numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fwd["o_f"], fwd["o_f_literal"], rtol=1e-12, atol=1e-14)
+    (out * torch.from_numpy(w["d_o"].astype(np.float64))).sum().backward()
+    for name, key in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg_c", "g_c"), ("dg_f", "g_f")):
+        np.testing.assert_allclose(bwd[name], ts[key].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+    full = O.forward(w["q"], w["k"], w["v"], np.zeros_like(w["g_c"]), None, topk=nk, cube=cube, kcube=kcube)
     for h in range(2):
         ref = F.scaled_dot_product_attention(
             *(torch.from_numpy(w[x][0, h].astype(np.float64).reshape(1, -1, 4)) for x in ("q", "k", "v")))
