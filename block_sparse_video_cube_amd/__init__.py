@@ -40,6 +40,7 @@ class Problem:
     pool: str = "mean"           # cube pooling of the coarse stage: "mean" or "max"
     layout: str = "raster"       # token order: "raster" [B,h,T,H,W,d] or "tiled" [B,h,Nc,Bt,d]
     cube: tuple = (4, 4, 4)      # cube sides (Ct, Ch, Cw); Bt = Ct*Ch*Cw tokens per tile
+    kcube: Optional[tuple] = None  # key-block sides; None => the cube (Bq x Bk tiles otherwise)
 
     @property
     def N(self) -> int:
@@ -54,6 +55,19 @@ class Problem:
         return self.N // self.Bt
 
     @property
+    def key_cube(self) -> tuple:
+        return tuple(self.kcube) if self.kcube is not None else tuple(self.cube)
+
+    @property
+    def Bk(self) -> int:
+        k = self.key_cube
+        return k[0] * k[1] * k[2]
+
+    @property
+    def Nk(self) -> int:
+        return self.N // self.Bk
+
+    @property
     def stride(self) -> int:
         return self.list_stride if self.list_stride else self.topk
 
@@ -66,7 +80,8 @@ class Problem:
         pool = {"mean": 0, "max": 1}.get(self.pool, 99)
         layout = {"raster": 0, "tiled": 1}.get(self.layout, 99)
         return VsaProblem(self.B, self.heads, self.T, self.H, self.W, self.head_dim, code,
-                          float(self.scale), self.topk, self.list_stride, pool, layout, *self.cube)
+                          float(self.scale), self.topk, self.list_stride, pool, layout, *self.cube,
+                          *(self.kcube if self.kcube is not None else (0, 0, 0)))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -152,8 +167,9 @@ def pad(p: Problem, x):
     return out
 
 
-def _pooled(p: Problem):
-    return (p.B, p.heads, p.Nc, p.head_dim)
+def _pooled(p: Problem, keys: bool = False):
+    """Shape of a pooled tensor: per query cube, or per key block with keys."""
+    return (p.B, p.heads, p.Nk if keys else p.Nc, p.head_dim)
 
 
 def forward(p: Problem, q, k, v, g_c=None, g_f=None, idx=None, lens=None, training: bool = False,
@@ -191,7 +207,7 @@ def saved_views(p: Problem, saved: torch.Tensor) -> dict:
         off += (n * esz + 255) // 256 * 256
         return t
 
-    out = {name: take(_pooled(p), torch.float32) for name in ("q_c", "k_c", "v_c", "o_c")}
+    out = {name: take(_pooled(p, name in ("k_c", "v_c")), torch.float32) for name in ("q_c", "k_c", "v_c", "o_c")}
     out["lse_c"] = take((p.B, p.heads, p.Nc), torch.float32)
     out["lse_f"] = take(_tokens(p), torch.float32)
     out["o_f"] = take(_raster(p), p.torch_dtype)
@@ -211,7 +227,7 @@ def backward(p: Problem, q, k, v, g_c, g_f, idx, lens, saved, d_o, ws: Optional[
 
 
 def pool(p: Problem, q, k, v, out=None):
-    qc, kc, vc = out if out is not None else (_empty(_pooled(p), torch.float32, q) for _ in range(3))
+    qc, kc, vc = out if out is not None else (_empty(_pooled(p, keys), torch.float32, q) for keys in (0, 1, 1))
     check(lib().vsa_pool(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(qc), _ptr(kc), _ptr(vc),
                          _stream(q.device)), "vsa_pool")
     return qc, kc, vc
@@ -275,7 +291,7 @@ def combine_backward(p: Problem, d_o, o_c, o_f, g_c=None, g_f=None):
 
 
 def index_transpose(p: Problem, idx, lens, ws: Optional[torch.Tensor] = None):
-    off = _empty((p.B, p.heads, p.Nc + 1), torch.int32, idx)
+    off = _empty((p.B, p.heads, p.Nk + 1), torch.int32, idx)
     k2q = _empty((p.B, p.heads, p.Nc * p.stride), torch.int32, idx)
     ws = workspace(p, idx, training=True) if ws is None else ws
     check(lib().vsa_index_transpose(ctypes.byref(p.c()), _ptr(idx), _ptr(lens), _ptr(off), _ptr(k2q), _ptr(ws),
@@ -294,7 +310,7 @@ def fine_backward(p: Problem, q, k, v, idx, lens, k2q_off, k2q, lse_f, d_o_f, de
 
 
 def coarse_backward(p: Problem, q_c, k_c, v_c, o_c, lse_c, d_o_c, ws: torch.Tensor):
-    dqc, dkc, dvc = (_empty(_pooled(p), torch.float32, q_c) for _ in range(3))
+    dqc, dkc, dvc = (_empty(_pooled(p, keys), torch.float32, q_c) for keys in (0, 1, 1))
     check(lib().vsa_coarse_backward(ctypes.byref(p.c()), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(o_c),
                                     _ptr(lse_c), _ptr(d_o_c), _ptr(dqc), _ptr(dkc), _ptr(dvc), _ptr(ws),
                                     ws.numel(), _stream(q_c.device)), "vsa_coarse_backward")

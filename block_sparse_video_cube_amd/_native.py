@@ -24,7 +24,8 @@ class VsaProblem(ctypes.Structure):
                 ("H", ctypes.c_int32), ("W", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("topk", ctypes.c_int32),
                 ("list_stride", ctypes.c_int32), ("pool_mode", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("cube_t", ctypes.c_int32), ("cube_h", ctypes.c_int32), ("cube_w", ctypes.c_int32)]
+                ("cube_t", ctypes.c_int32), ("cube_h", ctypes.c_int32), ("cube_w", ctypes.c_int32),
+                ("kcube_t", ctypes.c_int32), ("kcube_h", ctypes.c_int32), ("kcube_w", ctypes.c_int32)]
 
 
 _P = ctypes.POINTER(VsaProblem)

@@ -1,4 +1,4 @@
-// List utilities of the backward: the index transpose (for each key cube,
+// List utilities of the backward: the index transpose (for each key block,
 // the query cubes whose lists hold it) and the list validator.
 // The transposed lists are what the dK / dV walk of the fine backward
 // (fine_bwd.hip) consumes; the validator checks caller-supplied lists.
@@ -8,8 +8,8 @@ namespace vsa {
 
 // ------------------------------------------------------------ list helpers
 // Index transpose through a key-major bitmask: bit i of row j of `bits`
-// (W = ceil(Nc / 32) words per row) is set when query cube i lists key cube
-// j. Counting a row's bits gives the length of j's list, and walking them
+// (Nk rows of W = ceil(Nq / 32) words) is set when query cube i lists key
+// block j. Counting a row's bits gives the length of j's list, and walking them
 // writes it in ascending order, so the result is deterministic.
 __global__ __launch_bounds__(256) void k2q_zero_kernel(uint32_t* __restrict__ bits, long n) {
   for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long)gridDim.x * 256) bits[e] = 0u;
@@ -17,28 +17,28 @@ __global__ __launch_bounds__(256) void k2q_zero_kernel(uint32_t* __restrict__ bi
 
 __global__ __launch_bounds__(256) void k2q_bits_kernel(const int32_t* __restrict__ idx,
                                                        const int32_t* __restrict__ len, uint32_t* __restrict__ bits,
-                                                       int Nc, int stride, int W) {
+                                                       int Nq, int Nk, int stride, int W) {
   const long e = (long)blockIdx.x * 256 + threadIdx.x;   // entry of this head's lists
   const long bh = blockIdx.y;
-  if (e >= (long)Nc * stride) return;
+  if (e >= (long)Nq * stride) return;
   const int i = (int)(e / stride), t = (int)(e - (long)i * stride);
-  const long row = bh * Nc + i;
+  const long row = bh * Nq + i;
   if (t >= min(max(len[row], 0), stride)) return;
   const int j = idx[row * stride + t];
-  if (j < 0 || j >= Nc) return;
-  atomicOr(&bits[(bh * Nc + j) * W + (i >> 5)], 1u << (i & 31));
+  if (j < 0 || j >= Nk) return;
+  atomicOr(&bits[(bh * Nk + j) * W + (i >> 5)], 1u << (i & 31));
 }
 
 // cnt[bh][j + 1] = number of query cubes listing j (cnt[bh][0] is set by the scan).
 __global__ __launch_bounds__(256) void k2q_count_kernel(const uint32_t* __restrict__ bits, int32_t* __restrict__ cnt,
-                                                        int Nc, int W) {
+                                                        int Nk, int W) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   const long bh = blockIdx.y;
-  if (j >= Nc) return;
-  const uint32_t* r = bits + (bh * Nc + j) * W;
+  if (j >= Nk) return;
+  const uint32_t* r = bits + (bh * Nk + j) * W;
   int c = 0;
   for (int w = 0; w < W; ++w) c += __popc(r[w]);
-  cnt[bh * (Nc + 1) + j + 1] = c;
+  cnt[bh * (Nk + 1) + j + 1] = c;
 }
 
 // In place: off[bh][0] = 0, off[bh][j+1] = count of j  ->  exclusive offsets.
@@ -65,13 +65,13 @@ __global__ __launch_bounds__(256) void k2q_scan_kernel(int32_t* __restrict__ off
 
 __global__ __launch_bounds__(256) void k2q_fill_kernel(const uint32_t* __restrict__ bits,
                                                        const int32_t* __restrict__ off, int32_t* __restrict__ k2q,
-                                                       int Nc, int stride, int W) {
+                                                       int Nq, int Nk, int stride, int W) {
   const int j = blockIdx.x * 256 + threadIdx.x;
   const long bh = blockIdx.y;
-  if (j >= Nc) return;
-  const uint32_t* r = bits + (bh * Nc + j) * W;
-  int32_t* out = k2q + bh * (long)Nc * stride;
-  int pos = off[bh * (Nc + 1) + j];
+  if (j >= Nk) return;
+  const uint32_t* r = bits + (bh * Nk + j) * W;
+  int32_t* out = k2q + bh * (long)Nq * stride;
+  int pos = off[bh * (Nk + 1) + j];
   for (int w = 0; w < W; ++w) {
     uint32_t word = r[w];
     while (word != 0u) {
@@ -85,21 +85,21 @@ int k2q_bits_words(int Nc) { return (Nc + 31) / 32; }
 
 hipError_t launch_index_transpose(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* k2q_off,
                                   int32_t* k2q, uint32_t* bits) {
-  const int Nc = L.g.Nc, W = k2q_bits_words(Nc);
-  const long nbits = (long)L.BH * Nc * W;
+  const int Nq = L.g.Nc, Nk = L.gk.Nc, W = k2q_bits_words(Nq);
+  const long nbits = (long)L.BH * Nk * W;
   hipLaunchKernelGGL(k2q_zero_kernel, dim3((unsigned)min((nbits + 255) / 256, 65536L)), dim3(256), 0, L.stream,
                      bits, nbits);
-  const long entries = (long)Nc * L.stride;
+  const long entries = (long)Nq * L.stride;
   hipLaunchKernelGGL(k2q_bits_kernel, dim3((unsigned)((entries + 255) / 256), L.BH), dim3(256), 0, L.stream, idx,
-                     len, bits, Nc, L.stride, W);
-  const dim3 grid((Nc + 255) / 256, L.BH);
-  hipLaunchKernelGGL(k2q_count_kernel, grid, dim3(256), 0, L.stream, bits, k2q_off, Nc, W);
-  hipLaunchKernelGGL(k2q_scan_kernel, dim3(L.BH), dim3(256), 0, L.stream, k2q_off, Nc);
-  hipLaunchKernelGGL(k2q_fill_kernel, grid, dim3(256), 0, L.stream, bits, k2q_off, k2q, Nc, L.stride, W);
+                     len, bits, Nq, Nk, L.stride, W);
+  const dim3 grid((Nk + 255) / 256, L.BH);
+  hipLaunchKernelGGL(k2q_count_kernel, grid, dim3(256), 0, L.stream, bits, k2q_off, Nk, W);
+  hipLaunchKernelGGL(k2q_scan_kernel, dim3(L.BH), dim3(256), 0, L.stream, k2q_off, Nk);
+  hipLaunchKernelGGL(k2q_fill_kernel, grid, dim3(256), 0, L.stream, bits, k2q_off, k2q, Nq, Nk, L.stride, W);
   return hipGetLastError();
 }
 
-// Lists valid? len in [0, stride], ids in [0, Nc), strictly increasing.
+// Lists valid? len in [0, stride], ids in [0, Nk), strictly increasing.
 __global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict__ idx,
                                                        const int32_t* __restrict__ len, int32_t* flag, long rows,
                                                        int Nc, int stride) {
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict
 hipError_t launch_validate_lists(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* flag) {
   const long rows = (long)L.BH * L.g.Nc;
   hipLaunchKernelGGL(validate_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, L.stream, idx, len,
-                     flag, rows, L.g.Nc, L.stride);
+                     flag, rows, L.gk.Nc, L.stride);
   return hipGetLastError();
 }
 

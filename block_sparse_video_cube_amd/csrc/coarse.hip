@@ -18,9 +18,9 @@
 //                     softmax applied to the operand as it is staged).
 // The backward of the coarse attention is here too; it shares these GEMMs.
 // Selecting on the logits picks the same set as selecting on A_c: the
-// softmax is increasing within a row. S_c is Nc^2 fp32 per (b, h) of
-// workspace (rows padded to a multiple of 4 floats), written once and read
-// twice (279 MB at the 720p latent).
+// softmax is increasing within a row. S_c is Nq x Nk fp32 per (b, h) of
+// workspace (Nq query cubes, Nk key blocks; rows padded to a multiple of 4
+// floats), written once and read twice (279 MB at the 720p latent).
 #include "vsa_kernels.h"
 
 namespace vsa {
@@ -38,18 +38,18 @@ __device__ __forceinline__ uint32_t fkey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One wave's 64x64 block of an "NT" product C = A B^T with A, B row-major
-// [Nc][D] (fp32 16x16x4 MFMAs, 4x4 blocks). Lane (r = lane%16, g = lane/16)
+// One wave's 64x64 block of an "NT" product C = A B^T with A [Na][D] and
+// B [Nb][D] row-major (fp32 16x16x4 MFMAs, 4x4 blocks). Lane (r = lane%16, g = lane/16)
 // holds, for channel group t, the float4 A[row r][16t + 4g .. +3] (and
 // likewise B), so four lanes cover 64 contiguous bytes of a row; k-step 4t+e
 // contracts channel 16t + 4g + e. With NBUF = 2 channel groups are
 // double-buffered in registers (the next group loads while this one's 64
 // MFMAs run); NBUF = 1 loads each group just before its MFMAs, 32 registers
-// fewer. Rows beyond Nc read as zero. acc[i][j][e] is
+// fewer. Rows beyond Na (of A) or Nb (of B) read as zero. acc[i][j][e] is
 // C[m0 + 16i + 4g + e][n0 + 16j + r].
 template <int D, int NBUF = 2>
-__device__ __forceinline__ void nt_block64(const float* __restrict__ A, const float* __restrict__ B, int Nc,
-                                           int m0, int n0, f32x4 acc[4][4]) {
+__device__ __forceinline__ void nt_block64(const float* __restrict__ A, const float* __restrict__ B, int Na,
+                                           int Nb, int m0, int n0, f32x4 acc[4][4]) {
   constexpr int KT = D / 16;
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   float4 av[NBUF][4], bv[NBUF][4];
@@ -57,9 +57,9 @@ __device__ __forceinline__ void nt_block64(const float* __restrict__ A, const fl
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ra = m0 + 16 * i + r, rb = n0 + 16 * i + r;
-      av[buf][i] = ra < Nc ? *reinterpret_cast<const float4*>(A + (long)ra * D + 16 * t + 4 * g)
+      av[buf][i] = ra < Na ? *reinterpret_cast<const float4*>(A + (long)ra * D + 16 * t + 4 * g)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
-      bv[buf][i] = rb < Nc ? *reinterpret_cast<const float4*>(B + (long)rb * D + 16 * t + 4 * g)
+      bv[buf][i] = rb < Nb ? *reinterpret_cast<const float4*>(B + (long)rb * D + 16 * t + 4 * g)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
@@ -87,37 +87,38 @@ __device__ __forceinline__ void nt_block64(const float* __restrict__ A, const fl
   }
 }
 
-// S[bh][i][j] = scale * Q_c[i] . K_c[j]; a workgroup of 4 waves owns a
-// 128x128 tile, each wave a 64x64 quarter.
+// S[bh][i][j] = scale * Q_c[i] . K_c[j] over Nq query cubes and Nk key
+// blocks; a workgroup of 4 waves owns a 128x128 tile, each wave a 64x64
+// quarter.
 template <int D>
 __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restrict__ qc,
                                                             const float* __restrict__ kc, float* __restrict__ s,
-                                                            int Nc, int ld, float scale) {
+                                                            int Nq, int Nk, int ld, float scale) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const long bh = blockIdx.z;
   const int m0 = blockIdx.y * 128 + (w >> 1) * 64, n0 = blockIdx.x * 128 + (w & 1) * 64;
-  if (m0 >= Nc || n0 >= Nc) return;   // wave-uniform; no barrier in this kernel
+  if (m0 >= Nq || n0 >= Nk) return;   // wave-uniform; no barrier in this kernel
   f32x4 acc[4][4];
-  nt_block64<D>(qc + bh * (long)Nc * D, kc + bh * (long)Nc * D, Nc, m0, n0, acc);
-  float* S = s + bh * (long)Nc * ld;
+  nt_block64<D>(qc + bh * (long)Nq * D, kc + bh * (long)Nk * D, Nq, Nk, m0, n0, acc);
+  float* S = s + bh * (long)Nq * ld;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + 16 * j + r;
-      if (col >= Nc) continue;
+      if (col >= Nk) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = m0 + 16 * i + 4 * g + e;
-        if (row < Nc) S[(long)row * ld + col] = acc[i][j][e] * scale;
+        if (row < Nq) S[(long)row * ld + col] = acc[i][j][e] * scale;
       }
     }
 }
 
-// C[bh][i][:] = scale * sum_j A[i][j] B[j][:] over an Nc x Nc fp32 matrix M
-// (row pitch ld) and B [Nc][D]: A = M, or A = M^T with TRANS_A, and with EXP
-// A[i][j] = exp(M[i][j] - lse[i]) (the coarse softmax applied as the tile is
-// staged). A workgroup owns 32 rows of C and every channel; k goes in chunks
+// C[bh][i][:] = scale * sum_j A[i][j] B[j][:] for i < R, j < Kd, with B
+// [Kd][D] and A = M (M is R x Kd) or A = M^T with TRANS_A (M is Kd x R);
+// M is fp32 with row pitch ld. With EXP A[i][j] = exp(M[i][j] - lse[i]) (the
+// coarse softmax applied as the tile is staged). A workgroup owns 32 rows of C and every channel; k goes in chunks
 // of 32 through LDS, double buffered: the A tile row-major and the B tile
 // transposed (channel-major), so that for 16x16x4 MFMA k-step s a lane of
 // lane group g contracts k = 8g + s and reads its eight A values and eight B
@@ -128,8 +129,8 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
 // keeps their 32-bank windows disjoint).
 template <int D, bool TRANS_A, bool EXP>
 __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restrict__ m, const float* __restrict__ lse,
-                                                          const float* __restrict__ b, float* __restrict__ c, int Nc,
-                                                          int ld, float scale) {
+                                                          const float* __restrict__ b, float* __restrict__ c, int R,
+                                                          int Kd, int ld, float scale) {
   constexpr int KC = 32, RP = KC + 4;           // k per chunk, LDS row pitch of A (floats)
   constexpr int BRP = KC + 8;                    // LDS row pitch of the transposed B tile
   constexpr int CB = D / 64;                     // 16-channel blocks per wave
@@ -140,45 +141,45 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const long bh = blockIdx.y;
   const int r0 = blockIdx.x * 32;
-  const float* M = m + bh * (long)Nc * ld;
-  const float* Bm = b + bh * (long)Nc * D;
+  const float* M = m + bh * (long)(TRANS_A ? Kd : R) * ld;
+  const float* Bm = b + bh * (long)Kd * D;
   // A staging role: without TRANS_A, row ai of the tile, k = 4aq .. 4aq+3
   // (M[r0 + ai][k0 + 4aq ..]); with TRANS_A, k = ai of the chunk and tile rows
   // 4aq .. 4aq+3 (M[k0 + ai][r0 + 4aq ..]), written transposed.
   const int ai = tid >> 3, aq = tid & 7;
-  const bool arow = r0 + ai < Nc;
-  const float alse = (EXP && arow) ? lse[bh * Nc + r0 + ai] : 0.f;
+  const bool arow = r0 + ai < R;
+  const float alse = (EXP && arow) ? lse[bh * R + r0 + ai] : 0.f;
   float4 ar, br[BF4];
   auto load = [&](int k0) {
     ar = make_float4(0.f, 0.f, 0.f, 0.f);
     if (!TRANS_A) {
       const int kk = k0 + 4 * aq;
-      if (arow && kk < Nc) {
+      if (arow && kk < Kd) {
         ar = *reinterpret_cast<const float4*>(M + (long)(r0 + ai) * ld + kk);   // ld % 4 == 0
         if (EXP) {
           ar.x = __expf(ar.x - alse);
-          ar.y = kk + 1 < Nc ? __expf(ar.y - alse) : 0.f;
-          ar.z = kk + 2 < Nc ? __expf(ar.z - alse) : 0.f;
-          ar.w = kk + 3 < Nc ? __expf(ar.w - alse) : 0.f;
+          ar.y = kk + 1 < Kd ? __expf(ar.y - alse) : 0.f;
+          ar.z = kk + 2 < Kd ? __expf(ar.z - alse) : 0.f;
+          ar.w = kk + 3 < Kd ? __expf(ar.w - alse) : 0.f;
         } else {
-          if (kk + 1 >= Nc) ar.y = 0.f;
-          if (kk + 2 >= Nc) ar.z = 0.f;
-          if (kk + 3 >= Nc) ar.w = 0.f;
+          if (kk + 1 >= Kd) ar.y = 0.f;
+          if (kk + 2 >= Kd) ar.z = 0.f;
+          if (kk + 3 >= Kd) ar.w = 0.f;
         }
       }
     } else {
       const int kk = k0 + ai, cc = r0 + 4 * aq;
-      if (kk < Nc && cc < Nc) {
+      if (kk < Kd && cc < R) {
         ar = *reinterpret_cast<const float4*>(M + (long)kk * ld + cc);
-        if (cc + 1 >= Nc) ar.y = 0.f;
-        if (cc + 2 >= Nc) ar.z = 0.f;
-        if (cc + 3 >= Nc) ar.w = 0.f;
+        if (cc + 1 >= R) ar.y = 0.f;
+        if (cc + 2 >= R) ar.z = 0.f;
+        if (cc + 3 >= R) ar.w = 0.f;
       }
     }
 #pragma unroll
     for (int j = 0; j < BF4; ++j) {
       const int f = tid + 256 * j, kap = f % KC, c4 = f / KC;
-      br[j] = k0 + kap < Nc ? *reinterpret_cast<const float4*>(Bm + (long)(k0 + kap) * D + 4 * c4)
+      br[j] = k0 + kap < Kd ? *reinterpret_cast<const float4*>(Bm + (long)(k0 + kap) * D + 4 * c4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nchunk = (Nc + KC - 1) / KC;
+  const int nchunk = (Kd + KC - 1) / KC;
   load(0);
   store(0);
   __syncthreads();
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
       __syncthreads();
     }
   }
-  float* C = c + bh * (long)Nc * D;
+  float* C = c + bh * (long)R * D;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = r0 + 16 * rb + 4 * g + e;
-        if (row < Nc) C[(long)row * D + col] = scale * acc[rb][cb][e];
+        if (row < R) C[(long)row * D + col] = scale * acc[rb][cb][e];
       }
     }
 }
@@ -259,24 +260,24 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
 // the most significant bit in which the row's keys differ (the bits above it
 // are shared by every key, and skipping them keeps the first histogram
 // spread over many buckets, so the LDS atomics rarely collide). Then every
-// key above it and the first (K - #above) keys equal to it, in ascending cube
-// order, are taken.
+// key above it and the first (K - #above) keys equal to it, in ascending
+// key-block order, are taken.
 template <int NCH>
 __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restrict__ s, float* __restrict__ lse,
                                                           int32_t* __restrict__ idx, int32_t* __restrict__ len,
-                                                          long rows, int Nc, int ld, int topk, int stride) {
+                                                          long rows, int Nk, int ld, int topk, int stride) {
   __shared__ int hist_all[4][256];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + w;
   if (row >= rows) return;   // wave-uniform; no block barrier below
   const float* srow = s + row * ld;
-  const int nused = (Nc + 63) >> 6;   // register slots holding any cube
+  const int nused = (Nk + 63) >> 6;   // register slots holding any key block
   float v[NCH];
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < NCH; ++t) {
     const int j = t * 64 + lane;
-    v[t] = j < Nc ? srow[j] : -INFINITY;
+    v[t] = j < Nk ? srow[j] : -INFINITY;
     mx = fmaxf(mx, v[t]);
   }
   mx = wave_max(mx);
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
   uint32_t kmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int t = 0; t < NCH; ++t) {
-    const bool valid = t * 64 + lane < Nc;
+    const bool valid = t * 64 + lane < Nk;
     key[t] = valid ? fkey(v[t]) : 0u;
     if (valid) kmin = min(kmin, key[t]);
   }
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
 #pragma unroll
     for (int t = 0; t < NCH; ++t) {
       if (t >= nused) break;
-      if ((t * 64 + lane) < Nc && (key[t] & pmask) == prefix) atomicAdd(&h[(key[t] >> shift) & dmask], 1);
+      if ((t * 64 + lane) < Nk && (key[t] & pmask) == prefix) atomicAdd(&h[(key[t] >> shift) & dmask], 1);
     }
     wave_sync();
     const int b0 = h[4 * lane], b1 = h[4 * lane + 1], b2 = h[4 * lane + 2], b3 = h[4 * lane + 3];
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
   for (int t = 0; t < NCH; ++t) {
     if (t >= nused) break;
     const int j = t * 64 + lane;
-    const bool valid = j < Nc;
+    const bool valid = j < Nk;
     const bool gt = valid && key[t] > prefix;
     const bool eq = valid && key[t] == prefix;
     const uint64_t beq = __ballot(eq);
@@ -373,43 +374,45 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
 
 int coarse_max_cubes() { return kCoarseMaxCubes; }
 
-// C = scale * op(M) B, see coarse_gemm_kernel.
+// C = scale * op(M) B with R output rows and Kd contracted; M is the
+// Nq x Nk coarse matrix (pitch coarse_ld(Nk)), see coarse_gemm_kernel.
 template <bool TRANS_A, bool EXP>
-static void launch_gemm(const Launch& L, const float* m, const float* lse, const float* b, float* c, float scale) {
-  const int Nc = L.g.Nc, ld = coarse_ld(Nc);
-  const dim3 grid((Nc + 31) / 32, L.BH);
+static void launch_gemm(const Launch& L, const float* m, const float* lse, const float* b, float* c, int R, int Kd,
+                        float scale) {
+  const int ld = coarse_ld(L.gk.Nc);
+  const dim3 grid((R + 31) / 32, L.BH);
   if (L.D == 64)
-    hipLaunchKernelGGL((coarse_gemm_kernel<64, TRANS_A, EXP>), grid, dim3(256), 0, L.stream, m, lse, b, c, Nc, ld,
-                       scale);
-  else
-    hipLaunchKernelGGL((coarse_gemm_kernel<128, TRANS_A, EXP>), grid, dim3(256), 0, L.stream, m, lse, b, c, Nc,
+    hipLaunchKernelGGL((coarse_gemm_kernel<64, TRANS_A, EXP>), grid, dim3(256), 0, L.stream, m, lse, b, c, R, Kd,
                        ld, scale);
+  else
+    hipLaunchKernelGGL((coarse_gemm_kernel<128, TRANS_A, EXP>), grid, dim3(256), 0, L.stream, m, lse, b, c, R,
+                       Kd, ld, scale);
 }
-int coarse_ld(int Nc) { return (Nc + 3) & ~3; }
+int coarse_ld(int Nk) { return (Nk + 3) & ~3; }
 
+// One wave per query cube; each row has Nk key-block logits.
 template <int NCH>
 static void launch_rows(const Launch& L, const float* s, float* lse, int32_t* idx, int32_t* len) {
   const long rows = (long)L.BH * L.g.Nc;
   hipLaunchKernelGGL((coarse_rows_kernel<NCH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream, s, lse,
-                     idx, len, rows, L.g.Nc, coarse_ld(L.g.Nc), L.topk, L.stride);
+                     idx, len, rows, L.gk.Nc, coarse_ld(L.gk.Nc), L.topk, L.stride);
 }
 
 hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, const float* vc, float* oc,
                          float* lse, int32_t* idx, int32_t* len, float* s_scratch) {
-  const int Nc = L.g.Nc, ld = coarse_ld(Nc);
-  const int t128 = (Nc + 127) / 128;
-  const dim3 block(256);
+  const int Nq = L.g.Nc, Nk = L.gk.Nc, ld = coarse_ld(Nk);
+  const dim3 tiles((Nk + 127) / 128, (Nq + 127) / 128, L.BH), block(256);
   if (L.D == 64)
-    hipLaunchKernelGGL((coarse_scores_kernel<64>), dim3(t128, t128, L.BH), block, 0, L.stream, qc, kc, s_scratch,
-                       Nc, ld, L.scale);
+    hipLaunchKernelGGL((coarse_scores_kernel<64>), tiles, block, 0, L.stream, qc, kc, s_scratch, Nq, Nk, ld,
+                       L.scale);
   else
-    hipLaunchKernelGGL((coarse_scores_kernel<128>), dim3(t128, t128, L.BH), block, 0, L.stream, qc, kc, s_scratch,
-                       Nc, ld, L.scale);
-  if (Nc <= 256) launch_rows<4>(L, s_scratch, lse, idx, len);
-  else if (Nc <= 512) launch_rows<8>(L, s_scratch, lse, idx, len);
-  else if (Nc <= 1024) launch_rows<16>(L, s_scratch, lse, idx, len);
+    hipLaunchKernelGGL((coarse_scores_kernel<128>), tiles, block, 0, L.stream, qc, kc, s_scratch, Nq, Nk, ld,
+                       L.scale);
+  if (Nk <= 256) launch_rows<4>(L, s_scratch, lse, idx, len);
+  else if (Nk <= 512) launch_rows<8>(L, s_scratch, lse, idx, len);
+  else if (Nk <= 1024) launch_rows<16>(L, s_scratch, lse, idx, len);
   else launch_rows<32>(L, s_scratch, lse, idx, len);
-  launch_gemm<false, true>(L, s_scratch, lse, vc, oc, 1.0f);
+  launch_gemm<false, true>(L, s_scratch, lse, vc, oc, Nq, Nk, 1.0f);
   return hipGetLastError();
 }
 
@@ -442,31 +445,31 @@ __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_kernel(const float* __r
                                                              const float* __restrict__ vc, const float* __restrict__ doc,
                                                              const float* __restrict__ lse, const float* __restrict__ dc,
                                                              float* __restrict__ pbuf, float* __restrict__ dsbuf,
-                                                             int Nc, int ld, float scale) {
+                                                             int Nq, int Nk, int ld, float scale) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const long bh = blockIdx.z;
   const int m0 = blockIdx.y * 128 + (w >> 1) * 64, n0 = blockIdx.x * 128 + (w & 1) * 64;
-  if (m0 >= Nc || n0 >= Nc) return;   // wave-uniform; no barrier in this kernel
-  const long base = bh * (long)Nc * D;
+  if (m0 >= Nq || n0 >= Nk) return;   // wave-uniform; no barrier in this kernel
+  const long qbase = bh * (long)Nq * D, kbase = bh * (long)Nk * D;
   f32x4 sacc[4][4], pacc[4][4];
-  nt_block64<D>(qc + base, kc + base, Nc, m0, n0, sacc);
+  nt_block64<D>(qc + qbase, kc + kbase, Nq, Nk, m0, n0, sacc);
   // The second product's loads start after the first product's MFMAs, so
   // only one set of operand buffers is live (two waves per SIMD).
   __builtin_amdgcn_sched_barrier(0);
-  nt_block64<D, 1>(doc + base, vc + base, Nc, m0, n0, pacc);
-  float* P = pbuf + bh * (long)Nc * ld;
-  float* DS = dsbuf + bh * (long)Nc * ld;
+  nt_block64<D, 1>(doc + qbase, vc + kbase, Nq, Nk, m0, n0, pacc);
+  float* P = pbuf + bh * (long)Nq * ld;
+  float* DS = dsbuf + bh * (long)Nq * ld;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = m0 + 16 * i + 4 * g + e;
-      if (row >= Nc) continue;
-      const float l = lse[bh * Nc + row], dd = dc[bh * Nc + row];
+      if (row >= Nq) continue;
+      const float l = lse[bh * Nq + row], dd = dc[bh * Nq + row];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = n0 + 16 * j + r;
-        if (col >= Nc) continue;
+        if (col >= Nk) continue;
         const float pv = __expf(sacc[i][j][e] * scale - l);
         P[(long)row * ld + col] = pv;
         DS[(long)row * ld + col] = pv * (pacc[i][j][e] - dd);
@@ -477,23 +480,23 @@ __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_kernel(const float* __r
 hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, const float* vc,
                              const float* oc, const float* lse, const float* doc, float* dqc, float* dkc,
                              float* dvc, float* ds_scratch, float* p_scratch, float* dc_scratch) {
-  const int Nc = L.g.Nc, ld = coarse_ld(Nc);
-  const long rows = (long)L.BH * Nc;
-  const int t128 = (Nc + 127) / 128;
+  const int Nq = L.g.Nc, Nk = L.gk.Nc, ld = coarse_ld(Nk);
+  const long rows = (long)L.BH * Nq;
+  const dim3 tiles((Nk + 127) / 128, (Nq + 127) / 128, L.BH);
   if (L.D == 64) {
     hipLaunchKernelGGL((coarse_bwd_delta_kernel<64>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream, doc,
                        oc, dc_scratch, rows);
-    hipLaunchKernelGGL((coarse_bwd_pds_kernel<64>), dim3(t128, t128, L.BH), dim3(256), 0, L.stream, qc, kc, vc, doc,
-                       lse, dc_scratch, p_scratch, ds_scratch, Nc, ld, L.scale);
+    hipLaunchKernelGGL((coarse_bwd_pds_kernel<64>), tiles, dim3(256), 0, L.stream, qc, kc, vc, doc, lse, dc_scratch,
+                       p_scratch, ds_scratch, Nq, Nk, ld, L.scale);
   } else {
     hipLaunchKernelGGL((coarse_bwd_delta_kernel<128>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream,
                        doc, oc, dc_scratch, rows);
-    hipLaunchKernelGGL((coarse_bwd_pds_kernel<128>), dim3(t128, t128, L.BH), dim3(256), 0, L.stream, qc, kc, vc, doc,
-                       lse, dc_scratch, p_scratch, ds_scratch, Nc, ld, L.scale);
+    hipLaunchKernelGGL((coarse_bwd_pds_kernel<128>), tiles, dim3(256), 0, L.stream, qc, kc, vc, doc, lse, dc_scratch,
+                       p_scratch, ds_scratch, Nq, Nk, ld, L.scale);
   }
-  launch_gemm<false, false>(L, ds_scratch, nullptr, kc, dqc, L.scale);
-  launch_gemm<true, false>(L, ds_scratch, nullptr, qc, dkc, L.scale);
-  launch_gemm<true, false>(L, p_scratch, nullptr, doc, dvc, 1.0f);
+  launch_gemm<false, false>(L, ds_scratch, nullptr, kc, dqc, Nq, Nk, L.scale);   // dQ_c = s dS K_c
+  launch_gemm<true, false>(L, ds_scratch, nullptr, qc, dkc, Nk, Nq, L.scale);    // dK_c = s dS^T Q_c
+  launch_gemm<true, false>(L, p_scratch, nullptr, doc, dvc, Nk, Nq, 1.0f);       // dV_c = P^T dO_c
   return hipGetLastError();
 }
 

@@ -7,15 +7,17 @@
 //   dV = P^T dO, dP = dO V^T, dS = P * (dP - delta), delta = rowsum(dO * O),
 //   dQ = s * dS K, dK = s * dS^T Q,
 // and the mean-pool spreads dX_c[c] / Bt over the cube's Bt tokens (the
-// max-pool variant sends it to the cube's maximum), added here.
+// max-pool variant sends it to the cube's maximum), added here. Key blocks
+// may have their own shape (Bk tokens); everything below that says "key
+// cube" means a key block then.
 //
 // Two kernels, both deterministic (no atomics), in the style of the forward:
-// a workgroup of NW = Bt/32 waves owns one cube, wave w its tokens
+// a workgroup of NW = Bt/32 (or Bk/32) waves owns one cube, wave w its tokens
 // 32w .. 32w+31, one per lane (column) of 32x32x16 bf16 MFMAs, and walks a
 // list of partner cubes in 32-token chunks: row tiles of the partner's
 // tensors staged in LDS by direct-to-LDS loads (each wave issues 1/NW; the
-// next chunk loads while this one is computed). The transposed operands come from the same row
-// tiles through LDS transpose reads.
+// next chunk loads while this one is computed). The transposed operands come
+// from the same row tiles through LDS transpose reads.
 //  * dQ, per query cube i over its list of key cubes (the forward's list):
 //      S^T = K_c Q^T, dP^T = V_c dO^T        A = K / V row tiles, B = the
 //                                            lane's Q / dO row (registers)
@@ -51,10 +53,11 @@ __device__ __forceinline__ void pooled_grad(const float* dxc, const uint8_t* arg
   }
 }
 
-// Processing order of the key cubes of every (b, h) for the dK / dV kernel:
-// descending length of their transposed lists, ties by cube id, so the
-// longest walks start first. One workgroup per (b, h): a bitonic sort of
-// ((Nc - count) << 32 | cube) keys in LDS.
+// Processing order of the Nc key cubes of every (b, h) for the dK / dV
+// kernel: descending length of their transposed lists, ties by cube id, so
+// the longest walks start first. One workgroup per (b, h): a bitonic sort of
+// ((Nc - count) << 32 | cube) keys in LDS (a count never exceeds the number
+// of query cubes, so the clamp at 0 only orders malformed offsets).
 __global__ __launch_bounds__(1024) void order_by_count_kernel(const int32_t* __restrict__ k2q_off,
                                                               int32_t* __restrict__ order, int Nc, int pow2) {
   __shared__ unsigned long long key[2048];
@@ -91,8 +94,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
     const float* __restrict__ lse_f, const bf16* __restrict__ dof, const float* __restrict__ delta,
-    const float* __restrict__ dqc, const uint8_t* __restrict__ qarg, bf16* __restrict__ dq, Grid g, int stride,
-    float scale) {
+    const float* __restrict__ dqc, const uint8_t* __restrict__ qarg, bf16* __restrict__ dq, Grid g, Grid gk,
+    int stride, float scale) {
   using G = ChunkGeom<D>;
   __shared__ __attribute__((aligned(16))) bf16 rk[2][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rv[2][G::RUNITS * 8];
@@ -125,15 +128,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
 
+  // Key chunks: key block list[c >> ksh], its chunk h = c & kmask.
+  const int ksh = chunk_shift(gk), kmask = (1 << ksh) - 1;
   uint32_t roff[G::RINS / NW];
-  row_tile_offsets<D, NW>(g, wv, lane, roff);
+  row_tile_offsets<D, NW>(gk, wv, lane, roff);
   uint32_t toffs[G::MB][2][2];   // transposed reads of the K row tile (dQ^T += K^T dS^T)
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, toffs[mb][s2]);
-  // Bytes from a cube's first row to the first row of its chunk h.
-  auto chunk_bytes = [&](int h) { return NW == 1 ? 0u : (uint32_t)(chunk_first(g, h) * D) * 2u; };
+  // Bytes from a key block's first row to the first row of its chunk h.
+  auto chunk_bytes = [&](int h) { return (uint32_t)(chunk_first(gk, h) * D) * 2u; };
   const char* Kb = reinterpret_cast<const char*>(k + tok0 * D);
   const char* Vb = reinterpret_cast<const char*>(v + tok0 * D);
   // Byte offsets of the list's cubes, 64 entries at a time, one per lane.
@@ -141,12 +146,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
   auto cubes = [&](int t0) {
     const int t = t0 + lane;
     int j = t < L ? list[t] : 0;
-    j = (j >= 0 && j < g.Nc) ? j : 0;
-    rcube = (uint32_t)cube_first(g, j) * (uint32_t)(D * 2);
+    j = (j >= 0 && j < gk.Nc) ? j : 0;
+    rcube = (uint32_t)cube_first(gk, j) * (uint32_t)(D * 2);
   };
   const uint32_t rkb = lds_addr(rk), rvb = lds_addr(rv);
   auto issue = [&](int c) {
-    const int e = c / NW, h = c % NW, st = c & 1;
+    const int e = c >> ksh, h = c & kmask, st = c & 1;
     if ((e & 63) == 0 && h == 0) cubes(e);
     const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + chunk_bytes(h);
     issue_row_tile<D, NW>(uniform_ptr(Kb + rc), roff, rkb + st * (G::RUNITS * 16), wv);
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
   // Per chunk: wait for this wave's loads, barrier (every wave's share is in
   // LDS and every wave is done with the other stage), issue the next chunk,
   // compute this one.
-  const int nch = NW * L;
+  const int nch = L << ksh;
   if (nch > 0) issue(0);
   for (int c = 0; c < nch; ++c) {
     wait_vmcnt<0>();
@@ -211,6 +216,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
     }
 }
 
+// In both dK / dV kernels g is the grid of key blocks (the workgroup's own
+// tokens) and gq the grid of query cubes (the partners walked).
+//
 // dK and dV at 64 channels: every wave computes both for its 32 keys, two
 // waves per SIMD. (At 128 channels the two accumulators, 128 registers, and
 // the lane's K and V rows do not fit 256 registers without spills; the
@@ -222,7 +230,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
     const bf16* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dkc,
     const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
-    bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, int stride, float scale) {
+    bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, Grid gq, int stride, float scale) {
   using G = ChunkGeom<D>;
   __shared__ __attribute__((aligned(16))) bf16 rq[2][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rd[2][G::RUNITS * 8];
@@ -237,8 +245,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
   const int j = order != nullptr ? order[slot] : slot - bh * g.Nc;
   const long tok0 = (long)bh * g.N;
   const int32_t* offs = k2q_off + (long)bh * (g.Nc + 1);
-  const int t0 = min(max(offs[j], 0), g.Nc * stride), t1 = min(max(offs[j + 1], t0), g.Nc * stride);
-  const int32_t* list = k2q + (long)bh * g.Nc * stride + t0;
+  const int t0 = min(max(offs[j], 0), gq.Nc * stride), t1 = min(max(offs[j + 1], t0), gq.Nc * stride);
+  const int32_t* list = k2q + (long)bh * gq.Nc * stride + t0;
   const int L = t1 - t0;
 
   // This lane's key: in-cube token 32wv + n32 of cube j.
@@ -256,15 +264,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) { adk[mb][e] = 0.f; adv[mb][e] = 0.f; }
 
+  // Query chunks: query cube list[c >> qsh], its chunk h = c & qmask.
+  const int qsh = chunk_shift(gq), qmask = (1 << qsh) - 1;
   uint32_t roff[G::RINS / NW];
-  row_tile_offsets<D, NW>(g, wv, lane, roff);
+  row_tile_offsets<D, NW>(gq, wv, lane, roff);
   uint32_t toffs[G::MB][2][2];   // transposed reads of the Q / dO row tiles
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, toffs[mb][s2]);
-  // Bytes from a cube's first row to the first row of its chunk h.
-  auto chunk_bytes = [&](int h) { return NW == 1 ? 0u : (uint32_t)(chunk_first(g, h) * D) * 2u; };
   const char* Qb = reinterpret_cast<const char*>(q + tok0 * D);
   const char* Db = reinterpret_cast<const char*>(dof + tok0 * D);
   const char* Lb = reinterpret_cast<const char*>(lse_f + tok0);
@@ -274,17 +282,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
   auto cubes = [&](int e0) {
     const int t = e0 + lane;
     int ii = t < L ? list[t] : 0;
-    ii = (ii >= 0 && ii < g.Nc) ? ii : 0;
-    rcube = cube_first(g, ii);
+    ii = (ii >= 0 && ii < gq.Nc) ? ii : 0;
+    rcube = cube_first(gq, ii);
   };
   const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd), rlb = lds_addr(rls), reb = lds_addr(rdl);
   // Rows 4t .. 4t+3 of a chunk are consecutive in memory (Cw >= 4): lane t
   // < 8 of wave 0 moves them for LSE (and delta) with one 16-byte load.
-  const uint32_t soff = (uint32_t)chunk_row(g, 4 * (lane & 7)) * 4u;
+  const uint32_t soff = (uint32_t)chunk_row(gq, 4 * (lane & 7)) * 4u;
   auto issue = [&](int c) {
-    const int e = c / NW, h = c % NW, st = c & 1;
+    const int e = c >> qsh, h = c & qmask, st = c & 1;
     if ((e & 63) == 0 && h == 0) cubes(e);
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(rcube, e & 63) + (uint32_t)chunk_first(g, h);
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(rcube, e & 63) + (uint32_t)chunk_first(gq, h);
     const uint32_t rc = r0 * (uint32_t)(D * 2);
     issue_row_tile<D, NW>(uniform_ptr(Qb + rc), roff, rqb + st * (G::RUNITS * 16), wv);
     issue_row_tile<D, NW>(uniform_ptr(Db + rc), roff, rdb + st * (G::RUNITS * 16), wv);
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     }
   };
 
-  const int nch = NW * L;
+  const int nch = L << qsh;
   if (nch > 0) issue(0);
   for (int c = 0; c < nch; ++c) {
     wait_vmcnt<0>();
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
     const bf16* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dkc,
     const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
-    bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, int stride, float scale) {
+    bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, Grid gq, int stride, float scale) {
   using G = ChunkGeom<D>;
   constexpr int NWT = 2 * NW;   // waves in the workgroup
   static_assert(G::RINS % NWT == 0, "every wave issues whole 1 KB loads");
@@ -394,8 +402,8 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   const int j = order != nullptr ? order[slot] : slot - bh * g.Nc;
   const long tok0 = (long)bh * g.N;
   const int32_t* offs = k2q_off + (long)bh * (g.Nc + 1);
-  const int t0 = min(max(offs[j], 0), g.Nc * stride), t1 = min(max(offs[j + 1], t0), g.Nc * stride);
-  const int32_t* list = k2q + (long)bh * g.Nc * stride + t0;
+  const int t0 = min(max(offs[j], 0), gq.Nc * stride), t1 = min(max(offs[j + 1], t0), gq.Nc * stride);
+  const int32_t* list = k2q + (long)bh * gq.Nc * stride + t0;
   const int L = t1 - t0;
 
   // This lane's key: in-cube token 32kw + n32 of cube j.
@@ -413,8 +421,9 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
 
+  const int qsh = chunk_shift(gq), qmask = (1 << qsh) - 1;
   uint32_t roff[G::RINS / NWT];
-  row_tile_offsets<D, NWT>(g, wv, lane, roff);
+  row_tile_offsets<D, NWT>(gq, wv, lane, roff);
   uint32_t toffs[G::MB][2][2];   // transposed reads of the Q / dO row tiles
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
@@ -428,16 +437,16 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   auto cubes = [&](int e0) {
     const int t = e0 + lane;
     int ii = t < L ? list[t] : 0;
-    ii = (ii >= 0 && ii < g.Nc) ? ii : 0;
-    rcube = cube_first(g, ii);
+    ii = (ii >= 0 && ii < gq.Nc) ? ii : 0;
+    rcube = cube_first(gq, ii);
   };
   const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd), rlb = lds_addr(rls), reb = lds_addr(rdl);
-  const uint32_t soff = (uint32_t)chunk_row(g, 4 * (lane & 7)) * 4u;
-  // Query chunks: query cube list[e], its chunk h (NW chunks per cube).
+  const uint32_t soff = (uint32_t)chunk_row(gq, 4 * (lane & 7)) * 4u;
+  // Query chunks: query cube list[c >> qsh], its chunk h = c & qmask.
   auto issue = [&](int c) {
-    const int e = c / NW, h = c % NW, st = c & 1;
+    const int e = c >> qsh, h = c & qmask, st = c & 1;
     if ((e & 63) == 0 && h == 0) cubes(e);
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(rcube, e & 63) + (uint32_t)chunk_first(g, h);
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(rcube, e & 63) + (uint32_t)chunk_first(gq, h);
     const uint32_t rc = r0 * (uint32_t)(D * 2);
     issue_row_tile<D, NWT>(uniform_ptr(Qb + rc), roff, rqb + st * (G::RUNITS * 16), wv);
     issue_row_tile<D, NWT>(uniform_ptr(Db + rc), roff, rdb + st * (G::RUNITS * 16), wv);
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     }
   };
 
-  const int nch = NW * L;
+  const int nch = L << qsh;
   if (nch > 0) issue(0);
   for (int c = 0; c < nch; ++c) {
     wait_vmcnt<0>();
@@ -527,28 +536,52 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
 
 hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_t* order) {
   int pow2 = 1;
-  while (pow2 < L.g.Nc) pow2 <<= 1;
+  while (pow2 < L.gk.Nc) pow2 <<= 1;
   if (pow2 > 2048) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(order_by_count_kernel, dim3(L.BH), dim3(1024), 0, L.stream, k2q_off, order, L.g.Nc, pow2);
+  hipLaunchKernelGGL(order_by_count_kernel, dim3(L.BH), dim3(1024), 0, L.stream, k2q_off, order, L.gk.Nc, pow2);
   return hipGetLastError();
 }
 
+// dQ: one workgroup of Bt/32 waves per query cube.
 template <int D, int NW>
+static void launch_dq(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
+                      const int32_t* len, const int32_t* qorder, const float* lse_f, const bf16* dof,
+                      const float* delta, const float* dqc, const uint8_t* qarg, bf16* dq) {
+  hipLaunchKernelGGL((fine_bwd_dq_kernel<D, NW>), dim3(L.BH * L.g.Nc), dim3(64 * NW), 0, L.stream, q, k, v, idx,
+                     len, qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.gk, L.stride, L.scale);
+}
+
+// dK / dV: one workgroup per key block, Bk/32 waves (64 channels) or 2 Bk/32
+// (128 channels, warp-specialized).
+template <int D, int NW>
+static void launch_dkdv(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* k2q_off,
+                        const int32_t* k2q, const int32_t* korder, const float* lse_f, const bf16* dof,
+                        const float* delta, const float* dkc, const float* dvc, const uint8_t* karg,
+                        const uint8_t* varg, bf16* dk, bf16* dv) {
+  const dim3 grid(L.BH * L.gk.Nc);
+  if constexpr (D == 64)
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW>), grid, dim3(64 * NW), 0, L.stream, q, k, v, k2q_off, k2q,
+                       korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.gk, L.g, L.stride, L.scale);
+  else
+    hipLaunchKernelGGL((fine_bwd_dkdv_ws_kernel<D, NW>), grid, dim3(128 * NW), 0, L.stream, q, k, v, k2q_off, k2q,
+                       korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.gk, L.g, L.stride, L.scale);
+}
+
+template <int D>
 static void fine_bwd_launch(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
                             const int32_t* len, const int32_t* qorder, const int32_t* k2q_off, const int32_t* k2q,
                             const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
                             const float* dqc, const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
                             const uint8_t* qarg, const uint8_t* karg, const uint8_t* varg) {
-  const int nitems = L.BH * L.g.Nc;
-  hipLaunchKernelGGL((fine_bwd_dq_kernel<D, NW>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v, idx, len,
-                     qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.stride, L.scale);
-  if constexpr (D == 64) {
-    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW>), dim3(nitems), dim3(64 * NW), 0, L.stream, q, k, v,
-                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
-  } else {
-    hipLaunchKernelGGL((fine_bwd_dkdv_ws_kernel<D, NW>), dim3(nitems), dim3(128 * NW), 0, L.stream, q, k, v,
-                       k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.g, L.stride, L.scale);
-  }
+  if (L.g.B == 32) launch_dq<D, 1>(L, q, k, v, idx, len, qorder, lse_f, dof, delta, dqc, qarg, dq);
+  else if (L.g.B == 128) launch_dq<D, 4>(L, q, k, v, idx, len, qorder, lse_f, dof, delta, dqc, qarg, dq);
+  else launch_dq<D, 2>(L, q, k, v, idx, len, qorder, lse_f, dof, delta, dqc, qarg, dq);
+  if (L.gk.B == 32)
+    launch_dkdv<D, 1>(L, q, k, v, k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv);
+  else if (L.gk.B == 128)
+    launch_dkdv<D, 4>(L, q, k, v, k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv);
+  else
+    launch_dkdv<D, 2>(L, q, k, v, k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv);
 }
 
 hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
@@ -556,20 +589,17 @@ hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const 
                            const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
                            const float* dqc, const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
                            const uint8_t* args) {
-  const int nitems = L.BH * L.g.Nc;
-  const long plane = (long)nitems * L.D;
+  // Argmax planes in launch_pool's layout: q (Nq cubes), then k and v (Nk blocks).
+  const long qplane = (long)L.BH * L.g.Nc * L.D, kplane = (long)L.BH * L.gk.Nc * L.D;
   const uint8_t* qarg = args;
-  const uint8_t* karg = args != nullptr ? args + plane : nullptr;
-  const uint8_t* varg = args != nullptr ? args + 2 * plane : nullptr;
-  if (L.D == 64) {
-    if (L.g.B == 32) fine_bwd_launch<64, 1>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
-    else if (L.g.B == 128) fine_bwd_launch<64, 4>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
-    else fine_bwd_launch<64, 2>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
-  } else {
-    if (L.g.B == 32) fine_bwd_launch<128, 1>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
-    else if (L.g.B == 128) fine_bwd_launch<128, 4>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
-    else fine_bwd_launch<128, 2>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk, dv, qarg, karg, varg);
-  }
+  const uint8_t* karg = args != nullptr ? args + qplane : nullptr;
+  const uint8_t* varg = args != nullptr ? args + qplane + kplane : nullptr;
+  if (L.D == 64)
+    fine_bwd_launch<64>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk,
+                        dv, qarg, karg, varg);
+  else
+    fine_bwd_launch<128>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq,
+                         dk, dv, qarg, karg, varg);
   return hipGetLastError();
 }
 

@@ -9,8 +9,9 @@
 //
 // bf16 kernel: a workgroup of NW = Bt/32 waves owns one query cube of Bt
 // tokens (two waves for the default 64-token cube); wave w owns the queries
-// 32w .. 32w+31 and walks the cube's list of key cubes in 32-key chunks with
-// an online softmax (32x32x16 bf16 MFMAs):
+// 32w .. 32w+31 and walks the cube's list of key blocks (Bk tokens each, Bk/32
+// chunks; a key block is the query cube unless the problem gives keys their
+// own tile) in 32-key chunks with an online softmax (32x32x16 bf16 MFMAs):
 //   S^T = K_chunk Q^T    A = the chunk's K row tile (LDS), B = the lane's Q
 //                        row (registers, loaded once);
 //   the accumulator gives every lane one query column and 16 of the 32 keys,
@@ -30,7 +31,7 @@ namespace vsa {
 
 // bf16 kernel geometry. A workgroup of NW waves owns one query cube; wave
 // w owns the 32 queries 32w .. 32w+31 (one MFMA column block). The cube's
-// list is walked in 32-key chunks (NW per key cube); each chunk's K and V
+// list is walked in 32-key chunks (Bk/32 per key block); each chunk's K and V
 // rows go to LDS once (direct-to-LDS loads, 1/NW issued by each wave) and
 // all waves read them. MFMAs are 32x32x16.
 template <int D> struct FineCfg {
@@ -46,13 +47,15 @@ template <int D> struct FineCfg {
   static constexpr int VST = D == 64 ? 3 : 2;
 };
 
-// Processing order of the query cubes of every (b, h): ascending by the first
-// two cubes of their lists (empty positions sort last), ties by cube id.
+// Processing order of the Nq query cubes of every (b, h): ascending by the
+// first two key blocks of their lists (ids < Nk; empty positions sort last),
+// ties by cube id.
 // Query cubes with similar lists then run side by side on an XCD and share
 // the key / value blocks in its L2. One workgroup per (b, h): a bitonic sort
 // of (signature << 32 | cube) keys in LDS.
 __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ len,
-                                                     int32_t* __restrict__ order, int Nc, int stride, int pow2) {
+                                                     int32_t* __restrict__ order, int Nc, int Nk, int stride,
+                                                     int pow2) {
   __shared__ unsigned long long key[2048];
   const long bh = blockIdx.x;
   for (int e = threadIdx.x; e < pow2; e += 1024) {
@@ -60,9 +63,9 @@ __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__
     if (e < Nc) {
       const long row = bh * Nc + e;
       const int n = min(max(len[row], 0), stride);
-      const uint32_t a = n > 0 ? (uint32_t)idx[row * stride] : (uint32_t)Nc;
-      const uint32_t b = n > 1 ? (uint32_t)idx[row * stride + 1] : (uint32_t)Nc;
-      const uint32_t sig = min(a, (uint32_t)Nc) * (uint32_t)(Nc + 1) + min(b, (uint32_t)Nc);
+      const uint32_t a = n > 0 ? (uint32_t)idx[row * stride] : (uint32_t)Nk;
+      const uint32_t b = n > 1 ? (uint32_t)idx[row * stride + 1] : (uint32_t)Nk;
+      const uint32_t sig = min(a, (uint32_t)Nk) * (uint32_t)(Nk + 1) + min(b, (uint32_t)Nk);
       kv = ((unsigned long long)sig << 32) | (uint32_t)e;
     }
     key[e] = kv;
@@ -83,12 +86,15 @@ __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__
   for (int e = threadIdx.x; e < Nc; e += 1024) order[bh * Nc + e] = (int32_t)(key[e] & 0xffffffffu);
 }
 
-template <int D, int NW, bool FUSED>
+// KSAME: key blocks are the query cubes (gk == g), so a key block has NW
+// chunks and its geometry is g's, both known at compile time; otherwise the
+// key blocks' grid gk is read at run time.
+template <int D, int NW, bool KSAME, bool FUSED>
 __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
     bf16* __restrict__ o_f, float* __restrict__ lse_f, const float* __restrict__ oc, const bf16* __restrict__ gc,
-    const bf16* __restrict__ gf, bf16* __restrict__ o, Grid g, int stride, float scale_log2) {
+    const bf16* __restrict__ gf, bf16* __restrict__ o, Grid g, Grid gk, int stride, float scale_log2) {
   using C = FineCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 kbuf[C::KST * C::KUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 vbuf[C::VST * C::VUNITS * 8];
@@ -106,7 +112,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   // from reading outside the tensors.
   const int L = min(max(len[item], 0), stride);
   const int32_t* list = idx + (long)item * stride;
-  auto cube_at = [&](int t) { const int j = list[t]; return (j >= 0 && j < g.Nc) ? j : 0; };
+  const Grid& kg = KSAME ? g : gk;   // grid of the key blocks
+  auto cube_at = [&](int t) { const int j = list[t]; return (j >= 0 && j < kg.Nc) ? j : 0; };
 
   // This lane's query: in-cube token 32wv + n32.
   const int qrow = cube_token(g, i, 32 * wv + n32);
@@ -123,17 +130,19 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
   float m = 0.f, lsum = 0.f;
 
-  // Loads of chunk c = key cube list[c/NW], chunk h = c%NW of it (tokens
-  // 32h .. 32h+31): this wave issues 1/NW of the K rows and of the V rows,
-  // both into row tiles. Per-lane byte offsets are fixed for the whole list:
-  // unit p = ins*64 + lane is key row kappa = p / U, logical unit (p % U) ^
-  // kswz(kappa), i.e. in-cube token 32h + kappa.
+  // Loads of chunk c = key block list[c >> ksh], chunk h = c & kmask of it
+  // (tokens 32h .. 32h+31; 2^ksh = Bk/32 chunks per block): this wave issues
+  // 1/NW of the K rows and of the V rows, both into row tiles. Per-lane byte
+  // offsets are fixed for the whole list: unit p = ins*64 + lane is key row
+  // kappa = p / U, logical unit (p % U) ^ kswz(kappa), i.e. in-block token
+  // 32h + kappa.
   constexpr int KPW = C::KINS / NW;   // loads per wave per K (or V) chunk
+  const int ksh = chunk_shift(kg), kmask = (1 << ksh) - 1;
   const uint32_t kbase = lds_addr(kbuf), vbase = lds_addr(vbuf);
   uint32_t koff[KPW];
-  row_tile_offsets<D, NW>(g, wv, lane, koff);
-  // Byte offsets of the list's cubes, 64 entries at a time, one per lane:
-  // kcube = first key row of the cube within this head's K (and V). A load
+  row_tile_offsets<D, NW>(kg, wv, lane, koff);
+  // Byte offsets of the list's key blocks, 64 entries at a time, one per
+  // lane: kcube = first key row of the block within this head's K (and V). A load
   // reads it with readlane, so the per-chunk address work is scalar and
   // division-free. The block of entries is refreshed when the first chunk of
   // entry 64 * n is loaded; K runs ahead of V, so V keeps its own copy.
@@ -141,16 +150,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   uint32_t kcube = 0, vcube = 0;
   auto cubes_k = [&](int t0) {
     const int t = t0 + lane;
-    kcube = (uint32_t)cube_first(g, t < L ? cube_at(t) : 0) * (uint32_t)(D * 2);
+    kcube = (uint32_t)cube_first(kg, t < L ? cube_at(t) : 0) * (uint32_t)(D * 2);
   };
   auto cubes_v = [&](int t0) {
     const int t = t0 + lane;
-    vcube = (uint32_t)cube_first(g, t < L ? cube_at(t) : 0) * (uint32_t)(D * 2);
+    vcube = (uint32_t)cube_first(kg, t < L ? cube_at(t) : 0) * (uint32_t)(D * 2);
   };
-  // Bytes from a cube's first row to the first row of its chunk h.
-  auto chunk_bytes = [&](int h) { return NW == 1 ? 0u : (uint32_t)(chunk_first(g, h) * D) * 2u; };
+  // Bytes from a key block's first row to the first row of its chunk h.
+  auto chunk_bytes = [&](int h) {
+    return (KSAME && NW == 1) ? 0u : (uint32_t)(chunk_first(kg, h) * D) * 2u;
+  };
   auto issue_k = [&](int c) {
-    const int e = c / NW, h = c % NW;
+    const int e = KSAME ? c / NW : c >> ksh, h = KSAME ? c % NW : c & kmask;
     if ((e & 63) == 0 && h == 0) cubes_k(e);
     const uint32_t dst = kbase + (c % C::KST) * (C::KUNITS * 16);
     const uint32_t kc = __builtin_amdgcn_readlane(kcube, e & 63);
@@ -159,7 +170,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     for (int t = 0; t < KPW; ++t) dma16(src, koff[t], dst + (wv * KPW + t) * 1024);
   };
   auto issue_v = [&](int c) {
-    const int e = c / NW, h = c % NW;
+    const int e = KSAME ? c / NW : c >> ksh, h = KSAME ? c % NW : c & kmask;
     if ((e & 63) == 0 && h == 0) cubes_v(e);
     const uint32_t dst = vbase + (c % C::VST) * (C::VUNITS * 16);
     const uint32_t vc = __builtin_amdgcn_readlane(vcube, e & 63);
@@ -201,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   // m starts at the row max of chunk 0). O and l always share m, so the
   // result is exact whatever the schedule.
   constexpr float kHeadroom = 16.0f;
-  const int nch = NW * L;
+  const int nch = KSAME ? NW * L : L << ksh;
   f32x16 sxa, sxb;
   if (nch > 0) {
     issue_k(0);
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(128) void fine_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, float* __restrict__ o_f,
     float* __restrict__ lse_f, const float* __restrict__ oc, const float* __restrict__ gc,
-    const float* __restrict__ gf, float* __restrict__ o, Grid g, int stride, float scale) {
+    const float* __restrict__ gf, float* __restrict__ o, Grid g, Grid gk, int stride, float scale) {
   constexpr int R = 32;   // key rows per LDS stage
   __shared__ float ks[R][D];
   __shared__ float vs[R][D];
@@ -389,13 +400,13 @@ __global__ __launch_bounds__(128) void fine_fwd_f32_kernel(
   float m = -INFINITY, l = 0.f;
   const int L = min(max(len[item], 0), stride);
   const int32_t* list = idx + (long)item * stride;
-  for (int t = 0; t < L * (g.B / R); ++t) {
-    const int j = list[t / (g.B / R)], r0 = (t % (g.B / R)) * R;
-    if (j < 0 || j >= g.Nc) continue;
+  for (int t = 0; t < L * (gk.B / R); ++t) {
+    const int j = list[t / (gk.B / R)], r0 = (t % (gk.B / R)) * R;
+    if (j < 0 || j >= gk.Nc) continue;
     __syncthreads();
     for (int e = tid; e < R * D; e += nt) {
       const int r = e / D, d = e - r * D;
-      const long src = (tok0 + cube_token(g, j, r0 + r)) * D + d;
+      const long src = (tok0 + cube_token(gk, j, r0 + r)) * D + d;
       ks[r][d] = k[src];
       vs[r][d] = v[src];
     }
@@ -432,9 +443,15 @@ static void fine_launch_bf16_nw(const Launch& L, const void* q, const void* k, c
                                 const int32_t* len, const int32_t* order, void* o_f, float* lse_f, const float* oc,
                                 const void* gc, const void* gf, void* o) {
   const int nitems = L.BH * L.g.Nc;
-  hipLaunchKernelGGL((fine_fwd_bf16_kernel<D, NW, FUSED>), dim3(nitems), dim3(64 * NW), 0, L.stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, idx, len, order, (bf16*)o_f, lse_f, oc,
-                     (const bf16*)gc, (const bf16*)gf, (bf16*)o, L.g, L.stride, L.scale * kLog2e);
+  const bool same = L.g.B == L.gk.B && L.g.lct == L.gk.lct && L.g.lch == L.gk.lch;
+  if (same)
+    hipLaunchKernelGGL((fine_fwd_bf16_kernel<D, NW, true, FUSED>), dim3(nitems), dim3(64 * NW), 0, L.stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, idx, len, order, (bf16*)o_f, lse_f, oc,
+                       (const bf16*)gc, (const bf16*)gf, (bf16*)o, L.g, L.gk, L.stride, L.scale * kLog2e);
+  else
+    hipLaunchKernelGGL((fine_fwd_bf16_kernel<D, NW, false, FUSED>), dim3(nitems), dim3(64 * NW), 0, L.stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, idx, len, order, (bf16*)o_f, lse_f, oc,
+                       (const bf16*)gc, (const bf16*)gf, (bf16*)o, L.g, L.gk, L.stride, L.scale * kLog2e);
 }
 
 // Waves per workgroup = cube tokens / 32 (32, 64 or 128 tokens).
@@ -454,14 +471,15 @@ static void fine_launch_f32(const Launch& L, const void* q, const void* k, const
   const int nitems = L.BH * L.g.Nc;
   hipLaunchKernelGGL((fine_fwd_f32_kernel<D, FUSED>), dim3(nitems), dim3(L.g.B), 0, L.stream, (const float*)q,
                      (const float*)k, (const float*)v, idx, len, (float*)o_f, lse_f, oc, (const float*)gc,
-                     (const float*)gf, (float*)o, L.g, L.stride, L.scale);
+                     (const float*)gf, (float*)o, L.g, L.gk, L.stride, L.scale);
 }
 
 hipError_t launch_order(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* order) {
   int pow2 = 1;
   while (pow2 < L.g.Nc) pow2 <<= 1;
   if (pow2 > 2048) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(order_kernel, dim3(L.BH), dim3(1024), 0, L.stream, idx, len, order, L.g.Nc, L.stride, pow2);
+  hipLaunchKernelGGL(order_kernel, dim3(L.BH), dim3(1024), 0, L.stream, idx, len, order, L.g.Nc, L.gk.Nc, L.stride,
+                     pow2);
   return hipGetLastError();
 }
 

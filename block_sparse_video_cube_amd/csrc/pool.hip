@@ -14,11 +14,14 @@
 
 namespace vsa {
 
-template <typename T, int D, bool MAX, int BT>
+// SEL: bit w set = tensor w (q, k, v) is pooled by this launch (all three
+// when queries and keys share the cube shape, else q alone or k and v).
+template <typename T, int D, bool MAX, int BT, int SEL>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, float* __restrict__ qc,
                                                    float* __restrict__ kc, float* __restrict__ vc,
-                                                   uint8_t* __restrict__ args, Grid g) {
+                                                   uint8_t* __restrict__ qa, uint8_t* __restrict__ ka,
+                                                   uint8_t* __restrict__ va, Grid g) {
   constexpr int CH = D / 8;            // 8-channel chunks per token row
   constexpr int RPP = 256 / CH;        // token rows per pass
   constexpr int PASSES = BT / RPP;     // BT = tokens per cube
@@ -30,10 +33,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   const int c = blockIdx.x;
   const int ch = tid % CH, rsub = tid / CH;
   const long base = bh * (long)g.N * D;
-  const long plane = (long)gridDim.y * g.Nc * D;   // one tensor's args
 
-  const T* srcs[3] = {q + base, k + base, v + base};
+  const T* srcs[3] = {q, k, v};
   float* dsts[3] = {qc, kc, vc};
+  uint8_t* args[3] = {qa, ka, va};
   // Every load of the three tensors is issued before any reduction, so a
   // thread keeps 3 * PASSES independent 16-byte loads in flight.
   float acc[3][8];
@@ -45,9 +48,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int l = p * RPP + rsub;   // increasing: a strict compare keeps the first maximum
-    const long off = (long)cube_token(g, c, l) * D + ch * 8;
+    const long off = base + (long)cube_token(g, c, l) * D + ch * 8;
 #pragma unroll
     for (int w = 0; w < 3; ++w) {
+      if (!(SEL & (1 << w))) continue;
       float x[8];
       load8(srcs[w] + off, x);
 #pragma unroll
@@ -70,6 +74,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   __syncthreads();
   for (int t = tid; t < 3 * D; t += 256) {
     const int w = t / D, col = t - w * D;
+    if (!(SEL & (1 << w))) continue;
     if (MAX) {
       float best = part[w][0][col];
       int ba = parg[w][0][col];
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
         if (y > best || (y == best && a < ba)) { best = y; ba = a; }   // ties: first in cube order
       }
       if (dsts[w] != nullptr) dsts[w][(bh * g.Nc + c) * D + col] = best;
-      if (args != nullptr) args[w * plane + (bh * g.Nc + c) * D + col] = (uint8_t)ba;
+      if (args[w] != nullptr) args[w][(bh * g.Nc + c) * D + col] = (uint8_t)ba;
     } else {
       float s = 0.f;
 #pragma unroll
@@ -90,24 +95,41 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   }
 }
 
-template <typename T, bool MAX, int BT>
-static void pool_launch_bt(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
-                           float* vc, uint8_t* args) {
-  const dim3 grid(L.g.Nc, L.BH), block(256);
+template <typename T, bool MAX, int BT, int SEL>
+static void pool_launch_bt(const Launch& L, const Grid& g, const void* q, const void* k, const void* v, float* qc,
+                           float* kc, float* vc, uint8_t* qa, uint8_t* ka, uint8_t* va) {
+  const dim3 grid(g.Nc, L.BH), block(256);
   if (L.D == 64)
-    hipLaunchKernelGGL((pool_kernel<T, 64, MAX, BT>), grid, block, 0, L.stream, (const T*)q, (const T*)k,
-                       (const T*)v, qc, kc, vc, args, L.g);
+    hipLaunchKernelGGL((pool_kernel<T, 64, MAX, BT, SEL>), grid, block, 0, L.stream, (const T*)q, (const T*)k,
+                       (const T*)v, qc, kc, vc, qa, ka, va, g);
   else
-    hipLaunchKernelGGL((pool_kernel<T, 128, MAX, BT>), grid, block, 0, L.stream, (const T*)q, (const T*)k,
-                       (const T*)v, qc, kc, vc, args, L.g);
+    hipLaunchKernelGGL((pool_kernel<T, 128, MAX, BT, SEL>), grid, block, 0, L.stream, (const T*)q, (const T*)k,
+                       (const T*)v, qc, kc, vc, qa, ka, va, g);
 }
 
+template <typename T, bool MAX, int SEL>
+static void pool_grid(const Launch& L, const Grid& g, const void* q, const void* k, const void* v, float* qc,
+                      float* kc, float* vc, uint8_t* qa, uint8_t* ka, uint8_t* va) {
+  if (g.B == 32) pool_launch_bt<T, MAX, 32, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
+  else if (g.B == 128) pool_launch_bt<T, MAX, 128, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
+  else pool_launch_bt<T, MAX, 64, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
+}
+
+// Queries pool over query cubes, keys and values over key blocks: one launch
+// when the two shapes agree, two otherwise.
 template <typename T, bool MAX>
 static void pool_launch(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
                         float* vc, uint8_t* args) {
-  if (L.g.B == 32) pool_launch_bt<T, MAX, 32>(L, q, k, v, qc, kc, vc, args);
-  else if (L.g.B == 128) pool_launch_bt<T, MAX, 128>(L, q, k, v, qc, kc, vc, args);
-  else pool_launch_bt<T, MAX, 64>(L, q, k, v, qc, kc, vc, args);
+  uint8_t* qa = args;
+  uint8_t* ka = args != nullptr ? args + (size_t)L.BH * L.g.Nc * L.D : nullptr;
+  uint8_t* va = args != nullptr ? ka + (size_t)L.BH * L.gk.Nc * L.D : nullptr;
+  const bool same = L.g.B == L.gk.B && L.g.lct == L.gk.lct && L.g.lch == L.gk.lch;
+  if (same) {
+    pool_grid<T, MAX, 7>(L, L.g, q, k, v, qc, kc, vc, qa, ka, va);
+  } else {
+    pool_grid<T, MAX, 1>(L, L.g, q, nullptr, nullptr, qc, nullptr, nullptr, qa, nullptr, nullptr);
+    pool_grid<T, MAX, 6>(L, L.gk, nullptr, k, v, nullptr, kc, vc, nullptr, ka, va);
+  }
 }
 
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,

@@ -14,7 +14,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Dims {
-  long BH, N, Nc, D, stride;
+  long BH, N, Nq, Nk, D, stride;   // Nq query cubes, Nk key blocks per (b, h)
   size_t elem;  // bytes per raster element
 };
 
@@ -26,28 +26,37 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
   if (p == nullptr) return VSA_ERR_NULL;
   if (p->B < 1 || p->heads < 1) return VSA_ERR_SHAPE;
   const int ct = p->cube_t ? p->cube_t : 4, ch = p->cube_h ? p->cube_h : 4, cw = p->cube_w ? p->cube_w : 4;
-  if (!pow2_side(ct) || !pow2_side(ch) || !pow2_side(cw) || cw < 4) return VSA_ERR_SHAPE;
+  const bool kown = p->kcube_t || p->kcube_h || p->kcube_w;   // key blocks of their own shape
+  const int kt = kown ? p->kcube_t : ct, kh = kown ? p->kcube_h : ch, kw = kown ? p->kcube_w : cw;
+  for (int side : {ct, ch, cw, kt, kh, kw})
+    if (!pow2_side(side)) return VSA_ERR_SHAPE;
+  if (cw < 4 || kw < 4) return VSA_ERR_SHAPE;
   if (p->T < ct || p->H < ch || p->W < cw || p->T % ct || p->H % ch || p->W % cw) return VSA_ERR_SHAPE;
-  const long Bt = (long)ct * ch * cw;
+  if (p->T % kt || p->H % kh || p->W % kw) return VSA_ERR_SHAPE;
+  const long Bt = (long)ct * ch * cw, Bk = (long)kt * kh * kw;
   if (Bt != 32 && Bt != 64 && Bt != 128) return VSA_ERR_UNSUPPORTED;
+  if (Bk != 32 && Bk != 64 && Bk != 128) return VSA_ERR_UNSUPPORTED;
+  const bool same = kt == ct && kh == ch && kw == cw;
   const long N = (long)p->T * p->H * p->W;
   const long BH = (long)p->B * p->heads;
   if (N > (1L << 30) || BH > (1L << 24)) return VSA_ERR_SHAPE;
   if (p->head_dim != 64 && p->head_dim != 128) return VSA_ERR_HEAD_DIM;
   if (p->dtype != VSA_F32 && p->dtype != VSA_BF16) return VSA_ERR_DTYPE;
-  const long Nc = N / Bt;
-  if (BH * Nc > 0x7fffffffL) return VSA_ERR_SHAPE;
+  const long Nc = N / Bt, Nk = N / Bk;
+  if (BH * (Nc > Nk ? Nc : Nk) > 0x7fffffffL) return VSA_ERR_SHAPE;
   if (BH * N * p->head_dim > (1L << 40)) return VSA_ERR_SHAPE;
   if (!std::isfinite(p->scale) || p->scale < 0.f) return VSA_ERR_SCALE;
-  if (p->topk < 0 || p->topk > Nc) return VSA_ERR_TOPK;
+  if (p->topk < 0 || p->topk > Nk) return VSA_ERR_TOPK;
   const long stride = p->list_stride == 0 ? p->topk : p->list_stride;
   if (p->topk > 0 && stride < p->topk) return VSA_ERR_TOPK;
-  if (stride < 1 || stride > Nc) return VSA_ERR_TOPK;
-  if (Nc > coarse_max_cubes()) return VSA_ERR_UNSUPPORTED;
+  if (stride < 1 || stride > Nk) return VSA_ERR_TOPK;
+  if (Nc > coarse_max_cubes() || Nk > coarse_max_cubes()) return VSA_ERR_UNSUPPORTED;
   if (p->pool_mode != VSA_POOL_MEAN && p->pool_mode != VSA_POOL_MAX) return VSA_ERR_UNSUPPORTED;
   if (p->layout != VSA_LAYOUT_RASTER && p->layout != VSA_LAYOUT_TILED) return VSA_ERR_UNSUPPORTED;
+  if (p->layout == VSA_LAYOUT_TILED && !same) return VSA_ERR_UNSUPPORTED;   // one cube-major order
   if (L != nullptr) {
     L->g = make_grid(p->T, p->H, p->W, p->layout == VSA_LAYOUT_TILED ? 1 : 0, ct, ch, cw);
+    L->gk = make_grid(p->T, p->H, p->W, p->layout == VSA_LAYOUT_TILED ? 1 : 0, kt, kh, kw);
     L->BH = (int)BH;
     L->D = p->head_dim;
     L->bf16 = p->dtype == VSA_BF16;
@@ -58,7 +67,7 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
     L->stream = nullptr;
   }
   if (d != nullptr) {
-    d->BH = BH; d->N = N; d->Nc = Nc; d->D = p->head_dim; d->stride = stride;
+    d->BH = BH; d->N = N; d->Nq = Nc; d->Nk = Nk; d->D = p->head_dim; d->stride = stride;
     d->elem = p->dtype == VSA_BF16 ? 2 : 4;
   }
   return VSA_OK;
@@ -99,12 +108,12 @@ struct Saved {
 Saved carve_saved(const Dims& d, void* base) {
   Carver c(base);
   Saved s;
-  const size_t pooled = d.BH * d.Nc * d.D;
-  s.qc = c.take<float>(pooled);
-  s.kc = c.take<float>(pooled);
-  s.vc = c.take<float>(pooled);
-  s.oc = c.take<float>(pooled);
-  s.lse_c = c.take<float>(d.BH * d.Nc);
+  const size_t pq = d.BH * d.Nq * d.D, pk = d.BH * d.Nk * d.D;
+  s.qc = c.take<float>(pq);
+  s.kc = c.take<float>(pk);
+  s.vc = c.take<float>(pk);
+  s.oc = c.take<float>(pq);
+  s.lse_c = c.take<float>(d.BH * d.Nq);
   s.lse_f = c.take<float>(d.BH * d.N);
   s.of = c.take<char>(d.BH * d.N * d.D * d.elem);
   s.bytes = c.off;
@@ -121,14 +130,14 @@ struct FwdWs {
 FwdWs carve_fwd_ws(const Dims& d, void* base) {
   Carver c(base);
   FwdWs w;
-  w.order = c.take<int32_t>(d.BH * d.Nc);
-  w.s = c.take<float>(d.BH * d.Nc * (size_t)coarse_ld((int)d.Nc));
-  const size_t pooled = d.BH * d.Nc * d.D;
-  w.qc = c.take<float>(pooled);
-  w.kc = c.take<float>(pooled);
-  w.vc = c.take<float>(pooled);
-  w.oc = c.take<float>(pooled);
-  w.lse_c = c.take<float>(d.BH * d.Nc);
+  w.order = c.take<int32_t>(d.BH * d.Nq);
+  w.s = c.take<float>(d.BH * d.Nq * (size_t)coarse_ld((int)d.Nk));
+  const size_t pq = d.BH * d.Nq * d.D, pk = d.BH * d.Nk * d.D;
+  w.qc = c.take<float>(pq);
+  w.kc = c.take<float>(pk);
+  w.vc = c.take<float>(pk);
+  w.oc = c.take<float>(pq);
+  w.lse_c = c.take<float>(d.BH * d.Nq);
   w.bytes = c.off;
   return w;
 }
@@ -148,21 +157,21 @@ BwdWs carve_bwd_ws(const Dims& d, void* base) {
   const size_t rast = d.BH * d.N * d.D;
   w.dof = c.take<bf16>(rast);
   w.delta = c.take<float>(d.BH * d.N);
-  const size_t pooled = d.BH * d.Nc * d.D;
-  w.doc = c.take<float>(pooled);
-  w.dqc = c.take<float>(pooled);
-  w.dkc = c.take<float>(pooled);
-  w.dvc = c.take<float>(pooled);
-  const size_t ldc = (size_t)coarse_ld((int)d.Nc);
-  w.p_scr = c.take<float>(d.BH * d.Nc * ldc);
-  w.ds_scr = c.take<float>(d.BH * d.Nc * ldc);
-  w.dc_scr = c.take<float>(d.BH * d.Nc);
-  w.k2q_off = c.take<int32_t>(d.BH * (d.Nc + 1));
-  w.k2q = c.take<int32_t>(d.BH * d.Nc * d.stride);
-  w.k2q_bits = c.take<uint32_t>(d.BH * d.Nc * (size_t)k2q_bits_words((int)d.Nc));
-  w.qorder = c.take<int32_t>(d.BH * d.Nc);
-  w.korder = c.take<int32_t>(d.BH * d.Nc);
-  w.args = c.take<uint8_t>(3 * d.BH * d.Nc * d.D);
+  const size_t pq = d.BH * d.Nq * d.D, pk = d.BH * d.Nk * d.D;
+  w.doc = c.take<float>(pq);
+  w.dqc = c.take<float>(pq);
+  w.dkc = c.take<float>(pk);
+  w.dvc = c.take<float>(pk);
+  const size_t ldc = (size_t)coarse_ld((int)d.Nk);
+  w.p_scr = c.take<float>(d.BH * d.Nq * ldc);
+  w.ds_scr = c.take<float>(d.BH * d.Nq * ldc);
+  w.dc_scr = c.take<float>(d.BH * d.Nq);
+  w.k2q_off = c.take<int32_t>(d.BH * (d.Nk + 1));
+  w.k2q = c.take<int32_t>(d.BH * d.Nq * d.stride);
+  w.k2q_bits = c.take<uint32_t>(d.BH * d.Nk * (size_t)k2q_bits_words((int)d.Nq));
+  w.qorder = c.take<int32_t>(d.BH * d.Nq);
+  w.korder = c.take<int32_t>(d.BH * d.Nk);
+  w.args = c.take<uint8_t>(d.BH * (d.Nq + 2 * d.Nk) * d.D);
   w.bytes = c.off;
   return w;
 }
@@ -177,10 +186,10 @@ const char* vsa_status_string(vsa_status s) {
   switch (s) {
     case VSA_OK: return "ok";
     case VSA_ERR_NULL: return "a required pointer is NULL";
-    case VSA_ERR_SHAPE: return "invalid shape (B, heads >= 1; T, H, W positive multiples of 4; sizes in range)";
+    case VSA_ERR_SHAPE: return "invalid shape (B, heads >= 1; T, H, W positive multiples of the cube and key-block sides; sizes in range)";
     case VSA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
     case VSA_ERR_DTYPE: return "unknown dtype";
-    case VSA_ERR_TOPK: return "topk outside [0, Nc] or invalid list_stride";
+    case VSA_ERR_TOPK: return "topk outside [0, Nk] or invalid list_stride";
     case VSA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case VSA_ERR_WORKSPACE: return "workspace or saved buffer too small";
     case VSA_ERR_INDEX: return "an index list is invalid";
@@ -487,14 +496,14 @@ vsa_status vsa_check_lists_host(const vsa_problem* p, const int32_t* idx, const 
   vsa_status st = check_problem(p, nullptr, &d);
   if (st != VSA_OK) return st;
   if (idx == nullptr || len == nullptr) return VSA_ERR_NULL;
-  const long rows = d.BH * d.Nc;
+  const long rows = d.BH * d.Nq;
   for (long r = 0; r < rows; ++r) {
     const int n = len[r];
     if (n < 0 || n > d.stride) return VSA_ERR_INDEX;
     int prev = -1;
     for (int t = 0; t < n; ++t) {
       const int v = idx[r * d.stride + t];
-      if (v <= prev || v >= d.Nc) return VSA_ERR_INDEX;
+      if (v <= prev || v >= d.Nk) return VSA_ERR_INDEX;
       prev = v;
     }
   }

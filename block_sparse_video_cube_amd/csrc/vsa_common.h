@@ -92,6 +92,8 @@ __device__ __forceinline__ int token_cube(const Grid& g, int n) {
 __host__ __device__ __forceinline__ int chunk_row(const Grid& g, int kappa) { return cube_rel(g, kappa); }
 // Rows between the first token of chunk h of a cube and the cube's first token.
 __host__ __device__ __forceinline__ int chunk_first(const Grid& g, int h) { return cube_rel(g, 32 * h); }
+// log2 of the 32-token chunks per cube (Bt in {32, 64, 128}).
+__host__ __device__ __forceinline__ int chunk_shift(const Grid& g) { return g.lct + g.lch + g.lcw - 5; }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2). Map block b so that every XCD gets one contiguous range of work items:

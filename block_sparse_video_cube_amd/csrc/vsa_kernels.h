@@ -7,7 +7,9 @@ namespace vsa {
 
 // Launch context shared by the launchers: one problem, one stream.
 struct Launch {
-  Grid g;
+  Grid g;          // query cubes (and every per-token or per-query-cube array)
+  Grid gk;         // key blocks (K, V and their pooled values); equal to g unless
+                   // the problem gives key blocks their own shape
   int BH;          // B * heads
   int D;           // head_dim (64 or 128)
   bool bf16;       // dtype of raster tensors
@@ -18,9 +20,10 @@ struct Launch {
   hipStream_t stream;
 };
 
-// Pooled q / k / v (fp32; each may be null = not written) and, with max
-// pooling, the in-cube index of each (cube, channel) maximum (args: 3 x
-// B*heads*Nc*D bytes for q, k, v; may be null).
+// Pooled q (query cubes) and k, v (key blocks), fp32, each may be null = not
+// written; with max pooling, the in-cube index of each (cube, channel)
+// maximum (args: q, k, v planes of B*heads*Nq*D, B*heads*Nk*D and
+// B*heads*Nk*D bytes; may be null).
 hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void* v, float* qc, float* kc,
                        float* vc, uint8_t* args = nullptr);
 
@@ -29,13 +32,13 @@ hipError_t launch_relayout(const Launch& L, const void* src, void* dst, bool to_
 hipError_t launch_crop_pad(const Launch& L, const void* src, void* dst, int ts, int hs, int ws, bool to_small);
 
 int coarse_max_cubes();
-// Row pitch (floats) of the coarse logits: Nc rounded up to a multiple of 4.
-int coarse_ld(int Nc);
-// s_scratch: B*heads*Nc*coarse_ld(Nc) fp32 (the coarse logits).
+// Row pitch (floats) of the coarse logits: Nk rounded up to a multiple of 4.
+int coarse_ld(int Nk);
+// s_scratch: B*heads*Nq*coarse_ld(Nk) fp32 (the coarse logits).
 hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, const float* vc, float* oc,
                          float* lse, int32_t* idx, int32_t* len, float* s_scratch);
 
-// Processing order of query cubes (BH*Nc int32) from their lists.
+// Processing order of query cubes (BH*Nq int32) from their lists.
 hipError_t launch_order(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* order);
 
 // Fine forward. For bf16, `order` (may be null = cube order) is the
@@ -52,15 +55,17 @@ hipError_t launch_combine_bwd(const Launch& L, const void* d_o, const float* oc,
                               const void* gc, const void* gf, void* dgc, void* dgf, void* dof,
                               float* delta, float* doc);
 
-// bits: B*heads*Nc*k2q_bits_words(Nc) uint32 of scratch.
-int k2q_bits_words(int Nc);
+// bits: B*heads*Nk*k2q_bits_words(Nq) uint32 of scratch; k2q_off has
+// B*heads*(Nk+1) entries, k2q B*heads*Nq*stride.
+int k2q_bits_words(int Nq);
 hipError_t launch_index_transpose(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* k2q_off,
                                   int32_t* k2q, uint32_t* bits);
-// Scratch: ds / p B*heads*Nc*coarse_ld(Nc) fp32, dc B*heads*Nc fp32.
+// Scratch: ds / p B*heads*Nq*coarse_ld(Nk) fp32, dc B*heads*Nq fp32.
 hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, const float* vc,
                              const float* oc, const float* lse, const float* doc, float* dqc, float* dkc,
                              float* dvc, float* ds_scratch, float* p_scratch, float* dc_scratch);
-// Key cubes of every (b, h) ordered by descending transposed-list length.
+// Key blocks of every (b, h) (BH*Nk int32) ordered by descending
+// transposed-list length.
 hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_t* order);
 // Fine backward (bf16): dq over the forward lists (qorder from launch_order,
 // may be null), dk / dv over the transposed lists (korder from

@@ -22,13 +22,17 @@
  *   order, head_dim fastest) in the problem's dtype (fp32 or bf16), unless the
  *   argument says otherwise. Pooled tensors ("_c") are fp32 [B, heads, Nc,
  *   head_dim], cubes in row-major order over (T/Ct, H/Ch, W/Cw); Nc = T*H*W/Bt.
+ *   Key blocks (vsa_problem.kcube_*) default to the query cube; when they
+ *   differ, keys and values are pooled per key block (k_c, v_c, dk_c, dv_c
+ *   are [B, heads, Nk, head_dim], Nk = T*H*W/Bk) while queries, o_c and
+ *   lse_c stay per query cube (Nq = Nc rows).
  *   Per-token scalars (LSE_f, delta) are fp32 [B, heads, T, H, W]. With the
  *   TILED layout (vsa_layout below) every token tensor and per-token array of
  *   the problem is cube-major instead ([B, heads, Nc, Bt, ...]): wherever an
  *   argument below says "raster", read "in the problem's token order".
  * - Index lists: idx is int32 [B, heads, Nc, list_stride], len int32
- *   [B, heads, Nc]. Row i holds len[i] strictly increasing key-cube ids in
- *   [0, Nc); entries beyond len[i] are ignored.
+ *   [B, heads, Nc]. Row i holds len[i] strictly increasing key-block ids in
+ *   [0, Nk); entries beyond len[i] are ignored.
  * - Every pointer is a device pointer unless documented as host, and must be
  *   16-byte aligned. The caller allocates and owns every buffer; the library
  *   never allocates or frees device memory and keeps no per-call state.
@@ -59,7 +63,7 @@ typedef enum {
                               overflows                                       */
   VSA_ERR_HEAD_DIM = 3,    /* head_dim not 64 or 128                         */
   VSA_ERR_DTYPE = 4,       /* unknown dtype                                  */
-  VSA_ERR_TOPK = 5,        /* topk outside [0, Nc] or list_stride invalid    */
+  VSA_ERR_TOPK = 5,        /* topk outside [0, Nk] or list_stride invalid    */
   VSA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned               */
   VSA_ERR_WORKSPACE = 7,   /* workspace / saved buffer smaller than required */
   VSA_ERR_INDEX = 8,       /* an index list failed validation                */
@@ -95,10 +99,10 @@ typedef struct {
   int32_t head_dim;      /* 64 or 128                                          */
   int32_t dtype;         /* vsa_dtype of every float tensor except pooled ones */
   float scale;           /* softmax scale of both stages; 0 => 1/sqrt(head_dim) */
-  int32_t topk;          /* > 0: keep the K best key cubes per query cube
-                            (1..Nc); 0: the caller supplies the lists          */
+  int32_t topk;          /* > 0: keep the K best key blocks per query cube
+                            (1..Nk); 0: the caller supplies the lists          */
   int32_t list_stride;   /* row stride of idx; 0 => topk. Top-K mode needs
-                            list_stride >= topk; list mode needs 1..Nc         */
+                            list_stride >= topk; list mode needs 1..Nk         */
   int32_t pool_mode;     /* vsa_pool_mode; 0 = mean                            */
   int32_t layout;        /* vsa_layout; 0 = raster                             */
   int32_t cube_t, cube_h, cube_w;
@@ -107,9 +111,19 @@ typedef struct {
                             (Ct, Ch, Cw) with tile size Bt = Ct*Ch*Cw and
                             weighs tile sizes in its design exploration.
                             Each side a power of two, Cw >= 4, Bt in
-                            {32, 64, 128}; query and key tiles are both Bt
-                            tokens (Bt x Bt blocks). In-cube token order is
-                            row-major (t', y', x').                           */
+                            {32, 64, 128}. In-cube token order is row-major
+                            (t', y', x').                                     */
+  int32_t kcube_t, kcube_h, kcube_w;
+                         /* sides of the key blocks; all 0 => the query cube.
+                            The same page's tile-size exploration compares
+                            query and key tiles of different sizes (Bq x Bk
+                            blocks, such as 64 x 16): keys and values are
+                            tiled and pooled by this shape, the coarse scores
+                            are Nq x Nk (Nq = N/Bt query cubes, Nk = N/Bk key
+                            blocks), index lists name key blocks, and topk /
+                            list_stride range over 1..Nk. Same rules as the
+                            cube: powers of two, kcube_w >= 4, Bk in {32, 64,
+                            128}. The tiled layout needs kcube = cube.       */
 } vsa_problem;
 
 /* Short text for a status code (static storage, never NULL). */
@@ -118,12 +132,13 @@ const char* vsa_status_string(vsa_status s);
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t vsa_version(void);
 
-/* Largest Nc (cubes per (b, h)) the coarse stage accepts in this build. */
+/* Largest Nc or Nk (cubes or key blocks per (b, h)) the coarse stage
+ * accepts in this build. */
 int32_t vsa_max_cubes(void);
 
 /* Bytes of device workspace vsa_forward (training = 0) or vsa_backward
  * (training = 1) needs for problem p; 0 if p is invalid. The workspace holds
- * scratch only (the coarse logits, fp32 Nc x Nc per (b, h), the processing
+ * scratch only (the coarse logits, fp32 Nc x Nk per (b, h), the processing
  * orders, and for the backward the coarse softmax and its gradient, d_o_f,
  * delta, the transposed lists and their bitmask); its contents are
  * meaningless between calls. */
@@ -131,7 +146,7 @@ size_t vsa_workspace_bytes(const vsa_problem* p, int32_t training);
 
 /* Bytes of the `saved` buffer a training forward fills and vsa_backward
  * reads. 0 if p is invalid. Layout, each region starting on a 256-byte
- * boundary of the buffer: Q_c, K_c, V_c, O_c (fp32 [B, heads, Nc,
+ * boundary of the buffer: Q_c, K_c, V_c, O_c (fp32 [B, heads, Nc or Nk,
  * head_dim] each), LSE_c (fp32 [B, heads, Nc]), LSE_f (fp32 [B, heads, T, H,
  * W]), O_f (dtype, raster). */
 size_t vsa_saved_bytes(const vsa_problem* p);
@@ -166,8 +181,9 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
 /* ---- stage-level entry points (same conventions; for per-stage parity and
  * timing; vsa_forward / vsa_backward chain exactly these kernels) ---------- */
 
-/* Step 1, cube mean-pool: q_c/k_c/v_c (fp32 [B, heads, Nc, head_dim]) are
- * the means of the Bt tokens of every cube (VSA summary page, Appendix B;
+/* Step 1, cube mean-pool: q_c (fp32 [B, heads, Nc, head_dim]) and k_c/v_c
+ * (fp32 [B, heads, Nk, head_dim]) are the means of the tokens of every cube
+ * or key block (VSA summary page, Appendix B;
  * reading notes key design 1), or their per-channel maxima when pool_mode
  * is VSA_POOL_MAX. */
 vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const void* v,
@@ -176,18 +192,18 @@ vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const vo
 /* Steps 2-3, coarse stage: S_c = scale * Q_c K_c^T, A_c = row softmax,
  * o_c = A_c V_c (fp32 [B, heads, Nc, head_dim]) and lse_c = log-sum-exp of
  * each row of S_c (fp32 [B, heads, Nc]). With topk > 0 it also writes idx /
- * len: per row the K largest logits (ties to the smaller cube id) as an
+ * len: per row the K largest logits (ties to the smaller key-block id) as an
  * ascending list (VSA summary page, section 2 and Appendix B; reading notes
  * key design 1, and the fused softmax + top-K + mask-to-index kernel of the
  * notes' training section). With topk == 0 idx / len are not touched (may be
- * NULL). S_c (fp32, Nc^2 per (b, h)) lives in the workspace
- * (ws_bytes >= vsa_workspace_bytes(p, 0)). Requires Nc <= vsa_max_cubes(). */
+ * NULL). S_c (fp32, Nc x Nk per (b, h)) lives in the workspace
+ * (ws_bytes >= vsa_workspace_bytes(p, 0)). Requires Nc, Nk <= vsa_max_cubes(). */
 vsa_status vsa_coarse(const vsa_problem* p, const float* q_c, const float* k_c, const float* v_c,
                       float* o_c, float* lse_c, int32_t* idx, int32_t* len, void* workspace,
                       size_t ws_bytes, void* stream);
 
 /* Step 4, fine block-sparse attention: for every query token of cube i,
- * softmax attention over the tokens of the cubes listed in row i only
+ * softmax attention over the tokens of the key blocks listed in row i only
  * (VSA summary page, section 2 "Fine stage" and Appendix B; reading notes key
  * design 2). o_f (dtype, raster) and lse_f (fp32 [B, heads, T, H, W]); an
  * empty list gives o_f = 0 and lse_f = -inf. For bf16, the workspace
@@ -224,8 +240,8 @@ vsa_status vsa_combine_backward(const vsa_problem* p, const void* d_o, const flo
                                 void* dg_c, void* dg_f, void* d_o_f, float* delta, float* d_o_c,
                                 void* stream);
 
-/* Index transpose for the backward: k2q_off int32 [B, heads, Nc + 1] and
- * k2q int32 [B, heads, Nc * list_stride]: for key cube j the query cubes i
+/* Index transpose for the backward: k2q_off int32 [B, heads, Nk + 1] and
+ * k2q int32 [B, heads, Nc * list_stride]: for key block j the query cubes i
  * whose list holds j, ascending, at k2q[(b,h) * Nc * list_stride +
  * k2q_off[(b,h)][j] ... k2q_off[(b,h)][j+1]). Uses a bitmask in the
  * workspace (ws_bytes >= vsa_workspace_bytes(p, 1)). */
@@ -234,9 +250,10 @@ vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const i
                                void* stream);
 
 /* Backward of step 4 and of the pooling: dq, dk, dv (dtype, raster) =
- * fine-attention gradient + (dq_c, dk_c, dv_c)[cube] / Bt (with max pooling
- * the pooled gradient goes to the cube's argmax token instead), where the pooled
- * gradients (fp32 [B, heads, Nc, head_dim]) come from vsa_coarse_backward.
+ * fine-attention gradient + (dq_c, dk_c, dv_c)[cube or key block] / its
+ * token count (with max pooling the pooled gradient goes to the argmax token
+ * instead), where the pooled gradients (fp32 [B, heads, Nc or Nk, head_dim])
+ * come from vsa_coarse_backward.
  * lse_f from the forward; d_o_f and delta from vsa_combine_backward
  * (workspace: ws_bytes >= vsa_workspace_bytes(p, 1)); k2q_off / k2q from
  * vsa_index_transpose. bf16 only. dQ walks each query cube's list, dK / dV
@@ -250,7 +267,8 @@ vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k,
                              size_t ws_bytes, void* stream);
 
 /* Backward of steps 1-2 at cube level (dense attention backward in fp32):
- * dq_c, dk_c, dv_c (fp32 [B, heads, Nc, head_dim]) from q_c, k_c, v_c, o_c,
+ * dq_c (Nc rows), dk_c, dv_c (Nk rows) (fp32 [B, heads, rows, head_dim])
+ * from q_c, k_c, v_c, o_c,
  * lse_c and d_o_c. workspace >= vsa_workspace_bytes(p, 1). */
 vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const float* k_c,
                                const float* v_c, const float* o_c, const float* lse_c,
@@ -259,7 +277,7 @@ vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const flo
 
 /* ---- list validation ----------------------------------------------------- */
 
-/* Token-order conversion: xt (cube-major [B, heads, Nc, 64, head_dim]) from
+/* Token-order conversion: xt (cube-major [B, heads, Nc, Bt, head_dim]) from
  * x (raster [B, heads, T, H, W, head_dim]) and back, both in the problem's
  * dtype; the problem's layout field is ignored. Not in place (x != xt). */
 vsa_status vsa_tile(const vsa_problem* p, const void* x, void* xt, void* stream);
@@ -292,7 +310,7 @@ vsa_status vsa_crop(const vsa_problem* p, const void* x, int32_t T, int32_t H, i
 vsa_status vsa_pad(const vsa_problem* p, const void* x, int32_t T, int32_t H, int32_t W, void* out, void* stream);
 
 /* Host check of explicit lists (host pointers): every len in [0, list_stride],
- * every listed id in [0, Nc), strictly increasing. Returns VSA_OK or
+ * every listed id in [0, Nk), strictly increasing. Returns VSA_OK or
  * VSA_ERR_INDEX. Runs on the CPU only. */
 vsa_status vsa_check_lists_host(const vsa_problem* p, const int32_t* idx, const int32_t* len);
 

@@ -131,6 +131,51 @@ def test_cube_shapes(cube, ok):
         assert st in (SHAPE, UNSUP)
 
 
+@pytest.mark.parametrize("kcube,ok", [((2, 4, 4), True), ((4, 4, 8), True), ((1, 8, 4), True), ((4, 4, 4), True),
+                                      ((1, 4, 4), False), ((4, 2, 2), False), ((3, 4, 4), False),
+                                      ((8, 4, 8), False), ((0, 4, 4), False)])
+def test_key_block_shapes(kcube, ok):
+    """Key blocks of their own shape (Bq x Bk tiles): the cube's rules, and
+    all-zero sides mean the query cube."""
+    p = _p(T=8, H=16, W=16, topk=1, kcube=kcube)
+    got = N.lib().vsa_workspace_bytes(ctypes.byref(p.c()), 0)
+    assert (got > 0) == ok
+    if ok:
+        assert p.Nk == 8 * 16 * 16 // (kcube[0] * kcube[1] * kcube[2])
+
+
+def test_key_blocks_set_list_bounds_and_sizes():
+    lib = N.lib()
+    # 64-token query cubes, 32-token key blocks: Nq = 32, Nk = 64 at 8x16x16.
+    p = _p(T=8, H=16, W=16, topk=64, kcube=(2, 4, 4))
+    assert p.Nc == 32 and p.Nk == 64
+    assert lib.vsa_workspace_bytes(ctypes.byref(p.c()), 0) > 0              # topk up to Nk
+    assert lib.vsa_workspace_bytes(ctypes.byref(_p(T=8, H=16, W=16, topk=65, kcube=(2, 4, 4)).c()), 0) == 0
+    # Same query cubes, 128-token key blocks: topk bound drops to Nk = 16.
+    assert lib.vsa_workspace_bytes(ctypes.byref(_p(T=8, H=16, W=16, topk=17, kcube=(4, 4, 8)).c()), 0) == 0
+    # Saved buffer holds K_c, V_c per key block: more key blocks, more bytes.
+    base = _p(T=8, H=16, W=16, topk=4)
+    assert V.saved_bytes(p) > V.saved_bytes(base)
+    assert V.workspace_bytes(p, True) > V.workspace_bytes(base, True)
+    # The all-zero key block is the query cube.
+    assert V.saved_bytes(_p(T=8, H=16, W=16, topk=4, kcube=(4, 4, 4))) == V.saved_bytes(base)
+    # One cube-major order: tiled layout needs key blocks = cubes.
+    t = _p(T=8, H=16, W=16, topk=4, kcube=(2, 4, 4), layout="tiled")
+    st = lib.vsa_forward(ctypes.byref(t.c()), *([FAKE] * 8), None, FAKE, 1 << 30, None)
+    assert st == UNSUP
+
+
+def test_check_lists_host_uses_key_block_range():
+    p = V.Problem(1, 1, 8, 8, 8, 64, topk=0, list_stride=4, kcube=(2, 4, 4))   # Nq = 8, Nk = 16
+    idx = np.array([[0, 9, 15, 0]] * 8, np.int32).reshape(1, 1, 8, 4)
+    lens = np.full((1, 1, 8), 3, np.int32)
+    V.check_lists_host(p, idx, lens)
+    idx[0, 0, 3, 2] = 16
+    with pytest.raises(V.VsaError) as e:
+        V.check_lists_host(p, idx, lens)
+    assert e.value.status == INDEX
+
+
 def test_cube_must_divide_latent():
     p = _p(T=6, H=8, W=8, cube=(4, 4, 4))
     assert N.lib().vsa_workspace_bytes(ctypes.byref(p.c()), 0) == 0

@@ -363,7 +363,7 @@ def backward_compare(x, p, dtype, rel=BF16_REL, gates=True):
     torch.cuda.synchronize()
     xg = (x["g_c"], x["g_f"]) if gates else (None, None)
     fwd = O.forward(x["q"], x["k"], x["v"], *xg, topk=0, idx=x["idx"], lens=x["len"], pool_mode=p.pool,
-                    cube=p.cube)
+                    cube=p.cube, kcube=p.kcube)
     assert_close(host(o), fwd["o"], dtype, "o")
     ref = O.backward(x["q"], x["k"], x["v"], *xg, x["d_o"], fwd)
     names = ("dq", "dk", "dv", "dg_c", "dg_f") if gates else ("dq", "dk", "dv")
@@ -373,15 +373,18 @@ def backward_compare(x, p, dtype, rel=BF16_REL, gates=True):
         assert g["dg_c"] is None and g["dg_f"] is None
 
 
-def _small_train_inputs(d=64, seed=5, heads=2, T=8, H=16, W=16, cube=(4, 4, 4)):
+def _small_train_inputs(d=64, seed=5, heads=2, T=8, H=16, W=16, cube=(4, 4, 4), kcube=None):
+    """Ragged random lists (lengths U{0..Nk}), one empty row and one full row."""
     x = WL.make_inputs_custom(1, heads, d, T, H, W, dtype="bf16", seed=seed)
     nc = T * H * W // (cube[0] * cube[1] * cube[2])
-    idx, lens = WL.random_lists(nc, heads * nc, 0, nc, seed=seed)
-    lens[0], lens[1] = 0, nc
-    idx[1, :nc] = np.arange(nc)
-    x["idx"] = idx.reshape(1, heads, nc, nc)
+    kc = cube if kcube is None else kcube
+    nk = T * H * W // (kc[0] * kc[1] * kc[2])
+    idx, lens = WL.random_lists(nk, heads * nc, 0, nk, seed=seed)
+    lens[0], lens[1] = 0, nk
+    idx[1, :nk] = np.arange(nk)
+    x["idx"] = idx.reshape(1, heads, nc, nk)
     x["len"] = lens.reshape(1, heads, nc)
-    p = V.Problem(1, heads, T, H, W, d, topk=0, list_stride=nc, cube=cube)
+    p = V.Problem(1, heads, T, H, W, d, topk=0, list_stride=nk, cube=cube, kcube=kcube)
     return x, p
 
 
@@ -687,3 +690,79 @@ def test_general_cube_tiled_equals_raster_and_max_pool(cube):
     torch.cuda.synchronize()
     assert np.array_equal(host(xp), O.tile(O.pad(host(xs), Tc, Hc, Wc), cube))
     assert torch.equal(back, xs)
+
+
+# ------------------------------- key blocks of their own shape (Bq x Bk tiles)
+# (query cube, key block): 64 x 32, 64 x 128, 32 x 128 and 128 x 32 tokens.
+TILE_PAIRS = [((4, 4, 4), (2, 4, 4)), ((4, 4, 4), (4, 4, 8)), ((2, 4, 4), (4, 4, 8)), ((4, 4, 8), (2, 4, 4))]
+
+
+@pytest.mark.parametrize("cube,kcube", TILE_PAIRS)
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+def test_key_block_forward_topk(cube, kcube, dtype, d):
+    """Nq x Nk coarse scores, top-K over key blocks bit-exact (near-tie
+    protocol), pooled tensors per cube / per key block, and the output on the
+    GPU's lists against the oracle."""
+    T, H, W, heads = 8, 16, 32, 2
+    nq = T * H * W // (cube[0] * cube[1] * cube[2])
+    nk = T * H * W // (kcube[0] * kcube[1] * kcube[2])
+    k = max(nk // 8, 1)
+    x = WL.make_inputs_custom(1, heads, d, T, H, W, dtype=dtype, seed=29, scale=1.0 if dtype == "bf16" else 0.125)
+    p = V.Problem(1, heads, T, H, W, d, dtype=dtype, topk=k, cube=cube, kcube=kcube)
+    dd = inputs_to_dev(x, dtype)
+    o, idx, lens, saved = V.forward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"], training=True)
+    torch.cuda.synchronize()
+    gi, gl = host(idx), host(lens)
+    assert gi.shape == (1, heads, nq, k) and (gl == k).all()
+    sel = O.forward(x["q"], x["k"], x["v"], topk=k, cube=cube, kcube=kcube)
+    assert sel["s_c"].shape == (1, heads, nq, nk)
+    near = check_topk(gi, sel, k)
+    assert near <= NEAR_FRAC * heads * nq
+    ref = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=gl, cube=cube, kcube=kcube)
+    assert_close(host(o), ref["o"], dtype, f"{cube}x{kcube} o")
+    sv = V.saved_views(p, saved)
+    assert_close(host(sv["o_f"]), ref["o_f"], dtype, f"{cube}x{kcube} o_f")
+    lse = host(sv["lse_f"])
+    assert np.abs(lse - ref["lse_f"]).max() <= (LSE_ABS if dtype == "bf16" else 1e-4)
+    for nm in ("q_c", "k_c", "v_c"):
+        np.testing.assert_allclose(host(sv[nm]), ref[nm], rtol=1e-4, atol=1e-5, err_msg=nm)
+    np.testing.assert_allclose(host(sv["lse_c"]), ref["lse_c"], rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("cube,kcube", TILE_PAIRS)
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_block_backward(cube, kcube, d):
+    """Whole backward with ragged lists over key blocks (an empty list and a
+    full one included): dQ walks key blocks, dK / dV walk query cubes."""
+    x, p = _small_train_inputs(d=d, seed=31, T=8, H=16, W=16, cube=cube, kcube=kcube)
+    backward_compare(x, p, "bf16")
+
+
+@pytest.mark.parametrize("cube,kcube", [((4, 4, 4), (2, 4, 4)), ((2, 4, 4), (4, 4, 8))])
+def test_key_block_max_pool_and_stages(cube, kcube):
+    """Max pooling per key block, and the stage entry points chained by hand
+    (pool, coarse, fine, combine, index transpose, backward stages) against
+    the oracle's pieces."""
+    x, p = _small_train_inputs(d=64, seed=37, T=8, H=16, W=16, cube=cube, kcube=kcube)
+    backward_compare(x, dataclasses.replace(p, pool="max"), "bf16")
+    d = inputs_to_dev(x, "bf16")
+    qc, kc, vc = V.pool(p, d["q"], d["k"], d["v"])
+    oc, lse_c, _, _ = V.coarse(p, qc, kc, vc)
+    torch.cuda.synchronize()
+    ref = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=x["idx"], lens=x["len"], cube=cube,
+                    kcube=kcube)
+    assert tuple(kc.shape) == (1, 2, p.Nk, 64) and tuple(qc.shape) == (1, 2, p.Nc, 64)
+    for nm, t in (("q_c", qc), ("k_c", kc), ("v_c", vc), ("o_c", oc), ("lse_c", lse_c)):
+        np.testing.assert_allclose(host(t), ref[nm], rtol=1e-4, atol=1e-5, err_msg=nm)
+    off, k2q = V.index_transpose(p, d["idx"], d["len"])
+    torch.cuda.synchronize()
+    off, k2q = host(off), host(k2q)
+    assert off.shape == (1, 2, p.Nk + 1)
+    for h in range(2):
+        rows = [[] for _ in range(p.Nk)]
+        for i in range(p.Nc):
+            for j in x["idx"][0, h, i, :x["len"][0, h, i]]:
+                rows[j].append(i)
+        got = [list(k2q[0, h, off[0, h, j]:off[0, h, j + 1]]) for j in range(p.Nk)]
+        assert got == rows
+    V.validate_lists(p, d["idx"], d["len"])
