@@ -170,17 +170,20 @@ def train_measure(name: str, steps: int, warmup: int) -> dict:
             "combine_bwd_frac_hbm_peak": round(cb_bytes / (st[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
-def tile_case(V, torch, name, q, k, v, gc, gf, cube, steps=5):
-    """Forward of one workload's inputs with cubes of shape `cube` at the same
-    token-level sparsity as K = 32 with 64-token tiles (K * Bt = 2048)."""
+def tile_case(V, torch, name, q, k, v, gc, gf, cube, steps=5, kcube=None):
+    """Forward of one workload's inputs with query cubes of shape `cube` and
+    key blocks of shape `kcube` (default: the cube) at the same token-level
+    sparsity as K = 32 with 64-token tiles (K * Bk = 2048 keys per query)."""
     B, heads, T, H, W, d = q.shape
     bt = cube[0] * cube[1] * cube[2]
-    p = V.Problem(B, heads, T, H, W, d, topk=max(1, 32 * 64 // bt), cube=cube)
+    kc = cube if kcube is None else kcube
+    bk = kc[0] * kc[1] * kc[2]
+    p = V.Problem(B, heads, T, H, W, d, topk=max(1, 32 * 64 // bk), cube=cube, kcube=kcube)
     ws = V.workspace(p, q)
     o = torch.empty_like(q)
     idx = torch.empty((B, heads, p.Nc, p.stride), dtype=torch.int32, device=q.device)
     lens = torch.empty((B, heads, p.Nc), dtype=torch.int32, device=q.device)
-    pooled = [torch.empty((B, heads, p.Nc, d), dtype=torch.float32, device=q.device) for _ in range(4)]
+    pooled = [torch.empty((B, heads, n, d), dtype=torch.float32, device=q.device) for n in (p.Nc, p.Nk, p.Nk, p.Nc)]
     lse_c = torch.empty((B, heads, p.Nc), dtype=torch.float32, device=q.device)
     for _ in range(2):
         V.forward(p, q, k, v, gc, gf, idx=idx, lens=lens, ws=ws, out=o)
@@ -198,8 +201,8 @@ def tile_case(V, torch, name, q, k, v, gc, gf, cube, steps=5):
     torch.cuda.synchronize()
     fwd_ms = ev[0].elapsed_time(ev[1]) / steps
     fine_ms = ev[2].elapsed_time(ev[3]) / steps
-    flop = 4.0 * bt * bt * d * int(lens.sum().item())
-    return {"workload": name, "cube": list(cube), "tile_tokens": bt, "topk": p.topk,
+    flop = 4.0 * bt * bk * d * int(lens.sum().item())
+    return {"workload": name, "cube": list(cube), "key_block": list(kc), "tile_tokens": [bt, bk], "topk": p.topk,
             "forward_ms": round(fwd_ms, 4), "fine_combine_ms": round(fine_ms, 4),
             "fine_TFLOP_per_s": round(flop / (fine_ms * 1e-3) / 1e12, 2),
             "forward_TFLOP_per_s": round(flop / (fwd_ms * 1e-3) / 1e12, 2),
@@ -208,25 +211,31 @@ def tile_case(V, torch, name, q, k, v, gc, gf, cube, steps=5):
 
 def tile_tradeoff(V, WL, torch, main_name, main_inputs):
     """The tile-size trade-off: the same inputs with 32-, 64- and 128-token
-    tiles where the latent allows them (a cube side must divide the latent's,
-    and Nc must stay within the coarse stage's limit)."""
+    tiles, square (Bt x Bt) and with 64-token query cubes over 32- or
+    128-token key blocks (Bq x Bk), where the latent allows them (a side must
+    divide the latent's, and Nc, Nk must stay within the coarse stage's
+    limit)."""
+    def fits(shape, cube):
+        T, H, W = shape
+        n = cube[0] * cube[1] * cube[2]
+        return not (T % cube[0] or H % cube[1] or W % cube[2]) and T * H * W // n <= V.max_cubes()
+
+    q64 = (4, 4, 4)
+    shapes = [(c, None) for c in ((4, 4, 4), (4, 4, 8), (2, 4, 4))] + [(q64, (2, 4, 4)), (q64, (4, 4, 8))]
     out = []
-    for cube in ((4, 4, 4), (4, 4, 8), (2, 4, 4)):
-        T, H, W = main_inputs[0].shape[2:5]
-        bt = cube[0] * cube[1] * cube[2]
-        if T % cube[0] or H % cube[1] or W % cube[2] or T * H * W // bt > V.max_cubes():
-            continue
-        out.append(tile_case(V, torch, main_name, *main_inputs, cube))
-        log(f"  tiles {cube}: {out[-1]}")
-    for name, cubes in (("bf16_480p_20x28x52", ((4, 4, 4), (2, 4, 4))),
-                        ("bf16_16x32x32_spikes", ((4, 4, 4), (2, 4, 4), (4, 4, 8)))):
-        x = WL.make_inputs(name)
-        t = [torch.from_numpy(x[n]).to("cuda:0").to(torch.bfloat16).contiguous() for n in ("q", "k", "v", "g_c", "g_f")]
-        del x
-        for cube in cubes:
-            out.append(tile_case(V, torch, name, *t, cube))
-            log(f"  tiles {cube}: {out[-1]}")
-        del t
+    for name, inputs in [(main_name, main_inputs), ("bf16_480p_20x28x52", None), ("bf16_16x32x32_spikes", None)]:
+        if inputs is None:
+            x = WL.make_inputs(name)
+            inputs = [torch.from_numpy(x[n]).to("cuda:0").to(torch.bfloat16).contiguous()
+                      for n in ("q", "k", "v", "g_c", "g_f")]
+            del x
+        shape = tuple(inputs[0].shape[2:5])
+        for cube, kcube in shapes:
+            if not fits(shape, cube) or (kcube is not None and not fits(shape, kcube)):
+                continue
+            out.append(tile_case(V, torch, name, *inputs, cube, kcube=kcube))
+            log(f"  tiles {cube} x {kcube or cube}: {out[-1]}")
+        del inputs
     return out
 
 
@@ -270,6 +279,9 @@ def main() -> int:
     ap.add_argument("--copy-mib", type=int, default=2048)
     ap.add_argument("--train", default="train_bf16_16x32x32_varlen,bf16_720p_24x44x80",
                     help="comma-separated workloads whose forward + backward are timed ('' = none)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the max-pool, tile-size and dense-attention context measurements (so a "
+                         "kernel trace of the run holds the benchmark workload's launches only)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -432,6 +444,29 @@ def main() -> int:
     }
     log(f"forward {ms_step:.3f} ms/step = {value:.1f} TFLOP/s; pool {stage_ms[0]:.3f} ms, "
         f"coarse {stage_ms[1]:.3f} ms, fine+combine {stage_ms[2]:.3f} ms ({achieved:.1f} TFLOP/s)")
+    line["variants"] = None
+    line["dense_attention_context"] = None
+    if not args.no_variants:
+        variants(args, V, WL, torch, w, p, (q, k, v, gc, gf), idx, lens, ws, o, achieved, line)
+    line["train"] = []
+    for name in [t for t in args.train.split(",") if t]:
+        log(f"timing forward + backward of {name}")
+        line["train"].append(train_measure(name, max(1, min(args.steps, 10)), 2))
+        log(f"  {line['train'][-1]}")
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_heads} head(s)")
+        line["cpu_baseline"] = cpu_baseline(w.name, list(range(args.cpu_heads)))
+        log(f"cpu baseline {line['cpu_baseline']['value']:.4f} TFLOP/s")
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def variants(args, V, WL, torch, w, p, inputs, idx, lens, ws, o, achieved, line):
+    """Context measurements beside the benchmark: the max-pool variant, the
+    tile-size trade-off and dense flash attention on the same chip."""
+    q, k, v, gc, gf = inputs
     # The max-pool variant of the coarse pooling on the same workload (forward).
     import dataclasses
     pm = dataclasses.replace(p, pool="max")
@@ -455,19 +490,6 @@ def main() -> int:
         ctx["fine_kernel_vs_dense"] = round(achieved / ctx["tflops"], 3)
     line["dense_attention_context"] = ctx
     log(f"dense flash SDPA context: {ctx}")
-    line["train"] = []
-    for name in [t for t in args.train.split(",") if t]:
-        log(f"timing forward + backward of {name}")
-        line["train"].append(train_measure(name, max(1, min(args.steps, 10)), 2))
-        log(f"  {line['train'][-1]}")
-    if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle on {args.cpu_heads} head(s)")
-        line["cpu_baseline"] = cpu_baseline(w.name, list(range(args.cpu_heads)))
-        log(f"cpu baseline {line['cpu_baseline']['value']:.4f} TFLOP/s")
-    else:
-        line["cpu_baseline"] = None
-    print(json.dumps(line), flush=True)
-    return 0
 
 
 if __name__ == "__main__":
