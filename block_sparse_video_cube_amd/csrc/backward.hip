@@ -99,6 +99,45 @@ hipError_t launch_index_transpose(const Launch& L, const int32_t* idx, const int
   return hipGetLastError();
 }
 
+// Union of the transposed lists of key blocks 2P and 2P + 1 (16-token
+// blocks, which the dK / dV kernels take two at a time): a merge of two
+// ascending lists, one thread per pair, written where block 2P's list starts
+// (the union is no longer than the two lists together). Offsets are clamped
+// to the k2q array, so malformed offsets cannot move a write outside it.
+__global__ __launch_bounds__(256) void k2q_pair_kernel(const int32_t* __restrict__ off,
+                                                       const int32_t* __restrict__ k2q, int32_t* __restrict__ k2u,
+                                                       int32_t* __restrict__ plen, int Nq, int Nk, int stride) {
+  const int P = blockIdx.x * 256 + threadIdx.x;
+  const long bh = blockIdx.y;
+  const int npairs = (Nk + 1) >> 1;
+  if (P >= npairs) return;
+  const int cap = Nq * stride;
+  const int32_t* o = off + bh * (Nk + 1);
+  const int32_t* src = k2q + bh * (long)cap;
+  int32_t* dst = k2u + bh * (long)cap;
+  int a = min(max(o[2 * P], 0), cap);
+  const int a1 = min(max(o[2 * P + 1], a), cap);
+  int b = a1;
+  const int b1 = 2 * P + 1 < Nk ? min(max(o[2 * P + 2], a1), cap) : a1;
+  const int w0 = a;
+  int w = w0;
+  while (a < a1 || b < b1) {
+    const int va = a < a1 ? src[a] : 0x7fffffff, vb = b < b1 ? src[b] : 0x7fffffff;
+    if (va == vb) { dst[w++] = va | (3 << 24); ++a; ++b; }
+    else if (va < vb) { dst[w++] = va | (1 << 24); ++a; }
+    else { dst[w++] = vb | (2 << 24); ++b; }
+  }
+  plen[bh * npairs + P] = w - w0;
+}
+
+hipError_t launch_key_pairs(const Launch& L, const int32_t* k2q_off, const int32_t* k2q, int32_t* k2u,
+                            int32_t* plen) {
+  const int Nk = L.gk.Nc, npairs = (Nk + 1) / 2;
+  hipLaunchKernelGGL(k2q_pair_kernel, dim3((npairs + 255) / 256, L.BH), dim3(256), 0, L.stream, k2q_off, k2q, k2u,
+                     plen, L.g.Nc, Nk, L.stride);
+  return hipGetLastError();
+}
+
 // Lists valid? len in [0, stride], ids in [0, Nk), strictly increasing.
 __global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict__ idx,
                                                        const int32_t* __restrict__ len, int32_t* flag, long rows,

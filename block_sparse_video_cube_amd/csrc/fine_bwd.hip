@@ -89,7 +89,7 @@ __global__ __launch_bounds__(1024) void order_by_count_kernel(const int32_t* __r
 
 // Two waves per SIMD (the register budget of 256 per lane holds the whole
 // working set without spills at either head dim).
-template <int D, int NW>
+template <int D, int NW, bool KPAIR>
 __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const int32_t* __restrict__ order,
@@ -128,10 +128,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
 
-  // Key chunks: key block list[c >> ksh], its chunk h = c & kmask.
-  const int ksh = chunk_shift(gk), kmask = (1 << ksh) - 1;
+  // Key chunks: key block list[c >> ksh], its chunk h = c & kmask; 16-token
+  // key blocks go two to a chunk (entries 2c, 2c + 1; the upper half of the
+  // last chunk of an odd list repeats the lower block and is masked).
+  constexpr bool kpair = KPAIR;   // gk.B == 16
+  const int ksh = kpair ? 0 : chunk_shift(gk), kmask = (1 << ksh) - 1;
   uint32_t roff[G::RINS / NW];
-  row_tile_offsets<D, NW>(gk, wv, lane, roff);
+  row_tile_offsets<D, NW>(gk, wv, lane, roff, kpair ? 15 : 31);
   uint32_t toffs[G::MB][2][2];   // transposed reads of the K row tile (dQ^T += K^T dS^T)
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
@@ -151,9 +154,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
   };
   const uint32_t rkb = lds_addr(rk), rvb = lds_addr(rv);
   auto issue = [&](int c) {
-    const int e = c >> ksh, h = c & kmask, st = c & 1;
+    const int e = kpair ? 2 * c : c >> ksh, h = kpair ? 0 : c & kmask, st = c & 1;
     if ((e & 63) == 0 && h == 0) cubes(e);
     const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + chunk_bytes(h);
+    if constexpr (kpair) {   // entries e, e + 1 share a block of 64 (e is even)
+      const uint32_t rc1 = __builtin_amdgcn_readlane(rcube, min(e + 1, L - 1) & 63);
+      issue_row_tile2<D, NW>(uniform_ptr(Kb + rc), uniform_ptr(Kb + rc1), roff, rkb + st * (G::RUNITS * 16), wv);
+      issue_row_tile2<D, NW>(uniform_ptr(Vb + rc), uniform_ptr(Vb + rc1), roff, rvb + st * (G::RUNITS * 16), wv);
+      return;
+    }
     issue_row_tile<D, NW>(uniform_ptr(Kb + rc), roff, rkb + st * (G::RUNITS * 16), wv);
     issue_row_tile<D, NW>(uniform_ptr(Vb + rc), roff, rvb + st * (G::RUNITS * 16), wv);
   };
@@ -161,7 +170,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
   // Per chunk: wait for this wave's loads, barrier (every wave's share is in
   // LDS and every wave is done with the other stage), issue the next chunk,
   // compute this one.
-  const int nch = L << ksh;
+  const int nch = kpair ? (L + 1) >> 1 : L << ksh;
+  const bool khalf = kpair && (L & 1);   // keys 16-31 of the last chunk absent
   if (nch > 0) issue(0);
   for (int c = 0; c < nch; ++c) {
     wait_vmcnt<0>();
@@ -181,6 +191,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
     for (int ks = 0; ks < G::KS; ++ks) {
       sx = mfma32_bf16(kf[ks], qf[ks], sx);
       dp = mfma32_bf16(vf[ks], df[ks], dp);
+    }
+    if (kpair && khalf && c == nch - 1) {   // accumulator entries 8-15 hold keys 16-31
+#pragma unroll
+      for (int e = 8; e < 16; ++e) sx[e] = -INFINITY;
     }
     bf16x8 sf[2];
 #pragma unroll
@@ -219,15 +233,60 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
 // In both dK / dV kernels g is the grid of key blocks (the workgroup's own
 // tokens) and gq the grid of query cubes (the partners walked).
 //
+// The keys a dK / dV workgroup owns and the query cubes it walks. Ordinary
+// blocks: key block j (its slot, through `order` when given), lane n32 of key
+// wave kw is the block's token 32 kw + n32, and the list is j's transposed
+// list. KPAIR (16-token key blocks, two per 32-key MFMA column block): blocks
+// 2P and 2P + 1, lane n32 is token n32 % 16 of block 2P + n32 / 16, and the
+// list is the union of the two transposed lists (k2q_pair_kernel), each entry
+// a query cube with bit 24 (listed by 2P) and bit 25 (by 2P + 1) set.
+struct KeyWalk {
+  int bh, j, lk, L;
+  bool own;   // the lane's key block exists (the last pair of an odd Nk has one)
+  const int32_t* list;
+};
+template <bool KPAIR>
+__device__ __forceinline__ KeyWalk key_walk(const Grid& g, const Grid& gq, const int32_t* k2q_off,
+                                            const int32_t* k2q, const int32_t* order, const int32_t* plen,
+                                            int stride, int kw, int n32) {
+  KeyWalk w;
+  const int slot = xcd_remap(blockIdx.x, gridDim.x);
+  const int cap = gq.Nc * stride;
+  if constexpr (KPAIR) {
+    const int npairs = (g.Nc + 1) >> 1;
+    w.bh = slot / npairs;
+    const int P = slot - w.bh * npairs;
+    const int32_t* offs = k2q_off + (long)w.bh * (g.Nc + 1);
+    const int t0 = min(max(offs[2 * P], 0), cap);
+    w.L = min(max(plen[(long)w.bh * npairs + P], 0), cap - t0);
+    w.list = k2q + (long)w.bh * cap + t0;
+    const int jl = 2 * P + (n32 >> 4);
+    w.own = jl < g.Nc;
+    w.j = w.own ? jl : 2 * P;
+    w.lk = n32 & 15;
+  } else {
+    w.bh = slot / g.Nc;
+    w.j = order != nullptr ? order[slot] : slot - w.bh * g.Nc;
+    const int32_t* offs = k2q_off + (long)w.bh * (g.Nc + 1);
+    const int t0 = min(max(offs[w.j], 0), cap), t1 = min(max(offs[w.j + 1], t0), cap);
+    w.list = k2q + (long)w.bh * cap + t0;
+    w.L = t1 - t0;
+    w.own = true;
+    w.lk = 32 * kw + n32;
+  }
+  return w;
+}
+//
 // dK and dV at 64 channels: every wave computes both for its 32 keys, two
 // waves per SIMD. (At 128 channels the two accumulators, 128 registers, and
 // the lane's K and V rows do not fit 256 registers without spills; the
 // warp-specialized kernel below splits the roles over the waves instead.)
-template <int D, int NW>
+template <int D, int NW, bool KPAIR>
 __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ k2q_off,
-    const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
+    const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const int32_t* __restrict__ plen,
+    const float* __restrict__ lse_f,
     const bf16* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dkc,
     const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
     bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, Grid gq, int stride, float scale) {
@@ -240,17 +299,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
 
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int slot = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = slot / g.Nc;
-  const int j = order != nullptr ? order[slot] : slot - bh * g.Nc;
+  const KeyWalk kwk = key_walk<KPAIR>(g, gq, k2q_off, k2q, order, plen, stride, wv, n32);
+  const int bh = kwk.bh, j = kwk.j, L = kwk.L;
+  const int32_t* list = kwk.list;
   const long tok0 = (long)bh * g.N;
-  const int32_t* offs = k2q_off + (long)bh * (g.Nc + 1);
-  const int t0 = min(max(offs[j], 0), gq.Nc * stride), t1 = min(max(offs[j + 1], t0), gq.Nc * stride);
-  const int32_t* list = k2q + (long)bh * gq.Nc * stride + t0;
-  const int L = t1 - t0;
 
-  // This lane's key: in-cube token 32wv + n32 of cube j.
-  const long n = tok0 + cube_token(g, j, 32 * wv + n32);
+  // This lane's key: token lk of key block j.
+  const long n = tok0 + cube_token(g, j, kwk.lk);
   bf16x8 kf[G::KS], vf[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
@@ -278,10 +333,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
   const char* Lb = reinterpret_cast<const char*>(lse_f + tok0);
   const char* Eb = reinterpret_cast<const char*>(delta + tok0);
   // Per lane, for 64 list entries at a time: the partner cube's first row.
-  int rcube = 0;
+  int rcube = 0, rflag = 3;
   auto cubes = [&](int e0) {
     const int t = e0 + lane;
     int ii = t < L ? list[t] : 0;
+    if constexpr (KPAIR) {
+      rflag = (ii >> 24) & 3;
+      ii &= 0xFFFFFF;
+    }
     ii = (ii >= 0 && ii < gq.Nc) ? ii : 0;
     rcube = cube_first(gq, ii);
   };
@@ -307,6 +366,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
   for (int c = 0; c < nch; ++c) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
+    // Whether the query cube of chunk c is listed by this lane's key block
+    // (read before issue(c + 1) may refresh the entries).
+    const bool kvalid = !KPAIR || ((__builtin_amdgcn_readlane(rflag, (c >> qsh) & 63) >> (n32 >> 4)) & 1);
     if (c + 1 < nch) issue(c + 1);
     const int st = c & 1;
     // LSE and delta of the accumulator rows this lane holds: rows 8m + 4hf + r.
@@ -330,7 +392,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);
+      float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);
+      if constexpr (KPAIR) p = kvalid ? p : 0.f;
       pf[e >> 3][e & 7] = (bf16)p;
       sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl[e]));
     }
@@ -349,8 +412,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
   const long cj = ((long)bh * g.Nc + j) * D;
   const uint8_t* karg_j = karg != nullptr ? karg + cj : nullptr;
   const uint8_t* varg_j = varg != nullptr ? varg + cj : nullptr;
-  const int lk = 32 * wv + n32;   // the key's position in its cube
+  const int lk = kwk.lk;   // the key's position in its block
   const float inv_b = 1.0f / (float)g.B;
+  if (!kwk.own) return;   // no barrier below
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
@@ -377,11 +441,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
 // roles swap with the workgroup's parity, so that the two workgroups sharing
 // a CU tend to put a wave of each role on every SIMD. One accumulator array
 // holds dV^T or dK^T, so a wave's working set is the dK pass's.
-template <int D, int NW>
+template <int D, int NW, bool KPAIR>
 __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ k2q_off,
-    const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const float* __restrict__ lse_f,
+    const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const int32_t* __restrict__ plen,
+    const float* __restrict__ lse_f,
     const bf16* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dkc,
     const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
     bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, Grid gq, int stride, float scale) {
@@ -397,17 +462,13 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kw = wv % NW;                                     // keys 32kw .. 32kw + 31
   const bool isk = ((wv / NW) ^ (int)(blockIdx.x & 1)) != 0;  // this wave computes dK (else dV)
-  const int slot = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = slot / g.Nc;
-  const int j = order != nullptr ? order[slot] : slot - bh * g.Nc;
+  const KeyWalk kwk = key_walk<KPAIR>(g, gq, k2q_off, k2q, order, plen, stride, kw, n32);
+  const int bh = kwk.bh, j = kwk.j, L = kwk.L;
+  const int32_t* list = kwk.list;
   const long tok0 = (long)bh * g.N;
-  const int32_t* offs = k2q_off + (long)bh * (g.Nc + 1);
-  const int t0 = min(max(offs[j], 0), gq.Nc * stride), t1 = min(max(offs[j + 1], t0), gq.Nc * stride);
-  const int32_t* list = k2q + (long)bh * gq.Nc * stride + t0;
-  const int L = t1 - t0;
 
-  // This lane's key: in-cube token 32kw + n32 of cube j.
-  const long n = tok0 + cube_token(g, j, 32 * kw + n32);
+  // This lane's key: token lk of key block j.
+  const long n = tok0 + cube_token(g, j, kwk.lk);
   bf16x8 kf[G::KS], vf[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) {
@@ -433,10 +494,14 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   const char* Db = reinterpret_cast<const char*>(dof + tok0 * D);
   const char* Lb = reinterpret_cast<const char*>(lse_f + tok0);
   const char* Eb = reinterpret_cast<const char*>(delta + tok0);
-  int rcube = 0;
+  int rcube = 0, rflag = 3;
   auto cubes = [&](int e0) {
     const int t = e0 + lane;
     int ii = t < L ? list[t] : 0;
+    if constexpr (KPAIR) {
+      rflag = (ii >> 24) & 3;
+      ii &= 0xFFFFFF;
+    }
     ii = (ii >= 0 && ii < gq.Nc) ? ii : 0;
     rcube = cube_first(gq, ii);
   };
@@ -461,6 +526,7 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   for (int c = 0; c < nch; ++c) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
+    const bool kvalid = !KPAIR || ((__builtin_amdgcn_readlane(rflag, (c >> qsh) & 63) >> (n32 >> 4)) & 1);
     if (c + 1 < nch) issue(c + 1);
     const int st = c & 1;
     float lse2[16];
@@ -477,6 +543,12 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     for (int ks = 0; ks < G::KS; ++ks) sx = mfma32_bf16(row_frag<D>(rq[st], n32, hf, ks), kf[ks], sx);
 #pragma unroll
     for (int e = 0; e < 16; ++e) sx[e] = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);   // P
+    if constexpr (KPAIR) {
+      if (!kvalid) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sx[e] = 0.f;
+      }
+    }
     const char* qtile = reinterpret_cast<const char*>(rq[st]);
     const char* dtile = reinterpret_cast<const char*>(rd[st]);
     if (isk) {
@@ -518,8 +590,9 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   const float* xc = (isk ? dkc : dvc) + cj;
   bf16* out = isk ? dk : dv;
   const float sc = isk ? scale : 1.0f;
-  const int lk = 32 * kw + n32;   // the key's position in its cube
+  const int lk = kwk.lk;   // the key's position in its block
   const float inv_b = 1.0f / (float)g.B;
+  if (!kwk.own) return;   // no barrier below
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
@@ -547,24 +620,31 @@ template <int D, int NW>
 static void launch_dq(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
                       const int32_t* len, const int32_t* qorder, const float* lse_f, const bf16* dof,
                       const float* delta, const float* dqc, const uint8_t* qarg, bf16* dq) {
-  hipLaunchKernelGGL((fine_bwd_dq_kernel<D, NW>), dim3(L.BH * L.g.Nc), dim3(64 * NW), 0, L.stream, q, k, v, idx,
-                     len, qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.gk, L.stride, L.scale);
+  if (L.gk.B == 16)
+    hipLaunchKernelGGL((fine_bwd_dq_kernel<D, NW, true>), dim3(L.BH * L.g.Nc), dim3(64 * NW), 0, L.stream, q, k, v,
+                       idx, len, qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.gk, L.stride, L.scale);
+  else
+    hipLaunchKernelGGL((fine_bwd_dq_kernel<D, NW, false>), dim3(L.BH * L.g.Nc), dim3(64 * NW), 0, L.stream, q, k, v,
+                       idx, len, qorder, lse_f, dof, delta, dqc, qarg, dq, L.g, L.gk, L.stride, L.scale);
 }
 
 // dK / dV: one workgroup per key block, Bk/32 waves (64 channels) or 2 Bk/32
-// (128 channels, warp-specialized).
-template <int D, int NW>
+// (128 channels, warp-specialized); 16-token key blocks go in pairs (KPAIR),
+// one 32-key wave (or two) per pair, over the pairs' union lists.
+template <int D, int NW, bool KPAIR>
 static void launch_dkdv(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* k2q_off,
-                        const int32_t* k2q, const int32_t* korder, const float* lse_f, const bf16* dof,
-                        const float* delta, const float* dkc, const float* dvc, const uint8_t* karg,
-                        const uint8_t* varg, bf16* dk, bf16* dv) {
-  const dim3 grid(L.BH * L.gk.Nc);
+                        const int32_t* k2q, const int32_t* korder, const int32_t* plen, const float* lse_f,
+                        const bf16* dof, const float* delta, const float* dkc, const float* dvc,
+                        const uint8_t* karg, const uint8_t* varg, bf16* dk, bf16* dv) {
+  const dim3 grid(L.BH * (KPAIR ? (L.gk.Nc + 1) / 2 : L.gk.Nc));
   if constexpr (D == 64)
-    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW>), grid, dim3(64 * NW), 0, L.stream, q, k, v, k2q_off, k2q,
-                       korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.gk, L.g, L.stride, L.scale);
+    hipLaunchKernelGGL((fine_bwd_dkdv_kernel<D, NW, KPAIR>), grid, dim3(64 * NW), 0, L.stream, q, k, v, k2q_off,
+                       k2q, korder, plen, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.gk, L.g, L.stride,
+                       L.scale);
   else
-    hipLaunchKernelGGL((fine_bwd_dkdv_ws_kernel<D, NW>), grid, dim3(128 * NW), 0, L.stream, q, k, v, k2q_off, k2q,
-                       korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.gk, L.g, L.stride, L.scale);
+    hipLaunchKernelGGL((fine_bwd_dkdv_ws_kernel<D, NW, KPAIR>), grid, dim3(128 * NW), 0, L.stream, q, k, v,
+                       k2q_off, k2q, korder, plen, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.gk, L.g,
+                       L.stride, L.scale);
 }
 
 template <int D>
@@ -572,34 +652,50 @@ static void fine_bwd_launch(const Launch& L, const bf16* q, const bf16* k, const
                             const int32_t* len, const int32_t* qorder, const int32_t* k2q_off, const int32_t* k2q,
                             const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
                             const float* dqc, const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
-                            const uint8_t* qarg, const uint8_t* karg, const uint8_t* varg) {
+                            const uint8_t* qarg, const uint8_t* karg, const uint8_t* varg, const int32_t* k2u,
+                            const int32_t* plen) {
   if (L.g.B == 32) launch_dq<D, 1>(L, q, k, v, idx, len, qorder, lse_f, dof, delta, dqc, qarg, dq);
   else if (L.g.B == 128) launch_dq<D, 4>(L, q, k, v, idx, len, qorder, lse_f, dof, delta, dqc, qarg, dq);
   else launch_dq<D, 2>(L, q, k, v, idx, len, qorder, lse_f, dof, delta, dqc, qarg, dq);
-  if (L.gk.B == 32)
-    launch_dkdv<D, 1>(L, q, k, v, k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv);
+  if (L.gk.B == 16)
+    launch_dkdv<D, 1, true>(L, q, k, v, k2q_off, k2u, nullptr, plen, lse_f, dof, delta, dkc, dvc, karg, varg, dk,
+                            dv);
+  else if (L.gk.B == 32)
+    launch_dkdv<D, 1, false>(L, q, k, v, k2q_off, k2q, korder, nullptr, lse_f, dof, delta, dkc, dvc, karg, varg,
+                             dk, dv);
   else if (L.gk.B == 128)
-    launch_dkdv<D, 4>(L, q, k, v, k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv);
+    launch_dkdv<D, 4, false>(L, q, k, v, k2q_off, k2q, korder, nullptr, lse_f, dof, delta, dkc, dvc, karg, varg,
+                             dk, dv);
   else
-    launch_dkdv<D, 2>(L, q, k, v, k2q_off, k2q, korder, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv);
+    launch_dkdv<D, 2, false>(L, q, k, v, k2q_off, k2q, korder, nullptr, lse_f, dof, delta, dkc, dvc, karg, varg,
+                             dk, dv);
 }
 
 hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
                            const int32_t* len, const int32_t* qorder, const int32_t* k2q_off, const int32_t* k2q,
                            const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
                            const float* dqc, const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
-                           const uint8_t* args) {
+                           const uint8_t* args, int32_t* pairs) {
   // Argmax planes in launch_pool's layout: q (Nq cubes), then k and v (Nk blocks).
   const long qplane = (long)L.BH * L.g.Nc * L.D, kplane = (long)L.BH * L.gk.Nc * L.D;
   const uint8_t* qarg = args;
   const uint8_t* karg = args != nullptr ? args + qplane : nullptr;
   const uint8_t* varg = args != nullptr ? args + qplane + kplane : nullptr;
+  int32_t* k2u = nullptr;
+  int32_t* plen = nullptr;
+  if (L.gk.B == 16) {
+    if (pairs == nullptr) return hipErrorInvalidValue;
+    k2u = pairs;
+    plen = pairs + (long)L.BH * L.g.Nc * L.stride;
+    const hipError_t e = launch_key_pairs(L, k2q_off, k2q, k2u, plen);
+    if (e != hipSuccess) return e;
+  }
   if (L.D == 64)
     fine_bwd_launch<64>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk,
-                        dv, qarg, karg, varg);
+                        dv, qarg, karg, varg, k2u, plen);
   else
     fine_bwd_launch<128>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq,
-                         dk, dv, qarg, karg, varg);
+                         dk, dv, qarg, karg, varg, k2u, plen);
   return hipGetLastError();
 }
 

@@ -64,17 +64,25 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
 
 // Per-lane byte offsets (within a chunk) of wave wv's share of a row tile's
 // loads when NW waves share them: load t of the wave is unit
-// p = (wv*RINS/NW + t)*64 + lane.
+// p = (wv*RINS/NW + t)*64 + lane. With rmask = 15 the chunk is two 16-token
+// blocks (rows 0-15 and 16-31, each load within one of them) and offsets are
+// taken from the first row of the row's own block.
 template <int D, int NW> __device__ __forceinline__ void row_tile_offsets(const Grid& g, int wv, int lane,
-                                                                          uint32_t* off) {
+                                                                          uint32_t* off, int rmask = 31) {
   using G = ChunkGeom<D>;
   static_assert(G::RINS % NW == 0, "every wave issues whole 1 KB loads");
 #pragma unroll
   for (int t = 0; t < G::RINS / NW; ++t) {
     const int p = (wv * (G::RINS / NW) + t) * 64 + lane, kappa = p / G::U;
     const int u = (p % G::U) ^ kswz<G::U>(kappa);
-    off[t] = (uint32_t)(chunk_row(g, kappa) * D + u * 8) * 2u;
+    off[t] = (uint32_t)(chunk_row(g, kappa & rmask) * D + u * 8) * 2u;
   }
+}
+// Whether load t of wave wv (NW waves sharing a row tile) fills rows 16-31
+// (a load covers 64 / U consecutive rows, never both halves).
+template <int D, int NW> __device__ __forceinline__ bool row_tile_upper(int wv, int t) {
+  using G = ChunkGeom<D>;
+  return (wv * (G::RINS / NW) + t) * 64 / G::U >= 16;
 }
 // Issue wave wv's share of a row tile: src = first row of the chunk, dst =
 // LDS byte address of the tile.
@@ -83,6 +91,15 @@ template <int D, int NW> __device__ __forceinline__ void issue_row_tile(const vo
   using G = ChunkGeom<D>;
 #pragma unroll
   for (int t = 0; t < G::RINS / NW; ++t) dma16(src, off[t], dst + (wv * (G::RINS / NW) + t) * 1024);
+}
+// The same for a chunk made of two 16-token blocks: rows 0-15 from srcA,
+// rows 16-31 from srcB (offsets from row_tile_offsets with rmask = 15).
+template <int D, int NW> __device__ __forceinline__ void issue_row_tile2(const void* srcA, const void* srcB,
+                                                                        const uint32_t* off, uint32_t dst, int wv) {
+  using G = ChunkGeom<D>;
+#pragma unroll
+  for (int t = 0; t < G::RINS / NW; ++t)
+    dma16(row_tile_upper<D, NW>(wv, t) ? srcB : srcA, off[t], dst + (wv * (G::RINS / NW) + t) * 1024);
 }
 // A operand fragment of a row tile (rows = tokens, k-step ks over channels).
 template <int D> __device__ __forceinline__ bf16x8 row_frag(const bf16* tile, int n32, int hf, int ks) {

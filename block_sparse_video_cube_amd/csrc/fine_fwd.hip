@@ -88,7 +88,10 @@ __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__
 
 // KSAME: key blocks are the query cubes (gk == g), so a key block has NW
 // chunks and its geometry is g's, both known at compile time; otherwise the
-// key blocks' grid gk is read at run time.
+// key blocks' grid gk is read at run time. Key blocks of 16 tokens are taken
+// two per chunk (list entries 2c and 2c + 1; the upper half of the last
+// chunk of an odd list repeats the lower block and is masked out of the
+// softmax).
 template <int D, int NW, bool KSAME, bool FUSED>
 __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -137,10 +140,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   // kappa = p / U, logical unit (p % U) ^ kswz(kappa), i.e. in-block token
   // 32h + kappa.
   constexpr int KPW = C::KINS / NW;   // loads per wave per K (or V) chunk
-  const int ksh = chunk_shift(kg), kmask = (1 << ksh) - 1;
+  const bool kpair = !KSAME && kg.B == 16;   // two 16-token key blocks per chunk
+  const int ksh = kpair ? 0 : chunk_shift(kg), kmask = (1 << ksh) - 1;
   const uint32_t kbase = lds_addr(kbuf), vbase = lds_addr(vbuf);
   uint32_t koff[KPW];
-  row_tile_offsets<D, NW>(kg, wv, lane, koff);
+  row_tile_offsets<D, NW>(kg, wv, lane, koff, kpair ? 15 : 31);
   // Byte offsets of the list's key blocks, 64 entries at a time, one per
   // lane: kcube = first key row of the block within this head's K (and V). A load
   // reads it with readlane, so the per-chunk address work is scalar and
@@ -160,23 +164,51 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   auto chunk_bytes = [&](int h) {
     return (KSAME && NW == 1) ? 0u : (uint32_t)(chunk_first(kg, h) * D) * 2u;
   };
+  // First list entry of chunk c and the chunk's part h of it.
+  auto entry_of = [&](int c, int& e, int& h) {
+    if (KSAME) { e = c / NW; h = c % NW; }
+    else if (kpair) { e = 2 * c; h = 0; }
+    else { e = c >> ksh; h = c & kmask; }
+  };
   auto issue_k = [&](int c) {
-    const int e = KSAME ? c / NW : c >> ksh, h = KSAME ? c % NW : c & kmask;
+    int e, h;
+    entry_of(c, e, h);
     if ((e & 63) == 0 && h == 0) cubes_k(e);
     const uint32_t dst = kbase + (c % C::KST) * (C::KUNITS * 16);
     const uint32_t kc = __builtin_amdgcn_readlane(kcube, e & 63);
     const void* src = uniform_ptr(reinterpret_cast<const char*>(K) + kc + chunk_bytes(h));
+    if (!KSAME && kpair) {   // entries e, e + 1 share a block of 64 (e is even)
+      const uint32_t kc1 = __builtin_amdgcn_readlane(kcube, min(e + 1, L - 1) & 63);
+      issue_row_tile2<D, NW>(src, uniform_ptr(reinterpret_cast<const char*>(K) + kc1), koff, dst, wv);
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < KPW; ++t) dma16(src, koff[t], dst + (wv * KPW + t) * 1024);
   };
   auto issue_v = [&](int c) {
-    const int e = KSAME ? c / NW : c >> ksh, h = KSAME ? c % NW : c & kmask;
+    int e, h;
+    entry_of(c, e, h);
     if ((e & 63) == 0 && h == 0) cubes_v(e);
     const uint32_t dst = vbase + (c % C::VST) * (C::VUNITS * 16);
     const uint32_t vc = __builtin_amdgcn_readlane(vcube, e & 63);
     const void* src = uniform_ptr(reinterpret_cast<const char*>(V) + vc + chunk_bytes(h));
+    if (!KSAME && kpair) {
+      const uint32_t vc1 = __builtin_amdgcn_readlane(vcube, min(e + 1, L - 1) & 63);
+      issue_row_tile2<D, NW>(src, uniform_ptr(reinterpret_cast<const char*>(V) + vc1), koff, dst, wv);
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < KPW; ++t) dma16(src, koff[t], dst + (wv * KPW + t) * 1024);
+  };
+  // Keys 16-31 of the last chunk of an odd list of 16-token blocks do not
+  // exist: their scores (accumulator entries 8-15) are set to -inf.
+  const int nch = KSAME ? NW * L : kpair ? (L + 1) >> 1 : L << ksh;
+  const bool khalf = !KSAME && kpair && (L & 1);
+  auto mask_tail = [&](f32x16& sx, int c) {
+    if (!KSAME && khalf && c == nch - 1) {
+#pragma unroll
+      for (int e = 8; e < 16; ++e) sx[e] = -INFINITY;
+    }
   };
   // S^T (32 keys x 32 queries) of the K chunk at kb: lane holds, at
   // accumulator index jj, key 8*(jj/4) + 4hf + jj%4 of the lane's query.
@@ -212,7 +244,6 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   // m starts at the row max of chunk 0). O and l always share m, so the
   // result is exact whatever the schedule.
   constexpr float kHeadroom = 16.0f;
-  const int nch = KSAME ? NW * L : L << ksh;
   f32x16 sxa, sxb;
   if (nch > 0) {
     issue_k(0);
@@ -225,6 +256,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     sxa = scores(kbuf);
+    mask_tail(sxa, 0);
     float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sxa[e]);
@@ -263,6 +295,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     if (c + C::VST - 1 < nch) issue_v(c + C::VST - 1);
     if (c + C::KST < nch) issue_k(c + C::KST);
 
+    mask_tail(sx, c);
     float mq = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mq = fmaxf(mq, sx[e]);
@@ -400,18 +433,19 @@ __global__ __launch_bounds__(128) void fine_fwd_f32_kernel(
   float m = -INFINITY, l = 0.f;
   const int L = min(max(len[item], 0), stride);
   const int32_t* list = idx + (long)item * stride;
-  for (int t = 0; t < L * (gk.B / R); ++t) {
-    const int j = list[t / (gk.B / R)], r0 = (t % (gk.B / R)) * R;
+  const int RS = min(R, gk.B), spb = gk.B / RS;   // rows per stage, stages per key block
+  for (int t = 0; t < L * spb; ++t) {
+    const int j = list[t / spb], r0 = (t % spb) * RS;
     if (j < 0 || j >= gk.Nc) continue;
     __syncthreads();
-    for (int e = tid; e < R * D; e += nt) {
+    for (int e = tid; e < RS * D; e += nt) {
       const int r = e / D, d = e - r * D;
       const long src = (tok0 + cube_token(gk, j, r0 + r)) * D + d;
       ks[r][d] = k[src];
       vs[r][d] = v[src];
     }
     __syncthreads();
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < RS; ++r) {
       float z = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) z = fmaf(qv[d], ks[r][d], z);

@@ -22,9 +22,9 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
                                                    float* __restrict__ kc, float* __restrict__ vc,
                                                    uint8_t* __restrict__ qa, uint8_t* __restrict__ ka,
                                                    uint8_t* __restrict__ va, Grid g) {
-  constexpr int CH = D / 8;            // 8-channel chunks per token row
-  constexpr int RPP = 256 / CH;        // token rows per pass
-  constexpr int PASSES = BT / RPP;     // BT = tokens per cube
+  constexpr int CH = D / 8;                      // 8-channel chunks per token row
+  constexpr int RPP = 256 / CH < BT ? 256 / CH : BT;   // token rows per pass (BT = tokens per cube)
+  constexpr int PASSES = BT / RPP;
   __shared__ float part[3][RPP][D + 4];
   __shared__ uint8_t parg[MAX ? 3 : 1][MAX ? RPP : 1][D + 4];
 
@@ -33,6 +33,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
   const int c = blockIdx.x;
   const int ch = tid % CH, rsub = tid / CH;
   const long base = bh * (long)g.N * D;
+  const bool active = rsub < RPP;   // small cubes leave threads without a row
 
   const T* srcs[3] = {q, k, v};
   float* dsts[3] = {qc, kc, vc};
@@ -47,6 +48,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
     for (int e = 0; e < 8; ++e) { acc[w][e] = MAX ? -INFINITY : 0.f; am[w][e] = 0; }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
+    if (!active) break;
     const int l = p * RPP + rsub;   // increasing: a strict compare keeps the first maximum
     const long off = base + (long)cube_token(g, c, l) * D + ch * 8;
 #pragma unroll
@@ -64,13 +66,15 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
       }
     }
   }
+  if (active) {
 #pragma unroll
-  for (int w = 0; w < 3; ++w)
+    for (int w = 0; w < 3; ++w)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      part[w][rsub][ch * 8 + e] = acc[w][e];
-      if (MAX) parg[w][rsub][ch * 8 + e] = (uint8_t)am[w][e];
-    }
+      for (int e = 0; e < 8; ++e) {
+        part[w][rsub][ch * 8 + e] = acc[w][e];
+        if (MAX) parg[w][rsub][ch * 8 + e] = (uint8_t)am[w][e];
+      }
+  }
   __syncthreads();
   for (int t = tid; t < 3 * D; t += 256) {
     const int w = t / D, col = t - w * D;
@@ -110,7 +114,8 @@ static void pool_launch_bt(const Launch& L, const Grid& g, const void* q, const 
 template <typename T, bool MAX, int SEL>
 static void pool_grid(const Launch& L, const Grid& g, const void* q, const void* k, const void* v, float* qc,
                       float* kc, float* vc, uint8_t* qa, uint8_t* ka, uint8_t* va) {
-  if (g.B == 32) pool_launch_bt<T, MAX, 32, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
+  if (g.B == 16) pool_launch_bt<T, MAX, 16, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
+  else if (g.B == 32) pool_launch_bt<T, MAX, 32, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
   else if (g.B == 128) pool_launch_bt<T, MAX, 128, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
   else pool_launch_bt<T, MAX, 64, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
 }

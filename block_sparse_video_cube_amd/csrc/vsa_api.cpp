@@ -14,7 +14,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Dims {
-  long BH, N, Nq, Nk, D, stride;   // Nq query cubes, Nk key blocks per (b, h)
+  long BH, N, Nq, Nk, Bk, D, stride;   // Nq query cubes, Nk key blocks of Bk tokens per (b, h)
   size_t elem;  // bytes per raster element
 };
 
@@ -35,7 +35,7 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
   if (p->T % kt || p->H % kh || p->W % kw) return VSA_ERR_SHAPE;
   const long Bt = (long)ct * ch * cw, Bk = (long)kt * kh * kw;
   if (Bt != 32 && Bt != 64 && Bt != 128) return VSA_ERR_UNSUPPORTED;
-  if (Bk != 32 && Bk != 64 && Bk != 128) return VSA_ERR_UNSUPPORTED;
+  if (Bk != 16 && Bk != 32 && Bk != 64 && Bk != 128) return VSA_ERR_UNSUPPORTED;
   const bool same = kt == ct && kh == ch && kw == cw;
   const long N = (long)p->T * p->H * p->W;
   const long BH = (long)p->B * p->heads;
@@ -67,7 +67,7 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
     L->stream = nullptr;
   }
   if (d != nullptr) {
-    d->BH = BH; d->N = N; d->Nq = Nc; d->Nk = Nk; d->D = p->head_dim; d->stride = stride;
+    d->BH = BH; d->N = N; d->Nq = Nc; d->Nk = Nk; d->Bk = Bk; d->D = p->head_dim; d->stride = stride;
     d->elem = p->dtype == VSA_BF16 ? 2 : 4;
   }
   return VSA_OK;
@@ -147,6 +147,7 @@ struct BwdWs {
   bf16* dof;   // d_o_f
   float *delta, *doc, *dqc, *dkc, *dvc, *p_scr, *ds_scr, *dc_scr;
   int32_t *k2q_off, *k2q, *qorder, *korder;
+  int32_t* pairs;   // 16-token key blocks: union lists of block pairs and their lengths
   uint32_t* k2q_bits;
   uint8_t* args;   // max pooling: argmax positions of q, k, v
   size_t bytes;
@@ -172,6 +173,7 @@ BwdWs carve_bwd_ws(const Dims& d, void* base) {
   w.qorder = c.take<int32_t>(d.BH * d.Nq);
   w.korder = c.take<int32_t>(d.BH * d.Nk);
   w.args = c.take<uint8_t>(d.BH * (d.Nq + 2 * d.Nk) * d.D);
+  w.pairs = d.Bk == 16 ? c.take<int32_t>(d.BH * d.Nq * d.stride + d.BH * ((d.Nk + 1) / 2)) : nullptr;
   w.bytes = c.off;
   return w;
 }
@@ -276,7 +278,7 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                         idx, len, ws.qorder, ws.k2q_off, ws.k2q, ws.korder, s.lse_f, ws.dof, ws.delta, ws.dqc,
                         ws.dkc, ws.dvc, static_cast<bf16*>(dq), static_cast<bf16*>(dk), static_cast<bf16*>(dv),
-                        L.pool_max ? ws.args : nullptr);
+                        L.pool_max ? ws.args : nullptr, ws.pairs);
   return hip_status(e);
 }
 
@@ -414,7 +416,7 @@ vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k,
     e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                         idx, len, ws.qorder, k2q_off, k2q, ws.korder, lse_f, static_cast<const bf16*>(d_o_f), delta,
                         dq_c, dk_c, dv_c, static_cast<bf16*>(dq), static_cast<bf16*>(dk), static_cast<bf16*>(dv),
-                        L.pool_max ? ws.args : nullptr);
+                        L.pool_max ? ws.args : nullptr, ws.pairs);
   return hip_status(e);
 }
 

@@ -68,9 +68,10 @@ typedef enum {
   VSA_ERR_WORKSPACE = 7,   /* workspace / saved buffer smaller than required */
   VSA_ERR_INDEX = 8,       /* an index list failed validation                */
   VSA_ERR_UNSUPPORTED = 9, /* valid request this build does not implement (a
-                              cube of other than 32, 64 or 128 tokens, too
-                              many cubes), an unknown pool_mode or layout, or
-                              in-place tiling                                 */
+                              cube of other than 32, 64 or 128 tokens, a key
+                              block of other than 16 to 128, too many cubes),
+                              an unknown pool_mode or layout, or in-place
+                              tiling                                          */
   VSA_ERR_HIP = 10,        /* a HIP call or kernel launch failed             */
   VSA_ERR_SCALE = 11       /* scale is negative, NaN or infinite             */
 } vsa_status;
@@ -121,9 +122,10 @@ typedef struct {
                             tiled and pooled by this shape, the coarse scores
                             are Nq x Nk (Nq = N/Bt query cubes, Nk = N/Bk key
                             blocks), index lists name key blocks, and topk /
-                            list_stride range over 1..Nk. Same rules as the
-                            cube: powers of two, kcube_w >= 4, Bk in {32, 64,
-                            128}. The tiled layout needs kcube = cube.       */
+                            list_stride range over 1..Nk. Powers of two,
+                            kcube_w >= 4, Bk in {16, 32, 64, 128} (16-token
+                            blocks are taken two at a time by the fine
+                            kernels). The tiled layout needs kcube = cube.  */
 } vsa_problem;
 
 /* Short text for a status code (static storage, never NULL). */

@@ -34,7 +34,8 @@ hipError_t launch_order_by_count(const Launch&, const int32_t*, int32_t*) { retu
 hipError_t launch_fine_bwd(const Launch&, const bf16*, const bf16*, const bf16*, const int32_t*, const int32_t*,
                            const int32_t*, const int32_t*, const int32_t*, const int32_t*, const float*, const bf16*,
                            const float*, const float*, const float*, const float*, bf16*, bf16*, bf16*,
-                           const uint8_t*) { return stub(); }
+                           const uint8_t*, int32_t*) { return stub(); }
+hipError_t launch_key_pairs(const Launch&, const int32_t*, const int32_t*, int32_t*, int32_t*) { return stub(); }
 hipError_t launch_validate_lists(const Launch&, const int32_t*, const int32_t*, int32_t*) { return stub(); }
 }  // namespace vsa
 

@@ -132,11 +132,12 @@ def test_cube_shapes(cube, ok):
 
 
 @pytest.mark.parametrize("kcube,ok", [((2, 4, 4), True), ((4, 4, 8), True), ((1, 8, 4), True), ((4, 4, 4), True),
-                                      ((1, 4, 4), False), ((4, 2, 2), False), ((3, 4, 4), False),
+                                      ((1, 4, 4), True), ((2, 2, 4), True), ((1, 1, 16), True),
+                                      ((1, 2, 4), False), ((4, 2, 2), False), ((3, 4, 4), False),
                                       ((8, 4, 8), False), ((0, 4, 4), False)])
 def test_key_block_shapes(kcube, ok):
-    """Key blocks of their own shape (Bq x Bk tiles): the cube's rules, and
-    all-zero sides mean the query cube."""
+    """Key blocks of their own shape (Bq x Bk tiles): powers of two, Cw >= 4,
+    16 to 128 tokens, and all-zero sides mean the query cube."""
     p = _p(T=8, H=16, W=16, topk=1, kcube=kcube)
     got = N.lib().vsa_workspace_bytes(ctypes.byref(p.c()), 0)
     assert (got > 0) == ok

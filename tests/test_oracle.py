@@ -399,7 +399,8 @@ def test_general_cube_forward_backward_match_autograd(cube):
         np.testing.assert_allclose(full["o"][0, h].reshape(-1, 4), ref[0].numpy(), rtol=1e-11, atol=1e-13)
 
 
-@pytest.mark.parametrize("cube,kcube", [((4, 4, 4), (2, 4, 4)), ((4, 4, 4), (4, 4, 8)), ((2, 4, 4), (4, 4, 4))])
+@pytest.mark.parametrize("cube,kcube", [((4, 4, 4), (2, 4, 4)), ((4, 4, 4), (4, 4, 8)), ((2, 4, 4), (4, 4, 4)),
+                                       ((4, 4, 4), (1, 4, 4))])
 def test_asymmetric_tiles_forward_backward_match_autograd(cube, kcube):
     """Query tiles and key blocks of different shapes (Bq x Bk tiles, the
     summary page's 64 x 16 example generalised): forward and backward against

@@ -693,8 +693,11 @@ def test_general_cube_tiled_equals_raster_and_max_pool(cube):
 
 
 # ------------------------------- key blocks of their own shape (Bq x Bk tiles)
-# (query cube, key block): 64 x 32, 64 x 128, 32 x 128 and 128 x 32 tokens.
-TILE_PAIRS = [((4, 4, 4), (2, 4, 4)), ((4, 4, 4), (4, 4, 8)), ((2, 4, 4), (4, 4, 8)), ((4, 4, 8), (2, 4, 4))]
+# (query cube, key block): 64 x 32, 64 x 128, 32 x 128, 128 x 32 tokens, and
+# 16-token key blocks (taken two per 32-key chunk): 64 x 16 (the summary
+# page's tile), 32 x 16, 128 x 16.
+TILE_PAIRS = [((4, 4, 4), (2, 4, 4)), ((4, 4, 4), (4, 4, 8)), ((2, 4, 4), (4, 4, 8)), ((4, 4, 8), (2, 4, 4)),
+              ((4, 4, 4), (1, 4, 4)), ((2, 4, 4), (2, 2, 4)), ((4, 4, 8), (1, 4, 4))]
 
 
 @pytest.mark.parametrize("cube,kcube", TILE_PAIRS)
@@ -717,7 +720,10 @@ def test_key_block_forward_topk(cube, kcube, dtype, d):
     sel = O.forward(x["q"], x["k"], x["v"], topk=k, cube=cube, kcube=kcube)
     assert sel["s_c"].shape == (1, heads, nq, nk)
     near = check_topk(gi, sel, k)
-    assert near <= NEAR_FRAC * heads * nq
+    # Sanity bound on the near-tie share (every row is still checked): with
+    # 16-token key blocks a row ranks 256 candidates for 32 places, and at 64
+    # rows the 5% share is 3 rows, so up to 8 are allowed.
+    assert near <= max(NEAR_FRAC * heads * nq, 8)
     ref = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=gl, cube=cube, kcube=kcube)
     assert_close(host(o), ref["o"], dtype, f"{cube}x{kcube} o")
     sv = V.saved_views(p, saved)
@@ -738,7 +744,7 @@ def test_key_block_backward(cube, kcube, d):
     backward_compare(x, p, "bf16")
 
 
-@pytest.mark.parametrize("cube,kcube", [((4, 4, 4), (2, 4, 4)), ((2, 4, 4), (4, 4, 8))])
+@pytest.mark.parametrize("cube,kcube", [((4, 4, 4), (2, 4, 4)), ((2, 4, 4), (4, 4, 8)), ((4, 4, 4), (1, 4, 4))])
 def test_key_block_max_pool_and_stages(cube, kcube):
     """Max pooling per key block, and the stage entry points chained by hand
     (pool, coarse, fine, combine, index transpose, backward stages) against
