@@ -435,12 +435,16 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
 }
 
 // dK and dV at 128 channels, warp-specialized: a workgroup of 2 NW waves owns
-// a key cube; NW waves compute dV (S, P, dV^T += dO^T P) and NW waves dK (S,
-// dP, dS, dK^T += Q^T dS) for the same keys, from one copy of every Q / dO
-// chunk in LDS (each of the 2 NW waves issues its share of the loads). The
-// roles swap with the workgroup's parity, so that the two workgroups sharing
-// a CU tend to put a wave of each role on every SIMD. One accumulator array
-// holds dV^T or dK^T, so a wave's working set is the dK pass's.
+// a key block. Per 32-key group, a dV wave forms S = Q_c K^T and P (the
+// lane's K row in registers), hands P to its partner dK wave through LDS and
+// accumulates dV^T += dO_c^T P; the dK wave forms dP = dO_c V^T (the lane's V
+// row in registers), dS = P * (dP - delta) with its partner's P, and
+// accumulates dK^T += Q_c^T dS. Both do 16 MFMAs per chunk and each keeps one
+// row operand and one accumulator array, so the working set fits two waves
+// per SIMD. The dK waves run one chunk behind (they need that chunk's P), so
+// Q / dO / LSE / delta chunks have three LDS stages and P two slots. The roles
+// swap with the workgroup's parity, so that the two workgroups sharing a CU
+// tend to put a wave of each role on every SIMD.
 template <int D, int NW, bool KPAIR>
 __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -452,11 +456,14 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, Grid gq, int stride, float scale) {
   using G = ChunkGeom<D>;
   constexpr int NWT = 2 * NW;   // waves in the workgroup
+  constexpr int QST = 3;        // stages of the Q / dO / LSE / delta chunks
   static_assert(G::RINS % NWT == 0, "every wave issues whole 1 KB loads");
-  __shared__ __attribute__((aligned(16))) bf16 rq[2][G::RUNITS * 8];
-  __shared__ __attribute__((aligned(16))) bf16 rd[2][G::RUNITS * 8];
-  __shared__ __attribute__((aligned(16))) float rls[2][32];
-  __shared__ __attribute__((aligned(16))) float rdl[2][32];
+  __shared__ __attribute__((aligned(16))) bf16 rq[QST][G::RUNITS * 8];
+  __shared__ __attribute__((aligned(16))) bf16 rd[QST][G::RUNITS * 8];
+  __shared__ __attribute__((aligned(16))) float rls[QST][32];
+  __shared__ __attribute__((aligned(16))) float rdl[QST][32];
+  // P of each dV wave's chunk, fp32, lane-major: [slot][key group][part][lane].
+  __shared__ __attribute__((aligned(16))) float4 xp[2][NW][4][64];
 
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -467,14 +474,13 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   const int32_t* list = kwk.list;
   const long tok0 = (long)bh * g.N;
 
-  // This lane's key: token lk of key block j.
+  // This lane's key: token lk of key block j. A dV wave keeps its K row (the
+  // B operand of S = Q K^T), a dK wave its V row (of dP = dO V^T).
   const long n = tok0 + cube_token(g, j, kwk.lk);
-  bf16x8 kf[G::KS], vf[G::KS];
+  bf16x8 kv[G::KS];
+  const bf16* kvrow = (isk ? v : k) + n * D;
 #pragma unroll
-  for (int ks = 0; ks < G::KS; ++ks) {
-    kf[ks] = *reinterpret_cast<const bf16x8*>(k + n * D + ks * 16 + hf * 8);
-    if (isk) vf[ks] = *reinterpret_cast<const bf16x8*>(v + n * D + ks * 16 + hf * 8);
-  }
+  for (int ks = 0; ks < G::KS; ++ks) kv[ks] = *reinterpret_cast<const bf16x8*>(kvrow + ks * 16 + hf * 8);
   const float sl2 = scale * kLog2e;
   f32x16 acc[G::MB];
 #pragma unroll
@@ -507,9 +513,10 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   };
   const uint32_t rqb = lds_addr(rq), rdb = lds_addr(rd), rlb = lds_addr(rls), reb = lds_addr(rdl);
   const uint32_t soff = (uint32_t)chunk_row(gq, 4 * (lane & 7)) * 4u;
-  // Query chunks: query cube list[c >> qsh], its chunk h = c & qmask.
+  // Query chunks: query cube list[c >> qsh], its chunk h = c & qmask, into
+  // stage c % QST.
   auto issue = [&](int c) {
-    const int e = c >> qsh, h = c & qmask, st = c & 1;
+    const int e = c >> qsh, h = c & qmask, st = c % QST;
     if ((e & 63) == 0 && h == 0) cubes(e);
     const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(rcube, e & 63) + (uint32_t)chunk_first(gq, h);
     const uint32_t rc = r0 * (uint32_t)(D * 2);
@@ -521,66 +528,81 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     }
   };
 
+  // Iteration c: the dV waves work on chunk c, the dK waves on chunk c - 1.
+  // At its top every wave's loads of chunk c have landed and the P of chunk
+  // c - 1 is in LDS (each wave waits for its own loads and LDS writes, then
+  // the barrier); chunk c + 1 is then issued into the stage chunk c - 2 used.
   const int nch = L << qsh;
   if (nch > 0) issue(0);
-  for (int c = 0; c < nch; ++c) {
-    wait_vmcnt<0>();
+  for (int c = 0; c <= nch; ++c) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    const bool kvalid = !KPAIR || ((__builtin_amdgcn_readlane(rflag, (c >> qsh) & 63) >> (n32 >> 4)) & 1);
+    // Whether the query cube of chunk c is listed by this lane's key block
+    // (read before issue(c + 1) may refresh the entries).
+    const bool kvalid =
+        !KPAIR || c >= nch || ((__builtin_amdgcn_readlane(rflag, (c >> qsh) & 63) >> (n32 >> 4)) & 1);
     if (c + 1 < nch) issue(c + 1);
-    const int st = c & 1;
-    float lse2[16];
+    if (!isk) {
+      if (c < nch) {
+        const int st = c % QST;
+        float lse2[16];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float4 a = *reinterpret_cast<const float4*>(&rls[st][8 * m + 4 * hf]);
-      lse2[4 * m + 0] = a.x * kLog2e; lse2[4 * m + 1] = a.y * kLog2e;
-      lse2[4 * m + 2] = a.z * kLog2e; lse2[4 * m + 3] = a.w * kLog2e;
-    }
-    f32x16 sx;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sx[e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) sx = mfma32_bf16(row_frag<D>(rq[st], n32, hf, ks), kf[ks], sx);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sx[e] = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);   // P
-    if constexpr (KPAIR) {
-      if (!kvalid) {
+        for (int m = 0; m < 4; ++m) {
+          const float4 a = *reinterpret_cast<const float4*>(&rls[st][8 * m + 4 * hf]);
+          lse2[4 * m + 0] = a.x * kLog2e; lse2[4 * m + 1] = a.y * kLog2e;
+          lse2[4 * m + 2] = a.z * kLog2e; lse2[4 * m + 3] = a.w * kLog2e;
+        }
+        f32x16 sx;
 #pragma unroll
         for (int e = 0; e < 16; ++e) sx[e] = 0.f;
-      }
-    }
-    const char* qtile = reinterpret_cast<const char*>(rq[st]);
-    const char* dtile = reinterpret_cast<const char*>(rd[st]);
-    if (isk) {
-      float dl[16];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * m + 4 * hf]);
-        dl[4 * m + 0] = b.x; dl[4 * m + 1] = b.y; dl[4 * m + 2] = b.z; dl[4 * m + 3] = b.w;
+        for (int ks = 0; ks < G::KS; ++ks) sx = mfma32_bf16(row_frag<D>(rq[st], n32, hf, ks), kv[ks], sx);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sx[e] = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);   // P
+        if constexpr (KPAIR) {
+          if (!kvalid) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sx[e] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          xp[c & 1][kw][t][lane] = make_float4(sx[4 * t], sx[4 * t + 1], sx[4 * t + 2], sx[4 * t + 3]);
+        bf16x8 pf[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (bf16)sx[e];
+        const char* dtile = reinterpret_cast<const char*>(rd[st]);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int mb = 0; mb < G::MB; ++mb)
+            acc[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], acc[mb]);
       }
+    } else if (c > 0) {
+      const int cp = c - 1, st = cp % QST;
       f32x16 dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) dp[e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), vf[ks], dp);
+      for (int ks = 0; ks < G::KS; ++ks) dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), kv[ks], dp);
       bf16x8 sf[2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        sf[e >> 3][e & 7] = (bf16)(sx[e] * (dp[e] - dl[e]));
+      for (int t = 0; t < 4; ++t) {
+        const float4 pv = xp[cp & 1][kw][t][lane];
+        const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * t + 4 * hf]);
+        const float p4[4] = {pv.x, pv.y, pv.z, pv.w}, d4[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * t + r;
+          sf[e >> 3][e & 7] = (bf16)(p4[r] * (dp[e] - d4[r]));
+        }
+      }
+      const char* qtile = reinterpret_cast<const char*>(rq[st]);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int mb = 0; mb < G::MB; ++mb)
           acc[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], acc[mb]);
-    } else {
-      bf16x8 pf[2];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (bf16)sx[e];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int mb = 0; mb < G::MB; ++mb)
-          acc[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], acc[mb]);
     }
   }
 
