@@ -282,6 +282,38 @@ def test_forward_720p_sampled():
     assert near <= NEAR_FRAC * 3 * w.Nc + 2
 
 
+def test_forward_max_cubes_sampled():
+    """The largest coarse problem the library accepts: Nc = vsa_max_cubes()
+    cubes per head (32x64x64 latent, 2048 cubes, 32 logits per lane in the
+    row kernel). Selection checked for every query cube, outputs for 32
+    sampled query cubes."""
+    T, H, W, d, k = 32, 64, 64, 64, 32
+    nc = T * H * W // 64
+    assert nc == V.max_cubes()
+    x = WL.make_inputs_custom(1, 1, d, T, H, W, dtype="bf16", seed=41)
+    p = V.Problem(1, 1, T, H, W, d, topk=k)
+    dd = inputs_to_dev(x, "bf16")
+    o, idx, lens, _ = V.forward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"])
+    torch.cuda.synchronize()
+    gi = host(idx)
+    assert (host(lens) == k).all()
+    qt, kt, vt = (O.tile(x[n].astype(np.float64))[0, 0] for n in ("q", "k", "v"))
+    s = 1 / np.sqrt(d)
+    S, _, oc, _ = O.coarse_attention(O.pool(qt), O.pool(kt), O.pool(vt), s)
+    ridx, margin = O.topk_rows(S, k)
+    tau = O.logit_error_bound(qt, kt, s, sig_bits=8)
+    ref = {"s_c": S[None, None], "tau": tau[None, None], "margin": margin[None, None], "idx": ridx[None, None]}
+    near = check_topk(gi, ref, k)
+    assert near <= NEAR_FRAC * nc + 2
+    rows = np.sort(np.random.default_rng(1).choice(nc, 32, replace=False))
+    of_rows, _ = O.fine_gathered(qt[rows], kt, vt, gi[0, 0][rows], np.full(32, k), s)
+    gct = O.tile(x["g_c"].astype(np.float64))[0, 0][rows]
+    gft = O.tile(x["g_f"].astype(np.float64))[0, 0][rows]
+    ref_o = oc[rows][:, None, :] * gct + of_rows * gft
+    got = O.tile(host(o))[0, 0][rows]
+    assert rel_err(got, ref_o) <= BF16_REL
+
+
 # ------------------------------------------------------------------ edge cases
 def test_all_cubes_selected_is_full_attention():
     """K = Nc with G_c = 0 and no fine gate reproduces full attention."""
