@@ -436,15 +436,16 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
 
 // dK and dV at 128 channels, warp-specialized: a workgroup of 2 NW waves owns
 // a key block. Per 32-key group, a dV wave forms S = Q_c K^T and P (the
-// lane's K row in registers), hands P to its partner dK wave through LDS and
-// accumulates dV^T += dO_c^T P; the dK wave forms dP = dO_c V^T (the lane's V
-// row in registers), dS = P * (dP - delta) with its partner's P, and
-// accumulates dK^T += Q_c^T dS. Both do 16 MFMAs per chunk and each keeps one
-// row operand and one accumulator array, so the working set fits two waves
-// per SIMD. The dK waves run one chunk behind (they need that chunk's P), so
-// Q / dO / LSE / delta chunks have three LDS stages and P two slots. The roles
-// swap with the workgroup's parity, so that the two workgroups sharing a CU
-// tend to put a wave of each role on every SIMD.
+// lane's K row in registers), hands P (bf16, the values dV is formed with) to
+// its partner dK wave through LDS and accumulates dV^T += dO_c^T P; the dK
+// wave forms dP = dO_c V^T (the lane's V row in registers), dS = P * (dP -
+// delta) with its partner's P, and accumulates dK^T += Q_c^T dS. Both do 16
+// MFMAs per chunk and each keeps one row operand and one accumulator array,
+// so the working set fits two waves per SIMD. The dK waves run one chunk
+// behind (they need that chunk's P) and chunks load two ahead, so Q / dO /
+// LSE / delta chunks have four LDS stages and P two slots. The roles swap
+// with the workgroup's parity, so that the two workgroups sharing a CU tend
+// to put a wave of each role on every SIMD.
 template <int D, int NW, bool KPAIR>
 __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -456,14 +457,14 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     bf16* __restrict__ dk, bf16* __restrict__ dv, Grid g, Grid gq, int stride, float scale) {
   using G = ChunkGeom<D>;
   constexpr int NWT = 2 * NW;   // waves in the workgroup
-  constexpr int QST = 3;        // stages of the Q / dO / LSE / delta chunks
+  constexpr int QST = 4;        // stages of the Q / dO / LSE / delta chunks
   static_assert(G::RINS % NWT == 0, "every wave issues whole 1 KB loads");
   __shared__ __attribute__((aligned(16))) bf16 rq[QST][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rd[QST][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) float rls[QST][32];
   __shared__ __attribute__((aligned(16))) float rdl[QST][32];
-  // P of each dV wave's chunk, fp32, lane-major: [slot][key group][part][lane].
-  __shared__ __attribute__((aligned(16))) float4 xp[2][NW][4][64];
+  // P of each dV wave's chunk, lane-major: [slot][key group][half][lane].
+  __shared__ __attribute__((aligned(16))) bf16x8 xp[2][NW][2][64];
 
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -531,17 +532,35 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   // Iteration c: the dV waves work on chunk c, the dK waves on chunk c - 1.
   // At its top every wave's loads of chunk c have landed and the P of chunk
   // c - 1 is in LDS (each wave waits for its own loads and LDS writes, then
-  // the barrier); chunk c + 1 is then issued into the stage chunk c - 2 used.
+  // the barrier); chunk c + 2 is then issued into the stage chunk c - 2 used.
+  // Wave 0 also issues the LSE and delta loads (two more per chunk).
   const int nch = L << qsh;
-  if (nch > 0) issue(0);
+  constexpr int RPW = G::RINS / NWT;   // loads per wave per row tile
+  // Whether the query cube of chunk c is listed by this lane's key block,
+  // read while c's block of 64 list entries is the one loaded (an issue()
+  // may refresh it for a later chunk).
+  auto kflag = [&](int c) {
+    return !KPAIR || ((__builtin_amdgcn_readlane(rflag, (c >> qsh) & 63) >> (n32 >> 4)) & 1);
+  };
+  bool kvalid_next = true;
+  if (nch > 0) {
+    issue(0);
+    kvalid_next = kflag(0);
+  }
+  if (nch > 1) issue(1);
   for (int c = 0; c <= nch; ++c) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // Chunk c has landed once only chunk c + 1's loads may be outstanding.
+    if (c + 1 < nch) {
+      if (wv == 0) wait_vmcnt<2 * RPW + 2>();
+      else wait_vmcnt<2 * RPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
-    // Whether the query cube of chunk c is listed by this lane's key block
-    // (read before issue(c + 1) may refresh the entries).
-    const bool kvalid =
-        !KPAIR || c >= nch || ((__builtin_amdgcn_readlane(rflag, (c >> qsh) & 63) >> (n32 >> 4)) & 1);
-    if (c + 1 < nch) issue(c + 1);
+    const bool kvalid = kvalid_next;
+    if (c + 1 < nch) kvalid_next = kflag(c + 1);   // chunk c + 1 was issued before chunk c + 2
+    if (c + 2 < nch) issue(c + 2);
     if (!isk) {
       if (c < nch) {
         const int st = c % QST;
@@ -565,12 +584,11 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
             for (int e = 0; e < 16; ++e) sx[e] = 0.f;
           }
         }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          xp[c & 1][kw][t][lane] = make_float4(sx[4 * t], sx[4 * t + 1], sx[4 * t + 2], sx[4 * t + 3]);
         bf16x8 pf[2];
 #pragma unroll
         for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (bf16)sx[e];
+        xp[c & 1][kw][0][lane] = pf[0];
+        xp[c & 1][kw][1][lane] = pf[1];
         const char* dtile = reinterpret_cast<const char*>(rd[st]);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
@@ -586,15 +604,15 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
 #pragma unroll
       for (int ks = 0; ks < G::KS; ++ks) dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), kv[ks], dp);
       bf16x8 sf[2];
+      const bf16x8 pp[2] = {xp[cp & 1][kw][0][lane], xp[cp & 1][kw][1][lane]};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const float4 pv = xp[cp & 1][kw][t][lane];
         const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * t + 4 * hf]);
-        const float p4[4] = {pv.x, pv.y, pv.z, pv.w}, d4[4] = {b.x, b.y, b.z, b.w};
+        const float d4[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = 4 * t + r;
-          sf[e >> 3][e & 7] = (bf16)(p4[r] * (dp[e] - d4[r]));
+          sf[e >> 3][e & 7] = (bf16)((float)pp[e >> 3][e & 7] * (dp[e] - d4[r]));
         }
       }
       const char* qtile = reinterpret_cast<const char*>(rq[st]);
