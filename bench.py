@@ -464,10 +464,42 @@ def main() -> int:
     return 0
 
 
+def selection_mass(torch, p, q, k, idx, lens, heads=(0, 20), rows=256, seed=0):
+    """Sanity figure for the selection (not a target): for sampled query
+    tokens, the share of their full softmax attention mass (fp32, all keys of
+    the head) that falls on the key cubes their cube's list selects."""
+    B, H_, T, H, W, d = q.shape
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    t = torch.arange(T * H * W, device=q.device)
+    tt, yy, xx = t // (H * W), (t // W) % H, t % W
+    ct, ch, cw = p.cube
+    cube_of = ((tt // ct) * (H // ch) + yy // ch) * (W // cw) + xx // cw
+    out = []
+    for h in heads:
+        if h >= H_:
+            continue
+        Q = q[0, h].reshape(-1, d).float()
+        K = k[0, h].reshape(-1, d).float()
+        r = torch.randint(0, T * H * W, (rows,), generator=g).to(q.device)
+        P = torch.softmax((Q[r] @ K.T) * (1.0 / d ** 0.5), dim=-1)
+        # Selected cubes per sampled row; entries past a row's length go to a
+        # spare last column, which is dropped.
+        sel = torch.zeros((rows, p.Nc + 1), dtype=torch.bool, device=q.device)
+        lists, n = idx[0, h][cube_of[r]].long(), lens[0, h][cube_of[r]]
+        valid = torch.arange(lists.shape[1], device=q.device)[None, :] < n[:, None]
+        sel.scatter_(1, torch.where(valid, lists, torch.full_like(lists, p.Nc)), True)
+        out.append(float((P * sel[:, :p.Nc][:, cube_of]).sum(-1).mean()))
+    return {"heads": [h for h in heads if h < H_], "query_tokens_per_head": rows,
+            "mean_selected_mass": [round(m, 4) for m in out]}
+
+
 def variants(args, V, WL, torch, w, p, inputs, idx, lens, ws, o, achieved, line):
-    """Context measurements beside the benchmark: the max-pool variant, the
-    tile-size trade-off and dense flash attention on the same chip."""
+    """Context measurements beside the benchmark: the share of attention mass
+    the selection keeps, the max-pool variant, the tile-size trade-off and
+    dense flash attention on the same chip."""
     q, k, v, gc, gf = inputs
+    line["selection_sanity"] = selection_mass(torch, p, q, k, idx, lens)
+    log(f"selected attention mass: {line['selection_sanity']}")
     # The max-pool variant of the coarse pooling on the same workload (forward).
     import dataclasses
     pm = dataclasses.replace(p, pool="max")
