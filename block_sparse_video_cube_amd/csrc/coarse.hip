@@ -259,9 +259,12 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
 // radix select finds the key of the K-th largest logit, 8 bits per pass from
 // the most significant bit in which the row's keys differ (the bits above it
 // are shared by every key, and skipping them keeps the first histogram
-// spread over many buckets, so the LDS atomics rarely collide). Then every
-// key above it and the first (K - #above) keys equal to it, in ascending
-// key-block order, are taken.
+// spread over many buckets, so the LDS atomics rarely collide). A pass whose
+// chosen bucket is taken whole (its count is the number still needed) ends
+// the search: the lower bits cannot change the set. Then every key above the
+// bucket and the first (K - #above) keys in it, in ascending key-block order,
+// are taken (with the search run to the last bit, the bucket is one key
+// value).
 template <int NCH>
 __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restrict__ s, float* __restrict__ lse,
                                                           int32_t* __restrict__ idx, int32_t* __restrict__ len,
@@ -330,25 +333,27 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
       if (lane + o < 64) incl += t;
     }
     int acc = incl - mine;
-    int found = -1, before = 0;
+    int found = -1, before = 0, fcount = 0;
     const int cnt[4] = {b3, b2, b1, b0};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (found < 0 && acc < krem && acc + cnt[q] >= krem) { found = 4 * lane + 3 - q; before = acc; }
+      if (found < 0 && acc < krem && acc + cnt[q] >= krem) { found = 4 * lane + 3 - q; before = acc; fcount = cnt[q]; }
       acc += cnt[q];
     }
     const uint64_t bal = __ballot(found >= 0);
     const int src = __ffsll((unsigned long long)bal) - 1;
     const int fb = __shfl(found, src, 64);
     const int fbefore = __shfl(before, src, 64);
+    const int fcnt = __shfl(fcount, src, 64);
     prefix |= (uint32_t)fb << shift;
     pmask |= dmask << shift;
     krem -= fbefore;
     hi -= nb;
     wave_sync();
+    if (fcnt == krem) break;   // the whole bucket is taken
   }
-  // prefix is the key of the K-th largest logit: take every larger one and
-  // the first krem equal ones in ascending cube order.
+  // prefix (on the bits of pmask) is the bucket of the K-th largest logit:
+  // take every key above it and the first krem in it in ascending order.
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t* out = idx + row * (long)stride;
   int taken = 0, eq_seen = 0;
@@ -357,8 +362,8 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
     if (t >= nused) break;
     const int j = t * 64 + lane;
     const bool valid = j < Nk;
-    const bool gt = valid && key[t] > prefix;
-    const bool eq = valid && key[t] == prefix;
+    const bool gt = valid && (key[t] & pmask) > prefix;
+    const bool eq = valid && (key[t] & pmask) == prefix;
     const uint64_t beq = __ballot(eq);
     const int eqr = eq_seen + __popcll(beq & lt_mask);
     const bool take = gt || (eq && eqr < krem);
