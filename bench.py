@@ -162,6 +162,8 @@ def train_measure(name: str, steps: int, warmup: int) -> dict:
     return {"workload": w.name, "steps": steps, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_tflops": round(fl_f / (fwd_ms * 1e-3) / 1e12, 2), "bwd_tflops": round(fl_b / (bwd_ms * 1e-3) / 1e12, 2),
             "computed_block_pairs": pairs,
+            "fwd_tokens_per_s": round(w.B * w.N / (fwd_ms * 1e-3), 1),
+            "train_step_tokens_per_s": round(w.B * w.N / ((fwd_ms + bwd_ms) * 1e-3), 1),
             "bwd_stages_ms": {"combine_bwd": round(st[0], 4), "index_transpose": round(st[1], 4),
                               "coarse_bwd": round(st[2], 4), "fine_bwd (dq, dk/dv, pool bwd)": round(st[3], 4)},
             "fine_bwd_tflops": round(fl_b / (st[3] * 1e-3) / 1e12, 2),
