@@ -11,13 +11,15 @@
 // may have their own shape (Bk tokens); everything below that says "key
 // cube" means a key block then.
 //
-// Two kernels, both deterministic (no atomics), in the style of the forward:
-// a workgroup of NW = Bt/32 (or Bk/32) waves owns one cube, wave w its tokens
-// 32w .. 32w+31, one per lane (column) of 32x32x16 bf16 MFMAs, and walks a
+// A dQ kernel and dK / dV kernels, all deterministic (no atomics), in the
+// style of the forward: a workgroup owns one cube (NW = Bt/32 or Bk/32 waves,
+// wave w its tokens 32w .. 32w+31, one per lane column of 32x32x16 bf16
+// MFMAs; at 128 channels the dK / dV workgroup has a dV wave and a dK wave
+// per 32 keys, and 16-token key blocks go two to a workgroup) and walks a
 // list of partner cubes in 32-token chunks: row tiles of the partner's
-// tensors staged in LDS by direct-to-LDS loads (each wave issues 1/NW; the
-// next chunk loads while this one is computed). The transposed operands come
-// from the same row tiles through LDS transpose reads.
+// tensors staged in LDS by direct-to-LDS loads (each wave issues its share;
+// later chunks load while this one is computed). The transposed operands
+// come from the same row tiles through LDS transpose reads.
 //  * dQ, per query cube i over its list of key cubes (the forward's list):
 //      S^T = K_c Q^T, dP^T = V_c dO^T        A = K / V row tiles, B = the
 //                                            lane's Q / dO row (registers)
@@ -53,13 +55,14 @@ __device__ __forceinline__ void pooled_grad(const float* dxc, const uint8_t* arg
   }
 }
 
-// Processing order of the Nc key cubes of every (b, h) for the dK / dV
-// kernel: descending length of their transposed lists, ties by cube id, so
+// Processing order of the Nc key blocks of every (b, h) for the dK / dV
+// kernel: descending length of their transposed lists, ties by block id, so
 // the longest walks start first. One workgroup per (b, h): a bitonic sort of
-// ((Nc - count) << 32 | cube) keys in LDS (a count never exceeds the number
-// of query cubes, so the clamp at 0 only orders malformed offsets).
+// ((Nq - count) << 32 | block) keys in LDS (a count never exceeds the Nq
+// query cubes, so the clamp at 0 only orders malformed offsets).
 __global__ __launch_bounds__(1024) void order_by_count_kernel(const int32_t* __restrict__ k2q_off,
-                                                              int32_t* __restrict__ order, int Nc, int pow2) {
+                                                              int32_t* __restrict__ order, int Nc, int Nq,
+                                                              int pow2) {
   __shared__ unsigned long long key[2048];
   const long bh = blockIdx.x;
   const int32_t* off = k2q_off + bh * (Nc + 1);
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(1024) void order_by_count_kernel(const int32_t* __r
     unsigned long long kv = ~0ull;
     if (e < Nc) {
       const int cnt = max(off[e + 1] - off[e], 0);
-      kv = ((unsigned long long)(uint32_t)max(Nc - cnt, 0) << 32) | (uint32_t)e;
+      kv = ((unsigned long long)(uint32_t)max(Nq - cnt, 0) << 32) | (uint32_t)e;
     }
     key[e] = kv;
   }
@@ -651,7 +654,8 @@ hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_
   int pow2 = 1;
   while (pow2 < L.gk.Nc) pow2 <<= 1;
   if (pow2 > 2048) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(order_by_count_kernel, dim3(L.BH), dim3(1024), 0, L.stream, k2q_off, order, L.gk.Nc, pow2);
+  hipLaunchKernelGGL(order_by_count_kernel, dim3(L.BH), dim3(1024), 0, L.stream, k2q_off, order, L.gk.Nc, L.g.Nc,
+                     pow2);
   return hipGetLastError();
 }
 
