@@ -430,6 +430,25 @@ def test_backward_small_ungated():
     backward_compare(x, p, "bf16", gates=False)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_single_cube_latent(d):
+    """The degenerate latent of one cube (4x4x4, Nc = 1): the coarse softmax
+    is 1, top-1 keeps the only cube, and the fine stage is full attention
+    over 64 tokens. Forward (top-K mode) and backward against the oracle."""
+    x = WL.make_inputs_custom(1, 2, d, 4, 4, 4, dtype="bf16", seed=43)
+    p = V.Problem(1, 2, 4, 4, 4, d, topk=1)
+    dd = inputs_to_dev(x, "bf16")
+    o, idx, lens, saved = V.forward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"], training=True)
+    g = V.backward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"], idx, lens, saved, dd["d_o"])
+    torch.cuda.synchronize()
+    assert (host(idx) == 0).all() and (host(lens) == 1).all()
+    fwd = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=1)
+    assert_close(host(o), fwd["o"], "bf16", "o")
+    ref = O.backward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], x["d_o"], fwd)
+    for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
+        assert_close(host(g[nm]), ref[nm], "bf16", nm)
+
+
 def test_backward_head_dim_128():
     x, p = _small_train_inputs(d=128, seed=8, heads=1, T=8, H=8, W=16)
     backward_compare(x, p, "bf16")
