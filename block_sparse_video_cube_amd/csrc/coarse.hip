@@ -124,18 +124,20 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
 // lane group g contracts k = 8g + s and reads its eight A values and eight B
 // values as two 16-byte LDS reads each. Wave w owns channels
 // [16*CB*w, 16*CB*(w+1)) of both 16-row blocks. The B tile is staged with k
-// varying fastest across lanes, so the transposing LDS stores of a wave fall
-// on consecutive banks (its two channel rows are BRP floats apart, which
-// keeps their 32-bank windows disjoint).
+// varying fastest across lanes: a wave's two lane halves store channel
+// groups two apart (eight tile rows, whose BRP = 36 pitch puts them 32 banks
+// apart), so the transposing stores are free of bank conflicts, and so are
+// the 16-lane reads of 16 consecutive tile rows (pitches 36 floats apart).
 template <int D, bool TRANS_A, bool EXP>
 __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restrict__ m, const float* __restrict__ lse,
                                                           const float* __restrict__ b, float* __restrict__ c, int R,
                                                           int Kd, int ld, float scale) {
   constexpr int KC = 32, RP = KC + 4;           // k per chunk, LDS row pitch of A (floats)
-  constexpr int BRP = KC + 8;                    // LDS row pitch of the transposed B tile
+  constexpr int BRP = KC + 4;                    // LDS row pitch of the transposed B tile
   constexpr int CB = D / 64;                     // 16-channel blocks per wave
   constexpr int BF4 = KC * D / 4 / 256;          // B float4 loads per thread per chunk
   static_assert(!(TRANS_A && EXP), "the softmax is applied along rows of M only");
+  static_assert(KC == 32 && BF4 * 8 * 4 == D, "B staging: 32 k per lane half, 8 channel groups per pass");
   __shared__ __attribute__((aligned(16))) float Al[2][32][RP];
   __shared__ __attribute__((aligned(16))) float Bl[2][D][BRP];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -147,6 +149,9 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
   // (M[r0 + ai][k0 + 4aq ..]); with TRANS_A, k = ai of the chunk and tile rows
   // 4aq .. 4aq+3 (M[k0 + ai][r0 + 4aq ..]), written transposed.
   const int ai = tid >> 3, aq = tid & 7;
+  // B staging role in pass j: k row kap of the chunk, channel group bc4 + 8 j
+  // (four channels).
+  const int kap = lane & 31, bc4 = (w & 1) + 4 * (w >> 1) + 2 * (lane >> 5);
   const bool arow = r0 + ai < R;
   const float alse = (EXP && arow) ? lse[bh * R + r0 + ai] : 0.f;
   float4 ar, br[BF4];
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
     }
 #pragma unroll
     for (int j = 0; j < BF4; ++j) {
-      const int f = tid + 256 * j, kap = f % KC, c4 = f / KC;
+      const int c4 = bc4 + 8 * j;
       br[j] = k0 + kap < Kd ? *reinterpret_cast<const float4*>(Bm + (long)(k0 + kap) * D + 4 * c4)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
     }
 #pragma unroll
     for (int j = 0; j < BF4; ++j) {
-      const int f = tid + 256 * j, kap = f % KC, c4 = f / KC;
+      const int c4 = bc4 + 8 * j;
       Bl[bb][4 * c4 + 0][kap] = br[j].x;
       Bl[bb][4 * c4 + 1][kap] = br[j].y;
       Bl[bb][4 * c4 + 2][kap] = br[j].z;
