@@ -823,3 +823,71 @@ def test_key_block_max_pool_and_stages(cube, kcube):
         got = [list(k2q[0, h, off[0, h, j]:off[0, h, j + 1]]) for j in range(p.Nk)]
         assert got == rows
     V.validate_lists(p, d["idx"], d["len"])
+
+
+# ------------------------------------------------ seeded random configurations
+def _random_case(seed):
+    """A seeded random problem: cube and key-block shapes, latent, heads,
+    head_dim, top-K or explicit ragged lists, list stride, pooling."""
+    rng = np.random.default_rng([seed, 4242])
+    cubes = [(4, 4, 4), (2, 4, 4), (4, 4, 8), (1, 8, 8), (2, 2, 8)]
+    kblocks = [None, (2, 4, 4), (4, 4, 8), (1, 4, 4), (2, 2, 4), (4, 4, 4)]
+    cube = cubes[rng.integers(len(cubes))]
+    kcube = kblocks[rng.integers(len(kblocks))]
+    kc = cube if kcube is None else kcube
+    lcm = [max(a, b) for a, b in zip(cube, kc)]   # sides are powers of two
+    T, H, W = (int(l * rng.integers(1, 4)) for l in lcm)
+    while T * H * W < 2 * max(np.prod(cube), np.prod(kc)):
+        W *= 2
+    heads = int(rng.integers(1, 3))
+    d = int(rng.choice([64, 128]))
+    nq = T * H * W // int(np.prod(cube))
+    nk = T * H * W // int(np.prod(kc))
+    explicit = bool(rng.integers(2))
+    pool = "max" if rng.integers(4) == 0 else "mean"
+    if explicit:
+        stride = int(rng.integers(1, nk + 1))
+        topk = 0
+    else:
+        topk = int(rng.integers(1, nk + 1))
+        stride = int(rng.integers(topk, nk + 1))
+    return dict(cube=cube, kcube=kcube, T=T, H=H, W=W, heads=heads, d=d, nq=nq, nk=nk, explicit=explicit,
+                topk=topk, stride=stride, pool=pool)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_configurations(seed):
+    """Forward and backward of seeded random problems against the oracle
+    (bf16; top-K rows checked by the near-tie protocol, outputs on the GPU's
+    lists)."""
+    c = _random_case(seed)
+    print(f"[random {seed}] {c}", flush=True)
+    x = WL.make_inputs_custom(1, c["heads"], c["d"], c["T"], c["H"], c["W"], dtype="bf16", seed=100 + seed)
+    p = V.Problem(1, c["heads"], c["T"], c["H"], c["W"], c["d"], topk=c["topk"], list_stride=c["stride"],
+                  cube=c["cube"], kcube=c["kcube"], pool=c["pool"])
+    dd = inputs_to_dev(x, "bf16")
+    if c["explicit"]:
+        idx, lens = WL.random_lists(c["nk"], c["heads"] * c["nq"], 0, c["stride"], seed=seed, stride=c["stride"])
+        x["idx"] = idx.reshape(1, c["heads"], c["nq"], c["stride"])
+        x["len"] = lens.reshape(1, c["heads"], c["nq"])
+        o, gi_t, gl_t, saved = V.forward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"],
+                                         idx=dev(x["idx"], torch.int32), lens=dev(x["len"], torch.int32),
+                                         training=True)
+    else:
+        o, gi_t, gl_t, saved = V.forward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"], training=True)
+    g = V.backward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"], gi_t, gl_t, saved, dd["d_o"])
+    torch.cuda.synchronize()
+    gi, gl = host(gi_t), host(gl_t)
+    if not c["explicit"]:
+        assert (gl == c["topk"]).all()
+        if c["stride"] > c["topk"]:
+            assert np.all(gi[..., c["topk"]:] == -1)
+        sel = O.forward(x["q"], x["k"], x["v"], topk=c["topk"], pool_mode=c["pool"], cube=c["cube"],
+                        kcube=c["kcube"])
+        check_topk(gi[..., :c["topk"]], sel, c["topk"])
+    fwd = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=gl, pool_mode=c["pool"],
+                    cube=c["cube"], kcube=c["kcube"])
+    assert_close(host(o), fwd["o"], "bf16", "o")
+    ref = O.backward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], x["d_o"], fwd)
+    for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
+        assert_close(host(g[nm]), ref[nm], "bf16", nm)
