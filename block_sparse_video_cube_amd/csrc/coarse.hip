@@ -123,23 +123,27 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
 // transposed (channel-major), so that for 16x16x4 MFMA k-step s a lane of
 // lane group g contracts k = 8g + s and reads its eight A values and eight B
 // values as two 16-byte LDS reads each. Wave w owns channels
-// [16*CB*w, 16*CB*(w+1)) of both 16-row blocks. The B tile is staged with k
-// varying fastest across lanes: a wave's two lane halves store channel
-// groups two apart (eight tile rows, whose BRP = 36 pitch puts them 32 banks
-// apart), so the transposing stores are free of bank conflicts, and so are
-// the 16-lane reads of 16 consecutive tile rows (pitches 36 floats apart).
+// [16*CB*w, 16*CB*(w+1)) of both 16-row blocks. Both tiles have rows of
+// KC = 32 floats with their 16-byte units XOR-permuted by row / 2 (tslot),
+// so the 16-lane reads of 16 consecutive rows fall on distinct banks; the B
+// tile is staged with k varying fastest across lanes, and the two lane halves
+// of a wave store rows of opposite parity (they swap the components of their
+// float4 in pairs), which keeps the transposing stores conflict-free too. At
+// 40 KB of LDS four workgroups fit a CU.
 template <int D, bool TRANS_A, bool EXP>
 __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restrict__ m, const float* __restrict__ lse,
                                                           const float* __restrict__ b, float* __restrict__ c, int R,
                                                           int Kd, int ld, float scale) {
-  constexpr int KC = 32, RP = KC + 4;           // k per chunk, LDS row pitch of A (floats)
-  constexpr int BRP = KC + 4;                    // LDS row pitch of the transposed B tile
+  constexpr int KC = 32;                         // k per chunk = floats per LDS tile row
   constexpr int CB = D / 64;                     // 16-channel blocks per wave
   constexpr int BF4 = KC * D / 4 / 256;          // B float4 loads per thread per chunk
   static_assert(!(TRANS_A && EXP), "the softmax is applied along rows of M only");
   static_assert(KC == 32 && BF4 * 8 * 4 == D, "B staging: 32 k per lane half, 8 channel groups per pass");
-  __shared__ __attribute__((aligned(16))) float Al[2][32][RP];
-  __shared__ __attribute__((aligned(16))) float Bl[2][D][BRP];
+  __shared__ __attribute__((aligned(16))) float Al[2][32 * KC];
+  __shared__ __attribute__((aligned(16))) float Bl[2][D * KC];
+  // Float index of element (row, k) of a tile: 16-byte unit k / 4 of the row
+  // is stored at unit (k / 4) ^ (row / 2 mod 8).
+  auto tslot = [](int row, int k) { return row * KC + ((((k >> 2) ^ (row >> 1)) & 7) << 2) + (k & 3); };
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const long bh = blockIdx.y;
   const int r0 = blockIdx.x * 32;
@@ -190,20 +194,23 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
   };
   auto store = [&](int bb) {
     if (!TRANS_A) {
-      *reinterpret_cast<float4*>(&Al[bb][ai][4 * aq]) = ar;
+      *reinterpret_cast<float4*>(&Al[bb][tslot(ai, 4 * aq)]) = ar;
     } else {
-      Al[bb][4 * aq + 0][ai] = ar.x;
-      Al[bb][4 * aq + 1][ai] = ar.y;
-      Al[bb][4 * aq + 2][ai] = ar.z;
-      Al[bb][4 * aq + 3][ai] = ar.w;
+      Al[bb][tslot(4 * aq + 0, ai)] = ar.x;
+      Al[bb][tslot(4 * aq + 1, ai)] = ar.y;
+      Al[bb][tslot(4 * aq + 2, ai)] = ar.z;
+      Al[bb][tslot(4 * aq + 3, ai)] = ar.w;
     }
+    const int hb = lane >> 5;   // the upper lane half stores component t ^ 1 in step t
 #pragma unroll
     for (int j = 0; j < BF4; ++j) {
       const int c4 = bc4 + 8 * j;
-      Bl[bb][4 * c4 + 0][kap] = br[j].x;
-      Bl[bb][4 * c4 + 1][kap] = br[j].y;
-      Bl[bb][4 * c4 + 2][kap] = br[j].z;
-      Bl[bb][4 * c4 + 3][kap] = br[j].w;
+      float4 v = br[j];
+      if (hb) v = make_float4(v.y, v.x, v.w, v.z);
+      Bl[bb][tslot(4 * c4 + (0 ^ hb), kap)] = v.x;
+      Bl[bb][tslot(4 * c4 + (1 ^ hb), kap)] = v.y;
+      Bl[bb][tslot(4 * c4 + (2 ^ hb), kap)] = v.z;
+      Bl[bb][tslot(4 * c4 + (3 ^ hb), kap)] = v.w;
     }
   };
   f32x4 acc[2][CB];
@@ -221,16 +228,16 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
     float av[2][8], bv[CB][8];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const float4 x0 = *reinterpret_cast<const float4*>(&Al[bb][16 * rb + r][8 * g]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&Al[bb][16 * rb + r][8 * g + 4]);
+      const float4 x0 = *reinterpret_cast<const float4*>(&Al[bb][tslot(16 * rb + r, 8 * g)]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&Al[bb][tslot(16 * rb + r, 8 * g + 4)]);
       av[rb][0] = x0.x; av[rb][1] = x0.y; av[rb][2] = x0.z; av[rb][3] = x0.w;
       av[rb][4] = x1.x; av[rb][5] = x1.y; av[rb][6] = x1.z; av[rb][7] = x1.w;
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int col = 16 * (CB * w + cb) + r;
-      const float4 x0 = *reinterpret_cast<const float4*>(&Bl[bb][col][8 * g]);
-      const float4 x1 = *reinterpret_cast<const float4*>(&Bl[bb][col][8 * g + 4]);
+      const float4 x0 = *reinterpret_cast<const float4*>(&Bl[bb][tslot(col, 8 * g)]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&Bl[bb][tslot(col, 8 * g + 4)]);
       bv[cb][0] = x0.x; bv[cb][1] = x0.y; bv[cb][2] = x0.z; bv[cb][3] = x0.w;
       bv[cb][4] = x1.x; bv[cb][5] = x1.y; bv[cb][6] = x1.z; bv[cb][7] = x1.w;
     }
