@@ -715,16 +715,189 @@ static void fine_bwd_launch(const Launch& L, const bf16* q, const bf16* k, const
                              dk, dv);
 }
 
-hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
+// fp32 path of the fine backward (fp32 problems, small correctness-first
+// shapes), fp32 arithmetic throughout. Each token is handled by TPT = D / 32
+// adjacent threads, thread `part` holding channels 32*part .. 32*part+31, so
+// that no thread keeps more than 4 x 32 floats; the dot products are summed
+// over the TPT threads with lane exchanges. The partner rows are staged in
+// LDS up to 32 at a time. The pooled gradient of the token's cube (or key
+// block) is added in the epilogue as in the bf16 kernels.
+constexpr int kF32Part = 32;   // channels per thread
+
+template <int TPT> __device__ __forceinline__ float part_sum(float x) {
+  if (TPT >= 2) x += __shfl_xor(x, 1);
+  if (TPT >= 4) x += __shfl_xor(x, 2);
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void fine_bwd_dq_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ len, const float* __restrict__ lse_f,
+    const float* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dqc,
+    const uint8_t* __restrict__ qarg, float* __restrict__ dq, Grid g, Grid gk, int stride, float scale) {
+  constexpr int R = 32, C = kF32Part, TPT = D / C;
+  __shared__ float ks[R][D];
+  __shared__ float vs[R][D];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tok = tid / TPT, c0 = (tid % TPT) * C;
+  const int item = blockIdx.x;
+  const int bh = item / g.Nc, i = item - bh * g.Nc;
+  const long tok0 = (long)bh * g.N;
+  const long n = tok0 + cube_token(g, i, tok);
+  float qv[C], dov[C], acc[C];
+#pragma unroll
+  for (int d = 0; d < C; ++d) { qv[d] = q[n * D + c0 + d]; dov[d] = dof[n * D + c0 + d]; acc[d] = 0.f; }
+  const float lse = lse_f[n], dl = delta[n];
+  const int L = min(max(len[item], 0), stride);
+  const int32_t* list = idx + (long)item * stride;
+  const int RS = min(R, gk.B), spb = gk.B / RS;   // rows per stage, stages per key block
+  for (int t = 0; t < L * spb; ++t) {
+    const int j = list[t / spb], r0 = (t % spb) * RS;
+    if (j < 0 || j >= gk.Nc) continue;
+    __syncthreads();
+    for (int e = tid; e < RS * D; e += nt) {
+      const int r = e / D, d = e - r * D;
+      const long src = (tok0 + cube_token(gk, j, r0 + r)) * D + d;
+      ks[r][d] = k[src];
+      vs[r][d] = v[src];
+    }
+    __syncthreads();
+    for (int r = 0; r < RS; ++r) {
+      float sc = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < C; ++d) {
+        sc = fmaf(qv[d], ks[r][c0 + d], sc);
+        dp = fmaf(dov[d], vs[r][c0 + d], dp);
+      }
+      sc = part_sum<TPT>(sc);
+      dp = part_sum<TPT>(dp);
+      const float ds = expf(sc * scale - lse) * (dp - dl);
+#pragma unroll
+      for (int d = 0; d < C; ++d) acc[d] = fmaf(ds, ks[r][c0 + d], acc[d]);
+    }
+  }
+  const long ci = ((long)bh * g.Nc + i) * D + c0;
+  const float inv_b = 1.0f / (float)g.B;
+#pragma unroll
+  for (int d = 0; d < C; ++d) {
+    const float pg = qarg == nullptr ? dqc[ci + d] * inv_b : (qarg[ci + d] == tok ? dqc[ci + d] : 0.f);
+    dq[n * D + c0 + d] = scale * acc[d] + pg;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void fine_bwd_dkdv_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const int32_t* __restrict__ k2q_off, const int32_t* __restrict__ k2q, const float* __restrict__ lse_f,
+    const float* __restrict__ dof, const float* __restrict__ delta, const float* __restrict__ dkc,
+    const float* __restrict__ dvc, const uint8_t* __restrict__ karg, const uint8_t* __restrict__ varg,
+    float* __restrict__ dk, float* __restrict__ dv, Grid g, Grid gq, int stride, float scale) {
+  constexpr int R = 32, C = kF32Part, TPT = D / C;
+  __shared__ float qs[R][D];
+  __shared__ float os[R][D];
+  __shared__ float ls[R];
+  __shared__ float es[R];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tok = tid / TPT, c0 = (tid % TPT) * C;
+  const int item = blockIdx.x;
+  const int bh = item / g.Nc, j = item - bh * g.Nc;   // g: key blocks, gq: query cubes
+  const long tok0 = (long)bh * g.N;
+  const long n = tok0 + cube_token(g, j, tok);
+  float kv[C], vv[C], adk[C], adv[C];
+#pragma unroll
+  for (int d = 0; d < C; ++d) {
+    kv[d] = k[n * D + c0 + d];
+    vv[d] = v[n * D + c0 + d];
+    adk[d] = 0.f;
+    adv[d] = 0.f;
+  }
+  const int cap = gq.Nc * stride;
+  const int32_t* offs = k2q_off + (long)bh * (g.Nc + 1);
+  const int t0 = min(max(offs[j], 0), cap), t1 = min(max(offs[j + 1], t0), cap);
+  const int32_t* list = k2q + (long)bh * cap + t0;
+  const int L = t1 - t0;
+  const int RS = min(R, gq.B), spc = gq.B / RS;   // rows per stage, stages per query cube
+  for (int t = 0; t < L * spc; ++t) {
+    const int i = list[t / spc], r0 = (t % spc) * RS;
+    if (i < 0 || i >= gq.Nc) continue;
+    __syncthreads();
+    for (int e = tid; e < RS * D; e += nt) {
+      const int r = e / D, d = e - r * D;
+      const long src = (tok0 + cube_token(gq, i, r0 + r)) * D + d;
+      qs[r][d] = q[src];
+      os[r][d] = dof[src];
+    }
+    for (int r = tid; r < RS; r += nt) {
+      const long tq = tok0 + cube_token(gq, i, r0 + r);
+      ls[r] = lse_f[tq];
+      es[r] = delta[tq];
+    }
+    __syncthreads();
+    for (int r = 0; r < RS; ++r) {
+      float sc = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < C; ++d) {
+        sc = fmaf(qs[r][c0 + d], kv[d], sc);
+        dp = fmaf(os[r][c0 + d], vv[d], dp);
+      }
+      sc = part_sum<TPT>(sc);
+      dp = part_sum<TPT>(dp);
+      const float p = expf(sc * scale - ls[r]);
+      const float ds = p * (dp - es[r]);
+#pragma unroll
+      for (int d = 0; d < C; ++d) {
+        adv[d] = fmaf(p, os[r][c0 + d], adv[d]);
+        adk[d] = fmaf(ds, qs[r][c0 + d], adk[d]);
+      }
+    }
+  }
+  const long cj = ((long)bh * g.Nc + j) * D + c0;
+  const float inv_b = 1.0f / (float)g.B;
+#pragma unroll
+  for (int d = 0; d < C; ++d) {
+    const float pk = karg == nullptr ? dkc[cj + d] * inv_b : (karg[cj + d] == tok ? dkc[cj + d] : 0.f);
+    const float pv = varg == nullptr ? dvc[cj + d] * inv_b : (varg[cj + d] == tok ? dvc[cj + d] : 0.f);
+    dk[n * D + c0 + d] = scale * adk[d] + pk;
+    dv[n * D + c0 + d] = adv[d] + pv;
+  }
+}
+
+template <int D>
+static void fine_bwd_launch_f32(const Launch& L, const float* q, const float* k, const float* v, const int32_t* idx,
+                                const int32_t* len, const int32_t* k2q_off, const int32_t* k2q, const float* lse_f,
+                                const float* dof, const float* delta, const float* dqc, const float* dkc,
+                                const float* dvc, float* dq, float* dk, float* dv, const uint8_t* qarg,
+                                const uint8_t* karg, const uint8_t* varg) {
+  constexpr int TPT = D / kF32Part;
+  hipLaunchKernelGGL((fine_bwd_dq_f32_kernel<D>), dim3(L.BH * L.g.Nc), dim3(L.g.B * TPT), 0, L.stream, q, k, v, idx,
+                     len, lse_f, dof, delta, dqc, qarg, dq, L.g, L.gk, L.stride, L.scale);
+  hipLaunchKernelGGL((fine_bwd_dkdv_f32_kernel<D>), dim3(L.BH * L.gk.Nc), dim3(L.gk.B * TPT), 0, L.stream, q, k, v,
+                     k2q_off, k2q, lse_f, dof, delta, dkc, dvc, karg, varg, dk, dv, L.gk, L.g, L.stride, L.scale);
+}
+
+hipError_t launch_fine_bwd(const Launch& L, const void* q, const void* k, const void* v, const int32_t* idx,
                            const int32_t* len, const int32_t* qorder, const int32_t* k2q_off, const int32_t* k2q,
-                           const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
-                           const float* dqc, const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
+                           const int32_t* korder, const float* lse_f, const void* dof, const float* delta,
+                           const float* dqc, const float* dkc, const float* dvc, void* dq, void* dk, void* dv,
                            const uint8_t* args, int32_t* pairs) {
   // Argmax planes in launch_pool's layout: q (Nq cubes), then k and v (Nk blocks).
   const long qplane = (long)L.BH * L.g.Nc * L.D, kplane = (long)L.BH * L.gk.Nc * L.D;
   const uint8_t* qarg = args;
   const uint8_t* karg = args != nullptr ? args + qplane : nullptr;
   const uint8_t* varg = args != nullptr ? args + qplane + kplane : nullptr;
+  if (!L.bf16) {
+    const float *fq = (const float*)q, *fk = (const float*)k, *fv = (const float*)v, *fdo = (const float*)dof;
+    if (L.D == 64)
+      fine_bwd_launch_f32<64>(L, fq, fk, fv, idx, len, k2q_off, k2q, lse_f, fdo, delta, dqc, dkc, dvc, (float*)dq,
+                              (float*)dk, (float*)dv, qarg, karg, varg);
+    else
+      fine_bwd_launch_f32<128>(L, fq, fk, fv, idx, len, k2q_off, k2q, lse_f, fdo, delta, dqc, dkc, dvc, (float*)dq,
+                               (float*)dk, (float*)dv, qarg, karg, varg);
+    return hipGetLastError();
+  }
+  const bf16 *bq = (const bf16*)q, *bk = (const bf16*)k, *bv = (const bf16*)v, *bdo = (const bf16*)dof;
+  bf16 *bdq = (bf16*)dq, *bdk = (bf16*)dk, *bdv = (bf16*)dv;
   int32_t* k2u = nullptr;
   int32_t* plen = nullptr;
   if (L.gk.B == 16) {
@@ -735,11 +908,11 @@ hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const 
     if (e != hipSuccess) return e;
   }
   if (L.D == 64)
-    fine_bwd_launch<64>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq, dk,
-                        dv, qarg, karg, varg, k2u, plen);
+    fine_bwd_launch<64>(L, bq, bk, bv, idx, len, qorder, k2q_off, k2q, korder, lse_f, bdo, delta, dqc, dkc, dvc, bdq,
+                        bdk, bdv, qarg, karg, varg, k2u, plen);
   else
-    fine_bwd_launch<128>(L, q, k, v, idx, len, qorder, k2q_off, k2q, korder, lse_f, dof, delta, dqc, dkc, dvc, dq,
-                         dk, dv, qarg, karg, varg, k2u, plen);
+    fine_bwd_launch<128>(L, bq, bk, bv, idx, len, qorder, k2q_off, k2q, korder, lse_f, bdo, delta, dqc, dkc, dvc,
+                         bdq, bdk, bdv, qarg, karg, varg, k2u, plen);
   return hipGetLastError();
 }
 

@@ -144,7 +144,7 @@ FwdWs carve_fwd_ws(const Dims& d, void* base) {
 
 // Backward workspace.
 struct BwdWs {
-  bf16* dof;   // d_o_f
+  void* dof;   // d_o_f, in the problem's dtype
   float *delta, *doc, *dqc, *dkc, *dvc, *p_scr, *ds_scr, *dc_scr;
   int32_t *k2q_off, *k2q, *qorder, *korder;
   int32_t* pairs;   // 16-token key blocks: union lists of block pairs and their lengths
@@ -156,7 +156,7 @@ BwdWs carve_bwd_ws(const Dims& d, void* base) {
   Carver c(base);
   BwdWs w;
   const size_t rast = d.BH * d.N * d.D;
-  w.dof = c.take<bf16>(rast);
+  w.dof = c.take<char>(rast * d.elem);
   w.delta = c.take<float>(d.BH * d.N);
   const size_t pq = d.BH * d.Nq * d.D, pk = d.BH * d.Nk * d.D;
   w.doc = c.take<float>(pq);
@@ -257,7 +257,6 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   Dims d;
   vsa_status st = check_problem(p, &L, &d);
   if (st != VSA_OK) return st;
-  if (!L.bf16) return VSA_ERR_UNSUPPORTED;
   st = check_ptrs({{q, true}, {k, true}, {v, true}, {g_c, false}, {g_f, false}, {idx, true}, {len, true},
                    {saved, true}, {d_o, true}, {dq, true}, {dk, true}, {dv, true}, {dg_c, false},
                    {dg_f, false}, {workspace, true}});
@@ -271,14 +270,12 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   if (e == hipSuccess) e = launch_index_transpose(L, idx, len, ws.k2q_off, ws.k2q, ws.k2q_bits);
   if (e == hipSuccess)
     e = launch_coarse_bwd(L, s.qc, s.kc, s.vc, s.oc, s.lse_c, ws.doc, ws.dqc, ws.dkc, ws.dvc, ws.ds_scr, ws.p_scr, ws.dc_scr);
-  if (e == hipSuccess) e = launch_order(L, idx, len, ws.qorder);
-  if (e == hipSuccess) e = launch_order_by_count(L, ws.k2q_off, ws.korder);
+  if (e == hipSuccess && L.bf16) e = launch_order(L, idx, len, ws.qorder);
+  if (e == hipSuccess && L.bf16) e = launch_order_by_count(L, ws.k2q_off, ws.korder);
   if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, ws.args);
   if (e == hipSuccess)
-    e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                        idx, len, ws.qorder, ws.k2q_off, ws.k2q, ws.korder, s.lse_f, ws.dof, ws.delta, ws.dqc,
-                        ws.dkc, ws.dvc, static_cast<bf16*>(dq), static_cast<bf16*>(dk), static_cast<bf16*>(dv),
-                        L.pool_max ? ws.args : nullptr, ws.pairs);
+    e = launch_fine_bwd(L, q, k, v, idx, len, ws.qorder, ws.k2q_off, ws.k2q, ws.korder, s.lse_f, ws.dof, ws.delta,
+                        ws.dqc, ws.dkc, ws.dvc, dq, dk, dv, L.pool_max ? ws.args : nullptr, ws.pairs);
   return hip_status(e);
 }
 
@@ -401,7 +398,6 @@ vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k,
   Dims d;
   vsa_status st = check_problem(p, &L, &d);
   if (st != VSA_OK) return st;
-  if (!L.bf16) return VSA_ERR_UNSUPPORTED;
   st = check_ptrs({{q, true}, {k, true}, {v, true}, {idx, true}, {len, true}, {k2q_off, true}, {k2q, true},
                    {lse_f, true}, {d_o_f, true}, {delta, true}, {dq_c, true}, {dk_c, true}, {dv_c, true},
                    {dq, true}, {dk, true}, {dv, true}, {workspace, true}});
@@ -409,14 +405,12 @@ vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k,
   const BwdWs ws = carve_bwd_ws(d, workspace);
   if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
   L.stream = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_order(L, idx, len, ws.qorder);
-  if (e == hipSuccess) e = launch_order_by_count(L, k2q_off, ws.korder);
+  hipError_t e = L.bf16 ? launch_order(L, idx, len, ws.qorder) : hipSuccess;
+  if (e == hipSuccess && L.bf16) e = launch_order_by_count(L, k2q_off, ws.korder);
   if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, ws.args);
   if (e == hipSuccess)
-    e = launch_fine_bwd(L, static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                        idx, len, ws.qorder, k2q_off, k2q, ws.korder, lse_f, static_cast<const bf16*>(d_o_f), delta,
-                        dq_c, dk_c, dv_c, static_cast<bf16*>(dq), static_cast<bf16*>(dk), static_cast<bf16*>(dv),
-                        L.pool_max ? ws.args : nullptr, ws.pairs);
+    e = launch_fine_bwd(L, q, k, v, idx, len, ws.qorder, k2q_off, k2q, ws.korder, lse_f, d_o_f, delta, dq_c, dk_c,
+                        dv_c, dq, dk, dv, L.pool_max ? ws.args : nullptr, ws.pairs);
   return hip_status(e);
 }
 

@@ -73,16 +73,18 @@ hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_
 // and bit 25 (by 2P + 1). k2u: B*heads*Nq*stride, plen: B*heads*ceil(Nk/2).
 hipError_t launch_key_pairs(const Launch& L, const int32_t* k2q_off, const int32_t* k2q, int32_t* k2u,
                             int32_t* plen);
-// Fine backward (bf16): dq over the forward lists (qorder from launch_order,
-// may be null), dk / dv over the transposed lists (korder from
-// launch_order_by_count, may be null). The pooled gradients dqc / dkc / dvc
-// are spread over their cubes (mean pooling), or go to the maxima given by
-// args (max pooling; layout of launch_pool's args). With 16-token key blocks
-// `pairs` is scratch for launch_key_pairs (k2u, then plen), else unused.
-hipError_t launch_fine_bwd(const Launch& L, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx,
+// Fine backward: dq over the forward lists (qorder from launch_order, may be
+// null), dk / dv over the transposed lists (korder from
+// launch_order_by_count, may be null); token tensors in the problem's dtype
+// (bf16: MFMA kernels; fp32: one thread per token). The pooled gradients dqc
+// / dkc / dvc are spread over their cubes (mean pooling), or go to the maxima
+// given by args (max pooling; layout of launch_pool's args). With 16-token
+// key blocks and bf16, `pairs` is scratch for launch_key_pairs (k2u, then
+// plen), else unused.
+hipError_t launch_fine_bwd(const Launch& L, const void* q, const void* k, const void* v, const int32_t* idx,
                            const int32_t* len, const int32_t* qorder, const int32_t* k2q_off, const int32_t* k2q,
-                           const int32_t* korder, const float* lse_f, const bf16* dof, const float* delta,
-                           const float* dqc, const float* dkc, const float* dvc, bf16* dq, bf16* dk, bf16* dv,
+                           const int32_t* korder, const float* lse_f, const void* dof, const float* delta,
+                           const float* dqc, const float* dkc, const float* dvc, void* dq, void* dk, void* dv,
                            const uint8_t* args, int32_t* pairs);
 
 hipError_t launch_validate_lists(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* flag);

@@ -173,8 +173,8 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
  * forward that filled `saved` (same q, k, v, g_c, g_f, idx, len), d_o
  * (dtype, raster). Outputs dq, dk, dv (dtype, raster) and dg_c, dg_f (dtype,
  * raster; each may be NULL when its gate was NULL, then it is not written).
- * workspace: ws_bytes >= vsa_workspace_bytes(p, 1). bf16 only in this build
- * (fp32 returns VSA_ERR_UNSUPPORTED). */
+ * workspace: ws_bytes >= vsa_workspace_bytes(p, 1). Both dtypes: bf16 runs
+ * the MFMA kernels, fp32 a one-thread-per-token path in fp32 arithmetic. */
 vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
                         const void* g_c, const void* g_f, const int32_t* idx, const int32_t* len,
                         const void* saved, const void* d_o, void* dq, void* dk, void* dv,
@@ -258,7 +258,7 @@ vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const i
  * come from vsa_coarse_backward.
  * lse_f from the forward; d_o_f and delta from vsa_combine_backward
  * (workspace: ws_bytes >= vsa_workspace_bytes(p, 1)); k2q_off / k2q from
- * vsa_index_transpose. bf16 only. dQ walks each query cube's list, dK / dV
+ * vsa_index_transpose. bf16 or fp32. dQ walks each query cube's list, dK / dV
  * walk the transposed lists, so no atomics are used and the result is
  * deterministic. */
 vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k, const void* v,

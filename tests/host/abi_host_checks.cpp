@@ -31,9 +31,9 @@ hipError_t launch_index_transpose(const Launch&, const int32_t*, const int32_t*,
 hipError_t launch_coarse_bwd(const Launch&, const float*, const float*, const float*, const float*, const float*,
                              const float*, float*, float*, float*, float*, float*, float*) { return stub(); }
 hipError_t launch_order_by_count(const Launch&, const int32_t*, int32_t*) { return stub(); }
-hipError_t launch_fine_bwd(const Launch&, const bf16*, const bf16*, const bf16*, const int32_t*, const int32_t*,
-                           const int32_t*, const int32_t*, const int32_t*, const int32_t*, const float*, const bf16*,
-                           const float*, const float*, const float*, const float*, bf16*, bf16*, bf16*,
+hipError_t launch_fine_bwd(const Launch&, const void*, const void*, const void*, const int32_t*, const int32_t*,
+                           const int32_t*, const int32_t*, const int32_t*, const int32_t*, const float*, const void*,
+                           const float*, const float*, const float*, const float*, void*, void*, void*,
                            const uint8_t*, int32_t*) { return stub(); }
 hipError_t launch_key_pairs(const Launch&, const int32_t*, const int32_t*, int32_t*, int32_t*) { return stub(); }
 hipError_t launch_validate_lists(const Launch&, const int32_t*, const int32_t*, int32_t*) { return stub(); }
@@ -86,10 +86,15 @@ int main() {
   CHECK(vsa_backward(&p, q.data(), q.data(), q.data(), nullptr, nullptr, idx.data(), len.data(), svp, q.data(),
                      o.data(), o.data(), o.data(), nullptr, nullptr, wsp, vsa_workspace_bytes(&p, 1),
                      nullptr) == VSA_ERR_HIP);
-  { vsa_problem f = base(); f.dtype = VSA_F32;
+  { vsa_problem f = base(); f.dtype = VSA_F32;   // fp32 backward: validated, then launched like bf16
+    std::vector<unsigned char> wf(vsa_workspace_bytes(&f, 1) + 256);
+    void* wfp = wf.data() + (256 - ((uintptr_t)wf.data() & 255)) % 256;
     CHECK(vsa_backward(&f, q.data(), q.data(), q.data(), nullptr, nullptr, idx.data(), len.data(), svp, q.data(),
-                       o.data(), o.data(), o.data(), nullptr, nullptr, wsp, ws.size() - 256, nullptr) ==
-          VSA_ERR_UNSUPPORTED); }
+                       o.data(), o.data(), o.data(), nullptr, nullptr, wfp, vsa_workspace_bytes(&f, 1), nullptr) ==
+          VSA_ERR_HIP);
+    CHECK(vsa_backward(&f, q.data(), q.data(), q.data(), nullptr, nullptr, idx.data(), len.data(), svp, q.data(),
+                       o.data(), o.data(), o.data(), nullptr, nullptr, wfp, vsa_workspace_bytes(&f, 1) - 1,
+                       nullptr) == VSA_ERR_WORKSPACE); }
   CHECK(vsa_tile(&p, q.data(), o.data(), nullptr) == VSA_ERR_HIP);
   CHECK(vsa_crop(&p, q.data(), 5, 7, 9, o.data(), nullptr) == VSA_ERR_HIP);
 

@@ -211,16 +211,16 @@ def test_null_problem():
     assert lib.vsa_workspace_bytes(None, 0) == 0
 
 
-def test_backward_fp32_unsupported_and_checks():
+def test_backward_checks_both_dtypes():
     lib = N.lib()
-    p = _p(dtype="f32")
-    args = [FAKE] * 15 + [1 << 40, None]
-    assert lib.vsa_backward(ctypes.byref(p.c()), *args) == UNSUP
-    pb = _p()
-    args = [FAKE] * 7 + [None] + [FAKE] * 7 + [1 << 40, None]      # saved NULL
-    assert lib.vsa_backward(ctypes.byref(pb.c()), *args) == NULL
-    args = [FAKE] * 15 + [V.workspace_bytes(pb, True) - 1, None]
-    assert lib.vsa_backward(ctypes.byref(pb.c()), *args) == WORKSPACE
+    for dt in ("bf16", "f32"):
+        pb = _p(dtype=dt)
+        args = [FAKE] * 7 + [None] + [FAKE] * 7 + [1 << 40, None]      # saved NULL
+        assert lib.vsa_backward(ctypes.byref(pb.c()), *args) == NULL
+        args = [FAKE] * 15 + [V.workspace_bytes(pb, True) - 1, None]
+        assert lib.vsa_backward(ctypes.byref(pb.c()), *args) == WORKSPACE
+        args = [FAKE] * 17 + [V.workspace_bytes(pb, True) - 1, None]
+        assert lib.vsa_fine_backward(ctypes.byref(pb.c()), *args) == WORKSPACE
 
 
 def test_stage_entry_points_validate():

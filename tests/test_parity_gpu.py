@@ -405,9 +405,10 @@ def backward_compare(x, p, dtype, rel=BF16_REL, gates=True):
         assert g["dg_c"] is None and g["dg_f"] is None
 
 
-def _small_train_inputs(d=64, seed=5, heads=2, T=8, H=16, W=16, cube=(4, 4, 4), kcube=None):
+def _small_train_inputs(d=64, seed=5, heads=2, T=8, H=16, W=16, cube=(4, 4, 4), kcube=None, dtype="bf16",
+                        scale=1.0):
     """Ragged random lists (lengths U{0..Nk}), one empty row and one full row."""
-    x = WL.make_inputs_custom(1, heads, d, T, H, W, dtype="bf16", seed=seed)
+    x = WL.make_inputs_custom(1, heads, d, T, H, W, dtype=dtype, seed=seed, scale=scale)
     nc = T * H * W // (cube[0] * cube[1] * cube[2])
     kc = cube if kcube is None else kcube
     nk = T * H * W // (kc[0] * kc[1] * kc[2])
@@ -416,7 +417,7 @@ def _small_train_inputs(d=64, seed=5, heads=2, T=8, H=16, W=16, cube=(4, 4, 4), 
     idx[1, :nk] = np.arange(nk)
     x["idx"] = idx.reshape(1, heads, nc, nk)
     x["len"] = lens.reshape(1, heads, nc)
-    p = V.Problem(1, heads, T, H, W, d, topk=0, list_stride=nk, cube=cube, kcube=kcube)
+    p = V.Problem(1, heads, T, H, W, d, dtype=dtype, topk=0, list_stride=nk, cube=cube, kcube=kcube)
     return x, p
 
 
@@ -447,6 +448,17 @@ def test_single_cube_latent(d):
     ref = O.backward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], x["d_o"], fwd)
     for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
         assert_close(host(g[nm]), ref[nm], "bf16", nm)
+
+
+@pytest.mark.parametrize("d,pool,cube,kcube,gates", [
+    (64, "mean", (4, 4, 4), None, True), (128, "max", (4, 4, 4), None, True), (64, "mean", (4, 4, 4), None, False),
+    (128, "mean", (2, 4, 4), (4, 4, 8), True), (64, "max", (4, 4, 8), (1, 4, 4), True),
+    (64, "mean", (4, 4, 4), (1, 4, 4), True)])
+def test_backward_fp32(d, pool, cube, kcube, gates):
+    """fp32 problems: the whole backward (fp32 kernels) on ragged lists with an
+    empty and a full row, against the oracle to 1e-4 absolute."""
+    x, p = _small_train_inputs(d=d, seed=61, T=8, H=16, W=16, cube=cube, kcube=kcube, dtype="f32", scale=0.25)
+    backward_compare(x, dataclasses.replace(p, pool=pool), "f32", gates=gates)
 
 
 def test_backward_head_dim_128():
@@ -855,17 +867,14 @@ def _random_case(seed):
                 topk=topk, stride=stride, pool=pool)
 
 
-@pytest.mark.parametrize("seed", range(48))
-def test_random_configurations(seed):
-    """Forward and backward of seeded random problems against the oracle
-    (bf16; top-K rows checked by the near-tie protocol, outputs on the GPU's
-    lists)."""
+def _run_random(seed, dtype):
     c = _random_case(seed)
-    print(f"[random {seed}] {c}", flush=True)
-    x = WL.make_inputs_custom(1, c["heads"], c["d"], c["T"], c["H"], c["W"], dtype="bf16", seed=100 + seed)
-    p = V.Problem(1, c["heads"], c["T"], c["H"], c["W"], c["d"], topk=c["topk"], list_stride=c["stride"],
-                  cube=c["cube"], kcube=c["kcube"], pool=c["pool"])
-    dd = inputs_to_dev(x, "bf16")
+    print(f"[random {dtype} {seed}] {c}", flush=True)
+    x = WL.make_inputs_custom(1, c["heads"], c["d"], c["T"], c["H"], c["W"], dtype=dtype, seed=100 + seed,
+                              scale=1.0 if dtype == "bf16" else 0.25)
+    p = V.Problem(1, c["heads"], c["T"], c["H"], c["W"], c["d"], dtype=dtype, topk=c["topk"],
+                  list_stride=c["stride"], cube=c["cube"], kcube=c["kcube"], pool=c["pool"])
+    dd = inputs_to_dev(x, dtype)
     if c["explicit"]:
         idx, lens = WL.random_lists(c["nk"], c["heads"] * c["nq"], 0, c["stride"], seed=seed, stride=c["stride"])
         x["idx"] = idx.reshape(1, c["heads"], c["nq"], c["stride"])
@@ -887,7 +896,21 @@ def test_random_configurations(seed):
         check_topk(gi[..., :c["topk"]], sel, c["topk"])
     fwd = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=gl, pool_mode=c["pool"],
                     cube=c["cube"], kcube=c["kcube"])
-    assert_close(host(o), fwd["o"], "bf16", "o")
+    assert_close(host(o), fwd["o"], dtype, "o")
     ref = O.backward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], x["d_o"], fwd)
     for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
-        assert_close(host(g[nm]), ref[nm], "bf16", nm)
+        assert_close(host(g[nm]), ref[nm], dtype, nm)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_configurations(seed):
+    """Forward and backward of seeded random problems against the oracle
+    (bf16; top-K rows checked by the near-tie protocol, outputs on the GPU's
+    lists)."""
+    _run_random(seed, "bf16")
+
+
+@pytest.mark.parametrize("seed", range(1000, 1020))
+def test_random_configurations_fp32(seed):
+    """The same for fp32 problems (fp32 kernels, 1e-4 absolute)."""
+    _run_random(seed, "f32")
