@@ -206,11 +206,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
       sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl));
     }
     const char* kt = reinterpret_cast<const char*>(rk[st]);
+    // Accumulating MFMAs at raised wave priority (issued back to back while
+    // the SIMD's other wave does its softmax; 2% faster over the backward).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb)
         acc[mb] = mfma32_bf16(rowt_frag(kt, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], acc[mb]);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // lane holds dQ^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query]; the
@@ -551,6 +555,11 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     kvalid_next = kflag(0);
   }
   if (nch > 1) issue(1);
+  // The first chunks' loads were issued back to back, so waiting for all of
+  // them here costs little, and it lets the compiler count the K / V rows as
+  // arrived (it would otherwise wait for them, and for every load in flight,
+  // before each chunk's MFMAs).
+  vm_settled();
   for (int c = 0; c <= nch; ++c) {
     // Chunk c has landed once only chunk c + 1's loads may be outstanding.
     if (c + 1 < nch) {
@@ -593,11 +602,13 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
         xp[c & 1][kw][0][lane] = pf[0];
         xp[c & 1][kw][1][lane] = pf[1];
         const char* dtile = reinterpret_cast<const char*>(rd[st]);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
           for (int mb = 0; mb < G::MB; ++mb)
             acc[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], acc[mb]);
+        __builtin_amdgcn_s_setprio(0);
       }
     } else if (c > 0) {
       const int cp = c - 1, st = cp % QST;
@@ -619,11 +630,13 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
         }
       }
       const char* qtile = reinterpret_cast<const char*>(rq[st]);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int mb = 0; mb < G::MB; ++mb)
           acc[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], acc[mb]);
+      __builtin_amdgcn_s_setprio(0);
     }
   }
 

@@ -62,6 +62,15 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// A wait for all vector-memory loads that the compiler itself sees. Its count
+// of outstanding loads ignores the direct-to-LDS loads above (inline
+// assembly), and where it cannot prove that registers loaded earlier (a
+// wave's Q fragments, say) have arrived it waits for them before their next
+// use, with counts that then also drain the direct-to-LDS loads in flight.
+// Placed where every load has already been waited for, this costs nothing and
+// marks those registers as arrived for the code that follows.
+__device__ __forceinline__ void vm_settled() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
 // Per-lane byte offsets (within a chunk) of wave wv's share of a row tile's
 // loads when NW waves share them: load t of the wave is unit
 // p = (wv*RINS/NW + t)*64 + lane. With rmask = 15 the chunk is two 16-token

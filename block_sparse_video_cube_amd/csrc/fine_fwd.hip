@@ -262,6 +262,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sxa[e]);
     m = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
   }
+  vm_settled();
   // Bytes of this lane's LDS fragments within a stage: K row fragment ks,
   // and the two transposed reads of V fragment (mb, s2).
   uint32_t koffs[C::KS], voffs[C::MB][2][2];
@@ -345,10 +346,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
       l1 = __builtin_amdgcn_fdot2_f32_bf16(a1, ones2, l1, false);
     }
     lsum += l0 + l1;
+    // The wave issues its O MFMAs at raised priority, so that they go out
+    // back to back and the other wave of the SIMD fills the matrix pipe's
+    // shadow with its softmax and LDS reads (measured 1% faster).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) acc[mb] = mfma32_bf16(vf[mb][s2], pf[s2], acc[mb]);
+    __builtin_amdgcn_s_setprio(0);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
