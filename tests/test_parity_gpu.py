@@ -546,6 +546,32 @@ def test_backward_stages():
         assert rel_err(host(got), ref[nm]) <= 1e-4, nm
 
 
+@pytest.mark.parametrize("dtype,pool,cube,kcube", [("bf16", "mean", (4, 4, 4), None),
+                                                    ("bf16", "max", (4, 4, 4), (1, 4, 4)),
+                                                    ("f32", "mean", (2, 4, 4), (4, 4, 8)),
+                                                    ("f32", "max", (4, 4, 4), None)])
+def test_fine_backward_stage(dtype, pool, cube, kcube):
+    """The fine-backward entry point on its own: the oracle's LSE_f, dO_f,
+    delta and pooled gradients in (rounded to the GPU dtypes), the GPU's
+    transposed lists; dQ, dK, dV (fine part plus pool backward) against the
+    oracle's."""
+    x, p = _small_train_inputs(seed=71, cube=cube, kcube=kcube, dtype=dtype, scale=1.0 if dtype == "bf16" else 0.25)
+    p = dataclasses.replace(p, pool=pool)
+    d = inputs_to_dev(x, dtype)
+    fwd = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=x["idx"], lens=x["len"], pool_mode=pool,
+                    cube=cube, kcube=kcube)
+    ref = O.backward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], x["d_o"], fwd)
+    f32 = lambda a: dev(np.asarray(a, dtype=np.float32), torch.float32)
+    ws = V.workspace(p, d["q"], training=True)
+    off, k2q = V.index_transpose(p, d["idx"], d["len"], ws=ws)
+    dq, dk, dv = V.fine_backward(p, d["q"], d["k"], d["v"], d["idx"], d["len"], off, k2q, f32(fwd["lse_f"]),
+                                 dev(np.asarray(ref["d_o_f"], dtype=np.float32), p.torch_dtype), f32(ref["delta"]),
+                                 f32(ref["dq_c"]), f32(ref["dk_c"]), f32(ref["dv_c"]), ws)
+    torch.cuda.synchronize()
+    for got, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        assert_close(host(got), ref[nm], dtype, nm)
+
+
 # ------------------------------------------------------- max-pool variant
 @pytest.mark.parametrize("name", ["C1", "C2"])
 def test_max_pool_forward_topk(name):
