@@ -22,7 +22,7 @@ from ._native import VSA_BF16, VSA_F32, VsaError, VsaProblem, check, lib
 __all__ = ["Problem", "VsaError", "forward", "backward", "pool", "coarse", "fine_forward", "fine_combine", "combine",
            "combine_backward", "index_transpose", "fine_backward", "coarse_backward",
            "check_lists_host", "validate_lists", "workspace_bytes", "saved_bytes", "max_cubes", "tile", "untile",
-           "compatible_latent", "crop", "pad", "saved_views"]
+           "compatible_latent", "crop", "pad", "saved_views", "attention"]
 
 
 @dataclass(frozen=True)
@@ -331,3 +331,31 @@ def validate_lists(p: Problem, idx, lens) -> None:
     flag = _empty((4,), torch.int32, idx)
     check(lib().vsa_validate_lists(ctypes.byref(p.c()), _ptr(idx), _ptr(lens), _ptr(flag), _stream(idx.device)),
           "vsa_validate_lists")
+
+
+class _Attention(torch.autograd.Function):
+    """forward / backward of the library as one differentiable operation (the
+    selection is piecewise constant: idx and lens carry no gradient)."""
+
+    @staticmethod
+    def forward(ctx, p, q, k, v, g_c, g_f, idx, lens):
+        o, idx, lens, saved = forward(p, q, k, v, g_c, g_f, idx=idx, lens=lens, training=True)
+        ctx.p = p
+        ctx.save_for_backward(q, k, v, g_c, g_f, idx, lens, saved)
+        ctx.mark_non_differentiable(idx, lens)
+        return o, idx, lens
+
+    @staticmethod
+    def backward(ctx, d_o, _d_idx, _d_lens):
+        q, k, v, g_c, g_f, idx, lens, saved = ctx.saved_tensors
+        g = backward(ctx.p, q, k, v, g_c, g_f, idx, lens, saved, d_o.contiguous())
+        return None, g["dq"], g["dk"], g["dv"], g["dg_c"], g["dg_f"], None, None
+
+
+def attention(p: Problem, q, k, v, g_c=None, g_f=None, idx=None, lens=None):
+    """Differentiable VSA attention: returns (o, idx, lens); gradients flow to
+    q, k, v and the gates given (NULL gates are the constant 1). In top-K mode
+    idx / lens are outputs (fresh tensors unless given); in explicit-list mode
+    (p.topk == 0) they are the caller's lists. Every tensor must be contiguous
+    on the GPU in p's dtype and layout."""
+    return _Attention.apply(p, q, k, v, g_c, g_f, idx, lens)

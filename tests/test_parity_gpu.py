@@ -572,6 +572,29 @@ def test_fine_backward_stage(dtype, pool, cube, kcube):
         assert_close(host(got), ref[nm], dtype, nm)
 
 
+@pytest.mark.parametrize("dtype,topk", [("bf16", 0), ("bf16", 5), ("f32", 0)])
+def test_autograd_attention(dtype, topk):
+    """The differentiable wrapper: torch autograd through the library's
+    forward and backward, gradients against the oracle on the lists used."""
+    x, p = _small_train_inputs(seed=81, dtype=dtype, scale=1.0 if dtype == "bf16" else 0.25)
+    d = inputs_to_dev(x, dtype)
+    leaves = [d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g_c", "g_f")]
+    if topk:
+        p = dataclasses.replace(p, topk=topk, list_stride=topk)
+        o, idx, lens = V.attention(p, *leaves)
+    else:
+        o, idx, lens = V.attention(p, *leaves, idx=d["idx"], lens=d["len"])
+    assert not idx.requires_grad and not lens.requires_grad
+    o.backward(d["d_o"])
+    torch.cuda.synchronize()
+    gi, gl = host(idx), host(lens)
+    fwd = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=gl)
+    assert_close(host(o), fwd["o"], dtype, "o")
+    ref = O.backward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], x["d_o"], fwd)
+    for t, nm in zip(leaves, ("dq", "dk", "dv", "dg_c", "dg_f")):
+        assert_close(host(t.grad), ref[nm], dtype, nm)
+
+
 # ------------------------------------------------------- max-pool variant
 @pytest.mark.parametrize("name", ["C1", "C2"])
 def test_max_pool_forward_topk(name):
