@@ -382,38 +382,73 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const long n = tok0 + qrow;
   if (lse_f != nullptr && hf == 0) lse_f[n] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
+  // The normalised O goes through LDS so that every global access of the
+  // epilogue is a whole 16-byte unit of a token row, whole rows per
+  // instruction. Written from the accumulator layout (lane: one query, four
+  // channels per fragment) and read back by rows, each a plain copy of 32
+  // token rows; the rounding to bf16 is the one O_f gets when it is stored.
+  // A wave uses the chunk stage of its own index (one stage holds 32 rows of
+  // D channels), once every wave is done with the stages.
+  __syncthreads();
+  bf16* tile = wv < C::KST ? kbuf + wv * (C::KUNITS * 8) : vbuf + (wv - C::KST) * (C::VUNITS * 8);
 #pragma unroll
   for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
-      const int ch = 32 * mb + 8 * jq + 4 * hf;
-      float of[4];
+      bf16x4 w;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) of[r] = acc[mb][4 * jq + r] * inv;
-      if (o_f != nullptr) {
-        bf16x4 w;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (bf16)of[r];
-        *reinterpret_cast<bf16x4*>(o_f + n * D + ch) = w;
-      }
-      if (FUSED) {
-        // Round O_f to bf16 first so the fused output equals the unfused
-        // combine of the stored O_f.
-        const float4 c4 = *reinterpret_cast<const float4*>(oc + ((long)bh * g.Nc + i) * D + ch);
-        const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-        bf16x4 gcv, gfv;
-        if (gc != nullptr) gcv = *reinterpret_cast<const bf16x4*>(gc + n * D + ch);
-        if (gf != nullptr) gfv = *reinterpret_cast<const bf16x4*>(gf + n * D + ch);
-        bf16x4 w;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = gc != nullptr ? (float)gcv[r] : 1.f;
-          const float b = gf != nullptr ? (float)gfv[r] : 1.f;
-          w[r] = (bf16)(cv[r] * a + (float)(bf16)of[r] * b);
-        }
-        *reinterpret_cast<bf16x4*>(o + n * D + ch) = w;
-      }
+      for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[mb][4 * jq + r] * inv);
+      *reinterpret_cast<bf16x4*>(tile + (n32 * C::U + ((4 * mb + jq) ^ kswz<C::U>(n32))) * 8 + 4 * hf) = w;
     }
+  constexpr int RPI = 64 / C::U, NIT = 32 / RPI;   // token rows per instruction, instructions per tile
+  const int u = lane % C::U, r0 = lane / C::U;      // this lane's unit (channels 8u .. 8u+7) and first row
+  bf16x8 ofv[NIT];
+  long nrow[NIT];
+#pragma unroll
+  for (int t = 0; t < NIT; ++t) {
+    const int row = t * RPI + r0;
+    ofv[t] = *reinterpret_cast<const bf16x8*>(tile + (row * C::U + (u ^ kswz<C::U>(row))) * 8);
+    nrow[t] = (tok0 + cube_token(g, i, 32 * wv + row)) * D + u * 8;
+  }
+  if (o_f != nullptr) {
+#pragma unroll
+    for (int t = 0; t < NIT; ++t) *reinterpret_cast<bf16x8*>(o_f + nrow[t]) = ofv[t];
+  }
+  if (FUSED) {
+    // The gated combine, O_f taken as rounded to bf16 (so the fused output
+    // equals the unfused combine of the stored O_f). Which gates exist is
+    // decided outside the loops, so that every load is issued before the
+    // first use.
+    const float4* ocr = reinterpret_cast<const float4*>(oc + ((long)bh * g.Nc + i) * D + u * 8);
+    const float4 oa = ocr[0], ob = ocr[1];
+    const float cv[8] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
+    auto combine = [&](auto HC, auto HF) {
+      constexpr bool kHC = decltype(HC)::value, kHF = decltype(HF)::value;
+      bf16x8 gcv[NIT], gfv[NIT];
+#pragma unroll
+      for (int t = 0; t < NIT; ++t) {
+        if (kHC) gcv[t] = *reinterpret_cast<const bf16x8*>(gc + nrow[t]);
+        if (kHF) gfv[t] = *reinterpret_cast<const bf16x8*>(gf + nrow[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < NIT; ++t) {
+        bf16x8 w;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float a = kHC ? (float)gcv[t][r] : 1.f;
+          const float b = kHF ? (float)gfv[t][r] : 1.f;
+          w[r] = (bf16)(cv[r] * a + (float)ofv[t][r] * b);
+        }
+        *reinterpret_cast<bf16x8*>(o + nrow[t]) = w;
+      }
+    };
+    using T1 = std::true_type;
+    using F0 = std::false_type;
+    if (gc != nullptr && gf != nullptr) combine(T1(), T1());
+    else if (gc != nullptr) combine(T1(), F0());
+    else if (gf != nullptr) combine(F0(), T1());
+    else combine(F0(), F0());
+  }
 }
 
 // fp32 path: one thread per query token (a workgroup of Bt threads per query
