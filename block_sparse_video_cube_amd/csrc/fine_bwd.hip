@@ -31,29 +31,12 @@
 //                                            lane's K / V row (registers)
 //      dS = P * (dP - delta)                 LSE and delta per row (query)
 //      dV^T += dO_c^T P, dK^T += Q_c^T dS     A = dO / Q row tiles read transposed
+#include <type_traits>
+
 #include "fine_common.h"
 #include "vsa_kernels.h"
 
 namespace vsa {
-
-// Pool backward for one token and channels ch .. ch+3 of its cube: the pooled
-// gradient / Bt (mean pooling; inv_b = 1/Bt, exact), or the whole pooled
-// gradient where the token holds the cube's maximum (arg = the cube's argmax
-// positions, max pooling).
-__device__ __forceinline__ void pooled_grad(const float* dxc, const uint8_t* arg, int ch, int l, float inv_b,
-                                            float out[4]) {
-  const float4 c4 = *reinterpret_cast<const float4*>(dxc + ch);
-  const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
-  if (arg == nullptr) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) out[r] = cv[r] * inv_b;
-  } else {
-    const uchar4 a4 = *reinterpret_cast<const uchar4*>(arg + ch);
-    const int av[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) out[r] = av[r] == l ? cv[r] : 0.f;
-  }
-}
 
 // Processing order of the Nc key blocks of every (b, h) for the dK / dV
 // kernel: descending length of their transposed lists, ties by block id, so
@@ -218,23 +201,99 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
   }
 
   // lane holds dQ^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query]; the
-  // pooled gradient goes to every token (mean) or to the cube's maximum.
+  // pooled gradient goes to every token (mean) or to the cube's maximum. The
+  // pooling mode is decided outside the loops so that all of the epilogue's
+  // loads are issued before the first use; the bf16 result then goes through
+  // this wave's chunk stage so that the stores cover whole 16-byte units of
+  // token rows.
   const float* dqc_i = dqc + ((long)bh * g.Nc + i) * D;
   const uint8_t* qarg_i = qarg != nullptr ? qarg + ((long)bh * g.Nc + i) * D : nullptr;
   const int lq = 32 * wv + n32;   // the query's position in its cube
   const float inv_b = 1.0f / (float)g.B;
+  __syncthreads();   // every wave is done with the chunk stages
+  bf16* tile = wv < 2 ? rk[wv] : rv[wv - 2];
+  auto finish = [&](auto MAXP) {
+    constexpr bool kMax = decltype(MAXP)::value;
+    float4 c4[G::MB][4];
+    uchar4 a4[G::MB][4];
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb)
+    for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      const int ch = 32 * mb + 8 * jq + 4 * hf;
-      float cv[4];
-      pooled_grad(dqc_i, qarg_i, ch, lq, inv_b, cv);
-      bf16x4 w;
+      for (int jq = 0; jq < 4; ++jq) {
+        const int ch = 32 * mb + 8 * jq + 4 * hf;
+        c4[mb][jq] = *reinterpret_cast<const float4*>(dqc_i + ch);
+        if (kMax) a4[mb][jq] = *reinterpret_cast<const uchar4*>(qarg_i + ch);
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = (bf16)(scale * acc[mb][4 * jq + r] + cv[r]);
-      *reinterpret_cast<bf16x4*>(dq + n * D + ch) = w;
-    }
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const float cv[4] = {c4[mb][jq].x, c4[mb][jq].y, c4[mb][jq].z, c4[mb][jq].w};
+        const int av[4] = {a4[mb][jq].x, a4[mb][jq].y, a4[mb][jq].z, a4[mb][jq].w};
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pg = kMax ? (av[r] == lq ? cv[r] : 0.f) : cv[r] * inv_b;
+          w[r] = (bf16)(scale * acc[mb][4 * jq + r] + pg);
+        }
+        *reinterpret_cast<bf16x4*>(tile + (n32 * G::U + ((4 * mb + jq) ^ kswz<G::U>(n32))) * 8 + 4 * hf) = w;
+      }
+  };
+  if (qarg_i != nullptr) finish(std::true_type());
+  else finish(std::false_type());
+  constexpr int RPI = 64 / G::U, NIT = 32 / RPI;   // token rows per instruction, instructions per tile
+  const int u = lane % G::U, r0 = lane / G::U;
+  bf16x8 out[NIT];
+#pragma unroll
+  for (int t = 0; t < NIT; ++t) {
+    const int row = t * RPI + r0;
+    out[t] = *reinterpret_cast<const bf16x8*>(tile + (row * G::U + (u ^ kswz<G::U>(row))) * 8);
+  }
+#pragma unroll
+  for (int t = 0; t < NIT; ++t) {
+    const int row = t * RPI + r0;
+    *reinterpret_cast<bf16x8*>(dq + (tok0 + cube_token(g, i, 32 * wv + row)) * D + u * 8) = out[t];
+  }
+}
+
+// The pooled gradient of every channel a lane holds in the accumulator
+// layout (channel 32mb + 8jq + 4hf + r at out[mb][4jq + r]), for token
+// position l. The pooling mode is decided once, outside the loops, so that all
+// loads are issued before the first use.
+template <int MB>
+__device__ __forceinline__ void pooled_grads(const float* dxc, const uint8_t* arg, int hf, int l, float inv_b,
+                                             float out[MB][16]) {
+  float4 c4[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) c4[mb][jq] = *reinterpret_cast<const float4*>(dxc + 32 * mb + 8 * jq + 4 * hf);
+  if (arg == nullptr) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        out[mb][4 * jq + 0] = c4[mb][jq].x * inv_b;
+        out[mb][4 * jq + 1] = c4[mb][jq].y * inv_b;
+        out[mb][4 * jq + 2] = c4[mb][jq].z * inv_b;
+        out[mb][4 * jq + 3] = c4[mb][jq].w * inv_b;
+      }
+  } else {
+    uchar4 a4[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) a4[mb][jq] = *reinterpret_cast<const uchar4*>(arg + 32 * mb + 8 * jq + 4 * hf);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        out[mb][4 * jq + 0] = a4[mb][jq].x == l ? c4[mb][jq].x : 0.f;
+        out[mb][4 * jq + 1] = a4[mb][jq].y == l ? c4[mb][jq].y : 0.f;
+        out[mb][4 * jq + 2] = a4[mb][jq].z == l ? c4[mb][jq].z : 0.f;
+        out[mb][4 * jq + 3] = a4[mb][jq].w == l ? c4[mb][jq].w : 0.f;
+      }
+  }
 }
 
 // In both dK / dV kernels g is the grid of key blocks (the workgroup's own
@@ -422,19 +481,19 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
   const int lk = kwk.lk;   // the key's position in its block
   const float inv_b = 1.0f / (float)g.B;
   if (!kwk.own) return;   // no barrier below
+  float kcv[G::MB][16], vcv[G::MB][16];
+  pooled_grads<G::MB>(dkc + cj, karg_j, hf, lk, inv_b, kcv);
+  pooled_grads<G::MB>(dvc + cj, varg_j, hf, lk, inv_b, vcv);
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
       const int ch = 32 * mb + 8 * jq + 4 * hf;
-      float kcv[4], vcv[4];
-      pooled_grad(dkc + cj, karg_j, ch, lk, inv_b, kcv);
-      pooled_grad(dvc + cj, varg_j, ch, lk, inv_b, vcv);
       bf16x4 wk, wvv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        wk[r] = (bf16)(scale * adk[mb][4 * jq + r] + kcv[r]);
-        wvv[r] = (bf16)(adv[mb][4 * jq + r] + vcv[r]);
+        wk[r] = (bf16)(scale * adk[mb][4 * jq + r] + kcv[mb][4 * jq + r]);
+        wvv[r] = (bf16)(adv[mb][4 * jq + r] + vcv[mb][4 * jq + r]);
       }
       *reinterpret_cast<bf16x4*>(dk + n * D + ch) = wk;
       *reinterpret_cast<bf16x4*>(dv + n * D + ch) = wvv;
@@ -649,17 +708,16 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   const int lk = kwk.lk;   // the key's position in its block
   const float inv_b = 1.0f / (float)g.B;
   if (!kwk.own) return;   // no barrier below
+  float cv[G::MB][16];
+  pooled_grads<G::MB>(xc, arg_j, hf, lk, inv_b, cv);
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int jq = 0; jq < 4; ++jq) {
-      const int ch = 32 * mb + 8 * jq + 4 * hf;
-      float cv[4];
-      pooled_grad(xc, arg_j, ch, lk, inv_b, cv);
       bf16x4 w4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w4[r] = (bf16)(sc * acc[mb][4 * jq + r] + cv[r]);
-      *reinterpret_cast<bf16x4*>(out + n * D + ch) = w4;
+      for (int r = 0; r < 4; ++r) w4[r] = (bf16)(sc * acc[mb][4 * jq + r] + cv[mb][4 * jq + r]);
+      *reinterpret_cast<bf16x4*>(out + n * D + 32 * mb + 8 * jq + 4 * hf) = w4;
     }
 }
 
