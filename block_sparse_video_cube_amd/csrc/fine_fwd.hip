@@ -292,6 +292,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
       else if (kin || vin) wait_vmcnt<KPW>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
+    } else if (NW > 1 && C::KST < nch) {
+      // K of chunk KST goes into stage 0, which every wave read for the
+      // prologue's scores: all of them must be past those reads first.
+      __builtin_amdgcn_s_barrier();
     }
     if (c + C::VST - 1 < nch) issue_v(c + C::VST - 1);
     if (c + C::KST < nch) issue_k(c + C::KST);
