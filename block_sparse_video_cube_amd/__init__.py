@@ -84,15 +84,83 @@ class Problem:
                           *(self.kcube if self.kcube is not None else (0, 0, 0)))
 
 
-def _ptr(t: Optional[torch.Tensor]):
-    if t is None:
-        return None
-    if not t.is_contiguous():
-        raise ValueError("tensors passed to the VSA library must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+def _numel(shape) -> int:
+    n = 1
+    for e in shape:
+        n *= int(e)
+    return n
+
+
+class _Args:
+    """Checks every tensor handed to one library call before anything is
+    launched: the C ABI receives bare pointers and cannot tell a CPU tensor,
+    a wrong dtype or a short buffer from a good one, and a kernel given one
+    would read or write outside it. Each tensor must be a contiguous tensor on
+    the same HIP device as the call's first tensor, of the expected dtype and
+    with exactly the expected number of elements (any shape with that count
+    is accepted, e.g. [B, h, N] for a [B, h, T, H, W] per-token array).
+    Violations raise ValueError. Wrappers pass the library function through
+    call(), which checks the devices last."""
+
+    def __init__(self, where: str):
+        self.where = where
+        self.tensors = []
+
+    def _common(self, name: str, t) -> None:
+        if not t.is_contiguous():
+            raise ValueError(f"{self.where}: {name} must be contiguous")
+        self.tensors.append((name, t))
+
+    def call(self, fn, *args):
+        """Checks that every tensor seen is on one HIP device, then calls fn.
+        (The device check comes last so that dtype and size errors of every
+        argument are reported first.)"""
+        dev = None
+        for name, t in self.tensors:
+            if t.device.type != "cuda":
+                raise ValueError(f"{self.where}: {name} must be on a HIP (cuda) device, got {t.device}")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{self.where}: {name} is on {t.device}, the call's tensors on {dev}")
+        return fn(*args)
+
+    def t(self, name: str, t, shape, dtype, required: bool = True):
+        """Pointer of tensor t of `shape` (its element count) and `dtype`;
+        None passes through when not required."""
+        if t is None:
+            if required:
+                raise ValueError(f"{self.where}: {name} is required")
+            return None
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{self.where}: {name} must be a torch.Tensor, got {type(t).__name__}")
+        if t.dtype != dtype:
+            raise ValueError(f"{self.where}: {name} must be {dtype}, got {t.dtype}")
+        if t.numel() != _numel(shape):
+            raise ValueError(f"{self.where}: {name} has {t.numel()} elements ({tuple(t.shape)}), "
+                             f"expected {_numel(shape)} ({tuple(shape)})")
+        self._common(name, t)
+        return ctypes.c_void_p(t.data_ptr())
+
+    def buf(self, name: str, t, min_bytes: int, required: bool = True):
+        """Pointer and byte size of a raw buffer (workspace, saved) of at
+        least min_bytes."""
+        if t is None:
+            if required:
+                raise ValueError(f"{self.where}: {name} is required")
+            return None, 0
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{self.where}: {name} must be a torch.Tensor, got {type(t).__name__}")
+        nbytes = t.numel() * t.element_size()
+        if nbytes < min_bytes:
+            raise ValueError(f"{self.where}: {name} holds {nbytes} bytes, needs {min_bytes}")
+        self._common(name, t)
+        return ctypes.c_void_p(t.data_ptr()), nbytes
 
 
 def _stream(device) -> ctypes.c_void_p:
+    if device.type != "cuda":   # rejected by _Args.call before any library call
+        return ctypes.c_void_p(0)
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -131,17 +199,37 @@ def _tokens(p: Problem):
     return _raster(p)[:-1]
 
 
+def _full(p: Problem):
+    """Raster shape [B, h, T, H, W, d] whatever the problem's layout."""
+    return (p.B, p.heads, p.T, p.H, p.W, p.head_dim)
+
+
+def _cubes(p: Problem):
+    """Cube-major shape [B, h, Nc, Bt, d]."""
+    return (p.B, p.heads, p.Nc, p.Bt, p.head_dim)
+
+
+def _lists(p: Problem):
+    return (p.B, p.heads, p.Nc, p.stride), (p.B, p.heads, p.Nc)
+
+
 def tile(p: Problem, x):
     """Cube-major copy [B, h, Nc, Bt, d] of a raster token tensor."""
-    xt = _empty((p.B, p.heads, p.Nc, p.Bt, p.head_dim), x.dtype, x)
-    check(lib().vsa_tile(ctypes.byref(p.c()), _ptr(x), _ptr(xt), _stream(x.device)), "vsa_tile")
+    a = _Args("vsa_tile")
+    px = a.t("x", x, _full(p), p.torch_dtype)
+    xt = _empty(_cubes(p), x.dtype, x)
+    check(a.call(lib().vsa_tile, ctypes.byref(p.c()), px, a.t("xt", xt, _cubes(p), p.torch_dtype), _stream(x.device)),
+          "vsa_tile")
     return xt
 
 
 def untile(p: Problem, xt):
     """Raster copy [B, h, T, H, W, d] of a cube-major token tensor."""
-    x = _empty((p.B, p.heads, p.T, p.H, p.W, p.head_dim), xt.dtype, xt)
-    check(lib().vsa_untile(ctypes.byref(p.c()), _ptr(xt), _ptr(x), _stream(xt.device)), "vsa_untile")
+    a = _Args("vsa_untile")
+    pxt = a.t("xt", xt, _cubes(p), p.torch_dtype)
+    x = _empty(_full(p), xt.dtype, xt)
+    check(a.call(lib().vsa_untile, ctypes.byref(p.c()), pxt, a.t("x", x, _full(p), p.torch_dtype), _stream(xt.device)),
+          "vsa_untile")
     return x
 
 
@@ -154,16 +242,27 @@ def compatible_latent(T: int, H: int, W: int, cube: tuple = (4, 4, 4)) -> tuple:
 
 def crop(p: Problem, x, T: int, H: int, W: int):
     """Raster [B, h, T, H, W, d] copy of the leading region of a token tensor of p (p's layout)."""
-    out = _empty((p.B, p.heads, T, H, W, p.head_dim), x.dtype, x)
-    check(lib().vsa_crop(ctypes.byref(p.c()), _ptr(x), T, H, W, _ptr(out), _stream(x.device)), "vsa_crop")
+    a = _Args("vsa_crop")
+    px = a.t("x", x, _raster(p), p.torch_dtype)
+    shape = (p.B, p.heads, T, H, W, p.head_dim)
+    if min(T, H, W) < 1:
+        raise ValueError(f"vsa_crop: region {T}x{H}x{W} is empty")
+    out = _empty(shape, x.dtype, x)
+    check(a.call(lib().vsa_crop, ctypes.byref(p.c()), px, T, H, W, a.t("out", out, shape, p.torch_dtype), _stream(x.device)),
+          "vsa_crop")
     return out
 
 
 def pad(p: Problem, x):
     """Token tensor of p (p's layout) holding raster x [B, h, T, H, W, d] at the origin, zeros elsewhere."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 6:
+        raise ValueError("vsa_pad: x must be a raster tensor [B, h, T, H, W, d]")
     T, H, W = x.shape[2:5]
+    a = _Args("vsa_pad")
+    px = a.t("x", x, (p.B, p.heads, T, H, W, p.head_dim), p.torch_dtype)
     out = _empty(_raster(p), x.dtype, x)
-    check(lib().vsa_pad(ctypes.byref(p.c()), _ptr(x), T, H, W, _ptr(out), _stream(x.device)), "vsa_pad")
+    check(a.call(lib().vsa_pad, ctypes.byref(p.c()), px, T, H, W, a.t("out", out, _raster(p), p.torch_dtype),
+                        _stream(x.device)), "vsa_pad")
     return out
 
 
@@ -172,23 +271,36 @@ def _pooled(p: Problem, keys: bool = False):
     return (p.B, p.heads, p.Nk if keys else p.Nc, p.head_dim)
 
 
+def _qkv(a: _Args, p: Problem, q, k, v):
+    td = p.torch_dtype
+    return a.t("q", q, _raster(p), td), a.t("k", k, _raster(p), td), a.t("v", v, _raster(p), td)
+
+
 def forward(p: Problem, q, k, v, g_c=None, g_f=None, idx=None, lens=None, training: bool = False,
             ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
             saved: Optional[torch.Tensor] = None):
     """Whole VSA forward. Returns (o, idx, lens, saved); saved is None unless
     training or a saved buffer (uint8, saved_bytes(p)) is passed in."""
+    a = _Args("vsa_forward")
+    td = p.torch_dtype
+    pq, pk, pv = _qkv(a, p, q, k, v)
+    pgc, pgf = a.t("g_c", g_c, _raster(p), td, False), a.t("g_f", g_f, _raster(p), td, False)
     if p.topk > 0:
         idx = _empty((p.B, p.heads, p.Nc, p.stride), torch.int32, q) if idx is None else idx
         lens = _empty((p.B, p.heads, p.Nc), torch.int32, q) if lens is None else lens
     elif idx is None or lens is None:
         raise ValueError("explicit-list mode (topk == 0) needs idx and lens")
-    o = _empty(_raster(p), p.torch_dtype, q) if out is None else out
+    ishape, lshape = _lists(p)
+    pidx, plen = a.t("idx", idx, ishape, torch.int32), a.t("lens", lens, lshape, torch.int32)
+    o = _empty(_raster(p), td, q) if out is None else out
+    po = a.t("out", o, _raster(p), td)
     if saved is None and training:
         saved = torch.empty(saved_bytes(p), dtype=torch.uint8, device=q.device)
+    psaved, _ = a.buf("saved", saved, saved_bytes(p), required=False)
     ws = workspace(p, q) if ws is None else ws
-    check(lib().vsa_forward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(g_c), _ptr(g_f), _ptr(idx),
-                            _ptr(lens), _ptr(o), _ptr(saved), _ptr(ws), ws.numel(), _stream(q.device)),
-          "vsa_forward")
+    pws, nws = a.buf("ws", ws, workspace_bytes(p))
+    check(a.call(lib().vsa_forward, ctypes.byref(p.c()), pq, pk, pv, pgc, pgf, pidx, plen, po, psaved, pws, nws,
+                            _stream(q.device)), "vsa_forward")
     return o, idx, lens, saved
 
 
@@ -199,9 +311,7 @@ def saved_views(p: Problem, saved: torch.Tensor) -> dict:
 
     def take(shape, dtype):
         nonlocal off
-        n = 1
-        for e in shape:
-            n *= e
+        n = _numel(shape)
         esz = torch.empty((), dtype=dtype).element_size()
         t = saved[off:off + n * esz].view(dtype).view(shape)
         off += (n * esz + 255) // 256 * 256
@@ -216,26 +326,45 @@ def saved_views(p: Problem, saved: torch.Tensor) -> dict:
 
 def backward(p: Problem, q, k, v, g_c, g_f, idx, lens, saved, d_o, ws: Optional[torch.Tensor] = None):
     """Whole VSA backward. Returns dict dq, dk, dv, dg_c, dg_f (gate grads None for NULL gates)."""
-    dq, dk, dv = (_empty(_raster(p), p.torch_dtype, q) for _ in range(3))
-    dgc = _empty(_raster(p), p.torch_dtype, q) if g_c is not None else None
-    dgf = _empty(_raster(p), p.torch_dtype, q) if g_f is not None else None
+    a = _Args("vsa_backward")
+    td = p.torch_dtype
+    pq, pk, pv = _qkv(a, p, q, k, v)
+    pgc, pgf = a.t("g_c", g_c, _raster(p), td, False), a.t("g_f", g_f, _raster(p), td, False)
+    ishape, lshape = _lists(p)
+    pidx, plen = a.t("idx", idx, ishape, torch.int32), a.t("lens", lens, lshape, torch.int32)
+    psaved, _ = a.buf("saved", saved, saved_bytes(p))
+    pdo = a.t("d_o", d_o, _raster(p), td)
+    dq, dk, dv = (_empty(_raster(p), td, q) for _ in range(3))
+    dgc = _empty(_raster(p), td, q) if g_c is not None else None
+    dgf = _empty(_raster(p), td, q) if g_f is not None else None
     ws = workspace(p, q, training=True) if ws is None else ws
-    check(lib().vsa_backward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(g_c), _ptr(g_f), _ptr(idx),
-                             _ptr(lens), _ptr(saved), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgc),
-                             _ptr(dgf), _ptr(ws), ws.numel(), _stream(q.device)), "vsa_backward")
+    pws, nws = a.buf("ws", ws, workspace_bytes(p, training=True))
+    check(a.call(lib().vsa_backward, ctypes.byref(p.c()), pq, pk, pv, pgc, pgf, pidx, plen, psaved, pdo,
+                             a.t("dq", dq, _raster(p), td), a.t("dk", dk, _raster(p), td),
+                             a.t("dv", dv, _raster(p), td), a.t("dg_c", dgc, _raster(p), td, False),
+                             a.t("dg_f", dgf, _raster(p), td, False), pws, nws, _stream(q.device)), "vsa_backward")
     return dict(dq=dq, dk=dk, dv=dv, dg_c=dgc, dg_f=dgf)
 
 
 def pool(p: Problem, q, k, v, out=None):
+    a = _Args("vsa_pool")
+    pq, pk, pv = _qkv(a, p, q, k, v)
     qc, kc, vc = out if out is not None else (_empty(_pooled(p, keys), torch.float32, q) for keys in (0, 1, 1))
-    check(lib().vsa_pool(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(qc), _ptr(kc), _ptr(vc),
+    f = torch.float32
+    check(a.call(lib().vsa_pool, ctypes.byref(p.c()), pq, pk, pv, a.t("q_c", qc, _pooled(p), f),
+                         a.t("k_c", kc, _pooled(p, True), f), a.t("v_c", vc, _pooled(p, True), f),
                          _stream(q.device)), "vsa_pool")
     return qc, kc, vc
 
 
 def coarse(p: Problem, q_c, k_c, v_c, out=None, ws: Optional[torch.Tensor] = None):
     """Coarse stage; out = (o_c, lse_c, idx, lens) reuses caller buffers."""
+    a = _Args("vsa_coarse")
+    f = torch.float32
+    pqc = a.t("q_c", q_c, _pooled(p), f)
+    pkc, pvc = a.t("k_c", k_c, _pooled(p, True), f), a.t("v_c", v_c, _pooled(p, True), f)
     ws = workspace(p, q_c) if ws is None else ws
+    pws, nws = a.buf("ws", ws, workspace_bytes(p))
     if out is not None:
         oc, lse, idx, lens = out
     else:
@@ -245,16 +374,25 @@ def coarse(p: Problem, q_c, k_c, v_c, out=None, ws: Optional[torch.Tensor] = Non
         if p.topk > 0:
             idx = _empty((p.B, p.heads, p.Nc, p.stride), torch.int32, q_c)
             lens = _empty((p.B, p.heads, p.Nc), torch.int32, q_c)
-    check(lib().vsa_coarse(ctypes.byref(p.c()), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(oc), _ptr(lse), _ptr(idx),
-                           _ptr(lens), _ptr(ws), ws.numel(), _stream(q_c.device)), "vsa_coarse")
+    ishape, lshape = _lists(p)
+    sel = p.topk > 0
+    check(a.call(lib().vsa_coarse, ctypes.byref(p.c()), pqc, pkc, pvc, a.t("o_c", oc, _pooled(p), f),
+                           a.t("lse_c", lse, (p.B, p.heads, p.Nc), f), a.t("idx", idx, ishape, torch.int32, sel),
+                           a.t("lens", lens, lshape, torch.int32, sel), pws, nws, _stream(q_c.device)), "vsa_coarse")
     return oc, lse, idx, lens
 
 
 def fine_forward(p: Problem, q, k, v, idx, lens, ws: Optional[torch.Tensor] = None):
+    a = _Args("vsa_fine_forward")
+    pq, pk, pv = _qkv(a, p, q, k, v)
+    ishape, lshape = _lists(p)
+    pidx, plen = a.t("idx", idx, ishape, torch.int32), a.t("lens", lens, lshape, torch.int32)
+    ws = workspace(p, q) if ws is None else ws
+    pws, nws = a.buf("ws", ws, workspace_bytes(p))
     of = _empty(_raster(p), p.torch_dtype, q)
     lse = _empty(_tokens(p), torch.float32, q)
-    check(lib().vsa_fine_forward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(lens), _ptr(of),
-                                 _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(q.device)),
+    check(a.call(lib().vsa_fine_forward, ctypes.byref(p.c()), pq, pk, pv, pidx, plen, a.t("o_f", of, _raster(p), p.torch_dtype),
+                                 a.t("lse_f", lse, _tokens(p), torch.float32), pws, nws, _stream(q.device)),
           "vsa_fine_forward")
     return of, lse
 
@@ -262,58 +400,107 @@ def fine_forward(p: Problem, q, k, v, idx, lens, ws: Optional[torch.Tensor] = No
 def fine_combine(p: Problem, q, k, v, idx, lens, o_c, g_c=None, g_f=None, ws: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None, with_fine: bool = False):
     """Fused fine stage + gated combine. Returns o, or (o, o_f, lse_f) with with_fine."""
-    o = _empty(_raster(p), p.torch_dtype, q) if out is None else out
-    of = _empty(_raster(p), p.torch_dtype, q) if with_fine else None
+    a = _Args("vsa_fine_combine")
+    td = p.torch_dtype
+    pq, pk, pv = _qkv(a, p, q, k, v)
+    ishape, lshape = _lists(p)
+    pidx, plen = a.t("idx", idx, ishape, torch.int32), a.t("lens", lens, lshape, torch.int32)
+    poc = a.t("o_c", o_c, _pooled(p), torch.float32)
+    pgc, pgf = a.t("g_c", g_c, _raster(p), td, False), a.t("g_f", g_f, _raster(p), td, False)
+    ws = workspace(p, q) if ws is None else ws
+    pws, nws = a.buf("ws", ws, workspace_bytes(p))
+    o = _empty(_raster(p), td, q) if out is None else out
+    of = _empty(_raster(p), td, q) if with_fine else None
     lse = _empty(_tokens(p), torch.float32, q) if with_fine else None
-    check(lib().vsa_fine_combine(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(lens), _ptr(o_c),
-                                 _ptr(g_c), _ptr(g_f), _ptr(o), _ptr(of), _ptr(lse), _ptr(ws),
-                                 0 if ws is None else ws.numel(), _stream(q.device)), "vsa_fine_combine")
+    check(a.call(lib().vsa_fine_combine, ctypes.byref(p.c()), pq, pk, pv, pidx, plen, poc, pgc, pgf,
+                                 a.t("out", o, _raster(p), td), a.t("o_f", of, _raster(p), td, False),
+                                 a.t("lse_f", lse, _tokens(p), torch.float32, False), pws, nws, _stream(q.device)),
+          "vsa_fine_combine")
     return (o, of, lse) if with_fine else o
 
 
 def combine(p: Problem, o_c, o_f, g_c=None, g_f=None):
-    o = _empty(_raster(p), p.torch_dtype, o_f)
-    check(lib().vsa_combine(ctypes.byref(p.c()), _ptr(o_c), _ptr(o_f), _ptr(g_c), _ptr(g_f), _ptr(o),
+    a = _Args("vsa_combine")
+    td = p.torch_dtype
+    pof = a.t("o_f", o_f, _raster(p), td)
+    poc = a.t("o_c", o_c, _pooled(p), torch.float32)
+    pgc, pgf = a.t("g_c", g_c, _raster(p), td, False), a.t("g_f", g_f, _raster(p), td, False)
+    o = _empty(_raster(p), td, o_f)
+    check(a.call(lib().vsa_combine, ctypes.byref(p.c()), poc, pof, pgc, pgf, a.t("o", o, _raster(p), td),
                             _stream(o_f.device)), "vsa_combine")
     return o
 
 
 def combine_backward(p: Problem, d_o, o_c, o_f, g_c=None, g_f=None):
-    dgc = _empty(_raster(p), p.torch_dtype, d_o) if g_c is not None else None
-    dgf = _empty(_raster(p), p.torch_dtype, d_o) if g_f is not None else None
-    dof = _empty(_raster(p), p.torch_dtype, d_o)
-    delta = _empty(_tokens(p), torch.float32, d_o)
-    doc = _empty(_pooled(p), torch.float32, d_o)
-    check(lib().vsa_combine_backward(ctypes.byref(p.c()), _ptr(d_o), _ptr(o_c), _ptr(o_f), _ptr(g_c), _ptr(g_f),
-                                     _ptr(dgc), _ptr(dgf), _ptr(dof), _ptr(delta), _ptr(doc), _stream(d_o.device)),
-          "vsa_combine_backward")
+    a = _Args("vsa_combine_backward")
+    td, f = p.torch_dtype, torch.float32
+    pdo = a.t("d_o", d_o, _raster(p), td)
+    poc, pof = a.t("o_c", o_c, _pooled(p), f), a.t("o_f", o_f, _raster(p), td)
+    pgc, pgf = a.t("g_c", g_c, _raster(p), td, False), a.t("g_f", g_f, _raster(p), td, False)
+    dgc = _empty(_raster(p), td, d_o) if g_c is not None else None
+    dgf = _empty(_raster(p), td, d_o) if g_f is not None else None
+    dof = _empty(_raster(p), td, d_o)
+    delta = _empty(_tokens(p), f, d_o)
+    doc = _empty(_pooled(p), f, d_o)
+    check(a.call(lib().vsa_combine_backward, ctypes.byref(p.c()), pdo, poc, pof, pgc, pgf,
+                                     a.t("dg_c", dgc, _raster(p), td, False), a.t("dg_f", dgf, _raster(p), td, False),
+                                     a.t("d_o_f", dof, _raster(p), td), a.t("delta", delta, _tokens(p), f),
+                                     a.t("d_o_c", doc, _pooled(p), f), _stream(d_o.device)), "vsa_combine_backward")
     return dict(dg_c=dgc, dg_f=dgf, d_o_f=dof, delta=delta, d_o_c=doc)
 
 
+def _k2q_shapes(p: Problem):
+    return (p.B, p.heads, p.Nk + 1), (p.B, p.heads, p.Nc * p.stride)
+
+
 def index_transpose(p: Problem, idx, lens, ws: Optional[torch.Tensor] = None):
-    off = _empty((p.B, p.heads, p.Nk + 1), torch.int32, idx)
-    k2q = _empty((p.B, p.heads, p.Nc * p.stride), torch.int32, idx)
+    a = _Args("vsa_index_transpose")
+    ishape, lshape = _lists(p)
+    pidx, plen = a.t("idx", idx, ishape, torch.int32), a.t("lens", lens, lshape, torch.int32)
     ws = workspace(p, idx, training=True) if ws is None else ws
-    check(lib().vsa_index_transpose(ctypes.byref(p.c()), _ptr(idx), _ptr(lens), _ptr(off), _ptr(k2q), _ptr(ws),
-                                    ws.numel(), _stream(idx.device)), "vsa_index_transpose")
+    pws, nws = a.buf("ws", ws, workspace_bytes(p, training=True))
+    oshape, kshape = _k2q_shapes(p)
+    off = _empty(oshape, torch.int32, idx)
+    k2q = _empty(kshape, torch.int32, idx)
+    check(a.call(lib().vsa_index_transpose, ctypes.byref(p.c()), pidx, plen, a.t("k2q_off", off, oshape, torch.int32),
+                                    a.t("k2q", k2q, kshape, torch.int32), pws, nws, _stream(idx.device)),
+          "vsa_index_transpose")
     return off, k2q
 
 
 def fine_backward(p: Problem, q, k, v, idx, lens, k2q_off, k2q, lse_f, d_o_f, delta, dq_c, dk_c, dv_c,
-                  ws: torch.Tensor):
-    dq, dk, dv = (_empty(_raster(p), p.torch_dtype, q) for _ in range(3))
-    check(lib().vsa_fine_backward(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(lens),
-                                  _ptr(k2q_off), _ptr(k2q), _ptr(lse_f), _ptr(d_o_f), _ptr(delta), _ptr(dq_c),
-                                  _ptr(dk_c), _ptr(dv_c), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                  ws: Optional[torch.Tensor] = None):
+    a = _Args("vsa_fine_backward")
+    td, f = p.torch_dtype, torch.float32
+    pq, pk, pv = _qkv(a, p, q, k, v)
+    ishape, lshape = _lists(p)
+    oshape, kshape = _k2q_shapes(p)
+    args = [pq, pk, pv, a.t("idx", idx, ishape, torch.int32), a.t("lens", lens, lshape, torch.int32),
+            a.t("k2q_off", k2q_off, oshape, torch.int32), a.t("k2q", k2q, kshape, torch.int32),
+            a.t("lse_f", lse_f, _tokens(p), f), a.t("d_o_f", d_o_f, _raster(p), td),
+            a.t("delta", delta, _tokens(p), f), a.t("dq_c", dq_c, _pooled(p), f),
+            a.t("dk_c", dk_c, _pooled(p, True), f), a.t("dv_c", dv_c, _pooled(p, True), f)]
+    ws = workspace(p, q, training=True) if ws is None else ws
+    pws, nws = a.buf("ws", ws, workspace_bytes(p, training=True))
+    dq, dk, dv = (_empty(_raster(p), td, q) for _ in range(3))
+    check(a.call(lib().vsa_fine_backward, ctypes.byref(p.c()), *args, a.t("dq", dq, _raster(p), td),
+                                  a.t("dk", dk, _raster(p), td), a.t("dv", dv, _raster(p), td), pws, nws,
                                   _stream(q.device)), "vsa_fine_backward")
     return dq, dk, dv
 
 
-def coarse_backward(p: Problem, q_c, k_c, v_c, o_c, lse_c, d_o_c, ws: torch.Tensor):
-    dqc, dkc, dvc = (_empty(_pooled(p, keys), torch.float32, q_c) for keys in (0, 1, 1))
-    check(lib().vsa_coarse_backward(ctypes.byref(p.c()), _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(o_c),
-                                    _ptr(lse_c), _ptr(d_o_c), _ptr(dqc), _ptr(dkc), _ptr(dvc), _ptr(ws),
-                                    ws.numel(), _stream(q_c.device)), "vsa_coarse_backward")
+def coarse_backward(p: Problem, q_c, k_c, v_c, o_c, lse_c, d_o_c, ws: Optional[torch.Tensor] = None):
+    a = _Args("vsa_coarse_backward")
+    f = torch.float32
+    args = [a.t("q_c", q_c, _pooled(p), f), a.t("k_c", k_c, _pooled(p, True), f),
+            a.t("v_c", v_c, _pooled(p, True), f), a.t("o_c", o_c, _pooled(p), f),
+            a.t("lse_c", lse_c, (p.B, p.heads, p.Nc), f), a.t("d_o_c", d_o_c, _pooled(p), f)]
+    ws = workspace(p, q_c, training=True) if ws is None else ws
+    pws, nws = a.buf("ws", ws, workspace_bytes(p, training=True))
+    dqc, dkc, dvc = (_empty(_pooled(p, keys), f, q_c) for keys in (0, 1, 1))
+    check(a.call(lib().vsa_coarse_backward, ctypes.byref(p.c()), *args, a.t("dq_c", dqc, _pooled(p), f),
+                                    a.t("dk_c", dkc, _pooled(p, True), f), a.t("dv_c", dvc, _pooled(p, True), f),
+                                    pws, nws, _stream(q_c.device)), "vsa_coarse_backward")
     return dqc, dkc, dvc
 
 
@@ -322,15 +509,22 @@ def check_lists_host(p: Problem, idx, lens) -> None:
     import numpy as np
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     lens = np.ascontiguousarray(lens, dtype=np.int32)
+    ishape, lshape = _lists(p)
+    if idx.size != _numel(ishape) or lens.size != _numel(lshape):
+        raise ValueError(f"vsa_check_lists_host: idx {idx.shape} / lens {lens.shape} do not hold "
+                         f"{ishape} / {lshape} elements")
     check(lib().vsa_check_lists_host(ctypes.byref(p.c()), idx.ctypes.data_as(ctypes.c_void_p),
                                      lens.ctypes.data_as(ctypes.c_void_p)), "vsa_check_lists_host")
 
 
 def validate_lists(p: Problem, idx, lens) -> None:
     """Device check of explicit lists (synchronises the current stream; raises VsaError)."""
+    a = _Args("vsa_validate_lists")
+    ishape, lshape = _lists(p)
+    pidx, plen = a.t("idx", idx, ishape, torch.int32), a.t("lens", lens, lshape, torch.int32)
     flag = _empty((4,), torch.int32, idx)
-    check(lib().vsa_validate_lists(ctypes.byref(p.c()), _ptr(idx), _ptr(lens), _ptr(flag), _stream(idx.device)),
-          "vsa_validate_lists")
+    check(a.call(lib().vsa_validate_lists, ctypes.byref(p.c()), pidx, plen, a.t("flag", flag, (4,), torch.int32),
+                                   _stream(idx.device)), "vsa_validate_lists")
 
 
 class _Attention(torch.autograd.Function):
