@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import argparse
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -39,17 +40,73 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the VSA HIP library cannot be built")
 
 
+# Sources whose kernels issue direct-to-LDS loads through inline assembly that
+# sets M0 (fine_common.h). M0 is a register the compiler reserves for its own
+# use, so it cannot be declared clobbered; instead every build checks the
+# generated gfx950 assembly of these sources (kept by -save-temps) and fails
+# if the compiler touches M0 anywhere else in a kernel that issues them.
+M0_SOURCES = ("fine_fwd.hip", "fine_bwd.hip")
+_DMA = "global_load_lds_dwordx4"
+_M0 = re.compile(r"\bm0\b")
+
+
+def check_m0(asm: str) -> list[str]:
+    """Findings in gfx950 assembly text: in every function that issues
+    global_load_lds_dwordx4, each instruction naming M0 must be an
+    `s_mov_b32 m0, <sgpr>` followed directly by `s_nop 0` and the load, and
+    every such load must be preceded by one. Returns the violations."""
+    bad = []
+    funcs, cur, name = [], [], None
+    for line in asm.splitlines():
+        code = line.split(";", 1)[0].strip()
+        if code.endswith(":") and not code.startswith(".") and " " not in code:
+            if name is not None:
+                funcs.append((name, cur))
+            name, cur = code[:-1], []
+            continue
+        if code and not code.startswith("."):
+            cur.append(code)
+    if name is not None:
+        funcs.append((name, cur))
+    for fname, ins in funcs:
+        if not any(i.startswith(_DMA) for i in ins):
+            continue
+        for n, i in enumerate(ins):
+            if i.startswith(_DMA):
+                if n < 2 or ins[n - 1] != "s_nop 0" or not re.fullmatch(r"s_mov_b32 m0, \S+", ins[n - 2]):
+                    bad.append(f"{fname}: {_DMA} #{n} without its own M0 set-up")
+                continue
+            if _M0.search(i) is None:
+                continue
+            if (re.fullmatch(r"s_mov_b32 m0, \S+", i) and n + 2 < len(ins) and ins[n + 1] == "s_nop 0"
+                    and ins[n + 2].startswith(_DMA)):
+                continue
+            bad.append(f"{fname}: M0 used outside the direct-to-LDS loads: {i}")
+    return bad
+
+
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", out]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    temps = ["-save-temps=obj"] if src in M0_SOURCES else []
+    cmd = [hipcc(), *FLAGS, *temps, *lang, "-c", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=OBJ)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{err}")
     if err.strip():
         sys.stderr.write(err + "\n")
+    if temps:
+        stem = os.path.splitext(os.path.basename(src))[0]
+        asm = os.path.join(OBJ, f"{stem}-hip-amdgcn-amd-amdhsa-{ARCH}.s")
+        with open(asm) as f:
+            text = f.read()
+        if _DMA not in text:
+            raise RuntimeError(f"{src}: no {_DMA} in {asm}; the M0 check saw no loads")
+        bad = check_m0(text)
+        if bad:
+            raise RuntimeError(f"{src}: M0 check failed:\n" + "\n".join(bad[:20]))
     return out
 
 

@@ -39,7 +39,10 @@ template <int U> __device__ __forceinline__ int kswz(int kappa) {
 // address lds + 16*l. Issued as inline assembly so that the compiler does not
 // treat later LDS reads of other stages as dependent on it; completion is
 // tracked by the vector-memory counter and waited for explicitly (wait_vmcnt).
-// The compiler never uses M0 in these kernels (checked on the generated code).
+// M0 is a register the compiler reserves, so it cannot be declared clobbered;
+// the build (build.py, check_m0) inspects the generated assembly of every
+// kernel that issues these loads and fails if the compiler uses M0 anywhere
+// else in it, so nothing can depend on M0 across this statement.
 // The address is a wave-uniform base (SGPRs) plus a per-lane 32-bit byte
 // offset, so issuing a load costs no vector instructions.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
