@@ -511,11 +511,6 @@ def fine_flops_forward(lens: np.ndarray, d: int, tile_size: int = TILE) -> float
     return 4.0 * tile_size * tile_size * d * float(np.sum(lens))
 
 
-def fine_flops_backward(lens: np.ndarray, d: int, tile_size: int = TILE) -> float:
-    """10*B*B*d FLOPs per block pair (2.5x the forward, the usual convention)."""
-    return 10.0 * tile_size * tile_size * d * float(np.sum(lens))
-
-
 def coarse_flops(B: int, nh: int, nc: int, d: int) -> float:
     """4*Nc^2*d per (b, h): the pooled score matrix and A_c V_c."""
     return 4.0 * B * nh * nc * nc * d

@@ -556,3 +556,45 @@ def test_pool_error_bound_exactness_claim():
         pair = (pair[:, 0::2, :] + pair[:, 1::2, :]).astype(np.float32)
     assert np.all(np.abs(pair[:, 0, :].astype(np.float64) / 64 - exact) <= bound)
     assert (bound == 0).mean() > 0.9
+
+
+# ------------------------------------------------- precision detection (tau)
+def test_bf16_exact_detects_bf16_values():
+    """_bf16_exact decides how many significant bits the inputs carry, hence
+    tau and which top-K rows must match bit for bit. bf16-rounded values
+    (torch's RNE conversion) are detected; generic fp32 values are not; a
+    single fp32 value among bf16 ones is enough to fail."""
+    import torch
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2, 3, 8, 8, 8, 64)).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert O._bf16_exact(xb)
+    assert not O._bf16_exact(x)
+    y = xb.copy()
+    y.flat[12345] = np.float32(1.0) + np.float32(2.0 ** -20)
+    assert not O._bf16_exact(y)
+    assert O._bf16_exact(np.zeros(4, np.float32))
+    # float64 inputs holding bf16 values are bf16-exact too (the check goes
+    # through fp32, which represents them exactly)
+    assert O._bf16_exact(xb.astype(np.float64))
+
+
+def test_forward_picks_sig_bits_from_input_precision():
+    """forward() bounds the pooling error with 8 significant bits for bf16
+    inputs and 24 for generic fp32 inputs: its tau equals logit_error_bound
+    called with those bits, and the fp32 bound is the larger one."""
+    import torch
+    rng = np.random.default_rng(4)
+    shape = (1, 1, 8, 8, 16, 64)
+    x32 = {n: rng.standard_normal(shape).astype(np.float32) for n in "qkv"}
+    xbf = {n: torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy() for n, a in x32.items()}
+    s = 1 / 8.0
+    for xs, bits in ((xbf, 8), (x32, 24)):
+        f = O.forward(xs["q"], xs["k"], xs["v"], topk=3)
+        qt = O.tile(xs["q"].astype(np.float64))[0, 0]
+        kt = O.tile(xs["k"].astype(np.float64))[0, 0]
+        assert np.array_equal(f["tau"][0, 0], O.logit_error_bound(qt, kt, s, sig_bits=bits))
+    f32 = O.forward(x32["q"], x32["k"], x32["v"], topk=3)["tau"]
+    qt = O.tile(x32["q"].astype(np.float64))[0, 0]
+    kt = O.tile(x32["k"].astype(np.float64))[0, 0]
+    assert np.all(f32[0, 0] > O.logit_error_bound(qt, kt, s, sig_bits=8))
