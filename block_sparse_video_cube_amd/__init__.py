@@ -19,7 +19,7 @@ import torch
 
 from ._native import VSA_BF16, VSA_F32, VsaError, VsaProblem, check, lib
 
-__all__ = ["Problem", "VsaError", "forward", "backward", "pool", "coarse", "fine_forward", "fine_combine", "combine",
+__all__ = ["Problem", "VsaError", "forward", "backward", "pool", "coarse", "fine_forward", "fine_combine", "fine_combine_noalloc", "combine",
            "combine_backward", "index_transpose", "fine_backward", "coarse_backward",
            "check_lists_host", "validate_lists", "workspace_bytes", "saved_bytes", "max_cubes", "tile", "untile",
            "compatible_latent", "crop", "pad", "saved_views", "attention"]
@@ -417,6 +417,28 @@ def fine_combine(p: Problem, q, k, v, idx, lens, o_c, g_c=None, g_f=None, ws: Op
                                  a.t("lse_f", lse, _tokens(p), torch.float32, False), pws, nws, _stream(q.device)),
           "vsa_fine_combine")
     return (o, of, lse) if with_fine else o
+
+
+def fine_combine_noalloc(p: Problem, q, k, v, idx, lens, o_c, g_c=None, g_f=None,
+                         out: Optional[torch.Tensor] = None, o_f: Optional[torch.Tensor] = None,
+                         lse_f: Optional[torch.Tensor] = None):
+    """fine_combine without a workspace: the library keeps its scratch in a
+    static device array (B * heads * Nc <= 1,048,576; overlapping calls on
+    one GPU race). Outputs are the caller's tensors when given (o_f / lse_f
+    optional); nothing else is allocated when `out` is given. Returns o."""
+    a = _Args("vsa_fine_combine_noalloc")
+    td = p.torch_dtype
+    pq, pk, pv = _qkv(a, p, q, k, v)
+    ishape, lshape = _lists(p)
+    pidx, plen = a.t("idx", idx, ishape, torch.int32), a.t("lens", lens, lshape, torch.int32)
+    poc = a.t("o_c", o_c, _pooled(p), torch.float32)
+    pgc, pgf = a.t("g_c", g_c, _raster(p), td, False), a.t("g_f", g_f, _raster(p), td, False)
+    o = _empty(_raster(p), td, q) if out is None else out
+    check(a.call(lib().vsa_fine_combine_noalloc, ctypes.byref(p.c()), pq, pk, pv, pidx, plen, poc, pgc, pgf,
+                 a.t("out", o, _raster(p), td), a.t("o_f", o_f, _raster(p), td, False),
+                 a.t("lse_f", lse_f, _tokens(p), torch.float32, False), _stream(q.device)),
+          "vsa_fine_combine_noalloc")
+    return o
 
 
 def combine(p: Problem, o_c, o_f, g_c=None, g_f=None):

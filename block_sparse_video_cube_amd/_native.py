@@ -51,6 +51,7 @@ SIGNATURES = {
     "vsa_coarse": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_fine_forward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_fine_combine": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
+    "vsa_fine_combine_noalloc": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v]),
     "vsa_combine": (_i32, [_P, _v, _v, _v, _v, _v, _v]),
     "vsa_combine_backward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v]),
     "vsa_index_transpose": (_i32, [_P, _v, _v, _v, _v, _v, _sz, _v]),

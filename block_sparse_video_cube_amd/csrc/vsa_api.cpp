@@ -1,7 +1,9 @@
 // C ABI of the VSA operator: validation, buffer layouts, kernel sequencing.
 // Declarations and contracts: include/vsa.h.
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/vsa.h"
 #include "vsa_kernels.h"
@@ -180,6 +182,39 @@ BwdWs carve_bwd_ws(const Dims& d, void* base) {
 
 inline vsa_status hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
 
+// ---- static scratch of vsa_fine_combine_noalloc ---------------------------
+// The query-cube processing order (one int32 per query cube of every
+// (b, h)), the only scratch of the fine + combine kernels, kept in a
+// file-scope device array so that the call allocates nothing. Each GPU holds
+// its own copy for the life of the process. Host code never uses the array's
+// name as an address: its device address is looked up per device.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+constexpr long kNoAllocMaxCubes = long(kNoAllocScratchBytes / sizeof(int32_t));
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+namespace {
+// Device address of `scratch` on the current device, looked up on the first
+// call there (with that device current) and kept; nullptr on failure.
+int32_t* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  int32_t* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return nullptr;
+  ptr = static_cast<int32_t*>(addr);
+  g_scratch[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
 }  // namespace
 
 extern "C" {
@@ -346,6 +381,30 @@ vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, 
     order = ws.order;
   }
   L.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = order != nullptr ? launch_order(L, idx, len, order) : hipSuccess;
+  if (e == hipSuccess) e = launch_fine_fwd(L, q, k, v, idx, len, order, o_f, lse_f, o_c, g_c, g_f, o);
+  return hip_status(e);
+}
+
+vsa_status vsa_fine_combine_noalloc(const vsa_problem* p, const void* q, const void* k, const void* v,
+                                    const int32_t* idx, const int32_t* len, const float* o_c, const void* g_c,
+                                    const void* g_f, void* o, void* o_f, float* lse_f, void* stream) {
+  Launch L;
+  Dims d;
+  vsa_status st = check_problem(p, &L, &d);
+  if (st != VSA_OK) return st;
+  st = check_ptrs({{q, true}, {k, true}, {v, true}, {idx, true}, {len, true}, {o_c, true}, {g_c, false},
+                   {g_f, false}, {o, true}, {o_f, false}, {lse_f, false}});
+  if (st != VSA_OK) return st;
+  if (d.BH * d.Nq > kNoAllocMaxCubes) return VSA_ERR_WORKSPACE;
+  int32_t* order = nullptr;
+  if (L.bf16) {
+    order = scratch_ptr();
+    if (order == nullptr) return VSA_ERR_HIP;
+  }
+  L.stream = static_cast<hipStream_t>(stream);
+  // launch_order writes all B*heads*Nq entries before the fine kernel reads
+  // any, so nothing left by an earlier call is ever read.
   hipError_t e = order != nullptr ? launch_order(L, idx, len, order) : hipSuccess;
   if (e == hipSuccess) e = launch_fine_fwd(L, q, k, v, idx, len, order, o_f, lse_f, o_c, g_c, g_f, o);
   return hip_status(e);

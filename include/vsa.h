@@ -226,6 +226,22 @@ vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, 
                             const void* g_c, const void* g_f, void* o, void* o_f, float* lse_f,
                             const void* workspace, size_t ws_bytes, void* stream);
 
+/* vsa_fine_combine without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). It runs the same kernels; the query-cube
+ * order they need lives in a 4 MiB device array inside the library (one per
+ * GPU, held until the process ends), so B * heads * Nc may not exceed
+ * 1,048,576 (VSA_ERR_WORKSPACE otherwise, before anything is enqueued). The
+ * call allocates nothing. It uses the array of the current device, so
+ * `stream` must belong to the current device; the first call on a device
+ * looks up the array's address (VSA_ERR_HIP if that fails). Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller; consecutive calls
+ * on one stream are safe. Arguments and results as for vsa_fine_combine. */
+vsa_status vsa_fine_combine_noalloc(const vsa_problem* p, const void* q, const void* k, const void* v,
+                                    const int32_t* idx, const int32_t* len, const float* o_c, const void* g_c,
+                                    const void* g_f, void* o, void* o_f, float* lse_f, void* stream);
+
 /* Step 5, gated combine + untile: o = O_c[cube(token)] * g_c + o_f * g_f
  * (reading notes key design 3; App. B repeat of the coarse output). Gates
  * NULL => ones. */

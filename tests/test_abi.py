@@ -273,3 +273,19 @@ def test_check_lists_host():
         with pytest.raises(V.VsaError) as e:
             V.check_lists_host(p, i2, l2)
         assert e.value.status == INDEX
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """vsa_fine_combine_noalloc refuses B * heads * Nc above 1,048,576 (its
+    static scratch) before any HIP call, and checks pointers like the others."""
+    lib = N.lib()
+    p = V.Problem(1, 1024, 32, 64, 64, 64, topk=0, list_stride=32)   # 1024 heads x 2048 cubes
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, None, None]
+    assert lib.vsa_fine_combine_noalloc(ctypes.byref(p.c()), *args) == WORKSPACE
+    small = _p(topk=0, list_stride=2)
+    bad = list(args)
+    bad[0] = None
+    assert lib.vsa_fine_combine_noalloc(ctypes.byref(small.c()), *bad) == NULL
+    bad = list(args)
+    bad[1] = MIS
+    assert lib.vsa_fine_combine_noalloc(ctypes.byref(small.c()), *bad) == ALIGN
