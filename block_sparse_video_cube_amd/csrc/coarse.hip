@@ -266,8 +266,79 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
     }
 }
 
+// The largest key x such that at least k of the wave's keys (one per lane,
+// `have` lanes taking part) are >= x: the k-th largest key, found bit by
+// bit from the top with ballots (no LDS traffic).
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t key, bool have, int k) {
+  uint32_t x = 0u;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = x | (1u << bit);
+    if (__popcll(__ballot(have && key >= c)) >= k) x = c;
+  }
+  return x;
+}
+
+// Top-K of a row for K <= 64 when few values can be in it (key[t] = the
+// order-preserving key of value t*64 + lane, 0 beyond Nk). The K-th largest
+// of the 64 lane maxima bounds the K-th largest value from below (K lanes
+// hold a value at least that large), so only values at or above it are
+// candidates. When there are at most 64 they are compacted one per lane in
+// ascending block order (cand: 64 slots of this wave's LDS), the K-th
+// largest candidate (the K-th largest value of the row) is found, and every
+// candidate above it plus the first ones equal to it (smaller ids win ties)
+// are written in that order, i.e. ascending. Returns false, having written
+// nothing, when there are more than 64 candidates.
+template <int NCH>
+__device__ __forceinline__ bool row_topk_few(const uint32_t (&key)[NCH], int Nk, int topk, int stride,
+                                             uint64_t* cand, int32_t* __restrict__ out,
+                                             int32_t* __restrict__ len_out) {
+  const int lane = threadIdx.x & 63;
+  const int nused = (Nk + 63) >> 6;
+  uint32_t lmax = 0u;
+#pragma unroll
+  for (int t = 0; t < NCH; ++t)
+    if (t < nused) lmax = max(lmax, key[t]);
+  const uint32_t thr = wave_kth_largest(lmax, true, topk);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int n = 0;
+#pragma unroll
+  for (int t = 0; t < NCH; ++t) {
+    if (t >= nused) break;
+    n += __popcll(__ballot(t * 64 + lane < Nk && key[t] >= thr));
+  }
+  if (n > 64) return false;
+  int pos = 0;
+#pragma unroll
+  for (int t = 0; t < NCH; ++t) {
+    if (t >= nused) break;
+    const int j = t * 64 + lane;
+    const bool c = j < Nk && key[t] >= thr;
+    const uint64_t b = __ballot(c);
+    if (c) cand[pos + __popcll(b & lt_mask)] = ((uint64_t)key[t] << 32) | (uint32_t)j;
+    pos += __popcll(b);
+  }
+  wave_sync();
+  const bool have = lane < n;
+  const uint64_t x = have ? cand[lane] : 0ull;
+  wave_sync();
+  const uint32_t ck = (uint32_t)(x >> 32);
+  const uint32_t kth = wave_kth_largest(ck, have, topk);
+  const int above = __popcll(__ballot(have && ck > kth));
+  const bool eq = have && ck == kth;
+  const int eq_rank = __popcll(__ballot(eq) & lt_mask);
+  const bool take = (have && ck > kth) || (eq && eq_rank < topk - above);
+  const int opos = __popcll(__ballot(take) & lt_mask);
+  if (take) out[opos] = (int32_t)(uint32_t)(x & 0xFFFFFFFFu);
+  for (int j = topk + lane; j < stride; j += 64) out[j] = -1;
+  if (lane == 0) *len_out = topk;
+  return true;
+}
+
 // One wave per row: LSE_c, and with topk > 0 the ascending top-K list.
-// Selection works on the order-preserving integer keys of the logits: a
+// With K <= 64 it first tries row_topk_few (ballots only); otherwise, or when
+// more than 64 values are candidates, selection works on the
+// order-preserving integer keys of the logits: a
 // radix select finds the key of the K-th largest logit, 8 bits per pass from
 // the most significant bit in which the row's keys differ (the bits above it
 // are shared by every key, and skipping them keeps the first histogram
@@ -281,7 +352,7 @@ template <int NCH>
 __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restrict__ s, float* __restrict__ lse,
                                                           int32_t* __restrict__ idx, int32_t* __restrict__ len,
                                                           long rows, int Nk, int ld, int topk, int stride) {
-  __shared__ int hist_all[4][256];
+  __shared__ __attribute__((aligned(16))) int hist_all[4][256];   // per wave: histogram or 64 candidates
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + w;
   if (row >= rows) return;   // wave-uniform; no block barrier below
@@ -315,6 +386,10 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
     key[t] = valid ? fkey(v[t]) : 0u;
     if (valid) kmin = min(kmin, key[t]);
   }
+  // Few candidates (the usual case for K <= 64): selected with ballots alone.
+  if (topk <= 64 && row_topk_few<NCH>(key, Nk, topk, stride, reinterpret_cast<uint64_t*>(h),
+                                      idx + row * (long)stride, len + row))
+    return;
   kmin = wave_min_u32(kmin);
   const uint32_t diff = kmin ^ fkey(mx);
   // Keys matching `prefix` on the bits of `pmask` are the candidates.

@@ -981,3 +981,47 @@ def test_random_configurations(seed):
 def test_random_configurations_fp32(seed):
     """The same for fp32 problems (fp32 kernels, 1e-4 absolute)."""
     _run_random(seed, "f32")
+
+
+def _cube_constant(per_cube, T, H, W):
+    """Token tensor [T, H, W, d] whose 64 tokens of cube c all equal per_cube[c]."""
+    t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    c = ((t // 4) * (H // 4) + y // 4) * (W // 4) + x // 4
+    return per_cube[c]
+
+
+@pytest.mark.parametrize("case,k", [("all_equal", 8), ("all_equal", 100), ("repeats", 32), ("repeats", 7),
+                                    ("repeats", 64), ("distinct", 100)])
+def test_topk_exact_ties_match_oracle_bit_for_bit(case, k):
+    """Top-K with exact ties. Every cube's tokens are equal, so pooling is
+    exact and the logits s * q_c . k_c are exact in fp32 (s = 1/8, multiples
+    of 1/64): the GPU's lists must equal the oracle's (stable descending
+    order, ties to the smaller cube id) on every row, whichever selection path
+    the row takes (few candidates, or the radix select when more than 64
+    values tie or K > 64)."""
+    T, H, W, d, heads = 16, 32, 32, 64, 2
+    nc = T * H * W // 64
+    rng = np.random.default_rng(17)
+    qc = np.zeros((heads, nc, d), np.float32)
+    kc = np.zeros((heads, nc, d), np.float32)
+    for h in range(heads):
+        qc[h, :, 0] = 1.0
+        if case == "all_equal":
+            kc[h, :, 0] = 0.5
+        elif case == "repeats":   # 50 distinct values, each 5 or 6 times
+            kc[h, :, 0] = (np.arange(nc) * (7 + h) % 50) / 8.0
+        else:
+            kc[h, :, 0] = rng.permutation(nc) / 8.0
+        qc[h, :, 1] = rng.integers(-4, 5, nc) / 4.0      # varies rows, leaves logits unchanged (k_c[:, 1] = 0)
+    q = np.stack([_cube_constant(qc[h], T, H, W) for h in range(heads)])[None]
+    kk = np.stack([_cube_constant(kc[h], T, H, W) for h in range(heads)])[None]
+    v = rng.standard_normal((1, heads, T, H, W, d)).astype(np.float32)
+    p = V.Problem(1, heads, T, H, W, d, topk=k)
+    dq, dk, dv = (dev(a, torch.bfloat16) for a in (q, kk, v))
+    qcg, kcg, vcg = V.pool(p, dq, dk, dv)
+    _, _, idx, lens = V.coarse(p, qcg, kcg, vcg)
+    torch.cuda.synchronize()
+    gi = host(idx)
+    assert (host(lens) == k).all()
+    ref = O.forward(q, kk, v, topk=k)
+    assert np.array_equal(gi, ref["idx"]), (case, k, np.argwhere((gi != ref["idx"]).any(-1))[:3].tolist())
