@@ -63,11 +63,7 @@ def cpu_baseline(workload: str, heads: list[int]) -> dict:
     import numpy as np
     import workloads as WL
     from oracle import vsa_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001 - threadpoolctl is optional
-        threads = 1
+    threads = _blas_threads()
     w = WL.get(workload)
     x = WL.make_inputs(workload, heads=heads)
     t0 = time.perf_counter()
@@ -78,6 +74,67 @@ def cpu_baseline(workload: str, heads: list[int]) -> dict:
             "sample": f"heads {heads} of {w.heads} (b=0) of the {workload} workload, full float64 forward "
                       f"(pool, coarse, top-{w.topk}, fine, combine): {dt:.1f} s",
             "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl is optional
+        return 1
+
+
+def cpu_full(workload: str, train_workload: str) -> dict:
+    """The oracle as it stands, at full size: the whole forward of every head
+    of `workload`, stage by stage (the oracle's own functions in the order of
+    its forward, one head at a time so that the float64 copies stay small),
+    and the forward + backward of every head of `train_workload`."""
+    import numpy as np
+    import workloads as WL
+    from oracle import vsa_oracle as O
+    w = WL.get(workload)
+    st = {"generate": 0.0, "tile_pool": 0.0, "coarse_topk": 0.0, "fine": 0.0, "combine_untile": 0.0}
+    pairs = 0
+    s = 1.0 / np.sqrt(w.head_dim)
+    for h in range(w.heads):
+        t0 = time.perf_counter()
+        x = WL.make_inputs(workload, heads=[h])
+        t1 = time.perf_counter()
+        qt, kt, vt = (O.tile(x[n].astype(np.float64)) for n in ("q", "k", "v"))
+        qc, kc, vc = O.pool(qt[0, 0]), O.pool(kt[0, 0]), O.pool(vt[0, 0])
+        t2 = time.perf_counter()
+        S, _, oc, _ = O.coarse_attention(qc, kc, vc, s)
+        idx, _ = O.topk_rows(S, w.topk)
+        t3 = time.perf_counter()
+        lens = np.full(w.Nc, w.topk)
+        of_t, _ = O.fine_gathered(qt[0, 0], kt[0, 0], vt[0, 0], idx, lens, s)
+        t4 = time.perf_counter()
+        of = O.untile(of_t[None, None], w.T, w.H, w.W)
+        O.combine(O.repeat_coarse(oc[None, None], w.T, w.H, w.W), of, x["g_c"].astype(np.float64),
+                  x["g_f"].astype(np.float64))
+        t5 = time.perf_counter()
+        pairs += int(lens.sum())
+        for k, a, b in (("generate", t0, t1), ("tile_pool", t1, t2), ("coarse_topk", t2, t3), ("fine", t3, t4),
+                        ("combine_untile", t4, t5)):
+            st[k] += b - a
+        log(f"  oracle head {h}: {t5 - t1:.1f} s")
+    fwd_s = sum(v for k, v in st.items() if k != "generate")
+    flop = 4.0 * 64 * 64 * w.head_dim * pairs
+    tw = WL.get(train_workload)
+    x = WL.make_inputs(train_workload)
+    t0 = time.perf_counter()
+    f = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=x["idx"], lens=x["len"])
+    t1 = time.perf_counter()
+    O.backward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], x["d_o"], f)
+    t2 = time.perf_counter()
+    tpairs = int(np.asarray(x["len"]).sum())
+    return {"kind": "oracle", "cores": _blas_threads(), "host_cpus": os.cpu_count(),
+            "forward": {"workload": workload, "heads": w.heads, "seconds": round(fwd_s, 2),
+                        "stage_seconds": {k: round(v, 2) for k, v in st.items()},
+                        "TFLOP_per_s": flop / fwd_s / 1e12, "tokens_per_s": w.B * w.N / fwd_s},
+            "train": {"workload": train_workload, "forward_seconds": round(t1 - t0, 2),
+                      "backward_seconds": round(t2 - t1, 2), "block_pairs": tpairs,
+                      "backward_TFLOP_per_s": 10.0 * 64 * 64 * tw.head_dim * tpairs / (t2 - t1) / 1e12}}
 
 
 def train_measure(name: str, steps: int, warmup: int) -> dict:
@@ -280,6 +337,9 @@ def main() -> int:
                          "(for counter collection); copy: a plain device copy of --copy-mib MiB, the "
                          "calibration of the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--copy-mib", type=int, default=2048)
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="only time the CPU oracle at full size (every head of the workload, by stage, and the "
+                         "training workload's forward + backward); prints one JSON line, uses no GPU")
     ap.add_argument("--train", default="train_bf16_16x32x32_varlen,bf16_720p_24x44x80",
                     help="comma-separated workloads whose forward + backward are timed ('' = none)")
     ap.add_argument("--no-variants", action="store_true",
@@ -292,6 +352,10 @@ def main() -> int:
               "(heads are independent; the multi-GPU sharding is a design note, not run). Use --gpus 1.",
               file=sys.stderr)
         return 2
+
+    if args.cpu_full:
+        print(json.dumps({"mode": "cpu_full", **cpu_full(args.workload, "train_bf16_16x32x32_varlen")}), flush=True)
+        return 0
 
     import numpy as np
     import torch
