@@ -25,7 +25,8 @@
 
 namespace vsa {
 
-constexpr int kCoarseMaxCubes = 2048;   // 32 logits per lane in coarse_rows
+constexpr int kCoarseMaxCubes = 8192;   // rows of up to 2048 logits in registers, longer ones streamed
+constexpr int kRowsInRegisters = 2048;
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -464,6 +465,136 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
   if (lane == 0) len[row] = topk;
 }
 
+// The rows kernel for rows longer than kRowsInRegisters: the same LSE_c and
+// selection (candidates with ballots for K <= 64 when at most 64 values can
+// be chosen, else the radix select), with the row read again from memory (L2)
+// in every pass instead of held in registers.
+__global__ __launch_bounds__(256) void coarse_rows_stream_kernel(const float* __restrict__ s, float* __restrict__ lse,
+                                                                 int32_t* __restrict__ idx, int32_t* __restrict__ len,
+                                                                 long rows, int Nk, int ld, int topk, int stride) {
+  __shared__ __attribute__((aligned(16))) int hist_all[4][256];   // per wave: histogram or 64 candidates
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + w;
+  if (row >= rows) return;   // wave-uniform; no block barrier below
+  const float* srow = s + row * ld;
+  const int nused = (Nk + 63) >> 6;
+  auto key_at = [&](int t) { const int j = t * 64 + lane; return j < Nk ? fkey(srow[j]) : 0u; };
+  float mx = -INFINITY;
+  for (int j = lane; j < Nk; j += 64) mx = fmaxf(mx, srow[j]);
+  mx = wave_max(mx);
+  float sm = 0.f;
+  for (int j = lane; j < Nk; j += 64) sm += __expf(srow[j] - mx);
+  sm = wave_sum(sm);
+  if (lane == 0) lse[row] = mx + __logf(sm);
+  if (topk <= 0) return;
+  int* h = hist_all[w];
+  int32_t* out = idx + row * (long)stride;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (topk <= 64) {   // candidates (see row_topk_few)
+    uint32_t lmax = 0u;
+    for (int t = 0; t < nused; ++t) lmax = max(lmax, key_at(t));
+    const uint32_t thr = wave_kth_largest(lmax, true, topk);
+    int n = 0;
+    for (int t = 0; t < nused; ++t) n += __popcll(__ballot(t * 64 + lane < Nk && key_at(t) >= thr));
+    if (n <= 64) {
+      uint64_t* cand = reinterpret_cast<uint64_t*>(h);
+      int pos = 0;
+      for (int t = 0; t < nused; ++t) {
+        const int j = t * 64 + lane;
+        const uint32_t kj = key_at(t);
+        const bool c = j < Nk && kj >= thr;
+        const uint64_t b = __ballot(c);
+        if (c) cand[pos + __popcll(b & lt_mask)] = ((uint64_t)kj << 32) | (uint32_t)j;
+        pos += __popcll(b);
+      }
+      wave_sync();
+      const bool have = lane < n;
+      const uint64_t x = have ? cand[lane] : 0ull;
+      wave_sync();
+      const uint32_t ck = (uint32_t)(x >> 32);
+      const uint32_t kth = wave_kth_largest(ck, have, topk);
+      const int above = __popcll(__ballot(have && ck > kth));
+      const bool eq = have && ck == kth;
+      const int eq_rank = __popcll(__ballot(eq) & lt_mask);
+      const bool take = (have && ck > kth) || (eq && eq_rank < topk - above);
+      const int opos = __popcll(__ballot(take) & lt_mask);
+      if (take) out[opos] = (int32_t)(uint32_t)(x & 0xFFFFFFFFu);
+      for (int j = topk + lane; j < stride; j += 64) out[j] = -1;
+      if (lane == 0) len[row] = topk;
+      return;
+    }
+  }
+  // Radix select (see row_topk), keys recomputed in every pass.
+  uint32_t kmin = 0xFFFFFFFFu;
+  for (int t = 0; t < nused; ++t)
+    if (t * 64 + lane < Nk) kmin = min(kmin, key_at(t));
+  kmin = wave_min_u32(kmin);
+  const uint32_t diff = kmin ^ fkey(mx);
+  uint32_t prefix = kmin, pmask = 0xFFFFFFFFu;
+  int krem = topk;
+  int hi = diff == 0u ? -1 : 31 - __clz(diff);
+  if (hi >= 0) {
+    pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+    prefix = kmin & pmask;
+  }
+  while (hi >= 0) {
+    const int nb = min(8, hi + 1), shift = hi - nb + 1;
+    const uint32_t dmask = (1u << nb) - 1u;
+    for (int b = lane; b < 256; b += 64) h[b] = 0;
+    wave_sync();
+    for (int t = 0; t < nused; ++t) {
+      const uint32_t k = key_at(t);
+      if ((t * 64 + lane) < Nk && (k & pmask) == prefix) atomicAdd(&h[(k >> shift) & dmask], 1);
+    }
+    wave_sync();
+    const int b0 = h[4 * lane], b1 = h[4 * lane + 1], b2 = h[4 * lane + 2], b3 = h[4 * lane + 3];
+    const int mine = b0 + b1 + b2 + b3;
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_down(incl, o, 64);
+      if (lane + o < 64) incl += t;
+    }
+    int acc = incl - mine;
+    int found = -1, before = 0, fcount = 0;
+    const int cnt[4] = {b3, b2, b1, b0};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (found < 0 && acc < krem && acc + cnt[q] >= krem) { found = 4 * lane + 3 - q; before = acc; fcount = cnt[q]; }
+      acc += cnt[q];
+    }
+    const uint64_t bal = __ballot(found >= 0);
+    const int src = __ffsll((unsigned long long)bal) - 1;
+    const int fb = __shfl(found, src, 64);
+    const int fbefore = __shfl(before, src, 64);
+    const int fcnt = __shfl(fcount, src, 64);
+    prefix |= (uint32_t)fb << shift;
+    pmask |= dmask << shift;
+    krem -= fbefore;
+    hi -= nb;
+    wave_sync();
+    if (fcnt == krem) break;
+  }
+  int taken = 0, eq_seen = 0;
+  for (int t = 0; t < nused; ++t) {
+    const int j = t * 64 + lane;
+    const uint32_t k = key_at(t);
+    const bool valid = j < Nk;
+    const bool gt = valid && (k & pmask) > prefix;
+    const bool eq = valid && (k & pmask) == prefix;
+    const uint64_t beq = __ballot(eq);
+    const int eqr = eq_seen + __popcll(beq & lt_mask);
+    const bool take = gt || (eq && eqr < krem);
+    const uint64_t bt = __ballot(take);
+    const int pos = taken + __popcll(bt & lt_mask);
+    if (take && pos < topk) out[pos] = j;
+    taken += __popcll(bt);
+    eq_seen += __popcll(beq);
+  }
+  for (int j = topk + lane; j < stride; j += 64) out[j] = -1;
+  if (lane == 0) len[row] = topk;
+}
+
 int coarse_max_cubes() { return kCoarseMaxCubes; }
 
 // C = scale * op(M) B with R output rows and Kd contracted; M is the
@@ -503,7 +634,12 @@ hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, cons
   if (Nk <= 256) launch_rows<4>(L, s_scratch, lse, idx, len);
   else if (Nk <= 512) launch_rows<8>(L, s_scratch, lse, idx, len);
   else if (Nk <= 1024) launch_rows<16>(L, s_scratch, lse, idx, len);
-  else launch_rows<32>(L, s_scratch, lse, idx, len);
+  else if (Nk <= kRowsInRegisters) launch_rows<32>(L, s_scratch, lse, idx, len);
+  else {
+    const long rows = (long)L.BH * L.g.Nc;
+    hipLaunchKernelGGL(coarse_rows_stream_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream, s_scratch,
+                       lse, idx, len, rows, Nk, ld, L.topk, L.stride);
+  }
   launch_gemm<false, true>(L, s_scratch, lse, vc, oc, Nq, Nk, 1.0f);
   return hipGetLastError();
 }

@@ -46,7 +46,7 @@ namespace vsa {
 __global__ __launch_bounds__(1024) void order_by_count_kernel(const int32_t* __restrict__ k2q_off,
                                                               int32_t* __restrict__ order, int Nc, int Nq,
                                                               int pow2) {
-  __shared__ unsigned long long key[2048];
+  __shared__ unsigned long long key[kMaxSortKeys];
   const long bh = blockIdx.x;
   const int32_t* off = k2q_off + bh * (Nc + 1);
   for (int e = threadIdx.x; e < pow2; e += 1024) {
@@ -724,7 +724,7 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
 hipError_t launch_order_by_count(const Launch& L, const int32_t* k2q_off, int32_t* order) {
   int pow2 = 1;
   while (pow2 < L.gk.Nc) pow2 <<= 1;
-  if (pow2 > 2048) return hipErrorInvalidValue;
+  if (pow2 > kMaxSortKeys) return hipErrorInvalidValue;
   hipLaunchKernelGGL(order_by_count_kernel, dim3(L.BH), dim3(1024), 0, L.stream, k2q_off, order, L.gk.Nc, L.g.Nc,
                      pow2);
   return hipGetLastError();

@@ -56,7 +56,7 @@ template <int D> struct FineCfg {
 __global__ __launch_bounds__(1024) void order_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ len,
                                                      int32_t* __restrict__ order, int Nc, int Nk, int stride,
                                                      int pow2) {
-  __shared__ unsigned long long key[2048];
+  __shared__ unsigned long long key[kMaxSortKeys];
   const long bh = blockIdx.x;
   for (int e = threadIdx.x; e < pow2; e += 1024) {
     unsigned long long kv = ~0ull;
@@ -556,7 +556,7 @@ static void fine_launch_f32(const Launch& L, const void* q, const void* k, const
 hipError_t launch_order(const Launch& L, const int32_t* idx, const int32_t* len, int32_t* order) {
   int pow2 = 1;
   while (pow2 < L.g.Nc) pow2 <<= 1;
-  if (pow2 > 2048) return hipErrorInvalidValue;
+  if (pow2 > kMaxSortKeys) return hipErrorInvalidValue;
   hipLaunchKernelGGL(order_kernel, dim3(L.BH), dim3(1024), 0, L.stream, idx, len, order, L.g.Nc, L.gk.Nc, L.stride,
                      pow2);
   return hipGetLastError();

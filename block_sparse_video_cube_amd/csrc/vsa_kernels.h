@@ -32,6 +32,9 @@ hipError_t launch_relayout(const Launch& L, const void* src, void* dst, bool to_
 hipError_t launch_crop_pad(const Launch& L, const void* src, void* dst, int ts, int hs, int ws, bool to_small);
 
 int coarse_max_cubes();
+// Keys of the bitonic order sorts (one workgroup per (b, h), keys in LDS):
+// the largest cube or key-block count per (b, h).
+constexpr int kMaxSortKeys = 8192;
 // Row pitch (floats) of the coarse logits: Nk rounded up to a multiple of 4.
 int coarse_ld(int Nk);
 // s_scratch: B*heads*Nq*coarse_ld(Nk) fp32 (the coarse logits).

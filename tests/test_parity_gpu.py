@@ -298,14 +298,20 @@ def test_forward_720p_heads():
     assert near <= NEAR_FRAC * len(heads) * w.Nc + 2
 
 
-def test_forward_max_cubes_sampled():
-    """The largest coarse problem the library accepts: Nc = vsa_max_cubes()
-    cubes per head (32x64x64 latent, 2048 cubes, 32 logits per lane in the
-    row kernel). Selection checked for every query cube, outputs for 32
-    sampled query cubes."""
-    T, H, W, d, k = 32, 64, 64, 64, 32
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T,H,W", [(32, 64, 64), (32, 128, 128)])
+def test_forward_max_cubes_sampled(T, H, W):
+    """The largest rows the coarse kernel holds in registers (32x64x64
+    latent, 2048 cubes, 32 logits per lane) and the largest coarse problem
+    the library accepts (32x128x128, Nc = vsa_max_cubes() = 8192 cubes, 524288
+    tokens, rows streamed). Selection checked for every query cube, outputs
+    for 32 sampled query cubes."""
+    d, k = 64, 32
     nc = T * H * W // 64
-    assert nc == V.max_cubes()
+    assert nc <= V.max_cubes()
+    if T * H == 32 * 128:
+        assert nc == V.max_cubes()
+    print(f"[max cubes] {T}x{H}x{W}: {nc} cubes", flush=True)
     x = WL.make_inputs_custom(1, 1, d, T, H, W, dtype="bf16", seed=41)
     p = V.Problem(1, 1, T, H, W, d, topk=k)
     dd = inputs_to_dev(x, "bf16")
@@ -990,16 +996,20 @@ def _cube_constant(per_cube, T, H, W):
     return per_cube[c]
 
 
-@pytest.mark.parametrize("case,k", [("all_equal", 8), ("all_equal", 100), ("repeats", 32), ("repeats", 7),
-                                    ("repeats", 64), ("distinct", 100)])
-def test_topk_exact_ties_match_oracle_bit_for_bit(case, k):
+@pytest.mark.parametrize("case,k,latent", [("all_equal", 8, (16, 32, 32)), ("all_equal", 100, (16, 32, 32)),
+                                           ("repeats", 32, (16, 32, 32)), ("repeats", 7, (16, 32, 32)),
+                                           ("repeats", 64, (16, 32, 32)), ("distinct", 100, (16, 32, 32)),
+                                           ("all_equal", 8, (32, 64, 128)), ("repeats", 32, (32, 64, 128)),
+                                           ("distinct", 100, (32, 64, 128))])
+def test_topk_exact_ties_match_oracle_bit_for_bit(case, k, latent):
     """Top-K with exact ties. Every cube's tokens are equal, so pooling is
     exact and the logits s * q_c . k_c are exact in fp32 (s = 1/8, multiples
     of 1/64): the GPU's lists must equal the oracle's (stable descending
     order, ties to the smaller cube id) on every row, whichever selection path
     the row takes (few candidates, or the radix select when more than 64
-    values tie or K > 64)."""
-    T, H, W, d, heads = 16, 32, 32, 64, 2
+    values tie or K > 64), and for rows in registers (256 cubes) as well as
+    streamed rows (4096 cubes)."""
+    (T, H, W), d, heads = latent, 64, 2
     nc = T * H * W // 64
     rng = np.random.default_rng(17)
     qc = np.zeros((heads, nc, d), np.float32)
@@ -1008,10 +1018,10 @@ def test_topk_exact_ties_match_oracle_bit_for_bit(case, k):
         qc[h, :, 0] = 1.0
         if case == "all_equal":
             kc[h, :, 0] = 0.5
-        elif case == "repeats":   # 50 distinct values, each 5 or 6 times
+        elif case == "repeats":   # 50 distinct values, each repeated
             kc[h, :, 0] = (np.arange(nc) * (7 + h) % 50) / 8.0
-        else:
-            kc[h, :, 0] = rng.permutation(nc) / 8.0
+        else:                     # distinct where bf16 allows (values up to 255/8 are exact)
+            kc[h, :, 0] = rng.permutation(nc) % 256 / 8.0
         qc[h, :, 1] = rng.integers(-4, 5, nc) / 4.0      # varies rows, leaves logits unchanged (k_c[:, 1] = 0)
     q = np.stack([_cube_constant(qc[h], T, H, W) for h in range(heads)])[None]
     kk = np.stack([_cube_constant(kc[h], T, H, W) for h in range(heads)])[None]
@@ -1023,5 +1033,8 @@ def test_topk_exact_ties_match_oracle_bit_for_bit(case, k):
     torch.cuda.synchronize()
     gi = host(idx)
     assert (host(lens) == k).all()
-    ref = O.forward(q, kk, v, topk=k)
-    assert np.array_equal(gi, ref["idx"]), (case, k, np.argwhere((gi != ref["idx"]).any(-1))[:3].tolist())
+    ridx = np.stack([O.topk_rows(O.coarse_attention(O.pool(O.tile(q[0, h].astype(np.float64))),
+                                                    O.pool(O.tile(kk[0, h].astype(np.float64))),
+                                                    O.pool(O.tile(v[0, h].astype(np.float64))), 1 / 8.0)[0], k)[0]
+                     for h in range(heads)])[None]
+    assert np.array_equal(gi, ridx), (case, k, np.argwhere((gi != ridx).any(-1))[:3].tolist())
