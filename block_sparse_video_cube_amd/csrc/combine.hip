@@ -123,6 +123,7 @@ static void combine_bwd_launch(const Launch& L, const void* d_o, const float* oc
                      (const T*)gc, (const T*)gf, (T*)dgc, (T*)dgf, (T*)dof, delta, doc, L.g)
   if (L.g.B == 32) VSA_COMBINE_BWD(32);
   else if (L.g.B == 128) VSA_COMBINE_BWD(128);
+  else if (L.g.B == 256) VSA_COMBINE_BWD(256);
   else VSA_COMBINE_BWD(64);
 #undef VSA_COMBINE_BWD
 }

@@ -47,6 +47,70 @@ hipError_t launch_relayout(const Launch& L, const void* src, void* dst, bool to_
   return hipGetLastError();
 }
 
+// ---- 256-token tiles as two 128-token halves (see half_grid) ------------
+// Lists of the query halves: half s of query cube c gets c's list, every
+// listed key block replaced by its two halves when key blocks are split (the
+// lists of the halves are not ascending; no fine kernel needs them to be).
+__global__ __launch_bounds__(256) void split_lists_kernel(const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ len, int32_t* __restrict__ idx2,
+                                                          int32_t* __restrict__ len2, Grid gq, Grid gq2, Grid gk,
+                                                          Grid gk2, int qsplit, int ksplit, int stride, int stride2) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  const long bh = blockIdx.y;
+  if (s >= gq2.Nc) return;
+  int c = s, hh = 0;
+  if (qsplit) half_parent(gq, gq2, s, c, hh);
+  const long row = bh * gq.Nc + c, row2 = bh * gq2.Nc + s;
+  const int L = min(max(len[row], 0), stride);
+  for (int t = 0; t < L; ++t) {
+    int j = idx[row * stride + t];
+    j = (j >= 0 && j < gk.Nc) ? j : 0;   // malformed entries stay in range
+    if (ksplit) {
+      idx2[row2 * stride2 + 2 * t] = half_index(gk, gk2, j, 0);
+      idx2[row2 * stride2 + 2 * t + 1] = half_index(gk, gk2, j, 1);
+    } else {
+      idx2[row2 * stride2 + t] = j;
+    }
+  }
+  len2[row2] = ksplit ? 2 * L : L;
+}
+
+// Per-half copies of per-cube fp32 rows of D values (O_c for the fused
+// combine, pooled gradients) scaled by mul, and of max-pool argmax positions
+// (the position within the half, or 255 = none when the maximum lies in the
+// other half). One workgroup per (b, h, half).
+__global__ __launch_bounds__(128) void split_rows_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                         const uint8_t* __restrict__ asrc, uint8_t* __restrict__ adst,
+                                                         Grid g, Grid g2, int D, float mul) {
+  const int s = blockIdx.x;
+  const long bh = blockIdx.y;
+  int c, hh;
+  half_parent(g, g2, s, c, hh);
+  const long from = (bh * g.Nc + c) * D, to = (bh * g2.Nc + s) * D;
+  for (int ch = threadIdx.x; ch < D; ch += 128) {
+    if (src != nullptr) dst[to + ch] = src[from + ch] * mul;
+    if (asrc != nullptr) {
+      const int a = asrc[from + ch] - 128 * hh;
+      adst[to + ch] = (a >= 0 && a < 128) ? (uint8_t)a : (uint8_t)255;
+    }
+  }
+}
+
+hipError_t launch_split_lists(const Launch& L, const Launch& S, const int32_t* idx, const int32_t* len, int32_t* idx2,
+                              int32_t* len2) {
+  const dim3 grid((S.g.Nc + 255) / 256, L.BH);
+  hipLaunchKernelGGL(split_lists_kernel, grid, dim3(256), 0, L.stream, idx, len, idx2, len2, L.g, S.g, L.gk, S.gk,
+                     (int)(L.g.B != S.g.B), (int)(L.gk.B != S.gk.B), L.stride, S.stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_rows(const Launch& L, const Grid& g, const Grid& g2, const float* src, float* dst,
+                             const uint8_t* asrc, uint8_t* adst, float mul) {
+  hipLaunchKernelGGL(split_rows_kernel, dim3(g2.Nc, L.BH), dim3(128), 0, L.stream, src, dst, asrc, adst, g, g2, L.D,
+                     mul);
+  return hipGetLastError();
+}
+
 // Index, in the problem's token order, of raster token (t, y, x).
 __device__ __forceinline__ long token_index(const Grid& g, int t, int y, int x) {
   if (!g.tiled) return ((long)t * g.H + y) * g.W + x;

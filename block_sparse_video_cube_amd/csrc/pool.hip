@@ -117,6 +117,7 @@ static void pool_grid(const Launch& L, const Grid& g, const void* q, const void*
   if (g.B == 16) pool_launch_bt<T, MAX, 16, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
   else if (g.B == 32) pool_launch_bt<T, MAX, 32, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
   else if (g.B == 128) pool_launch_bt<T, MAX, 128, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
+  else if (g.B == 256) pool_launch_bt<T, MAX, 256, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
   else pool_launch_bt<T, MAX, 64, SEL>(L, g, q, k, v, qc, kc, vc, qa, ka, va);
 }
 

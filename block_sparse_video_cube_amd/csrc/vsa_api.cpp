@@ -18,6 +18,9 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 struct Dims {
   long BH, N, Nq, Nk, Bk, D, stride;   // Nq query cubes, Nk key blocks of Bk tokens per (b, h)
   size_t elem;  // bytes per raster element
+  // The fine kernels' view (256-token cubes / key blocks as 128-token halves):
+  bool qsplit, ksplit;
+  long Nq2, Nk2, stride2;
 };
 
 // A cube side: a power of two in [1, 128].
@@ -36,8 +39,8 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
   if (p->T < ct || p->H < ch || p->W < cw || p->T % ct || p->H % ch || p->W % cw) return VSA_ERR_SHAPE;
   if (p->T % kt || p->H % kh || p->W % kw) return VSA_ERR_SHAPE;
   const long Bt = (long)ct * ch * cw, Bk = (long)kt * kh * kw;
-  if (Bt != 32 && Bt != 64 && Bt != 128) return VSA_ERR_UNSUPPORTED;
-  if (Bk != 16 && Bk != 32 && Bk != 64 && Bk != 128) return VSA_ERR_UNSUPPORTED;
+  if (Bt != 32 && Bt != 64 && Bt != 128 && Bt != 256) return VSA_ERR_UNSUPPORTED;
+  if (Bk != 16 && Bk != 32 && Bk != 64 && Bk != 128 && Bk != 256) return VSA_ERR_UNSUPPORTED;
   const bool same = kt == ct && kh == ch && kw == cw;
   const long N = (long)p->T * p->H * p->W;
   const long BH = (long)p->B * p->heads;
@@ -71,8 +74,26 @@ vsa_status check_problem(const vsa_problem* p, Launch* L, Dims* d) {
   if (d != nullptr) {
     d->BH = BH; d->N = N; d->Nq = Nc; d->Nk = Nk; d->Bk = Bk; d->D = p->head_dim; d->stride = stride;
     d->elem = p->dtype == VSA_BF16 ? 2 : 4;
+    d->qsplit = Bt == 256;
+    d->ksplit = Bk == 256;
+    d->Nq2 = d->qsplit ? 2 * Nc : Nc;
+    d->Nk2 = d->ksplit ? 2 * Nk : Nk;
+    d->stride2 = d->ksplit ? 2 * stride : stride;
   }
   return VSA_OK;
+}
+
+// The launch context of the fine kernels: 256-token query cubes and key
+// blocks become their 128-token halves (half_grid), lists double with split
+// key blocks.
+Launch fine_view(const Launch& L) {
+  Launch S = L;
+  if (L.g.B == 256) S.g = half_grid(L.g);
+  if (L.gk.B == 256) {
+    S.gk = half_grid(L.gk);
+    S.stride = 2 * L.stride;
+  }
+  return S;
 }
 
 inline bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
@@ -127,12 +148,18 @@ Saved carve_saved(const Dims& d, void* base) {
 struct FwdWs {
   int32_t* order;
   float *s, *qc, *kc, *vc, *oc, *lse_c;
+  int32_t *idx2, *len2;   // lists of the query halves (256-token tiles only)
+  float* oc2;             // O_c per query half (256-token query cubes only)
   size_t bytes;
 };
 FwdWs carve_fwd_ws(const Dims& d, void* base) {
   Carver c(base);
   FwdWs w;
-  w.order = c.take<int32_t>(d.BH * d.Nq);
+  w.order = c.take<int32_t>(d.BH * d.Nq2);
+  const bool split = d.qsplit || d.ksplit;
+  w.idx2 = split ? c.take<int32_t>(d.BH * d.Nq2 * d.stride2) : nullptr;
+  w.len2 = split ? c.take<int32_t>(d.BH * d.Nq2) : nullptr;
+  w.oc2 = d.qsplit ? c.take<float>(d.BH * d.Nq2 * d.D) : nullptr;
   w.s = c.take<float>(d.BH * d.Nq * (size_t)coarse_ld((int)d.Nk));
   const size_t pq = d.BH * d.Nq * d.D, pk = d.BH * d.Nk * d.D;
   w.qc = c.take<float>(pq);
@@ -152,6 +179,11 @@ struct BwdWs {
   int32_t* pairs;   // 16-token key blocks: union lists of block pairs and their lengths
   uint32_t* k2q_bits;
   uint8_t* args;   // max pooling: argmax positions of q, k, v
+  // 256-token tiles: lists of the query halves, pooled gradients and argmax
+  // positions per half (null where a side is not split)
+  int32_t *idx2, *len2;
+  float *dqc2, *dkc2, *dvc2;
+  uint8_t* args2;
   size_t bytes;
 };
 BwdWs carve_bwd_ws(const Dims& d, void* base) {
@@ -169,18 +201,117 @@ BwdWs carve_bwd_ws(const Dims& d, void* base) {
   w.p_scr = c.take<float>(d.BH * d.Nq * ldc);
   w.ds_scr = c.take<float>(d.BH * d.Nq * ldc);
   w.dc_scr = c.take<float>(d.BH * d.Nq);
-  w.k2q_off = c.take<int32_t>(d.BH * (d.Nk + 1));
-  w.k2q = c.take<int32_t>(d.BH * d.Nq * d.stride);
-  w.k2q_bits = c.take<uint32_t>(d.BH * d.Nk * (size_t)k2q_bits_words((int)d.Nq));
-  w.qorder = c.take<int32_t>(d.BH * d.Nq);
-  w.korder = c.take<int32_t>(d.BH * d.Nk);
+  // Transposed lists, orders and pairs are sized for the fine kernels' view
+  // (at least the cubes' own sizes, which vsa_index_transpose uses).
+  w.k2q_off = c.take<int32_t>(d.BH * (d.Nk2 + 1));
+  w.k2q = c.take<int32_t>(d.BH * d.Nq2 * d.stride2);
+  w.k2q_bits = c.take<uint32_t>(d.BH * d.Nk2 * (size_t)k2q_bits_words((int)d.Nq2));
+  w.qorder = c.take<int32_t>(d.BH * d.Nq2);
+  w.korder = c.take<int32_t>(d.BH * d.Nk2);
   w.args = c.take<uint8_t>(d.BH * (d.Nq + 2 * d.Nk) * d.D);
-  w.pairs = d.Bk == 16 ? c.take<int32_t>(d.BH * d.Nq * d.stride + d.BH * ((d.Nk + 1) / 2)) : nullptr;
+  w.pairs = d.Bk == 16 ? c.take<int32_t>(d.BH * d.Nq2 * d.stride2 + d.BH * ((d.Nk + 1) / 2)) : nullptr;
+  const bool split = d.qsplit || d.ksplit;
+  w.idx2 = split ? c.take<int32_t>(d.BH * d.Nq2 * d.stride2) : nullptr;
+  w.len2 = split ? c.take<int32_t>(d.BH * d.Nq2) : nullptr;
+  w.dqc2 = d.qsplit ? c.take<float>(d.BH * d.Nq2 * d.D) : nullptr;
+  w.dkc2 = d.ksplit ? c.take<float>(d.BH * d.Nk2 * d.D) : nullptr;
+  w.dvc2 = d.ksplit ? c.take<float>(d.BH * d.Nk2 * d.D) : nullptr;
+  w.args2 = split ? c.take<uint8_t>(d.BH * (d.Nq2 + 2 * d.Nk2) * d.D) : nullptr;
   w.bytes = c.off;
   return w;
 }
 
 inline vsa_status hip_status(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
+
+// The fine forward (with the fused combine when oc is not null) on the
+// cubes' lists. With 256-token tiles the kernels run on the 128-token halves:
+// the lists (and O_c) are expanded first.
+hipError_t run_fine_forward(const Launch& L, const Dims& d, const FwdWs& ws, const void* q, const void* k,
+                            const void* v, const int32_t* idx, const int32_t* len, void* of, float* lse_f,
+                            const float* oc, const void* g_c, const void* g_f, void* o) {
+  const Launch S = fine_view(L);
+  const int32_t *fi = idx, *fl = len;
+  const float* foc = oc;
+  hipError_t e = hipSuccess;
+  if (d.qsplit || d.ksplit) {
+    e = launch_split_lists(L, S, idx, len, ws.idx2, ws.len2);
+    fi = ws.idx2;
+    fl = ws.len2;
+    if (e == hipSuccess && d.qsplit && oc != nullptr) {
+      e = launch_split_rows(L, L.g, S.g, oc, ws.oc2, nullptr, nullptr, 1.0f);
+      foc = ws.oc2;
+    }
+  }
+  int32_t* order = L.bf16 ? ws.order : nullptr;
+  if (e == hipSuccess && order != nullptr) e = launch_order(S, fi, fl, order);
+  if (e == hipSuccess) e = launch_fine_fwd(S, q, k, v, fi, fl, order, of, lse_f, foc, g_c, g_f, o);
+  return e;
+}
+
+// The fine backward with the pool backward. k2q_off / k2q: the transposed
+// lists when the caller has them for the kernels' view (null: built here into
+// the workspace). With 256-token tiles the kernels run on the 128-token
+// halves: lists, pooled gradients (mean pooling: halved, since a half's
+// kernel divides by its 128 tokens) and max-pool argmax positions are
+// expanded first, and the transposed lists are always built here.
+hipError_t run_fine_backward(const Launch& L, const Dims& d, const BwdWs& ws, const void* q, const void* k,
+                             const void* v, const int32_t* idx, const int32_t* len, const int32_t* k2q_off,
+                             const int32_t* k2q, const float* lse_f, const void* dof, const float* delta,
+                             const float* dqc, const float* dkc, const float* dvc, void* dq, void* dk, void* dv) {
+  const Launch S = fine_view(L);
+  const bool split = d.qsplit || d.ksplit;
+  const int32_t *fi = idx, *fl = len;
+  const float *fq = dqc, *fk = dkc, *fv = dvc;
+  const float mul = L.pool_max ? 1.0f : 0.5f;
+  hipError_t e = hipSuccess;
+  if (split) {
+    e = launch_split_lists(L, S, idx, len, ws.idx2, ws.len2);
+    fi = ws.idx2;
+    fl = ws.len2;
+    if (e == hipSuccess && d.qsplit) {
+      e = launch_split_rows(L, L.g, S.g, dqc, ws.dqc2, nullptr, nullptr, mul);
+      fq = ws.dqc2;
+    }
+    if (e == hipSuccess && d.ksplit) e = launch_split_rows(L, L.gk, S.gk, dkc, ws.dkc2, nullptr, nullptr, mul);
+    if (e == hipSuccess && d.ksplit) e = launch_split_rows(L, L.gk, S.gk, dvc, ws.dvc2, nullptr, nullptr, mul);
+    if (d.ksplit) {
+      fk = ws.dkc2;
+      fv = ws.dvc2;
+    }
+  }
+  if (split || k2q_off == nullptr) {
+    if (e == hipSuccess) e = launch_index_transpose(S, fi, fl, ws.k2q_off, ws.k2q, ws.k2q_bits);
+    k2q_off = ws.k2q_off;
+    k2q = ws.k2q;
+  }
+  if (e == hipSuccess && L.bf16) e = launch_order(S, fi, fl, ws.qorder);
+  if (e == hipSuccess && L.bf16) e = launch_order_by_count(S, k2q_off, ws.korder);
+  const uint8_t* args = nullptr;
+  if (e == hipSuccess && L.pool_max) {
+    e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, ws.args);
+    args = ws.args;
+    if (e == hipSuccess && split) {
+      // planes q (query cubes), k and v (key blocks) of the halves' view
+      const size_t D = (size_t)L.D, pq = (size_t)d.BH * d.Nq * D, pk = (size_t)d.BH * d.Nk * D;
+      const size_t pq2 = (size_t)d.BH * d.Nq2 * D, pk2 = (size_t)d.BH * d.Nk2 * D;
+      const uint8_t* a = ws.args;
+      uint8_t* a2 = ws.args2;
+      e = d.qsplit ? launch_split_rows(L, L.g, S.g, nullptr, nullptr, a, a2, 1.0f)
+                   : hipMemcpyAsync(a2, a, pq, hipMemcpyDeviceToDevice, L.stream);
+      for (int w = 0; w < 2 && e == hipSuccess; ++w) {
+        const uint8_t* src = a + pq + w * pk;
+        uint8_t* dst = a2 + pq2 + w * pk2;
+        e = d.ksplit ? launch_split_rows(L, L.gk, S.gk, nullptr, nullptr, src, dst, 1.0f)
+                     : hipMemcpyAsync(dst, src, pk, hipMemcpyDeviceToDevice, L.stream);
+      }
+      args = ws.args2;
+    }
+  }
+  if (e == hipSuccess)
+    e = launch_fine_bwd(S, q, k, v, fi, fl, ws.qorder, k2q_off, k2q, ws.korder, lse_f, dof, delta, fq, fk, fv, dq,
+                        dk, dv, args, ws.pairs);
+  return e;
+}
 
 // ---- static scratch of vsa_fine_combine_noalloc ---------------------------
 // The query-cube processing order (one int32 per query cube of every
@@ -278,9 +409,7 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
   hipError_t e = launch_pool(L, q, k, v, qc, kc, vc);
   if (e == hipSuccess)
     e = launch_coarse(L, qc, kc, vc, oc, lse_c, L.topk > 0 ? idx : nullptr, L.topk > 0 ? len : nullptr, ws.s);
-  if (e == hipSuccess && L.bf16) e = launch_order(L, idx, len, ws.order);
-  if (e == hipSuccess)
-    e = launch_fine_fwd(L, q, k, v, idx, len, L.bf16 ? ws.order : nullptr, of, lse_f, oc, g_c, g_f, o);
+  if (e == hipSuccess) e = run_fine_forward(L, d, ws, q, k, v, idx, len, of, lse_f, oc, g_c, g_f, o);
   return hip_status(e);
 }
 
@@ -302,15 +431,11 @@ vsa_status vsa_backward(const vsa_problem* p, const void* q, const void* k, cons
   L.stream = static_cast<hipStream_t>(stream);
   hipError_t e = launch_combine_bwd(L, d_o, s.oc, s.of, g_c, g_f, g_c ? dg_c : nullptr, g_f ? dg_f : nullptr,
                                     ws.dof, ws.delta, ws.doc);
-  if (e == hipSuccess) e = launch_index_transpose(L, idx, len, ws.k2q_off, ws.k2q, ws.k2q_bits);
   if (e == hipSuccess)
     e = launch_coarse_bwd(L, s.qc, s.kc, s.vc, s.oc, s.lse_c, ws.doc, ws.dqc, ws.dkc, ws.dvc, ws.ds_scr, ws.p_scr, ws.dc_scr);
-  if (e == hipSuccess && L.bf16) e = launch_order(L, idx, len, ws.qorder);
-  if (e == hipSuccess && L.bf16) e = launch_order_by_count(L, ws.k2q_off, ws.korder);
-  if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, ws.args);
   if (e == hipSuccess)
-    e = launch_fine_bwd(L, q, k, v, idx, len, ws.qorder, ws.k2q_off, ws.k2q, ws.korder, s.lse_f, ws.dof, ws.delta,
-                        ws.dqc, ws.dkc, ws.dvc, dq, dk, dv, L.pool_max ? ws.args : nullptr, ws.pairs);
+    e = run_fine_backward(L, d, ws, q, k, v, idx, len, nullptr, nullptr, s.lse_f, ws.dof, ws.delta, ws.dqc, ws.dkc,
+                          ws.dvc, dq, dk, dv);
   return hip_status(e);
 }
 
@@ -348,20 +473,17 @@ vsa_status vsa_fine_forward(const vsa_problem* p, const void* q, const void* k, 
   Dims d;
   vsa_status st = check_problem(p, &L, &d);
   if (st != VSA_OK) return st;
+  const bool need_ws = L.bf16 || d.qsplit || d.ksplit;
   st = check_ptrs({{q, true}, {k, true}, {v, true}, {idx, true}, {len, true}, {o_f, true}, {lse_f, true},
-                   {workspace, L.bf16}});
+                   {workspace, need_ws}});
   if (st != VSA_OK) return st;
-  int32_t* order = nullptr;
-  if (L.bf16) {
-    const FwdWs ws = carve_fwd_ws(d, const_cast<void*>(workspace));
+  FwdWs ws{};
+  if (need_ws) {
+    ws = carve_fwd_ws(d, const_cast<void*>(workspace));
     if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
-    order = ws.order;
   }
   L.stream = static_cast<hipStream_t>(stream);
-  hipError_t e = order != nullptr ? launch_order(L, idx, len, order) : hipSuccess;
-  if (e == hipSuccess)
-    e = launch_fine_fwd(L, q, k, v, idx, len, order, o_f, lse_f, nullptr, nullptr, nullptr, nullptr);
-  return hip_status(e);
+  return hip_status(run_fine_forward(L, d, ws, q, k, v, idx, len, o_f, lse_f, nullptr, nullptr, nullptr, nullptr));
 }
 
 vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
@@ -371,19 +493,17 @@ vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, 
   Dims d;
   vsa_status st = check_problem(p, &L, &d);
   if (st != VSA_OK) return st;
+  const bool need_ws = L.bf16 || d.qsplit || d.ksplit;
   st = check_ptrs({{q, true}, {k, true}, {v, true}, {idx, true}, {len, true}, {o_c, true}, {g_c, false},
-                   {g_f, false}, {o, true}, {o_f, false}, {lse_f, false}, {workspace, L.bf16}});
+                   {g_f, false}, {o, true}, {o_f, false}, {lse_f, false}, {workspace, need_ws}});
   if (st != VSA_OK) return st;
-  int32_t* order = nullptr;
-  if (L.bf16) {
-    const FwdWs ws = carve_fwd_ws(d, const_cast<void*>(workspace));
+  FwdWs ws{};
+  if (need_ws) {
+    ws = carve_fwd_ws(d, const_cast<void*>(workspace));
     if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
-    order = ws.order;
   }
   L.stream = static_cast<hipStream_t>(stream);
-  hipError_t e = order != nullptr ? launch_order(L, idx, len, order) : hipSuccess;
-  if (e == hipSuccess) e = launch_fine_fwd(L, q, k, v, idx, len, order, o_f, lse_f, o_c, g_c, g_f, o);
-  return hip_status(e);
+  return hip_status(run_fine_forward(L, d, ws, q, k, v, idx, len, o_f, lse_f, o_c, g_c, g_f, o));
 }
 
 vsa_status vsa_fine_combine_noalloc(const vsa_problem* p, const void* q, const void* k, const void* v,
@@ -397,6 +517,7 @@ vsa_status vsa_fine_combine_noalloc(const vsa_problem* p, const void* q, const v
                    {g_f, false}, {o, true}, {o_f, false}, {lse_f, false}});
   if (st != VSA_OK) return st;
   if (d.BH * d.Nq > kNoAllocMaxCubes) return VSA_ERR_WORKSPACE;
+  if (d.qsplit || d.ksplit) return VSA_ERR_UNSUPPORTED;   // 256-token tiles need expanded lists (a workspace)
   int32_t* order = nullptr;
   if (L.bf16) {
     order = scratch_ptr();
@@ -464,13 +585,8 @@ vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k,
   const BwdWs ws = carve_bwd_ws(d, workspace);
   if (ws_bytes < ws.bytes) return VSA_ERR_WORKSPACE;
   L.stream = static_cast<hipStream_t>(stream);
-  hipError_t e = L.bf16 ? launch_order(L, idx, len, ws.qorder) : hipSuccess;
-  if (e == hipSuccess && L.bf16) e = launch_order_by_count(L, k2q_off, ws.korder);
-  if (e == hipSuccess && L.pool_max) e = launch_pool(L, q, k, v, nullptr, nullptr, nullptr, ws.args);
-  if (e == hipSuccess)
-    e = launch_fine_bwd(L, q, k, v, idx, len, ws.qorder, k2q_off, k2q, ws.korder, lse_f, d_o_f, delta, dq_c, dk_c,
-                        dv_c, dq, dk, dv, L.pool_max ? ws.args : nullptr, ws.pairs);
-  return hip_status(e);
+  return hip_status(run_fine_backward(L, d, ws, q, k, v, idx, len, k2q_off, k2q, lse_f, d_o_f, delta, dq_c, dk_c,
+                                      dv_c, dq, dk, dv));
 }
 
 vsa_status vsa_coarse_backward(const vsa_problem* p, const float* q_c, const float* k_c, const float* v_c,

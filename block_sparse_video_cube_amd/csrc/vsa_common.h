@@ -57,6 +57,37 @@ __host__ __device__ inline Grid make_grid(int T, int H, int W, int tiled = 0, in
   return g;
 }
 
+// Halves of a 256-token cube or key block: the cube split in two along its
+// first side longer than 1 (t, else y, else x). Tokens keep their order: in
+// row-major (t', y', x') order the first 128 tokens of the cube are exactly
+// its first half, in the half's own row-major order. In the raster layout the
+// halves form the grid of the halved shape (row-major); in the tiled layout
+// half hh of cube c is entry 2c + hh (tokens 256c + 128hh + l). The fine
+// kernels handle 256-token tiles as these 128-token halves.
+__host__ __device__ inline Grid half_grid(const Grid& g) {
+  int ct = 1 << g.lct, ch = 1 << g.lch, cw = 1 << g.lcw;
+  if (ct > 1) ct >>= 1;
+  else if (ch > 1) ch >>= 1;
+  else cw >>= 1;
+  return make_grid(g.T, g.H, g.W, g.tiled, ct, ch, cw);
+}
+// Index in h2 = half_grid(g) of half hh of cube c of g.
+__host__ __device__ inline int half_index(const Grid& g, const Grid& h2, int c, int hh) {
+  if (g.tiled) return 2 * c + hh;
+  const int xc = c % g.Wn, r = c / g.Wn, yc = r % g.Hn, tc = r / g.Hn;
+  if (g.lct > 0) return ((2 * tc + hh) * h2.Hn + yc) * h2.Wn + xc;
+  if (g.lch > 0) return (tc * h2.Hn + 2 * yc + hh) * h2.Wn + xc;
+  return (tc * h2.Hn + yc) * h2.Wn + 2 * xc + hh;
+}
+// The cube c of g and half hh of entry s of h2 = half_grid(g).
+__host__ __device__ inline void half_parent(const Grid& g, const Grid& h2, int s, int& c, int& hh) {
+  if (g.tiled) { c = s >> 1; hh = s & 1; return; }
+  const int xs = s % h2.Wn, r = s / h2.Wn, ys = r % h2.Hn, ts = r / h2.Hn;
+  if (g.lct > 0) { hh = ts & 1; c = ((ts >> 1) * g.Hn + ys) * g.Wn + xs; }
+  else if (g.lch > 0) { hh = ys & 1; c = (ts * g.Hn + (ys >> 1)) * g.Wn + xs; }
+  else { hh = xs & 1; c = (ts * g.Hn + ys) * g.Wn + (xs >> 1); }
+}
+
 // Index (row) of token 0 of cube c in the problem's token order.
 __host__ __device__ __forceinline__ int cube_first(const Grid& g, int c) {
   if (g.tiled) return c * g.B;

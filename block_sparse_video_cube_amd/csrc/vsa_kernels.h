@@ -31,6 +31,16 @@ hipError_t launch_pool(const Launch& L, const void* q, const void* k, const void
 hipError_t launch_relayout(const Launch& L, const void* src, void* dst, bool to_tiled);
 hipError_t launch_crop_pad(const Launch& L, const void* src, void* dst, int ts, int hs, int ws, bool to_small);
 
+// 256-token tiles as 128-token halves (half_grid): S is L with g and / or
+// gk replaced by their half grids and stride doubled when key blocks are
+// split. Lists of the query halves (idx2 [BH, S.g.Nc, S.stride], len2) from
+// the cubes' lists; per-half copies of per-cube rows (D fp32 values, times
+// mul; either of src / asrc may be null) and max-pool argmax bytes.
+hipError_t launch_split_lists(const Launch& L, const Launch& S, const int32_t* idx, const int32_t* len, int32_t* idx2,
+                              int32_t* len2);
+hipError_t launch_split_rows(const Launch& L, const Grid& g, const Grid& g2, const float* src, float* dst,
+                             const uint8_t* asrc, uint8_t* adst, float mul);
+
 int coarse_max_cubes();
 // Keys of the bitonic order sorts (one workgroup per (b, h), keys in LDS):
 // the largest cube or key-block count per (b, h).

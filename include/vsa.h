@@ -68,8 +68,8 @@ typedef enum {
   VSA_ERR_WORKSPACE = 7,   /* workspace / saved buffer smaller than required */
   VSA_ERR_INDEX = 8,       /* an index list failed validation                */
   VSA_ERR_UNSUPPORTED = 9, /* valid request this build does not implement (a
-                              cube of other than 32, 64 or 128 tokens, a key
-                              block of other than 16 to 128, too many cubes),
+                              cube of other than 32 to 256 tokens, a key
+                              block of other than 16 to 256, too many cubes),
                               an unknown pool_mode or layout, or in-place
                               tiling                                          */
   VSA_ERR_HIP = 10,        /* a HIP call or kernel launch failed             */
@@ -112,8 +112,11 @@ typedef struct {
                             (Ct, Ch, Cw) with tile size Bt = Ct*Ch*Cw and
                             weighs tile sizes in its design exploration.
                             Each side a power of two, Cw >= 4, Bt in
-                            {32, 64, 128}. In-cube token order is row-major
-                            (t', y', x').                                     */
+                            {32, 64, 128, 256}. In-cube token order is
+                            row-major (t', y', x'). The fine kernels take a
+                            256-token cube as its two 128-token halves (split
+                            along its first side longer than 1); pooling, the
+                            coarse stage and the lists stay per cube.         */
   int32_t kcube_t, kcube_h, kcube_w;
                          /* sides of the key blocks; all 0 => the query cube.
                             The same page's tile-size exploration compares
@@ -123,9 +126,10 @@ typedef struct {
                             are Nq x Nk (Nq = N/Bt query cubes, Nk = N/Bk key
                             blocks), index lists name key blocks, and topk /
                             list_stride range over 1..Nk. Powers of two,
-                            kcube_w >= 4, Bk in {16, 32, 64, 128} (16-token
-                            blocks are taken two at a time by the fine
-                            kernels). The tiled layout needs kcube = cube.  */
+                            kcube_w >= 4, Bk in {16, 32, 64, 128, 256}
+                            (16-token blocks are taken two at a time by the
+                            fine kernels, 256-token blocks as two halves).
+                            The tiled layout needs kcube = cube.            */
 } vsa_problem;
 
 /* Short text for a status code (static storage, never NULL). */
@@ -135,7 +139,7 @@ const char* vsa_status_string(vsa_status s);
 int32_t vsa_version(void);
 
 /* Largest Nc or Nk (cubes or key blocks per (b, h)) the coarse stage
- * accepts in this build. */
+ * accepts in this build (8192). */
 int32_t vsa_max_cubes(void);
 
 /* Bytes of device workspace vsa_forward (training = 0) or vsa_backward
@@ -232,7 +236,9 @@ vsa_status vsa_fine_combine(const vsa_problem* p, const void* q, const void* k, 
  * order they need lives in a 4 MiB device array inside the library (one per
  * GPU, held until the process ends), so B * heads * Nc may not exceed
  * 1,048,576 (VSA_ERR_WORKSPACE otherwise, before anything is enqueued). The
- * call allocates nothing. It uses the array of the current device, so
+ * call allocates nothing. Problems with 256-token cubes or key blocks are
+ * refused (VSA_ERR_UNSUPPORTED: their expanded lists need a workspace). It
+ * uses the array of the current device, so
  * `stream` must belong to the current device; the first call on a device
  * looks up the array's address (VSA_ERR_HIP if that fails). Every call on a
  * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
@@ -276,7 +282,9 @@ vsa_status vsa_index_transpose(const vsa_problem* p, const int32_t* idx, const i
  * (workspace: ws_bytes >= vsa_workspace_bytes(p, 1)); k2q_off / k2q from
  * vsa_index_transpose. bf16 or fp32. dQ walks each query cube's list, dK / dV
  * walk the transposed lists, so no atomics are used and the result is
- * deterministic. */
+ * deterministic. With 256-token cubes or key blocks the kernels run on their
+ * 128-token halves and build the halves' transposed lists in the workspace
+ * themselves (k2q_off / k2q must still be valid pointers; they are not read). */
 vsa_status vsa_fine_backward(const vsa_problem* p, const void* q, const void* k, const void* v,
                              const int32_t* idx, const int32_t* len, const int32_t* k2q_off,
                              const int32_t* k2q, const float* lse_f, const void* d_o_f,

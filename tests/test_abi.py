@@ -117,9 +117,10 @@ def test_crop_pad_validation():
 
 @pytest.mark.parametrize("cube,ok", [((4, 4, 4), True), ((2, 4, 4), True), ((4, 4, 8), True), ((1, 8, 8), True),
                                      ((8, 4, 4), True), ((2, 2, 8), True), ((4, 8, 2), False), ((3, 4, 4), False),
-                                     ((2, 2, 4), False), ((4, 8, 8), False)])
+                                     ((2, 2, 4), False), ((4, 8, 8), True), ((1, 16, 16), True),
+                                     ((8, 8, 8), False), ((2, 16, 16), False)])
 def test_cube_shapes(cube, ok):
-    """Cube sides: powers of two with Cw >= 4 and 32, 64 or 128 tokens."""
+    """Cube sides: powers of two with Cw >= 4 and 32, 64, 128 or 256 tokens."""
     p = _p(T=8, H=16, W=16, cube=cube, topk=1)
     bt = cube[0] * cube[1] * cube[2]
     got = N.lib().vsa_workspace_bytes(ctypes.byref(p.c()), 0)
@@ -134,10 +135,10 @@ def test_cube_shapes(cube, ok):
 @pytest.mark.parametrize("kcube,ok", [((2, 4, 4), True), ((4, 4, 8), True), ((1, 8, 4), True), ((4, 4, 4), True),
                                       ((1, 4, 4), True), ((2, 2, 4), True), ((1, 1, 16), True),
                                       ((1, 2, 4), False), ((4, 2, 2), False), ((3, 4, 4), False),
-                                      ((8, 4, 8), False), ((0, 4, 4), False)])
+                                      ((8, 4, 8), True), ((0, 4, 4), False), ((8, 8, 8), False)])
 def test_key_block_shapes(kcube, ok):
     """Key blocks of their own shape (Bq x Bk tiles): powers of two, Cw >= 4,
-    16 to 128 tokens, and all-zero sides mean the query cube."""
+    16 to 256 tokens, and all-zero sides mean the query cube."""
     p = _p(T=8, H=16, W=16, topk=1, kcube=kcube)
     got = N.lib().vsa_workspace_bytes(ctypes.byref(p.c()), 0)
     assert (got > 0) == ok

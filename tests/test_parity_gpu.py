@@ -475,7 +475,8 @@ def test_single_cube_latent(d):
 @pytest.mark.parametrize("d,pool,cube,kcube,gates", [
     (64, "mean", (4, 4, 4), None, True), (128, "max", (4, 4, 4), None, True), (64, "mean", (4, 4, 4), None, False),
     (128, "mean", (2, 4, 4), (4, 4, 8), True), (64, "max", (4, 4, 8), (1, 4, 4), True),
-    (64, "mean", (4, 4, 4), (1, 4, 4), True)])
+    (64, "mean", (4, 4, 4), (1, 4, 4), True), (64, "mean", (4, 8, 8), None, True),
+    (128, "max", (1, 16, 16), (4, 8, 8), True)])
 def test_backward_fp32(d, pool, cube, kcube, gates):
     """fp32 problems: the whole backward (fp32 kernels) on ragged lists with an
     empty and a full row, against the oracle to 1e-4 absolute."""
@@ -573,7 +574,10 @@ def test_backward_stages():
 @pytest.mark.parametrize("dtype,pool,cube,kcube", [("bf16", "mean", (4, 4, 4), None),
                                                     ("bf16", "max", (4, 4, 4), (1, 4, 4)),
                                                     ("f32", "mean", (2, 4, 4), (4, 4, 8)),
-                                                    ("f32", "max", (4, 4, 4), None)])
+                                                    ("f32", "max", (4, 4, 4), None),
+                                                    ("bf16", "max", (4, 8, 8), (4, 4, 4)),
+                                                    ("bf16", "mean", (4, 4, 4), (1, 16, 16)),
+                                                    ("f32", "max", (1, 16, 16), None)])
 def test_fine_backward_stage(dtype, pool, cube, kcube):
     """The fine-backward entry point on its own: the oracle's LSE_f, dO_f,
     delta and pooled gradients in (rounded to the GPU dtypes), the GPU's
@@ -758,14 +762,15 @@ def test_forward_on_compatible_latent_then_crop():
 
 
 # ------------------------------------------- other cube shapes (tile sizes)
-CUBES = [(2, 4, 4), (4, 4, 8), (1, 8, 8)]   # 32, 128 and another 64-token tile
+CUBES = [(2, 4, 4), (4, 4, 8), (1, 8, 8),   # 32, 128 and another 64-token tile
+         (4, 8, 8), (1, 16, 16)]            # 256-token tiles (split along t and along y)
 
 
 @pytest.mark.parametrize("cube", CUBES)
 @pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 64)])
 def test_general_cube_forward_topk(cube, dtype, d):
     """Top-K selection bit-exact (near-tie protocol) and the output against the
-    oracle on the GPU's lists, for tiles of 32, 64 and 128 tokens."""
+    oracle on the GPU's lists, for tiles of 32, 64, 128 and 256 tokens."""
     T, H, W, heads = 8, 16, 32, 2
     bt = cube[0] * cube[1] * cube[2]
     nc = T * H * W // bt
@@ -796,7 +801,7 @@ def test_general_cube_backward(cube, d):
     backward_compare(x, p, "bf16")
 
 
-@pytest.mark.parametrize("cube", [(4, 4, 8), (2, 4, 4)])
+@pytest.mark.parametrize("cube", [(4, 4, 8), (2, 4, 4), (4, 8, 8)])
 def test_general_cube_tiled_equals_raster_and_max_pool(cube):
     x, p = _small_train_inputs(d=64, seed=23, T=8, H=16, W=16, cube=cube)
     pm = dataclasses.replace(p, pool="max")
@@ -815,7 +820,13 @@ def test_general_cube_tiled_equals_raster_and_max_pool(cube):
     torch.cuda.synchronize()
     assert torch.equal(V.untile(p, ot), o)
     for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
-        assert torch.equal(V.untile(p, gt[nm]), g[nm]), nm
+        if p.Bt == 256 and nm in ("dk", "dv"):
+            # The fine kernels take a 256-token cube as two halves, numbered
+            # row-major in the raster layout and 2c + h in the tiled one, so
+            # dK / dV sum over the query halves in another order.
+            assert_close(host(V.untile(p, gt[nm])), host(g[nm]), "bf16", nm)
+        else:
+            assert torch.equal(V.untile(p, gt[nm]), g[nm]), nm
     # crop / pad with this cube, from the tiled layout
     Tc, Hc, Wc = V.compatible_latent(7, 13, 9, cube)
     assert (Tc, Hc, Wc) == O.compatible_latent(7, 13, 9, cube)
@@ -833,7 +844,9 @@ def test_general_cube_tiled_equals_raster_and_max_pool(cube):
 # 16-token key blocks (taken two per 32-key chunk): 64 x 16 (the summary
 # page's tile), 32 x 16, 128 x 16.
 TILE_PAIRS = [((4, 4, 4), (2, 4, 4)), ((4, 4, 4), (4, 4, 8)), ((2, 4, 4), (4, 4, 8)), ((4, 4, 8), (2, 4, 4)),
-              ((4, 4, 4), (1, 4, 4)), ((2, 4, 4), (2, 2, 4)), ((4, 4, 8), (1, 4, 4))]
+              ((4, 4, 4), (1, 4, 4)), ((2, 4, 4), (2, 2, 4)), ((4, 4, 8), (1, 4, 4)),
+              # 256-token query cubes or key blocks (the fine kernels run on 128-token halves)
+              ((4, 8, 8), (4, 4, 4)), ((4, 4, 4), (4, 8, 8)), ((4, 8, 8), (1, 16, 16)), ((4, 8, 8), (1, 4, 4))]
 
 
 @pytest.mark.parametrize("cube,kcube", TILE_PAIRS)
