@@ -17,7 +17,7 @@ static hipError_t stub() { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_pool(const Launch&, const void*, const void*, const void*, float*, float*, float*, uint8_t*) { return stub(); }
 hipError_t launch_relayout(const Launch&, const void*, void*, bool) { return stub(); }
 hipError_t launch_crop_pad(const Launch&, const void*, void*, int, int, int, bool) { return stub(); }
-int coarse_max_cubes() { return 2048; }
+int coarse_max_cubes() { return 8192; }
 int coarse_ld(int Nc) { return (Nc + 3) & ~3; }
 hipError_t launch_coarse(const Launch&, const float*, const float*, const float*, float*, float*, int32_t*, int32_t*, float*) { return stub(); }
 hipError_t launch_order(const Launch&, const int32_t*, const int32_t*, int32_t*) { return stub(); }
@@ -37,6 +37,8 @@ hipError_t launch_fine_bwd(const Launch&, const void*, const void*, const void*,
                            const uint8_t*, int32_t*) { return stub(); }
 hipError_t launch_key_pairs(const Launch&, const int32_t*, const int32_t*, int32_t*, int32_t*) { return stub(); }
 hipError_t launch_validate_lists(const Launch&, const int32_t*, const int32_t*, int32_t*) { return stub(); }
+hipError_t launch_split_lists(const Launch&, const Launch&, const int32_t*, const int32_t*, int32_t*, int32_t*) { return stub(); }
+hipError_t launch_split_rows(const Launch&, const Grid&, const Grid&, const float*, float*, const uint8_t*, uint8_t*, float) { return stub(); }
 }  // namespace vsa
 
 static int failures = 0;
