@@ -269,19 +269,19 @@ def tile_case(V, torch, name, q, k, v, gc, gf, cube, steps=5, kcube=None):
 
 
 def tile_tradeoff(V, WL, torch, main_name, main_inputs):
-    """The tile-size trade-off: the same inputs with 32-, 64- and 128-token
-    tiles, square (Bt x Bt) and with 64-token query cubes over 16-, 32- or
-    128-token key blocks (Bq x Bk), where the latent allows them (a side must
-    divide the latent's, and Nc, Nk must stay within the coarse stage's
-    limit)."""
+    """The tile-size trade-off: the same inputs with 32-, 64-, 128- and
+    256-token tiles, square (Bt x Bt) and with 64-token query cubes over 16-,
+    32-, 128- or 256-token key blocks (Bq x Bk), where the latent allows them
+    (a side must divide the latent's, and Nc, Nk must stay within the coarse
+    stage's limit)."""
     def fits(shape, cube):
         T, H, W = shape
         n = cube[0] * cube[1] * cube[2]
         return not (T % cube[0] or H % cube[1] or W % cube[2]) and T * H * W // n <= V.max_cubes()
 
     q64 = (4, 4, 4)
-    shapes = [(c, None) for c in ((4, 4, 4), (4, 4, 8), (2, 4, 4))] + [(q64, (1, 4, 4)), (q64, (2, 4, 4)),
-                                                                         (q64, (4, 4, 8))]
+    shapes = [(c, None) for c in ((4, 4, 4), (4, 4, 8), (2, 4, 4), (4, 8, 8))] + [(q64, (1, 4, 4)), (q64, (2, 4, 4)),
+                                                                                    (q64, (4, 4, 8)), (q64, (4, 8, 8))]
     out = []
     for name, inputs in [(main_name, main_inputs), ("bf16_480p_20x28x52", None), ("bf16_16x32x32_spikes", None)]:
         if inputs is None:
