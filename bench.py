@@ -33,6 +33,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_combine_720p_traffic.json")
+STAGE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "stages_720p_traffic.json")
 FINE_SRC = os.path.join(ROOT, "block_sparse_video_cube_amd", "csrc", "fine_fwd.hip")
 
 
@@ -41,21 +42,42 @@ def log(msg: str) -> None:
 
 
 def fine_source_hash() -> str:
-    with open(FINE_SRC, "rb") as f:
+    return source_hash(FINE_SRC)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per launch of the fine kernel from the committed counter
-    summary, or None when absent or taken on a different kernel source."""
+    summary, or None when absent, taken on another workload or on a
+    different kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != fine_source_hash():
+    if t.get("kernel_source_sha256_16") != fine_source_hash() or t.get("workload") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def stage_traffic(workload: str, label: str):
+    """Counter bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) per dispatch
+    of one stage kernel from the committed summary, or None when absent,
+    taken on another workload or on a different source of that kernel."""
+    try:
+        with open(STAGE_TRAFFIC_FILE) as f:
+            t = json.load(f)
+        e = t["kernels"][label]
+        if t.get("workload") != workload or e["source_sha256_16"] != source_hash(os.path.join(ROOT, e["source"])):
+            return None
+    except (OSError, ValueError, KeyError):
+        return None
+    return {"hbm_bytes": e["hbm_bytes"], "fetch_bytes": e["fetch_bytes"], "write_bytes": e["write_bytes"],
+            "over_algorithmic": round(e["hbm_bytes"] / e["algorithmic_bytes"], 3)}
 
 
 def cpu_baseline(workload: str, heads: list[int]) -> dict:
@@ -226,7 +248,8 @@ def train_measure(name: str, steps: int, warmup: int) -> dict:
             "fine_bwd_tflops": round(fl_b / (st[3] * 1e-3) / 1e12, 2),
             "fine_bwd_frac_bf16_peak": round(fl_b / (st[3] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "combine_bwd_GB_per_s": round(cb_bytes / (st[0] * 1e-3) / 1e9, 1),
-            "combine_bwd_frac_hbm_peak": round(cb_bytes / (st[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "combine_bwd_frac_hbm_peak": round(cb_bytes / (st[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "combine_bwd_traffic": stage_traffic(w.name, "combine_bwd")}
 
 
 def tile_case(V, torch, name, q, k, v, gc, gf, cube, steps=5, kcube=None):
@@ -484,7 +507,7 @@ def main() -> int:
     fine_bytes = 6 * raster * esz + pooled_b + bh * w.Nc * p.stride * 4 * 2
     value = fine_flop / (ms_step * 1e-3) / 1e12
     achieved = fine_flop / (stage_ms[2] * 1e-3) / 1e12
-    traffic = measured_traffic()
+    traffic = measured_traffic(w.name)
     line = {
         "metric": "VSA attention TFLOP/s (computed blocks) + % bf16 MFMA peak, 720p fwd",
         "value": round(value, 2),
@@ -516,10 +539,13 @@ def main() -> int:
                      "GB_per_s": round(pool_bytes / (stage_ms[0] * 1e-3) / 1e9, 1),
                      "frac": round(pool_bytes / (stage_ms[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "cold_ms": round(pool_cold_ms, 4),
-                     "cold_frac": round(pool_bytes / (pool_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                     "cold_frac": round(pool_bytes / (pool_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": stage_traffic(w.name, "pool")},
             "coarse_topk": {"ms": round(stage_ms[1], 4), "bound": "mfma_fp32", "flop": coarse_flop,
                             "TFLOP_per_s": round(coarse_flop / (stage_ms[1] * 1e-3) / 1e12, 2),
-                            "frac": round(coarse_flop / (stage_ms[1] * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)},
+                            "frac": round(coarse_flop / (stage_ms[1] * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                            "traffic": {n: stage_traffic(w.name, n)
+                                        for n in ("coarse_scores", "coarse_rows", "coarse_gemm (O_c)")}},
             "fine_combine": {"ms": round(stage_ms[2], 4), "bound": "mfma", "flop": fine_flop,
                              "TFLOP_per_s": round(achieved, 2), "frac": round(achieved / PEAK_BF16_TFLOPS, 4)},
         },
