@@ -96,8 +96,9 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
                                                             const float* __restrict__ kc, float* __restrict__ s,
                                                             int Nq, int Nk, int ld, float scale) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const long bh = blockIdx.z;
-  const int m0 = blockIdx.y * 128 + (w >> 1) * 64, n0 = blockIdx.x * 128 + (w & 1) * 64;
+  const Tile3 t = tile3((Nk + 127) / 128, (Nq + 127) / 128);
+  const long bh = t.z;
+  const int m0 = t.y * 128 + (w >> 1) * 64, n0 = t.x * 128 + (w & 1) * 64;
   if (m0 >= Nq || n0 >= Nk) return;   // wave-uniform; no barrier in this kernel
   f32x4 acc[4][4];
   nt_block64<D>(qc + bh * (long)Nq * D, kc + bh * (long)Nk * D, Nq, Nk, m0, n0, acc);
@@ -146,8 +147,9 @@ __global__ __launch_bounds__(256) void coarse_gemm_kernel(const float* __restric
   // is stored at unit (k / 4) ^ (row / 2 mod 8).
   auto tslot = [](int row, int k) { return row * KC + ((((k >> 2) ^ (row >> 1)) & 7) << 2) + (k & 3); };
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-  const long bh = blockIdx.y;
-  const int r0 = blockIdx.x * 32;
+  const Tile3 t = tile3((R + 31) / 32, 1);
+  const long bh = t.z;
+  const int r0 = t.x * 32;
   const float* M = m + bh * (long)(TRANS_A ? Kd : R) * ld;
   const float* Bm = b + bh * (long)Kd * D;
   // A staging role: without TRANS_A, row ai of the tile, k = 4aq .. 4aq+3
@@ -603,7 +605,7 @@ template <bool TRANS_A, bool EXP>
 static void launch_gemm(const Launch& L, const float* m, const float* lse, const float* b, float* c, int R, int Kd,
                         float scale) {
   const int ld = coarse_ld(L.gk.Nc);
-  const dim3 grid((R + 31) / 32, L.BH);
+  const dim3 grid((unsigned)((R + 31) / 32 * L.BH));
   if (L.D == 64)
     hipLaunchKernelGGL((coarse_gemm_kernel<64, TRANS_A, EXP>), grid, dim3(256), 0, L.stream, m, lse, b, c, R, Kd,
                        ld, scale);
@@ -624,7 +626,7 @@ static void launch_rows(const Launch& L, const float* s, float* lse, int32_t* id
 hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, const float* vc, float* oc,
                          float* lse, int32_t* idx, int32_t* len, float* s_scratch) {
   const int Nq = L.g.Nc, Nk = L.gk.Nc, ld = coarse_ld(Nk);
-  const dim3 tiles((Nk + 127) / 128, (Nq + 127) / 128, L.BH), block(256);
+  const dim3 tiles((unsigned)((Nk + 127) / 128 * ((Nq + 127) / 128) * L.BH)), block(256);
   if (L.D == 64)
     hipLaunchKernelGGL((coarse_scores_kernel<64>), tiles, block, 0, L.stream, qc, kc, s_scratch, Nq, Nk, ld,
                        L.scale);
@@ -675,8 +677,9 @@ __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_kernel(const float* __r
                                                              float* __restrict__ pbuf, float* __restrict__ dsbuf,
                                                              int Nq, int Nk, int ld, float scale) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const long bh = blockIdx.z;
-  const int m0 = blockIdx.y * 128 + (w >> 1) * 64, n0 = blockIdx.x * 128 + (w & 1) * 64;
+  const Tile3 t = tile3((Nk + 127) / 128, (Nq + 127) / 128);
+  const long bh = t.z;
+  const int m0 = t.y * 128 + (w >> 1) * 64, n0 = t.x * 128 + (w & 1) * 64;
   if (m0 >= Nq || n0 >= Nk) return;   // wave-uniform; no barrier in this kernel
   const long qbase = bh * (long)Nq * D, kbase = bh * (long)Nk * D;
   f32x4 sacc[4][4], pacc[4][4];
@@ -710,7 +713,7 @@ hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, 
                              float* dvc, float* ds_scratch, float* p_scratch, float* dc_scratch) {
   const int Nq = L.g.Nc, Nk = L.gk.Nc, ld = coarse_ld(Nk);
   const long rows = (long)L.BH * Nq;
-  const dim3 tiles((Nk + 127) / 128, (Nq + 127) / 128, L.BH);
+  const dim3 tiles((unsigned)((Nk + 127) / 128 * ((Nq + 127) / 128) * L.BH));
   if (L.D == 64) {
     hipLaunchKernelGGL((coarse_bwd_delta_kernel<64>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream, doc,
                        oc, dc_scratch, rows);

@@ -134,6 +134,18 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   const int x = b & 7, k = b >> 3;
   return x * q + (x < rem ? x : rem) + k;
 }
+// Tile (x, y) of head z of a 1-D grid over nx * ny tiles per head (x
+// fastest), through xcd_remap: each XCD takes whole heads, whose operands
+// then stay in its L2 instead of being fetched by every XCD.
+struct Tile3 {
+  int x, y;
+  long z;
+};
+__device__ __forceinline__ Tile3 tile3(int nx, int ny) {
+  const int s = xcd_remap(blockIdx.x, gridDim.x);
+  const int r = s / nx;
+  return Tile3{s - r * nx, r % ny, r / ny};
+}
 
 
 template <typename T> struct Io;
