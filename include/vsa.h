@@ -173,7 +173,12 @@ vsa_status vsa_forward(const vsa_problem* p, const void* q, const void* k, const
                        void* o, void* saved, void* workspace, size_t ws_bytes, void* stream);
 
 /* Whole backward of sum(O * dO) with the selection held constant (the top-K
- * mask is piecewise constant and carries no gradient). Inputs as for the
+ * mask is piecewise constant and carries no gradient). The method is trained
+ * end to end as one differentiable operator, the gate letting the learned
+ * coarse and fine branches both receive gradient (VSA summary page,
+ * Abstract, and section 1 "Introduction", the gated combination): this entry
+ * point returns the gradients of both branches, the coarse one through the
+ * pooling into every token of a cube. Inputs as for the
  * forward that filled `saved` (same q, k, v, g_c, g_f, idx, len), d_o
  * (dtype, raster). Outputs dq, dk, dv (dtype, raster) and dg_c, dg_f (dtype,
  * raster; each may be NULL when its gate was NULL, then it is not written).
