@@ -619,7 +619,15 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
   // arrived (it would otherwise wait for them, and for every load in flight,
   // before each chunk's MFMAs).
   vm_settled();
-  for (int c = 0; c <= nch; ++c) {
+  // Iteration c of the walk. Its LDS stage U = c % QST is a compile-time
+  // constant (the walk below is unrolled by QST), so every LDS address is a
+  // constant offset from a loop-invariant lane address; the role is one too,
+  // so each role runs its own copy of the loop and its accumulator stays in
+  // place across iterations.
+  static_assert(QST == 4, "the walk is unrolled by four");
+  auto iter = [&](auto role, auto stage, int c) {
+    constexpr bool ISK = decltype(role)::value;
+    constexpr int U = decltype(stage)::value;
     // Chunk c has landed once only chunk c + 1's loads may be outstanding.
     if (c + 1 < nch) {
       if (wv == 0) wait_vmcnt<2 * RPW + 2>();
@@ -632,9 +640,9 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
     const bool kvalid = kvalid_next;
     if (c + 1 < nch) kvalid_next = kflag(c + 1);   // chunk c + 1 was issued before chunk c + 2
     if (c + 2 < nch) issue(c + 2);
-    if (!isk) {
+    if constexpr (!ISK) {
       if (c < nch) {
-        const int st = c % QST;
+        constexpr int st = U;
         float lse2[16];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -658,8 +666,8 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
         bf16x8 pf[2];
 #pragma unroll
         for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (bf16)sx[e];
-        xp[c & 1][kw][0][lane] = pf[0];
-        xp[c & 1][kw][1][lane] = pf[1];
+        xp[U & 1][kw][0][lane] = pf[0];
+        xp[U & 1][kw][1][lane] = pf[1];
         const char* dtile = reinterpret_cast<const char*>(rd[st]);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -669,35 +677,49 @@ __global__ __launch_bounds__(128 * NW, 2) void fine_bwd_dkdv_ws_kernel(
             acc[mb] = mfma32_bf16(rowt_frag(dtile, toffs[mb][s2][0], toffs[mb][s2][1]), pf[s2], acc[mb]);
         __builtin_amdgcn_s_setprio(0);
       }
-    } else if (c > 0) {
-      const int cp = c - 1, st = cp % QST;
-      f32x16 dp;
+    } else {
+      (void)kvalid;
+      if (c > 0) {   // chunk c - 1: its stage and P slot
+        constexpr int st = (U + QST - 1) % QST, slot = (U + 1) & 1;
+        f32x16 dp;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) dp[e] = 0.f;
+        for (int e = 0; e < 16; ++e) dp[e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), kv[ks], dp);
-      bf16x8 sf[2];
-      const bf16x8 pp[2] = {xp[cp & 1][kw][0][lane], xp[cp & 1][kw][1][lane]};
+        for (int ks = 0; ks < G::KS; ++ks) dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), kv[ks], dp);
+        bf16x8 sf[2];
+        const bf16x8 pp[2] = {xp[slot][kw][0][lane], xp[slot][kw][1][lane]};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * t + 4 * hf]);
-        const float d4[4] = {b.x, b.y, b.z, b.w};
+        for (int t = 0; t < 4; ++t) {
+          const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * t + 4 * hf]);
+          const float d4[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * t + r;
-          sf[e >> 3][e & 7] = (bf16)((float)pp[e >> 3][e & 7] * (dp[e] - d4[r]));
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * t + r;
+            sf[e >> 3][e & 7] = (bf16)((float)pp[e >> 3][e & 7] * (dp[e] - d4[r]));
+          }
         }
+        const char* qtile = reinterpret_cast<const char*>(rq[st]);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int mb = 0; mb < G::MB; ++mb)
+            acc[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], acc[mb]);
+        __builtin_amdgcn_s_setprio(0);
       }
-      const char* qtile = reinterpret_cast<const char*>(rq[st]);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int mb = 0; mb < G::MB; ++mb)
-          acc[mb] = mfma32_bf16(rowt_frag(qtile, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], acc[mb]);
-      __builtin_amdgcn_s_setprio(0);
     }
-  }
+  };
+  // Both roles run iterations 0 .. nch, one barrier each.
+  auto walk = [&](auto role) {
+    for (int c = 0; c <= nch; c += QST) {
+      iter(role, std::integral_constant<int, 0>{}, c);
+      if (c + 1 <= nch) iter(role, std::integral_constant<int, 1>{}, c + 1);
+      if (c + 2 <= nch) iter(role, std::integral_constant<int, 2>{}, c + 2);
+      if (c + 3 <= nch) iter(role, std::integral_constant<int, 3>{}, c + 3);
+    }
+  };
+  if (isk) walk(std::true_type{});
+  else walk(std::false_type{});
 
   // lane holds d{K,V}^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its key]
   const long cj = ((long)bh * g.Nc + j) * D;
