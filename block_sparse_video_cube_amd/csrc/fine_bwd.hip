@@ -343,12 +343,16 @@ __device__ __forceinline__ KeyWalk key_walk(const Grid& g, const Grid& gq, const
   return w;
 }
 //
-// dK and dV at 64 channels: every wave computes both for its 32 keys, two
-// waves per SIMD. (At 128 channels the two accumulators, 128 registers, and
-// the lane's K and V rows do not fit 256 registers without spills; the
-// warp-specialized kernel below splits the roles over the waves instead.)
+// dK and dV at 64 channels: every wave computes both for its 32 keys. With
+// two or more waves per workgroup the kernel is held to 168 registers, three
+// waves per SIMD (measured 4% faster on the training workload than two, at
+// one spilled register); a one-wave workgroup's LDS stages allow no more than
+// about two per SIMD, so it keeps the 256-register budget. (At 128 channels
+// the two accumulators, 128 registers, and the lane's K and V rows do not fit
+// 256 registers without spills; the warp-specialized kernel below splits the
+// roles over the waves instead.)
 template <int D, int NW, bool KPAIR>
-__global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * NW, NW == 1 ? 2 : 3) void fine_bwd_dkdv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ k2q_off,
     const int32_t* __restrict__ k2q, const int32_t* __restrict__ order, const int32_t* __restrict__ plen,
@@ -438,15 +442,6 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
     if (c + 1 < nch) issue(c + 1);
     const int st = c & 1;
     // LSE and delta of the accumulator rows this lane holds: rows 8m + 4hf + r.
-    float lse2[16], dl[16];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float4 a = *reinterpret_cast<const float4*>(&rls[st][8 * m + 4 * hf]);
-      lse2[4 * m + 0] = a.x * kLog2e; lse2[4 * m + 1] = a.y * kLog2e;
-      lse2[4 * m + 2] = a.z * kLog2e; lse2[4 * m + 3] = a.w * kLog2e;
-      const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * m + 4 * hf]);
-      dl[4 * m + 0] = b.x; dl[4 * m + 1] = b.y; dl[4 * m + 2] = b.z; dl[4 * m + 3] = b.w;
-    }
     f32x16 sx, dp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { sx[e] = 0.f; dp[e] = 0.f; }
@@ -455,13 +450,22 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dkdv_kernel(
       sx = mfma32_bf16(row_frag<D>(rq[st], n32, hf, ks), kf[ks], sx);
       dp = mfma32_bf16(row_frag<D>(rd[st], n32, hf, ks), vf[ks], dp);
     }
+    // LSE (to log2 units) and delta of the accumulator rows this lane holds
+    // (rows 8m + 4hf + r), read four at a time where they are used.
     bf16x8 pf[2], sf[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2[e]);
-      if constexpr (KPAIR) p = kvalid ? p : 0.f;
-      pf[e >> 3][e & 7] = (bf16)p;
-      sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl[e]));
+    for (int m = 0; m < 4; ++m) {
+      const float4 a = *reinterpret_cast<const float4*>(&rls[st][8 * m + 4 * hf]);
+      const float4 b = *reinterpret_cast<const float4*>(&rdl[st][8 * m + 4 * hf]);
+      const float la[4] = {a.x, a.y, a.z, a.w}, db[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 4 * m + r;
+        float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - la[r] * kLog2e);
+        if constexpr (KPAIR) p = kvalid ? p : 0.f;
+        pf[e >> 3][e & 7] = (bf16)p;
+        sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - db[r]));
+      }
     }
     const char* qtile = reinterpret_cast<const char*>(rq[st]);
     const char* dtile = reinterpret_cast<const char*>(rd[st]);
