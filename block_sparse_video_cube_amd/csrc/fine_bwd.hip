@@ -158,12 +158,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
   // compute this one.
   const int nch = kpair ? (L + 1) >> 1 : L << ksh;
   const bool khalf = kpair && (L & 1);   // keys 16-31 of the last chunk absent
-  if (nch > 0) issue(0);
-  for (int c = 0; c < nch; ++c) {
+  // The loop is unrolled by the two stages so that the stage, and with it
+  // every LDS address, is a compile-time constant.
+  auto step = [&](auto stage, int c) {
+    constexpr int st = decltype(stage)::value;
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (c + 1 < nch) issue(c + 1);
-    const int st = c & 1;
     bf16x8 kf[G::KS], vf[G::KS];
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
@@ -198,6 +199,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
       for (int mb = 0; mb < G::MB; ++mb)
         acc[mb] = mfma32_bf16(rowt_frag(kt, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], acc[mb]);
     __builtin_amdgcn_s_setprio(0);
+  };
+  if (nch > 0) issue(0);
+  for (int c = 0; c < nch; c += 2) {
+    step(std::integral_constant<int, 0>(), c);
+    if (c + 1 < nch) step(std::integral_constant<int, 1>(), c + 1);
   }
 
   // lane holds dQ^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query]; the
