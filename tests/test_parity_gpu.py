@@ -538,6 +538,33 @@ def test_backward_720p_heads():
             assert_close(host(g[nm][:, h:h + 1]), ref[nm], "bf16", f"{nm}[head {h}]")
 
 
+@pytest.mark.timeout(900)
+def test_backward_long_clip():
+    """A training step on a clip of 4096 cubes (32x64x128 latent, 262144
+    tokens, one head, d = 64, top-32 lists from the forward). Past 2048
+    cubes the coarse rows are streamed, the longest-first key order sorts
+    4096 keys and the transposed lists' bitmask has 128 words per key block.
+    Every output and gradient is checked against the oracle on the GPU's
+    lists."""
+    T, H, W, d, k = 32, 64, 128, 64, 32
+    x = WL.make_inputs_custom(1, 1, d, T, H, W, dtype="bf16", seed=43)
+    p = V.Problem(1, 1, T, H, W, d, topk=k)
+    assert p.Nc == 4096
+    print(f"[long clip bwd] {T}x{H}x{W}: {p.Nc} cubes", flush=True)
+    dd = inputs_to_dev(x, "bf16")
+    o, idx, lens, saved = V.forward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"], training=True)
+    g = V.backward(p, dd["q"], dd["k"], dd["v"], dd["g_c"], dd["g_f"], idx, lens, saved, dd["d_o"])
+    torch.cuda.synchronize()
+    gi, gl = host(idx), host(lens)
+    assert (gl == k).all()
+    print("[long clip bwd] oracle forward + backward", flush=True)
+    fwd = O.forward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], topk=0, idx=gi, lens=gl)
+    assert_close(host(o), fwd["o"], "bf16", "o")
+    ref = O.backward(x["q"], x["k"], x["v"], x["g_c"], x["g_f"], x["d_o"], fwd)
+    for nm in ("dq", "dk", "dv", "dg_c", "dg_f"):
+        assert_close(host(g[nm]), ref[nm], "bf16", nm)
+
+
 def test_backward_stages():
     x, p = _small_train_inputs(seed=12)
     d = inputs_to_dev(x, "bf16")
