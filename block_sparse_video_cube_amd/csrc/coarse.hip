@@ -469,8 +469,11 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
 
 // The rows kernel for rows longer than kRowsInRegisters: the same LSE_c and
 // selection (candidates with ballots for K <= 64 when at most 64 values can
-// be chosen, else the radix select), with the row read again from memory (L2)
-// in every pass instead of held in registers.
+// be chosen, else the radix select), with the row read again from memory in
+// every pass instead of held in registers. The first read forms each lane's
+// running maximum and rescaled exponential sum (so LSE_c takes one pass) and
+// the lane's largest and smallest keys (the key map preserves order); with
+// K <= 64 the second counts and collects the candidates together.
 __global__ __launch_bounds__(256) void coarse_rows_stream_kernel(const float* __restrict__ s, float* __restrict__ lse,
                                                                  int32_t* __restrict__ idx, int32_t* __restrict__ len,
                                                                  long rows, int Nk, int ld, int topk, int stride) {
@@ -481,34 +484,40 @@ __global__ __launch_bounds__(256) void coarse_rows_stream_kernel(const float* __
   const float* srow = s + row * ld;
   const int nused = (Nk + 63) >> 6;
   auto key_at = [&](int t) { const int j = t * 64 + lane; return j < Nk ? fkey(srow[j]) : 0u; };
-  float mx = -INFINITY;
-  for (int j = lane; j < Nk; j += 64) mx = fmaxf(mx, srow[j]);
-  mx = wave_max(mx);
-  float sm = 0.f;
-  for (int j = lane; j < Nk; j += 64) sm += __expf(srow[j] - mx);
-  sm = wave_sum(sm);
+  float ml = -INFINITY, sl = 0.f;   // this lane's running maximum and sum of exp(x - ml)
+  float mn = INFINITY;              // and its minimum (the radix select's lowest key)
+  for (int j = lane; j < Nk; j += 64) {
+    const float x = srow[j];
+    mn = fminf(mn, x);
+    if (x > ml) {
+      sl = sl * __expf(ml - x) + 1.0f;
+      ml = x;
+    } else {
+      sl += __expf(x - ml);
+    }
+  }
+  const float mx = wave_max(ml);
+  const float sm = wave_sum(ml == -INFINITY ? 0.f : sl * __expf(ml - mx));
   if (lane == 0) lse[row] = mx + __logf(sm);
   if (topk <= 0) return;
   int* h = hist_all[w];
   int32_t* out = idx + row * (long)stride;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   if (topk <= 64) {   // candidates (see row_topk_few)
-    uint32_t lmax = 0u;
-    for (int t = 0; t < nused; ++t) lmax = max(lmax, key_at(t));
+    const uint32_t lmax = ml == -INFINITY ? 0u : fkey(ml);   // lanes without a value hold key 0
     const uint32_t thr = wave_kth_largest(lmax, true, topk);
-    int n = 0;
-    for (int t = 0; t < nused; ++t) n += __popcll(__ballot(t * 64 + lane < Nk && key_at(t) >= thr));
+    uint64_t* cand = reinterpret_cast<uint64_t*>(h);
+    int n = 0;   // candidates seen; the first 64 are kept
+    for (int t = 0; t < nused; ++t) {
+      const int j = t * 64 + lane;
+      const uint32_t kj = key_at(t);
+      const bool c = j < Nk && kj >= thr;
+      const uint64_t b = __ballot(c);
+      const int slot = n + __popcll(b & lt_mask);
+      if (c && slot < 64) cand[slot] = ((uint64_t)kj << 32) | (uint32_t)j;
+      n += __popcll(b);
+    }
     if (n <= 64) {
-      uint64_t* cand = reinterpret_cast<uint64_t*>(h);
-      int pos = 0;
-      for (int t = 0; t < nused; ++t) {
-        const int j = t * 64 + lane;
-        const uint32_t kj = key_at(t);
-        const bool c = j < Nk && kj >= thr;
-        const uint64_t b = __ballot(c);
-        if (c) cand[pos + __popcll(b & lt_mask)] = ((uint64_t)kj << 32) | (uint32_t)j;
-        pos += __popcll(b);
-      }
       wave_sync();
       const bool have = lane < n;
       const uint64_t x = have ? cand[lane] : 0ull;
@@ -527,10 +536,7 @@ __global__ __launch_bounds__(256) void coarse_rows_stream_kernel(const float* __
     }
   }
   // Radix select (see row_topk), keys recomputed in every pass.
-  uint32_t kmin = 0xFFFFFFFFu;
-  for (int t = 0; t < nused; ++t)
-    if (t * 64 + lane < Nk) kmin = min(kmin, key_at(t));
-  kmin = wave_min_u32(kmin);
+  const uint32_t kmin = wave_min_u32(mn == INFINITY ? 0xFFFFFFFFu : fkey(mn));
   const uint32_t diff = kmin ^ fkey(mx);
   uint32_t prefix = kmin, pmask = 0xFFFFFFFFu;
   int krem = topk;
