@@ -7,7 +7,7 @@
 // reading notes, key design 1 (A_c, O_c, row Top-K into mask M) and the
 // training section (softmax, Top-K and mask-to-index fused in one kernel).
 //
-// Three kernels per forward call, all fp32:
+// Three kernels per forward call:
 //   1. coarse_scores: S = scale * Q_c K_c^T (fp32 MFMA GEMM) into workspace;
 //   2. coarse_rows:   one wave per row: row max / sum -> LSE_c, then the exact
 //                     top-K by a 4-pass radix select on the order-preserving
@@ -15,13 +15,17 @@
 //                     one ordered pass that writes the ascending index list
 //                     (softmax, top-K and mask-to-index in one kernel);
 //   3. coarse_gemm:   O_c = exp(S - LSE_c) V_c (an LDS-tiled GEMM, the
-//                     softmax applied to the operand as it is staged).
+//                     softmax applied to the operand as it is staged); for
+//                     bf16 problems coarse_pv_bf16 instead, the same product
+//                     on bf16 MFMAs with a three-term split of the fp32
+//                     operands (fp32-level accuracy).
 // The backward of the coarse attention is here too; it shares these GEMMs.
 // Selecting on the logits picks the same set as selecting on A_c: the
 // softmax is increasing within a row. S_c is Nq x Nk fp32 per (b, h) of
 // workspace (Nq query cubes, Nk key blocks; rows padded to a multiple of 4
 // floats), written once and read twice (279 MB at the 720p latent).
 #include "vsa_kernels.h"
+#include "fine_common.h"
 
 namespace vsa {
 
@@ -619,6 +623,167 @@ static void launch_gemm(const Launch& L, const float* m, const float* lse, const
     hipLaunchKernelGGL((coarse_gemm_kernel<128, TRANS_A, EXP>), grid, dim3(256), 0, L.stream, m, lse, b, c, R,
                        Kd, ld, scale);
 }
+// O_c = exp(S - LSE_c) V_c of a bf16 problem, on bf16 MFMAs (32x32x16, fp32
+// accumulation) with every fp32 operand split into a bf16 head and a bf16
+// tail (hi = bf16(x), lo = bf16(x - hi); bf16 rounding is within 2^-8 of
+// the value rounded) and the product formed as P_hi V_hi + P_hi V_lo +
+// P_lo V_hi: the dropped P_lo V_lo and the tails' rounding leave each term
+// within 3 * 2^-16 of exact, so O_c keeps near-fp32 accuracy at matrix-core
+// rate (three
+// bf16 products take less matrix time than one fp32 product, and less than
+// the read of S at HBM rate). A workgroup of four waves owns
+// 128 rows of O_c, wave w the rows 32w .. 32w+31 (one per lane column) in the
+// transposed form O_c^T += V_chunk^T P^T over chunks of 32 key blocks. The
+// chunk's V_c rows (fp32, split) form two bf16 row tiles in LDS, double
+// buffered with one barrier per chunk, whose transposed A fragments come from
+// LDS transpose reads; each lane forms its row's P^T fragments from S
+// directly, in the key order those reads deliver (for k-step s2, slot e is
+// key 16 s2 + 8(e/4) + 4hf + e%4: two float4 loads). S loads run two chunks
+// ahead, V_c one.
+template <int D>
+__global__ __launch_bounds__(256, 2) void coarse_pv_bf16_kernel(const float* __restrict__ s,
+                                                               const float* __restrict__ lse,
+                                                               const float* __restrict__ vc, float* __restrict__ oc,
+                                                               int Nq, int Nk, int ld) {
+  using G = ChunkGeom<D>;
+  constexpr int MB = G::MB, U = G::U;
+  constexpr int UPT = 32 * U / 256;   // 16-byte units of a V tile staged per thread
+  __shared__ __attribute__((aligned(16))) bf16 vt[2][2][32 * D];   // [buffer][hi, lo]
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n32 = lane & 31, hf = lane >> 5;
+  const Tile3 t = tile3((Nq + 127) / 128, 1);
+  const long bh = t.z;
+  const int row = t.x * 128 + 32 * w + n32;
+  const bool rvalid = row < Nq;
+  const float* V = vc + bh * (long)Nk * D;
+  const int nch = (Nk + 31) / 32;
+
+  // Every load below is unconditional (addresses clamped into the arrays):
+  // the compiler can then count them and waits only for the oldest (its waits
+  // for loads under a branch drain every load in flight, the S loads issued
+  // two chunks ahead included). Clamped rows and keys are masked or meet P = 0.
+  const int kmax = (Nk - 1) & ~3;   // last float4 of a row of S that starts below Nk
+  const float* srow = s + (bh * Nq + min(row, Nq - 1)) * (long)ld;
+  const float l2 = lse[bh * Nq + min(row, Nq - 1)] * kLog2e;
+  // S of chunk c for this lane: [s2][half] = keys 32c + 16 s2 + 8 half + 4hf .. +3.
+  auto load_s = [&](float4 (&x)[2][2], int c) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        x[s2][h] = *reinterpret_cast<const float4*>(srow + min(32 * c + 16 * s2 + 8 * h + 4 * hf, kmax));
+  };
+  // P^T fragments (head and tail) of chunk c from its S values; keys beyond
+  // Nk (only in the last chunk) give 0.
+  auto make_p = [&](const float4 (&x)[2][2], int c, bf16x8 (&ph)[2], bf16x8 (&pl)[2]) {
+    const bool full = 32 * c + 32 <= Nk;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = 32 * c + 16 * s2 + 8 * h + 4 * hf;
+        const float v[4] = {x[s2][h].x, x[s2][h].y, x[s2][h].z, x[s2][h].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(v[e], kLog2e, -l2));
+          if (!full && kk + e >= Nk) pv = 0.f;
+          const bf16 hi = (bf16)pv;
+          ph[s2][4 * h + e] = hi;
+          pl[s2][4 * h + e] = (bf16)(pv - (float)hi);
+        }
+      }
+  };
+  // V_c rows of chunk c, unit p = j*256 + tid of a tile: row kappa = p / U,
+  // channels 8(p % U) .. +7; rows beyond Nk repeat the last one (their P is 0).
+  float4 vr[UPT][2];
+  auto load_v = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      const int p = j * 256 + tid, kappa = p / U, u = p % U, key = min(32 * c + kappa, Nk - 1);
+      const float4* src = reinterpret_cast<const float4*>(V + (long)key * D + 8 * u);
+      vr[j][0] = src[0];
+      vr[j][1] = src[1];
+    }
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      const int p = j * 256 + tid, kappa = p / U, u = p % U;
+      const float x[8] = {vr[j][0].x, vr[j][0].y, vr[j][0].z, vr[j][0].w,
+                          vr[j][1].x, vr[j][1].y, vr[j][1].z, vr[j][1].w};
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = (bf16)x[e];
+        lo[e] = (bf16)(x[e] - (float)hi[e]);
+      }
+      const int at = (kappa * U + (u ^ kswz<U>(kappa))) * 8;
+      *reinterpret_cast<bf16x8*>(&vt[buf][0][at]) = hi;
+      *reinterpret_cast<bf16x8*>(&vt[buf][1][at]) = lo;
+    }
+  };
+  uint32_t voffs[MB][2][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, voffs[mb][s2]);
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
+  float4 sa[2][2], sb[2][2];
+  load_s(sa, 0);
+  load_s(sb, min(1, nch - 1));
+  load_v(0);
+  store_v(0);
+  load_v(min(1, nch - 1));
+  __syncthreads();
+  // Chunk c: P from its S (loaded two chunks ago), the next-but-one chunk's S
+  // into the same registers, the MFMAs on tiles c % 2, then tiles (c+1) % 2
+  // (last read in chunk c - 1, which ended with a barrier) receive chunk
+  // c + 1 and the loads of chunk c + 2's V_c go out (chunk indices past the
+  // end are clamped: those loads are never used).
+  auto step = [&](auto B, float4 (&x)[2][2], int c) {
+    constexpr int buf = decltype(B)::value;
+    bf16x8 ph[2], pl[2];
+    make_p(x, c, ph, pl);
+    load_s(x, min(c + 2, nch - 1));
+    const char* th = reinterpret_cast<const char*>(vt[buf][0]);
+    const char* tl = reinterpret_cast<const char*>(vt[buf][1]);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 ah = rowt_frag(th, voffs[mb][s2][0], voffs[mb][s2][1]);
+        const bf16x8 al = rowt_frag(tl, voffs[mb][s2][0], voffs[mb][s2][1]);
+        acc[mb] = mfma32_bf16(al, ph[s2], acc[mb]);
+        acc[mb] = mfma32_bf16(ah, pl[s2], acc[mb]);
+        acc[mb] = mfma32_bf16(ah, ph[s2], acc[mb]);
+      }
+    store_v(buf ^ 1);
+    load_v(min(c + 2, nch - 1));
+    __syncthreads();
+  };
+  // An even number of steps, none of them under a branch (so the compiler
+  // keeps every load where it is issued): with an odd chunk count the last
+  // step is chunk nch, all of whose keys lie beyond Nk (P = 0).
+  for (int c = 0; c < nch; c += 2) {
+    step(std::integral_constant<int, 0>{}, sa, c);
+    step(std::integral_constant<int, 1>{}, sb, c + 1);
+  }
+  if (!rvalid) return;
+  // acc[mb][jj] = O_c^T[channel 32mb + 8(jj/4) + 4hf + jj%4][row]: four
+  // consecutive channels per float4.
+  float* orow = oc + (bh * Nq + row) * (long)D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(orow + 32 * mb + 8 * q + 4 * hf) =
+          make_float4(acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]);
+}
+
 int coarse_ld(int Nk) { return (Nk + 3) & ~3; }
 
 // One wave per query cube; each row has Nk key-block logits.
@@ -648,7 +813,15 @@ hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, cons
     hipLaunchKernelGGL(coarse_rows_stream_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream, s_scratch,
                        lse, idx, len, rows, Nk, ld, L.topk, L.stride);
   }
-  launch_gemm<false, true>(L, s_scratch, lse, vc, oc, Nq, Nk, 1.0f);
+  if (L.bf16) {
+    const dim3 grid((unsigned)((Nq + 127) / 128 * L.BH));
+    if (L.D == 64)
+      hipLaunchKernelGGL((coarse_pv_bf16_kernel<64>), grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nq, Nk, ld);
+    else
+      hipLaunchKernelGGL((coarse_pv_bf16_kernel<128>), grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nq, Nk, ld);
+  } else {
+    launch_gemm<false, true>(L, s_scratch, lse, vc, oc, Nq, Nk, 1.0f);
+  }
   return hipGetLastError();
 }
 

@@ -208,7 +208,10 @@ vsa_status vsa_pool(const vsa_problem* p, const void* q, const void* k, const vo
  * key design 1, and the fused softmax + top-K + mask-to-index kernel of the
  * notes' training section). With topk == 0 idx / len are not touched (may be
  * NULL). S_c (fp32, Nc x Nk per (b, h)) lives in the workspace
- * (ws_bytes >= vsa_workspace_bytes(p, 0)). Requires Nc, Nk <= vsa_max_cubes(). */
+ * (ws_bytes >= vsa_workspace_bytes(p, 0)). Requires Nc, Nk <= vsa_max_cubes().
+ * The logits, LSE and selection are computed in fp32; for bf16 problems the
+ * product A_c V_c runs on bf16 matrix cores with each fp32 operand split into
+ * a bf16 head and tail (relative error at most 3 * 2^-16 per term). */
 vsa_status vsa_coarse(const vsa_problem* p, const float* q_c, const float* k_c, const float* v_c,
                       float* o_c, float* lse_c, int32_t* idx, int32_t* len, void* workspace,
                       size_t ws_bytes, void* stream);
