@@ -545,7 +545,7 @@ def main() -> int:
                             "TFLOP_per_s": round(coarse_flop / (stage_ms[1] * 1e-3) / 1e12, 2),
                             "frac": round(coarse_flop / (stage_ms[1] * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
                             "traffic": {n: stage_traffic(w.name, n)
-                                        for n in ("coarse_scores", "coarse_rows", "coarse_gemm (O_c)")}},
+                                        for n in ("coarse_scores", "coarse_rows", "coarse_pv (O_c)")}},
             "fine_combine": {"ms": round(stage_ms[2], 4), "bound": "mfma", "flop": fine_flop,
                              "TFLOP_per_s": round(achieved, 2), "frac": round(achieved / PEAK_BF16_TFLOPS, 4)},
         },

@@ -121,6 +121,108 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
     }
 }
 
+// The coarse logits of a bf16 problem on bf16 MFMAs, to fp32 accuracy: every
+// fp32 operand x is split exactly into three bf16 pieces, x = hi + mid + lo
+// (hi = bf16(x), mid = bf16(x - hi), lo = x - hi - mid, which needs no more
+// than bf16's 8 significant bits), and the dot product over channels is
+// formed from the six piece products whose size exceeds 2^-24 of the whole:
+// hi.hi into one accumulator, hi.mid, mid.hi, hi.lo, lo.hi and mid.mid into a
+// second (each product of two bf16 values is exact in fp32), the two added at
+// the end. Against an fp32 dot product this adds at most 2^-23 of sum |q||k|
+// per channel for the dropped products (mid.lo, lo.mid, lo.lo) and the
+// rounding of the second accumulator, whose partial sums stay below 2^-7 of
+// the first's scale: the error bound grows by under 10% (the oracle's logit
+// error bound counts this arithmetic). Workgroup of four waves per 128 x 128
+// tile of S, a wave per 64 x 64 quarter as four 32 x 32 MFMA tiles; a lane
+// reads its own row of Q_c (A operand) and of K_c (B operand) 8 channels per
+// k-step, no LDS. Rows past Nq / Nk are clamped for the loads (unconditional,
+// so the compiler waits only for the oldest) and not stored.
+__device__ __forceinline__ void split3(const float4& x0, const float4& x1, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+  const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (bf16)x[e];
+    const float r1 = x[e] - (float)hi[e];
+    mid[e] = (bf16)r1;
+    lo[e] = (bf16)(r1 - (float)mid[e]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void coarse_scores_split_kernel(const float* __restrict__ qc,
+                                                                    const float* __restrict__ kc,
+                                                                    float* __restrict__ s, int Nq, int Nk, int ld,
+                                                                    float scale) {
+  constexpr int KS = D / 16;   // k-steps of 16 channels
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
+  const Tile3 t = tile3((Nk + 127) / 128, (Nq + 127) / 128);
+  const long bh = t.z;
+  const int m0 = t.y * 128 + (w >> 1) * 64, n0 = t.x * 128 + (w & 1) * 64;
+  if (m0 >= Nq || n0 >= Nk) return;   // wave-uniform; no barrier in this kernel
+  // This lane's rows: A[i] = Q_c row m0 + 32i + n32, B[j] = K_c row n0 + 32j + n32,
+  // channels 16ks + 8hf .. +7 in k-step ks (the 32x32x16 operand layout).
+  const float* A[2];
+  const float* B[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    A[i] = qc + (bh * Nq + min(m0 + 32 * i + n32, Nq - 1)) * (long)D + 8 * hf;
+    B[i] = kc + (bh * Nk + min(n0 + 32 * i + n32, Nk - 1)) * (long)D + 8 * hf;
+  }
+  f32x16 hh[2][2], xx[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) hh[i][j][e] = xx[i][j][e] = 0.f;
+  float4 ra[2][2], rb[2][2];
+  auto load = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ra[i][0] = *reinterpret_cast<const float4*>(A[i] + 16 * ks);
+      ra[i][1] = *reinterpret_cast<const float4*>(A[i] + 16 * ks + 4);
+      rb[i][0] = *reinterpret_cast<const float4*>(B[i] + 16 * ks);
+      rb[i][1] = *reinterpret_cast<const float4*>(B[i] + 16 * ks + 4);
+    }
+  };
+  load(0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 ah[2], am[2], al[2], bh8[2], bm[2], bl[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      split3(ra[i][0], ra[i][1], ah[i], am[i], al[i]);
+      split3(rb[i][0], rb[i][1], bh8[i], bm[i], bl[i]);
+    }
+    if (ks + 1 < KS) load(ks + 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        xx[i][j] = mfma32_bf16(am[i], bm[j], xx[i][j]);
+        xx[i][j] = mfma32_bf16(al[i], bh8[j], xx[i][j]);
+        xx[i][j] = mfma32_bf16(ah[i], bl[j], xx[i][j]);
+        xx[i][j] = mfma32_bf16(am[i], bh8[j], xx[i][j]);
+        xx[i][j] = mfma32_bf16(ah[i], bm[j], xx[i][j]);
+        hh[i][j] = mfma32_bf16(ah[i], bh8[j], hh[i][j]);
+      }
+  }
+  // hh[i][j][jj] + xx[i][j][jj] = S[row m0 + 32i + 8(jj/4) + 4hf + jj%4][col n0 + 32j + n32] / scale.
+  float* S = s + bh * (long)Nq * ld;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + 32 * j + n32;
+    if (col >= Nk) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int row = m0 + 32 * i + 8 * (jj >> 2) + 4 * hf + (jj & 3);
+        if (row < Nq) S[(long)row * ld + col] = (hh[i][j][jj] + xx[i][j][jj]) * scale;
+      }
+  }
+}
+
 // C[bh][i][:] = scale * sum_j A[i][j] B[j][:] for i < R, j < Kd, with B
 // [Kd][D] and A = M (M is R x Kd) or A = M^T with TRANS_A (M is Kd x R);
 // M is fp32 with row pitch ld. With EXP A[i][j] = exp(M[i][j] - lse[i]) (the
@@ -798,7 +900,13 @@ hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, cons
                          float* lse, int32_t* idx, int32_t* len, float* s_scratch) {
   const int Nq = L.g.Nc, Nk = L.gk.Nc, ld = coarse_ld(Nk);
   const dim3 tiles((unsigned)((Nk + 127) / 128 * ((Nq + 127) / 128) * L.BH)), block(256);
-  if (L.D == 64)
+  if (L.bf16 && L.D == 64)
+    hipLaunchKernelGGL((coarse_scores_split_kernel<64>), tiles, block, 0, L.stream, qc, kc, s_scratch, Nq, Nk, ld,
+                       L.scale);
+  else if (L.bf16)
+    hipLaunchKernelGGL((coarse_scores_split_kernel<128>), tiles, block, 0, L.stream, qc, kc, s_scratch, Nq, Nk, ld,
+                       L.scale);
+  else if (L.D == 64)
     hipLaunchKernelGGL((coarse_scores_kernel<64>), tiles, block, 0, L.stream, qc, kc, s_scratch, Nq, Nk, ld,
                        L.scale);
   else

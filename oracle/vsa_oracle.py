@@ -242,16 +242,31 @@ def logit_error_bound(qt: np.ndarray, kt: np.ndarray, scale: float, sig_bits: in
     """Per-row bound on |fp32 coarse logit - exact logit| for one (b, h).
 
     The fp32 path pools B inputs (error bounded by ``_pool_error_bound``),
-    forms the d-term dot product of the pooled rows (error at most gamma_d
-    times the sum of absolute products, any order: the standard forward error
-    bound of recursive summation) and multiplies by the fp32 scale (a few
-    unit roundings of |S|). Returns tau[i] = max_j bound(i, j); two logits of
-    a row compare the same way in fp32 and exactly whenever they differ by
-    more than 2*tau[i].
+    forms the d-term dot product x . y of the pooled rows and multiplies by
+    the fp32 scale (a few unit roundings of |S|). The dot product is formed
+    in one of two ways:
+    * as an fp32 dot product: error at most gamma_d * sum |x||y|, any order
+      (the standard forward error bound of recursive summation);
+    * on bf16 matrix units, from the exact split of every pooled value into
+      three bf16 pieces x = hi + mid + lo (|hi| <= (1+2^-8)|x|,
+      |mid| <= 2^-8 (1+2^-8)|x|, |lo| <= 2^-16 |x|; bf16 keeps 8 significant
+      bits): the products hi*hi summed in one fp32 accumulator, hi*mid,
+      mid*hi, hi*lo, lo*hi and mid*mid (each exact in fp32) in a second, the
+      two added. Its error is at most gamma_d (1+2^-8)^2 for the first sum,
+      gamma_5d (2^-7 + 3*2^-16)(1+2^-8)^2 for the second, one rounding of the
+      final addition and 2^-23 (1+2^-8) + 2^-32 for the dropped products
+      (mid*lo, lo*mid, lo*lo), all times sum |x||y|: a larger factor than
+      gamma_d, so it bounds both forms and is the one used.
+    Returns tau[i] = max_j bound(i, j); two logits of a row compare the same
+    way in fp32 and exactly whenever they differ by more than 2*tau[i].
     """
     u = 2.0 ** -24
     d = qt.shape[-1]
-    gd = d * u / (1 - d * u)
+    gamma = lambda n: n * u / (1 - n * u)
+    r = (1 + 2.0 ** -8) ** 2
+    cross = (2.0 ** -7 + 3 * 2.0 ** -16) * r
+    gd = (gamma(d) * r + gamma(5 * d) * cross + u * (1 + gamma(5 * d)) * (r + cross)
+          + 2.0 ** -23 * (1 + 2.0 ** -8) + 2.0 ** -32)
     qc, kc = np.abs(pool(qt, pool_mode)), np.abs(pool(kt, pool_mode))
     if pool_mode == "max":   # a maximum of exact values is exact
         eq, ek = np.zeros_like(qc), np.zeros_like(kc)

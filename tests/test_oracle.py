@@ -211,6 +211,49 @@ def test_logit_error_bound_covers_fp32_pool_and_dot():
     assert np.all(tau < 1e-3)
 
 
+def _bf16_round(x32):
+    """Round fp32 values to the nearest bf16 (ties to even), kept as fp32."""
+    b = x32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("name", ["C2", "C3"])
+def test_logit_error_bound_covers_split_bf16_products(name):
+    """The logits may be formed on bf16 matrix units from an exact split of
+    each pooled fp32 value into three bf16 pieces, six piece products in two
+    fp32 accumulators (hi*hi; hi*mid, mid*hi, hi*lo, lo*hi, mid*mid): the
+    split is exact and an fp32 emulation of that arithmetic stays inside the
+    bound; dropping the second accumulator would not."""
+    w = WL.get(name)
+    x = WL.make_inputs(name, heads=[0])
+    qt, kt = O.tile(x["q"][0, 0].astype(np.float64)), O.tile(x["k"][0, 0].astype(np.float64))
+    s = 1 / np.sqrt(w.head_dim)
+    tau = O.logit_error_bound(qt, kt, s)
+    exact = s * (O.pool(qt) @ O.pool(kt).T)
+
+    def split(v):
+        hi = _bf16_round(v)
+        r1 = (v - hi).astype(np.float32)
+        mid = _bf16_round(r1)
+        lo = (r1 - mid).astype(np.float32)
+        assert np.array_equal(_bf16_round(lo), lo)
+        assert np.array_equal(hi.astype(np.float64) + mid + lo, v.astype(np.float64))
+        return hi, mid, lo
+
+    qc32 = qt.astype(np.float32).sum(1, dtype=np.float32) / np.float32(qt.shape[1])
+    kc32 = kt.astype(np.float32).sum(1, dtype=np.float32) / np.float32(kt.shape[1])
+    (qh, qm, ql), (kh, km, kl) = split(qc32), split(kc32)
+    acc_hh = (qh @ kh.T).astype(np.float32)
+    acc_x = np.zeros_like(acc_hh)
+    for a_, b_ in ((qh, km), (qm, kh), (qh, kl), (ql, kh), (qm, km)):
+        acc_x = (acc_x + (a_ @ b_.T).astype(np.float32)).astype(np.float32)
+    s32 = ((acc_hh + acc_x).astype(np.float32) * np.float32(s)).astype(np.float32)
+    assert np.all(np.abs(s32 - exact).max(1) <= tau)
+    hh_only = (acc_hh * np.float32(s)).astype(np.float32)
+    assert np.any(np.abs(hh_only - exact).max(1) > tau)
+
+
 # --------------------------------------------------------------- step 4: fine
 def test_fine_all_blocks_is_full_attention():
     """With every cube listed the fine stage is textbook attention (SDPA, float64)."""
