@@ -742,11 +742,13 @@ static void launch_gemm(const Launch& L, const float* m, const float* lse, const
 // directly, in the key order those reads deliver (for k-step s2, slot e is
 // key 16 s2 + 8(e/4) + 4hf + e%4: two float4 loads). S loads run two chunks
 // ahead, V_c one.
-template <int D>
+// The same kernel without EXP forms C = scale * M B for any fp32 M (the
+// coarse backward's dQ_c = s dS K_c): M takes the place of P, B of V_c.
+template <int D, bool EXP>
 __global__ __launch_bounds__(256, 2) void coarse_pv_bf16_kernel(const float* __restrict__ s,
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ vc, float* __restrict__ oc,
-                                                               int Nq, int Nk, int ld) {
+                                                               int Nq, int Nk, int ld, float scale) {
   using G = ChunkGeom<D>;
   constexpr int MB = G::MB, U = G::U;
   constexpr int UPT = 32 * U / 256;   // 16-byte units of a V tile staged per thread
@@ -765,7 +767,7 @@ __global__ __launch_bounds__(256, 2) void coarse_pv_bf16_kernel(const float* __r
   // two chunks ahead included). Clamped rows and keys are masked or meet P = 0.
   const int kmax = (Nk - 1) & ~3;   // last float4 of a row of S that starts below Nk
   const float* srow = s + (bh * Nq + min(row, Nq - 1)) * (long)ld;
-  const float l2 = lse[bh * Nq + min(row, Nq - 1)] * kLog2e;
+  const float l2 = EXP ? lse[bh * Nq + min(row, Nq - 1)] * kLog2e : 0.f;
   // S of chunk c for this lane: [s2][half] = keys 32c + 16 s2 + 8 half + 4hf .. +3.
   auto load_s = [&](float4 (&x)[2][2], int c) {
 #pragma unroll
@@ -786,7 +788,7 @@ __global__ __launch_bounds__(256, 2) void coarse_pv_bf16_kernel(const float* __r
         const float v[4] = {x[s2][h].x, x[s2][h].y, x[s2][h].z, x[s2][h].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pv = __builtin_amdgcn_exp2f(fmaf(v[e], kLog2e, -l2));
+          float pv = EXP ? __builtin_amdgcn_exp2f(fmaf(v[e], kLog2e, -l2)) : v[e];
           if (!full && kk + e >= Nk) pv = 0.f;
           const bf16 hi = (bf16)pv;
           ph[s2][4 * h + e] = hi;
@@ -883,7 +885,8 @@ __global__ __launch_bounds__(256, 2) void coarse_pv_bf16_kernel(const float* __r
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       *reinterpret_cast<float4*>(orow + 32 * mb + 8 * q + 4 * hf) =
-          make_float4(acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]);
+          make_float4(acc[mb][4 * q] * scale, acc[mb][4 * q + 1] * scale, acc[mb][4 * q + 2] * scale,
+                      acc[mb][4 * q + 3] * scale);
 }
 
 int coarse_ld(int Nk) { return (Nk + 3) & ~3; }
@@ -924,9 +927,11 @@ hipError_t launch_coarse(const Launch& L, const float* qc, const float* kc, cons
   if (L.bf16) {
     const dim3 grid((unsigned)((Nq + 127) / 128 * L.BH));
     if (L.D == 64)
-      hipLaunchKernelGGL((coarse_pv_bf16_kernel<64>), grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nq, Nk, ld);
+      hipLaunchKernelGGL((coarse_pv_bf16_kernel<64, true>), grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nq,
+                         Nk, ld, 1.0f);
     else
-      hipLaunchKernelGGL((coarse_pv_bf16_kernel<128>), grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nq, Nk, ld);
+      hipLaunchKernelGGL((coarse_pv_bf16_kernel<128, true>), grid, block, 0, L.stream, s_scratch, lse, vc, oc, Nq,
+                         Nk, ld, 1.0f);
   } else {
     launch_gemm<false, true>(L, s_scratch, lse, vc, oc, Nq, Nk, 1.0f);
   }
@@ -995,22 +1000,267 @@ __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_kernel(const float* __r
     }
 }
 
+// P and dS of a bf16 problem: S = s Q_c K_c^T and dP = dO_c V_c^T each from
+// the exact three-piece split of their fp32 operands (six piece products in
+// two accumulators, as the forward's logits: fp32-level accuracy), then
+// P = exp(S - LSE_c) and dS = P (dP - delta) elementwise. A workgroup of four
+// waves owns a 128 x 64 tile, wave w the rows 32w .. 32w+31 as two 32 x 32
+// MFMA tiles; loads are unconditional (rows clamped) and one k-step ahead.
+template <int D>
+__global__ __launch_bounds__(256, 2) void coarse_bwd_pds_split_kernel(
+    const float* __restrict__ qc, const float* __restrict__ kc, const float* __restrict__ vc,
+    const float* __restrict__ doc, const float* __restrict__ lse, const float* __restrict__ dc,
+    float* __restrict__ pbuf, float* __restrict__ dsbuf, int Nq, int Nk, int ld, float scale) {
+  constexpr int KS = D / 16;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
+  const Tile3 t = tile3((Nk + 63) / 64, (Nq + 127) / 128);
+  const long bh = t.z;
+  const int m0 = t.y * 128 + 32 * w, n0 = t.x * 64;
+  if (m0 >= Nq) return;   // wave-uniform; no barrier in this kernel
+  // out[j] = X Y^T on rows m0 .. m0+31 of X and n0 + 32j .. +31 of Y.
+  auto nt_split = [&](const float* X, const float* Y, f32x16 (&out)[2]) {
+    const float* A = X + (bh * Nq + min(m0 + n32, Nq - 1)) * (long)D + 8 * hf;
+    const float* B[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) B[j] = Y + (bh * Nk + min(n0 + 32 * j + n32, Nk - 1)) * (long)D + 8 * hf;
+    f32x16 hh[2], xx[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) hh[j][e] = xx[j][e] = 0.f;
+    float4 ra[2], rb[2][2];
+    auto load = [&](int ks) {
+      ra[0] = *reinterpret_cast<const float4*>(A + 16 * ks);
+      ra[1] = *reinterpret_cast<const float4*>(A + 16 * ks + 4);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        rb[j][0] = *reinterpret_cast<const float4*>(B[j] + 16 * ks);
+        rb[j][1] = *reinterpret_cast<const float4*>(B[j] + 16 * ks + 4);
+      }
+    };
+    load(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 ah, am, al, bh8[2], bm[2], bl[2];
+      split3(ra[0], ra[1], ah, am, al);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) split3(rb[j][0], rb[j][1], bh8[j], bm[j], bl[j]);
+      if (ks + 1 < KS) load(ks + 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        xx[j] = mfma32_bf16(am, bm[j], xx[j]);
+        xx[j] = mfma32_bf16(al, bh8[j], xx[j]);
+        xx[j] = mfma32_bf16(ah, bl[j], xx[j]);
+        xx[j] = mfma32_bf16(am, bh8[j], xx[j]);
+        xx[j] = mfma32_bf16(ah, bm[j], xx[j]);
+        hh[j] = mfma32_bf16(ah, bh8[j], hh[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) out[j] = hh[j] + xx[j];
+  };
+  f32x16 sv[2], dp[2];
+  nt_split(qc, kc, sv);
+  __builtin_amdgcn_sched_barrier(0);
+  nt_split(doc, vc, dp);
+  // sv[j][jj], dp[j][jj]: row m0 + 8(jj/4) + 4hf + jj%4, column n0 + 32j + n32.
+  float* P = pbuf + bh * (long)Nq * ld;
+  float* DS = dsbuf + bh * (long)Nq * ld;
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const int row = m0 + 8 * (jj >> 2) + 4 * hf + (jj & 3);
+    if (row >= Nq) continue;
+    const float l = lse[bh * Nq + row], dd = dc[bh * Nq + row];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + 32 * j + n32;
+      if (col >= Nk) continue;
+      const float pv = __expf(sv[j][jj] * scale - l);
+      P[(long)row * ld + col] = pv;
+      DS[(long)row * ld + col] = pv * (dp[j][jj] - dd);
+    }
+  }
+}
+
+// C = scale * M^T B of a bf16 problem (the coarse backward's dK_c = s dS^T Q_c
+// and dV_c = P^T dO_c): M is Kd x R with row pitch ld, B is Kd x D, C is
+// R x D, all fp32. The products run on bf16 MFMAs with the head / tail split
+// of M and B (three products, each term within 3 * 2^-16 of exact). A
+// workgroup of four waves owns 128 rows of C, wave w the rows 32w .. 32w+31,
+// in the transposed form C^T (D x 32) += B_chunk^T M_chunk over chunks of 32
+// k: the chunk's rows of M (the workgroup's 128 columns) and of B (D columns)
+// are split into bf16 row tiles in LDS, double buffered with one barrier per
+// chunk, and both operands come from them by LDS transpose reads (rows = k;
+// both take the same order of k). Loads are unconditional: rows past Kd are
+// clamped and their M values zeroed, columns past the row clamped (they only
+// reach rows of C that are not stored).
+template <int D>
+__global__ __launch_bounds__(256, 2) void coarse_tn_bf16_kernel(const float* __restrict__ m,
+                                                               const float* __restrict__ b, float* __restrict__ c,
+                                                               int R, int Kd, int ld, float scale) {
+  using G = ChunkGeom<D>;
+  constexpr int MB = G::MB, U = G::U, UM = 16;   // M tiles: 128 columns
+  constexpr int UPTB = 32 * U / 256, UPTM = 32 * UM / 256;
+  __shared__ __attribute__((aligned(16))) bf16 mt[2][2][32 * 128];   // [buffer][hi, lo]
+  __shared__ __attribute__((aligned(16))) bf16 bt[2][2][32 * D];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n32 = lane & 31, hf = lane >> 5;
+  const Tile3 t = tile3((R + 127) / 128, 1);
+  const long bh = t.z;
+  const int r0 = t.x * 128;
+  const float* Mh = m + bh * (long)Kd * ld;
+  const float* Bh = b + bh * (long)Kd * D;
+  const int nch = (Kd + 31) / 32;
+  float4 vm[UPTM][2], vb[UPTB][2];
+  auto load = [&](int ch) {
+#pragma unroll
+    for (int j = 0; j < UPTM; ++j) {
+      const int p = j * 256 + tid, kappa = p / UM, u = p % UM, k = 32 * ch + kappa;
+      const float* src = Mh + (long)min(k, Kd - 1) * ld;
+      const int x0 = min(r0 + 8 * u, ld - 4), x1 = min(r0 + 8 * u + 4, ld - 4);
+      const float4 a0 = *reinterpret_cast<const float4*>(src + x0);
+      const float4 a1 = *reinterpret_cast<const float4*>(src + x1);
+      const bool in = k < Kd;
+      vm[j][0] = in ? a0 : make_float4(0.f, 0.f, 0.f, 0.f);
+      vm[j][1] = in ? a1 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < UPTB; ++j) {
+      const int p = j * 256 + tid, kappa = p / U, u = p % U;
+      const float4* src = reinterpret_cast<const float4*>(Bh + (long)min(32 * ch + kappa, Kd - 1) * D + 8 * u);
+      vb[j][0] = src[0];
+      vb[j][1] = src[1];
+    }
+  };
+  auto split2 = [](const float4 (&x)[2], bf16x8& hi, bf16x8& lo) {
+    const float v[8] = {x[0].x, x[0].y, x[0].z, x[0].w, x[1].x, x[1].y, x[1].z, x[1].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = (bf16)v[e];
+      lo[e] = (bf16)(v[e] - (float)hi[e]);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < UPTM; ++j) {
+      const int p = j * 256 + tid, kappa = p / UM, u = p % UM;
+      bf16x8 hi, lo;
+      split2(vm[j], hi, lo);
+      const int at = (kappa * UM + (u ^ kswz<UM>(kappa))) * 8;
+      *reinterpret_cast<bf16x8*>(&mt[buf][0][at]) = hi;
+      *reinterpret_cast<bf16x8*>(&mt[buf][1][at]) = lo;
+    }
+#pragma unroll
+    for (int j = 0; j < UPTB; ++j) {
+      const int p = j * 256 + tid, kappa = p / U, u = p % U;
+      bf16x8 hi, lo;
+      split2(vb[j], hi, lo);
+      const int at = (kappa * U + (u ^ kswz<U>(kappa))) * 8;
+      *reinterpret_cast<bf16x8*>(&bt[buf][0][at]) = hi;
+      *reinterpret_cast<bf16x8*>(&bt[buf][1][at]) = lo;
+    }
+  };
+  uint32_t boffs[MB][2][2], moffs[2][2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    rowt_offsets<128>(lane, w, s2, moffs[s2]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) rowt_offsets<D>(lane, mb, s2, boffs[mb][s2]);
+  }
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
+  load(0);
+  store(0);
+  load(1);
+  __syncthreads();
+  // Chunk ch: the MFMAs on tiles ch % 2, then tiles (ch+1) % 2 (last read in
+  // chunk ch - 1, which ended with a barrier) receive chunk ch + 1 and the
+  // loads of chunk ch + 2 go out. An even number of steps, none under a
+  // branch; chunks past the last one load zeroed rows of M (so a step past
+  // the last chunk adds nothing).
+  auto step = [&](auto BUF, int ch) {
+    constexpr int buf = decltype(BUF)::value;
+    const char* mh = reinterpret_cast<const char*>(mt[buf][0]);
+    const char* ml = reinterpret_cast<const char*>(mt[buf][1]);
+    const char* th = reinterpret_cast<const char*>(bt[buf][0]);
+    const char* tl = reinterpret_cast<const char*>(bt[buf][1]);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 fmh = rowt_frag(mh, moffs[s2][0], moffs[s2][1]);
+      const bf16x8 fml = rowt_frag(ml, moffs[s2][0], moffs[s2][1]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 fbh = rowt_frag(th, boffs[mb][s2][0], boffs[mb][s2][1]);
+        const bf16x8 fbl = rowt_frag(tl, boffs[mb][s2][0], boffs[mb][s2][1]);
+        acc[mb] = mfma32_bf16(fbl, fmh, acc[mb]);
+        acc[mb] = mfma32_bf16(fbh, fml, acc[mb]);
+        acc[mb] = mfma32_bf16(fbh, fmh, acc[mb]);
+      }
+    }
+    store(buf ^ 1);
+    load(ch + 2);
+    __syncthreads();
+  };
+  for (int ch = 0; ch < nch; ch += 2) {
+    step(std::integral_constant<int, 0>{}, ch);
+    step(std::integral_constant<int, 1>{}, ch + 1);
+  }
+  const int row = r0 + 32 * w + n32;
+  if (row >= R) return;
+  // acc[mb][jj] = C^T[channel 32mb + 8(jj/4) + 4hf + jj%4][row].
+  float* crow = c + (bh * R + row) * (long)D;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(crow + 32 * mb + 8 * q + 4 * hf) =
+          make_float4(acc[mb][4 * q] * scale, acc[mb][4 * q + 1] * scale, acc[mb][4 * q + 2] * scale,
+                      acc[mb][4 * q + 3] * scale);
+}
+
 hipError_t launch_coarse_bwd(const Launch& L, const float* qc, const float* kc, const float* vc,
                              const float* oc, const float* lse, const float* doc, float* dqc, float* dkc,
                              float* dvc, float* ds_scratch, float* p_scratch, float* dc_scratch) {
   const int Nq = L.g.Nc, Nk = L.gk.Nc, ld = coarse_ld(Nk);
   const long rows = (long)L.BH * Nq;
   const dim3 tiles((unsigned)((Nk + 127) / 128 * ((Nq + 127) / 128) * L.BH));
+  const dim3 tiles64((unsigned)((Nk + 63) / 64 * ((Nq + 127) / 128) * L.BH));
   if (L.D == 64) {
     hipLaunchKernelGGL((coarse_bwd_delta_kernel<64>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream, doc,
                        oc, dc_scratch, rows);
-    hipLaunchKernelGGL((coarse_bwd_pds_kernel<64>), tiles, dim3(256), 0, L.stream, qc, kc, vc, doc, lse, dc_scratch,
-                       p_scratch, ds_scratch, Nq, Nk, ld, L.scale);
+    if (L.bf16)
+      hipLaunchKernelGGL((coarse_bwd_pds_split_kernel<64>), tiles64, dim3(256), 0, L.stream, qc, kc, vc, doc, lse,
+                         dc_scratch, p_scratch, ds_scratch, Nq, Nk, ld, L.scale);
+    else
+      hipLaunchKernelGGL((coarse_bwd_pds_kernel<64>), tiles, dim3(256), 0, L.stream, qc, kc, vc, doc, lse,
+                         dc_scratch, p_scratch, ds_scratch, Nq, Nk, ld, L.scale);
   } else {
     hipLaunchKernelGGL((coarse_bwd_delta_kernel<128>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, L.stream,
                        doc, oc, dc_scratch, rows);
-    hipLaunchKernelGGL((coarse_bwd_pds_kernel<128>), tiles, dim3(256), 0, L.stream, qc, kc, vc, doc, lse, dc_scratch,
-                       p_scratch, ds_scratch, Nq, Nk, ld, L.scale);
+    if (L.bf16)
+      hipLaunchKernelGGL((coarse_bwd_pds_split_kernel<128>), tiles64, dim3(256), 0, L.stream, qc, kc, vc, doc, lse,
+                         dc_scratch, p_scratch, ds_scratch, Nq, Nk, ld, L.scale);
+    else
+      hipLaunchKernelGGL((coarse_bwd_pds_kernel<128>), tiles, dim3(256), 0, L.stream, qc, kc, vc, doc, lse,
+                         dc_scratch, p_scratch, ds_scratch, Nq, Nk, ld, L.scale);
+  }
+  if (L.bf16) {
+    const dim3 block(256), gq((unsigned)((Nq + 127) / 128 * L.BH)), gk((unsigned)((Nk + 127) / 128 * L.BH));
+    if (L.D == 64) {
+      hipLaunchKernelGGL((coarse_pv_bf16_kernel<64, false>), gq, block, 0, L.stream, ds_scratch, nullptr, kc, dqc,
+                         Nq, Nk, ld, L.scale);
+      hipLaunchKernelGGL((coarse_tn_bf16_kernel<64>), gk, block, 0, L.stream, ds_scratch, qc, dkc, Nk, Nq, ld, L.scale);
+      hipLaunchKernelGGL((coarse_tn_bf16_kernel<64>), gk, block, 0, L.stream, p_scratch, doc, dvc, Nk, Nq, ld, 1.0f);
+    } else {
+      hipLaunchKernelGGL((coarse_pv_bf16_kernel<128, false>), gq, block, 0, L.stream, ds_scratch, nullptr, kc, dqc,
+                         Nq, Nk, ld, L.scale);
+      hipLaunchKernelGGL((coarse_tn_bf16_kernel<128>), gk, block, 0, L.stream, ds_scratch, qc, dkc, Nk, Nq, ld,
+                         L.scale);
+      hipLaunchKernelGGL((coarse_tn_bf16_kernel<128>), gk, block, 0, L.stream, p_scratch, doc, dvc, Nk, Nq, ld, 1.0f);
+    }
+    return hipGetLastError();
   }
   launch_gemm<false, false>(L, ds_scratch, nullptr, kc, dqc, Nq, Nk, L.scale);   // dQ_c = s dS K_c
   launch_gemm<true, false>(L, ds_scratch, nullptr, qc, dkc, Nk, Nq, L.scale);    // dK_c = s dS^T Q_c
