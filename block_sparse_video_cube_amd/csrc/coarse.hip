@@ -195,6 +195,9 @@ __global__ __launch_bounds__(256, 2) void coarse_scores_split_kernel(const float
       split3(rb[i][0], rb[i][1], bh8[i], bm[i], bl[i]);
     }
     if (ks + 1 < KS) load(ks + 1);
+    // The next step's loads go out here, a whole step of MFMAs ahead of their
+    // use (left alone, the scheduler sinks them next to it and waits there).
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1046,6 +1049,7 @@ __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_split_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) split3(rb[j][0], rb[j][1], bh8[j], bm[j], bl[j]);
       if (ks + 1 < KS) load(ks + 1);
+      __builtin_amdgcn_sched_barrier(0);   // keep the loads a step ahead of their use
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         xx[j] = mfma32_bf16(am, bm[j], xx[j]);
@@ -1059,6 +1063,17 @@ __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_split_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) out[j] = hh[j] + xx[j];
   };
+  // LSE and delta of this lane's rows m0 + 8q + 4hf + 0..3 (loaded first, so
+  // their latency hides behind the products; rows past Nq are clamped).
+  float lq[4][4], dq[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const long r = bh * Nq + min(m0 + 8 * q + 4 * hf + e, Nq - 1);
+      lq[q][e] = lse[r];
+      dq[q][e] = dc[r];
+    }
   f32x16 sv[2], dp[2];
   nt_split(qc, kc, sv);
   __builtin_amdgcn_sched_barrier(0);
@@ -1070,7 +1085,7 @@ __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_split_kernel(
   for (int jj = 0; jj < 16; ++jj) {
     const int row = m0 + 8 * (jj >> 2) + 4 * hf + (jj & 3);
     if (row >= Nq) continue;
-    const float l = lse[bh * Nq + row], dd = dc[bh * Nq + row];
+    const float l = lq[jj >> 2][jj & 3], dd = dq[jj >> 2][jj & 3];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + 32 * j + n32;
@@ -1199,6 +1214,9 @@ __global__ __launch_bounds__(256, 2) void coarse_tn_bf16_kernel(const float* __r
         acc[mb] = mfma32_bf16(fbh, fmh, acc[mb]);
       }
     }
+    // The stores wait for loads issued at the end of the previous step: keep
+    // them after this step's MFMAs so that those cover the load latency.
+    __builtin_amdgcn_sched_barrier(0);
     store(buf ^ 1);
     load(ch + 2);
     __syncthreads();
