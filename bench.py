@@ -499,6 +499,7 @@ def main() -> int:
     n_pairs = int(lens.sum().item())
     fine_flop = 4.0 * 64 * 64 * w.head_dim * n_pairs
     coarse_flop = 4.0 * w.B * w.heads * w.Nc * w.Nc * w.head_dim
+    coarse_mfma_flop = coarse_flop / 2 * (6 + 3) if w.dtype == "bf16" else coarse_flop
     esz = 2 if w.dtype == "bf16" else 4
     bh = w.B * w.heads
     raster = bh * w.N * w.head_dim
@@ -541,9 +542,15 @@ def main() -> int:
                      "cold_ms": round(pool_cold_ms, 4),
                      "cold_frac": round(pool_bytes / (pool_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": stage_traffic(w.name, "pool")},
-            "coarse_topk": {"ms": round(stage_ms[1], 4), "bound": "mfma_fp32", "flop": coarse_flop,
+            # The two coarse products in fp32 terms; bf16 problems run them on bf16 MFMAs with split
+            # fp32 operands (six piece products for the logits, three for O_c), counted separately.
+            "coarse_topk": {"ms": round(stage_ms[1], 4), "bound": "mfma", "flop": coarse_flop,
                             "TFLOP_per_s": round(coarse_flop / (stage_ms[1] * 1e-3) / 1e12, 2),
                             "frac": round(coarse_flop / (stage_ms[1] * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+                            "frac_of": "fp32 MFMA peak (fp32-equivalent work)",
+                            "mfma_flop_executed": coarse_mfma_flop,
+                            "frac_bf16_peak_executed": (round(coarse_mfma_flop / (stage_ms[1] * 1e-3) / 1e12
+                                                              / PEAK_BF16_TFLOPS, 4) if w.dtype == "bf16" else None),
                             "traffic": {n: stage_traffic(w.name, n)
                                         for n in ("coarse_scores", "coarse_rows", "coarse_pv (O_c)")}},
             "fine_combine": {"ms": round(stage_ms[2], 4), "bound": "mfma", "flop": fine_flop,
