@@ -132,11 +132,16 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
 // per channel for the dropped products (mid.lo, lo.mid, lo.lo) and the
 // rounding of the second accumulator, whose partial sums stay below 2^-7 of
 // the first's scale: the error bound grows by under 10% (the oracle's logit
-// error bound counts this arithmetic). Workgroup of four waves per 128 x 128
-// tile of S, a wave per 64 x 64 quarter as four 32 x 32 MFMA tiles; a lane
-// reads its own row of Q_c (A operand) and of K_c (B operand) 8 channels per
-// k-step, no LDS. Rows past Nq / Nk are clamped for the loads (unconditional,
-// so the compiler waits only for the oldest) and not stored.
+// error bound counts this arithmetic). A workgroup of four waves owns a
+// 128 x 128 tile of S, a wave a 64 x 64 quarter as four 32 x 32 MFMA tiles.
+// Per k-step of 16 channels the workgroup loads the tile's 128 rows of Q_c
+// and of K_c once (coalesced, a row's 64 bytes by four lanes), splits every
+// value once, and stages the pieces in LDS (double buffered, one barrier per
+// k-step), where each wave reads its MFMA fragments (a row's 8 channels,
+// 16 bytes, per lane). S leaves through LDS as whole 16-byte row units. The
+// vector memory path bounds this kernel (address and data units about 85%
+// busy with per-lane fragment loads and 4-byte stores), so both go in fewer,
+// wider accesses. Rows past Nq / Nk are clamped for the loads and not stored.
 __device__ __forceinline__ void split3(const float4& x0, const float4& x1, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
   const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
@@ -153,21 +158,60 @@ __global__ __launch_bounds__(256, 2) void coarse_scores_split_kernel(const float
                                                                     const float* __restrict__ kc,
                                                                     float* __restrict__ s, int Nq, int Nk, int ld,
                                                                     float scale) {
-  constexpr int KS = D / 16;   // k-steps of 16 channels
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
+  constexpr int KS = D / 16;        // k-steps of 16 channels
+  constexpr int PT = 128 * 16;      // bf16 per piece tile (128 rows x 16 channels)
+  constexpr int EP = 72;            // floats per row of a wave's 64 x 64 output tile in LDS
+  constexpr int STAGE_B = 2 * 2 * 3 * PT * 2, EPI_B = 4 * 64 * EP * 4;
+  __shared__ __attribute__((aligned(16))) char smem[STAGE_B > EPI_B ? STAGE_B : EPI_B];
+  bf16* stage = reinterpret_cast<bf16*>(smem);   // [buffer][A, B][hi, mid, lo][row][16 channels]
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n32 = lane & 31, hf = lane >> 5;
   const Tile3 t = tile3((Nk + 127) / 128, (Nq + 127) / 128);
   const long bh = t.z;
-  const int m0 = t.y * 128 + (w >> 1) * 64, n0 = t.x * 128 + (w & 1) * 64;
-  if (m0 >= Nq || n0 >= Nk) return;   // wave-uniform; no barrier in this kernel
-  // This lane's rows: A[i] = Q_c row m0 + 32i + n32, B[j] = K_c row n0 + 32j + n32,
-  // channels 16ks + 8hf .. +7 in k-step ks (the 32x32x16 operand layout).
-  const float* A[2];
-  const float* B[2];
+  const int M0 = t.y * 128, N0 = t.x * 128, wm = (w >> 1) * 64, wn = (w & 1) * 64;
+  // Staging role: float4 idx = tid + 256j of the k-step's tile, row idx / 4,
+  // channels 4 (idx % 4) .. +3.
+  const float* Ar[2];
+  const float* Br[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    A[i] = qc + (bh * Nq + min(m0 + 32 * i + n32, Nq - 1)) * (long)D + 8 * hf;
-    B[i] = kc + (bh * Nk + min(n0 + 32 * i + n32, Nk - 1)) * (long)D + 8 * hf;
+  for (int j = 0; j < 2; ++j) {
+    const int idx = tid + 256 * j, row = idx >> 2, q4 = idx & 3;
+    Ar[j] = qc + (bh * Nq + min(M0 + row, Nq - 1)) * (long)D + 4 * q4;
+    Br[j] = kc + (bh * Nk + min(N0 + row, Nk - 1)) * (long)D + 4 * q4;
   }
+  float4 ra[2], rb[2];
+  auto load = [&](int ks) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ra[j] = *reinterpret_cast<const float4*>(Ar[j] + 16 * ks);
+      rb[j] = *reinterpret_cast<const float4*>(Br[j] + 16 * ks);
+    }
+  };
+  auto put = [&](bf16* piece0, const float4& x, int idx) {
+    const float v[4] = {x.x, x.y, x.z, x.w};
+    bf16x4 hi, mid, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = (bf16)v[e];
+      const float r1 = v[e] - (float)hi[e];
+      mid[e] = (bf16)r1;
+      lo[e] = (bf16)(r1 - (float)mid[e]);
+    }
+    const int at = (idx >> 2) * 16 + (idx & 3) * 4;
+    *reinterpret_cast<bf16x4*>(piece0 + at) = hi;
+    *reinterpret_cast<bf16x4*>(piece0 + PT + at) = mid;
+    *reinterpret_cast<bf16x4*>(piece0 + 2 * PT + at) = lo;
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      put(stage + (buf * 2 + 0) * 3 * PT, ra[j], tid + 256 * j);
+      put(stage + (buf * 2 + 1) * 3 * PT, rb[j], tid + 256 * j);
+    }
+  };
+  // Fragment of piece p for the lane's row r of operand ab: channels 8hf .. +7.
+  auto frag = [&](int buf, int ab, int p, int r) {
+    return *reinterpret_cast<const bf16x8*>(stage + ((buf * 2 + ab) * 3 + p) * PT + r * 16 + 8 * hf);
+  };
   f32x16 hh[2][2], xx[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -175,29 +219,24 @@ __global__ __launch_bounds__(256, 2) void coarse_scores_split_kernel(const float
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) hh[i][j][e] = xx[i][j][e] = 0.f;
-  float4 ra[2][2], rb[2][2];
-  auto load = [&](int ks) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[i][0] = *reinterpret_cast<const float4*>(A[i] + 16 * ks);
-      ra[i][1] = *reinterpret_cast<const float4*>(A[i] + 16 * ks + 4);
-      rb[i][0] = *reinterpret_cast<const float4*>(B[i] + 16 * ks);
-      rb[i][1] = *reinterpret_cast<const float4*>(B[i] + 16 * ks + 4);
-    }
-  };
   load(0);
+  store(0);
+  if (KS > 1) load(1);
+  __syncthreads();
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
+    const int buf = ks & 1;
     bf16x8 ah[2], am[2], al[2], bh8[2], bm[2], bl[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      split3(ra[i][0], ra[i][1], ah[i], am[i], al[i]);
-      split3(rb[i][0], rb[i][1], bh8[i], bm[i], bl[i]);
+      const int ra_ = wm + 32 * i + n32, rb_ = wn + 32 * i + n32;
+      ah[i] = frag(buf, 0, 0, ra_);
+      am[i] = frag(buf, 0, 1, ra_);
+      al[i] = frag(buf, 0, 2, ra_);
+      bh8[i] = frag(buf, 1, 0, rb_);
+      bm[i] = frag(buf, 1, 1, rb_);
+      bl[i] = frag(buf, 1, 2, rb_);
     }
-    if (ks + 1 < KS) load(ks + 1);
-    // The next step's loads go out here, a whole step of MFMAs ahead of their
-    // use (left alone, the scheduler sinks them next to it and waits there).
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -209,20 +248,35 @@ __global__ __launch_bounds__(256, 2) void coarse_scores_split_kernel(const float
         xx[i][j] = mfma32_bf16(ah[i], bm[j], xx[i][j]);
         hh[i][j] = mfma32_bf16(ah[i], bh8[j], hh[i][j]);
       }
+    if (ks + 1 < KS) {
+      // Buffer buf ^ 1 was last read in step ks - 1, which ended with a
+      // barrier. Kept after the MFMAs, which cover the latency of its loads.
+      __builtin_amdgcn_sched_barrier(0);
+      store(buf ^ 1);
+      if (ks + 2 < KS) load(ks + 2);
+      __syncthreads();
+    }
   }
-  // hh[i][j][jj] + xx[i][j][jj] = S[row m0 + 32i + 8(jj/4) + 4hf + jj%4][col n0 + 32j + n32] / scale.
+  // hh[i][j][jj] + xx[i][j][jj] = S[row wm + 32i + 8(jj/4) + 4hf + jj%4][col wn + 32j + n32] / scale
+  // (within the tile). Through LDS (every wave is past its last staging read),
+  // then out as rows of 16-byte units.
+  __syncthreads();
+  float* et = reinterpret_cast<float*>(smem) + w * 64 * EP;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj)
+        et[(32 * i + 8 * (jj >> 2) + 4 * hf + (jj & 3)) * EP + 32 * j + n32] = (hh[i][j][jj] + xx[i][j][jj]) * scale;
+  wave_sync();
   float* S = s + bh * (long)Nq * ld;
+  const int c4 = 4 * (lane & 15), col = N0 + wn + c4;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + 32 * j + n32;
-    if (col >= Nk) continue;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const int row = m0 + 32 * i + 8 * (jj >> 2) + 4 * hf + (jj & 3);
-        if (row < Nq) S[(long)row * ld + col] = (hh[i][j][jj] + xx[i][j][jj]) * scale;
-      }
+  for (int st = 0; st < 16; ++st) {
+    const int r = 4 * st + (lane >> 4), row = M0 + wm + r;
+    const float4 v = *reinterpret_cast<const float4*>(et + r * EP + c4);
+    if (row < Nq && col < ld) *reinterpret_cast<float4*>(S + (long)row * ld + col) = v;   // ld % 4 == 0
   }
 }
 
