@@ -1062,48 +1062,98 @@ __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_kernel(const float* __r
 // two accumulators, as the forward's logits: fp32-level accuracy), then
 // P = exp(S - LSE_c) and dS = P (dP - delta) elementwise. A workgroup of four
 // waves owns a 128 x 64 tile, wave w the rows 32w .. 32w+31 as two 32 x 32
-// MFMA tiles; loads are unconditional (rows clamped) and one k-step ahead.
+// MFMA tiles. As in the scores kernel, each k-step's operand rows are loaded
+// once per workgroup (coalesced), split once and staged in LDS (double
+// buffered), and P and dS leave through LDS as 16-byte row units.
 template <int D>
 __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_split_kernel(
     const float* __restrict__ qc, const float* __restrict__ kc, const float* __restrict__ vc,
     const float* __restrict__ doc, const float* __restrict__ lse, const float* __restrict__ dc,
     float* __restrict__ pbuf, float* __restrict__ dsbuf, int Nq, int Nk, int ld, float scale) {
   constexpr int KS = D / 16;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
+  constexpr int PA = 128 * 16, PB = 64 * 16;          // bf16 per piece tile of X (128 rows), Y (64 rows)
+  constexpr int BUF = 3 * (PA + PB);                  // bf16 per staging buffer
+  constexpr int EP = 72;                              // floats per row of a wave's 32 x 64 output tile
+  constexpr int STAGE_B = 2 * BUF * 2, EPI_B = 4 * 32 * EP * 4;
+  __shared__ __attribute__((aligned(16))) char smem[STAGE_B > EPI_B ? STAGE_B : EPI_B];
+  bf16* stage = reinterpret_cast<bf16*>(smem);   // [buffer][X hi, mid, lo][Y hi, mid, lo]
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n32 = lane & 31, hf = lane >> 5;
   const Tile3 t = tile3((Nk + 63) / 64, (Nq + 127) / 128);
   const long bh = t.z;
-  const int m0 = t.y * 128 + 32 * w, n0 = t.x * 64;
-  if (m0 >= Nq) return;   // wave-uniform; no barrier in this kernel
-  // out[j] = X Y^T on rows m0 .. m0+31 of X and n0 + 32j .. +31 of Y.
-  auto nt_split = [&](const float* X, const float* Y, f32x16 (&out)[2]) {
-    const float* A = X + (bh * Nq + min(m0 + n32, Nq - 1)) * (long)D + 8 * hf;
-    const float* B[2];
+  const int M0 = t.y * 128, N0 = t.x * 64;
+  // LSE and delta of this lane's rows M0 + 32w + 8q + 4hf + 0..3 (rows past
+  // Nq clamped), loaded first so that their latency hides behind the products.
+  float lq[4][4], dq[4][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) B[j] = Y + (bh * Nk + min(n0 + 32 * j + n32, Nk - 1)) * (long)D + 8 * hf;
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const long r = bh * Nq + min(M0 + 32 * w + 8 * q + 4 * hf + e, Nq - 1);
+      lq[q][e] = lse[r];
+      dq[q][e] = dc[r];
+    }
+  auto put = [&](bf16* piece0, int pt, const float4& x, int idx) {
+    const float v[4] = {x.x, x.y, x.z, x.w};
+    bf16x4 hi, mid, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = (bf16)v[e];
+      const float r1 = v[e] - (float)hi[e];
+      mid[e] = (bf16)r1;
+      lo[e] = (bf16)(r1 - (float)mid[e]);
+    }
+    const int at = (idx >> 2) * 16 + (idx & 3) * 4;
+    *reinterpret_cast<bf16x4*>(piece0 + at) = hi;
+    *reinterpret_cast<bf16x4*>(piece0 + pt + at) = mid;
+    *reinterpret_cast<bf16x4*>(piece0 + 2 * pt + at) = lo;
+  };
+  // out[j] = X Y^T on the wave's rows of X and rows N0 + 32j .. +31 of Y.
+  auto nt_split = [&](const float* X, const float* Y, f32x16 (&out)[2]) {
+    // Staging role: X float4s tid, tid + 256 (row idx / 4 of 128), Y float4 tid (row idx / 4 of 64).
+    const float* Xr[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      Xr[j] = X + (bh * Nq + min(M0 + ((tid + 256 * j) >> 2), Nq - 1)) * (long)D + 4 * (tid & 3);
+    const float* Yr = Y + (bh * Nk + min(N0 + (tid >> 2), Nk - 1)) * (long)D + 4 * (tid & 3);
+    float4 rx[2], ry;
+    auto load = [&](int ks) {
+      rx[0] = *reinterpret_cast<const float4*>(Xr[0] + 16 * ks);
+      rx[1] = *reinterpret_cast<const float4*>(Xr[1] + 16 * ks);
+      ry = *reinterpret_cast<const float4*>(Yr + 16 * ks);
+    };
+    auto store = [&](int buf) {
+      bf16* b0 = stage + buf * BUF;
+      put(b0, PA, rx[0], tid);
+      put(b0, PA, rx[1], tid + 256);
+      put(b0 + 3 * PA, PB, ry, tid);
+    };
+    auto fx = [&](int buf, int p, int r) {
+      return *reinterpret_cast<const bf16x8*>(stage + buf * BUF + p * PA + r * 16 + 8 * hf);
+    };
+    auto fy = [&](int buf, int p, int r) {
+      return *reinterpret_cast<const bf16x8*>(stage + buf * BUF + 3 * PA + p * PB + r * 16 + 8 * hf);
+    };
     f32x16 hh[2], xx[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) hh[j][e] = xx[j][e] = 0.f;
-    float4 ra[2], rb[2][2];
-    auto load = [&](int ks) {
-      ra[0] = *reinterpret_cast<const float4*>(A + 16 * ks);
-      ra[1] = *reinterpret_cast<const float4*>(A + 16 * ks + 4);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        rb[j][0] = *reinterpret_cast<const float4*>(B[j] + 16 * ks);
-        rb[j][1] = *reinterpret_cast<const float4*>(B[j] + 16 * ks + 4);
-      }
-    };
     load(0);
+    store(0);
+    if (KS > 1) load(1);
+    __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 ah, am, al, bh8[2], bm[2], bl[2];
-      split3(ra[0], ra[1], ah, am, al);
+      const int buf = ks & 1;
+      const int rx_ = 32 * w + n32;
+      const bf16x8 ah = fx(buf, 0, rx_), am = fx(buf, 1, rx_), al = fx(buf, 2, rx_);
+      bf16x8 bh8[2], bm[2], bl[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) split3(rb[j][0], rb[j][1], bh8[j], bm[j], bl[j]);
-      if (ks + 1 < KS) load(ks + 1);
-      __builtin_amdgcn_sched_barrier(0);   // keep the loads a step ahead of their use
+      for (int j = 0; j < 2; ++j) {
+        bh8[j] = fy(buf, 0, 32 * j + n32);
+        bm[j] = fy(buf, 1, 32 * j + n32);
+        bl[j] = fy(buf, 2, 32 * j + n32);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         xx[j] = mfma32_bf16(am, bm[j], xx[j]);
@@ -1113,42 +1163,48 @@ __global__ __launch_bounds__(256, 2) void coarse_bwd_pds_split_kernel(
         xx[j] = mfma32_bf16(ah, bm[j], xx[j]);
         hh[j] = mfma32_bf16(ah, bh8[j], hh[j]);
       }
+      if (ks + 1 < KS) {
+        __builtin_amdgcn_sched_barrier(0);   // the store's loads were issued a step ago
+        store(buf ^ 1);
+        if (ks + 2 < KS) load(ks + 2);
+      }
+      __syncthreads();   // also frees the buffers for the next product or the epilogue
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) out[j] = hh[j] + xx[j];
   };
-  // LSE and delta of this lane's rows m0 + 8q + 4hf + 0..3 (loaded first, so
-  // their latency hides behind the products; rows past Nq are clamped).
-  float lq[4][4], dq[4][4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const long r = bh * Nq + min(m0 + 8 * q + 4 * hf + e, Nq - 1);
-      lq[q][e] = lse[r];
-      dq[q][e] = dc[r];
-    }
   f32x16 sv[2], dp[2];
   nt_split(qc, kc, sv);
-  __builtin_amdgcn_sched_barrier(0);
   nt_split(doc, vc, dp);
-  // sv[j][jj], dp[j][jj]: row m0 + 8(jj/4) + 4hf + jj%4, column n0 + 32j + n32.
-  float* P = pbuf + bh * (long)Nq * ld;
-  float* DS = dsbuf + bh * (long)Nq * ld;
+  // sv[j][jj], dp[j][jj]: row 32w + 8(jj/4) + 4hf + jj%4, column 32j + n32 of the tile.
+  // P, then dS, through the wave's LDS tile and out as 16-byte row units.
+  float* et = reinterpret_cast<float*>(smem) + w * 32 * EP;
+  const int c4 = 4 * (lane & 15), col = N0 + c4;
+  auto emit = [&](float* dst) {
+    wave_sync();
 #pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    const int row = m0 + 8 * (jj >> 2) + 4 * hf + (jj & 3);
-    if (row >= Nq) continue;
-    const float l = lq[jj >> 2][jj & 3], dd = dq[jj >> 2][jj & 3];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + 32 * j + n32;
-      if (col >= Nk) continue;
-      const float pv = __expf(sv[j][jj] * scale - l);
-      P[(long)row * ld + col] = pv;
-      DS[(long)row * ld + col] = pv * (dp[j][jj] - dd);
+    for (int st = 0; st < 8; ++st) {
+      const int r = 4 * st + (lane >> 4), row = M0 + 32 * w + r;
+      const float4 v = *reinterpret_cast<const float4*>(et + r * EP + c4);
+      if (row < Nq && col < ld) *reinterpret_cast<float4*>(dst + (long)row * ld + col) = v;   // ld % 4 == 0
     }
-  }
+    wave_sync();
+  };
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      const float pv = __expf(sv[j][jj] * scale - lq[jj >> 2][jj & 3]);
+      sv[j][jj] = pv;
+      et[(8 * (jj >> 2) + 4 * hf + (jj & 3)) * EP + 32 * j + n32] = pv;
+    }
+  emit(pbuf + bh * (long)Nq * ld);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+      et[(8 * (jj >> 2) + 4 * hf + (jj & 3)) * EP + 32 * j + n32] = sv[j][jj] * (dp[j][jj] - dq[jj >> 2][jj & 3]);
+  emit(dsbuf + bh * (long)Nq * ld);
 }
 
 // C = scale * M^T B of a bf16 problem (the coarse backward's dK_c = s dS^T Q_c
