@@ -481,7 +481,9 @@ __device__ __forceinline__ bool row_topk_few(const uint32_t (&key)[NCH], int Nk,
     const int j = t * 64 + lane;
     const bool c = j < Nk && key[t] >= thr;
     const uint64_t b = __ballot(c);
-    if (c) cand[pos + __popcll(b & lt_mask)] = ((uint64_t)key[t] << 32) | (uint32_t)j;
+    // Every lane writes (no branch): a non-candidate into its own slot past
+    // the 64 candidate slots.
+    cand[c ? pos + __popcll(b & lt_mask) : 64 + lane] = ((uint64_t)key[t] << 32) | (uint32_t)j;
     pos += __popcll(b);
   }
   wave_sync();
@@ -529,7 +531,8 @@ __global__ __launch_bounds__(256) void coarse_rows_kernel(const float* __restric
 #pragma unroll
   for (int t = 0; t < NCH; ++t) {
     const int j = t * 64 + lane;
-    v[t] = j < Nk ? srow[j] : -INFINITY;
+    const float x = srow[min(j, Nk - 1)];   // unconditional (no branch per slot)
+    v[t] = j < Nk ? x : -INFINITY;
     mx = fmaxf(mx, v[t]);
   }
   mx = wave_max(mx);
