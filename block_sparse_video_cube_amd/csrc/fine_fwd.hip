@@ -225,26 +225,50 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     for (int ks = 0; ks < C::KS; ++ks) sx = mfma32_bf16(kf[ks], qf[ks], sx);
     return sx;
   };
-  // Software pipeline over chunks. Iteration c forms P from the scores of
-  // chunk c (computed in iteration c - 1) while the MFMAs of the scores of
-  // chunk c + 1 run, then adds V_c^T P^T into O^T. K chunks are loaded KST - 1
-  // iterations ahead of their scores, V chunks VST - 1 ahead of their use;
-  // iteration c issues V of chunk c + VST - 1 and then K of chunk c + KST.
-  // At its top it needs K of c + 1 and V of c; loads retire in order, so only
-  // the loads issued in iteration c - 1 for later chunks (K of c + KST - 1 and,
-  // with three V stages, V of c + 1) may stay in flight. Each wave waits for
-  // its own loads, then a barrier (a bare s_barrier: a fenced one would also
-  // wait for the loads in flight) makes every wave's share visible and frees
-  // the stages about to be refilled (K of c, V of c + 1 - VST, read before).
+  // Three-stage software pipeline over chunks. Step c issues the score MFMAs
+  // of chunk c + 2 and the O MFMAs of chunk c (P of chunk c was formed in
+  // step c - 1), and between them, one slice per MFMA, forms P of chunk c + 1
+  // from its scores (computed in step c - 1). The softmax work then runs in
+  // the shadow of all sixteen MFMAs of the step instead of only the score
+  // MFMAs, and none of it waits for an MFMA of the same step.
+  //
+  // K chunks are loaded KST - 1 steps ahead of their scores (step c issues K
+  // of c + KST + 1 into the stage that held K of c + 1), V chunks VST - 1
+  // steps ahead of their use (step c issues V of c + VST - 1). At its top
+  // step c needs K of c + 2 and V of c; loads retire in order, so only the
+  // loads issued in step c - 1 for later chunks (K of c + KST and, with three
+  // V stages, V of c + 1) may stay in flight. Each wave waits for its own
+  // loads, then a barrier (a bare s_barrier: a fenced one would also wait for
+  // the loads in flight) makes every wave's share visible and frees the
+  // stages about to be refilled (K of c + 1 and V of c - 1, read in step
+  // c - 1).
   //
   // Online softmax against a lazily moved reference max m (log2 units): P =
-  // 2^(s*c - m) is formed as long as no exponent exceeds 16 (P < 2^16, so
-  // bf16 P and the fp32 sums keep their relative precision). Otherwise m
-  // moves up to the chunk's row max first and O and l are rescaled (rare:
-  // m starts at the row max of chunk 0). O and l always share m, so the
-  // result is exact whatever the schedule.
-  constexpr float kHeadroom = 16.0f;
+  // 2^(s*c - m) is formed with the current m, and kept when the lane's sum of
+  // the chunk's P is at most 2^16 (so every P is, and bf16 P and the fp32
+  // sums keep their relative precision). Otherwise (rare: m starts at the row
+  // max of chunk 0) m moves up to the chunk's row max, O (which by then holds
+  // chunk c) and l are rescaled, and P is formed again. O and l always share
+  // m, so the result is exact whatever the schedule.
+  constexpr float kSumCap = 65536.0f;
   f32x16 sxa, sxb;
+  bf16x8 pfa[2], pfb[2];
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
+  // P of a chunk from its scores sx against m, into pf; returns the lane's
+  // row sum of the rounded P (the weights O is formed with).
+  auto form_p = [&](const f32x16& sx, bf16x8 (&pf)[2]) {
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      pf[e >> 3][e & 7] = (bf16)__builtin_amdgcn_exp2f(sx[e] * scale_log2 - m);
+      pf[e >> 3][(e & 7) + 1] = (bf16)__builtin_amdgcn_exp2f(sx[e + 1] * scale_log2 - m);
+      const bf16x2 a = {pf[e >> 3][e & 7], pf[e >> 3][(e & 7) + 1]};
+      if (e & 2) l1 = __builtin_amdgcn_fdot2_f32_bf16(a, ones2, l1, false);
+      else l0 = __builtin_amdgcn_fdot2_f32_bf16(a, ones2, l0, false);
+    }
+    return l0 + l1;
+  };
   if (nch > 0) {
     issue_k(0);
 #pragma unroll
@@ -254,15 +278,22 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     for (int c0 = 1; c0 < C::KST; ++c0)
       if (c0 < nch) issue_k(c0);
     wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    sxa = scores(kbuf);
-    mask_tail(sxa, 0);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sxa[e]);
-    m = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
   }
   vm_settled();
+  if (nch > 0) {
+    __builtin_amdgcn_s_barrier();
+    f32x16 s0 = scores(kbuf);
+    if (nch > 1) sxa = scores(kbuf + C::KUNITS * 8);
+    mask_tail(s0, 0);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s0[e]);
+    m = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    lsum = form_p(s0, pfa);
+    // K of chunk KST goes into stage 0, which every wave read for S of chunk 0.
+    if (NW > 1) __builtin_amdgcn_s_barrier();
+    if (C::KST < nch) issue_k(C::KST);
+  }
   // Bytes of this lane's LDS fragments within a stage: K row fragment ks,
   // and the two transposed reads of V fragment (mb, s2).
   uint32_t koffs[C::KS], voffs[C::MB][2][2];
@@ -274,91 +305,114 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
     for (int s2 = 0; s2 < 2; ++s2) rowt_offsets<D>(lane, mb, s2, voffs[mb][s2]);
   const char* kbytes = reinterpret_cast<const char*>(kbuf);
   const char* vbytes = reinterpret_cast<const char*>(vbuf);
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
 
-  // One chunk; P is the chunk's position in the 6-chunk unrolled block
-  // (6 is a multiple of both stage counts, so both stages are constants and
-  // every LDS address is a per-lane register plus an immediate). sx holds
-  // the scores of chunk c, sn receives those of chunk c + 1.
-  auto step = [&](auto P, f32x16& sx, f32x16& sn, int c) {
-    constexpr int p = decltype(P)::value;
+  // The top of step c: wait for this wave's loads of K of c + 2 and V of c,
+  // barrier, then issue the step's loads.
+  auto step_top = [&](int c) {
     if (c > 0) {
-      // Loads issued in iteration c - 1 that iteration c does not need yet:
-      // K of c - 1 + KST and, with three V stages, V of c + 1.
-      const bool kin = c - 1 + C::KST < nch;
+      const bool kin = c + C::KST < nch;
       const bool vin = C::VST >= 3 && c + C::VST - 2 < nch;
       if (kin && vin) wait_vmcnt<2 * KPW>();
       else if (kin || vin) wait_vmcnt<KPW>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-    } else if (NW > 1 && C::KST < nch) {
-      // K of chunk KST goes into stage 0, which every wave read for the
-      // prologue's scores: all of them must be past those reads first.
-      __builtin_amdgcn_s_barrier();
     }
     if (c + C::VST - 1 < nch) issue_v(c + C::VST - 1);
-    if (c + C::KST < nch) issue_k(c + C::KST);
-
-    mask_tail(sx, c);
-    float mq = -INFINITY;
+    if (c + C::KST + 1 < nch) issue_k(c + C::KST + 1);
+  };
+  // The lazily moved reference max (see above): P of chunk c + 1 was formed
+  // from sx into pn with lane sum lc. Returns the sum to add to l.
+  auto settle = [&](const f32x16& sx, bf16x8 (&pn)[2], float lc) {
+    if (__any(!(lc <= kSumCap))) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mq = fmaxf(mq, sx[e]);
-    mq = mq * scale_log2 - m;
-    if (__any(mq > kHeadroom)) {
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sx[e]);
+      const float mq = mx * scale_log2 - m;
       const float shift = fmaxf(fmaxf(mq, __shfl_xor(mq, 32, 64)), 0.0f);
       const float alpha = __builtin_amdgcn_exp2f(-shift);
       m += shift;
       lsum *= alpha;
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) acc[mb] *= alpha;
+      lc = form_p(sx, pn);
     }
-    // Scores of chunk c + 1 (when c + 1 == nch they read a stale stage and
-    // are discarded) interleaved with P of chunk c, then O^T += V_c^T P^T.
-    // Every LDS fragment is read first, so LDS latency is paid once; the
-    // scheduling fences keep each score MFMA next to an independent slice of
-    // the softmax, which runs while the MFMA does.
-    constexpr uint32_t kst = ((p + 1) % C::KST) * C::KUNITS * 16, vst = (p % C::VST) * C::VUNITS * 16;
+    return lc;
+  };
+  // One step with chunks c + 1 and c + 2 in the list; P is its position in
+  // the 6-step unrolled block (6 is a multiple of both stage counts, so every
+  // stage is a constant and every LDS address a per-lane register plus an
+  // immediate). sx: scores of chunk c + 1, sn: receives those of c + 2, pc:
+  // P of chunk c, pn: receives P of chunk c + 1.
+  static_assert(C::KS == 2 * C::MB, "one O MFMA per score MFMA");
+  auto step = [&](auto PP, f32x16& sx, f32x16& sn, bf16x8 (&pc)[2], bf16x8 (&pn)[2], int c) {
+    constexpr int p = decltype(PP)::value;
+    step_top(c);
+    mask_tail(sx, c + 1);
+    constexpr uint32_t kst = ((p + 2) % C::KST) * C::KUNITS * 16, vst = (p % C::VST) * C::VUNITS * 16;
+    // Slot j: score MFMA j/2 (even j) or O MFMA j/2 (odd j), then 16/NSLOT
+    // exponentials of chunk c + 1 (pairs rounded to bf16 and summed). Each
+    // slot's LDS fragment is read LA slots ahead, so that few are live.
+    constexpr int NSLOT = 2 * C::KS, PER = 16 / NSLOT, LA = 3;
     bf16x8 kf[C::KS], vf[C::MB][2];
+    auto fetch = [&](int j) {
+      if (j % 2 == 0) {
+        kf[j / 2] = *reinterpret_cast<const bf16x8*>(kbytes + kst + koffs[j / 2]);
+      } else {
+        const int t = j / 2, s2 = t / C::MB, mb = t % C::MB;
+        vf[mb][s2] = rowt_frag(vbytes + vst, voffs[mb][s2][0], voffs[mb][s2][1]);
+      }
+    };
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(kbytes + kst + koffs[ks]);
-#pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) vf[mb][s2] = rowt_frag(vbytes + vst, voffs[mb][s2][0], voffs[mb][s2][1]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < LA; ++j) fetch(j);
 #pragma unroll
     for (int e = 0; e < 16; ++e) sn[e] = 0.f;
-    bf16x8 pf[2];
-    constexpr int PER = 16 / C::KS;   // softmax entries per score MFMA
+    __builtin_amdgcn_sched_barrier(0);
+    float l0 = 0.f, l1 = 0.f, pend = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      sn = mfma32_bf16(kf[ks], qf[ks], sn);
+    for (int j = 0; j < NSLOT; ++j) {
+      if (j + LA < NSLOT) fetch(j + LA);
+      if (j % 2 == 0) {
+        sn = mfma32_bf16(kf[j / 2], qf[j / 2], sn);
+      } else {
+        const int t = j / 2, s2 = t / C::MB, mb = t % C::MB;
+        acc[mb] = mfma32_bf16(vf[mb][s2], pc[s2], acc[mb]);
+      }
 #pragma unroll
-      for (int t = 0; t < PER; ++t) {
-        const int e = ks * PER + t;
-        pf[e >> 3][e & 7] = (bf16)__builtin_amdgcn_exp2f(sx[e] * scale_log2 - m);
+      for (int r = 0; r < PER; ++r) {
+        const int e = j * PER + r;
+        const float x = __builtin_amdgcn_exp2f(sx[e] * scale_log2 - m);
+        if (e % 2 == 0) {
+          pend = x;
+        } else {
+          pn[e >> 3][(e & 7) - 1] = (bf16)pend;
+          pn[e >> 3][e & 7] = (bf16)x;
+          const bf16x2 a = {pn[e >> 3][(e & 7) - 1], pn[e >> 3][e & 7]};
+          if (e & 2) l1 = __builtin_amdgcn_fdot2_f32_bf16(a, ones2, l1, false);
+          else l0 = __builtin_amdgcn_fdot2_f32_bf16(a, ones2, l0, false);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Row sums of the rounded P (the weights O is formed with), two at a time.
-    float l0 = 0.f, l1 = 0.f;
+    lsum += settle(sx, pn, l0 + l1);
+  };
+  // One of the last two steps (no chunk c + 2; chunk c + 1 when more): the
+  // O MFMAs of chunk c from the V stage of c, known only at run time here.
+  auto tail = [&](f32x16& sx, bf16x8 (&pc)[2], bf16x8 (&pn)[2], int c) {
+    step_top(c);
+    const char* vb = vbytes + (c % C::VST) * (C::VUNITS * 16);
+    bf16x8 vf[C::MB][2];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const bf16x2 a0 = {pf[0][e], pf[0][e + 1]}, a1 = {pf[1][e], pf[1][e + 1]};
-      l0 = __builtin_amdgcn_fdot2_f32_bf16(a0, ones2, l0, false);
-      l1 = __builtin_amdgcn_fdot2_f32_bf16(a1, ones2, l1, false);
-    }
-    lsum += l0 + l1;
-    // The wave issues its O MFMAs at raised priority, so that they go out
-    // back to back and the other wave of the SIMD fills the matrix pipe's
-    // shadow with its softmax and LDS reads (measured 1% faster).
-    __builtin_amdgcn_s_setprio(1);
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) vf[mb][s2] = rowt_frag(vb, voffs[mb][s2][0], voffs[mb][s2][1]);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) acc[mb] = mfma32_bf16(vf[mb][s2], pf[s2], acc[mb]);
-    __builtin_amdgcn_s_setprio(0);
+      for (int mb = 0; mb < C::MB; ++mb) acc[mb] = mfma32_bf16(vf[mb][s2], pc[s2], acc[mb]);
+    if (c + 1 < nch) {
+      mask_tail(sx, c + 1);
+      lsum += settle(sx, pn, form_p(sx, pn));
+    }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -367,18 +421,32 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_fwd_bf16_kernel(
   using I4 = std::integral_constant<int, 4>;
   using I5 = std::integral_constant<int, 5>;
   static_assert(6 % C::KST == 0 && 6 % C::VST == 0, "stages must divide the unroll");
-  for (int c0 = 0; c0 < nch; c0 += 6) {
-    step(I0(), sxa, sxb, c0);
-    if (c0 + 1 >= nch) break;
-    step(I1(), sxb, sxa, c0 + 1);
-    if (c0 + 2 >= nch) break;
-    step(I2(), sxa, sxb, c0 + 2);
-    if (c0 + 3 >= nch) break;
-    step(I3(), sxb, sxa, c0 + 3);
-    if (c0 + 4 >= nch) break;
-    step(I4(), sxa, sxb, c0 + 4);
-    if (c0 + 5 >= nch) break;
-    step(I5(), sxb, sxa, c0 + 5);
+  const int nfull = nch - 2;   // steps with chunks c + 1 and c + 2
+  int c = 0;
+  for (; c + 6 <= nfull; c += 6) {
+    step(I0(), sxa, sxb, pfa, pfb, c);
+    step(I1(), sxb, sxa, pfb, pfa, c + 1);
+    step(I2(), sxa, sxb, pfa, pfb, c + 2);
+    step(I3(), sxb, sxa, pfb, pfa, c + 3);
+    step(I4(), sxa, sxb, pfa, pfb, c + 4);
+    step(I5(), sxb, sxa, pfb, pfa, c + 5);
+  }
+  if (c < nfull) {
+    step(I0(), sxa, sxb, pfa, pfb, c);
+    if (c + 1 < nfull) {
+      step(I1(), sxb, sxa, pfb, pfa, c + 1);
+      if (c + 2 < nfull) {
+        step(I2(), sxa, sxb, pfa, pfb, c + 2);
+        if (c + 3 < nfull) {
+          step(I3(), sxb, sxa, pfb, pfa, c + 3);
+          if (c + 4 < nfull) step(I4(), sxa, sxb, pfa, pfb, c + 4);
+        }
+      }
+    }
+  }
+  for (c = nfull > 0 ? nfull : 0; c < nch; ++c) {
+    if (c & 1) tail(sxb, pfb, pfa, c);
+    else tail(sxa, pfa, pfb, c);
   }
 
   // Epilogue: lane holds O^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query].
