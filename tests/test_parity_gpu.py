@@ -165,6 +165,40 @@ def test_fine_forward_parity_ragged_lists(name, heads):
     assert np.all(host(of)[~live] == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", ["ramp", "jump"])
+def test_fine_forward_rising_logits(case, d):
+    """Logits that rise along the list far beyond the first chunk's maximum,
+    so the online softmax must move its reference maximum mid-row: "ramp" adds
+    about 3 nats per key cube (several moves per row), "jump" puts the last
+    key cube 100 nats above the rest (2^144 overflows fp32 before the move).
+    Every query cube lists every key cube in ascending order."""
+    T, H, W, heads = 8, 8, 16, 2
+    nc = T * H * W // 64
+    rng = np.random.default_rng(11 + d)
+    u = np.ones(d, np.float32)
+    q = (u + 0.1 * rng.standard_normal((1, heads, T, H, W, d))).astype(np.float32)
+    k = (0.1 * rng.standard_normal((1, heads, T, H, W, d))).astype(np.float32)
+    v = rng.standard_normal((1, heads, T, H, W, d)).astype(np.float32)
+    # key cube j of the (4, 4, 4) grid: tokens t in [4tc, 4tc+4), y in [4yc, ..), x in [4xc, ..)
+    for j in range(nc):
+        tc, r = divmod(j, (H // 4) * (W // 4))
+        yc, xc = divmod(r, W // 4)
+        b = 3.0 * j if case == "ramp" else (100.0 if j == nc - 1 else 0.0)
+        k[:, :, 4 * tc:4 * tc + 4, 4 * yc:4 * yc + 4, 4 * xc:4 * xc + 4, :] += b * u / np.sqrt(d)
+    q, k, v = (WL.round_bf16(a) for a in (q, k, v))
+    idx = np.broadcast_to(np.arange(nc, dtype=np.int32), (1, heads, nc, nc)).copy()
+    lens = np.full((1, heads, nc), nc, np.int32)
+    p = V.Problem(1, heads, T, H, W, d, topk=0, list_stride=nc)
+    tq, tk, tv = (dev(a, torch.bfloat16) for a in (q, k, v))
+    of, lse = V.fine_forward(p, tq, tk, tv, dev(idx, torch.int32), dev(lens, torch.int32))
+    torch.cuda.synchronize()
+    ref = O.forward(q, k, v, topk=0, idx=idx, lens=lens)
+    assert np.all(np.isfinite(host(of))) and np.all(np.isfinite(host(lse)))
+    assert_close(host(of), ref["o_f"], "bf16", "o_f")
+    assert float(np.abs(host(lse) - ref["lse_f"]).max()) <= LSE_ABS
+
+
 @pytest.mark.parametrize("name", ["C1", "C2"])
 def test_combine_parity(name):
     w = WL.get(name)
