@@ -467,47 +467,58 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && NW >= 2) ? 3 : 2) void fine_fw
   // token rows; the rounding to bf16 is the one O_f gets when it is stored.
   // A wave uses the chunk stage of its own index (one stage holds 32 rows of
   // D channels), once every wave is done with the stages.
-  __syncthreads();
-  bf16* tile = wv < C::KST ? kbuf + wv * (C::KUNITS * 8) : vbuf + (wv - C::KST) * (C::VUNITS * 8);
-#pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      bf16x4 w;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[mb][4 * jq + r] * inv);
-      *reinterpret_cast<bf16x4*>(tile + (n32 * C::U + ((4 * mb + jq) ^ kswz<C::U>(n32))) * 8 + 4 * hf) = w;
-    }
   constexpr int RPI = 64 / C::U, NIT = 32 / RPI;   // token rows per instruction, instructions per tile
   const int u = lane % C::U, r0 = lane / C::U;      // this lane's unit (channels 8u .. 8u+7) and first row
-  bf16x8 ofv[NIT];
   long nrow[NIT];
 #pragma unroll
-  for (int t = 0; t < NIT; ++t) {
-    const int row = t * RPI + r0;
-    ofv[t] = *reinterpret_cast<const bf16x8*>(tile + (row * C::U + (u ^ kswz<C::U>(row))) * 8);
-    nrow[t] = (tok0 + cube_token(g, i, 32 * wv + row)) * D + u * 8;
-  }
-  if (o_f != nullptr) {
+  for (int t = 0; t < NIT; ++t) nrow[t] = (tok0 + cube_token(g, i, 32 * wv + t * RPI + r0)) * D + u * 8;
+  bf16* tile = wv < C::KST ? kbuf + wv * (C::KUNITS * 8) : vbuf + (wv - C::KST) * (C::VUNITS * 8);
+  auto stage_o = [&](bf16x8 (&ofv)[NIT]) {
+    // Every wave is past its last read of the chunk stages (each read was
+    // consumed by an MFMA before the wave left the loop, and no chunk load is
+    // in flight), so a bare barrier frees them; loads the caller issued
+    // before it (the gates) stay in flight.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int t = 0; t < NIT; ++t) *reinterpret_cast<bf16x8*>(o_f + nrow[t]) = ofv[t];
-  }
-  if (FUSED) {
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        bf16x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[mb][4 * jq + r] * inv);
+        *reinterpret_cast<bf16x4*>(tile + (n32 * C::U + ((4 * mb + jq) ^ kswz<C::U>(n32))) * 8 + 4 * hf) = w;
+      }
+#pragma unroll
+    for (int t = 0; t < NIT; ++t) {
+      const int row = t * RPI + r0;
+      ofv[t] = *reinterpret_cast<const bf16x8*>(tile + (row * C::U + (u ^ kswz<C::U>(row))) * 8);
+    }
+    if (o_f != nullptr) {
+#pragma unroll
+      for (int t = 0; t < NIT; ++t) *reinterpret_cast<bf16x8*>(o_f + nrow[t]) = ofv[t];
+    }
+  };
+  if constexpr (!FUSED) {
+    bf16x8 ofv[NIT];
+    stage_o(ofv);
+  } else {
     // The gated combine, O_f taken as rounded to bf16 (so the fused output
     // equals the unfused combine of the stored O_f). Which gates exist is
-    // decided outside the loops, so that every load is issued before the
-    // first use.
-    const float4* ocr = reinterpret_cast<const float4*>(oc + ((long)bh * g.Nc + i) * D + u * 8);
-    const float4 oa = ocr[0], ob = ocr[1];
-    const float cv[8] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
+    // decided outside the loops, and O_c and the gates are loaded before O
+    // is staged, so that their latency overlaps the staging.
     auto combine = [&](auto HC, auto HF) {
       constexpr bool kHC = decltype(HC)::value, kHF = decltype(HF)::value;
+      const float4* ocr = reinterpret_cast<const float4*>(oc + ((long)bh * g.Nc + i) * D + u * 8);
+      const float4 oa = ocr[0], ob = ocr[1];
       bf16x8 gcv[NIT], gfv[NIT];
 #pragma unroll
       for (int t = 0; t < NIT; ++t) {
         if (kHC) gcv[t] = *reinterpret_cast<const bf16x8*>(gc + nrow[t]);
         if (kHF) gfv[t] = *reinterpret_cast<const bf16x8*>(gf + nrow[t]);
       }
+      bf16x8 ofv[NIT];
+      stage_o(ofv);
+      const float cv[8] = {oa.x, oa.y, oa.z, oa.w, ob.x, ob.y, ob.z, ob.w};
 #pragma unroll
       for (int t = 0; t < NIT; ++t) {
         bf16x8 w;
