@@ -83,7 +83,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
     const float* __restrict__ dqc, const uint8_t* __restrict__ qarg, bf16* __restrict__ dq, Grid g, Grid gk,
     int stride, float scale) {
   using G = ChunkGeom<D>;
-  __shared__ __attribute__((aligned(16))) bf16 rk[2][G::RUNITS * 8];
+  // Three K stages (chunk c for S, c - 1 for the dQ MFMAs, c + 1 loading) and
+  // two V stages (c for dP, c + 1 loading): 40 KB at 128 channels.
+  __shared__ __attribute__((aligned(16))) bf16 rk[3][G::RUNITS * 8];
   __shared__ __attribute__((aligned(16))) bf16 rv[2][G::RUNITS * 8];
 
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
@@ -140,70 +142,132 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
   };
   const uint32_t rkb = lds_addr(rk), rvb = lds_addr(rv);
   auto issue = [&](int c) {
-    const int e = kpair ? 2 * c : c >> ksh, h = kpair ? 0 : c & kmask, st = c & 1;
+    const int e = kpair ? 2 * c : c >> ksh, h = kpair ? 0 : c & kmask, sk = c % 3, sv = c & 1;
     if ((e & 63) == 0 && h == 0) cubes(e);
     const uint32_t rc = __builtin_amdgcn_readlane(rcube, e & 63) + chunk_bytes(h);
     if constexpr (kpair) {   // entries e, e + 1 share a block of 64 (e is even)
       const uint32_t rc1 = __builtin_amdgcn_readlane(rcube, min(e + 1, L - 1) & 63);
-      issue_row_tile2<D, NW>(uniform_ptr(Kb + rc), uniform_ptr(Kb + rc1), roff, rkb + st * (G::RUNITS * 16), wv);
-      issue_row_tile2<D, NW>(uniform_ptr(Vb + rc), uniform_ptr(Vb + rc1), roff, rvb + st * (G::RUNITS * 16), wv);
+      issue_row_tile2<D, NW>(uniform_ptr(Kb + rc), uniform_ptr(Kb + rc1), roff, rkb + sk * (G::RUNITS * 16), wv);
+      issue_row_tile2<D, NW>(uniform_ptr(Vb + rc), uniform_ptr(Vb + rc1), roff, rvb + sv * (G::RUNITS * 16), wv);
       return;
     }
-    issue_row_tile<D, NW>(uniform_ptr(Kb + rc), roff, rkb + st * (G::RUNITS * 16), wv);
-    issue_row_tile<D, NW>(uniform_ptr(Vb + rc), roff, rvb + st * (G::RUNITS * 16), wv);
+    issue_row_tile<D, NW>(uniform_ptr(Kb + rc), roff, rkb + sk * (G::RUNITS * 16), wv);
+    issue_row_tile<D, NW>(uniform_ptr(Vb + rc), roff, rvb + sv * (G::RUNITS * 16), wv);
   };
 
-  // Per chunk: wait for this wave's loads, barrier (every wave's share is in
-  // LDS and every wave is done with the other stage), issue the next chunk,
-  // compute this one.
+  // Step c: wait for this wave's loads of chunk c, barrier (every wave's share
+  // is in LDS; every wave is done with the stages chunk c + 1 refills: K of
+  // c - 2, V of c - 1), issue chunk c + 1, then: the score MFMAs of chunk c;
+  // its dP MFMAs, with P = 2^(s*c - LSE) formed one slice per MFMA once the
+  // scores are in; and the dQ MFMAs of chunk c - 1 (dS formed in step c - 1,
+  // K of c - 1 still in its stage), with dS of chunk c formed one slice per
+  // MFMA. Softmax and dS work thus run under the MFMAs of the same wave.
   const int nch = kpair ? (L + 1) >> 1 : L << ksh;
   const bool khalf = kpair && (L & 1);   // keys 16-31 of the last chunk absent
-  // The loop is unrolled by the two stages so that the stage, and with it
-  // every LDS address, is a compile-time constant.
-  auto step = [&](auto stage, int c) {
-    constexpr int st = decltype(stage)::value;
+  bf16x8 dsa[2], dsb[2];   // dS of a chunk, as the B operand of its dQ MFMAs
+  // The loop is unrolled by six (both stage counts divide it) so that every
+  // stage, and with it every LDS address, is a compile-time constant. A step
+  // is a sequence of slots, one MFMA each: the score MFMAs, the dP MFMAs (with
+  // the exponentials), the dQ MFMAs of chunk c - 1 (with dS of chunk c); each
+  // slot's LDS fragment is read three slots ahead, so that few are live. DQ:
+  // there is a chunk c - 1.
+  auto step = [&](auto PP, auto DQ, const bf16x8 (&dprev)[2], bf16x8 (&dcur)[2], int c) {
+    constexpr int p = decltype(PP)::value;
+    constexpr bool kDq = decltype(DQ)::value;
+    constexpr int sk = p % 3, sv = p % 2, skp = (p + 2) % 3;   // K stage of c, V stage of c, K stage of c - 1
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (c + 1 < nch) issue(c + 1);
-    bf16x8 kf[G::KS], vf[G::KS];
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      kf[ks] = row_frag<D>(rk[st], n32, hf, ks);
-      vf[ks] = row_frag<D>(rv[st], n32, hf, ks);
-    }
+    constexpr int NS = G::KS, NT = 2 * G::MB, NSLOT = 2 * NS + NT, LA = 3;
+    constexpr int PER = 16 / NS, PT = 16 / NT;   // exponentials per dP slot, dS values per dQ slot
+    const char* ktp = reinterpret_cast<const char*>(rk[skp]);
+    bf16x8 kf[NS], vf[NS], tf[NT];
+    auto fetch = [&](int j) {
+      if (j < NS) kf[j] = row_frag<D>(rk[sk], n32, hf, j);
+      else if (j < 2 * NS) vf[j - NS] = row_frag<D>(rv[sv], n32, hf, j - NS);
+      else if (kDq) {
+        const int t = j - 2 * NS, s2 = t / G::MB, mb = t % G::MB;
+        tf[t] = rowt_frag(ktp, toffs[mb][s2][0], toffs[mb][s2][1]);
+      }
+    };
     f32x16 sx, dp;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { sx[e] = 0.f; dp[e] = 0.f; }
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      sx = mfma32_bf16(kf[ks], qf[ks], sx);
-      dp = mfma32_bf16(vf[ks], df[ks], dp);
+    for (int j = 0; j < LA; ++j) fetch(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) {
+      if (j + LA < NSLOT) fetch(j + LA);
+      if (j < NS) {
+        sx = mfma32_bf16(kf[j], qf[j], sx);
+        if (j == NS - 1 && kpair && khalf && c == nch - 1) {   // accumulator entries 8-15 hold keys 16-31
+#pragma unroll
+          for (int e = 8; e < 16; ++e) sx[e] = -INFINITY;
+        }
+      } else if (j < 2 * NS) {
+        dp = mfma32_bf16(vf[j - NS], df[j - NS], dp);
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+          const int e = (j - NS) * PER + r;
+          sx[e] = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2);   // P
+        }
+      } else {
+        const int t = j - 2 * NS, s2 = t / G::MB, mb = t % G::MB;
+        if (kDq) acc[mb] = mfma32_bf16(tf[t], dprev[s2], acc[mb]);
+#pragma unroll
+        for (int r = 0; r < PT; ++r) {
+          const int e = t * PT + r;
+          dcur[e >> 3][e & 7] = (bf16)(sx[e] * (dp[e] - dl));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kpair && khalf && c == nch - 1) {   // accumulator entries 8-15 hold keys 16-31
-#pragma unroll
-      for (int e = 8; e < 16; ++e) sx[e] = -INFINITY;
-    }
-    bf16x8 sf[2];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(sx[e] * sl2 - lse2);
-      sf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dl));
-    }
-    const char* kt = reinterpret_cast<const char*>(rk[st]);
-    // Accumulating MFMAs at raised wave priority (issued back to back while
-    // the SIMD's other wave does its softmax; 2% faster over the backward).
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int mb = 0; mb < G::MB; ++mb)
-        acc[mb] = mfma32_bf16(rowt_frag(kt, toffs[mb][s2][0], toffs[mb][s2][1]), sf[s2], acc[mb]);
-    __builtin_amdgcn_s_setprio(0);
   };
-  if (nch > 0) issue(0);
-  for (int c = 0; c < nch; c += 2) {
-    step(std::integral_constant<int, 0>(), c);
-    if (c + 1 < nch) step(std::integral_constant<int, 1>(), c + 1);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using T1 = std::true_type;
+  using F0 = std::false_type;
+  // Step c writes dS of chunk c into dsa (c even) or dsb (c odd).
+  if (nch > 0) {
+    issue(0);
+    step(I0(), F0(), dsb, dsa, 0);
+  }
+  int c = 1;
+  for (; c + 6 <= nch; c += 6) {
+    step(I1(), T1(), dsa, dsb, c);
+    step(I2(), T1(), dsb, dsa, c + 1);
+    step(I3(), T1(), dsa, dsb, c + 2);
+    step(I4(), T1(), dsb, dsa, c + 3);
+    step(I5(), T1(), dsa, dsb, c + 4);
+    step(I0(), T1(), dsb, dsa, c + 5);
+  }
+  if (c < nch) {
+    step(I1(), T1(), dsa, dsb, c);
+    if (c + 1 < nch) {
+      step(I2(), T1(), dsb, dsa, c + 1);
+      if (c + 2 < nch) {
+        step(I3(), T1(), dsa, dsb, c + 2);
+        if (c + 3 < nch) {
+          step(I4(), T1(), dsb, dsa, c + 3);
+          if (c + 4 < nch) step(I5(), T1(), dsa, dsb, c + 4);
+        }
+      }
+    }
+  }
+  if (nch > 0) {   // the dQ MFMAs of the last chunk (its dS and K stage)
+    const int cl = nch - 1;
+    const char* ktl = reinterpret_cast<const char*>(rk[cl % 3]);
+    const bf16x8(&dl_)[2] = (cl & 1) ? dsb : dsa;
+#pragma unroll
+    for (int t = 0; t < 2 * G::MB; ++t) {
+      const int s2 = t / G::MB, mb = t % G::MB;
+      acc[mb] = mfma32_bf16(rowt_frag(ktl, toffs[mb][s2][0], toffs[mb][s2][1]), dl_[s2], acc[mb]);
+    }
   }
 
   // lane holds dQ^T[channel 32mb + 8(jj/4) + 4hf + jj%4][its query]; the
@@ -217,7 +281,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fine_bwd_dq_kernel(
   const int lq = 32 * wv + n32;   // the query's position in its cube
   const float inv_b = 1.0f / (float)g.B;
   __syncthreads();   // every wave is done with the chunk stages
-  bf16* tile = wv < 2 ? rk[wv] : rv[wv - 2];
+  bf16* tile = wv < 3 ? rk[wv] : rv[wv - 3];
   auto finish = [&](auto MAXP) {
     constexpr bool kMax = decltype(MAXP)::value;
     float4 c4[G::MB][4];
