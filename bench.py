@@ -347,6 +347,56 @@ def dense_flash_context(heads: int, n: int, d: int, reps: int = 3):
         return {"error": repr(e)[:200]}
 
 
+def probe_measure(V, torch) -> dict:
+    """The chip measurements behind two bounds of the kernels (event-timed):
+    32x32x16 bf16 MFMA streams with N independent vector instructions after
+    each MFMA (FMA or exp2), at one and two waves per SIMD; and the best
+    streaming read of a 2.595 GB buffer (the pool stage's input at 720p) over
+    grid sizes, loads in flight and plain or non-temporal loads, warm and
+    after a 512 MB write that evicts the 256 MB Infinity Cache."""
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3
+    iters = 20000
+    out = torch.empty(65536 * 2, dtype=torch.float32, device="cuda:0")
+    mfma = []
+    for waves in (1, 2):
+        o = out[:65536 * waves]
+        for op, valus in ((0, (0, 4, 8, 16)), (1, (1, 2, 4, 8))):
+            for valu in valus:
+                V.probe_mfma_valu(valu, op, waves, iters // 10, o)
+                sec = timed(lambda: V.probe_mfma_valu(valu, op, waves, iters, o))
+                flop = 4.0 * iters * 32768 * 1024 * waves
+                mfma.append({"waves_per_simd": waves, "valu_per_mfma": valu, "op": ("fma", "exp2")[op],
+                             "ms": round(sec * 1e3, 3), "TFLOP_per_s": round(flop / sec / 1e12, 1)})
+    n = 3 * 40 * 84480 * 128 * 2
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    best = {}
+    for nt in (False, True):
+        loads = "nontemporal" if nt else "plain"
+        best[loads] = {"warm": None, "cold": None}
+        for blocks in (1024, 2048, 4096, 8192, 16384, 32768):
+            res = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+            for inflight in (1, 2, 4, 8, 16):
+                V.probe_stream_read(src, blocks, inflight, res, nt)
+                warm = min(timed(lambda: V.probe_stream_read(src, blocks, inflight, res, nt)) for _ in range(3))
+                colds = []
+                for _ in range(3):
+                    scratch.fill_(1)
+                    colds.append(timed(lambda: V.probe_stream_read(src, blocks, inflight, res, nt)))
+                for kind, sec in (("warm", warm), ("cold", min(colds))):
+                    tbs = n / sec / 1e12
+                    if best[loads][kind] is None or tbs > best[loads][kind]["TB_per_s"]:
+                        best[loads][kind] = {"TB_per_s": round(tbs, 3), "frac_of_8TB_per_s": round(tbs / 8.0, 4),
+                                             "blocks": blocks, "loads_in_flight": inflight}
+    return {"mfma_valu": mfma, "stream_read_bytes": n, "stream_read_best": best}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,10 +405,12 @@ def main() -> int:
     ap.add_argument("--workload", default="bf16_720p_24x44x80")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads of the oracle sample")
-    ap.add_argument("--mode", choices=["forward", "fine", "copy"], default="forward",
+    ap.add_argument("--mode", choices=["forward", "fine", "copy", "probe"], default="forward",
                     help="forward: the benchmark; fine: only the fused fine kernel, --steps launches "
                          "(for counter collection); copy: a plain device copy of --copy-mib MiB, the "
-                         "calibration of the FETCH_SIZE / WRITE_SIZE counters")
+                         "calibration of the FETCH_SIZE / WRITE_SIZE counters; probe: the chip "
+                         "measurements behind the kernels' bounds (MFMA / vector-ALU overlap, streaming "
+                         "read of HBM), one JSON line")
     ap.add_argument("--copy-mib", type=int, default=2048)
     ap.add_argument("--cpu-full", action="store_true",
                     help="only time the CPU oracle at full size (every head of the workload, by stage, and the "
@@ -395,6 +447,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"mode": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
                           "copies": args.steps}), flush=True)
+        return 0
+    if args.mode == "probe":
+        print(json.dumps({"mode": "probe", **probe_measure(V, torch)}), flush=True)
         return 0
     w = WL.get(args.workload)
     log(f"generating {w.name} inputs")

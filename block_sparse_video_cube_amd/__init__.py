@@ -22,7 +22,7 @@ from ._native import VSA_BF16, VSA_F32, VsaError, VsaProblem, check, lib
 __all__ = ["Problem", "VsaError", "forward", "backward", "pool", "coarse", "fine_forward", "fine_combine", "fine_combine_noalloc", "combine",
            "combine_backward", "index_transpose", "fine_backward", "coarse_backward",
            "check_lists_host", "validate_lists", "workspace_bytes", "saved_bytes", "max_cubes", "tile", "untile",
-           "compatible_latent", "crop", "pad", "saved_views", "attention"]
+           "compatible_latent", "crop", "pad", "saved_views", "attention", "probe_mfma_valu", "probe_stream_read"]
 
 
 @dataclass(frozen=True)
@@ -547,6 +547,30 @@ def validate_lists(p: Problem, idx, lens) -> None:
     flag = _empty((4,), torch.int32, idx)
     check(a.call(lib().vsa_validate_lists, ctypes.byref(p.c()), pidx, plen, a.t("flag", flag, (4,), torch.int32),
                                    _stream(idx.device)), "vsa_validate_lists")
+
+
+# Measurement aids (include/vsa_probe.h); not steps of the operator.
+def probe_mfma_valu(valu: int, op: int, waves_per_simd: int, iters: int, out) -> None:
+    """Enqueues the MFMA / vector-ALU overlap probe on the current stream
+    (out: float32, 65536 * waves_per_simd elements)."""
+    a = _Args("vsa_probe_mfma_valu")
+    po = a.t("out", out, (65536 * waves_per_simd,), torch.float32)
+    check(a.call(lib().vsa_probe_mfma_valu, valu, op, waves_per_simd, iters, po, _stream(out.device)),
+          "vsa_probe_mfma_valu")
+
+
+def probe_stream_read(src, blocks: int, inflight: int, out, nontemporal: bool = False) -> None:
+    """Enqueues a streaming read of all of src (any contiguous tensor whose
+    byte size is a multiple of 16) on the current stream (out: float32,
+    blocks * 256 elements), with non-temporal loads when asked."""
+    a = _Args("vsa_probe_stream_read")
+    if not isinstance(src, torch.Tensor):
+        raise ValueError("vsa_probe_stream_read: src must be a torch.Tensor")
+    a._common("src", src)
+    po = a.t("out", out, (blocks * 256,), torch.float32)
+    nbytes = src.numel() * src.element_size()
+    check(a.call(lib().vsa_probe_stream_read, ctypes.c_void_p(src.data_ptr()), nbytes, blocks, inflight,
+                 int(bool(nontemporal)), po, _stream(out.device)), "vsa_probe_stream_read")
 
 
 class _Attention(torch.autograd.Function):

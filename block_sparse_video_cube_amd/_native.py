@@ -33,7 +33,7 @@ _v = ctypes.c_void_p
 _sz = ctypes.c_size_t
 _i32 = ctypes.c_int32
 
-# name -> (restype, argtypes); every symbol include/vsa.h declares.
+# name -> (restype, argtypes); every symbol include/vsa.h and include/vsa_probe.h declare.
 SIGNATURES = {
     "vsa_tile": (_i32, [_P, _v, _v, _v]),
     "vsa_untile": (_i32, [_P, _v, _v, _v]),
@@ -60,6 +60,9 @@ SIGNATURES = {
     "vsa_coarse_backward": (_i32, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v, _sz, _v]),
     "vsa_check_lists_host": (_i32, [_P, _v, _v]),
     "vsa_validate_lists": (_i32, [_P, _v, _v, _v, _v]),
+    # include/vsa_probe.h: measurement aids
+    "vsa_probe_mfma_valu": (_i32, [_i32, _i32, _i32, _i32, _v, _v]),
+    "vsa_probe_stream_read": (_i32, [_v, _sz, _i32, _i32, _i32, _v, _v]),
 }
 
 _lib = None

@@ -22,7 +22,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pool.hip", "coarse.hip", "fine_fwd.hip", "fine_bwd.hip", "combine.hip", "backward.hip", "layout.hip", "vsa_api.cpp"]
+SOURCES = ["pool.hip", "coarse.hip", "fine_fwd.hip", "fine_bwd.hip", "combine.hip", "backward.hip", "layout.hip",
+           "probe.hip", "vsa_api.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -12,14 +12,18 @@ from block_sparse_video_cube_amd import _native as N
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vsa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, NULL, SHAPE, HEAD_DIM, DTYPE, TOPK, ALIGN, WORKSPACE, INDEX, UNSUP, HIP, SCALE = range(12)
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported_and_bound():
@@ -290,3 +294,21 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     bad = list(args)
     bad[1] = MIS
     assert lib.vsa_fine_combine_noalloc(ctypes.byref(small.c()), *bad) == ALIGN
+
+
+def test_probe_arguments_rejected_on_the_host():
+    """The measurement aids reject bad arguments before any HIP call."""
+    lib = N.lib()
+    buf = ctypes.c_void_p(16)   # never dereferenced: every call below fails its host checks
+    assert lib.vsa_probe_mfma_valu(4, 0, 1, 10, None, None) == NULL
+    assert lib.vsa_probe_mfma_valu(3, 0, 1, 10, buf, None) == UNSUP
+    assert lib.vsa_probe_mfma_valu(4, 2, 1, 10, buf, None) == UNSUP
+    assert lib.vsa_probe_mfma_valu(4, 0, 3, 10, buf, None) == UNSUP
+    assert lib.vsa_probe_mfma_valu(4, 0, 2, 0, buf, None) == SHAPE
+    assert lib.vsa_probe_stream_read(None, 1024, 4, 4, 0, buf, None) == NULL
+    assert lib.vsa_probe_stream_read(ctypes.c_void_p(8), 1024, 4, 4, 0, buf, None) == ALIGN
+    assert lib.vsa_probe_stream_read(buf, 1000, 4, 4, 0, buf, None) == ALIGN
+    assert lib.vsa_probe_stream_read(buf, 0, 4, 4, 0, buf, None) == SHAPE
+    assert lib.vsa_probe_stream_read(buf, 1024, 0, 4, 0, buf, None) == SHAPE
+    assert lib.vsa_probe_stream_read(buf, 1024, 4, 3, 0, buf, None) == UNSUP
+    assert lib.vsa_probe_stream_read(buf, 1024, 4, 4, 2, buf, None) == UNSUP
