@@ -58,11 +58,11 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const long tok = base + cube_token(g, c, l);
     const long off = tok * D + ch * 8;
     float dov[8], ofv[8], a[8], b[8];
-    load8(d_o + off, dov);
-    load8(of + off, ofv);
-    if (gc != nullptr) load8(gc + off, a);
+    load8_nt(d_o + off, dov);
+    load8_nt(of + off, ofv);
+    if (gc != nullptr) load8_nt(gc + off, a);
     else for (int i = 0; i < 8; ++i) a[i] = 1.f;
-    if (gf != nullptr) load8(gf + off, b);
+    if (gf != nullptr) load8_nt(gf + off, b);
     else for (int i = 0; i < 8; ++i) b[i] = 1.f;
     float r1[8], r2[8], r3[8];
     float dsum = 0.f;
@@ -74,9 +74,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
       dsum += r3[i] * ofv[i];
       acc[i] += dov[i] * a[i];
     }
-    if (dgc != nullptr) store8(dgc + off, r1);
-    if (dgf != nullptr) store8(dgf + off, r2);
-    store8(dof + off, r3);
+    if (dgc != nullptr) store8_nt(dgc + off, r1);
+    if (dgf != nullptr) store8_nt(dgf + off, r2);
+    store8_nt(dof + off, r3);
 #pragma unroll
     for (int o = CH / 2; o >= 1; o >>= 1) dsum += __shfl_xor(dsum, o, 64);
     if (ch == 0) delta[tok] = dsum;

@@ -495,7 +495,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && NW >= 2) ? 3 : 2) void fine_fw
     }
     if (o_f != nullptr) {
 #pragma unroll
-      for (int t = 0; t < NIT; ++t) *reinterpret_cast<bf16x8*>(o_f + nrow[t]) = ofv[t];
+      for (int t = 0; t < NIT; ++t) __builtin_nontemporal_store(ofv[t], reinterpret_cast<bf16x8*>(o_f + nrow[t]));
     }
   };
   if constexpr (!FUSED) {
@@ -513,8 +513,8 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && NW >= 2) ? 3 : 2) void fine_fw
       bf16x8 gcv[NIT], gfv[NIT];
 #pragma unroll
       for (int t = 0; t < NIT; ++t) {
-        if (kHC) gcv[t] = *reinterpret_cast<const bf16x8*>(gc + nrow[t]);
-        if (kHF) gfv[t] = *reinterpret_cast<const bf16x8*>(gf + nrow[t]);
+        if (kHC) gcv[t] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(gc + nrow[t]));
+        if (kHF) gfv[t] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(gf + nrow[t]));
       }
       bf16x8 ofv[NIT];
       stage_o(ofv);
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(64 * NW, (D == 64 && NW >= 2) ? 3 : 2) void fine_fw
           const float b = kHF ? (float)gfv[t][r] : 1.f;
           w[r] = (bf16)(cv[r] * a + (float)ofv[t][r] * b);
         }
-        *reinterpret_cast<bf16x8*>(o + nrow[t]) = w;
+        __builtin_nontemporal_store(w, reinterpret_cast<bf16x8*>(o + nrow[t]));
       }
     };
     using T1 = std::true_type;

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, cons
     for (int w = 0; w < 3; ++w) {
       if (!(SEL & (1 << w))) continue;
       float x[8];
-      load8(srcs[w] + off, x);
+      load8_nt(srcs[w] + off, x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (MAX) {
