@@ -394,7 +394,16 @@ def probe_measure(V, torch) -> dict:
                     if best[loads][kind] is None or tbs > best[loads][kind]["TB_per_s"]:
                         best[loads][kind] = {"TB_per_s": round(tbs, 3), "frac_of_8TB_per_s": round(tbs / 8.0, 4),
                                              "blocks": blocks, "loads_in_flight": inflight}
-    return {"mfma_valu": mfma, "stream_read_bytes": n, "stream_read_best": best}
+    # L2-resident chunks into LDS (the fine kernels' load path): 2048
+    # workgroups of two waves (four per CU), 2000 chunks of 16 KB each.
+    l2src = torch.ones(1 << 19, dtype=torch.float32, device="cuda:0")   # 2 MB
+    l2out = torch.empty(2048 * 128, dtype=torch.float32, device="cuda:0")
+    l2lds = {}
+    for mode, name in ((0, "direct_to_lds"), (1, "registers_then_lds_writes")):
+        V.probe_l2_to_lds(mode, l2src, 2048, 200, l2out)
+        sec = min(timed(lambda: V.probe_l2_to_lds(mode, l2src, 2048, 2000, l2out)) for _ in range(3))
+        l2lds[name] = {"ms": round(sec * 1e3, 3), "TB_per_s": round(2048 * 2000 * 16384 / sec / 1e12, 2)}
+    return {"mfma_valu": mfma, "stream_read_bytes": n, "stream_read_best": best, "l2_to_lds": l2lds}
 
 
 def main() -> int:

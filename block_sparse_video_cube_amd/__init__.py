@@ -22,7 +22,8 @@ from ._native import VSA_BF16, VSA_F32, VsaError, VsaProblem, check, lib
 __all__ = ["Problem", "VsaError", "forward", "backward", "pool", "coarse", "fine_forward", "fine_combine", "fine_combine_noalloc", "combine",
            "combine_backward", "index_transpose", "fine_backward", "coarse_backward",
            "check_lists_host", "validate_lists", "workspace_bytes", "saved_bytes", "max_cubes", "tile", "untile",
-           "compatible_latent", "crop", "pad", "saved_views", "attention", "probe_mfma_valu", "probe_stream_read"]
+           "compatible_latent", "crop", "pad", "saved_views", "attention", "probe_mfma_valu", "probe_stream_read",
+           "probe_l2_to_lds"]
 
 
 @dataclass(frozen=True)
@@ -571,6 +572,21 @@ def probe_stream_read(src, blocks: int, inflight: int, out, nontemporal: bool = 
     nbytes = src.numel() * src.element_size()
     check(a.call(lib().vsa_probe_stream_read, ctypes.c_void_p(src.data_ptr()), nbytes, blocks, inflight,
                  int(bool(nontemporal)), po, _stream(out.device)), "vsa_probe_stream_read")
+
+
+def probe_l2_to_lds(mode: int, src, blocks: int, iters: int, out) -> None:
+    """Enqueues the L2-to-LDS probe on the current stream: mode 0 direct-to-LDS
+    loads, 1 loads into registers and LDS writes; src: a contiguous tensor
+    whose byte size is a power of two (16 KB .. 1 GB); out: float32,
+    blocks * 128 elements."""
+    a = _Args("vsa_probe_l2_to_lds")
+    if not isinstance(src, torch.Tensor):
+        raise ValueError("vsa_probe_l2_to_lds: src must be a torch.Tensor")
+    a._common("src", src)
+    po = a.t("out", out, (blocks * 128,), torch.float32)
+    nbytes = src.numel() * src.element_size()
+    check(a.call(lib().vsa_probe_l2_to_lds, mode, ctypes.c_void_p(src.data_ptr()), nbytes, blocks, iters, po,
+                 _stream(out.device)), "vsa_probe_l2_to_lds")
 
 
 class _Attention(torch.autograd.Function):

@@ -63,6 +63,7 @@ SIGNATURES = {
     # include/vsa_probe.h: measurement aids
     "vsa_probe_mfma_valu": (_i32, [_i32, _i32, _i32, _i32, _v, _v]),
     "vsa_probe_stream_read": (_i32, [_v, _sz, _i32, _i32, _i32, _v, _v]),
+    "vsa_probe_l2_to_lds": (_i32, [_i32, _v, _sz, _i32, _i32, _v, _v]),
 }
 
 _lib = None

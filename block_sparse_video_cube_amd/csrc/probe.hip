@@ -3,13 +3,17 @@
 //  * how much independent vector-ALU work hides under 32x32x16 bf16 MFMAs,
 //    at one or two waves per SIMD (the budget of the fine kernels' softmax);
 //  * the rate of a plain streaming read of HBM (the ceiling of the pool and
-//    combine-backward stages, which read every input element once).
-// Both kernels stay inside their buffers and run a fixed number of
+//    combine-backward stages, which read every input element once);
+//  * the rate at which L2-resident data reaches LDS, by direct-to-LDS loads
+//    (the fine kernels' chunk path) or by loads into registers and LDS
+//    writes.
+// The kernels stay inside their buffers and run a fixed number of
 // iterations; their outputs only keep the work from being removed.
 #include <stdint.h>
 
 #include "../../include/vsa.h"
 #include "../../include/vsa_probe.h"
+#include "fine_common.h"
 #include "vsa_common.h"
 
 namespace vsa {
@@ -97,6 +101,65 @@ static hipError_t launch_stream_read(const f32x4* s4, long n16, int blocks, int 
   return hipGetLastError();
 }
 
+// L2 to LDS: workgroups of two waves with 40 KB of LDS (four per CU, as in
+// the fine forward). Iteration c moves the 16 KB chunk at byte
+// ((blockIdx * 7 + c) * 16 KB) mod src_bytes of src into stage c % 2, each
+// wave 8 KB in 1 KB loads, the next chunk's loads in flight while the
+// current one completes, a barrier per iteration. MODE 0: direct-to-LDS
+// loads; 1: 16-byte loads into registers, then LDS writes.
+constexpr int kL2Stage = 16384;
+template <int MODE>
+__global__ __launch_bounds__(128) void probe_l2_lds_kernel(const char* __restrict__ src, uint32_t src_mask,
+                                                           int iters, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) char buf[2 * kL2Stage + 8192];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  auto chunk_src = [&](int c) {
+    const uint32_t off = ((uint32_t)(blockIdx.x * 7 + c) * (uint32_t)kL2Stage) & src_mask;
+    return reinterpret_cast<const char*>(uniform_ptr(src + off));
+  };
+  if constexpr (MODE == 0) {
+    const uint32_t base = lds_addr(buf);
+    auto issue = [&](int c) {
+      const char* s = chunk_src(c);
+      const uint32_t dst = base + (c & 1) * kL2Stage;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) dma16(s, (uint32_t)((wv * 8 + t) * 1024 + lane * 16), dst + (wv * 8 + t) * 1024);
+    };
+    issue(0);
+    for (int c = 0; c < iters; ++c) {
+      if (c + 1 < iters) {
+        issue(c + 1);
+        wait_vmcnt<8>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();
+    }
+    vm_settled();
+  } else {
+    f32x4 cur[8], nxt[8];
+    auto load = [&](int c, f32x4 (&r)[8]) {
+      const char* s = chunk_src(c);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) r[t] = *reinterpret_cast<const f32x4*>(s + (wv * 8 + t) * 1024 + lane * 16);
+    };
+    load(0, cur);
+    for (int c = 0; c < iters; ++c) {
+      if (c + 1 < iters) load(c + 1, nxt);
+      char* d = buf + (c & 1) * kL2Stage;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(d + (wv * 8 + t) * 1024 + lane * 16) = cur[t];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int t = 0; t < 8; ++t) cur[t] = nxt[t];
+    }
+  }
+  __syncthreads();
+  out[blockIdx.x * 128 + threadIdx.x] = reinterpret_cast<const float*>(buf)[(threadIdx.x * 37) & (2 * kL2Stage / 4 - 1)];
+}
+
 template <int NV, int OP>
 static hipError_t launch_probe_mfma(int waves, int iters, float* out, hipStream_t st) {
   const dim3 grid(256 * waves), block(256);
@@ -149,6 +212,24 @@ int32_t vsa_probe_stream_read(const void* src, size_t bytes, int32_t blocks, int
   const hipError_t e = nontemporal ? vsa::launch_stream_read<true>(s4, n16, blocks, inflight, out, st)
                                    : vsa::launch_stream_read<false>(s4, n16, blocks, inflight, out, st);
   return e == hipSuccess ? VSA_OK : VSA_ERR_HIP;
+}
+
+int32_t vsa_probe_l2_to_lds(int32_t mode, const void* src, size_t src_bytes, int32_t blocks, int32_t iters,
+                            float* out, void* stream) {
+  if (src == nullptr || out == nullptr) return VSA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) != 0) return VSA_ERR_ALIGN;
+  if (src_bytes < (size_t)vsa::kL2Stage || src_bytes > ((size_t)1 << 30) || (src_bytes & (src_bytes - 1)) != 0)
+    return VSA_ERR_SHAPE;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1) return VSA_ERR_SHAPE;
+  if (mode != 0 && mode != 1) return VSA_ERR_UNSUPPORTED;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const char* s = static_cast<const char*>(src);
+  const uint32_t mask = (uint32_t)(src_bytes - 1);
+  if (mode == 0)
+    hipLaunchKernelGGL(vsa::probe_l2_lds_kernel<0>, dim3(blocks), dim3(128), 0, st, s, mask, iters, out);
+  else
+    hipLaunchKernelGGL(vsa::probe_l2_lds_kernel<1>, dim3(blocks), dim3(128), 0, st, s, mask, iters, out);
+  return hipGetLastError() == hipSuccess ? VSA_OK : VSA_ERR_HIP;
 }
 
 }  // extern "C"

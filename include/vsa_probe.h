@@ -1,6 +1,6 @@
 /*
  * vsa_probe.h - measurement aids of the VSA library for one AMD Instinct
- * MI355X (gfx950). They are not steps of the operator: they measure two
+ * MI355X (gfx950). They are not steps of the operator: they measure
  * properties of the chip that bound its kernels, so that the bounds quoted
  * with those kernels can be reproduced (bench.py --mode probe).
  *
@@ -46,6 +46,20 @@ int32_t vsa_probe_mfma_valu(int32_t valu, int32_t op, int32_t waves_per_simd, in
  * (inflight, nontemporal). */
 int32_t vsa_probe_stream_read(const void* src, size_t bytes, int32_t blocks, int32_t inflight, int32_t nontemporal,
                               float* out, void* stream);
+
+/* L2-resident data into LDS (the chunk path of the fine kernels). `blocks`
+ * workgroups of two waves, each with 40 KB of LDS (four per CU), run `iters`
+ * iterations; iteration c moves the 16 KB chunk at byte offset
+ * ((block * 7 + c) * 16384) mod src_bytes of src into one of two LDS stages,
+ * by direct-to-LDS loads (mode 0) or by 16-byte loads into registers and LDS
+ * writes (mode 1), with the next chunk's loads in flight and a barrier per
+ * iteration: blocks * iters * 16384 bytes in all. src_bytes: a power of two
+ * from 16384 to 2^30 (2 MB keeps the source in every XCD's L2); out:
+ * blocks * 128 floats, written.
+ * Errors: VSA_ERR_NULL, VSA_ERR_ALIGN (src), VSA_ERR_SHAPE (src_bytes, blocks
+ * outside [1, 2^20], iters < 1), VSA_ERR_UNSUPPORTED (mode). */
+int32_t vsa_probe_l2_to_lds(int32_t mode, const void* src, size_t src_bytes, int32_t blocks, int32_t iters,
+                            float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,7 @@ def header_functions():
     names = set()
     for h in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text))
+        names |= set(re.findall(r"\b(vsa_[a-z0-9_]+)\s*\(", text))
     return sorted(names)
 
 
@@ -312,3 +312,11 @@ def test_probe_arguments_rejected_on_the_host():
     assert lib.vsa_probe_stream_read(buf, 1024, 0, 4, 0, buf, None) == SHAPE
     assert lib.vsa_probe_stream_read(buf, 1024, 4, 3, 0, buf, None) == UNSUP
     assert lib.vsa_probe_stream_read(buf, 1024, 4, 4, 2, buf, None) == UNSUP
+    assert lib.vsa_probe_l2_to_lds(0, None, 1 << 21, 4, 4, buf, None) == NULL
+    assert lib.vsa_probe_l2_to_lds(0, buf, 1 << 21, 4, 4, None, None) == NULL
+    assert lib.vsa_probe_l2_to_lds(0, ctypes.c_void_p(8), 1 << 21, 4, 4, buf, None) == ALIGN
+    assert lib.vsa_probe_l2_to_lds(0, buf, 3 << 20, 4, 4, buf, None) == SHAPE
+    assert lib.vsa_probe_l2_to_lds(0, buf, 8192, 4, 4, buf, None) == SHAPE
+    assert lib.vsa_probe_l2_to_lds(0, buf, 1 << 21, 0, 4, buf, None) == SHAPE
+    assert lib.vsa_probe_l2_to_lds(0, buf, 1 << 21, 4, 0, buf, None) == SHAPE
+    assert lib.vsa_probe_l2_to_lds(2, buf, 1 << 21, 4, 4, buf, None) == UNSUP

@@ -1,7 +1,8 @@
 """The chip probes of include/vsa_probe.h on the GPU: the streaming read
 reaches every element exactly once (its per-thread sums of a buffer of ones
 add up to the element count, for ragged sizes, every in-flight depth and both
-load kinds), and the MFMA / vector-ALU probe runs and writes its whole output."""
+load kinds); the MFMA / vector-ALU probe and the L2-to-LDS probe run and
+write their whole output (the latter the values of the chunks it moved)."""
 import pytest
 import torch
 
@@ -33,3 +34,15 @@ def test_mfma_valu_probe_runs(waves, op, valu):
     assert not torch.isnan(out).any()
     if op == 0:
         assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("src_floats,blocks,iters", [(4096, 1, 2), (1 << 19, 37, 5), (1 << 16, 512, 3)])
+def test_l2_to_lds_probe_moves_the_source(mode, src_floats, blocks, iters):
+    src = torch.full((src_floats,), 3.0, dtype=torch.float32, device=DEV)
+    out = torch.full((blocks * 128,), float("nan"), dtype=torch.float32, device=DEV)
+    V.probe_l2_to_lds(mode, src, blocks, iters, out)
+    torch.cuda.synchronize()
+    # Every thread reads back one float of the two LDS stages, both filled
+    # from the source once there are at least two iterations.
+    assert (out == 3.0).all()
